@@ -1,0 +1,351 @@
+"""Pins for the CPU oracle: every check here is computed by something other than the oracle.
+
+* brute force over all subsets on tiny inputs (masks, double prune, FFI select);
+* invariants (group counts, mask2 subset of mask1, idempotence, identity cases);
+* the added sparsity of SLoPe's Lemma 2.1 (§2.1, App. T.1), statistically;
+* library routines: torch autograd and ``F.linear`` in float64, the LoRA merge
+  identity (a LoRA product can be folded into the base weight: "efficient
+  training for the gpu-poor", section PEFT), and central finite differences.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import ffi, layer, nm
+from sra_inputs import WORKLOADS, layer_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- brute force helpers
+
+def brute_group_keep(mags, eligible, n):
+    """Max-sum subset of the eligible positions, size min(n, #eligible), lexicographically
+    smallest among the maxima.  Equivalent to top-n by (|w| desc, index asc)."""
+    E = [i for i in range(len(mags)) if eligible[i]]
+    s = min(n, len(E))
+    best, best_set = None, None
+    for comb in itertools.combinations(E, s):   # combinations come out in lexicographic order
+        tot = sum(mags[i] for i in comb)
+        if best is None or tot > best:
+            best, best_set = tot, comb
+    return set(best_set)
+
+
+def brute_mask1(W, n, m):
+    rows, cols = W.shape
+    mask = np.zeros_like(W, dtype=bool)
+    for r in range(rows):
+        for g in range(cols // m):
+            mags = [abs(float(W[r, g * m + a])) for a in range(m)]
+            for a in brute_group_keep(mags, [True] * m, n):
+                mask[r, g * m + a] = True
+    return mask
+
+
+def brute_double_prune(Ws, mask1, n, m):
+    """Returns (mask2 in Ws orientation, stored positions of P in P orientation, P dense)."""
+    rows, cols = Ws.shape
+    mask2 = np.zeros_like(mask1)
+    storedT = np.zeros((cols, rows), dtype=bool)
+    PT = np.zeros((cols, rows))
+    for c in range(cols):
+        for g in range(rows // m):
+            mags = [abs(float(Ws[g * m + a, c])) for a in range(m)]
+            elig = [bool(mask1[g * m + a, c]) for a in range(m)]
+            kept = brute_group_keep(mags, elig, n)
+            pad = [a for a in range(m) if a not in kept][: n - len(kept)]
+            for a in kept:
+                mask2[g * m + a, c] = True
+                PT[c, g * m + a] = Ws[g * m + a, c]
+            for a in pad:
+                storedT[c, g * m + a] = True
+            for a in kept:
+                storedT[c, g * m + a] = True
+    return mask2, storedT, PT
+
+
+def tie_heavy(rng, shape, alphabet=(0.0, -0.0, 0.5, -0.5, 1.0, 2.0)):
+    return np.array(rng.choice(np.array(alphabet), size=shape), dtype=np.float64)
+
+
+NM_CASES = [(1, 2), (2, 4), (1, 4), (3, 4), (2, 2), (4, 4)]
+
+
+# ----------------------------------------------------------------------------- a1: N:M mask + format
+
+@pytest.mark.parametrize("n,m", NM_CASES)
+@pytest.mark.parametrize("kind", ["gauss", "ties"])
+def test_mask1_matches_brute_force(n, m, kind):
+    rng = np.random.default_rng(100 * n + m)
+    for trial in range(6):
+        rows, cols = int(rng.integers(1, 7)), m * int(rng.integers(1, 9))
+        W = rng.standard_normal((rows, cols)) if kind == "gauss" else tie_heavy(rng, (rows, cols))
+        assert np.array_equal(nm.nm_mask(W, n, m), brute_mask1(W, n, m))
+
+
+def test_pack_golden_example():
+    g = json.load(open(os.path.join(GOLDEN, "nm_pack_example.json")))
+    W = np.array(g["W"])
+    vals, meta, mask1 = nm.compress(W, g["n"], g["m"])
+    assert np.array_equal(vals, np.array(g["values"]))
+    assert np.array_equal(np.signbit(vals), np.signbit(np.array(g["values"])))
+    assert np.array_equal(nm.unpack_fields(meta, 8), np.array(g["fields"]))
+    assert meta.dtype == np.uint32 and meta.tolist() == g["meta_words"]
+
+
+@pytest.mark.parametrize("n,m", NM_CASES)
+def test_compress_invariants(n, m):
+    rng = np.random.default_rng(7)
+    W = tie_heavy(rng, (12, 64)) if n != m else rng.standard_normal((12, 64))
+    vals, meta, mask1 = nm.compress(W, n, m)
+    g = mask1.reshape(12, -1, m)
+    assert np.all(g.sum(-1) == n)                                       # exactly n stored per group
+    assert np.all((W * mask1 != 0).reshape(12, -1, m).sum(-1) <= n)    # at most n nonzeros per group
+    dense, stored = nm.decompress(vals, meta, n, m, 64)
+    assert np.array_equal(stored, mask1)
+    assert np.array_equal(dense, np.where(mask1, W, 0.0))             # decompress(compress(W)) = W o mask1
+    v2, meta2, _ = nm.compress(dense, n, m)                            # idempotent on the pruned weight
+    assert np.array_equal(nm.decompress(v2, meta2, n, m, 64)[0], dense)
+    assert meta.shape == (12, nm.meta_words_per_row(64, n, m))
+    if n == m:
+        assert mask1.all() and np.array_equal(vals, W)
+
+
+def test_kept_magnitudes_dominate():
+    """Every kept entry is at least as large as every dropped entry of its group."""
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((64, 128)).astype(np.float32).astype(np.float64)
+    mask1 = nm.nm_mask(W, 2, 4)
+    mg = np.abs(W).reshape(64, 32, 4)
+    kg = mask1.reshape(64, 32, 4)
+    kept_min = np.where(kg, mg, np.inf).min(-1)
+    drop_max = np.where(~kg, mg, -np.inf).max(-1)
+    assert np.all(kept_min >= drop_max)
+
+
+# ----------------------------------------------------------------------------- a2: double prune
+
+@pytest.mark.parametrize("n,m", NM_CASES)
+@pytest.mark.parametrize("kind", ["gauss", "ties"])
+def test_double_prune_matches_brute_force(n, m, kind):
+    rng = np.random.default_rng(31 * n + m)
+    for trial in range(4):
+        rows, cols = m * int(rng.integers(1, 6)), m * int(rng.integers(1, 6))
+        W = rng.standard_normal((rows, cols)) if kind == "gauss" else tie_heavy(rng, (rows, cols))
+        vals, meta, mask1 = nm.compress(W, n, m)
+        Pv, Pm, mask2, Wdp = nm.double_prune(vals, meta, n, m, cols)
+        Ws = np.where(mask1, W, 0.0)
+        b_mask2, b_storedT, b_PT = brute_double_prune(Ws, mask1, n, m)
+        assert np.array_equal(mask2, b_mask2)
+        PT, storedT = nm.decompress(Pv, Pm, n, m, rows)
+        assert np.array_equal(storedT, b_storedT)
+        assert np.array_equal(PT, b_PT)
+        assert np.array_equal(Wdp, np.where(b_mask2, Ws, 0.0))
+        assert not np.any(mask2 & ~mask1)                               # mask2 subset of mask1
+        # padding entries are +0.0
+        pad = storedT & ~mask2.T
+        assert np.all(PT[pad] == 0.0) and not np.any(np.signbit(PT[pad]))
+
+
+def test_double_prune_identity_when_dense():
+    """With N = M nothing is pruned twice: P is the exact transpose."""
+    W = np.random.default_rng(0).standard_normal((8, 12))
+    vals, meta, _ = nm.compress(W, 4, 4)
+    Pv, Pm, mask2, Wdp = nm.double_prune(vals, meta, 4, 4, 12)
+    assert mask2.all() and np.array_equal(Wdp, W)
+    assert np.array_equal(nm.decompress(Pv, Pm, 4, 4, 8)[0], W.T)
+
+
+def _binomial_added_zeros(n, m):
+    """Lemma 2.1's model (App. T.1): Y ~ Binomial(M, N/M) nonzeros in an M-block of Ws^T; the
+    second prune removes max(Y - N, 0) of them; report the expected fraction of the block."""
+    p = n / m
+    e = sum((y - n) * math.comb(m, y) * p ** y * (1 - p) ** (m - y) for y in range(n + 1, m + 1))
+    return e / m
+
+
+def test_lemma_2_1_closed_form_against_page():
+    g = json.load(open(os.path.join(GOLDEN, "lemma_2_1.json")))
+    for key, reproduced in g["reproduced_by_binomial_model"].items():
+        n, m = map(int, key.split(":"))
+        model = _binomial_added_zeros(n, m)
+        if reproduced:
+            assert model == pytest.approx(g["printed"][key], abs=1e-12)
+        else:   # the 2:8 discrepancy, recorded rather than enforced
+            assert model == pytest.approx(0.0584, abs=5e-4)
+            assert abs(model - g["printed"][key]) > 0.02
+
+
+@pytest.mark.parametrize("n,m,tol", [(2, 4, 6e-4), (1, 2, 6e-4)])
+def test_lemma_2_1_statistics(n, m, tol):
+    """Gaussian weights at the OPT-350M fc1 size: the oracle's double prune removes the fraction
+    the page prints (12.5% at 1:2, 9.375% at 2:4), within ~4 standard errors."""
+    g = json.load(open(os.path.join(GOLDEN, "lemma_2_1.json")))
+    rng = np.random.default_rng(0)
+    W = rng.standard_normal((4096, 1024)).astype(np.float32).astype(np.float64)
+    vals, meta, mask1 = nm.compress(W, n, m)
+    _, _, mask2, _ = nm.double_prune(vals, meta, n, m, 1024)
+    frac = (mask1 & ~mask2).sum() / W.size
+    assert abs(frac - g["printed"][f"{n}:{m}"]) < tol
+
+
+# ----------------------------------------------------------------------------- a3: fixed fan-in
+
+def brute_ffi_cols(row, k):
+    K = len(row)
+    keep = []
+    for a in range(K):
+        outrank = sum(1 for j in range(K) if abs(row[j]) > abs(row[a]) or (abs(row[j]) == abs(row[a]) and j < a))
+        if outrank < k:
+            keep.append(a)
+    return keep
+
+
+@pytest.mark.parametrize("kind", ["gauss", "ties"])
+def test_ffi_select_matches_brute_force(kind):
+    rng = np.random.default_rng(11)
+    for trial in range(10):
+        rows, K = int(rng.integers(1, 6)), int(rng.integers(1, 40))
+        k = int(rng.integers(1, K + 1))
+        W = rng.standard_normal((rows, K)) if kind == "gauss" else tie_heavy(rng, (rows, K))
+        vals, cols = ffi.select(W, k)
+        assert cols.dtype == np.int16 and cols.shape == (rows, k)
+        for r in range(rows):
+            assert cols[r].tolist() == brute_ffi_cols(W[r].tolist(), k)
+            assert np.array_equal(vals[r], W[r, cols[r].astype(int)])
+
+
+def test_ffi_recovers_generator_columns():
+    wl = WORKLOADS["ffi90_4096"]
+    from sra_inputs import ffi_weight
+    rng = np.random.Generator(np.random.PCG64(5))
+    W, cols = ffi_weight(rng, 256, wl.K, wl.ffi_k, 0.02, "bf16")
+    Wd = W.to(torch.float64).numpy()
+    assert np.all((Wd != 0).sum(1) == wl.ffi_k)
+    vals, got = ffi.select(Wd, wl.ffi_k)
+    assert np.array_equal(got.astype(np.int64), cols)
+    assert np.all((vals != 0).sum(1) == wl.ffi_k)
+
+
+def test_ffi_identity_and_transpose():
+    rng = np.random.default_rng(2)
+    W = tie_heavy(rng, (9, 21))
+    vals, cols = ffi.select(W, 21)                     # k = K keeps everything
+    assert np.array_equal(ffi.to_dense(vals, cols, 21), W)
+    vals, cols = ffi.select(W, 5)
+    D = ffi.to_dense(vals, cols, 21)
+    row_ptr, ids, tv = ffi.transpose(vals, cols, 21)
+    assert row_ptr[0] == 0 and row_ptr[-1] == 9 * 5 and np.all(np.diff(row_ptr) >= 0)
+    assert np.array_equal(ffi.csr_to_dense(row_ptr, ids, tv, 9), D.T)
+    for c in range(21):                                # row ids ascending inside each column
+        seg = ids[row_ptr[c]:row_ptr[c + 1]]
+        assert np.all(np.diff(seg.astype(int)) > 0)
+
+
+# ----------------------------------------------------------------------------- a4-a8: layer math
+
+def _tiny_layer(seed=0, T=7, K=16, N=12, r=3):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K))
+    W = rng.standard_normal((N, K))
+    A = rng.standard_normal((r, K)) * 0.5
+    B = rng.standard_normal((N, r)) * 0.5
+    dY = rng.standard_normal((T, N))
+    vals, meta, mask1 = nm.compress(W, 2, 4)
+    Ws = np.where(mask1, W, 0.0)
+    _, _, mask2, Wdp = nm.double_prune(vals, meta, 2, 4, K)
+    return X, Ws, Wdp, A, B, dY
+
+
+def t64(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)
+
+
+def test_forward_reduces_to_linear_without_adapter():
+    X, Ws, _, A, B, _ = _tiny_layer()
+    Y, U = layer.forward(X, Ws, np.zeros_like(A), np.zeros_like(B))
+    assert np.allclose(Y, F.linear(t64(X), t64(Ws)).numpy(), rtol=1e-13, atol=1e-13)
+    Y0, U0 = layer.forward(X, Ws, A[:0], B[:, :0])     # rank 0
+    assert U0.shape == (X.shape[0], 0)
+    assert np.allclose(Y0, F.linear(t64(X), t64(Ws)).numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_forward_lora_merge_identity():
+    """LoRA can be merged into the base weight: Y = X (Ws + B A)^T."""
+    X, Ws, _, A, B, _ = _tiny_layer(1)
+    Y, U = layer.forward(X, Ws, A, B)
+    merged = F.linear(t64(X), t64(Ws) + t64(B) @ t64(A)).numpy()
+    assert np.allclose(Y, merged, rtol=1e-12, atol=1e-12)
+    assert np.allclose(U, F.linear(t64(X), t64(A)).numpy(), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("r", [0, 1, 3, 8])
+def test_backward_matches_autograd(r):
+    X, Ws, Wdp, A, B, dY = _tiny_layer(2, r=r)
+    Xt, At, Bt = t64(X).requires_grad_(), t64(A).requires_grad_(), t64(B).requires_grad_()
+    # substituted forward: the double-pruned weight carries dX
+    U = F.linear(Xt, At)
+    U.retain_grad()
+    Y = F.linear(Xt, t64(Wdp)) + F.linear(U, Bt)
+    (Y * t64(dY)).sum().backward()
+    g = layer.backward(dY, X, Wdp, A, B)
+    assert np.allclose(g["dX"], Xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dA"], At.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dB"], Bt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dU"], U.grad.numpy(), rtol=1e-12, atol=1e-12)
+    g2 = layer.backward(dY, X, Wdp, A, B, dx_adapter=False)
+    assert np.allclose(g2["dX"], F.linear(t64(dY), t64(Wdp).T).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_finite_differences():
+    """L(A, B, X) = sum(dY * Y) is linear in each argument, so central differences are exact
+    up to rounding.  dX is the gradient of the forward that uses the double-pruned weight."""
+    X, Ws, Wdp, A, B, dY = _tiny_layer(3, T=3, K=8, N=8, r=2)
+    g = layer.backward(dY, X, Wdp, A, B)
+
+    def loss(X_, A_, B_):
+        return float(np.sum(dY * (X_ @ Wdp.T + (X_ @ A_.T) @ B_.T)))
+
+    h = 0.5
+    for name, arr in (("dA", A), ("dB", B), ("dX", X)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p, q = arr.copy(), arr.copy()
+            p[idx] += h
+            q[idx] -= h
+            args_p = {"dA": (X, p, B), "dB": (X, A, p), "dX": (p, A, B)}[name]
+            args_q = {"dA": (X, q, B), "dB": (X, A, q), "dX": (q, A, B)}[name]
+            num[idx] = (loss(*args_p) - loss(*args_q)) / (2 * h)
+        assert np.allclose(g[name], num, rtol=1e-10, atol=1e-10), name
+
+
+def test_double_pruned_dx_differs_from_true_gradient():
+    """Sanity for the reading that dX uses Wdp: on a Gaussian weight the two differ."""
+    X, Ws, Wdp, A, B, dY = _tiny_layer(4, T=4, K=32, N=32, r=0)
+    assert not np.array_equal(Ws, Wdp)
+    assert not np.allclose(layer.backward(dY, X, Wdp, A, B)["dX"], dY @ Ws)
+
+
+def test_rel_err_metric():
+    assert layer.rel_err([1.0, 0.0], [1.0, 0.0]) == 0.0
+    assert layer.rel_err([1.02], [1.0]) == pytest.approx(0.02 / 1.001)
+    assert layer.rel_err([1e-3], [0.0]) == pytest.approx(1.0)
+
+
+def test_inputs_are_seeded_and_rounded():
+    wl = WORKLOADS["tiny_f32"]
+    a = layer_inputs(wl, seed=0)
+    b = layer_inputs(wl, seed=0)
+    for k in ("X", "W", "A", "B", "dY"):
+        assert torch.equal(a[k], b[k]) and a[k].dtype == torch.float32
+    assert a["X"].shape == (8, 64) and a["W"].shape == (32, 64) and a["A"].shape == (4, 64)
+    assert a["B"].shape == (32, 4) and a["dY"].shape == (8, 32)
+    c = layer_inputs(WORKLOADS["opt350m_fc1"], seed=0, T=16)
+    assert c["X"].dtype == torch.bfloat16
