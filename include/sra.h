@@ -1,0 +1,195 @@
+/*
+ * sra.h -- C ABI of libsra, a structured-sparse plus low-rank linear layer for AMD MI355X (gfx950).
+ *
+ * The layer (SLoPe paperlayer summary, §2.2 "Lazy low-rank adapters"; LoRA as described in
+ * "efficient training for the gpu-poor", section PEFT):
+ *
+ *     forward   U  = X A^T                      (fp32)
+ *               Y  = X Ws^T + U B^T
+ *     backward  dU = dY B                       (fp32)
+ *               dB = dY^T U,  dA = dU^T X       (fp32)
+ *               dX = dY P^T + dU A              (P = double-pruned Ws^T for N:M weights,
+ *                                                the exact transpose for fixed fan-in weights)
+ *
+ * Shapes: X [T,K], Ws [N,K] (N outputs, K inputs), A [r,K], B [N,r], Y/dY [T,N], dX [T,K].
+ * Ws is either N:M sparse along K (2:4: every 4 consecutive inputs keep 2; SLoPe §2.1) or fixed
+ * fan-in (every output row keeps exactly k inputs at arbitrary columns; SQuAsh project update).
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major and contiguous.  Pointers are device pointers unless marked "host".
+ *     Device pointers must be 16-byte aligned.
+ *   - Ownership: the caller allocates and frees every buffer, including outputs and the
+ *     workspace; the library allocates no device memory and keeps no pointer after a call returns.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; a call returns after launching.  Calls on different streams may overlap.
+ *   - Errors: every call returns an sra_status.  All argument checks happen on the host before any
+ *     launch, so a non-OK status means nothing was enqueued, except SRA_ERR_HIP, which reports a
+ *     launch failure (some earlier kernels of the same call may have been enqueued).
+ *     sra_last_error() returns a message for the last failing call of the calling thread.
+ *   - Inputs must be finite.  Values of dtype X (bf16 or fp32) are: X, dY, A, B, Y, dX and the
+ *     compressed values; U, dU, dA and dB are always fp32.
+ *   - Tie rule for every magnitude selection: larger |w| first; equal magnitudes go to the lower
+ *     index; +0 and -0 are equal.
+ */
+#ifndef SRA_H
+#define SRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SRA_ABI_VERSION 1
+
+typedef enum {
+  SRA_OK = 0,
+  SRA_ERR_INVALID_ARG = -1, /* null pointer, bad shape, misaligned pointer, inconsistent descriptor */
+  SRA_ERR_UNSUPPORTED = -2, /* valid request outside what the kernels implement (e.g. N:M other than 2:4) */
+  SRA_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than the *_workspace query returned */
+  SRA_ERR_HIP = -4          /* a HIP launch failed; see sra_last_error() */
+} sra_status;
+
+typedef enum { SRA_BF16 = 0, SRA_F32 = 1 } sra_dtype;
+
+typedef enum {
+  SRA_FMT_NM = 0,  /* N:M along cols: values [rows, cols*n/m], meta [rows, sra_nm_meta_words] */
+  SRA_FMT_ELL = 1, /* fixed fan-in: values [rows, k], index int16 [rows, k], columns ascending */
+  SRA_FMT_CSR = 2  /* transpose of an ELL matrix: row_ptr int32 [rows+1], index int16 [nnz],
+                      values [nnz], column ids ascending inside each row */
+} sra_format;
+
+/*
+ * Description of a compressed sparse matrix (caller-owned; the library only reads it, except that
+ * sra_double_prune / sra_ffi_transpose fill the shape fields of their output descriptor).
+ *
+ * rows x cols is the logical dense shape; every row is reduced over its cols.  For the forward the
+ * matrix is Ws (rows = N outputs, cols = K); for the backward it is P (rows = K, cols = N).
+ *
+ * N:M canonical format (SLoPe §2.1 N:M prune, layout of this library): row i keeps, in each group
+ * of m consecutive columns, n entries.  values[i, :] holds the kept entries in ascending column
+ * order.  meta[i, :] holds each kept entry's position inside its group as a 2-bit field, fields in
+ * kept order, packed least-significant first, 16 fields per uint32 word; the unused high fields of
+ * the last word are zero.  Word count per row: sra_nm_meta_words(cols, n, m).
+ */
+typedef struct sra_sparse {
+  int32_t format;   /* sra_format */
+  int32_t dtype;    /* sra_dtype of values */
+  int64_t rows;
+  int64_t cols;
+  int32_t n, m;     /* SRA_FMT_NM */
+  int32_t k;        /* SRA_FMT_ELL: entries per row */
+  int64_t nnz;      /* SRA_FMT_CSR: stored entries (= rows_of_ELL * k) */
+  void* values;
+  uint32_t* meta;   /* SRA_FMT_NM */
+  int16_t* index;   /* SRA_FMT_ELL / SRA_FMT_CSR */
+  int32_t* row_ptr; /* SRA_FMT_CSR */
+} sra_sparse;
+
+/* ABI version of the loaded library (SRA_ABI_VERSION when it matches this header). */
+int32_t sra_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread (host string, owned by the
+ * library, valid until the next call on that thread).  Empty string if none. */
+const char* sra_last_error(void);
+
+/* Number of uint32 metadata words per row for an N:M row of `cols` columns: ceil(cols*n/m/16). */
+int64_t sra_nm_meta_words(int64_t cols, int32_t n, int32_t m);
+
+/*
+ * compress(W, N, M) -- first N:M prune (SLoPe §2.1; the mask is chosen once and kept fixed).
+ * W [rows, cols] dense (dtype) -> out->values [rows, cols*n/m], out->meta [rows, meta_words].
+ * In each group of m consecutive columns the n entries of largest magnitude are kept.
+ * Supported: n = 2, m = 4, cols % 32 == 0.  The caller sets out->values and out->meta; the call
+ * fills the remaining descriptor fields (format, dtype, rows, cols, n, m).
+ */
+sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
+                        int32_t m, sra_sparse* out /* host */, void* stream);
+
+/*
+ * double_prune -- P = prune_NM(Ws^T) (SLoPe §1 and §2.1: the N:M-pruned weight is transposed and
+ * N:M-pruned again along the other dimension, so the backward product is also N:M).
+ * Ws: SRA_FMT_NM, rows = N outputs, cols = K.  P: caller sets P->values [K, N*n/m] and
+ * P->meta [K, meta_words(N)]; the call fills the other fields (rows = K, cols = N).
+ * In each group of m consecutive outputs of one input column, only entries kept by Ws are
+ * eligible; the n largest eligible are kept.  A group with fewer than n eligible entries is padded
+ * with its lowest unused positions holding +0.0, so every group stores exactly n.
+ * Supported: 2:4, Ws->rows % 32 == 0, Ws->cols % 32 == 0.
+ */
+sra_status sra_double_prune(const sra_sparse* Ws /* host */, sra_sparse* P /* host */, void* stream);
+
+/*
+ * compress_ffi(W, k) -- fixed fan-in selection (SQuAsh project update): every row of W
+ * [rows, cols] keeps its k largest-magnitude entries.  out->values [rows, k] and out->index
+ * (int16) [rows, k] with columns ascending; set by the caller, other fields filled by the call.
+ * Needs 1 <= k <= cols <= 32767.
+ */
+sra_status sra_compress_ffi(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t k,
+                            sra_sparse* out /* host */, void* stream);
+
+/* Workspace bytes for sra_ffi_transpose of an ELL matrix with `rows` rows and `cols` columns. */
+sra_status sra_ffi_transpose_workspace(int64_t rows, int64_t cols, int32_t k, size_t* bytes /* host */);
+
+/*
+ * ffi_transpose -- exact transpose of a fixed fan-in weight for the backward (SLoPe §2.3 keeps
+ * sparse formats for a weight and its transpose).  Ws: SRA_FMT_ELL [rows, cols].  WsT: caller
+ * sets row_ptr [cols+1], index [rows*k], values [rows*k]; the call fills the other fields
+ * (format CSR, rows = Ws->cols, cols = Ws->rows, nnz).  Entries of each CSR row are ordered by
+ * ascending original row.
+ */
+sra_status sra_ffi_transpose(const sra_sparse* Ws /* host */, sra_sparse* WsT /* host */, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Workspace bytes for sra_sparse_lora_fwd (T tokens, rank r). */
+sra_status sra_fwd_workspace(const sra_sparse* Ws /* host */, int64_t T, int32_t r,
+                             size_t* bytes /* host */);
+
+/*
+ * sparse_lora_fwd -- Y = X Ws^T + (X A^T) B^T (SLoPe §2.2; the adapter product is fused into the
+ * sparse product's epilogue, cf. SLoPe §2.4 and App. D, so Y is written once).
+ * Ws: SRA_FMT_NM (2:4) or SRA_FMT_ELL, rows = N, cols = K.  X [T,K], A [r,K], B [N,r], Y [T,N].
+ * U_out [T,r] fp32 receives U = X A^T when non-NULL (keep it for the backward).
+ * r = 0 means no adapter (A, B, U_out ignored).  T = 0 is a no-op.  Y has dtype Ws->dtype.
+ * bf16 accumulates in fp32 (U is kept in fp32); fp32 accumulates in fp64.
+ * Supported: 0 <= r <= 256 (2:4 weights need K % 32 == 0, as for sra_compress).
+ */
+sra_status sra_sparse_lora_fwd(const sra_sparse* Ws /* host */, const void* X, int64_t T,
+                               const void* A, const void* B, int32_t r, void* Y, float* U_out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+enum {
+  SRA_GRAD_DX = 1,       /* compute dX */
+  SRA_GRAD_DA = 2,       /* compute dA */
+  SRA_GRAD_DB = 4,       /* compute dB */
+  SRA_DX_NO_ADAPTER = 8  /* dX without the dU A term (sparse product only) */
+};
+
+/* Workspace bytes for sra_sparse_lora_bwd. */
+sra_status sra_bwd_workspace(const sra_sparse* P /* host */, int64_t T, int32_t r, uint32_t flags,
+                             size_t* bytes /* host */);
+
+/*
+ * sparse_lora_bwd -- double-pruned backward (SLoPe §1, §2.1; the output gradient dY is never
+ * pruned, SLoPe App. J).
+ * P: for N:M weights the output of sra_double_prune (rows = K, cols = N); for fixed fan-in weights
+ * the CSR of sra_ffi_transpose (rows = K, cols = N).
+ * dY [T,N], X [T,K], A [r,K], B [N,r] (dtype P->dtype); T tokens.  U [T,r] fp32 from the forward, or NULL
+ * to recompute it from X and A.  Outputs (each only if its flag is set): dX [T,K] (dtype),
+ * dA [r,K] fp32, dB [N,r] fp32.  dU_out [T,r] fp32 receives dU = dY B when non-NULL and r > 0.
+ * Flags without r > 0 (dA, dB) are ignored.
+ * dA and dB reduce over all T tokens in a fixed order (results do not depend on the stream).
+ * fp32 weights keep U and dU in fp64 inside the call (U is recomputed from X and A; the U
+ * argument is not read).
+ * T = 0 writes zeros to dA and dB.
+ */
+sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, const void* X,
+                               int64_t T, const float* U, const void* A, const void* B, int32_t r,
+                               uint32_t flags, void* dX, float* dA, float* dB, float* dU_out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SRA_H */

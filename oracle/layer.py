@@ -24,23 +24,27 @@ def forward(X, Ws, A, B):
     return Y, U
 
 
-def backward(dY, X, Wsub, A, B, U=None, dx_adapter=True):
+def backward(dY, X, Wsub, A, B, U=None, dx_adapter=True, want=("dU", "dB", "dA", "dX")):
     """Gradients of L = sum(dY * Y) for the forward Y = X Wsub^T + (X A^T) B^T.
 
     For N:M weights ``Wsub`` is the double-pruned weight Wdp (so dX is the
     gradient of the substituted forward, not of the original one); for FFI
     weights it is Ws itself.  Returns dict with dU [T,r], dB [N,r], dA [r,K],
-    dX [T,K].  ``dx_adapter=False`` drops the dU A term from dX.
+    dX [T,K].  ``dx_adapter=False`` drops the dU A term from dX.  ``want`` limits which are
+    computed, so a caller can evaluate a restricted sub-problem cheaply.
     """
-    if U is None:
-        U = X @ A.T
+    out = {}
     dU = dY @ B
-    dB = dY.T @ U
-    dA = dU.T @ X
-    dX = dY @ Wsub
-    if dx_adapter:
-        dX = dX + dU @ A
-    return {"dU": dU, "dB": dB, "dA": dA, "dX": dX}
+    if "dU" in want:
+        out["dU"] = dU
+    if "dB" in want:
+        out["dB"] = dY.T @ (X @ A.T if U is None else U)
+    if "dA" in want:
+        out["dA"] = dU.T @ X
+    if "dX" in want:
+        dX = dY @ Wsub
+        out["dX"] = dX + dU @ A if dx_adapter else dX
+    return out
 
 
 def rel_err(got, ref, floor=1e-3):

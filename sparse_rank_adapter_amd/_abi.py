@@ -1,0 +1,81 @@
+"""ctypes declarations of libsra's C ABI (include/sra.h).  Marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsra.so")
+
+SRA_OK, SRA_ERR_INVALID_ARG, SRA_ERR_UNSUPPORTED, SRA_ERR_WORKSPACE, SRA_ERR_HIP = 0, -1, -2, -3, -4
+STATUS_NAMES = {0: "SRA_OK", -1: "SRA_ERR_INVALID_ARG", -2: "SRA_ERR_UNSUPPORTED",
+                -3: "SRA_ERR_WORKSPACE", -4: "SRA_ERR_HIP"}
+SRA_BF16, SRA_F32 = 0, 1
+SRA_FMT_NM, SRA_FMT_ELL, SRA_FMT_CSR = 0, 1, 2
+SRA_GRAD_DX, SRA_GRAD_DA, SRA_GRAD_DB, SRA_DX_NO_ADAPTER = 1, 2, 4, 8
+
+# every symbol include/sra.h declares
+EXPORTS = (
+    "sra_abi_version", "sra_last_error", "sra_nm_meta_words", "sra_compress", "sra_double_prune",
+    "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
+    "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd",
+)
+
+
+class SraSparse(ctypes.Structure):
+    _fields_ = [
+        ("format", c_int32), ("dtype", c_int32), ("rows", c_int64), ("cols", c_int64),
+        ("n", c_int32), ("m", c_int32), ("k", c_int32), ("nnz", c_int64),
+        ("values", c_void_p), ("meta", c_void_p), ("index", c_void_p), ("row_ptr", c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libsra.so (after torch, so both share torch's HIP runtime).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- loads the HIP runtime the library must share
+
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m sparse_rank_adapter_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = POINTER(SraSparse)
+    sig = {
+        "sra_abi_version": (c_int32, []),
+        "sra_last_error": (c_char_p, []),
+        "sra_nm_meta_words": (c_int64, [c_int64, c_int32, c_int32]),
+        "sra_compress": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32, P, c_void_p]),
+        "sra_double_prune": (c_int32, [P, P, c_void_p]),
+        "sra_compress_ffi": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, P, c_void_p]),
+        "sra_ffi_transpose_workspace": (c_int32, [c_int64, c_int64, c_int32, POINTER(c_size_t)]),
+        "sra_ffi_transpose": (c_int32, [P, P, c_void_p, c_size_t, c_void_p]),
+        "sra_fwd_workspace": (c_int32, [P, c_int64, c_int32, POINTER(c_size_t)]),
+        "sra_sparse_lora_fwd": (c_int32, [P, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p,
+                                          c_void_p, c_void_p, c_size_t, c_void_p]),
+        "sra_bwd_workspace": (c_int32, [P, c_int64, c_int32, c_uint32, POINTER(c_size_t)]),
+        "sra_sparse_lora_bwd": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                                          c_int32, c_uint32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_size_t, c_void_p]),
+    }
+    assert set(sig) == set(EXPORTS)
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class SraError(RuntimeError):
+    def __init__(self, call: str, status: int, msg: str):
+        super().__init__(f"{call} -> {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def check(call: str, status: int):
+    if status != SRA_OK:
+        raise SraError(call, status, load().sra_last_error().decode())

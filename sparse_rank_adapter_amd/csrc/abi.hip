@@ -1,0 +1,464 @@
+// C ABI of libsra: argument validation, workspace layout and kernel dispatch.
+// Every check runs on the host before the first launch of a call.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <algorithm>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sra_status fail(sra_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bool debug_sync() {
+  static const int v = [] {
+    const char* e = getenv("SRA_DEBUG");
+    return e ? atoi(e) : 0;
+  }();
+  return v != 0;
+}
+
+sra_status hip_done(hipError_t e, hipStream_t s, const char* what) {
+  if (e != hipSuccess) return fail(SRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  if (debug_sync()) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(SRA_ERR_HIP, "%s (sync): %s", what, hipGetErrorString(e));
+  }
+  return SRA_OK;
+}
+
+#define SRA_TRY(expr)                   \
+  do {                                  \
+    const sra_status st_ = (expr);      \
+    if (st_ != SRA_OK) return st_;      \
+  } while (0)
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == SRA_BF16 ? 2 : 4; }
+
+sra_status check_dtype(int dtype) {
+  if (dtype != SRA_BF16 && dtype != SRA_F32) return fail(SRA_ERR_INVALID_ARG, "dtype %d is not SRA_BF16 or SRA_F32", dtype);
+  return SRA_OK;
+}
+
+sra_status check_ptr(const void* p, bool needed, const char* name) {
+  if (!needed) return SRA_OK;
+  if (!p) return fail(SRA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!al16(p)) return fail(SRA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return SRA_OK;
+}
+
+sra_status check_nm(int64_t rows, int64_t cols, int n, int m) {
+  if (rows < 0 || cols < 0) return fail(SRA_ERR_INVALID_ARG, "negative shape");
+  if (n < 1 || m < n || m > 4) return fail(SRA_ERR_INVALID_ARG, "invalid N:M %d:%d", n, m);
+  if (n != 2 || m != 4) return fail(SRA_ERR_UNSUPPORTED, "only 2:4 is implemented (got %d:%d)", n, m);
+  if (cols % 32) return fail(SRA_ERR_UNSUPPORTED, "grouped dimension %lld is not a multiple of 32", (long long)cols);
+  return SRA_OK;
+}
+
+sra_status check_sparse(const sra_sparse* S, const char* name) {
+  if (!S) return fail(SRA_ERR_INVALID_ARG, "%s descriptor is NULL", name);
+  SRA_TRY(check_dtype(S->dtype));
+  if (S->rows < 0 || S->cols < 0) return fail(SRA_ERR_INVALID_ARG, "%s has a negative shape", name);
+  const bool any = S->rows > 0 && S->cols > 0;
+  if (S->format == SRA_FMT_NM) {
+    SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
+    SRA_TRY(check_ptr(S->values, any, "values"));
+    SRA_TRY(check_ptr(S->meta, any, "meta"));
+  } else if (S->format == SRA_FMT_ELL) {
+    if (S->cols > 32767) return fail(SRA_ERR_INVALID_ARG, "%s: ELL needs cols <= 32767", name);
+    if (S->k < 1 || S->k > S->cols) return fail(SRA_ERR_INVALID_ARG, "%s: need 1 <= k <= cols", name);
+    if (S->rows * (int64_t)S->k > INT32_MAX) return fail(SRA_ERR_UNSUPPORTED, "%s: rows*k exceeds int32", name);
+    SRA_TRY(check_ptr(S->values, any, "values"));
+    SRA_TRY(check_ptr(S->index, any, "index"));
+  } else if (S->format == SRA_FMT_CSR) {
+    if (S->cols > 32767) return fail(SRA_ERR_INVALID_ARG, "%s: CSR column ids are int16 (cols <= 32767)", name);
+    if (S->nnz < 0 || S->nnz > INT32_MAX) return fail(SRA_ERR_INVALID_ARG, "%s: bad nnz", name);
+    SRA_TRY(check_ptr(S->row_ptr, S->rows > 0, "row_ptr"));
+    SRA_TRY(check_ptr(S->values, S->nnz > 0, "values"));
+    SRA_TRY(check_ptr(S->index, S->nnz > 0, "index"));
+  } else {
+    return fail(SRA_ERR_INVALID_ARG, "%s: unknown format %d", name, S->format);
+  }
+  return SRA_OK;
+}
+
+// Bump allocation inside the caller's workspace (256-byte aligned pieces).
+struct Arena {
+  size_t used = 0;
+  size_t take(size_t bytes) {
+    const size_t off = used;
+    used += (bytes + 255) & ~(size_t)255;
+    return off;
+  }
+};
+
+sra::F32Sparse f32_view(const sra_sparse* S) {
+  sra::F32Sparse v{};
+  v.format = S->format;
+  v.rows = S->rows;
+  v.cols = S->cols;
+  v.vals = (const uint32_t*)S->values;
+  v.meta = S->meta;
+  v.meta_stride = S->format == SRA_FMT_NM ? sra_nm_meta_words(S->cols, S->n, S->m) : 0;
+  v.idx = S->index;
+  v.row_ptr = S->row_ptr;
+  v.k = S->k;
+  return v;
+}
+
+// ---------------------------------------------------------------- forward plan
+struct FwdPlan {
+  size_t u_off = 0, u64_off = 0, gemm_off = 0, total = 0;
+  bool own_u = false;
+};
+
+sra_status validate_fwd(const sra_sparse* Ws, int64_t T, int32_t r) {
+  SRA_TRY(check_sparse(Ws, "Ws"));
+  if (Ws->format == SRA_FMT_CSR) return fail(SRA_ERR_INVALID_ARG, "forward takes an N:M or ELL weight, not CSR");
+  if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
+  if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
+  if (Ws->format == SRA_FMT_NM && Ws->dtype == SRA_BF16 && Ws->cols == 0)
+    return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 forward needs K > 0");
+  return SRA_OK;
+}
+
+size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan* plan) {
+  Arena a;
+  FwdPlan p;
+  p.own_u = own_u && r > 0 && Ws->dtype == SRA_BF16;
+  if (p.own_u) p.u_off = a.take((size_t)T * r * 4);
+  if (Ws->dtype == SRA_F32 && r > 0) p.u64_off = a.take((size_t)T * r * 8);
+  if (Ws->dtype == SRA_BF16 && r > 0) {
+    p.gemm_off = a.take(sra::adapter_gemm_ws(T, r, Ws->cols));
+  }
+  p.total = a.used;
+  if (plan) *plan = p;
+  return p.total;
+}
+
+// ---------------------------------------------------------------- backward plan
+struct BwdPlan {
+  bool need_du = false, need_u = false, own_du = false, own_u = false;
+  size_t u_off = 0, du_off = 0, u64_off = 0, du64_off = 0, gemm_off = 0, total = 0;
+};
+
+sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
+  SRA_TRY(check_sparse(P, "P"));
+  if (P->format == SRA_FMT_ELL) return fail(SRA_ERR_INVALID_ARG, "backward takes the double-pruned N:M weight or the CSR transpose, not ELL");
+  if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
+  if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
+  if (flags & ~15u) return fail(SRA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (P->format == SRA_FMT_NM && P->dtype == SRA_BF16 && (flags & SRA_GRAD_DX) && P->cols == 0)
+    return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 dX needs N > 0");
+  return SRA_OK;
+}
+
+size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool have_u,
+                 bool have_du, BwdPlan* plan) {
+  BwdPlan p;
+  const int64_t K = P->rows, N = P->cols;
+  const bool dx = flags & SRA_GRAD_DX, da = flags & SRA_GRAD_DA, db = flags & SRA_GRAD_DB;
+  const bool dx_ad = dx && !(flags & SRA_DX_NO_ADAPTER);
+  p.need_du = r > 0 && (dx_ad || da || have_du);
+  p.need_u = r > 0 && db;
+  Arena a;
+  if (P->dtype == SRA_F32) {  // fp32: U and dU stay fp64; U is always recomputed
+    if (p.need_u) p.u64_off = a.take((size_t)T * r * 8);
+    if (p.need_du) p.du64_off = a.take((size_t)T * r * 8);
+    p.total = a.used;
+    if (plan) *plan = p;
+    return p.total;
+  }
+  p.own_du = p.need_du && !have_du;
+  p.own_u = p.need_u && !have_u;
+  if (p.own_u) p.u_off = a.take((size_t)T * r * 4);
+  if (p.own_du) p.du_off = a.take((size_t)T * r * 4);
+  if (P->dtype == SRA_BF16 && r > 0) {
+    size_t g = 0;
+    if (p.own_u) g = std::max(g, sra::adapter_gemm_ws(T, r, K));
+    if (p.need_du) g = std::max(g, sra::adapter_gemm_ws(T, r, N));
+    if (db) g = std::max(g, sra::adapter_gemm_ws(N, r, T));
+    if (da) g = std::max(g, sra::adapter_gemm_ws(r, K, T));
+    p.gemm_off = a.take(g);
+  }
+  p.total = a.used;
+  if (plan) *plan = p;
+  return p.total;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sra_abi_version(void) { return SRA_ABI_VERSION; }
+
+const char* sra_last_error(void) { return g_err.c_str(); }
+
+int64_t sra_nm_meta_words(int64_t cols, int32_t n, int32_t m) {
+  if (m <= 0 || n <= 0 || cols < 0) return 0;
+  const int64_t fields = cols / m * n;
+  return (fields + 15) / 16;
+}
+
+sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
+                        int32_t m, sra_sparse* out, void* stream) {
+  SRA_TRY(check_dtype(dtype));
+  SRA_TRY(check_nm(rows, cols, n, m));
+  if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
+  const bool any = rows > 0 && cols > 0;
+  SRA_TRY(check_ptr(W, any, "W"));
+  SRA_TRY(check_ptr(out->values, any, "out->values"));
+  SRA_TRY(check_ptr(out->meta, any, "out->meta"));
+  out->format = SRA_FMT_NM;
+  out->dtype = dtype;
+  out->rows = rows;
+  out->cols = cols;
+  out->n = n;
+  out->m = m;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_compress24(dtype, W, rows, cols, out->values, out->meta, s), s, "compress");
+}
+
+sra_status sra_double_prune(const sra_sparse* Ws, sra_sparse* P, void* stream) {
+  SRA_TRY(check_sparse(Ws, "Ws"));
+  if (Ws->format != SRA_FMT_NM) return fail(SRA_ERR_INVALID_ARG, "double_prune needs an N:M weight");
+  SRA_TRY(check_nm(Ws->cols, Ws->rows, Ws->n, Ws->m));  // the second prune groups along rows
+  if (!P) return fail(SRA_ERR_INVALID_ARG, "P descriptor is NULL");
+  const bool any = Ws->rows > 0 && Ws->cols > 0;
+  SRA_TRY(check_ptr(P->values, any, "P->values"));
+  SRA_TRY(check_ptr(P->meta, any, "P->meta"));
+  P->format = SRA_FMT_NM;
+  P->dtype = Ws->dtype;
+  P->rows = Ws->cols;
+  P->cols = Ws->rows;
+  P->n = Ws->n;
+  P->m = Ws->m;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_double_prune24(Ws->dtype, Ws->values, Ws->meta, Ws->rows, Ws->cols,
+                                             P->values, P->meta, s),
+                  s, "double_prune");
+}
+
+sra_status sra_compress_ffi(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t k,
+                            sra_sparse* out, void* stream) {
+  SRA_TRY(check_dtype(dtype));
+  if (rows < 0 || cols < 1 || cols > 32767) return fail(SRA_ERR_INVALID_ARG, "need rows >= 0 and 1 <= cols <= 32767");
+  if (k < 1 || k > cols) return fail(SRA_ERR_INVALID_ARG, "need 1 <= k <= cols (k = %d)", k);
+  if (rows > UINT32_MAX / 2) return fail(SRA_ERR_UNSUPPORTED, "too many rows");
+  if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
+  SRA_TRY(check_ptr(W, rows > 0, "W"));
+  SRA_TRY(check_ptr(out->values, rows > 0, "out->values"));
+  SRA_TRY(check_ptr(out->index, rows > 0, "out->index"));
+  out->format = SRA_FMT_ELL;
+  out->dtype = dtype;
+  out->rows = rows;
+  out->cols = cols;
+  out->k = k;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_compress_ffi(dtype, W, rows, cols, k, out->values, out->index, s), s,
+                  "compress_ffi");
+}
+
+sra_status sra_ffi_transpose_workspace(int64_t rows, int64_t cols, int32_t k, size_t* bytes) {
+  if (!bytes) return fail(SRA_ERR_INVALID_ARG, "bytes is NULL");
+  if (rows < 0 || cols < 1 || cols > 32767 || k < 1 || k > cols) return fail(SRA_ERR_INVALID_ARG, "bad ELL shape");
+  *bytes = sra::ffi_transpose_ws(rows, cols);
+  return SRA_OK;
+}
+
+sra_status sra_ffi_transpose(const sra_sparse* Ws, sra_sparse* WsT, void* ws, size_t ws_bytes,
+                             void* stream) {
+  SRA_TRY(check_sparse(Ws, "Ws"));
+  if (Ws->format != SRA_FMT_ELL) return fail(SRA_ERR_INVALID_ARG, "ffi_transpose needs an ELL weight");
+  if (!WsT) return fail(SRA_ERR_INVALID_ARG, "WsT descriptor is NULL");
+  const int64_t nnz = Ws->rows * Ws->k;
+  if (Ws->rows > 32767) return fail(SRA_ERR_INVALID_ARG, "transpose column ids are int16: rows must be <= 32767");
+  SRA_TRY(check_ptr(WsT->row_ptr, true, "WsT->row_ptr"));
+  SRA_TRY(check_ptr(WsT->index, nnz > 0, "WsT->index"));
+  SRA_TRY(check_ptr(WsT->values, nnz > 0, "WsT->values"));
+  const size_t need = sra::ffi_transpose_ws(Ws->rows, Ws->cols);
+  if (!ws || ws_bytes < need) return fail(SRA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!al16(ws)) return fail(SRA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  WsT->format = SRA_FMT_CSR;
+  WsT->dtype = Ws->dtype;
+  WsT->rows = Ws->cols;
+  WsT->cols = Ws->rows;
+  WsT->nnz = nnz;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_ffi_transpose(Ws->dtype, Ws->values, Ws->index, Ws->rows, Ws->cols,
+                                            Ws->k, WsT->row_ptr, WsT->index, WsT->values, ws, s),
+                  s, "ffi_transpose");
+}
+
+sra_status sra_fwd_workspace(const sra_sparse* Ws, int64_t T, int32_t r, size_t* bytes) {
+  SRA_TRY(validate_fwd(Ws, T, r));
+  if (!bytes) return fail(SRA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = fwd_bytes(Ws, T, r, /*own_u=*/true, nullptr);
+  return SRA_OK;
+}
+
+sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, const void* A,
+                               const void* B, int32_t r, void* Y, float* U_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  SRA_TRY(validate_fwd(Ws, T, r));
+  const int64_t N = Ws->rows, K = Ws->cols;
+  const bool any = T > 0;
+  SRA_TRY(check_ptr(X, any && K > 0, "X"));
+  SRA_TRY(check_ptr(Y, any && N > 0, "Y"));
+  SRA_TRY(check_ptr(A, any && r > 0 && K > 0, "A"));
+  SRA_TRY(check_ptr(B, any && r > 0 && N > 0, "B"));
+  if (U_out) SRA_TRY(check_ptr(U_out, true, "U_out"));
+  FwdPlan plan;
+  fwd_bytes(Ws, T, r, U_out == nullptr, &plan);
+  if (plan.total > 0 && (!ws || ws_bytes < plan.total))
+    return fail(SRA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", plan.total, ws_bytes);
+  if (plan.total > 0 && !al16(ws)) return fail(SRA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (T == 0) return SRA_OK;
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* wsb = (uint8_t*)ws;
+  float* U = r > 0 ? (U_out ? U_out : (float*)(wsb + plan.u_off)) : nullptr;
+
+  if (Ws->dtype == SRA_F32) {
+    double* U64 = r > 0 ? (double*)(wsb + plan.u64_off) : nullptr;
+    if (r > 0)
+      SRA_TRY(hip_done(sra::launch_f32_adapter_u((const float*)X, (const float*)A, T, K, r, U64,
+                                                 U_out, s), s, "fwd U"));
+    const sra::F32Sparse S = f32_view(Ws);
+    return hip_done(sra::launch_f32_spmm(S, (const float*)X, T, U64, (const float*)B, r, 1, r,
+                                         (float*)Y, s), s, "fwd spmm f32");
+  }
+  if (r > 0) {
+    const sra::Operand P{X, K, 1, false}, Q{A, K, 1, false};
+    SRA_TRY(hip_done(sra::launch_adapter_gemm(P, Q, T, r, K, U, wsb + plan.gemm_off, s), s, "fwd U"));
+  }
+  sra::Epilogue ep;
+  ep.U = U;
+  ep.E = (const uint16_t*)B;
+  ep.e_row_stride = r;
+  ep.e_j_stride = 1;
+  ep.r = r;
+  if (Ws->format == SRA_FMT_NM)
+    return hip_done(sra::launch_spmm24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
+                                            (const uint16_t*)X, T, ep, (uint16_t*)Y, s),
+                    s, "fwd spmm 2:4");
+  return hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_ELL, (const uint16_t*)Ws->values, Ws->index,
+                                            nullptr, Ws->k, N, K, (const uint16_t*)X, T, ep,
+                                            (uint16_t*)Y, s),
+                  s, "fwd spmm ffi");
+}
+
+sra_status sra_bwd_workspace(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, size_t* bytes) {
+  SRA_TRY(validate_bwd(P, T, r, flags));
+  if (!bytes) return fail(SRA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = bwd_bytes(P, T, r, flags, /*have_u=*/false, /*have_du=*/false, nullptr);
+  return SRA_OK;
+}
+
+sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* X, int64_t T,
+                               const float* U,
+                               const void* A, const void* B, int32_t r, uint32_t flags, void* dX,
+                               float* dA, float* dB, float* dU_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  SRA_TRY(validate_bwd(P, T, r, flags));
+  const int64_t K = P->rows, N = P->cols;
+  const bool fdx = flags & SRA_GRAD_DX, fda = (flags & SRA_GRAD_DA) && r > 0,
+             fdb = (flags & SRA_GRAD_DB) && r > 0;
+  const bool dx_ad = fdx && !(flags & SRA_DX_NO_ADAPTER) && r > 0;
+  BwdPlan plan;
+  bwd_bytes(P, T, r, flags, U != nullptr, dU_out != nullptr, &plan);
+  const bool any = T > 0;
+  SRA_TRY(check_ptr(dY, any && N > 0 && (fdx || plan.need_du || fdb), "dY"));
+  const bool recompute_u = plan.own_u || (P->dtype == SRA_F32 && plan.need_u);
+  SRA_TRY(check_ptr(X, any && K > 0 && (fda || recompute_u), "X"));
+  SRA_TRY(check_ptr(A, any && r > 0 && K > 0 && (dx_ad || recompute_u), "A"));
+  SRA_TRY(check_ptr(B, any && r > 0 && N > 0 && plan.need_du, "B"));
+  SRA_TRY(check_ptr(dX, fdx && any && K > 0, "dX"));
+  SRA_TRY(check_ptr(dA, fda && K > 0, "dA"));
+  SRA_TRY(check_ptr(dB, fdb && N > 0, "dB"));
+  if (U) SRA_TRY(check_ptr(U, true, "U"));
+  if (dU_out) SRA_TRY(check_ptr(dU_out, true, "dU_out"));
+  if (plan.total > 0 && (!ws || ws_bytes < plan.total))
+    return fail(SRA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", plan.total, ws_bytes);
+  if (plan.total > 0 && !al16(ws)) return fail(SRA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    if (fda) SRA_TRY(hip_done(sra::launch_fill_f32(dA, (int64_t)r * K, 0.f, s), s, "zero dA"));
+    if (fdb) SRA_TRY(hip_done(sra::launch_fill_f32(dB, N * (int64_t)r, 0.f, s), s, "zero dB"));
+    return SRA_OK;
+  }
+  uint8_t* wsb = (uint8_t*)ws;
+  const float* Uv = plan.need_u ? (plan.own_u ? (const float*)(wsb + plan.u_off) : U) : nullptr;
+  float* dU = plan.need_du ? (plan.own_du ? (float*)(wsb + plan.du_off) : dU_out) : nullptr;
+  void* gws = wsb ? wsb + plan.gemm_off : nullptr;
+
+  if (P->dtype == SRA_F32) {
+    double* U64 = plan.need_u ? (double*)(wsb + plan.u64_off) : nullptr;
+    double* dU64 = plan.need_du ? (double*)(wsb + plan.du64_off) : nullptr;
+    if (plan.need_u)
+      SRA_TRY(hip_done(sra::launch_f32_adapter_u((const float*)X, (const float*)A, T, K, r, U64,
+                                                 nullptr, s), s, "bwd U"));
+    if (plan.need_du)
+      SRA_TRY(hip_done(sra::launch_f32_du((const float*)dY, (const float*)B, T, N, r, dU64, dU_out, s),
+                       s, "bwd dU"));
+    if (fdx)
+      SRA_TRY(hip_done(sra::launch_f32_spmm(f32_view(P), (const float*)dY, T, dU64, (const float*)A,
+                                            1, K, dx_ad ? r : 0, (float*)dX, s), s, "bwd dX f32"));
+    if (fdb)
+      SRA_TRY(hip_done(sra::launch_f32_tn((const float*)dY, nullptr, N, nullptr, U64, r, T, N, r,
+                                          dB, s), s, "bwd dB"));
+    if (fda)
+      SRA_TRY(hip_done(sra::launch_f32_tn(nullptr, dU64, r, (const float*)X, nullptr, K, T, r, K,
+                                          dA, s), s, "bwd dA"));
+    return SRA_OK;
+  }
+  if (plan.own_u) {
+    const sra::Operand Pp{X, K, 1, false}, Qq{A, K, 1, false};
+    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, T, r, K, (float*)Uv, gws, s), s, "bwd U"));
+  }
+  if (plan.need_du) {
+    const sra::Operand Pp{dY, N, 1, false}, Qq{B, 1, r, false};
+    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, T, r, N, dU, gws, s), s, "bwd dU"));
+  }
+  if (fdx) {
+    sra::Epilogue ep;
+    ep.U = dU;
+    ep.E = (const uint16_t*)A;
+    ep.e_row_stride = 1;
+    ep.e_j_stride = K;
+    ep.r = dx_ad ? r : 0;
+    if (P->format == SRA_FMT_NM)
+      SRA_TRY(hip_done(sra::launch_spmm24_bf16((const uint16_t*)P->values, P->meta, K, N,
+                                               (const uint16_t*)dY, T, ep, (uint16_t*)dX, s),
+                       s, "bwd dX 2:4"));
+    else
+      SRA_TRY(hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_CSR, (const uint16_t*)P->values, P->index,
+                                                 P->row_ptr, 0, K, N, (const uint16_t*)dY, T, ep,
+                                                 (uint16_t*)dX, s),
+                       s, "bwd dX ffi"));
+  }
+  if (fdb) {
+    const sra::Operand Pp{dY, 1, N, false}, Qq{Uv, 1, r, true};
+    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, N, r, T, dB, gws, s), s, "bwd dB"));
+  }
+  if (fda) {
+    const sra::Operand Pp{dU, 1, r, true}, Qq{X, 1, K, false};
+    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, r, K, T, dA, gws, s), s, "bwd dA"));
+  }
+  return SRA_OK;
+}
+
+}  // extern "C"

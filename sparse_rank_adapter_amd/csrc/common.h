@@ -1,0 +1,125 @@
+// Internal helpers shared by the HIP sources of libsra (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sra.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SRA_DEV __device__ __forceinline__
+
+// ---- bf16 bit helpers (values travel as raw uint16_t; arithmetic is fp32 or wider)
+SRA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+// round-to-nearest-even fp32 -> bf16 (inputs are finite)
+SRA_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+SRA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Magnitude key: the value's bits with the sign cleared, compared as an unsigned integer.
+// For finite IEEE values this orders by |w| exactly, with +0 == -0.
+SRA_DEV uint32_t mag_key(uint16_t b) { return (uint32_t)(b & 0x7FFFu); }
+SRA_DEV uint32_t mag_key(uint32_t b) { return b & 0x7FFFFFFFu; }
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> { static SRA_DEV double to_f64(uint16_t b) { return (double)bf16_to_f32(b); } };
+template <> struct Elem<uint32_t> { static SRA_DEV double to_f64(uint32_t b) { return (double)__uint_as_float(b); } };
+
+SRA_DEV double load_f64(const uint16_t* p, int64_t i) { return (double)bf16_to_f32(p[i]); }
+SRA_DEV double load_f64(const uint32_t* p, int64_t i) { return (double)__uint_as_float(p[i]); }
+
+// Split an fp32 value into bf16 hi + lo with x ~= hi + lo (|x - hi - lo| <= 2^-17 |x|).
+SRA_DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+// Three-way split x ~= hi + mid + lo (|x - hi - mid - lo| <= 2^-26 |x|, below fp32 rounding);
+// each difference is exact in fp32.
+SRA_DEV void split3_bf16(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  const float r1 = x - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+}
+
+// ---- host-side launchers implemented in the kernel sources (internal C++ linkage)
+namespace sra {
+
+hipError_t launch_compress24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
+                             uint32_t* meta, hipStream_t s);
+hipError_t launch_double_prune24(int dtype, const void* vals, const uint32_t* meta, int64_t rows,
+                                 int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s);
+hipError_t launch_compress_ffi(int dtype, const void* W, int64_t rows, int64_t cols, int k,
+                               void* vals, int16_t* idx, hipStream_t s);
+size_t ffi_transpose_ws(int64_t rows, int64_t cols);
+hipError_t launch_ffi_transpose(int dtype, const void* vals, const int16_t* idx, int64_t rows,
+                                int64_t cols, int k, int32_t* row_ptr, int16_t* t_idx, void* t_vals,
+                                void* ws, hipStream_t s);
+
+// fp32 path (fp64 accumulation)
+struct F32Sparse {  // a row-iterable sparse matrix: rows x cols, reduced over cols
+  int format;
+  int64_t rows, cols;
+  const uint32_t* vals;   // fp32 bits
+  const uint32_t* meta;   // NM 2:4
+  int64_t meta_stride;    // words per row
+  const int16_t* idx;     // ELL / CSR
+  const int32_t* row_ptr; // CSR
+  int k;                  // ELL
+};
+hipError_t launch_f32_adapter_u(const float* X, const float* A, int64_t T, int64_t K, int r,
+                                double* U64, float* U32, hipStream_t s);
+hipError_t launch_f32_spmm(const F32Sparse& S, const float* Act, int64_t T, const double* U64,
+                           const float* E, int64_t e_row_stride, int64_t e_j_stride, int r,
+                           float* Out, hipStream_t s);
+hipError_t launch_f32_du(const float* dY, const float* B, int64_t T, int64_t N, int r,
+                         double* dU64, float* dU32, hipStream_t s);
+hipError_t launch_f32_tn(const float* Pf, const double* Pd, int64_t ldp, const float* Qf,
+                         const double* Qd, int64_t ldq, int64_t T, int64_t M, int64_t Nn,
+                         float* Out, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+// bf16 2:4 SpMM with fused low-rank epilogue:
+//   Out[t][row] = sum_c Act[t][c] * S[row][c] + sum_j U[t][j] * E(row, j)
+struct Epilogue {
+  const float* U = nullptr;     // [T][r] fp32
+  const uint16_t* E = nullptr;  // bf16, element (row, j) at E[row*e_row_stride + j*e_j_stride]
+  int64_t e_row_stride = 0, e_j_stride = 0;
+  int r = 0;
+};
+hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+                              const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
+                              hipStream_t s);
+size_t spmm24_decode_ws(int64_t R, int64_t C, int64_t T);
+hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
+                                int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
+                                uint16_t* out, hipStream_t s);
+// fixed fan-in bf16 SpMM (ELL forward / CSR backward) with the same epilogue
+hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t* idx,
+                                const int32_t* row_ptr, int k, int64_t R, int64_t C,
+                                const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
+                                hipStream_t s);
+
+// Skinny adapter products, fp32 result:  Out[m][n] = sum_c P(m,c) Q(n,c)
+// element (m,c) of P at P[m*sPm + c*sPc]; `p_f32` selects fp32 storage (else bf16 bits).
+struct Operand {
+  const void* ptr;
+  int64_t s_row, s_red;  // strides of the non-reduced index and of the reduction index
+  bool f32;
+};
+size_t adapter_gemm_ws(int64_t M, int64_t Nn, int64_t C);
+hipError_t launch_adapter_gemm(const Operand& P, const Operand& Q, int64_t M, int64_t Nn, int64_t C,
+                               float* out, void* ws, hipStream_t s);
+
+}  // namespace sra

@@ -1,0 +1,163 @@
+"""Host-side tests of libsra's C ABI (no GPU needed, no kernel is launched).
+
+Every call below fails validation, or is a pure host query, so it returns before any HIP call.
+Pointers handed to the library are fake (aligned integers); they are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_rank_adapter_amd import _abi
+from sparse_rank_adapter_amd._abi import (SRA_BF16, SRA_ERR_INVALID_ARG, SRA_ERR_UNSUPPORTED,
+                                          SRA_ERR_WORKSPACE, SRA_F32, SRA_FMT_CSR, SRA_FMT_ELL,
+                                          SRA_FMT_NM, SRA_OK, SraSparse)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.fail("libsra.so is not built (run __graft_entry__.build())")
+    return _abi.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "sra.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sra_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert sorted(_abi.EXPORTS) == declared
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_sizes(lib):
+    assert lib.sra_abi_version() == 1
+    assert lib.sra_nm_meta_words(64, 2, 4) == 2
+    assert lib.sra_nm_meta_words(4096, 2, 4) == 128
+    assert lib.sra_nm_meta_words(96, 2, 4) == 3
+    assert lib.sra_nm_meta_words(16, 2, 4) == 1   # 8 fields, one partly filled word
+
+
+def nm_desc(rows=64, cols=128, dtype=SRA_BF16, n=2, m=4):
+    d = SraSparse()
+    d.format, d.dtype, d.rows, d.cols, d.n, d.m = SRA_FMT_NM, dtype, rows, cols, n, m
+    d.values, d.meta = FAKE, FAKE
+    return d
+
+
+def ell_desc(rows=64, cols=128, k=8, dtype=SRA_BF16):
+    d = SraSparse()
+    d.format, d.dtype, d.rows, d.cols, d.k = SRA_FMT_ELL, dtype, rows, cols, k
+    d.values, d.index = FAKE, FAKE
+    return d
+
+
+def err(lib):
+    return lib.sra_last_error().decode()
+
+
+@pytest.mark.parametrize("n,m,code", [(1, 4, SRA_ERR_UNSUPPORTED), (2, 8, SRA_ERR_INVALID_ARG),
+                                      (3, 2, SRA_ERR_INVALID_ARG), (0, 4, SRA_ERR_INVALID_ARG)])
+def test_compress_rejects_patterns(lib, n, m, code):
+    d = SraSparse()
+    d.values, d.meta = FAKE, FAKE
+    assert lib.sra_compress(FAKE, SRA_BF16, 4, 64, n, m, ctypes.byref(d), None) == code
+    assert err(lib)
+
+
+def test_compress_validation(lib):
+    d = SraSparse()
+    d.values, d.meta = FAKE, FAKE
+    assert lib.sra_compress(FAKE, 7, 4, 64, 2, 4, ctypes.byref(d), None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_compress(FAKE, SRA_BF16, 4, 48, 2, 4, ctypes.byref(d), None) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_compress(None, SRA_BF16, 4, 64, 2, 4, ctypes.byref(d), None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_compress(FAKE + 2, SRA_BF16, 4, 64, 2, 4, ctypes.byref(d), None) == SRA_ERR_INVALID_ARG
+    assert "aligned" in err(lib)
+    assert lib.sra_compress(FAKE, SRA_BF16, -1, 64, 2, 4, ctypes.byref(d), None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_compress(FAKE, SRA_BF16, 4, 64, 2, 4, None, None) == SRA_ERR_INVALID_ARG
+
+
+def test_double_prune_validation(lib):
+    P = SraSparse()
+    P.values, P.meta = FAKE, FAKE
+    bad = nm_desc(rows=36)               # second prune groups along rows: 36 % 32 != 0
+    assert lib.sra_double_prune(ctypes.byref(bad), ctypes.byref(P), None) == SRA_ERR_UNSUPPORTED
+    e = ell_desc()
+    assert lib.sra_double_prune(ctypes.byref(e), ctypes.byref(P), None) == SRA_ERR_INVALID_ARG
+    ok = nm_desc()
+    assert lib.sra_double_prune(ctypes.byref(ok), None, None) == SRA_ERR_INVALID_ARG
+
+
+def test_ffi_validation(lib):
+    d = SraSparse()
+    d.values, d.index = FAKE, FAKE
+    assert lib.sra_compress_ffi(FAKE, SRA_BF16, 4, 64, 0, ctypes.byref(d), None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_compress_ffi(FAKE, SRA_BF16, 4, 64, 65, ctypes.byref(d), None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_compress_ffi(FAKE, SRA_BF16, 4, 40000, 8, ctypes.byref(d), None) == SRA_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert lib.sra_ffi_transpose_workspace(4096, 4096, 410, ctypes.byref(n)) == SRA_OK
+    assert n.value >= 64 * 4096 * 4
+    T_ = SraSparse()
+    T_.row_ptr, T_.index, T_.values = FAKE, FAKE, FAKE
+    e = ell_desc()
+    assert lib.sra_ffi_transpose(ctypes.byref(e), ctypes.byref(T_), FAKE, 16, None) == SRA_ERR_WORKSPACE
+    assert lib.sra_ffi_transpose(ctypes.byref(e), ctypes.byref(T_), None, 1 << 30, None) == SRA_ERR_WORKSPACE
+
+
+def test_fwd_validation_and_workspace(lib):
+    d = nm_desc(rows=4096, cols=1024)
+    n = ctypes.c_size_t()
+    assert lib.sra_fwd_workspace(ctypes.byref(d), 2048, 16, ctypes.byref(n)) == SRA_OK
+    assert n.value >= 2048 * 16 * 4          # room for U when the caller does not keep it
+    assert lib.sra_fwd_workspace(ctypes.byref(d), 2048, 257, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_fwd_workspace(ctypes.byref(d), -1, 16, ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    d48 = nm_desc(rows=64, cols=48)           # 2:4 needs K % 32 == 0
+    assert lib.sra_fwd_workspace(ctypes.byref(d48), 8, 4, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    f32 = nm_desc(rows=64, cols=96, dtype=SRA_F32)
+    assert lib.sra_fwd_workspace(ctypes.byref(f32), 8, 4, ctypes.byref(n)) == SRA_OK
+    csr = SraSparse()
+    csr.format, csr.dtype, csr.rows, csr.cols = SRA_FMT_CSR, SRA_BF16, 8, 8
+    assert lib.sra_fwd_workspace(ctypes.byref(csr), 8, 4, ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    # workspace too small / missing
+    big = ctypes.c_size_t()
+    lib.sra_fwd_workspace(ctypes.byref(d), 2048, 16, ctypes.byref(big))
+    st = lib.sra_sparse_lora_fwd(ctypes.byref(d), FAKE, 2048, FAKE, FAKE, 16, FAKE, None, FAKE, 16, None)
+    assert st == SRA_ERR_WORKSPACE
+    st = lib.sra_sparse_lora_fwd(ctypes.byref(d), None, 2048, FAKE, FAKE, 16, FAKE, None, FAKE, big.value, None)
+    assert st == SRA_ERR_INVALID_ARG and "X" in err(lib)
+    st = lib.sra_sparse_lora_fwd(ctypes.byref(d), FAKE, 2048, None, FAKE, 16, FAKE, None, FAKE, big.value, None)
+    assert st == SRA_ERR_INVALID_ARG and "A" in err(lib)
+
+
+def test_bwd_validation(lib):
+    P = nm_desc(rows=1024, cols=4096)
+    n = ctypes.c_size_t()
+    assert lib.sra_bwd_workspace(ctypes.byref(P), 2048, 16, 7, ctypes.byref(n)) == SRA_OK
+    assert lib.sra_bwd_workspace(ctypes.byref(P), 2048, 16, 16, ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    e = ell_desc()
+    assert lib.sra_bwd_workspace(ctypes.byref(e), 8, 4, 7, ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    lib.sra_bwd_workspace(ctypes.byref(P), 2048, 16, 7, ctypes.byref(n))
+    st = lib.sra_sparse_lora_bwd(ctypes.byref(P), FAKE, FAKE, 2048, FAKE, FAKE, FAKE, 16, 7,
+                                 None, FAKE, FAKE, None, FAKE, n.value, None)
+    assert st == SRA_ERR_INVALID_ARG and "dX" in err(lib)
+    st = lib.sra_sparse_lora_bwd(ctypes.byref(P), FAKE, FAKE, 2048, FAKE, FAKE, FAKE, 16, 7,
+                                 FAKE, FAKE, FAKE, None, None, 0, None)
+    assert st == SRA_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_when_library_missing(tmp_path):
+    saved = _abi._lib
+    _abi._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            _abi.load(str(tmp_path / "libsra.so"))
+    finally:
+        _abi._lib = saved

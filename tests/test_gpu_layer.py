@@ -1,0 +1,210 @@
+"""GPU parity of the layer calls (sparse_lora_fwd / sparse_lora_bwd) against the oracle.
+
+Floats: max |gpu - oracle| / (|oracle| + 1e-3) <= 2e-2 for bf16 and <= 1e-5 for fp32.  Full-size
+workloads compare sampled token rows / output columns that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_rank_adapter_amd as sra
+from oracle import ffi as offi
+from oracle import layer as olayer
+from oracle import nm as onm
+from sra_inputs import WORKLOADS, Workload, layer_inputs
+from tests._util import Report, bits, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def nm_oracle_weights(W64, k_groups=None):
+    """(Ws, Wdp) dense float64 from the oracle; optionally only for some 4-column groups of K."""
+    if k_groups is not None:
+        cols = (k_groups[:, None] * 4 + np.arange(4)[None, :]).ravel()
+        W64 = W64[:, cols]
+    v, m, mask1 = onm.compress(W64, 2, 4)
+    Ws = np.where(mask1, W64, 0.0)
+    _, _, _, Wdp = onm.double_prune(v, m, 2, 4, W64.shape[1])
+    return Ws, Wdp
+
+
+def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, r=None,
+           check_bwd=True, flags_adapter=True):
+    """Runs fwd + bwd on the GPU and compares (optionally on sampled token rows, output columns
+    of Y / dB and 4-column groups of K for dX / dA)."""
+    inp = layer_inputs(wl, seed=seed, T=T)
+    dtype = inp["X"].dtype
+    if r is not None and r != wl.r:
+        inp["A"], inp["B"] = inp["A"][:r].contiguous(), inp["B"][:, :r].contiguous()
+    rr = inp["A"].shape[0]
+    X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
+    S = sra.compress(W)
+    Y, U = sra.sparse_lora_fwd(S, X, A if rr else None, B if rr else None)
+    g = {}
+    if check_bwd:
+        P = sra.double_prune(S)
+        g = sra.sparse_lora_bwd(P, dY, X, U, A if rr else None, B if rr else None,
+                                dx_adapter=flags_adapter, want_du=True)
+    torch.cuda.synchronize()
+
+    X64, A64, B64, dY64 = (f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    Tn = X64.shape[0]
+    rows = np.arange(Tn) if rows is None else rows
+    cols_n = np.arange(wl.N) if cols_n is None else cols_n
+    # forward: Y[rows][:, cols_n] needs Ws rows cols_n (mask1 is local to each row)
+    Ws_n, _ = nm_oracle_weights(f64(inp["W"][torch.from_numpy(cols_n)]))
+    Yo, Uo = olayer.forward(X64[rows], Ws_n, A64, B64[cols_n])
+    rep = Report(dtype)
+    rep.add("Y", f64(Y[rows][:, cols_n]), Yo)
+    if rr:
+        rep.add("U", U[rows].cpu().numpy(), Uo)
+    if not check_bwd:
+        rep.check()
+        return
+    # backward, each output on a restricted problem the oracle solves independently:
+    #   dX[rows][:, kcols], dU[rows]  -- token rows and K columns (Wdp columns are local to their
+    #                                    4-column groups of K, the second prune to its column)
+    #   dB[cols_n]                    -- output columns
+    #   dA[:, kcols]                  -- K columns
+    if k_groups is None:
+        k_groups = np.arange(wl.K // 4)
+    kcols = (k_groups[:, None] * 4 + np.arange(4)[None, :]).ravel()
+    _, Wdp_k = nm_oracle_weights(f64(inp["W"]), k_groups)
+    gx = olayer.backward(dY64[rows], X64[rows][:, kcols], Wdp_k, A64[:, kcols], B64,
+                         dx_adapter=flags_adapter, want=("dX", "dU"))
+    rep.add("dX", f64(g["dX"][rows][:, kcols]), gx["dX"])
+    if rr:
+        rep.add("dU", g["dU"][rows].cpu().numpy(), gx["dU"])
+        gb = olayer.backward(dY64[:, cols_n], X64, None, A64, B64[cols_n], want=("dB",))
+        rep.add("dB", g["dB"][cols_n].cpu().numpy(), gb["dB"])
+        ga = olayer.backward(dY64, X64[:, kcols], None, A64[:, kcols], B64, want=("dA",))
+        rep.add("dA", g["dA"][:, kcols].cpu().numpy(), ga["dA"])
+    rep.check()
+
+
+def test_tiny_f32_fwd_bwd(gpu):
+    """The tiny fp32 check: X 8x64, W 32x64 pruned 2:4, rank 4, seed 0; tolerance 1e-5."""
+    wl = WORKLOADS["tiny_f32"]
+    run_nm(wl)
+
+
+@pytest.mark.parametrize("T,K,N,r", [(1, 64, 32, 4), (5, 64, 96, 16), (130, 192, 160, 20),
+                                     (257, 128, 64, 0), (64, 256, 256, 32), (300, 64, 32, 8)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes(gpu, T, K, N, r, dtype):
+    wl = Workload("ragged", T=T, K=K, N=N, r=r, dtype=dtype, fmt="nm")
+    run_nm(wl, seed=T + K)
+
+
+def test_no_adapter_flag(gpu):
+    wl = Workload("noad", T=96, K=128, N=64, r=8, dtype="bf16", fmt="nm")
+    run_nm(wl, seed=5, flags_adapter=False)
+
+
+def test_opt350m_fc1_full(gpu):
+    run_nm(WORKLOADS["opt350m_fc1"])
+
+
+@pytest.mark.parametrize("name", ["opt13b_fc1", "opt13b_fc2"])
+def test_opt13b_sampled(gpu, name):
+    wl = WORKLOADS[name]
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 62, replace=False)]))
+    cols_n = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 254, replace=False)]))
+    k_groups = np.unique(np.concatenate([[0, wl.K // 4 - 1], rng.choice(wl.K // 4, 30, replace=False)]))
+    run_nm(wl, rows=rows, cols_n=cols_n, k_groups=k_groups)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_opt66b_decode_sampled(gpu, T):
+    wl = WORKLOADS["opt66b_ffn_decode"]
+    rng = np.random.default_rng(T)
+    cols_n = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 510, replace=False)]))
+    run_nm(wl, T=T, cols_n=cols_n, check_bwd=False)
+
+
+def test_deterministic_and_t0(gpu):
+    wl = Workload("det", T=200, K=256, N=128, r=16, dtype="bf16", fmt="nm")
+    inp = layer_inputs(wl, seed=9)
+    X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
+    S = sra.compress(W)
+    P = sra.double_prune(S)
+    outs = []
+    for _ in range(2):
+        Y, U = sra.sparse_lora_fwd(S, X, A, B)
+        g = sra.sparse_lora_bwd(P, dY, X, U, A, B, want_du=True)
+        outs.append([Y.clone(), U.clone()] + [g[k].clone() for k in ("dX", "dA", "dB", "dU")])
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+    # T = 0: forward is a no-op, the backward writes zero adapter gradients
+    X0, dY0 = X[:0], dY[:0]
+    Y0, _ = sra.sparse_lora_fwd(S, X0, A, B)
+    g0 = sra.sparse_lora_bwd(P, dY0, X0, None, A, B, out={"dA": torch.full_like(A, 7, dtype=torch.float32),
+                                                          "dB": torch.full_like(B, 7, dtype=torch.float32)})
+    torch.cuda.synchronize()
+    assert Y0.shape == (0, wl.N) and g0["dX"].shape == (0, wl.K)
+    assert torch.count_nonzero(g0["dA"]) == 0 and torch.count_nonzero(g0["dB"]) == 0
+
+
+def test_u_recomputed_when_not_given(gpu):
+    wl = Workload("rec", T=70, K=128, N=96, r=12, dtype="bf16", fmt="nm")
+    inp = layer_inputs(wl, seed=11)
+    X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
+    S = sra.compress(W)
+    P = sra.double_prune(S)
+    _, U = sra.sparse_lora_fwd(S, X, A, B)
+    g1 = sra.sparse_lora_bwd(P, dY, X, U, A, B)
+    g2 = sra.sparse_lora_bwd(P, dY, X, None, A, B)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(g1["dX"]), bits(g2["dX"]))
+    assert torch.equal(g1["dB"], g2["dB"]) and torch.equal(g1["dA"], g2["dA"])
+
+
+# ----------------------------------------------------------------------------- fixed fan-in
+
+def run_ffi(wl: Workload, T=None, seed=0, rows=None, cols_n=None, kcols=None):
+    inp = layer_inputs(wl, seed=seed, T=T)
+    dtype = inp["X"].dtype
+    X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
+    rr = A.shape[0]
+    S = sra.compress_ffi(W, wl.ffi_k)
+    ST = sra.ffi_transpose(S)
+    Y, U = sra.sparse_lora_fwd(S, X, A if rr else None, B if rr else None)
+    g = sra.sparse_lora_bwd(ST, dY, X, U, A if rr else None, B if rr else None, want_du=True)
+    torch.cuda.synchronize()
+    X64, W64, A64, B64, dY64 = (f64(inp[k]) for k in ("X", "W", "A", "B", "dY"))
+    rows = np.arange(X64.shape[0]) if rows is None else rows
+    cols_n = np.arange(wl.N) if cols_n is None else cols_n
+    kcols = np.arange(wl.K) if kcols is None else kcols
+    vals, cols = offi.select(W64, wl.ffi_k)
+    Ws = offi.to_dense(vals, cols, wl.K)
+    Yo, _ = olayer.forward(X64[rows], Ws[cols_n], A64, B64[cols_n])
+    rep = Report(dtype)
+    rep.add("Y", f64(Y[rows][:, cols_n]), Yo)
+    gx = olayer.backward(dY64[rows], X64[rows][:, kcols], Ws[:, kcols], A64[:, kcols], B64,
+                         want=("dX", "dU"))
+    rep.add("dX", f64(g["dX"][rows][:, kcols]), gx["dX"])
+    if rr:
+        rep.add("dU", g["dU"][rows].cpu().numpy(), gx["dU"])
+        gb = olayer.backward(dY64[:, cols_n], X64, None, A64, B64[cols_n], want=("dB",))
+        rep.add("dB", g["dB"][cols_n].cpu().numpy(), gb["dB"])
+        ga = olayer.backward(dY64, X64[:, kcols], None, A64[:, kcols], B64, want=("dA",))
+        rep.add("dA", g["dA"][:, kcols].cpu().numpy(), ga["dA"])
+    rep.check()
+
+
+@pytest.mark.parametrize("T,K,N,k,r", [(3, 37, 5, 7, 2), (130, 300, 64, 17, 16), (64, 512, 200, 64, 0)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ffi_ragged(gpu, T, K, N, k, r, dtype):
+    wl = Workload("ffi_ragged", T=T, K=K, N=N, r=r, dtype=dtype, fmt="ffi", ffi_k=k)
+    run_ffi(wl, seed=k)
+
+
+def test_ffi90_sampled(gpu):
+    wl = WORKLOADS["ffi90_4096"]
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 126, replace=False)]))
+    cols = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 254, replace=False)]))
+    run_ffi(wl, rows=rows, cols_n=cols, kcols=cols)
