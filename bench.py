@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the structured-sparse plus low-rank linear layer on one MI355X.
+
+A step is one pass of the hot path over one batch of seeded synthetic input, on the OPT-350M fc1
+shape by default (X 2048 x 1024, W 4096 x 1024 pruned 2:4, rank-16 adapter, bf16 / fp32 accum):
+
+    compress(W) -> double_prune -> forward (U, Y) -> backward (dU, dX, dB, dA)
+
+Re-compressing every step mirrors SLoPe's training loop, which refreshes both compressed forms
+after each optimizer update (SLoPe paperlayer summary §2.3).  The step is captured once in a HIP
+graph and replayed.  Prints ONE JSON line with the throughput (dense-equivalent TFLOP/s), the
+speedup over the dense bf16 GEMMs of the same layer (hipBLASLt through torch, same protocol), the
+roofline of the dominant kernel (timed live with HIP events around that kernel alone) and the CPU
+oracle timed on a bounded sample as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload opt350m_fc1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse+LoRA linear dense-equiv TFLOP/s & GB/s; speedup vs dense bf16 GEMM"
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA (published); 2:4 work is priced as stored flops
+PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="opt350m_fc1",
+                    choices=["opt350m_fc1", "opt13b_fc1", "opt13b_fc2", "ffi90_4096", "opt66b_ffn_decode"])
+    ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
+    ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle sampling")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- work / bytes model
+
+def step_model(wl, T, with_bwd=True, with_compress=True):
+    """Dense-equivalent flops, algorithmic (stored) flops and algorithmic HBM bytes of one step."""
+    K, N, r, e = wl.K, wl.N, wl.r, 2
+    if wl.fmt == "ffi":
+        w_bytes = N * wl.ffi_k * (e + 2)             # ELL values + int16 columns
+        sparse_macs = T * N * wl.ffi_k
+    else:
+        w_bytes = N * K // 2 * e + N * K // 8        # stored values + 2-bit metadata
+        sparse_macs = T * N * K // 2
+    dense_eq = 2 * T * N * K + 2 * T * r * (K + N)  # forward
+    algo = 2 * sparse_macs + 2 * T * r * (K + N)
+    bytes_ = T * K * e + w_bytes + (r * K + N * r) * e + T * N * e + T * r * 4
+    if with_bwd:
+        dense_eq += 2 * T * N * K + 4 * T * r * (N + K)
+        algo += 2 * sparse_macs + 4 * T * r * (N + K)
+        bytes_ += T * N * e + T * K * e + w_bytes + T * r * 4 + (r * K + N * r) * e + T * K * e \
+            + (r * K + N * r) * 4
+    if with_compress and wl.fmt == "nm":
+        bytes_ += N * K * e + w_bytes                # compress: read W, write Ws
+        bytes_ += 2 * w_bytes                        # double prune: read Ws, write P
+    return dense_eq, algo, bytes_
+
+
+# ----------------------------------------------------------------------------- GPU timing helpers
+
+def time_graph(fn, steps, warmup, use_graph=True):
+    """Wall-clock ms per call of fn over `steps` calls (graph replays), sync on both sides."""
+    import torch
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        run = g.replay
+    else:
+        run = fn
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_kernel(which, call, reps):
+    """Average duration (ms) of one kernel class inside `call`, from HIP events placed around
+    that kernel alone by the library's profiling hook, on the stream it is launched on."""
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sra.time_next_kernel(which, e0, e1)
+        call()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in pairs)
+    return sum(ts) / len(ts)
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(wl, inp, budget_s, dense_eq_per_step):
+    """The oracle (float64, numpy) on the same step, repeated within a time budget."""
+    import numpy as np
+
+    from oracle import layer as olayer
+    from oracle import nm as onm
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the host's view
+        cores = os.cpu_count() or 1
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    X, W, A, B, dY = (f64(inp[k]) for k in ("X", "W", "A", "B", "dY"))
+    reps, t_total = 0, 0.0
+    while t_total < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        v, m, mask1 = onm.compress(W, 2, 4)
+        _, _, _, Wdp = onm.double_prune(v, m, 2, 4, wl.K)
+        Y, U = olayer.forward(X, np.where(mask1, W, 0.0), A, B)
+        olayer.backward(dY, X, Wdp, A, B, U)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps >= 50:
+            break
+    return {"value": round(dense_eq_per_step * reps / t_total / 1e12, 4), "unit": "TFLOP/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} full {wl.name} steps (compress + double_prune + fwd + bwd) in float64 "
+                      f"numpy, {t_total:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def bench_nm_layer(args, wl):
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    from sparse_rank_adapter_amd._abi import SRA_KERNEL_COMPRESS, SRA_KERNEL_DOUBLE_PRUNE, SRA_KERNEL_SPMM24
+    from sra_inputs import layer_inputs
+
+    dev = torch.device("cuda:0")
+    inp = layer_inputs(wl, seed=0)
+    X, W, A, B, dY = (inp[k].to(dev) for k in ("X", "W", "A", "B", "dY"))
+    T, r = wl.T, wl.r
+    S = sra.compress(W)
+    P = sra.double_prune(S)
+    Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
+    U = torch.empty((T, r), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(max(1, sra.fwd_workspace(S, T, r)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, sra.bwd_workspace(P, T, r)), dtype=torch.uint8, device=dev)
+    grads = {"dX": torch.empty((T, wl.K), dtype=X.dtype, device=dev),
+             "dA": torch.empty((r, wl.K), dtype=torch.float32, device=dev),
+             "dB": torch.empty((wl.N, r), dtype=torch.float32, device=dev)}
+
+    def fwd():
+        sra.sparse_lora_fwd(S, X, A, B, Y=Y, U=U, ws=ws_f)
+
+    def bwd():
+        sra.sparse_lora_bwd(P, dY, X, U, A, B, ws=ws_b, out=grads)
+
+    def step():
+        sra.compress(W, out=S)
+        sra.double_prune(S, out=P)
+        fwd()
+        bwd()
+
+    graph = not args.no_graph
+    ms = time_graph(step, args.steps, args.warmup, graph)
+    ms_fwd = time_graph(fwd, args.steps, args.warmup, graph)
+    ms_bwd = time_graph(bwd, args.steps, args.warmup, graph)
+    ms_cmp = time_graph(lambda: (sra.compress(W, out=S), sra.double_prune(S, out=P)), args.steps,
+                        args.warmup, graph)
+    # dense bf16 baseline: the same layer's forward and input-gradient GEMMs (hipBLASLt)
+    Wd = W.contiguous()
+    d_fwd = time_graph(lambda: torch.nn.functional.linear(X, Wd), args.steps, args.warmup, graph)
+    d_bwd = time_graph(lambda: torch.matmul(dY, Wd), args.steps, args.warmup, graph)
+
+    # per-kernel durations inside the real calls (eager, hook-armed)
+    reps = max(10, args.steps)
+    k_fwd = time_kernel(SRA_KERNEL_SPMM24, fwd, reps)
+    k_bwd = time_kernel(SRA_KERNEL_SPMM24, lambda: sra.sparse_lora_bwd(P, dY, X, U, A, B, ws=ws_b, out=grads), reps)
+    k_cmp = time_kernel(SRA_KERNEL_COMPRESS, lambda: sra.compress(W, out=S), reps)
+    k_dp = time_kernel(SRA_KERNEL_DOUBLE_PRUNE, lambda: sra.double_prune(S, out=P), reps)
+
+    dense_eq, algo, nbytes = step_model(wl, T)
+    # dominant kernel: the slower of the two SpMM launches; algorithmic flops per launch are the
+    # stored-half products plus the adapter epilogue (2 T N K/2 + 2 T r R)
+    spmm_flops_fwd = 2 * T * wl.N * (wl.K // 2) + 2 * T * r * wl.N
+    spmm_flops_bwd = 2 * T * wl.K * (wl.N // 2) + 2 * T * r * wl.K
+    if k_bwd >= k_fwd:
+        kname, kms, kflops = "k_spmm24 (backward dX = dY P^T + dU A)", k_bwd, spmm_flops_bwd
+    else:
+        kname, kms, kflops = "k_spmm24 (forward Y = X Ws^T + U B^T)", k_fwd, spmm_flops_fwd
+    achieved = kflops / (kms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(dense_eq / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "K": wl.K, "N": wl.N, "r": r, "sparsity": "2:4",
+                   "step": "compress + double_prune + fwd + bwd (dX, dA, dB)",
+                   "graph": graph, "seed": 0},
+        "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "speedup_vs_dense": round((d_fwd + d_bwd) / ms, 3),
+        "detail_ms": {"step": round(ms, 5), "fwd": round(ms_fwd, 5), "bwd": round(ms_bwd, 5),
+                      "compress+double_prune": round(ms_cmp, 5), "dense_fwd_gemm": round(d_fwd, 5),
+                      "dense_dx_gemm": round(d_bwd, 5)},
+        "speedup_fwd_vs_dense_fwd": round(d_fwd / ms_fwd, 3),
+        "speedup_bwd_vs_dense_dx": round(d_bwd / ms_bwd, 3),
+        "kernel_ms": {"spmm24_fwd": round(k_fwd, 5), "spmm24_bwd": round(k_bwd, 5),
+                      "compress": round(k_cmp, 5), "double_prune": round(k_dp, 5)},
+        "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4), "traffic": None},
+    }
+    return out, inp, dense_eq
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the layer on a single MI355X and has no "
+              "multi-GPU path (sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from sra_inputs import WORKLOADS
+    wl = WORKLOADS[args.workload]
+    if wl.fmt != "nm" or wl.name == "opt66b_ffn_decode":
+        raise SystemExit(f"workload {wl.name} is not wired into bench.py yet")
+    out, inp, dense_eq = bench_nm_layer(args, wl)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget, dense_eq)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -188,6 +188,26 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, c
                                uint32_t flags, void* dX, float* dA, float* dB, float* dU_out,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* Kernel classes for sra_time_next_kernel. */
+enum {
+  SRA_KERNEL_COMPRESS = 1,     /* 2:4 compression (sra_compress) */
+  SRA_KERNEL_DOUBLE_PRUNE = 2, /* sra_double_prune */
+  SRA_KERNEL_SPMM24 = 3,       /* bf16 2:4 SpMM + fused adapter epilogue (forward Y, backward dX) */
+  SRA_KERNEL_ADAPTER = 4,      /* adapter products U, dU, dB, dA (one launch each) */
+  SRA_KERNEL_DECODE24 = 5,     /* bf16 2:4 decode SpMM (forward with T <= 16) */
+  SRA_KERNEL_SPMM_FFI = 6      /* bf16 fixed fan-in SpMM (forward Y, backward dX) */
+};
+
+/*
+ * Profiling hook for benchmarks (not needed for computing anything).  Arms the calling thread so
+ * that the next launch of a kernel of class `which` records `start` and `stop` (hipEvent_t,
+ * created by the caller with timing enabled) immediately around that one kernel, through
+ * hipExtLaunchKernelGGL.  One kernel class can be armed at a time; arming again replaces the
+ * previous request, and which = 0 disarms.  The events must not be used while a stream is being
+ * captured into a graph.
+ */
+sra_status sra_time_next_kernel(int32_t which, void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

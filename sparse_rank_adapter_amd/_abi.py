@@ -18,8 +18,10 @@ SRA_GRAD_DX, SRA_GRAD_DA, SRA_GRAD_DB, SRA_DX_NO_ADAPTER = 1, 2, 4, 8
 EXPORTS = (
     "sra_abi_version", "sra_last_error", "sra_nm_meta_words", "sra_compress", "sra_double_prune",
     "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
-    "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd",
+    "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_time_next_kernel",
 )
+SRA_KERNEL_COMPRESS, SRA_KERNEL_DOUBLE_PRUNE, SRA_KERNEL_SPMM24 = 1, 2, 3
+SRA_KERNEL_ADAPTER, SRA_KERNEL_DECODE24, SRA_KERNEL_SPMM_FFI = 4, 5, 6
 
 
 class SraSparse(ctypes.Structure):
@@ -60,6 +62,7 @@ def load(path: str = LIB_PATH):
         "sra_sparse_lora_bwd": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                                           c_int32, c_uint32, c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_size_t, c_void_p]),
+        "sra_time_next_kernel": (c_int32, [c_int32, c_void_p, c_void_p]),
     }
     assert set(sig) == set(EXPORTS)
     for name, (res, args) in sig.items():

@@ -74,25 +74,28 @@ def meta_words(cols: int, n: int = 2, m: int = 4) -> int:
     return int(load().sra_nm_meta_words(cols, n, m))
 
 
-def compress(W: torch.Tensor, n: int = 2, m: int = 4) -> SparseMatrix:
-    """compress(W, N, M): first N:M prune along W's columns."""
+def compress(W: torch.Tensor, n: int = 2, m: int = 4, out: SparseMatrix | None = None) -> SparseMatrix:
+    """compress(W, N, M): first N:M prune along W's columns (into `out`'s buffers if given)."""
     lib = load()
     _dev(W)
     rows, cols = W.shape
-    vals = torch.empty((rows, cols // m * n), dtype=W.dtype, device=W.device)
-    meta = torch.empty((rows, meta_words(cols, n, m)), dtype=torch.int32, device=W.device)
-    out = SparseMatrix(SRA_FMT_NM, W.dtype, rows, cols, vals, meta=meta, n=n, m=m)
+    if out is None:
+        vals = torch.empty((rows, cols // m * n), dtype=W.dtype, device=W.device)
+        meta = torch.empty((rows, meta_words(cols, n, m)), dtype=torch.int32, device=W.device)
+        out = SparseMatrix(SRA_FMT_NM, W.dtype, rows, cols, vals, meta=meta, n=n, m=m)
     d = out.desc()
     check("sra_compress", lib.sra_compress(_p(W), _dt(W), rows, cols, n, m, ctypes.byref(d), _stream(W.device)))
     return out
 
 
-def double_prune(Ws: SparseMatrix) -> SparseMatrix:
-    """P = prune_NM(Ws^T): rows = Ws.cols, cols = Ws.rows."""
+def double_prune(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMatrix:
+    """P = prune_NM(Ws^T): rows = Ws.cols, cols = Ws.rows (into `out`'s buffers if given)."""
     lib = load()
-    vals = torch.empty((Ws.cols, Ws.rows // Ws.m * Ws.n), dtype=Ws.dtype, device=Ws.device)
-    meta = torch.empty((Ws.cols, meta_words(Ws.rows, Ws.n, Ws.m)), dtype=torch.int32, device=Ws.device)
-    P = SparseMatrix(SRA_FMT_NM, Ws.dtype, Ws.cols, Ws.rows, vals, meta=meta, n=Ws.n, m=Ws.m)
+    P = out
+    if P is None:
+        vals = torch.empty((Ws.cols, Ws.rows // Ws.m * Ws.n), dtype=Ws.dtype, device=Ws.device)
+        meta = torch.empty((Ws.cols, meta_words(Ws.rows, Ws.n, Ws.m)), dtype=torch.int32, device=Ws.device)
+        P = SparseMatrix(SRA_FMT_NM, Ws.dtype, Ws.cols, Ws.rows, vals, meta=meta, n=Ws.n, m=Ws.m)
     dw, dp = Ws.desc(), P.desc()
     check("sra_double_prune", lib.sra_double_prune(ctypes.byref(dw), ctypes.byref(dp), _stream(Ws.device)))
     return P
@@ -125,6 +128,22 @@ def ffi_transpose(Ws: SparseMatrix) -> SparseMatrix:
     dw, dt = Ws.desc(), T_.desc()
     check("sra_ffi_transpose", lib.sra_ffi_transpose(ctypes.byref(dw), ctypes.byref(dt), _p(ws), nbytes.value, _stream(Ws.device)))
     return T_
+
+
+def time_next_kernel(which: int, start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
+    """Arm the profiling hook: the next launch of kernel class `which` records start/stop."""
+    for e in (start, stop):
+        if e.cuda_event == 0:  # torch creates events lazily
+            e.record()
+    check("sra_time_next_kernel", load().sra_time_next_kernel(which, ctypes.c_void_p(start.cuda_event),
+                                                              ctypes.c_void_p(stop.cuda_event)))
+
+
+def bwd_workspace(P: SparseMatrix, T: int, r: int, flags: int = SRA_GRAD_DX | SRA_GRAD_DA | SRA_GRAD_DB) -> int:
+    n = ctypes.c_size_t()
+    d = P.desc()
+    check("sra_bwd_workspace", load().sra_bwd_workspace(ctypes.byref(d), T, r, flags, ctypes.byref(n)))
+    return n.value
 
 
 def fwd_workspace(Ws: SparseMatrix, T: int, r: int) -> int:

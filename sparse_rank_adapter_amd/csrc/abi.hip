@@ -11,6 +11,8 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local int g_time_which = 0;
+thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
 
 sra_status fail(sra_status st, const char* fmt, ...) {
   char buf[512];
@@ -202,7 +204,32 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
 
 }  // namespace
 
+namespace sra {
+bool take_timing(int which, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_time_which == 0 || g_time_which != which) return false;
+  *start = g_time_start;
+  *stop = g_time_stop;
+  g_time_which = 0;
+  return true;
+}
+}  // namespace sra
+
 extern "C" {
+
+sra_status sra_time_next_kernel(int32_t which, void* start, void* stop) {
+  if (which == 0) {
+    g_time_which = 0;
+    return SRA_OK;
+  }
+  if (which < SRA_KERNEL_COMPRESS || which > SRA_KERNEL_SPMM_FFI)
+    return fail(SRA_ERR_INVALID_ARG, "unknown kernel class %d", which);
+  if (!start || !stop) return fail(SRA_ERR_INVALID_ARG, "start and stop events are required");
+  g_time_which = which;
+  g_time_start = (hipEvent_t)start;
+  g_time_stop = (hipEvent_t)stop;
+  return SRA_OK;
+}
+
 
 int32_t sra_abi_version(void) { return SRA_ABI_VERSION; }
 

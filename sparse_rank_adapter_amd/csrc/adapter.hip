@@ -211,7 +211,7 @@ hipError_t launch_adapter_gemm(const Operand& P, const Operand& Q, int64_t M, in
   const int Seff = (int)((C + cps - 1) / cps);
   const int n_tm = (int)((M + BM - 1) / BM), n_tn = (int)((Nn + BN - 1) / BN);
   double* part = Seff > 1 ? (double*)ws : nullptr;
-  hipLaunchKernelGGL(k_adapter_gemm, dim3((unsigned)(n_tm * n_tn), (unsigned)Seff), dim3(256), 0,
+  launch(SRA_KERNEL_ADAPTER, k_adapter_gemm, dim3((unsigned)(n_tm * n_tn), (unsigned)Seff), dim3(256), 0,
                      s, P, Q, M, Nn, C, cps, part, out, n_tn);
   if (Seff > 1) {
     const int64_t n = M * Nn;

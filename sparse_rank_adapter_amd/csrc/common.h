@@ -1,6 +1,7 @@
 // Internal helpers shared by the HIP sources of libsra (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,6 +56,21 @@ SRA_DEV void split3_bf16(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
 
 // ---- host-side launchers implemented in the kernel sources (internal C++ linkage)
 namespace sra {
+
+// Profiling hook (sra_time_next_kernel): returns true, and the events, exactly once after the
+// calling thread armed kernel class `which`.
+bool take_timing(int which, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch through hipExtLaunchKernelGGL with the armed events when this kernel class is armed.
+template <typename K, typename... Args>
+inline void launch(int which, K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                   Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (take_timing(which, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 hipError_t launch_compress24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
                              uint32_t* meta, hipStream_t s);

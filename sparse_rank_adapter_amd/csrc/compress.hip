@@ -134,10 +134,10 @@ hipError_t launch_compress24(int dtype, const void* W, int64_t rows, int64_t col
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 255) / 256));
   if (dtype == SRA_BF16)
-    hipLaunchKernelGGL(k_compress24<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, rows,
+    launch(SRA_KERNEL_COMPRESS, k_compress24<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, rows,
                        wpr, (uint16_t*)vals, meta);
   else
-    hipLaunchKernelGGL(k_compress24<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)W, rows,
+    launch(SRA_KERNEL_COMPRESS, k_compress24<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)W, rows,
                        wpr, (uint32_t*)vals, meta);
   return hipGetLastError();
 }
@@ -147,10 +147,10 @@ hipError_t launch_double_prune24(int dtype, const void* vals, const uint32_t* me
   if (rows == 0 || cols == 0) return hipSuccess;
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
   if (dtype == SRA_BF16)
-    hipLaunchKernelGGL(k_double_prune24<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)vals,
+    launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune24<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)vals,
                        meta, rows, cols, (uint16_t*)p_vals, p_meta);
   else
-    hipLaunchKernelGGL(k_double_prune24<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)vals,
+    launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune24<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)vals,
                        meta, rows, cols, (uint32_t*)p_vals, p_meta);
   return hipGetLastError();
 }

@@ -246,7 +246,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
                               hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
   const int n_rt = (int)((R + BR - 1) / BR), n_tt = (int)((T + BT - 1) / BT);
-  hipLaunchKernelGGL(k_spmm24, dim3((unsigned)(n_rt * n_tt)), dim3(256), 0, s, s_vals, s_meta, R,
+  launch(SRA_KERNEL_SPMM24, k_spmm24, dim3((unsigned)(n_rt * n_tt)), dim3(256), 0, s, s_vals, s_meta, R,
                      C, act, T, ep, out, n_rt, n_tt);
   return hipGetLastError();
 }

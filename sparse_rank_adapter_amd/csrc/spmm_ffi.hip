@@ -42,7 +42,7 @@ hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t*
                                 hipStream_t s) {
   const int64_t n = T * R;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_spmm_ffi_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, format,
+  launch(SRA_KERNEL_SPMM_FFI, k_spmm_ffi_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, format,
                      vals, idx, row_ptr, k, R, C, act, T, ep, out);
   return hipGetLastError();
 }
