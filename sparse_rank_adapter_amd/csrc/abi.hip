@@ -144,9 +144,12 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
   p.own_u = own_u && r > 0 && Ws->dtype == SRA_BF16;
   if (p.own_u) p.u_off = a.take((size_t)T * r * 4);
   if (Ws->dtype == SRA_F32 && r > 0) p.u64_off = a.take((size_t)T * r * 8);
-  if (Ws->dtype == SRA_BF16 && r > 0) {
-    p.gemm_off = a.take(sra::adapter_gemm_ws(T, r, Ws->cols));
+  if (Ws->dtype == SRA_BF16) {
+    size_t g = r > 0 ? sra::adapter_rows_ws(T, Ws->cols, r) : 0;
+    if (Ws->format == SRA_FMT_NM) g = std::max(g, sra::spmm24_ws(Ws->rows, Ws->cols, T));
+    p.gemm_off = a.take(g);
   }
+
   p.total = a.used;
   if (plan) *plan = p;
   return p.total;
@@ -155,7 +158,7 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
 // ---------------------------------------------------------------- backward plan
 struct BwdPlan {
   bool need_du = false, need_u = false, own_du = false, own_u = false;
-  size_t u_off = 0, du_off = 0, u64_off = 0, du64_off = 0, gemm_off = 0, total = 0;
+  size_t u_off = 0, du_off = 0, u64_off = 0, du64_off = 0, gemm_off = 0, spmm_off = 0, total = 0;
 };
 
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
@@ -189,14 +192,17 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   p.own_u = p.need_u && !have_u;
   if (p.own_u) p.u_off = a.take((size_t)T * r * 4);
   if (p.own_du) p.du_off = a.take((size_t)T * r * 4);
+  if (da && r > 0) p.du64_off = a.take((size_t)T * r * 8);  // dU in fp64 feeds dA
   if (P->dtype == SRA_BF16 && r > 0) {
     size_t g = 0;
-    if (p.own_u) g = std::max(g, sra::adapter_gemm_ws(T, r, K));
-    if (p.need_du) g = std::max(g, sra::adapter_gemm_ws(T, r, N));
-    if (db) g = std::max(g, sra::adapter_gemm_ws(N, r, T));
-    if (da) g = std::max(g, sra::adapter_gemm_ws(r, K, T));
+    if (p.own_u) g = std::max(g, sra::adapter_rows_ws(T, K, r));
+    if (p.need_du) g = std::max(g, sra::adapter_rows_ws(T, N, r));
+    if (db) g = std::max(g, sra::adapter_cols_ws(T, N, r));
+    if (da) g = std::max(g, sra::adapter_cols_ws(T, K, r));
     p.gemm_off = a.take(g);
   }
+  if (P->dtype == SRA_BF16 && P->format == SRA_FMT_NM && dx)
+    p.spmm_off = a.take(sra::spmm24_ws(K, N, T));
   p.total = a.used;
   if (plan) *plan = p;
   return p.total;
@@ -368,10 +374,9 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     return hip_done(sra::launch_f32_spmm(S, (const float*)X, T, U64, (const float*)B, r, 1, r,
                                          (float*)Y, s), s, "fwd spmm f32");
   }
-  if (r > 0) {
-    const sra::Operand P{X, K, 1, false}, Q{A, K, 1, false};
-    SRA_TRY(hip_done(sra::launch_adapter_gemm(P, Q, T, r, K, U, wsb + plan.gemm_off, s), s, "fwd U"));
-  }
+  if (r > 0)
+    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, 1, r,
+                                              U, nullptr, wsb + plan.gemm_off, s), s, "fwd U"));
   sra::Epilogue ep;
   ep.U = U;
   ep.E = (const uint16_t*)B;
@@ -380,7 +385,8 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
   ep.r = r;
   if (Ws->format == SRA_FMT_NM)
     return hip_done(sra::launch_spmm24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
-                                            (const uint16_t*)X, T, ep, (uint16_t*)Y, s),
+                                            (const uint16_t*)X, T, ep, (uint16_t*)Y,
+                                            wsb ? wsb + plan.gemm_off : nullptr, s),
                     s, "fwd spmm 2:4");
   return hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_ELL, (const uint16_t*)Ws->values, Ws->index,
                                             nullptr, Ws->k, N, K, (const uint16_t*)X, T, ep,
@@ -452,14 +458,13 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                           dA, s), s, "bwd dA"));
     return SRA_OK;
   }
-  if (plan.own_u) {
-    const sra::Operand Pp{X, K, 1, false}, Qq{A, K, 1, false};
-    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, T, r, K, (float*)Uv, gws, s), s, "bwd U"));
-  }
-  if (plan.need_du) {
-    const sra::Operand Pp{dY, N, 1, false}, Qq{B, 1, r, false};
-    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, T, r, N, dU, gws, s), s, "bwd dU"));
-  }
+  double* dU64 = fda ? (double*)(wsb + plan.du64_off) : nullptr;
+  if (plan.own_u)
+    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, 1, r,
+                                              (float*)Uv, nullptr, gws, s), s, "bwd U"));
+  if (plan.need_du)
+    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)dY, T, N, (const uint16_t*)B, 1, r, r,
+                                              dU, dU64, gws, s), s, "bwd dU"));
   if (fdx) {
     sra::Epilogue ep;
     ep.U = dU;
@@ -469,7 +474,8 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     ep.r = dx_ad ? r : 0;
     if (P->format == SRA_FMT_NM)
       SRA_TRY(hip_done(sra::launch_spmm24_bf16((const uint16_t*)P->values, P->meta, K, N,
-                                               (const uint16_t*)dY, T, ep, (uint16_t*)dX, s),
+                                               (const uint16_t*)dY, T, ep, (uint16_t*)dX,
+                                               wsb ? wsb + plan.spmm_off : nullptr, s),
                        s, "bwd dX 2:4"));
     else
       SRA_TRY(hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_CSR, (const uint16_t*)P->values, P->index,
@@ -477,14 +483,12 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                                  (uint16_t*)dX, s),
                        s, "bwd dX ffi"));
   }
-  if (fdb) {
-    const sra::Operand Pp{dY, 1, N, false}, Qq{Uv, 1, r, true};
-    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, N, r, T, dB, gws, s), s, "bwd dB"));
-  }
-  if (fda) {
-    const sra::Operand Pp{dU, 1, r, true}, Qq{X, 1, K, false};
-    SRA_TRY(hip_done(sra::launch_adapter_gemm(Pp, Qq, r, K, T, dA, gws, s), s, "bwd dA"));
-  }
+  if (fdb)
+    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)dY, T, N, Uv, nullptr, r, false, dB,
+                                              gws, s), s, "bwd dB"));
+  if (fda)
+    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)X, T, K, nullptr, dU64, r, true, dA,
+                                              gws, s), s, "bwd dA"));
   return SRA_OK;
 }
 

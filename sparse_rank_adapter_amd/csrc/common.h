@@ -53,6 +53,16 @@ SRA_DEV void split3_bf16(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   mid = f32_to_bf16(r1);
   lo = f32_to_bf16(r1 - bf16_to_f32(mid));
 }
+// Four-way split of an fp64 value into bf16 parts (error about 2^-33 |x|); the remainders are
+// formed in fp64, so each part is the correctly rounded bf16 of what is left.
+SRA_DEV void split4_bf16(double x, uint16_t p[4]) {
+  double rem = x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = f32_to_bf16((float)rem);
+    rem -= (double)bf16_to_f32(p[i]);
+  }
+}
 
 // ---- host-side launchers implemented in the kernel sources (internal C++ linkage)
 namespace sra {
@@ -114,9 +124,10 @@ struct Epilogue {
   int64_t e_row_stride = 0, e_j_stride = 0;
   int r = 0;
 };
+size_t spmm24_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
-                              hipStream_t s);
+                              void* ws, hipStream_t s);
 size_t spmm24_decode_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
@@ -127,15 +138,18 @@ hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t*
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                                 hipStream_t s);
 
-// Skinny adapter products, fp32 result:  Out[m][n] = sum_c P(m,c) Q(n,c)
-// element (m,c) of P at P[m*sPm + c*sPc]; `p_f32` selects fp32 storage (else bf16 bits).
-struct Operand {
-  const void* ptr;
-  int64_t s_row, s_red;  // strides of the non-reduced index and of the reduction index
-  bool f32;
-};
-size_t adapter_gemm_ws(int64_t M, int64_t Nn, int64_t C);
-hipError_t launch_adapter_gemm(const Operand& P, const Operand& Q, int64_t M, int64_t Nn, int64_t C,
-                               float* out, void* ws, hipStream_t s);
+// Adapter products (fp32 results):
+//   rows: out[t][j] = sum_c act[t][c] * Wt(j, c), Wt(j, c) = wt[j*wt_sj + c*wt_sc]   (U, dU)
+//   cols: out[m][j] = sum_t act[t][m] * V[t][j], written as [m][j] or transposed [j][m] (dB, dA)
+// rows also writes an fp64 copy of the result to out64 when non-null; cols reads V as fp32
+// (V32) or fp64 (V64), whichever is non-null.
+size_t adapter_rows_ws(int64_t T, int64_t C, int r);
+hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const uint16_t* wt,
+                               int64_t wt_sj, int64_t wt_sc, int r, float* out, double* out64,
+                               void* ws, hipStream_t s);
+size_t adapter_cols_ws(int64_t T, int64_t M, int r);
+hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const float* V32,
+                               const double* V64, int r, bool out_transposed, float* out, void* ws,
+                               hipStream_t s);
 
 }  // namespace sra

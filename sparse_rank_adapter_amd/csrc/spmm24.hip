@@ -14,31 +14,28 @@
 // v_smfmac_f32_32x32x32_bf16 is two 8-element runs, at 8g and 8g+16 of the 32-column step
 // (g = lane / 32), both plain 16-byte LDS reads.
 //
-// Tiling: 128 weight rows x 128 tokens per workgroup, 4 waves of 64 x 64 (2 x 2 accumulators),
-// 64 logical columns per stage (C % 32 == 0; a final half stage is zero-filled).  Stages are double-buffered in LDS with register prefetch; LDS
-// rows are padded by 16 bytes so the 128-bit fragment reads of 16 consecutive lanes hit 16
-// distinct 4-bank groups.  The epilogue adds U E^T with dense 32x32x16 MFMAs on the same
-// accumulators; U stays fp32 through a bf16 hi + lo split.  Workgroup ids are remapped so that
-// tiles sharing weight rows land on the same XCD (and its L2).
+// Tiling (template): each of the 4 waves owns FR x FT accumulators of 32x32 (a wave tile of
+// 32FR rows x 32FT tokens); the waves form a WR x WT grid.  Per SMFMAC cycle a wave reads
+// 1024/(32FT) bytes of weights and 2048/(32FR) bytes of activations from LDS, so larger wave tiles
+// cut LDS traffic; larger workgroup tiles cut L2 re-reads; small problems need small tiles (or a
+// split of the reduction) to occupy 256 CUs.  64 logical columns per stage (C % 32 == 0; a final
+// half stage is zero-filled), double-buffered LDS with register prefetch, rows padded by 16
+// bytes so the 128-bit fragment reads of 16 consecutive lanes hit distinct bank groups.
+// The epilogue adds U E^T with dense 32x32x16 MFMAs on the same accumulators; U stays fp32
+// through a bf16 hi + lo split.  A split of the reduction over S workgroups writes fp32 partial
+// tiles (the first split adds the epilogue) that a second kernel sums in a fixed order, so the
+// result is deterministic.  Workgroup ids are remapped so each XCD runs a contiguous range of
+// tiles, ordered in groups of 8 row tiles so concurrent workgroups share both operands in L2.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 
 namespace {
 
-constexpr int BR = 128, BT = 128, BC = 64;
+constexpr int BC = 64;
 constexpr int A_LD = 80;   // bytes per compressed row in LDS (32 bf16 + pad)
 constexpr int B_LD = 144;  // bytes per activation row in LDS (64 bf16 + pad)
-
-struct __align__(16) Smem {
-  uint8_t a[2][BR * A_LD];
-  uint32_t m[2][BR * 2];
-  uint8_t b[2][BT * B_LD];
-};
-
-struct Prefetch {
-  u32x4 a[2];
-  u32x2 m;
-  u32x4 b[4];
-};
 
 SRA_DEV int xcd_remap(int bid, int nblocks) {
   // Hardware dispatches consecutive workgroup ids round-robin over the 8 XCDs; give each XCD a
@@ -49,121 +46,163 @@ SRA_DEV int xcd_remap(int bid, int nblocks) {
   return (bid & 7) * per + (bid >> 3);
 }
 
-__global__ __launch_bounds__(256, 2) void k_spmm24(const uint16_t* __restrict__ s_vals,
-                                                   const uint32_t* __restrict__ s_meta, int64_t R,
-                                                   int64_t C, const uint16_t* __restrict__ act,
-                                                   int64_t T, sra::Epilogue ep,
-                                                   uint16_t* __restrict__ out, int n_rt,
-                                                   int n_tt) {
+// Logical tile id -> (row tile, token tile) in groups of 8 row tiles: consecutive ids (which run
+// concurrently on one XCD) sweep 8 row tiles for each token tile, so the XCD's L2 serves both
+// operands to ~8 workgroups each instead of re-streaming activations once per row tile.
+SRA_DEV void tile_coords(int L, int n_rt, int n_tt, int& rt, int& tt) {
+  constexpr int G = 8;
+  const int per_group = G * n_tt;
+  const int group = L / per_group, first = group * G;
+  const int gsize = min(G, n_rt - first);
+  const int in = L - group * per_group;
+  rt = first + in % gsize;
+  tt = in / gsize;
+}
+
+template <int FR, int FT, int WR, int WT>
+struct Tile {
+  static constexpr int BR = 32 * FR * WR, BT = 32 * FT * WT;
+  static constexpr int NA = BR * 4 / 256;             // 16-byte value chunks per lane
+  static constexpr int NB = BT * 8 / 256;             // 16-byte activation chunks per lane
+  static constexpr int OCC = (FR * FT >= 8) ? 1 : 2;  // workgroups per CU the registers allow
+  struct __align__(16) Smem {
+    uint8_t a[2][BR * A_LD];
+    uint32_t m[2][BR * 2];
+    uint8_t b[2][BT * B_LD];
+  };
+  struct Prefetch {
+    u32x4 a[NA];
+    u32x2 m;
+    u32x4 b[NB];
+  };
+};
+
+template <int FR, int FT, int WR, int WT>
+__global__ __launch_bounds__(256, (Tile<FR, FT, WR, WT>::OCC)) void k_spmm24(
+    const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
+    const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
+    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
+  using TL = Tile<FR, FT, WR, WT>;
+  constexpr int BR = TL::BR, BT = TL::BT, NA = TL::NA, NB = TL::NB;
+  static_assert(WR * WT == 4, "4 waves");
+  static_assert(NA >= 1 && NB >= 1, "tile too small for the loaders");
+  using Smem = typename TL::Smem;
+  using Prefetch = typename TL::Prefetch;
   __shared__ Smem sm;
+
   const int tid = threadIdx.x;
-  const int tile = xcd_remap(blockIdx.x, n_rt * n_tt);
-  const int rt = tile / n_tt, tt = tile - rt * n_tt;
+  int rt, tt;
+  tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
   const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT;
   const int64_t cv = C / 2, cm = C / 32;  // stored values / meta words per weight row
-  const int nC = (int)((C + BC - 1) / BC);
+  const int nC_all = (int)((C + BC - 1) / BC);
+  const int z = blockIdx.y;
+  const int c_beg = z * stages_per_split;
+  const int c_end = min(nC_all, c_beg + stages_per_split);
 
   // The last stage may be half full (C % 64 == 32): its upper 32 columns load as zeros.
   auto load = [&](int c, Prefetch& p) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i, r = q >> 2, part = q & 3;
-      const int64_t row = row0 + r, off = (int64_t)c * 32 + part * 8;
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, part_ = q & 3;
+      const int64_t row = row0 + r, off = (int64_t)c * 32 + part_ * 8;
       p.a[i] = (row < R && off < cv) ? *reinterpret_cast<const u32x4*>(s_vals + row * cv + off)
                                      : u32x4{0, 0, 0, 0};
     }
+    p.m = u32x2{0, 0};
     if (tid < BR) {
       const int64_t row = row0 + tid, w = (int64_t)c * 2;
-      p.m = u32x2{0, 0};
       if (row < R) {
         p.m[0] = s_meta[row * cm + w];
         if (w + 1 < cm) p.m[1] = s_meta[row * cm + w + 1];
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, tk = q >> 3, part = q & 7;
-      const int64_t t = t0 + tk, off = (int64_t)c * BC + part * 8;
+    for (int i = 0; i < NB; ++i) {
+      const int q = tid + 256 * i, tk = q >> 3, part_ = q & 7;
+      const int64_t t = t0 + tk, off = (int64_t)c * BC + part_ * 8;
       p.b[i] = (t < T && off < C) ? *reinterpret_cast<const u32x4*>(act + t * C + off)
                                   : u32x4{0, 0, 0, 0};
     }
   };
   auto store = [&](int buf, const Prefetch& p) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i, r = q >> 2, part = q & 3;
-      *reinterpret_cast<u32x4*>(&sm.a[buf][r * A_LD + part * 16]) = p.a[i];
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, part_ = q & 3;
+      *reinterpret_cast<u32x4*>(&sm.a[buf][r * A_LD + part_ * 16]) = p.a[i];
     }
     if (tid < BR) *reinterpret_cast<u32x2*>(&sm.m[buf][tid * 2]) = p.m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, tk = q >> 3, part = q & 7;
-      *reinterpret_cast<u32x4*>(&sm.b[buf][tk * B_LD + part * 16]) = p.b[i];
+    for (int i = 0; i < NB; ++i) {
+      const int q = tid + 256 * i, tk = q >> 3, part_ = q & 7;
+      *reinterpret_cast<u32x4*>(&sm.b[buf][tk * B_LD + part_ * 16]) = p.b[i];
     }
   };
 
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int wr = wave >> 1, wt = wave & 1;
-  f32x16 acc[2][2];
+  const int wr = wave / WT, wt = wave % WT;
+  f32x16 acc[FR][FT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FR; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FT; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 af[2];
-      int idx[2];
+      bf16x8 af[FR];
+      int idx[FR];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wr * 64 + i * 32 + li;
+      for (int i = 0; i < FR; ++i) {
+        const int r = wr * 32 * FR + i * 32 + li;
         af[i] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][r * A_LD + 32 * s + 16 * g]);
         idx[i] = (int)(sm.m[buf][r * 2 + s] >> (16 * g));
       }
-      bf16x16 bfr[2];
+      bf16x16 bfr[FT];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int tk = wt * 64 + j * 32 + li;
+      for (int j = 0; j < FT; ++j) {
+        const int tk = wt * 32 * FT + j * 32 + li;
         const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&sm.b[buf][tk * B_LD + 64 * s + 16 * g]);
         const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&sm.b[buf][tk * B_LD + 64 * s + 32 + 16 * g]);
         bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FR; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FT; ++j)
           acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[i], bfr[j], acc[i][j], idx[i], 0, 0);
     }
   };
 
-  {
-    Prefetch p;
-    load(0, p);
-    store(0, p);
-  }
-  __syncthreads();
-  for (int c = 0; c < nC; ++c) {
-    Prefetch p;
-    const bool more = c + 1 < nC;
-    if (more) load(c + 1, p);
-    compute(c & 1);
-    if (more) store((c + 1) & 1, p);
+  if (c_beg < c_end) {
+    {
+      Prefetch p;
+      load(c_beg, p);
+      store(0, p);
+    }
     __syncthreads();
+    for (int c = c_beg; c < c_end; ++c) {
+      Prefetch p;
+      const bool more = c + 1 < c_end;
+      if (more) load(c + 1, p);
+      compute((c - c_beg) & 1);
+      if (more) store((c + 1 - c_beg) & 1, p);
+      __syncthreads();
+    }
   }
 
-  // ---- fused low-rank epilogue: acc += E(rows, :) U(tokens, :)^T
-  if (ep.r > 0) {
+  // ---- fused low-rank epilogue (first split only): acc += E(rows, :) U(tokens, :)^T
+  if (ep.r > 0 && z == 0) {
     const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0;
     const bool u_vec = (ep.r & 7) == 0;
     for (int jj = 0; jj < ep.r; jj += 16) {
       const int jb = jj + 8 * g;
-      bf16x8 ef[2];
+      bf16x8 ef[FR];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t row = row0 + wr * 64 + i * 32 + li;
+      for (int i = 0; i < FR; ++i) {
+        const int64_t row = row0 + wr * 32 * FR + i * 32 + li;
         union { u32x4 v; uint16_t h[8]; bf16x8 b; } x;
         x.v = u32x4{0, 0, 0, 0};
         if (row < R) {
@@ -178,8 +217,8 @@ __global__ __launch_bounds__(256, 2) void k_spmm24(const uint16_t* __restrict__ 
         ef[i] = x.b;
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t t = t0 + wt * 64 + j * 32 + li;
+      for (int j = 0; j < FT; ++j) {
+        const int64_t t = t0 + wt * 32 * FT + j * 32 + li;
         float u[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) u[q] = 0.f;
@@ -203,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void k_spmm24(const uint16_t* __restrict__ 
 #pragma unroll
         for (int q = 0; q < 8; ++q) split_bf16(u[q], hi.h[q], lo.h[q]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < FR; ++i) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[i], hi.b, acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[i], lo.b, acc[i][j], 0, 0, 0);
         }
@@ -214,14 +253,26 @@ __global__ __launch_bounds__(256, 2) void k_spmm24(const uint16_t* __restrict__ 
   // ---- store: lane holds, for token (col) li, rows 8a + 4g + {0..3}
   const bool r4 = (R & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FR; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t t = t0 + wt * 64 + j * 32 + li;
+    for (int j = 0; j < FT; ++j) {
+      const int64_t t = t0 + wt * 32 * FT + j * 32 + li;
       if (t >= T) continue;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int64_t rb = row0 + wr * 64 + i * 32 + 8 * a + 4 * g;
+        const int64_t rb = row0 + wr * 32 * FR + i * 32 + 8 * a + 4 * g;
+        if (part) {  // fp32 partial of split z, in the output's [t][row] layout
+          float* o = part + ((int64_t)z * T + t) * R + rb;
+          if (r4 && rb + 3 < R) {
+            *reinterpret_cast<f32x4*>(o) = f32x4{acc[i][j][4 * a], acc[i][j][4 * a + 1],
+                                                 acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]};
+          } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              if (rb + b < R) o[b] = acc[i][j][4 * a + b];
+          }
+          continue;
+        }
         uint16_t* o = out + t * R + rb;
         if (r4 && rb + 3 < R) {
           u32x2 v;
@@ -237,17 +288,629 @@ __global__ __launch_bounds__(256, 2) void k_spmm24(const uint16_t* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Pipelined variant (C % 64 == 0): operands move global -> LDS with global_load_lds (no register
+// staging) into a ring of NS stage buffers, issued NS-1 stages ahead of the MFMAs.  Every wave
+// issues the same number L of 1 KB (dwordx4) / 256 B (dword, metadata) transfers per stage, so
+// "stage c has landed" is a compile-time vmcnt.  A DMA writes lane i's 16 bytes at slot i of its
+// 1 KB block, so each lane chooses which global chunk to fetch: LDS rows are XOR-swizzled
+// (chunk ^ f(row)) instead of padded, and the 128-bit fragment reads of 16 consecutive lanes
+// still hit 16 distinct bank groups.  Rows / tokens past the edge read a clamped valid address
+// and their results are never stored.
+template <int FR, int FT, int WR, int WT, int NS>
+struct PTile {
+  static constexpr int BR = 32 * FR * WR, BT = 32 * FT * WT;
+  static constexpr int LA = BR / 64, LM = BR / 128, LB = BT / 32;  // transfers per wave per stage
+  static constexpr int L = LA + LM + LB;
+  static constexpr int A_BYTES = BR * 64, M_BYTES = BR * 8, B_BYTES = BT * 128;
+  static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int OCC = (FR * FT >= 8 || 2 * LDS > 160 * 1024) ? 1 : 2;
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+SRA_DEV void dma16(const void* g, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_block, 16, 0, 0);
+}
+SRA_DEV void dma4(const void* g, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_block, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N) only (expcnt / lgkmcnt left at their maxima), gfx9 encoding
+template <int N>
+SRA_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int FR, int FT, int WR, int WT, int NS>
+__global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm24_pipe(
+    const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
+    const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
+    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
+  using TL = PTile<FR, FT, WR, WT, NS>;
+  constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
+  static_assert(WR * WT == 4, "4 waves");
+  static_assert(BR % 128 == 0 && BT % 32 == 0, "transfer counts must be whole per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  int rt, tt;
+  tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
+  const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT;
+  const int64_t cv = C / 2, cm = C / 32;
+  const int nC_all = (int)(C / BC);
+  const int z = blockIdx.y;
+  const int c_beg = z * stages_per_split;
+  const int c_end = min(nC_all, c_beg + stages_per_split);
+
+  // Per-lane source pointers for stage 0; stage c adds c*32 values / c*64 activations / 2c words.
+  const uint16_t* a_src[TL::LA];
+  int a_dst[TL::LA];
+#pragma unroll
+  for (int k = 0; k < TL::LA; ++k) {
+    const int b = k * 4 + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
+    const int ch = pos ^ ((row >> 2) & 3);
+    const int64_t grow = min(row0 + row, R - 1);
+    a_src[k] = s_vals + grow * cv + ch * 8;
+    a_dst[k] = b * 1024;
+  }
+  const uint32_t* m_src[TL::LM];
+  int m_dst[TL::LM];
+#pragma unroll
+  for (int k = 0; k < TL::LM; ++k) {
+    const int b = k * 4 + wave, row = 32 * b + (lane >> 1);
+    const int64_t grow = min(row0 + row, R - 1);
+    m_src[k] = s_meta + grow * cm + (lane & 1);
+    m_dst[k] = TL::A_BYTES + b * 256;
+  }
+  const uint16_t* b_src[TL::LB];
+  int b_dst[TL::LB];
+#pragma unroll
+  for (int k = 0; k < TL::LB; ++k) {
+    const int b = k * 4 + wave, tk = 8 * b + (lane >> 3), pos = lane & 7;
+    const int ch = pos ^ ((tk >> 1) & 7);
+    const int64_t gt = min(t0 + tk, T - 1);
+    b_src[k] = act + gt * C + ch * 8;
+    b_dst[k] = TL::A_BYTES + TL::M_BYTES + b * 1024;
+  }
+  auto issue = [&](int c, int buf) {
+    uint8_t* base = smem + buf * TL::STAGE;
+#pragma unroll
+    for (int k = 0; k < TL::LA; ++k) dma16(a_src[k] + (int64_t)c * 32, base + a_dst[k]);
+#pragma unroll
+    for (int k = 0; k < TL::LM; ++k) dma4(m_src[k] + (int64_t)c * 2, base + m_dst[k]);
+#pragma unroll
+    for (int k = 0; k < TL::LB; ++k) dma16(b_src[k] + (int64_t)c * BC, base + b_dst[k]);
+  };
+
+  f32x16 acc[FR][FT];
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int wr = wave / WT, wt = wave % WT;
+  auto compute = [&](int buf) {
+    const uint8_t* A = smem + buf * TL::STAGE;
+    const uint32_t* M = reinterpret_cast<const uint32_t*>(A + TL::A_BYTES);
+    const uint8_t* B = A + TL::A_BYTES + TL::M_BYTES;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[FR];
+      int idx[FR];
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int r = wr * 32 * FR + i * 32 + li;
+        af[i] = *reinterpret_cast<const bf16x8*>(A + r * 64 + (((2 * s + g) ^ ((r >> 2) & 3)) << 4));
+        idx[i] = (int)(M[r * 2 + s] >> (16 * g));
+      }
+      bf16x16 bfr[FT];
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int tk = wt * 32 * FT + j * 32 + li, sw = (tk >> 1) & 7;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 * s + g) ^ sw) << 4));
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 * s + 2 + g) ^ sw) << 4));
+        bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FT; ++j)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[i], bfr[j], acc[i][j], idx[i], 0, 0);
+    }
+  };
+
+  constexpr int D = NS - 1;  // stages in flight ahead of the one being computed
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (c_beg + d < c_end) issue(c_beg + d, d);
+  for (int c = c_beg; c < c_end; ++c) {
+    const int in_flight = min(D, c_end - c);  // stages c .. c+in_flight-1 were issued
+    if (in_flight >= 4) wait_vm<(3 * L < 63 ? 3 * L : 63)>();
+    else if (in_flight == 3) wait_vm<2 * L>();
+    else if (in_flight == 2) wait_vm<L>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // stage c visible to all waves; stage c-1 fully consumed
+    if (c + D < c_end) issue(c + D, (c - c_beg + D) % NS);
+    compute((c - c_beg) % NS);
+  }
+
+  // ---- fused low-rank epilogue (first split only): acc += E(rows, :) U(tokens, :)^T
+  if (ep.r > 0 && z == 0) {
+    const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0;
+    const bool u_vec = (ep.r & 7) == 0;
+    for (int jj = 0; jj < ep.r; jj += 16) {
+      const int jb = jj + 8 * g;
+      bf16x8 ef[FR];
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int64_t row = row0 + wr * 32 * FR + i * 32 + li;
+        union { u32x4 v; uint16_t h[8]; bf16x8 b; } x;
+        x.v = u32x4{0, 0, 0, 0};
+        if (row < R) {
+          if (e_vec && jb + 8 <= ep.r) {
+            x.v = *reinterpret_cast<const u32x4*>(ep.E + row * ep.e_row_stride + jb);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (jb + q < ep.r) x.h[q] = ep.E[row * ep.e_row_stride + (int64_t)(jb + q) * ep.e_j_stride];
+          }
+        }
+        ef[i] = x.b;
+      }
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int64_t t = t0 + wt * 32 * FT + j * 32 + li;
+        float u[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[q] = 0.f;
+        if (t < T) {
+          const float* up = ep.U + t * ep.r + jb;
+          if (u_vec && jb + 8 <= ep.r) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              u[q] = a0[q];
+              u[q + 4] = a1[q];
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (jb + q < ep.r) u[q] = up[q];
+          }
+        }
+        union { uint16_t h[8]; bf16x8 b; } hi, lo;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) split_bf16(u[q], hi.h[q], lo.h[q]);
+#pragma unroll
+        for (int i = 0; i < FR; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[i], hi.b, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[i], lo.b, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const bool r4 = (R & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int64_t t = t0 + wt * 32 * FT + j * 32 + li;
+      if (t >= T) continue;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int64_t rb = row0 + wr * 32 * FR + i * 32 + 8 * a + 4 * g;
+        if (part) {
+          float* o = part + ((int64_t)z * T + t) * R + rb;
+          if (r4 && rb + 3 < R) {
+            *reinterpret_cast<f32x4*>(o) = f32x4{acc[i][j][4 * a], acc[i][j][4 * a + 1],
+                                                 acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]};
+          } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              if (rb + b < R) o[b] = acc[i][j][4 * a + b];
+          }
+          continue;
+        }
+        uint16_t* o = out + t * R + rb;
+        if (r4 && rb + 3 < R) {
+          u32x2 v;
+          v[0] = pack_bf16x2(acc[i][j][4 * a + 0], acc[i][j][4 * a + 1]);
+          v[1] = pack_bf16x2(acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]);
+          *reinterpret_cast<u32x2*>(o) = v;
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (rb + b < R) o[b] = f32_to_bf16(acc[i][j][4 * a + b]);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Pipelined variant on v_smfmac_f32_16x16x64_bf16, which moves stored (non-zero) work ~20% faster
+// on gfx950 than the 32x32x32 form.  Same LDS ring, DMA transfers and swizzles as above; per
+// 64-column stage one SMFMAC per (16 weight rows, 16 tokens) pair.  Lane l of an A fragment holds
+// row l%16 and logical columns 16(l/16)..+15 (16 contiguous bytes = swizzled chunk l/16 of the
+// row); its metadata is the (l/16)&1 half of word (l/16)/2.  Lane l of a B fragment holds token
+// l%16 and columns 8(l/16)..+7 and 32+8(l/16)..+7 (chunks l/16 and 4 + l/16).  Accumulator lane l
+// holds rows 4(l/16)..+3 of token l%16.
+template <int FR, int FT, int WR, int WT, int NS>
+struct QTile {
+  static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
+  static constexpr int LA = BR / 64, LM = BR / 128, LB = BT / 32;
+  static constexpr int L = LA + LM + LB;
+  static constexpr int A_BYTES = BR * 64, M_BYTES = BR * 8, B_BYTES = BT * 128;
+  static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int OCC = (FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
+};
+
+template <int FR, int FT, int WR, int WT, int NS>
+__global__ __launch_bounds__(256, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm24_q(
+    const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
+    const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
+    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
+  using TL = QTile<FR, FT, WR, WT, NS>;
+  constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
+  static_assert(WR * WT == 4, "4 waves");
+  static_assert(BR % 128 == 0 && BT % 32 == 0, "transfer counts must be whole per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, q4 = lane >> 4, l16 = lane & 15;
+  int rt, tt;
+  tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
+  const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT;
+  const int64_t cv = C / 2, cm = C / 32;
+  const int nC_all = (int)(C / BC);
+  const int z = blockIdx.y;
+  const int c_beg = z * stages_per_split;
+  const int c_end = min(nC_all, c_beg + stages_per_split);
+
+  const uint16_t* a_src[TL::LA];
+  int a_dst[TL::LA];
+#pragma unroll
+  for (int k = 0; k < TL::LA; ++k) {
+    const int b = k * 4 + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
+    const int ch = pos ^ ((row >> 2) & 3);
+    const int64_t grow = min(row0 + row, R - 1);
+    a_src[k] = s_vals + grow * cv + ch * 8;
+    a_dst[k] = b * 1024;
+  }
+  const uint32_t* m_src[TL::LM];
+  int m_dst[TL::LM];
+#pragma unroll
+  for (int k = 0; k < TL::LM; ++k) {
+    const int b = k * 4 + wave, row = 32 * b + (lane >> 1);
+    const int64_t grow = min(row0 + row, R - 1);
+    m_src[k] = s_meta + grow * cm + (lane & 1);
+    m_dst[k] = TL::A_BYTES + b * 256;
+  }
+  const uint16_t* b_src[TL::LB];
+  int b_dst[TL::LB];
+#pragma unroll
+  for (int k = 0; k < TL::LB; ++k) {
+    const int b = k * 4 + wave, tk = 8 * b + (lane >> 3), pos = lane & 7;
+    const int ch = pos ^ ((tk >> 1) & 7);
+    const int64_t gt = min(t0 + tk, T - 1);
+    b_src[k] = act + gt * C + ch * 8;
+    b_dst[k] = TL::A_BYTES + TL::M_BYTES + b * 1024;
+  }
+  auto issue = [&](int c, int buf) {
+    uint8_t* base = smem + buf * TL::STAGE;
+#pragma unroll
+    for (int k = 0; k < TL::LA; ++k) dma16(a_src[k] + (int64_t)c * 32, base + a_dst[k]);
+#pragma unroll
+    for (int k = 0; k < TL::LM; ++k) dma4(m_src[k] + (int64_t)c * 2, base + m_dst[k]);
+#pragma unroll
+    for (int k = 0; k < TL::LB; ++k) dma16(b_src[k] + (int64_t)c * BC, base + b_dst[k]);
+  };
+
+  f32x4 acc[FR][FT];
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wr = wave / WT, wt = wave % WT;
+  auto compute = [&](int buf) {
+    const uint8_t* A = smem + buf * TL::STAGE;
+    const uint32_t* M = reinterpret_cast<const uint32_t*>(A + TL::A_BYTES);
+    const uint8_t* B = A + TL::A_BYTES + TL::M_BYTES;
+    bf16x16 bfr[FT];
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int tk = wt * 16 * FT + j * 16 + l16, sw = (tk >> 1) & 7;
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + ((q4 ^ sw) << 4));
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
+      bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    }
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      const int r = wr * 16 * FR + i * 16 + l16;
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + r * 64 + ((q4 ^ ((r >> 2) & 3)) << 4));
+      const int idx = (int)(M[r * 2 + (q4 >> 1)] >> (16 * (q4 & 1)));
+#pragma unroll
+      for (int j = 0; j < FT; ++j)
+        acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af, bfr[j], acc[i][j], idx, 0, 0);
+    }
+  };
+
+  constexpr int D = NS - 1;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (c_beg + d < c_end) issue(c_beg + d, d);
+  for (int c = c_beg; c < c_end; ++c) {
+    const int in_flight = min(D, c_end - c);
+    if (in_flight >= 4) wait_vm<(3 * L < 63 ? 3 * L : 63)>();
+    else if (in_flight == 3) wait_vm<2 * L>();
+    else if (in_flight == 2) wait_vm<L>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (c + D < c_end) issue(c + D, (c - c_beg + D) % NS);
+    compute((c - c_beg) % NS);
+  }
+
+  // ---- fused low-rank epilogue (first split only), dense v_mfma_f32_16x16x32_bf16:
+  //      A operand = E rows (lane: row l%16, j = 8(l/16)..+7), B operand = U^T (token l%16)
+  if (ep.r > 0 && z == 0) {
+    const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0;
+    const bool u_vec = (ep.r & 7) == 0;
+    for (int jj = 0; jj < ep.r; jj += 32) {
+      const int jb = jj + 8 * q4;
+      union UH { uint16_t h[8]; bf16x8 b; };
+      UH uhi[FT], ulo[FT];
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int64_t t = t0 + wt * 16 * FT + j * 16 + l16;
+        float u[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[q] = 0.f;
+        if (t < T) {
+          const float* up = ep.U + t * ep.r + jb;
+          if (u_vec && jb + 8 <= ep.r) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              u[q] = a0[q];
+              u[q + 4] = a1[q];
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (jb + q < ep.r) u[q] = up[q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) split_bf16(u[q], uhi[j].h[q], ulo[j].h[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int64_t row = row0 + wr * 16 * FR + i * 16 + l16;
+        union { u32x4 v; uint16_t h[8]; bf16x8 b; } x;
+        x.v = u32x4{0, 0, 0, 0};
+        if (row < R) {
+          if (e_vec && jb + 8 <= ep.r) {
+            x.v = *reinterpret_cast<const u32x4*>(ep.E + row * ep.e_row_stride + jb);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (jb + q < ep.r) x.h[q] = ep.E[row * ep.e_row_stride + (int64_t)(jb + q) * ep.e_j_stride];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, uhi[j].b, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, ulo[j].b, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- store: lane holds rows 4(l/16)..+3 of token l%16
+  const bool r4 = (R & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int64_t t = t0 + wt * 16 * FT + j * 16 + l16;
+      if (t >= T) continue;
+      const int64_t rb = row0 + wr * 16 * FR + i * 16 + 4 * q4;
+      if (part) {
+        float* o = part + ((int64_t)z * T + t) * R + rb;
+        if (r4 && rb + 3 < R) {
+          *reinterpret_cast<f32x4*>(o) = acc[i][j];
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (rb + b < R) o[b] = acc[i][j][b];
+        }
+        continue;
+      }
+      uint16_t* o = out + t * R + rb;
+      if (r4 && rb + 3 < R) {
+        u32x2 v;
+        v[0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        v[1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<u32x2*>(o) = v;
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (rb + b < R) o[b] = f32_to_bf16(acc[i][j][b]);
+      }
+    }
+}
+
+// Fixed-order sum of the S fp32 partials, rounded once to bf16.
+__global__ void k_splitk_reduce(const float* __restrict__ part, int S, int64_t n,
+                                uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 4 <= n) {
+    f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
+    for (int k = 1; k < S; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)k * n + i);
+      s += v;
+    }
+    u32x2 o;
+    o[0] = pack_bf16x2(s[0], s[1]);
+    o[1] = pack_bf16x2(s[2], s[3]);
+    *reinterpret_cast<u32x2*>(out + i) = o;
+  } else {
+    for (int64_t e = i; e < n; ++e) {
+      float s = part[e];
+      for (int k = 1; k < S; ++k) s += part[(int64_t)k * n + e];
+      out[e] = f32_to_bf16(s);
+    }
+  }
+}
+
+struct Cfg {
+  int id, br, bt;
+  bool pipe;
+};
+// register-staged (any C % 32 == 0):
+//   0 = 256x256 (4x4 accumulators per wave), 1 = 256x128 (4x2), 2 = 128x256 (2x4),
+//   3 = 128x128 (2x2), 4 = 128x64 (2x1), 5 = 64x128 (1x2)
+// LDS-DMA pipelined (C % 64 == 0):
+//   10 = 256x256 (3 stages), 11 = 256x128 (4), 12 = 128x256 (3), 13 = 128x128 (3), 14 = 128x64 (4)
+// LDS-DMA pipelined on 16x16x64 SMFMAC (C % 64 == 0):
+//   20 = 256x128 (waves 128x64, 4 stages), 21 = 128x256 (waves 64x128, 3), 22 = 256x256 (3),
+//   23 = 128x128 (waves 64x64, 3), 24 = 128x64 (waves 64x32, 4)
+constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 256, false},
+                         {3, 128, 128, false}, {4, 128, 64, false},  {5, 64, 128, false},
+                         {10, 256, 256, true}, {11, 256, 128, true}, {12, 128, 256, true},
+                         {13, 128, 128, true}, {14, 128, 64, true},
+                         {20, 256, 128, true}, {21, 128, 256, true}, {22, 256, 256, true},
+                         {23, 128, 128, true}, {24, 128, 64, true}};
+
+Cfg cfg_by_id(int id) {
+  for (const Cfg& c : kCfgs)
+    if (c.id == id) return c;
+  return kCfgs[3];
+}
+
+struct Plan {
+  Cfg cfg;
+  int splits;
+  int stages_per_split;
+};
+
+Plan plan_for(int64_t R, int64_t C, int64_t T) {
+  const int nC = (int)((C + BC - 1) / BC);
+  const bool pipe_ok = C % 64 == 0;
+  Plan p{cfg_by_id(pipe_ok ? 13 : 3), 1, nC};
+  if (T <= 0 || R <= 0 || nC <= 0) return p;
+  const char* env = getenv("SRA_SPMM24_CFG");  // tuning override: "<cfg id>[,<splits>]"
+  if (env && *env) {
+    Cfg c = cfg_by_id(atoi(env));
+    if (c.pipe && !pipe_ok) c = cfg_by_id(3);
+    p.cfg = c;
+    const char* comma = strchr(env, ',');
+    p.splits = comma ? atoi(comma + 1) : 1;
+  } else {
+    // Measured on MI355X (2:4, bf16): 256x256 tiles win once there are enough of them to fill the
+    // GPU twice; otherwise 128x128 (two workgroups per CU), splitting the reduction when even those
+    // leave CUs idle.
+    auto tiles = [&](int br, int bt) { return ((R + br - 1) / br) * ((T + bt - 1) / bt); };
+    if (pipe_ok && tiles(256, 256) >= 512) {
+      p.cfg = cfg_by_id(10);
+    } else {
+      p.cfg = cfg_by_id(pipe_ok ? 13 : 3);
+      const int64_t t = tiles(128, 128);
+      if (t < 240) {
+        int s = (int)((256 + t - 1) / t);
+        if (s > nC / 8) s = nC / 8;  // keep >= 8 stages per split
+        p.splits = s < 1 ? 1 : s;
+      }
+    }
+  }
+  if (p.splits < 1) p.splits = 1;
+  if (p.splits > nC) p.splits = nC;
+  p.stages_per_split = (nC + p.splits - 1) / p.splits;
+  p.splits = (nC + p.stages_per_split - 1) / p.stages_per_split;
+  return p;
+}
+
+template <int FR, int FT, int WR, int WT, int NS>
+void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+              const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
+              const Plan& p, hipStream_t s) {
+  using TL = QTile<FR, FT, WR, WT, NS>;
+  const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
+  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_q<FR, FT, WR, WT, NS>,
+              dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(256), 0, s, s_vals, s_meta, R,
+              C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
+}
+
+template <int FR, int FT, int WR, int WT>
+void launch_cfg(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+                const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
+                const Plan& p, hipStream_t s) {
+  using TL = Tile<FR, FT, WR, WT>;
+  const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
+  sra::launch(SRA_KERNEL_SPMM24, k_spmm24<FR, FT, WR, WT>,
+              dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(256), 0, s, s_vals, s_meta, R,
+              C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
+}
+
+template <int FR, int FT, int WR, int WT, int NS>
+void launch_pipe(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+                 const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out,
+                 float* part, const Plan& p, hipStream_t s) {
+  using TL = PTile<FR, FT, WR, WT, NS>;
+  const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
+  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_pipe<FR, FT, WR, WT, NS>,
+              dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(256), 0, s, s_vals, s_meta, R,
+              C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
+}
+
 }  // namespace
 
 namespace sra {
 
+size_t spmm24_ws(int64_t R, int64_t C, int64_t T) {
+  const Plan p = plan_for(R, C, T);
+  return p.splits > 1 ? (size_t)p.splits * T * R * sizeof(float) : 0;
+}
+
 hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
-                              hipStream_t s) {
+                              void* ws, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
-  const int n_rt = (int)((R + BR - 1) / BR), n_tt = (int)((T + BT - 1) / BT);
-  launch(SRA_KERNEL_SPMM24, k_spmm24, dim3((unsigned)(n_rt * n_tt)), dim3(256), 0, s, s_vals, s_meta, R,
-                     C, act, T, ep, out, n_rt, n_tt);
+  const Plan p = plan_for(R, C, T);
+  float* part = p.splits > 1 ? (float*)ws : nullptr;
+  switch (p.cfg.id) {
+    case 20: launch_q<8, 4, 2, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 21: launch_q<4, 8, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 22: launch_q<8, 8, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 23: launch_q<4, 4, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 24: launch_q<4, 2, 2, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 10: launch_pipe<4, 4, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 11: launch_pipe<4, 2, 2, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 12: launch_pipe<2, 4, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 13: launch_pipe<2, 2, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 14: launch_pipe<2, 1, 2, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 0: launch_cfg<4, 4, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 1: launch_cfg<4, 2, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 2: launch_cfg<2, 4, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 4: launch_cfg<2, 1, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 5: launch_cfg<1, 2, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    default: launch_cfg<2, 2, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+  }
+  if (p.splits > 1) {
+    const int64_t n = T * R;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, s,
+                       part, p.splits, n, out);
+  }
   return hipGetLastError();
 }
 

@@ -137,6 +137,19 @@ def test_fwd_validation_and_workspace(lib):
     assert st == SRA_ERR_INVALID_ARG and "A" in err(lib)
 
 
+@pytest.mark.parametrize("T", [0, 1, 7, 2048])
+@pytest.mark.parametrize("r", [0, 16, 256])
+@pytest.mark.parametrize("shape", [(4096, 1024), (1024, 4096), (32, 64), (64, 96)])
+def test_workspace_queries_any_size(lib, T, r, shape):
+    """Pure host sizing logic: never fails or traps for valid shapes, including T = 0."""
+    for dtype in (SRA_BF16, SRA_F32):
+        d = nm_desc(rows=shape[0], cols=shape[1], dtype=dtype)
+        n = ctypes.c_size_t()
+        assert lib.sra_fwd_workspace(ctypes.byref(d), T, r, ctypes.byref(n)) == SRA_OK
+        for flags in (1, 2, 4, 7, 15):
+            assert lib.sra_bwd_workspace(ctypes.byref(d), T, r, flags, ctypes.byref(n)) == SRA_OK
+
+
 def test_bwd_validation(lib):
     P = nm_desc(rows=1024, cols=4096)
     n = ctypes.c_size_t()

@@ -1,0 +1,52 @@
+"""Every tile configuration of the 2:4 SpMM (register-staged and LDS-DMA pipelined), with and
+without a split of the reduction, against the oracle on a ragged problem.
+
+Without a split every configuration performs the same SMFMAC sequence per output element, so
+results must also be bit-identical to the default plan's.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_rank_adapter_amd as sra
+from oracle import layer as olayer
+from oracle import nm as onm
+from sra_inputs import Workload, layer_inputs
+from tests._util import Report, bits, f64
+
+pytestmark = pytest.mark.gpu
+
+CFGS = [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 20, 21, 22, 23, 24]
+
+
+@pytest.fixture(scope="module")
+def problem(gpu):
+    # K % 64 == 0 so the pipelined kernels apply; T, N ragged against every tile size
+    wl = Workload("cfg", T=300, K=640, N=544, r=24, dtype="bf16", fmt="nm")
+    inp = layer_inputs(wl, seed=21)
+    X, W, A, B = (inp[k].cuda() for k in ("X", "W", "A", "B"))
+    S = sra.compress(W)
+    Y0, U0 = sra.sparse_lora_fwd(S, X, A, B)
+    torch.cuda.synchronize()
+    W64 = f64(inp["W"])
+    v, m, mask1 = onm.compress(W64, 2, 4)
+    Yo, _ = olayer.forward(f64(inp["X"]), np.where(mask1, W64, 0.0), f64(inp["A"]), f64(inp["B"]))
+    return dict(S=S, X=X, A=A, B=B, Y0=Y0, Yo=Yo)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("cfg", CFGS)
+def test_config(problem, cfg, splits):
+    os.environ["SRA_SPMM24_CFG"] = f"{cfg},{splits}"
+    try:
+        Y, _ = sra.sparse_lora_fwd(problem["S"], problem["X"], problem["A"], problem["B"])
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("SRA_SPMM24_CFG", None)
+    rep = Report(torch.bfloat16)
+    rep.add("Y", f64(Y), problem["Yo"])
+    rep.check()
+    if splits == 1:
+        assert np.array_equal(bits(Y), bits(problem["Y0"]))
