@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle sampling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the OPT-66B decode measurements appended to the training-step line")
     return ap.parse_args()
 
 
@@ -239,6 +241,62 @@ def bench_nm_layer(args, wl):
     return out, inp, dense_eq
 
 
+def decode_bytes(wl, T, kernel_only=False):
+    """Algorithmic HBM bytes of one decode forward call (or of the decode kernel alone: the
+    down-projection U = X A^T reads A in its own launch, the kernel reads U instead)."""
+    K, N, r, e = wl.K, wl.N, wl.r, 2
+    w = N * K // 2 * e + N * K // 8                      # stored values + 2-bit metadata
+    common = w + N * r * e + T * K * e + T * N * e      # + B, X, Y
+    return common + (T * r * 4 if kernel_only else r * K * e)
+
+
+def bench_decode(args, wl, Ts):
+    """Forward at decode token counts.  Two compressed copies of the weight (2 x 382 MB) are
+    alternated so that the 256 MB Infinity Cache cannot serve a repeated read; the dense
+    comparator alternates two dense copies the same way."""
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    from sparse_rank_adapter_amd._abi import SRA_KERNEL_DECODE24
+    from sra_inputs import layer_inputs
+
+    dev = torch.device("cuda:0")
+    inp = layer_inputs(wl, seed=0, T=max(Ts), with_dy=False)
+    X, W, A, B = (inp[k].to(dev) for k in ("X", "W", "A", "B"))
+    r = wl.r
+    copies = (sra.compress(W), sra.compress(W))
+    dense = (W, W.clone())
+    rows = []
+    for T in Ts:
+        Xt = X[:T].contiguous()
+        Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
+        U = torch.empty((T, r), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, sra.fwd_workspace(copies[0], T, r)), dtype=torch.uint8, device=dev)
+
+        def both():
+            for S in copies:
+                sra.sparse_lora_fwd(S, Xt, A, B, Y=Y, U=U, ws=ws)
+
+        flip = [0]
+
+        def one():
+            S = copies[flip[0] & 1]
+            flip[0] += 1
+            sra.sparse_lora_fwd(S, Xt, A, B, Y=Y, U=U, ws=ws)
+
+        call_ms = time_graph(both, args.steps, args.warmup, not args.no_graph) / 2
+        k_ms = time_kernel(SRA_KERNEL_DECODE24, one, max(20, args.steps))
+        d_ms = time_graph(lambda: [torch.nn.functional.linear(Xt, Wd) for Wd in dense], args.steps,
+                          args.warmup, not args.no_graph) / 2
+        kb = decode_bytes(wl, T, kernel_only=True)
+        rows.append({"T": T, "call_us": round(call_ms * 1e3, 2), "kernel_us": round(k_ms * 1e3, 2),
+                     "kernel_GBps": round(kb / (k_ms * 1e-3) / 1e9, 1),
+                     "kernel_frac_hbm": round(kb / (k_ms * 1e-3) / PEAK_HBM_BPS, 4),
+                     "call_GBps": round(decode_bytes(wl, T) / (call_ms * 1e-3) / 1e9, 1),
+                     "dense_us": round(d_ms * 1e3, 2), "speedup_vs_dense": round(d_ms / call_ms, 3)})
+    return rows
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,9 +310,26 @@ def main():
         sys.exit(1)
     from sra_inputs import WORKLOADS
     wl = WORKLOADS[args.workload]
-    if wl.fmt != "nm" or wl.name == "opt66b_ffn_decode":
+    if wl.name == "opt66b_ffn_decode":
+        rows = bench_decode(args, wl, (args.decode_t,))
+        d = rows[0]
+        out = {"metric": METRIC, "value": d["call_GBps"], "unit": "GB/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": d["call_us"] / 1e3,
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic",
+               "config": {"workload": wl.name, "T": args.decode_t, "K": wl.K, "N": wl.N, "r": wl.r,
+                          "sparsity": "2:4", "step": "forward (U = X A^T, Y = X Ws^T + U B^T)"},
+               "decode": rows,
+               "roofline": {"kernel": "k_decode24", "bound": "hbm", "achieved": d["kernel_GBps"],
+                            "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                            "frac": d["kernel_frac_hbm"], "traffic": None}}
+        print(json.dumps(out), flush=True)
+        return
+    if wl.fmt != "nm":
         raise SystemExit(f"workload {wl.name} is not wired into bench.py yet")
     out, inp, dense_eq = bench_nm_layer(args, wl)
+    if not args.no_decode:
+        out["decode_opt66b_ffn"] = bench_decode(args, WORKLOADS["opt66b_ffn_decode"], (1, 4, 16))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget, dense_eq)
     print(json.dumps(out), flush=True)

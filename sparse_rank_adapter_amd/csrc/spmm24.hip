@@ -785,12 +785,14 @@ struct Cfg {
 // LDS-DMA pipelined on 16x16x64 SMFMAC (C % 64 == 0):
 //   20 = 256x128 (waves 128x64, 4 stages), 21 = 128x256 (waves 64x128, 3), 22 = 256x256 (3),
 //   23 = 128x128 (waves 64x64, 3), 24 = 128x64 (waves 64x32, 4)
+// streaming decode kernel (T <= 16, one 16-token column tile, weight read once from HBM):
+//   30 = 64 weight rows per workgroup (decode24.hip)
 constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 256, false},
                          {3, 128, 128, false}, {4, 128, 64, false},  {5, 64, 128, false},
                          {10, 256, 256, true}, {11, 256, 128, true}, {12, 128, 256, true},
                          {13, 128, 128, true}, {14, 128, 64, true},
                          {20, 256, 128, true}, {21, 128, 256, true}, {22, 256, 256, true},
-                         {23, 128, 128, true}, {24, 128, 64, true}};
+                         {23, 128, 128, true}, {24, 128, 64, true},  {30, 64, 16, false}};
 
 Cfg cfg_by_id(int id) {
   for (const Cfg& c : kCfgs)
@@ -813,6 +815,7 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
   if (env && *env) {
     Cfg c = cfg_by_id(atoi(env));
     if (c.pipe && !pipe_ok) c = cfg_by_id(3);
+    if (c.id == 30 && T > 16) c = cfg_by_id(3);
     p.cfg = c;
     const char* comma = strchr(env, ',');
     p.splits = comma ? atoi(comma + 1) : 1;
@@ -821,7 +824,9 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
     // GPU twice; otherwise 128x128 (two workgroups per CU), splitting the reduction when even those
     // leave CUs idle.
     auto tiles = [&](int br, int bt) { return ((R + br - 1) / br) * ((T + bt - 1) / bt); };
-    if (pipe_ok && tiles(256, 256) >= 512) {
+    if (T <= 16) {
+      p.cfg = cfg_by_id(30);  // few tokens: bound by reading the weight once
+    } else if (pipe_ok && tiles(256, 256) >= 512) {
       p.cfg = cfg_by_id(10);
     } else {
       p.cfg = cfg_by_id(pipe_ok ? 13 : 3);
@@ -833,7 +838,7 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
       }
     }
   }
-  if (p.splits < 1) p.splits = 1;
+  if (p.splits < 1 || p.cfg.id == 30) p.splits = 1;
   if (p.splits > nC) p.splits = nC;
   p.stages_per_split = (nC + p.splits - 1) / p.splits;
   p.splits = (nC + p.stages_per_split - 1) / p.stages_per_split;
@@ -889,6 +894,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
   const Plan p = plan_for(R, C, T);
   float* part = p.splits > 1 ? (float*)ws : nullptr;
   switch (p.cfg.id) {
+    case 30: return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s);
     case 20: launch_q<8, 4, 2, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 21: launch_q<4, 8, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 22: launch_q<8, 8, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;

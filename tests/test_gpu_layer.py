@@ -90,7 +90,10 @@ def test_tiny_f32_fwd_bwd(gpu):
 
 @pytest.mark.parametrize("T,K,N,r", [(1, 64, 32, 4), (5, 64, 96, 16), (130, 192, 160, 20),
                                      (257, 128, 64, 0), (64, 256, 256, 32), (300, 64, 32, 8),
-                                     (33, 96, 64, 1), (100, 64, 96, 80), (70, 320, 192, 48)])
+                                     (33, 96, 64, 1), (100, 64, 96, 80), (70, 320, 192, 48),
+                                     # T <= 16 takes the streaming decode kernel: half 64-column
+                                     # steps (K or N % 64 == 32), ragged row tiles, 16 tokens
+                                     (3, 96, 96, 24), (16, 160, 224, 8), (1, 32, 32, 0), (16, 512, 64, 64)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ragged_shapes(gpu, T, K, N, r, dtype):
     wl = Workload("ragged", T=T, K=K, N=N, r=r, dtype=dtype, fmt="nm")
