@@ -159,6 +159,7 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
 struct BwdPlan {
   bool need_du = false, need_u = false, own_du = false, own_u = false;
   size_t u_off = 0, du_off = 0, u64_off = 0, du64_off = 0, gemm_off = 0, spmm_off = 0, total = 0;
+  size_t wt_off = 0, vtu_off = 0, vtdu_off = 0;  // packed B^T, split U^T (dB), split dU^T (dA)
 };
 
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
@@ -192,7 +193,9 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   p.own_u = p.need_u && !have_u;
   if (p.own_u) p.u_off = a.take((size_t)T * r * 4);
   if (p.own_du) p.du_off = a.take((size_t)T * r * 4);
-  if (da && r > 0) p.du64_off = a.take((size_t)T * r * 8);  // dU in fp64 feeds dA
+  if (p.need_du) p.wt_off = a.take(sra::adapter_wt_bytes(N, r));
+  if (db && r > 0) p.vtu_off = a.take(sra::adapter_vt_bytes(T, r, 3));
+  if (da && r > 0) p.vtdu_off = a.take(sra::adapter_vt_bytes(T, r, 4));  // dU (fp64 sum) split for dA
   if (P->dtype == SRA_BF16 && r > 0) {
     size_t g = 0;
     if (p.own_u) g = std::max(g, sra::adapter_rows_ws(T, K, r));
@@ -375,8 +378,8 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
                                          (float*)Y, s), s, "fwd spmm f32");
   }
   if (r > 0)
-    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, 1, r,
-                                              U, nullptr, wsb + plan.gemm_off, s), s, "fwd U"));
+    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, r, U,
+                                              nullptr, nullptr, wsb + plan.gemm_off, s), s, "fwd U"));
   sra::Epilogue ep;
   ep.U = U;
   ep.E = (const uint16_t*)B;
@@ -458,13 +461,17 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                           dA, s), s, "bwd dA"));
     return SRA_OK;
   }
-  double* dU64 = fda ? (double*)(wsb + plan.du64_off) : nullptr;
+  uint16_t* wt = plan.need_du ? (uint16_t*)(wsb + plan.wt_off) : nullptr;
+  uint16_t* vtU = fdb ? (uint16_t*)(wsb + plan.vtu_off) : nullptr;
+  uint16_t* vtdU = fda ? (uint16_t*)(wsb + plan.vtdu_off) : nullptr;
   if (plan.own_u)
-    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, 1, r,
-                                              (float*)Uv, nullptr, gws, s), s, "bwd U"));
+    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, r,
+                                              (float*)Uv, nullptr, nullptr, gws, s), s, "bwd U"));
+  SRA_TRY(hip_done(sra::launch_adapter_bwd_prep((const uint16_t*)B, N, r, wt, Uv, T, vtU, s), s,
+                   "bwd prep"));
   if (plan.need_du)
-    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)dY, T, N, (const uint16_t*)B, 1, r, r,
-                                              dU, dU64, gws, s), s, "bwd dU"));
+    SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)dY, T, N, wt, sra::packed_wt_ld(N), r,
+                                              dU, nullptr, vtdU, gws, s), s, "bwd dU"));
   if (fdx) {
     sra::Epilogue ep;
     ep.U = dU;
@@ -484,11 +491,11 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                        s, "bwd dX ffi"));
   }
   if (fdb)
-    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)dY, T, N, Uv, nullptr, r, false, dB,
-                                              gws, s), s, "bwd dB"));
+    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)dY, T, N, vtU, 3, r, false, dB, gws, s),
+                     s, "bwd dB"));
   if (fda)
-    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)X, T, K, nullptr, dU64, r, true, dA,
-                                              gws, s), s, "bwd dA"));
+    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)X, T, K, vtdU, 4, r, true, dA, gws, s),
+                     s, "bwd dA"));
   return SRA_OK;
 }
 

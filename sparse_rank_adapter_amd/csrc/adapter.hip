@@ -16,10 +16,10 @@
 // cols: Out[m][j] = sum_t Act[t][m] V[t][j].  The reduction runs over tokens, the slow dim of Act,
 //   so each 64-token x 64-column Act tile is staged in LDS as [t][m] and a lane gathers its 8
 //   tokens of one column from there.  dB and dA sum thousands of token products whose total can
-//   cancel by orders of magnitude, so V's rounding is amplified ~sqrt(T) times: a pre-pass stores
-//   V^T as bf16 parts [part][j][t] -- three parts for fp32 V (U; split error below fp32 rounding),
-//   four for the fp64 dU that the rows kernel hands over for dA -- which then read as contiguous
-//   16-byte fragments.
+//   cancel by orders of magnitude, so V's rounding is amplified ~sqrt(T) times: V^T arrives as
+//   bf16 parts [part][j][t] -- three parts for fp32 V (U, split by the backward prep kernel; split
+//   error below fp32 rounding), four for fp64 dU (written by the rows kernel that produces it) --
+//   which read as contiguous 16-byte fragments.
 // Both use v_mfma_f32_16x16x32_bf16 and move every 32-step MFMA partial into fp64 registers (fp32
 // rounding only acts inside one 32-term dot product); slices write fp64 partials that one more
 // kernel sums in a fixed order, so results are independent of scheduling.
@@ -63,13 +63,23 @@ SRA_DEV u32x4 load8(const uint16_t* __restrict__ p, int64_t i, int64_t lim, bool
 // ------------------------------------------------------------------------------------ rows
 // grid: (ceil(T/16), ceil(r/(16 JT)), S); slice z covers c in [z*c_per, min(C, (z+1)*c_per)).
 // Wave w takes the 32-column steps w, w+4, w+8, ... of its slice, UB steps per batch.
+// When vt is non-null the result is also written as V^T split into four bf16 parts,
+// vt[p][j][t] (rows rp, columns Tp; the zero padding is the caller's), ready for the cols kernel.
+SRA_DEV void write_vt4(uint16_t* __restrict__ vt, int rp, int64_t Tp, int j, int64_t t, double v) {
+  uint16_t p4[4];
+  split4_bf16(v, p4);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + t] = p4[p];
+}
+
 template <int JT, int UB>
 __global__ __launch_bounds__(256) void k_adapter_rows(const uint16_t* __restrict__ act, int64_t T,
                                                       int64_t C, const uint16_t* __restrict__ wt,
                                                       int64_t ldw, int r, int64_t c_per,
                                                       double* __restrict__ part,
                                                       float* __restrict__ out,
-                                                      double* __restrict__ out64) {
+                                                      double* __restrict__ out64,
+                                                      uint16_t* __restrict__ vt, int rp, int64_t Tp) {
   __shared__ double red[3][JT * 4][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * 16, t = t0 + lr;
@@ -131,6 +141,19 @@ __global__ __launch_bounds__(256) void k_adapter_rows(const uint16_t* __restrict
     if (b + 2 < nb) load(b + 2, fa0, fw0);
     if (b + 1 < nb) compute(b + 1, fa1, fw1);
   }
+  // V^T columns T .. Tp-1 (padding to a multiple of 8) must read as zero in the cols kernel
+  if (vt && blockIdx.z == 0 && w == 0) {
+#pragma unroll
+    for (int a = 0; a < JT; ++a) {
+      const int j = j0 + 16 * a + lr;
+      const int64_t tt = t0 + 4 * lg;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j < r && tt + e >= T && tt + e < Tp)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + tt + e] = 0;
+    }
+  }
   // waves 1..3 hand their sums to wave 0, which adds them in wave order
   if (w > 0) {
 #pragma unroll
@@ -161,30 +184,51 @@ __global__ __launch_bounds__(256) void k_adapter_rows(const uint16_t* __restrict
       } else {
         if (out) out[tt * r + j] = (float)s;
         if (out64) out64[tt * r + j] = s;
+        if (vt) write_vt4(vt, rp, Tp, j, tt, s);
       }
     }
   }
 }
 
-// wt[j][c] = src[j*sj + c*sc] for j < r, c < C, rows of stride ldw >= C (a 64 x 64 tile per
-// workgroup, transposed through LDS so that B [C x r] (sj = 1) is read and written coalesced).
-__global__ void k_pack_w(const uint16_t* __restrict__ src, int64_t C, int r, int64_t sj, int64_t sc,
-                         int64_t ldw, uint16_t* __restrict__ wt) {
+// Backward prep, one launch for two independent inputs of the adapter gradients:
+//   blocks [0, n_pack):  wt[j][c] = B[c][j] (c < C, j < r; rows of stride ldw), a 64 x 64 tile per
+//                        block transposed through LDS so reads and writes are coalesced;
+//   blocks [n_pack, ..): vt[p][j][t], U^T split into three bf16 parts (j < rp, t < Tp, zero
+//                        outside r x T), 256 entries per block.
+__global__ void k_bwd_prep(const uint16_t* __restrict__ B, int64_t C, int r, int64_t ldw,
+                           uint16_t* __restrict__ wt, int n_pack, int pack_cx,
+                           const float* __restrict__ U, int64_t T, int rp, int64_t Tp,
+                           uint16_t* __restrict__ vt) {
   __shared__ uint16_t tile[64][65];
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
-  const int j0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 256 threads: 4 rows at a time
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i;
-    const int j = j0 + tx;
-    tile[i][tx] = (c < C && j < r) ? src[(int64_t)j * sj + c * sc] : (uint16_t)0;
+  const int bid = blockIdx.x;
+  if (bid < n_pack) {
+    const int64_t c0 = (int64_t)(bid % pack_cx) * 64;
+    const int j0 = (bid / pack_cx) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 256 threads: 4 rows at a time
+    uint16_t v[16];  // all loads issued before the first LDS store
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int64_t c = c0 + ty + 4 * k;
+      const int j = j0 + tx;
+      v[k] = (c < C && j < r) ? B[c * r + j] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tile[ty + 4 * k][tx] = v[k];
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+      const int j = j0 + i;
+      const int64_t c = c0 + tx;
+      if (j < r && c < C) wt[(int64_t)j * ldw + c] = tile[tx][i];
+    }
+    return;
   }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int j = j0 + i;
-    const int64_t c = c0 + tx;
-    if (j < r && c < C) wt[(int64_t)j * ldw + c] = tile[tx][i];
-  }
+  const int64_t i = (int64_t)(bid - n_pack) * 256 + threadIdx.x;  // i = j * Tp + t
+  if (i >= (int64_t)rp * Tp) return;
+  const int j = (int)(i / Tp);
+  const int64_t t = i - (int64_t)j * Tp;
+  uint16_t p[3] = {0, 0, 0};
+  if (j < r && t < T) split3_bf16(U[t * r + j], p[0], p[1], p[2]);
+  for (int q = 0; q < 3; ++q) vt[((int64_t)q * rp + j) * Tp + t] = p[q];
 }
 
 // ------------------------------------------------------------------------------------ cols
@@ -192,22 +236,9 @@ constexpr int CS = 64;        // tokens per staged tile
 constexpr int ALD = 64 + 8;   // LDS row of the Act tile [t][m] (elements; 144 B keeps 16 B alignment)
 constexpr int VLD = CS + 8;   // LDS row of the V^T tile [j][t]
 
-// V^T parts: vt[p][j][t] for j < rp (r rounded up to 16; rows past r are 0) and t < Tp (T rounded
-// up to 8; columns past T are 0).  fp32 V -> 3 parts, fp64 V -> 4 parts.
-__global__ void k_split_vt(const float* __restrict__ V32, const double* __restrict__ V64, int64_t T,
-                           int r, int rp, int64_t Tp, uint16_t* __restrict__ vt) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // i = j * Tp + t (t fastest)
-  if (i >= (int64_t)rp * Tp) return;
-  const int j = (int)(i / Tp);
-  const int64_t t = i - (int64_t)j * Tp;
-  uint16_t p[4] = {0, 0, 0, 0};
-  if (j < r && t < T) {
-    if (V64) split4_bf16(V64[t * r + j], p);
-    else split3_bf16(V32[t * r + j], p[0], p[1], p[2]);
-  }
-  const int parts = V64 ? 4 : 3;
-  for (int q = 0; q < parts; ++q) vt[((int64_t)q * rp + j) * Tp + t] = p[q];
-}
+// V^T parts: vt[p][j][t] for j < rp (r rounded up to 16) and t < Tp (T rounded up to 8; columns
+// past T are 0).  fp32 V (U) -> 3 parts written by the backward prep kernel, fp64 V (dU) -> 4 parts
+// written by the rows kernel (or its slice reduction).
 
 // grid: (ceil(M/64), ceil(r/(16 JT)), S); slice z covers tokens [z*t_per, min(T, (z+1)*t_per)),
 // t_per % CS == 0.  Wave w owns columns m0 + 16w .. +15.
@@ -325,7 +356,8 @@ __global__ __launch_bounds__(256) void k_adapter_cols(const uint16_t* __restrict
 
 // out[i] = sum_k part[k][i], summed in slice order
 __global__ void k_reduce_parts(const double* __restrict__ part, int S, int64_t n,
-                               float* __restrict__ out, double* __restrict__ out64) {
+                               float* __restrict__ out, double* __restrict__ out64, int r,
+                               uint16_t* __restrict__ vt, int rp, int64_t Tp) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   double s = 0.0;
@@ -340,6 +372,7 @@ __global__ void k_reduce_parts(const double* __restrict__ part, int S, int64_t n
   for (; k < S; ++k) s += part[(int64_t)k * n + i];
   if (out) out[i] = (float)s;
   if (out64) out64[i] = s;
+  if (vt) write_vt4(vt, rp, Tp, (int)(i % r), i / r, s);  // rows output [T][r]
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -360,32 +393,38 @@ int64_t slice_len(int64_t blocks, int64_t len, int64_t min_len, int64_t quantum,
 }
 
 struct RowsPlan {
-  int jt, ub;
-  int64_t c_per, ldw;
-  int S;
-  bool pack;  // weight needs transposing into the workspace
-  size_t w_bytes, part_bytes;
+  int jt, ub, S;
+  int64_t c_per;
+  size_t part_bytes;
 };
 
-RowsPlan rows_plan(int64_t T, int64_t C, int r, int64_t wt_sj, int64_t wt_sc, const void* wt) {
+// Slices of the reduction: none once the token x adapter blocks fill the GPU; with a medium
+// number of blocks, slices of about 1024 columns (each wave then has two batches in flight);
+// with few blocks (decode), enough slices for ~512 workgroups.
+RowsPlan rows_plan(int64_t T, int64_t C, int r) {
   RowsPlan p;
   p.jt = pick_jt(r);
   p.ub = p.jt >= 4 ? 2 : 4;
-  // used in place when its rows are c-contiguous, 16-byte aligned and (for r > 1) 8-aligned apart
-  p.pack = !(wt_sc == 1 && (r == 1 || (wt_sj & 7) == 0) && (((uintptr_t)wt) & 15) == 0);
-  p.ldw = p.pack || r == 1 ? round_up(C, 8) : wt_sj;
-  p.w_bytes = p.pack ? align256((size_t)r * p.ldw * 2) : 0;
+  const int64_t quantum = 128 * p.ub;
   const int64_t blocks = cdiv(T, 16) * cdiv(r, 16 * p.jt);
-  p.c_per = slice_len(blocks, C, 128 * p.ub, 128 * p.ub, 512);
+  if (blocks >= 512) {
+    p.c_per = round_up(C, quantum);
+  } else if (blocks >= 64) {
+    const int64_t s1 = cdiv(C, 1024), s2 = cdiv(1024, blocks);
+    const int64_t S = s1 < s2 ? s1 : s2;
+    p.c_per = round_up(cdiv(C, S < 1 ? 1 : S), quantum);
+  } else {
+    p.c_per = slice_len(blocks, C, quantum, quantum, 512);
+  }
   p.S = (int)cdiv(C, p.c_per);
   p.part_bytes = p.S > 1 ? (size_t)p.S * T * r * sizeof(double) : 0;
   return p;
 }
 
 struct ColsPlan {
-  int jt, S, rp;
-  int64_t t_per, Tp;
-  size_t vt_bytes, part_bytes;
+  int jt, S;
+  int64_t t_per;
+  size_t part_bytes;
 };
 
 ColsPlan cols_plan(int64_t T, int64_t M, int r) {
@@ -394,9 +433,6 @@ ColsPlan cols_plan(int64_t T, int64_t M, int r) {
   const int64_t blocks = cdiv(M, 64) * cdiv(r, 16 * p.jt);
   p.t_per = slice_len(blocks, T, 128, CS, 512);
   p.S = (int)cdiv(T, p.t_per);
-  p.Tp = round_up(T, 8);
-  p.rp = (int)round_up(r, 16);
-  p.vt_bytes = align256((size_t)4 * p.rp * p.Tp * 2);
   p.part_bytes = p.S > 1 ? (size_t)p.S * M * r * sizeof(double) : 0;
   return p;
 }
@@ -404,9 +440,9 @@ ColsPlan cols_plan(int64_t T, int64_t M, int r) {
 template <int JT, int UB>
 void rows_launch(dim3 grid, hipStream_t s, const uint16_t* act, int64_t T, int64_t C,
                  const uint16_t* wt, int64_t ldw, int r, int64_t c_per, double* part, float* out,
-                 double* out64) {
+                 double* out64, uint16_t* vt, int rp, int64_t Tp) {
   sra::launch(SRA_KERNEL_ADAPTER, k_adapter_rows<JT, UB>, grid, dim3(256), 0, s, act, T, C, wt,
-              ldw, r, c_per, part, out, out64);
+              ldw, r, c_per, part, out, out64, vt, rp, Tp);
 }
 
 template <int JT>
@@ -421,74 +457,83 @@ void cols_launch(dim3 grid, hipStream_t s, const uint16_t* act, int64_t T, int64
 
 namespace sra {
 
-// The workspace size depends on the weight's strides only through whether it must be packed;
-// the query assumes it must (the larger case).
+int64_t vt_rows(int r) { return round_up(r, 16); }
+int64_t vt_cols(int64_t T) { return round_up(T, 8); }
+size_t adapter_vt_bytes(int64_t T, int r, int parts) {
+  return align256((size_t)parts * vt_rows(r) * vt_cols(T) * 2);
+}
+int64_t packed_wt_ld(int64_t C) { return round_up(C, 8); }
+size_t adapter_wt_bytes(int64_t C, int r) { return align256((size_t)r * packed_wt_ld(C) * 2); }
+
+hipError_t launch_adapter_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* wt,
+                                   const float* U, int64_t T, uint16_t* vtU, hipStream_t s) {
+  if (r == 0 || (!wt && !vtU)) return hipSuccess;
+  const int pack_cx = wt ? (int)cdiv(N, 64) : 0;
+  const int n_pack = wt ? pack_cx * (int)cdiv(r, 64) : 0;
+  const int rp = (int)vt_rows(r);
+  const int64_t Tp = vt_cols(T);
+  const int n_split = vtU ? (int)cdiv((int64_t)rp * Tp, 256) : 0;
+  if (n_pack + n_split == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)(n_pack + n_split)), dim3(256), 0, s, B, N, r,
+                     packed_wt_ld(N), wt, n_pack, pack_cx > 0 ? pack_cx : 1, U, T, rp, Tp, vtU);
+  return hipGetLastError();
+}
+
 size_t adapter_rows_ws(int64_t T, int64_t C, int r) {
   if (T <= 0 || C <= 0 || r <= 0) return 0;
-  const RowsPlan p = rows_plan(T, C, r, 1, r, nullptr);  // partial sizes do not depend on wt
-  return align256((size_t)r * round_up(C, 8) * 2) + p.part_bytes;
+  return rows_plan(T, C, r).part_bytes;
 }
 
 hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const uint16_t* wt,
-                               int64_t wt_sj, int64_t wt_sc, int r, float* out, double* out64,
+                               int64_t ldw, int r, float* out, double* out64, uint16_t* vt,
                                void* ws, hipStream_t s) {
   if (T == 0 || r == 0) return hipSuccess;
   if (C == 0) {
-    if (out64) return hipErrorInvalidValue;  // callers never ask for fp64 with an empty reduction
+    if (out64 || vt) return hipErrorInvalidValue;  // callers never ask for fp64 with an empty reduction
     return launch_fill_f32(out, T * r, 0.f, s);
   }
-  const RowsPlan p = rows_plan(T, C, r, wt_sj, wt_sc, wt);
-  uint8_t* wsb = (uint8_t*)ws;
-  const uint16_t* w = wt;
-  if (p.pack) {
-    uint16_t* wp = (uint16_t*)wsb;
-    const dim3 tg((unsigned)cdiv(C, 64), (unsigned)cdiv(r, 64));
-    hipLaunchKernelGGL(k_pack_w, tg, dim3(256), 0, s, wt, C, r, wt_sj, wt_sc, p.ldw, wp);
-    w = wp;
-  }
-  double* part = p.S > 1 ? (double*)(wsb + align256((size_t)r * round_up(C, 8) * 2)) : nullptr;
+  const RowsPlan p = rows_plan(T, C, r);
+  double* part = p.S > 1 ? (double*)ws : nullptr;
+  const int rp = (int)vt_rows(r);
+  const int64_t Tp = vt_cols(T);
   const dim3 grid((unsigned)cdiv(T, 16), (unsigned)cdiv(r, 16 * p.jt), (unsigned)p.S);
   switch (p.jt) {
-    case 1: rows_launch<1, 4>(grid, s, act, T, C, w, p.ldw, r, p.c_per, part, out, out64); break;
-    case 2: rows_launch<2, 4>(grid, s, act, T, C, w, p.ldw, r, p.c_per, part, out, out64); break;
-    default: rows_launch<4, 2>(grid, s, act, T, C, w, p.ldw, r, p.c_per, part, out, out64); break;
+    case 1: rows_launch<1, 4>(grid, s, act, T, C, wt, ldw, r, p.c_per, part, out, out64, vt, rp, Tp); break;
+    case 2: rows_launch<2, 4>(grid, s, act, T, C, wt, ldw, r, p.c_per, part, out, out64, vt, rp, Tp); break;
+    default: rows_launch<4, 2>(grid, s, act, T, C, wt, ldw, r, p.c_per, part, out, out64, vt, rp, Tp); break;
   }
   if (p.S > 1) {
     const int64_t n = T * r;
     hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, p.S,
-                       n, out, out64);
+                       n, out, out64, r, vt, rp, Tp);
   }
   return hipGetLastError();
 }
 
 size_t adapter_cols_ws(int64_t T, int64_t M, int r) {
   if (T <= 0 || M <= 0 || r <= 0) return 0;
-  const ColsPlan p = cols_plan(T, M, r);
-  return p.vt_bytes + p.part_bytes;
+  return cols_plan(T, M, r).part_bytes;
 }
 
-hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const float* V32,
-                               const double* V64, int r, bool out_transposed, float* out, void* ws,
+hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const uint16_t* vt,
+                               int parts, int r, bool out_transposed, float* out, void* ws,
                                hipStream_t s) {
   if (M == 0 || r == 0) return hipSuccess;
   if (T == 0) return launch_fill_f32(out, M * r, 0.f, s);
   const ColsPlan p = cols_plan(T, M, r);
-  uint16_t* vt = (uint16_t*)ws;
-  double* part = p.S > 1 ? (double*)((uint8_t*)ws + p.vt_bytes) : nullptr;
-  const int parts = V64 ? 4 : 3;
-  const int64_t nvt = (int64_t)p.rp * p.Tp;
-  hipLaunchKernelGGL(k_split_vt, dim3((unsigned)cdiv(nvt, 256)), dim3(256), 0, s, V32, V64, T, r,
-                     p.rp, p.Tp, vt);
+  double* part = p.S > 1 ? (double*)ws : nullptr;
+  const int rp = (int)vt_rows(r);
+  const int64_t Tp = vt_cols(T);
   const dim3 grid((unsigned)cdiv(M, 64), (unsigned)cdiv(r, 16 * p.jt), (unsigned)p.S);
   switch (p.jt) {
-    case 1: cols_launch<1>(grid, s, act, T, M, vt, parts, r, p.rp, p.Tp, p.t_per, out_transposed, part, out); break;
-    case 2: cols_launch<2>(grid, s, act, T, M, vt, parts, r, p.rp, p.Tp, p.t_per, out_transposed, part, out); break;
-    default: cols_launch<4>(grid, s, act, T, M, vt, parts, r, p.rp, p.Tp, p.t_per, out_transposed, part, out); break;
+    case 1: cols_launch<1>(grid, s, act, T, M, vt, parts, r, rp, Tp, p.t_per, out_transposed, part, out); break;
+    case 2: cols_launch<2>(grid, s, act, T, M, vt, parts, r, rp, Tp, p.t_per, out_transposed, part, out); break;
+    default: cols_launch<4>(grid, s, act, T, M, vt, parts, r, rp, Tp, p.t_per, out_transposed, part, out); break;
   }
   if (p.S > 1) {
     const int64_t n = M * r;
     hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, p.S,
-                       n, out, nullptr);
+                       n, out, nullptr, r, nullptr, 0, 0);
   }
   return hipGetLastError();
 }

@@ -139,17 +139,26 @@ hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t*
                                 hipStream_t s);
 
 // Adapter products (fp32 results):
-//   rows: out[t][j] = sum_c act[t][c] * Wt(j, c), Wt(j, c) = wt[j*wt_sj + c*wt_sc]   (U, dU)
+//   rows: out[t][j] = sum_c act[t][c] * wt[j*ldw + c]                              (U, dU)
 //   cols: out[m][j] = sum_t act[t][m] * V[t][j], written as [m][j] or transposed [j][m] (dB, dA)
-// rows also writes an fp64 copy of the result to out64 when non-null; cols reads V as fp32
-// (V32) or fp64 (V64), whichever is non-null.
+// rows also writes an fp64 copy (out64) and/or V^T split into four bf16 parts (vt) when non-null;
+// cols reads V^T as `parts` bf16 parts vt[p][j][t], rows vt_rows(r), columns vt_cols(T), zero past
+// T.  The backward prep kernel packs B^T for the dU product (wt [r][packed_wt_ld(N)]) and splits
+// U^T into three parts for dB; either output may be null.
+int64_t vt_rows(int r);
+int64_t vt_cols(int64_t T);
+size_t adapter_vt_bytes(int64_t T, int r, int parts);
+int64_t packed_wt_ld(int64_t C);
+size_t adapter_wt_bytes(int64_t C, int r);
+hipError_t launch_adapter_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* wt,
+                                   const float* U, int64_t T, uint16_t* vtU, hipStream_t s);
 size_t adapter_rows_ws(int64_t T, int64_t C, int r);
 hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const uint16_t* wt,
-                               int64_t wt_sj, int64_t wt_sc, int r, float* out, double* out64,
+                               int64_t ldw, int r, float* out, double* out64, uint16_t* vt,
                                void* ws, hipStream_t s);
 size_t adapter_cols_ws(int64_t T, int64_t M, int r);
-hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const float* V32,
-                               const double* V64, int r, bool out_transposed, float* out, void* ws,
+hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const uint16_t* vt,
+                               int parts, int r, bool out_transposed, float* out, void* ws,
                                hipStream_t s);
 
 }  // namespace sra

@@ -59,6 +59,59 @@ SRA_DEV void tile_coords(int L, int n_rt, int n_tt, int& rt, int& tt) {
   tt = in / gsize;
 }
 
+
+// Output tile staged through LDS so that global stores are whole 16-byte vectors along a token's
+// row of Y (consecutive weight rows): the MFMA accumulator layout gives each lane 4 rows of one
+// token, which written directly would be 8-byte pieces 2R bytes apart.  Layout [token][row] with a
+// 16-byte pad per token row; bf16 for the final output, fp32 for split-K partials.
+template <int BR, bool F32>
+struct OutStage {
+  static constexpr int LD = BR + (F32 ? 4 : 8);  // elements per staged token row
+  static constexpr int EV = F32 ? 4 : 8;         // elements per 16-byte vector
+  template <int BT>
+  static constexpr int bytes() { return BT * LD * (F32 ? 4 : 2); }
+  // four consecutive rows (row .. row+3) of token tok
+  static SRA_DEV void put(uint8_t* smem, int tok, int row, float v0, float v1, float v2, float v3) {
+    if constexpr (F32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(smem) + tok * LD + row) = f32x4{v0, v1, v2, v3};
+    } else {
+      u32x2 p;
+      p[0] = pack_bf16x2(v0, v1);
+      p[1] = pack_bf16x2(v2, v3);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(smem) + tok * LD + row) = p;
+    }
+  }
+  // copy the staged BT x BR tile to dst[(t0 + tok) * R + row0 + row], inside T x R
+  template <int BT>
+  static SRA_DEV void flush(const uint8_t* smem, void* dst, int64_t row0, int64_t t0, int64_t R,
+                            int64_t T) {
+    constexpr int VPR = BR / EV;
+    const bool vec = R % EV == 0;
+    for (int v = threadIdx.x; v < BT * VPR; v += blockDim.x) {
+      const int tok = v / VPR, ch = v - tok * VPR;
+      const int64_t t = t0 + tok, row = row0 + (int64_t)ch * EV;
+      if (t >= T || row >= R) continue;
+      if constexpr (F32) {
+        const float* src = reinterpret_cast<const float*>(smem) + tok * LD + ch * EV;
+        float* o = reinterpret_cast<float*>(dst) + t * R + row;
+        if (vec && row + EV <= R) {
+          *reinterpret_cast<f32x4*>(o) = *reinterpret_cast<const f32x4*>(src);
+        } else {
+          for (int e = 0; e < EV && row + e < R; ++e) o[e] = src[e];
+        }
+      } else {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(smem) + tok * LD + ch * EV;
+        uint16_t* o = reinterpret_cast<uint16_t*>(dst) + t * R + row;
+        if (vec && row + EV <= R) {
+          *reinterpret_cast<u32x4*>(o) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          for (int e = 0; e < EV && row + e < R; ++e) o[e] = src[e];
+        }
+      }
+    }
+  }
+};
+
 template <int FR, int FT, int WR, int WT>
 struct Tile {
   static constexpr int BR = 32 * FR * WR, BT = 32 * FT * WT;
@@ -496,6 +549,29 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
     }
   }
 
+  // ---- store: lane holds rows 8a+4g .. +3 of token li in each 32x32 accumulator
+  using OB = OutStage<BR, false>;
+  using OP = OutStage<BR, true>;
+  constexpr bool stage_bf16 = OB::template bytes<BT>() <= TL::LDS;
+  constexpr bool stage_f32 = OP::template bytes<BT>() <= TL::LDS;
+  if ((part && stage_f32) || (!part && stage_bf16)) {
+    __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+      for (int j = 0; j < FT; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int tok = wt * 32 * FT + j * 32 + li, row = wr * 32 * FR + i * 32 + 8 * a + 4 * g;
+          const f32x16& c = acc[i][j];
+          if (part) OP::put(smem, tok, row, c[4 * a], c[4 * a + 1], c[4 * a + 2], c[4 * a + 3]);
+          else OB::put(smem, tok, row, c[4 * a], c[4 * a + 1], c[4 * a + 2], c[4 * a + 3]);
+        }
+    __syncthreads();
+    if (part) OP::template flush<BT>(smem, part + (int64_t)z * T * R, row0, t0, R, T);
+    else OB::template flush<BT>(smem, out, row0, t0, R, T);
+    return;
+  }
   const bool r4 = (R & 3) == 0;
 #pragma unroll
   for (int i = 0; i < FR; ++i)
@@ -543,24 +619,26 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
 // holds rows 4(l/16)..+3 of token l%16.
 template <int FR, int FT, int WR, int WT, int NS>
 struct QTile {
+  static constexpr int NW = WR * WT;  // waves per workgroup: 4 or 8
   static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
-  static constexpr int LA = BR / 64, LM = BR / 128, LB = BT / 32;
+  static constexpr int LA = BR / (16 * NW), LM = BR / (32 * NW), LB = BT / (8 * NW);
   static constexpr int L = LA + LM + LB;
   static constexpr int A_BYTES = BR * 64, M_BYTES = BR * 8, B_BYTES = BT * 128;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
   static constexpr int LDS = NS * STAGE;
-  static constexpr int OCC = (FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
+  static constexpr int OCC = (NW == 8 || FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
 };
 
 template <int FR, int FT, int WR, int WT, int NS>
-__global__ __launch_bounds__(256, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm24_q(
+__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
     float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
   using TL = QTile<FR, FT, WR, WT, NS>;
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
-  static_assert(WR * WT == 4, "4 waves");
-  static_assert(BR % 128 == 0 && BT % 32 == 0, "transfer counts must be whole per wave");
+  constexpr int NW = TL::NW;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(BR % (32 * NW) == 0 && BT % (8 * NW) == 0, "transfer counts must be whole per wave");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
 
   const int tid = threadIdx.x;
@@ -578,7 +656,7 @@ __global__ __launch_bounds__(256, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
   int a_dst[TL::LA];
 #pragma unroll
   for (int k = 0; k < TL::LA; ++k) {
-    const int b = k * 4 + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
+    const int b = k * NW + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
     const int ch = pos ^ ((row >> 2) & 3);
     const int64_t grow = min(row0 + row, R - 1);
     a_src[k] = s_vals + grow * cv + ch * 8;
@@ -588,7 +666,7 @@ __global__ __launch_bounds__(256, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
   int m_dst[TL::LM];
 #pragma unroll
   for (int k = 0; k < TL::LM; ++k) {
-    const int b = k * 4 + wave, row = 32 * b + (lane >> 1);
+    const int b = k * NW + wave, row = 32 * b + (lane >> 1);
     const int64_t grow = min(row0 + row, R - 1);
     m_src[k] = s_meta + grow * cm + (lane & 1);
     m_dst[k] = TL::A_BYTES + b * 256;
@@ -597,7 +675,7 @@ __global__ __launch_bounds__(256, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
   int b_dst[TL::LB];
 #pragma unroll
   for (int k = 0; k < TL::LB; ++k) {
-    const int b = k * 4 + wave, tk = 8 * b + (lane >> 3), pos = lane & 7;
+    const int b = k * NW + wave, tk = 8 * b + (lane >> 3), pos = lane & 7;
     const int ch = pos ^ ((tk >> 1) & 7);
     const int64_t gt = min(t0 + tk, T - 1);
     b_src[k] = act + gt * C + ch * 8;
@@ -716,6 +794,290 @@ __global__ __launch_bounds__(256, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
   }
 
   // ---- store: lane holds rows 4(l/16)..+3 of token l%16
+  using OB = OutStage<BR, false>;
+  using OP = OutStage<BR, true>;
+  constexpr bool stage_bf16 = OB::template bytes<BT>() <= TL::LDS;
+  constexpr bool stage_f32 = OP::template bytes<BT>() <= TL::LDS;
+  if ((part && stage_f32) || (!part && stage_bf16)) {
+    __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int tok = wt * 16 * FT + j * 16 + l16, row = wr * 16 * FR + i * 16 + 4 * q4;
+        const f32x4& c = acc[i][j];
+        if (part) OP::put(smem, tok, row, c[0], c[1], c[2], c[3]);
+        else OB::put(smem, tok, row, c[0], c[1], c[2], c[3]);
+      }
+    __syncthreads();
+    if (part) OP::template flush<BT>(smem, part + (int64_t)z * T * R, row0, t0, R, T);
+    else OB::template flush<BT>(smem, out, row0, t0, R, T);
+    return;
+  }
+  const bool r4 = (R & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int64_t t = t0 + wt * 16 * FT + j * 16 + l16;
+      if (t >= T) continue;
+      const int64_t rb = row0 + wr * 16 * FR + i * 16 + 4 * q4;
+      if (part) {
+        float* o = part + ((int64_t)z * T + t) * R + rb;
+        if (r4 && rb + 3 < R) {
+          *reinterpret_cast<f32x4*>(o) = acc[i][j];
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (rb + b < R) o[b] = acc[i][j][b];
+        }
+        continue;
+      }
+      uint16_t* o = out + t * R + rb;
+      if (r4 && rb + 3 < R) {
+        u32x2 v;
+        v[0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        v[1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<u32x2*>(o) = v;
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (rb + b < R) o[b] = f32_to_bf16(acc[i][j][b]);
+      }
+    }
+}
+
+// Wide-stage variant (C % 128 == 0) on v_smfmac_f32_16x16x64_bf16.  Global -> LDS transfer
+// throughput of LDS-DMA on gfx950 depends on the length of the contiguous run each row
+// contributes: 128-byte runs move ~1.6x more per second than 64-byte runs and ~12x more than the
+// 8-byte metadata runs of a 64-column stage.  So a stage here is 128 logical columns (128 B of
+// stored values per weight row, 256 B per token) and metadata is fetched in super-stages of MS
+// stages (16 B per row per stage, MS*16-byte runs) into a double buffer of its own, one super-stage
+// ahead.  Swizzles: value rows chunk ^ (row & 7) (8 chunks of 16 B), token rows chunk ^ (t & 15)
+// (16 chunks), metadata rows chunk ^ ((row >> 2) & 3) (MS = 4 chunks); each keeps the 16 lanes of
+// a fragment read on distinct banks.  Operand lane layouts are the 16x16x64 ones above.
+template <int FR, int FT, int NS, int MS>
+struct WTile {
+  static constexpr int WR = 2, WT = 2;
+  static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
+  static constexpr int LA = BR / 32, LB = BT / 16;    // 1 KB transfers per wave per stage
+  static constexpr int LM = BR * MS * 16 / 4096;      // per wave per super-stage
+  static constexpr int L = LA + LB;
+  static constexpr int A_BYTES = BR * 128, B_BYTES = BT * 256, STAGE = A_BYTES + B_BYTES;
+  static constexpr int M_BYTES = BR * MS * 16;        // one metadata buffer
+  static constexpr int LDS = NS * STAGE + 2 * M_BYTES;
+};
+constexpr int BCW = 128;  // logical columns per wide stage
+
+template <int FR, int FT, int NS, int MS>
+__global__ __launch_bounds__(256, 1) void k_spmm24_w(
+    const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
+    const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
+    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
+  using TL = WTile<FR, FT, NS, MS>;
+  constexpr int BR = TL::BR, BT = TL::BT, L = TL::L, WT = TL::WT, NW = 4;
+  static_assert(MS == 4, "metadata chunk swizzle assumes 4 chunks per row");
+  static_assert(TL::LDS <= 160 * 1024, "LDS");
+  static_assert((BR * MS * 16) % 4096 == 0, "metadata transfers must be whole per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, q4 = lane >> 4, l16 = lane & 15;
+  int rt, tt;
+  tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
+  const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT;
+  const int64_t cv = C / 2, cm = C / 32;
+  const int nC_all = (int)(C / BCW);
+  const int z = blockIdx.y;
+  const int c_beg = z * stages_per_split;
+  const int c_end = min(nC_all, c_beg + stages_per_split);
+
+  // values: 1 KB block b = 8 rows x 128 B; lane -> row 8b + lane/8, slot lane%8 holds chunk slot^(row&7)
+  const uint16_t* a_src[TL::LA];
+  int a_dst[TL::LA];
+#pragma unroll
+  for (int k = 0; k < TL::LA; ++k) {
+    const int b = k * NW + wave, row = 8 * b + (lane >> 3), pos = lane & 7;
+    const int ch = pos ^ (row & 7);
+    const int64_t grow = min(row0 + row, R - 1);
+    a_src[k] = s_vals + grow * cv + ch * 8;
+    a_dst[k] = b * 1024;
+  }
+  // tokens: 1 KB block b = 4 tokens x 256 B; slot lane%16 holds chunk slot^(t&15)
+  const uint16_t* b_src[TL::LB];
+  int b_dst[TL::LB];
+#pragma unroll
+  for (int k = 0; k < TL::LB; ++k) {
+    const int b = k * NW + wave, tk = 4 * b + (lane >> 4), pos = lane & 15;
+    const int ch = pos ^ (tk & 15);
+    const int64_t gt = min(t0 + tk, T - 1);
+    b_src[k] = act + gt * C + ch * 8;
+    b_dst[k] = TL::A_BYTES + b * 1024;
+  }
+  // metadata: 1 KB block b = 16 rows x 64 B (4 stages of 16 B); slot lane%4 holds chunk
+  // slot^((row>>2)&3); chunk = stage within the super-stage
+  const uint32_t* m_row[TL::LM];
+  int m_ch[TL::LM], m_dst[TL::LM];
+#pragma unroll
+  for (int k = 0; k < TL::LM; ++k) {
+    const int b = k * NW + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
+    m_ch[k] = pos ^ ((row >> 2) & 3);
+    const int64_t grow = min(row0 + row, R - 1);
+    m_row[k] = s_meta + grow * cm;
+    m_dst[k] = b * 1024;
+  }
+  uint8_t* const mbuf = smem + NS * TL::STAGE;
+  auto issue = [&](int c, int buf) {
+    uint8_t* base = smem + buf * TL::STAGE;
+#pragma unroll
+    for (int k = 0; k < TL::LA; ++k) dma16(a_src[k] + (int64_t)c * 64, base + a_dst[k]);
+#pragma unroll
+    for (int k = 0; k < TL::LB; ++k) dma16(b_src[k] + (int64_t)c * BCW, base + b_dst[k]);
+  };
+  // super-stage g covers stages c_beg + MS*g .. +MS-1; 4 metadata words per stage.  Words past
+  // the row end (a partial last super-stage) are clamped to the row's last 16 bytes and unused.
+  auto issue_meta = [&](int g) {
+    uint8_t* base = mbuf + (g & 1) * TL::M_BYTES;
+#pragma unroll
+    for (int k = 0; k < TL::LM; ++k) {
+      int64_t w = 4 * ((int64_t)c_beg + MS * g + m_ch[k]);
+      if (w > cm - 4) w = cm - 4;
+      dma16(m_row[k] + w, base + m_dst[k]);
+    }
+  };
+
+  f32x4 acc[FR][FT];
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wr = wave / WT, wt = wave % WT;
+  auto compute = [&](int buf, int c) {
+    const uint8_t* A = smem + buf * TL::STAGE;
+    const uint8_t* B = A + TL::A_BYTES;
+    const int u = (c - c_beg) % MS;
+    const uint32_t* M = reinterpret_cast<const uint32_t*>(mbuf + (((c - c_beg) / MS) & 1) * TL::M_BYTES);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x16 bfr[FT];
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int tk = wt * 16 * FT + j * 16 + l16, sw = tk & 15;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 256 + (((8 * s + q4) ^ sw) << 4));
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 256 + (((8 * s + 4 + q4) ^ sw) << 4));
+        bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int r = wr * 16 * FR + i * 16 + l16;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + r * 128 + (((4 * s + q4) ^ (r & 7)) << 4));
+        const int word = ((u ^ ((r >> 2) & 3)) << 2) + 2 * s + (q4 >> 1);
+        const int idx = (int)(M[r * (MS * 4) + word] >> (16 * (q4 & 1)));
+#pragma unroll
+        for (int j = 0; j < FT; ++j)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af, bfr[j], acc[i][j], idx, 0, 0);
+      }
+    }
+  };
+
+  constexpr int D = NS - 1;
+  if (c_beg < c_end) issue_meta(0);
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (c_beg + d < c_end) issue(c_beg + d, d);
+  for (int c = c_beg; c < c_end; ++c) {
+    // stages c .. c+in_flight-1 and every earlier transfer (metadata included) are issued; waiting
+    // for at most (in_flight-1)*L outstanding completes stage c and all older metadata
+    const int in_flight = min(D, c_end - c);
+    if (in_flight >= 3) wait_vm<(2 * L < 63 ? 2 * L : 63)>();
+    else if (in_flight == 2) wait_vm<L>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // stage c visible; stage c-1 and its super-stage reads done
+    const int rel = c - c_beg;
+    if (rel % MS == 0 && c + MS < c_end) issue_meta(rel / MS + 1);
+    if (c + D < c_end) issue(c + D, (rel + D) % NS);
+    compute(rel % NS, c);
+  }
+
+  // ---- fused low-rank epilogue (first split only), dense v_mfma_f32_16x16x32_bf16:
+  //      A operand = E rows (lane: row l%16, j = 8(l/16)..+7), B operand = U^T (token l%16)
+  if (ep.r > 0 && z == 0) {
+    const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0;
+    const bool u_vec = (ep.r & 7) == 0;
+    for (int jj = 0; jj < ep.r; jj += 32) {
+      const int jb = jj + 8 * q4;
+      union UH { uint16_t h[8]; bf16x8 b; };
+      UH uhi[FT], ulo[FT];
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int64_t t = t0 + wt * 16 * FT + j * 16 + l16;
+        float u[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[q] = 0.f;
+        if (t < T) {
+          const float* up = ep.U + t * ep.r + jb;
+          if (u_vec && jb + 8 <= ep.r) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              u[q] = a0[q];
+              u[q + 4] = a1[q];
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (jb + q < ep.r) u[q] = up[q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) split_bf16(u[q], uhi[j].h[q], ulo[j].h[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int64_t row = row0 + wr * 16 * FR + i * 16 + l16;
+        union { u32x4 v; uint16_t h[8]; bf16x8 b; } x;
+        x.v = u32x4{0, 0, 0, 0};
+        if (row < R) {
+          if (e_vec && jb + 8 <= ep.r) {
+            x.v = *reinterpret_cast<const u32x4*>(ep.E + row * ep.e_row_stride + jb);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (jb + q < ep.r) x.h[q] = ep.E[row * ep.e_row_stride + (int64_t)(jb + q) * ep.e_j_stride];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, uhi[j].b, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, ulo[j].b, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- store: lane holds rows 4(l/16)..+3 of token l%16
+  using OB = OutStage<BR, false>;
+  using OP = OutStage<BR, true>;
+  constexpr bool stage_bf16 = OB::template bytes<BT>() <= TL::LDS;
+  constexpr bool stage_f32 = OP::template bytes<BT>() <= TL::LDS;
+  if ((part && stage_f32) || (!part && stage_bf16)) {
+    __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int tok = wt * 16 * FT + j * 16 + l16, row = wr * 16 * FR + i * 16 + 4 * q4;
+        const f32x4& c = acc[i][j];
+        if (part) OP::put(smem, tok, row, c[0], c[1], c[2], c[3]);
+        else OB::put(smem, tok, row, c[0], c[1], c[2], c[3]);
+      }
+    __syncthreads();
+    if (part) OP::template flush<BT>(smem, part + (int64_t)z * T * R, row0, t0, R, T);
+    else OB::template flush<BT>(smem, out, row0, t0, R, T);
+    return;
+  }
   const bool r4 = (R & 3) == 0;
 #pragma unroll
   for (int i = 0; i < FR; ++i)
@@ -776,6 +1138,7 @@ __global__ void k_splitk_reduce(const float* __restrict__ part, int S, int64_t n
 struct Cfg {
   int id, br, bt;
   bool pipe;
+  int width = 64;  // logical columns per stage
 };
 // register-staged (any C % 32 == 0):
 //   0 = 256x256 (4x4 accumulators per wave), 1 = 256x128 (4x2), 2 = 128x256 (2x4),
@@ -785,6 +1148,10 @@ struct Cfg {
 // LDS-DMA pipelined on 16x16x64 SMFMAC (C % 64 == 0):
 //   20 = 256x128 (waves 128x64, 4 stages), 21 = 128x256 (waves 64x128, 3), 22 = 256x256 (3),
 //   23 = 128x128 (waves 64x64, 3), 24 = 128x64 (waves 64x32, 4)
+// wide stages (128 columns, C % 128 == 0) on 16x16x64 SMFMAC, metadata in 4-stage super-stages:
+//   40 = 256x128 (waves 128x64, 2 stages), 41 = 128x128 (waves 64x64, 3), 44 = 256x64 (waves 128x32, 2)
+// eight waves (512 threads) on 16x16x64 SMFMAC, 64-column stages:
+//   50 = 256x128 (4x2 waves of 64x64, 4 stages), 51 = 256x256 (4x2 waves of 64x128, 3)
 // streaming decode kernel (T <= 16, one 16-token column tile, weight read once from HBM):
 //   30 = 64 weight rows per workgroup (decode24.hip)
 constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 256, false},
@@ -792,7 +1159,9 @@ constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 25
                          {10, 256, 256, true}, {11, 256, 128, true}, {12, 128, 256, true},
                          {13, 128, 128, true}, {14, 128, 64, true},
                          {20, 256, 128, true}, {21, 128, 256, true}, {22, 256, 256, true},
-                         {23, 128, 128, true}, {24, 128, 64, true},  {30, 64, 16, false}};
+                         {23, 128, 128, true}, {24, 128, 64, true},  {30, 64, 16, false},
+                         {40, 256, 128, true, 128}, {41, 128, 128, true, 128},
+                         {44, 256, 64, true, 128}, {50, 256, 128, true}, {51, 256, 256, true}};
 
 Cfg cfg_by_id(int id) {
   for (const Cfg& c : kCfgs)
@@ -807,37 +1176,41 @@ struct Plan {
 };
 
 Plan plan_for(int64_t R, int64_t C, int64_t T) {
-  const int nC = (int)((C + BC - 1) / BC);
-  const bool pipe_ok = C % 64 == 0;
-  Plan p{cfg_by_id(pipe_ok ? 13 : 3), 1, nC};
-  if (T <= 0 || R <= 0 || nC <= 0) return p;
+  const bool pipe_ok = C % 64 == 0, wide_ok = C % 128 == 0;
+  Plan p{cfg_by_id(pipe_ok ? 13 : 3), 1, 1};
+  if (T <= 0 || R <= 0 || C <= 0) return p;
   const char* env = getenv("SRA_SPMM24_CFG");  // tuning override: "<cfg id>[,<splits>]"
   if (env && *env) {
     Cfg c = cfg_by_id(atoi(env));
+    if (c.width == 128 && !wide_ok) c = cfg_by_id(pipe_ok ? 13 : 3);
     if (c.pipe && !pipe_ok) c = cfg_by_id(3);
     if (c.id == 30 && T > 16) c = cfg_by_id(3);
     p.cfg = c;
     const char* comma = strchr(env, ',');
     p.splits = comma ? atoi(comma + 1) : 1;
   } else {
-    // Measured on MI355X (2:4, bf16): 256x256 tiles win once there are enough of them to fill the
-    // GPU twice; otherwise 128x128 (two workgroups per CU), splitting the reduction when even those
-    // leave CUs idle.
+    // Measured on MI355X (2:4, bf16): eight-wave 256x256 tiles win once there are enough of them
+    // to fill the GPU twice, eight-wave 256x128 once those fill it; otherwise 128x128 (two
+    // workgroups per CU), splitting the reduction when even those leave CUs idle.
     auto tiles = [&](int br, int bt) { return ((R + br - 1) / br) * ((T + bt - 1) / bt); };
     if (T <= 16) {
       p.cfg = cfg_by_id(30);  // few tokens: bound by reading the weight once
     } else if (pipe_ok && tiles(256, 256) >= 512) {
-      p.cfg = cfg_by_id(10);
+      p.cfg = cfg_by_id(51);
+    } else if (pipe_ok && tiles(256, 128) >= 240) {
+      p.cfg = cfg_by_id(50);
     } else {
       p.cfg = cfg_by_id(pipe_ok ? 13 : 3);
       const int64_t t = tiles(128, 128);
       if (t < 240) {
+        const int nC = (int)((C + p.cfg.width - 1) / p.cfg.width);
         int s = (int)((256 + t - 1) / t);
         if (s > nC / 8) s = nC / 8;  // keep >= 8 stages per split
         p.splits = s < 1 ? 1 : s;
       }
     }
   }
+  const int nC = (int)((C + p.cfg.width - 1) / p.cfg.width);
   if (p.splits < 1 || p.cfg.id == 30) p.splits = 1;
   if (p.splits > nC) p.splits = nC;
   p.stages_per_split = (nC + p.splits - 1) / p.splits;
@@ -852,7 +1225,7 @@ void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t
   using TL = QTile<FR, FT, WR, WT, NS>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
   sra::launch(SRA_KERNEL_SPMM24, k_spmm24_q<FR, FT, WR, WT, NS>,
-              dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(256), 0, s, s_vals, s_meta, R,
+              dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(64 * TL::NW), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
 
@@ -863,6 +1236,17 @@ void launch_cfg(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64
   using TL = Tile<FR, FT, WR, WT>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
   sra::launch(SRA_KERNEL_SPMM24, k_spmm24<FR, FT, WR, WT>,
+              dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(256), 0, s, s_vals, s_meta, R,
+              C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
+}
+
+template <int FR, int FT, int NS, int MS>
+void launch_w(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+              const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
+              const Plan& p, hipStream_t s) {
+  using TL = WTile<FR, FT, NS, MS>;
+  const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
+  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_w<FR, FT, NS, MS>,
               dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(256), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
@@ -895,6 +1279,11 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
   float* part = p.splits > 1 ? (float*)ws : nullptr;
   switch (p.cfg.id) {
     case 30: return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s);
+    case 50: launch_q<4, 4, 4, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 51: launch_q<4, 8, 4, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 40: launch_w<8, 4, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 41: launch_w<4, 4, 3, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 44: launch_w<8, 2, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 20: launch_q<8, 4, 2, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 21: launch_q<4, 8, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 22: launch_q<8, 8, 2, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;

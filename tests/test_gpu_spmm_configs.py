@@ -1,4 +1,4 @@
-"""Every tile configuration of the 2:4 SpMM (register-staged and LDS-DMA pipelined), with and
+"""Every tile configuration of the 2:4 SpMM (register-staged, LDS-DMA pipelined, wide-stage), with and
 without a split of the reduction, against the oracle on a ragged problem.
 
 Without a split every configuration performs the same SMFMAC sequence per output element, so
@@ -18,7 +18,7 @@ from tests._util import Report, bits, f64
 
 pytestmark = pytest.mark.gpu
 
-CFGS = [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 20, 21, 22, 23, 24]
+CFGS = [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 20, 21, 22, 23, 24, 40, 41, 44, 50, 51]
 
 
 @pytest.fixture(scope="module")
