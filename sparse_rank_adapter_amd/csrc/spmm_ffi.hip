@@ -1,35 +1,173 @@
 // bf16 fixed fan-in SpMM with the low-rank epilogue (SQuAsh project update: fixed fan-in sparse
-// weights; SLoPe paperlayer summary §2.3 keeps the weight and its transpose).
+// weights, applied with the activations resident in LDS and a per-row loop over (index, value)
+// pairs; SLoPe paperlayer summary §2.3 keeps the weight and its transpose).
 //   forward  (ELL, rows = N):  Y[t][n]  = sum_j X[t][col(n,j)] val(n,j) + sum_j U[t][j] B[n][j]
 //   backward (CSR, rows = K):  dX[t][k] = sum_e dY[t][row(e)] val(e)    + sum_j dU[t][j] A[j][k]
-// Gather form: one lane per output element, fp32 accumulation.
+//
+// With ~10% of the columns kept at arbitrary positions there is no dense sub-block for MFMA, and
+// every product needs one activation value picked by the stored index: the kernel is bound by
+// those picks (LDS) and by the VALU.  A workgroup owns 64 tokens (one per lane) and 64 sparse rows
+// (16 per wave).  The activations of its tokens are staged in LDS one 256-column chunk at a time
+// as [column][token], so the pick for a stored index is one 128-byte row read by the whole wave
+// without bank conflicts; the LDS footprint stays small so that several workgroups share a CU.  A row's (index, value) pairs are fetched 64 at a time, one per lane,
+// and broadcast with v_readlane; indices ascend within a row, so each row keeps a cursor into its
+// list from chunk to chunk.  Accumulation is fp32; the adapter term is added in fp32 from the fp32
+// U, and the output tile goes out through LDS as contiguous row segments of Y.
 #include "common.h"
 
 namespace {
 
-__global__ __launch_bounds__(256) void k_spmm_ffi_gather(int format, const uint16_t* __restrict__ vals,
-                                                         const int16_t* __restrict__ idx,
-                                                         const int32_t* __restrict__ row_ptr, int k,
-                                                         int64_t R, int64_t C,
-                                                         const uint16_t* __restrict__ act, int64_t T,
-                                                         sra::Epilogue ep, uint16_t* __restrict__ out) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= T * R) return;
-  const int64_t t = id / R, row = id - t * R;
-  const uint16_t* a = act + t * C;
-  float acc = 0.f;
-  int64_t b, e;
-  if (format == SRA_FMT_ELL) {
-    b = row * k;
-    e = b + k;
-  } else {
-    b = row_ptr[row];
-    e = row_ptr[row + 1];
+constexpr int TT = 64;     // tokens per workgroup (one per lane)
+constexpr int RPW = 16;    // sparse rows per wave
+constexpr int RB = 4 * RPW;
+constexpr int KC = 256;    // activation columns per LDS chunk (32 KB)
+
+__global__ __launch_bounds__(256) void k_spmm_ffi(int format, const uint16_t* __restrict__ vals,
+                                                  const int16_t* __restrict__ idx,
+                                                  const int32_t* __restrict__ row_ptr, int k,
+                                                  int64_t R, int64_t C,
+                                                  const uint16_t* __restrict__ act, int64_t T,
+                                                  sra::Epilogue ep, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[KC * TT];  // [column][token]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: row addresses go scalar
+  const int64_t t0 = (int64_t)blockIdx.x * TT, rw0 = (int64_t)blockIdx.y * RB + w * RPW;
+  const int64_t t = t0 + lane;
+  const bool c_vec = (C & 7) == 0;
+
+  // per-row state: running sums in registers (one per row and token), cursor and end of each row's
+  // list (wave-uniform, so scalar registers); the row loop is unrolled
+  float acc[RPW];
+  int cur[RPW], fin[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int64_t row = rw0 + i;
+    acc[i] = 0.f;
+    int b = 0, e = 0;
+    if (row < R) {
+      if (format == SRA_FMT_ELL) {
+        b = (int)(row * k);
+        e = b + k;
+      } else {
+        b = row_ptr[row];
+        e = row_ptr[row + 1];
+      }
+    }
+    cur[i] = b;
+    fin[i] = e;
   }
-  for (int64_t q = b; q < e; ++q) acc += bf16_to_f32(a[idx[q]]) * bf16_to_f32(vals[q]);
-  for (int j = 0; j < ep.r; ++j)
-    acc += ep.U[t * ep.r + j] * bf16_to_f32(ep.E[row * ep.e_row_stride + (int64_t)j * ep.e_j_stride]);
-  out[id] = f32_to_bf16(acc);
+
+  for (int64_t c0 = 0; c0 < C; c0 += KC) {
+    __syncthreads();  // the previous chunk has been consumed
+    // stage X[t0 .. t0+63][c0 .. c0+KC) as xs[c][t]: lane -> (token, 8 consecutive columns);
+    // consecutive lanes take consecutive tokens, so the transposing 2-byte LDS writes of a wave
+    // fall on distinct banks
+    for (int v = tid; v < TT * (KC / 8); v += 256) {
+      const int tok = v % TT, cc = (v / TT) * 8;
+      union { u32x4 v; uint16_t h[8]; } x;
+      x.v = u32x4{0, 0, 0, 0};
+      const int64_t tg = t0 + tok, cg = c0 + cc;
+      if (tg < T && cg < C) {
+        const uint16_t* p = act + tg * C + cg;
+        if (c_vec && cg + 8 <= C) {
+          x.v = *reinterpret_cast<const u32x4*>(p);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (cg + q < C) x.h[q] = p[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xs[(cc + q) * TT + tok] = x.h[q];
+    }
+    __syncthreads();
+    const int cend = (int)(C - c0 < KC ? C - c0 : KC);  // columns of this chunk
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      int e = cur[i];
+      const int ee = fin[i];
+      float a = acc[i];
+      while (e < ee) {
+        // pairs e .. e+63, one per lane: index in the low half, bf16 value in the high half
+        const int ej = e + lane;
+        const uint32_t pk = ej < ee ? (uint32_t)(uint16_t)idx[ej] | ((uint32_t)vals[ej] << 16) : 0u;
+        const int n = ee - e < 64 ? ee - e : 64;
+        int j = 0;
+        // four pairs at a time while the fourth still lies in this chunk (indices ascend), so
+        // four LDS picks are in flight together
+        for (; j + 4 <= n; j += 4) {
+          const uint32_t e3 = __builtin_amdgcn_readlane(pk, j + 3);
+          if ((int)(e3 & 0xFFFFu) - (int)c0 >= cend) break;
+          uint32_t en[4];
+          en[0] = __builtin_amdgcn_readlane(pk, j);
+          en[1] = __builtin_amdgcn_readlane(pk, j + 1);
+          en[2] = __builtin_amdgcn_readlane(pk, j + 2);
+          en[3] = e3;
+          float x[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = bf16_to_f32(xs[((int)(en[q] & 0xFFFFu) - (int)c0) * TT + lane]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a += x[q] * __uint_as_float(en[q] & 0xFFFF0000u);
+        }
+        for (; j < n; ++j) {
+          const uint32_t ent = __builtin_amdgcn_readlane(pk, j);
+          const int col = (int)(ent & 0xFFFFu) - (int)c0;
+          if (col >= cend) break;  // the rest of the row lies in later chunks
+          a += bf16_to_f32(xs[col * TT + lane]) * __uint_as_float(ent & 0xFFFF0000u);
+        }
+        e += j;
+        if (j < n) break;
+      }
+      acc[i] = a;
+      cur[i] = e;
+    }
+  }
+
+  // adapter term: acc[i] += sum_j U[t][j] E(row_i, j), two adapter columns at a time (E is read
+  // as scalars: 2 x 16 per step)
+  if (ep.r > 0) {
+    const bool t_ok = t < T;
+#pragma unroll 1
+    for (int j0 = 0; j0 < ep.r; j0 += 2) {
+      float u[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) u[q] = (t_ok && j0 + q < ep.r) ? ep.U[t * ep.r + j0 + q] : 0.f;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int64_t row = rw0 + i;
+        if (row >= R) continue;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          if (j0 + q < ep.r)
+            acc[i] += u[q] * bf16_to_f32(ep.E[row * ep.e_row_stride + (int64_t)(j0 + q) * ep.e_j_stride]);
+      }
+    }
+  }
+
+  // store through LDS: tile [token][row] bf16, then each token's 64 rows as one 128-byte segment
+  __syncthreads();
+  uint16_t* ot = xs;  // [TT][RB + 8]
+  constexpr int OLD = RB + 8;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) ot[lane * OLD + w * RPW + i] = f32_to_bf16(acc[i]);
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.y * RB;
+  const bool r_vec = (R & 7) == 0;
+  for (int v = tid; v < TT * (RB / 8); v += 256) {
+    const int tok = v / (RB / 8), rr = (v % (RB / 8)) * 8;
+    const int64_t tg = t0 + tok, row = r0 + rr;
+    if (tg >= T || row >= R) continue;
+    uint16_t* o = out + tg * R + row;
+    const uint16_t* src = ot + tok * OLD + rr;
+    if (r_vec && row + 8 <= R) {
+      union { u32x4 v; uint16_t h[8]; } x;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x.h[q] = src[q];
+      *reinterpret_cast<u32x4*>(o) = x.v;
+    } else {
+      for (int q = 0; q < 8 && row + q < R; ++q) o[q] = src[q];
+    }
+  }
 }
 
 }  // namespace
@@ -40,10 +178,10 @@ hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t*
                                 const int32_t* row_ptr, int k, int64_t R, int64_t C,
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                                 hipStream_t s) {
-  const int64_t n = T * R;
-  if (n == 0) return hipSuccess;
-  launch(SRA_KERNEL_SPMM_FFI, k_spmm_ffi_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, format,
-                     vals, idx, row_ptr, k, R, C, act, T, ep, out);
+  if (T == 0 || R == 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + TT - 1) / TT), (unsigned)((R + RB - 1) / RB));
+  launch(SRA_KERNEL_SPMM_FFI, k_spmm_ffi, grid, dim3(256), 0, s, format, vals, idx, row_ptr, k, R,
+         C, act, T, ep, out);
   return hipGetLastError();
 }
 
