@@ -32,6 +32,17 @@ PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA (published); 2:4 work is pri
 PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E (published)
 PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of `bench.py --loop
+# <call>` (profiles/opt350m_fc1_spmm24_traffic.md, profiles/opt66b_ffn_decode_traffic.md), each
+# counter scaled by the factor that makes a plain 256 MiB elementwise copy read and write 256 MiB
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the kernel configuration the planner picks for
+# that call; a key missing here (kernel changed since the counters were taken) reports null.
+TRAFFIC_BYTES = {
+    "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,2,2,2,3>,split2": 26905.6 * 1024 * 2.0 + 16384.0 * 1024,
+    "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,4>": 13812.9 * 1024 * 2.0 + 16384.0 * 1024,
+    "opt66b_ffn_decode/T16/k_decode24": 196310.1 * 1024 * 2.0 + 1152.5 * 1024,
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -44,6 +55,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle sampling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loop", choices=["spmm_fwd", "spmm_bwd", "decode", "copy"], default=None,
+                    help="run one call of the default workload --steps times and exit (for "
+                         "rocprofv3 counter runs); 'copy' copies 256 MiB (counter calibration)")
     ap.add_argument("--no-ffi", action="store_true",
                     help="skip the fixed fan-in (90% sparse) layer measured beside the main line")
     ap.add_argument("--no-decode", action="store_true",
@@ -227,8 +241,11 @@ def bench_nm_layer(args, wl):
     spmm_flops_bwd = 2 * T * wl.K * (wl.N // 2) + 2 * T * r * wl.K
     if k_bwd >= k_fwd:
         kname, kms, kflops = "k_spmm24 (backward dX = dY P^T + dU A)", k_bwd, spmm_flops_bwd
+        tkey = f"{wl.name}/spmm24_bwd/k_spmm24_pipe<2,2,2,2,3>,split2"
     else:
         kname, kms, kflops = "k_spmm24 (forward Y = X Ws^T + U B^T)", k_fwd, spmm_flops_fwd
+        tkey = f"{wl.name}/spmm24_fwd/k_spmm24_q<4,4,4,2,4>"
+    traffic = TRAFFIC_BYTES.get(tkey)
     achieved = kflops / (kms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -257,7 +274,8 @@ def bench_nm_layer(args, wl):
                       "compress": round(k_cmp, 5), "double_prune": round(k_dp, 5)},
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4), "traffic": None},
+                     "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4),
+                     "traffic": round(traffic) if traffic else None},
     }
     return out, inp, dense_eq
 
@@ -369,6 +387,41 @@ def bench_ffi(args, wl):
             "compress_ffi_ms": round(ms_setup, 5)}
 
 
+def loop_calls(args):
+    """Repeat one call for counter collection: no timing, no output but a last line."""
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    from sra_inputs import WORKLOADS, layer_inputs
+
+    dev = torch.device("cuda:0")
+    if args.loop == "copy":
+        # a plain elementwise kernel that reads 256 MiB and writes 256 MiB
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(f"copy 256 MiB x {args.steps}", flush=True)
+        return
+    wl = WORKLOADS["opt66b_ffn_decode" if args.loop == "decode" else args.workload]
+    T = args.decode_t if args.loop == "decode" else wl.T
+    inp = layer_inputs(wl, seed=0, T=T, with_dy=args.loop == "spmm_bwd")
+    X, W, A, B = (inp[k].to(dev) for k in ("X", "W", "A", "B"))
+    S = sra.compress(W)
+    Y, U = sra.sparse_lora_fwd(S, X, A, B)
+    if args.loop == "spmm_bwd":
+        P = sra.double_prune(S)
+        dY = inp["dY"].to(dev)
+        for _ in range(args.steps):
+            sra.sparse_lora_bwd(P, dY, X, U, A, B)
+    else:
+        for _ in range(args.steps):
+            sra.sparse_lora_fwd(S, X, A, B, Y=Y, U=U)
+    torch.cuda.synchronize()
+    print(f"{args.loop} {wl.name} T={T} x {args.steps}", flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -380,6 +433,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.loop:
+        loop_calls(args)
+        return
     from sra_inputs import WORKLOADS
     wl = WORKLOADS[args.workload]
     if wl.name == "opt66b_ffn_decode":
@@ -394,7 +450,8 @@ def main():
                "decode": rows,
                "roofline": {"kernel": "k_decode24", "bound": "hbm", "achieved": d["kernel_GBps"],
                             "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
-                            "frac": d["kernel_frac_hbm"], "traffic": None}}
+                            "frac": d["kernel_frac_hbm"],
+                            "traffic": TRAFFIC_BYTES.get(f"{wl.name}/T{args.decode_t}/k_decode24")}}
         print(json.dumps(out), flush=True)
         return
     if wl.fmt != "nm":
