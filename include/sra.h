@@ -120,6 +120,18 @@ sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols
 sra_status sra_double_prune(const sra_sparse* Ws /* host */, sra_sparse* P /* host */, void* stream);
 
 /*
+ * compress_pair -- sra_compress followed by sra_double_prune in one pass over W, with bit-identical
+ * results: for training loops that refresh both compressed forms of a weight after every update
+ * (SLoPe §2.3 keeps compressed formats of the weight and of its transpose; the masks stay fixed).
+ * Ws receives compress(W) (rows x cols), P receives double_prune(Ws) (cols x rows); the caller
+ * sets the values and meta pointers of both, the call fills the other fields.
+ * Supported: 2:4, rows % 32 == 0, cols % 32 == 0.
+ */
+sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
+                             int32_t m, sra_sparse* Ws /* host */, sra_sparse* P /* host */,
+                             void* stream);
+
+/*
  * compress_ffi(W, k) -- fixed fan-in selection (SQuAsh project update): every row of W
  * [rows, cols] keeps its k largest-magnitude entries.  out->values [rows, k] and out->index
  * (int16) [rows, k] with columns ascending; set by the caller, other fields filled by the call.
@@ -190,7 +202,7 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, c
 
 /* Kernel classes for sra_time_next_kernel. */
 enum {
-  SRA_KERNEL_COMPRESS = 1,     /* 2:4 compression (sra_compress) */
+  SRA_KERNEL_COMPRESS = 1,     /* 2:4 compression (sra_compress, sra_compress_pair) */
   SRA_KERNEL_DOUBLE_PRUNE = 2, /* sra_double_prune */
   SRA_KERNEL_SPMM24 = 3,       /* bf16 2:4 SpMM + fused adapter epilogue (forward Y, backward dX) */
   SRA_KERNEL_ADAPTER = 4,      /* adapter products U, dU, dB, dA (one launch each) */

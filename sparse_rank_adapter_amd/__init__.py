@@ -4,6 +4,6 @@ The compute lives in ``libsra.so`` (hand-written HIP for gfx950, C ABI in ``incl
 this package only marshals torch tensors into those calls.  Importing it does not load the
 library; the first call does, and raises if it has not been built.
 """
-from .api import (SparseMatrix, bwd_workspace, compress, compress_ffi,  # noqa: F401
+from .api import (SparseMatrix, bwd_workspace, compress, compress_ffi, compress_pair,  # noqa: F401
                   double_prune, ffi_transpose, fwd_workspace, meta_words, sparse_lora_bwd,
                   sparse_lora_fwd, time_next_kernel)

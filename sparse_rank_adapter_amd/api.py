@@ -101,6 +101,28 @@ def double_prune(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMat
     return P
 
 
+def compress_pair(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | None = None):
+    """(compress(W), double_prune(compress(W))) in one pass over W; `out` = (Ws, P) reuses buffers."""
+    lib = load()
+    _dev(W)
+    rows, cols = W.shape
+    if out is None:
+        Ws = SparseMatrix(SRA_FMT_NM, W.dtype, rows, cols,
+                          torch.empty((rows, cols // m * n), dtype=W.dtype, device=W.device),
+                          meta=torch.empty((rows, meta_words(cols, n, m)), dtype=torch.int32, device=W.device),
+                          n=n, m=m)
+        P = SparseMatrix(SRA_FMT_NM, W.dtype, cols, rows,
+                         torch.empty((cols, rows // m * n), dtype=W.dtype, device=W.device),
+                         meta=torch.empty((cols, meta_words(rows, n, m)), dtype=torch.int32, device=W.device),
+                         n=n, m=m)
+    else:
+        Ws, P = out
+    dw, dp = Ws.desc(), P.desc()
+    check("sra_compress_pair", lib.sra_compress_pair(_p(W), _dt(W), rows, cols, n, m, ctypes.byref(dw),
+                                                     ctypes.byref(dp), _stream(W.device)))
+    return Ws, P
+
+
 def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:
     """compress_ffi(W, k): keep the k largest-magnitude entries of every row (ELL, int16 columns)."""
     lib = load()

@@ -289,6 +289,32 @@ sra_status sra_double_prune(const sra_sparse* Ws, sra_sparse* P, void* stream) {
                   s, "double_prune");
 }
 
+sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
+                             int32_t m, sra_sparse* Ws, sra_sparse* P, void* stream) {
+  SRA_TRY(check_dtype(dtype));
+  SRA_TRY(check_nm(rows, cols, n, m));
+  SRA_TRY(check_nm(cols, rows, n, m));  // the second prune groups along rows
+  if (!Ws || !P) return fail(SRA_ERR_INVALID_ARG, "output descriptor is NULL");
+  const bool any = rows > 0 && cols > 0;
+  SRA_TRY(check_ptr(W, any, "W"));
+  SRA_TRY(check_ptr(Ws->values, any, "Ws->values"));
+  SRA_TRY(check_ptr(Ws->meta, any, "Ws->meta"));
+  SRA_TRY(check_ptr(P->values, any, "P->values"));
+  SRA_TRY(check_ptr(P->meta, any, "P->meta"));
+  Ws->format = P->format = SRA_FMT_NM;
+  Ws->dtype = P->dtype = dtype;
+  Ws->rows = rows;
+  Ws->cols = cols;
+  P->rows = cols;
+  P->cols = rows;
+  Ws->n = P->n = n;
+  Ws->m = P->m = m;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_compress_pair24(dtype, W, rows, cols, Ws->values, Ws->meta, P->values,
+                                              P->meta, s),
+                  s, "compress_pair");
+}
+
 sra_status sra_compress_ffi(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t k,
                             sra_sparse* out, void* stream) {
   SRA_TRY(check_dtype(dtype));

@@ -84,6 +84,8 @@ inline void launch(int which, K kernel, dim3 grid, dim3 block, size_t lds, hipSt
 
 hipError_t launch_compress24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
                              uint32_t* meta, hipStream_t s);
+hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
+                                  uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s);
 hipError_t launch_double_prune24(int dtype, const void* vals, const uint32_t* meta, int64_t rows,
                                  int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s);
 hipError_t launch_compress_ffi(int dtype, const void* W, int64_t rows, int64_t cols, int k,

@@ -124,9 +124,98 @@ __global__ __launch_bounds__(256) void k_double_prune24(const T* __restrict__ va
   pm[prow * (rows / 32) + ostart / 32] = word;
 }
 
+// Both prunes in one pass over W, for training loops that refresh Ws and P together after each
+// weight update: a 128 x 64 tile of W is read once; each lane ranks one row's 32-column block (the
+// first prune, written to Ws as in k_compress24) and drops the survivors' keys and values into the
+// LDS tiles the second prune reads (as k_double_prune24 builds them from Ws), then each lane ranks
+// one column's 32-row block and writes P.  Same selection code, so the bits match the two-kernel
+// path exactly.
+template <typename T>
+__global__ __launch_bounds__(256) void k_compress_pair24(const T* __restrict__ W, int64_t rows,
+                                                         int64_t cols, T* __restrict__ vals,
+                                                         uint32_t* __restrict__ meta,
+                                                         T* __restrict__ pv,
+                                                         uint32_t* __restrict__ pm) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ uint32_t key[128][65];
+  __shared__ T val[128][65];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 128;
+  {
+    const int lr = tid >> 1, h = tid & 1;
+    const int64_t row = r0 + lr, cb = c0 + 32 * h;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      key[lr][32 * h + i] = 0;
+      val[lr][32 * h + i] = (T)0;
+    }
+    if (row < rows && cb < cols) {
+      union { u32x4 v[32 / VEC]; T e[32]; } x;
+      const u32x4* src = reinterpret_cast<const u32x4*>(W + row * cols + cb);
+#pragma unroll
+      for (int i = 0; i < 32 / VEC; ++i) x.v[i] = src[i];
+      union { u32x4 v[16 / VEC]; T e[16]; } o;
+      uint32_t word = 0;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        uint32_t k[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) k[a] = mag_key(x.e[4 * g + a]);
+        int p0, p1;
+        top2_of4(k, p0, p1);
+        o.e[2 * g] = x.e[4 * g + p0];
+        o.e[2 * g + 1] = x.e[4 * g + p1];
+        word |= (uint32_t)(p0 | (p1 << 2)) << (4 * g);
+        key[lr][32 * h + 4 * g + p0] = k[p0] + 1;
+        val[lr][32 * h + 4 * g + p0] = x.e[4 * g + p0];
+        key[lr][32 * h + 4 * g + p1] = k[p1] + 1;
+        val[lr][32 * h + 4 * g + p1] = x.e[4 * g + p1];
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(vals + row * (cols / 2) + cb / 2);
+#pragma unroll
+      for (int i = 0; i < 16 / VEC; ++i) dst[i] = o.v[i];
+      meta[row * (cols / 32) + cb / 32] = word;
+    }
+  }
+  __syncthreads();
+  const int c = tid & 63, b = tid >> 6;
+  const int64_t prow = c0 + c, ostart = r0 + 32 * b;
+  if (prow >= cols || ostart >= rows) return;
+  union { u32x4 v[16 / VEC]; T e[16]; } o;
+  uint32_t word = 0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    uint32_t k[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) k[a] = key[32 * b + 4 * g + a][c];
+    int p0, p1;
+    top2_of4(k, p0, p1);
+    o.e[2 * g] = val[32 * b + 4 * g + p0][c];
+    o.e[2 * g + 1] = val[32 * b + 4 * g + p1][c];
+    word |= (uint32_t)(p0 | (p1 << 2)) << (4 * g);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(pv + prow * (rows / 2) + ostart / 2);
+#pragma unroll
+  for (int i = 0; i < 16 / VEC; ++i) dst[i] = o.v[i];
+  pm[prow * (rows / 32) + ostart / 32] = word;
+}
+
 }  // namespace
 
 namespace sra {
+
+hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
+                                  uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
+  if (dtype == SRA_BF16)
+    launch(SRA_KERNEL_COMPRESS, k_compress_pair24<uint16_t>, grid, dim3(256), 0, s,
+           (const uint16_t*)W, rows, cols, (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
+  else
+    launch(SRA_KERNEL_COMPRESS, k_compress_pair24<uint32_t>, grid, dim3(256), 0, s,
+           (const uint32_t*)W, rows, cols, (uint32_t*)vals, meta, (uint32_t*)p_vals, p_meta);
+  return hipGetLastError();
+}
 
 hipError_t launch_compress24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
                              uint32_t* meta, hipStream_t s) {

@@ -617,28 +617,34 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
 // row); its metadata is the (l/16)&1 half of word (l/16)/2.  Lane l of a B fragment holds token
 // l%16 and columns 8(l/16)..+7 and 32+8(l/16)..+7 (chunks l/16 and 4 + l/16).  Accumulator lane l
 // holds rows 4(l/16)..+3 of token l%16.
-template <int FR, int FT, int WR, int WT, int NS>
+// MS > 0: metadata is not part of a stage but fetched in super-stages of MS stages (8 B per row per
+// stage, so MS = 8 gives 64-byte runs instead of 8-byte ones, which LDS-DMA moves ~7x faster per
+// byte) into a double buffer of its own, one super-stage ahead; needs C % 128 == 0 and no split.
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0>
 struct QTile {
   static constexpr int NW = WR * WT;  // waves per workgroup: 4 or 8
   static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
-  static constexpr int LA = BR / (16 * NW), LM = BR / (32 * NW), LB = BT / (8 * NW);
+  static constexpr int LA = BR / (16 * NW), LM = MS ? 0 : BR / (32 * NW), LB = BT / (8 * NW);
   static constexpr int L = LA + LM + LB;
-  static constexpr int A_BYTES = BR * 64, M_BYTES = BR * 8, B_BYTES = BT * 128;
+  static constexpr int A_BYTES = BR * 64, M_BYTES = MS ? 0 : BR * 8, B_BYTES = BT * 128;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
-  static constexpr int LDS = NS * STAGE;
+  static constexpr int MSB = MS ? BR * MS * 8 : 0;            // one metadata super-stage buffer
+  static constexpr int LMS = MS ? MSB / (1024 * NW) : 0;      // its 1 KB transfers per wave
+  static constexpr int LDS = NS * STAGE + 2 * MSB;
   static constexpr int OCC = (NW == 8 || FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
 };
 
-template <int FR, int FT, int WR, int WT, int NS>
-__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm24_q(
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0>
+__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
     float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
-  using TL = QTile<FR, FT, WR, WT, NS>;
+  using TL = QTile<FR, FT, WR, WT, NS, MS>;
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   constexpr int NW = TL::NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(BR % (32 * NW) == 0 && BT % (8 * NW) == 0, "transfer counts must be whole per wave");
+  static_assert(MS == 0 || (MS == 8 && TL::MSB % (1024 * NW) == 0), "metadata super-stages of 8");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
 
   const int tid = threadIdx.x;
@@ -662,8 +668,8 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS>::OCC)) voi
     a_src[k] = s_vals + grow * cv + ch * 8;
     a_dst[k] = b * 1024;
   }
-  const uint32_t* m_src[TL::LM];
-  int m_dst[TL::LM];
+  const uint32_t* m_src[TL::LM ? TL::LM : 1];
+  int m_dst[TL::LM ? TL::LM : 1];
 #pragma unroll
   for (int k = 0; k < TL::LM; ++k) {
     const int b = k * NW + wave, row = 32 * b + (lane >> 1);
@@ -671,6 +677,28 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS>::OCC)) voi
     m_src[k] = s_meta + grow * cm + (lane & 1);
     m_dst[k] = TL::A_BYTES + b * 256;
   }
+  // super-stage metadata: 1 KB block b = 16 rows x 64 B; slot lane%4 holds 16-byte chunk
+  // slot^((row>>2)&3), chunk ch = stages 2ch and 2ch+1 of the super-stage
+  const uint32_t* ms_row[TL::LMS ? TL::LMS : 1];
+  int ms_ch[TL::LMS ? TL::LMS : 1], ms_dst[TL::LMS ? TL::LMS : 1];
+#pragma unroll
+  for (int k = 0; k < TL::LMS; ++k) {
+    const int b = k * NW + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
+    ms_ch[k] = pos ^ ((row >> 2) & 3);
+    const int64_t grow = min(row0 + row, R - 1);
+    ms_row[k] = s_meta + grow * cm;
+    ms_dst[k] = b * 1024;
+  }
+  uint8_t* const msbuf = smem + NS * TL::STAGE;
+  auto issue_meta = [&](int g) {
+    uint8_t* base = msbuf + (g & 1) * TL::MSB;
+#pragma unroll
+    for (int k = 0; k < TL::LMS; ++k) {
+      int64_t w = 2 * ((int64_t)c_beg + MS * g) + 4 * ms_ch[k];  // two words per stage
+      if (w > cm - 4) w = cm - 4;  // past the row's end: clamped, never read
+      dma16(ms_row[k] + w, base + ms_dst[k]);
+    }
+  };
   const uint16_t* b_src[TL::LB];
   int b_dst[TL::LB];
 #pragma unroll
@@ -698,9 +726,11 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS>::OCC)) voi
     for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int wr = wave / WT, wt = wave % WT;
-  auto compute = [&](int buf) {
+  auto compute = [&](int buf, int rel) {
     const uint8_t* A = smem + buf * TL::STAGE;
     const uint32_t* M = reinterpret_cast<const uint32_t*>(A + TL::A_BYTES);
+    const uint8_t* MS_buf = msbuf + (MS ? ((rel / (MS ? MS : 1)) & 1) * TL::MSB : 0);
+    const int u = MS ? rel % (MS ? MS : 1) : 0;
     const uint8_t* B = A + TL::A_BYTES + TL::M_BYTES;
     bf16x16 bfr[FT];
 #pragma unroll
@@ -714,7 +744,15 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS>::OCC)) voi
     for (int i = 0; i < FR; ++i) {
       const int r = wr * 16 * FR + i * 16 + l16;
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + r * 64 + ((q4 ^ ((r >> 2) & 3)) << 4));
-      const int idx = (int)(M[r * 2 + (q4 >> 1)] >> (16 * (q4 & 1)));
+      uint32_t mword;
+      if constexpr (MS > 0) {
+        const int chunk = (u >> 1) ^ ((r >> 2) & 3);
+        mword = *reinterpret_cast<const uint32_t*>(MS_buf + r * (MS * 8) + (chunk << 4) +
+                                                   4 * (2 * (u & 1) + (q4 >> 1)));
+      } else {
+        mword = M[r * 2 + (q4 >> 1)];
+      }
+      const int idx = (int)(mword >> (16 * (q4 & 1)));
 #pragma unroll
       for (int j = 0; j < FT; ++j)
         acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af, bfr[j], acc[i][j], idx, 0, 0);
@@ -722,18 +760,27 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS>::OCC)) voi
   };
 
   constexpr int D = NS - 1;
+  if constexpr (MS > 0) {
+    if (c_beg < c_end) issue_meta(0);
+  }
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (c_beg + d < c_end) issue(c_beg + d, d);
   for (int c = c_beg; c < c_end; ++c) {
+    // waiting for at most (in_flight-1)*L outstanding transfers completes stage c and every older
+    // one, including the metadata of stage c's super-stage (issued before stage c's own loads)
     const int in_flight = min(D, c_end - c);
     if (in_flight >= 4) wait_vm<(3 * L < 63 ? 3 * L : 63)>();
     else if (in_flight == 3) wait_vm<2 * L>();
     else if (in_flight == 2) wait_vm<L>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    if (c + D < c_end) issue(c + D, (c - c_beg + D) % NS);
-    compute((c - c_beg) % NS);
+    const int rel = c - c_beg;
+    if constexpr (MS > 0) {
+      if (rel % MS == 0 && c + MS < c_end) issue_meta(rel / MS + 1);
+    }
+    if (c + D < c_end) issue(c + D, (rel + D) % NS);
+    compute(rel % NS, rel);
   }
 
   // ---- fused low-rank epilogue (first split only), dense v_mfma_f32_16x16x32_bf16:
@@ -1138,7 +1185,8 @@ __global__ void k_splitk_reduce(const float* __restrict__ part, int S, int64_t n
 struct Cfg {
   int id, br, bt;
   bool pipe;
-  int width = 64;  // logical columns per stage
+  int width = 64;      // logical columns per stage
+  bool super = false;  // metadata in super-stages: C % 128 == 0 and no split of the reduction
 };
 // register-staged (any C % 32 == 0):
 //   0 = 256x256 (4x4 accumulators per wave), 1 = 256x128 (4x2), 2 = 128x256 (2x4),
@@ -1152,6 +1200,9 @@ struct Cfg {
 //   40 = 256x128 (waves 128x64, 2 stages), 41 = 128x128 (waves 64x64, 3), 44 = 256x64 (waves 128x32, 2)
 // eight waves (512 threads) on 16x16x64 SMFMAC, 64-column stages:
 //   50 = 256x128 (4x2 waves of 64x64, 4 stages), 51 = 256x256 (4x2 waves of 64x128, 3)
+// the same with metadata in 8-stage super-stages (C % 128 == 0, no split):
+//   55 = 256x128 (8 waves, 4 stages), 56 = 128x64 (4 waves, 4), 57 = 128x128 (4 waves, 3),
+//   58 = 256x256 (8 waves, 2)
 // streaming decode kernel (T <= 16, one 16-token column tile, weight read once from HBM):
 //   30 = 64 weight rows per workgroup (decode24.hip)
 constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 256, false},
@@ -1161,7 +1212,9 @@ constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 25
                          {20, 256, 128, true}, {21, 128, 256, true}, {22, 256, 256, true},
                          {23, 128, 128, true}, {24, 128, 64, true},  {30, 64, 16, false},
                          {40, 256, 128, true, 128}, {41, 128, 128, true, 128},
-                         {44, 256, 64, true, 128}, {50, 256, 128, true}, {51, 256, 256, true}};
+                         {44, 256, 64, true, 128}, {50, 256, 128, true}, {51, 256, 256, true},
+                         {55, 256, 128, true, 64, true}, {56, 128, 64, true, 64, true},
+                         {57, 128, 128, true, 64, true}, {58, 256, 256, true, 64, true}};
 
 Cfg cfg_by_id(int id) {
   for (const Cfg& c : kCfgs)
@@ -1182,7 +1235,7 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
   const char* env = getenv("SRA_SPMM24_CFG");  // tuning override: "<cfg id>[,<splits>]"
   if (env && *env) {
     Cfg c = cfg_by_id(atoi(env));
-    if (c.width == 128 && !wide_ok) c = cfg_by_id(pipe_ok ? 13 : 3);
+    if ((c.width == 128 || c.super) && !wide_ok) c = cfg_by_id(pipe_ok ? 13 : 3);
     if (c.pipe && !pipe_ok) c = cfg_by_id(3);
     if (c.id == 30 && T > 16) c = cfg_by_id(3);
     p.cfg = c;
@@ -1190,15 +1243,19 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
     p.splits = comma ? atoi(comma + 1) : 1;
   } else {
     // Measured on MI355X (2:4, bf16): eight-wave 256x256 tiles win once there are enough of them
-    // to fill the GPU twice, eight-wave 256x128 once those fill it; otherwise 128x128 (two
-    // workgroups per CU), splitting the reduction when even those leave CUs idle.
+    // to fill the GPU twice, eight-wave 256x128 once those fill it (both with metadata in
+    // super-stages when C % 128 == 0), 128x64 for long reductions that would otherwise need a
+    // split; otherwise 128x128 (two workgroups per CU), splitting the reduction when even those
+    // leave CUs idle.
     auto tiles = [&](int br, int bt) { return ((R + br - 1) / br) * ((T + bt - 1) / bt); };
     if (T <= 16) {
       p.cfg = cfg_by_id(30);  // few tokens: bound by reading the weight once
     } else if (pipe_ok && tiles(256, 256) >= 512) {
-      p.cfg = cfg_by_id(51);
+      p.cfg = cfg_by_id(wide_ok ? 58 : 51);
     } else if (pipe_ok && tiles(256, 128) >= 240) {
-      p.cfg = cfg_by_id(50);
+      p.cfg = cfg_by_id(wide_ok ? 55 : 50);
+    } else if (pipe_ok && tiles(128, 64) >= 240 && C >= 2048) {
+      p.cfg = cfg_by_id(14);  // long reductions: 128x64 tiles beat 128x128 split plus its reduction
     } else {
       p.cfg = cfg_by_id(pipe_ok ? 13 : 3);
       const int64_t t = tiles(128, 128);
@@ -1211,20 +1268,20 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
     }
   }
   const int nC = (int)((C + p.cfg.width - 1) / p.cfg.width);
-  if (p.splits < 1 || p.cfg.id == 30) p.splits = 1;
+  if (p.splits < 1 || p.cfg.id == 30 || p.cfg.super) p.splits = 1;
   if (p.splits > nC) p.splits = nC;
   p.stages_per_split = (nC + p.splits - 1) / p.splits;
   p.splits = (nC + p.stages_per_split - 1) / p.stages_per_split;
   return p;
 }
 
-template <int FR, int FT, int WR, int WT, int NS>
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0>
 void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
               const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
               const Plan& p, hipStream_t s) {
-  using TL = QTile<FR, FT, WR, WT, NS>;
+  using TL = QTile<FR, FT, WR, WT, NS, MS>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
-  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_q<FR, FT, WR, WT, NS>,
+  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_q<FR, FT, WR, WT, NS, MS>,
               dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(64 * TL::NW), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
@@ -1279,6 +1336,10 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
   float* part = p.splits > 1 ? (float*)ws : nullptr;
   switch (p.cfg.id) {
     case 30: return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s);
+    case 55: launch_q<4, 4, 4, 2, 4, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 56: launch_q<4, 2, 2, 2, 4, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 57: launch_q<4, 4, 2, 2, 3, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 58: launch_q<4, 8, 4, 2, 2, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 50: launch_q<4, 4, 4, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 51: launch_q<4, 8, 4, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 40: launch_w<8, 4, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;

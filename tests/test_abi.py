@@ -96,6 +96,18 @@ def test_double_prune_validation(lib):
     assert lib.sra_double_prune(ctypes.byref(ok), None, None) == SRA_ERR_INVALID_ARG
 
 
+def test_compress_pair_validation(lib):
+    S, P = SraSparse(), SraSparse()
+    S.values, S.meta, P.values, P.meta = FAKE, FAKE, FAKE, FAKE
+    # both dimensions are grouped: rows 36 is not a multiple of 32
+    assert lib.sra_compress_pair(FAKE, SRA_BF16, 36, 64, 2, 4, ctypes.byref(S), ctypes.byref(P), None) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_compress_pair(FAKE, SRA_BF16, 64, 48, 2, 4, ctypes.byref(S), ctypes.byref(P), None) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_compress_pair(FAKE, SRA_BF16, 64, 64, 2, 4, ctypes.byref(S), None, None) == SRA_ERR_INVALID_ARG
+    P.meta = None
+    assert lib.sra_compress_pair(FAKE, SRA_BF16, 64, 64, 2, 4, ctypes.byref(S), ctypes.byref(P), None) == SRA_ERR_INVALID_ARG
+    assert "P->meta" in err(lib)
+
+
 def test_ffi_validation(lib):
     d = SraSparse()
     d.values, d.index = FAKE, FAKE

@@ -67,6 +67,32 @@ def test_double_prune_ties(gpu, dtype, shape):
     check_double_prune(tie_heavy(shape, seed=7 + shape[1], dtype=dtype), dtype)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(32, 32), (96, 160), (160, 224), (256, 1024)])
+def test_compress_pair_matches_two_kernels(gpu, dtype, shape):
+    """compress_pair (one pass) is bit-identical to compress then double_prune, and to the oracle."""
+    W_cpu = tie_heavy(shape, seed=3 + shape[0], dtype=dtype)
+    S, P = check_double_prune(W_cpu, dtype)
+    S2, P2 = sra.compress_pair(W_cpu.cuda())
+    torch.cuda.synchronize()
+    assert (S2.rows, S2.cols, P2.rows, P2.cols) == (S.rows, S.cols, P.rows, P.cols)
+    for a, b in ((S2.values, S.values), (P2.values, P.values)):
+        assert np.array_equal(bits(a), bits(b))
+    for a, b in ((S2.meta, S.meta), (P2.meta, P.meta)):
+        assert np.array_equal(meta_u32(a), meta_u32(b))
+
+
+def test_compress_pair_opt350m_fc1(gpu):
+    W = layer_inputs(WORKLOADS["opt350m_fc1"], with_dy=False)["W"]
+    S, P = check_double_prune(W, torch.bfloat16, col_groups=np.arange(0, 256, 7))
+    S2, P2 = sra.compress_pair(W.cuda())
+    torch.cuda.synchronize()
+    for a, b in ((S2.values, S.values), (P2.values, P.values)):
+        assert np.array_equal(bits(a), bits(b))
+    for a, b in ((S2.meta, S.meta), (P2.meta, P.meta)):
+        assert np.array_equal(meta_u32(a), meta_u32(b))
+
+
 def test_double_prune_tiny_f32(gpu):
     check_double_prune(layer_inputs(WORKLOADS["tiny_f32"])["W"], torch.float32)
 
