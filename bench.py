@@ -39,8 +39,8 @@ PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the kernel configuration the planner picks for
 # that call; a key missing here (kernel changed since the counters were taken) reports null.
 TRAFFIC_BYTES = {
-    "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4>": 26886.5 * 1024 * 2.0 + 4096.0 * 1024,
-    "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,4,8>": 13815.2 * 1024 * 2.0 + 16384.0 * 1024,
+    "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27355.7 * 1024 * 2.0 + 4352.0 * 1024,
+    "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13826.3 * 1024 * 2.0 + 16512.0 * 1024,
     "opt66b_ffn_decode/T16/k_decode24": 196310.1 * 1024 * 2.0 + 1152.5 * 1024,
 }
 
@@ -241,10 +241,10 @@ def bench_nm_layer(args, wl):
     spmm_flops_bwd = 2 * T * wl.K * (wl.N // 2) + 2 * T * r * wl.K
     if k_bwd >= k_fwd:
         kname, kms, kflops = "k_spmm24 (backward dX = dY P^T + dU A)", k_bwd, spmm_flops_bwd
-        tkey = f"{wl.name}/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4>"
+        tkey = f"{wl.name}/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>"
     else:
         kname, kms, kflops = "k_spmm24 (forward Y = X Ws^T + U B^T)", k_fwd, spmm_flops_fwd
-        tkey = f"{wl.name}/spmm24_fwd/k_spmm24_q<4,4,4,2,4,8>"
+        tkey = f"{wl.name}/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>"
     traffic = TRAFFIC_BYTES.get(tkey)
     achieved = kflops / (kms * 1e-3) / 1e12
     out = {

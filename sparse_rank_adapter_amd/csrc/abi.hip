@@ -403,7 +403,9 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     return hip_done(sra::launch_f32_spmm(S, (const float*)X, T, U64, (const float*)B, r, 1, r,
                                          (float*)Y, s), s, "fwd spmm f32");
   }
-  if (r > 0)
+  // U = X A^T: computed inside the SpMM when its plan allows, else by the adapter kernel first
+  const bool fuse = r > 0 && Ws->format == SRA_FMT_NM && sra::spmm24_fuses_adapter(N, K, T, r);
+  if (r > 0 && !fuse)
     SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, r, U,
                                               nullptr, nullptr, wsb + plan.gemm_off, s), s, "fwd U"));
   sra::Epilogue ep;
@@ -412,6 +414,11 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
   ep.e_row_stride = r;
   ep.e_j_stride = 1;
   ep.r = r;
+  if (fuse) {
+    ep.G = (const uint16_t*)A;
+    ep.g_ld = K;
+    ep.u_out = U_out;
+  }
   if (Ws->format == SRA_FMT_NM)
     return hip_done(sra::launch_spmm24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
                                             (const uint16_t*)X, T, ep, (uint16_t*)Y,
@@ -495,7 +502,10 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                               (float*)Uv, nullptr, nullptr, gws, s), s, "bwd U"));
   SRA_TRY(hip_done(sra::launch_adapter_bwd_prep((const uint16_t*)B, N, r, wt, Uv, T, vtU, s), s,
                    "bwd prep"));
-  if (plan.need_du)
+  // dU = dY B: computed inside the dX SpMM (which also writes dU_out and dU^T's parts for dA)
+  // when its plan allows, else by the adapter kernel first
+  const bool fuse = dx_ad && P->format == SRA_FMT_NM && sra::spmm24_fuses_adapter(K, N, T, r);
+  if (plan.need_du && !fuse)
     SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)dY, T, N, wt, sra::packed_wt_ld(N), r,
                                               dU, nullptr, vtdU, gws, s), s, "bwd dU"));
   if (fdx) {
@@ -505,6 +515,14 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     ep.e_row_stride = 1;
     ep.e_j_stride = K;
     ep.r = dx_ad ? r : 0;
+    if (fuse) {
+      ep.G = wt;
+      ep.g_ld = sra::packed_wt_ld(N);
+      ep.u_out = dU_out;
+      ep.vt = vtdU;
+      ep.vt_rp = (int)sra::vt_rows(r);
+      ep.vt_tp = sra::vt_cols(T);
+    }
     if (P->format == SRA_FMT_NM)
       SRA_TRY(hip_done(sra::launch_spmm24_bf16((const uint16_t*)P->values, P->meta, K, N,
                                                (const uint16_t*)dY, T, ep, (uint16_t*)dX,

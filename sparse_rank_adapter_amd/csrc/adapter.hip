@@ -63,14 +63,8 @@ SRA_DEV u32x4 load8(const uint16_t* __restrict__ p, int64_t i, int64_t lim, bool
 // ------------------------------------------------------------------------------------ rows
 // grid: (ceil(T/16), ceil(r/(16 JT)), S); slice z covers c in [z*c_per, min(C, (z+1)*c_per)).
 // Wave w takes the 32-column steps w, w+4, w+8, ... of its slice, UB steps per batch.
-// When vt is non-null the result is also written as V^T split into four bf16 parts,
+// When vt is non-null the result is also written as V^T split into four bf16 parts (write_vt4),
 // vt[p][j][t] (rows rp, columns Tp; the zero padding is the caller's), ready for the cols kernel.
-SRA_DEV void write_vt4(uint16_t* __restrict__ vt, int rp, int64_t Tp, int j, int64_t t, double v) {
-  uint16_t p4[4];
-  split4_bf16(v, p4);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + t] = p4[p];
-}
 
 template <int JT, int UB>
 __global__ __launch_bounds__(256) void k_adapter_rows(const uint16_t* __restrict__ act, int64_t T,

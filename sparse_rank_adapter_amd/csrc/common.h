@@ -63,6 +63,14 @@ SRA_DEV void split4_bf16(double x, uint16_t p[4]) {
     rem -= (double)bf16_to_f32(p[i]);
   }
 }
+// V^T in four bf16 parts, vt[p][j][t] (rp rows per part, Tp columns), the operand layout of the
+// adapter-gradient kernel for an fp64 V.
+SRA_DEV void write_vt4(uint16_t* __restrict__ vt, int rp, int64_t Tp, int j, int64_t t, double v) {
+  uint16_t p4[4];
+  split4_bf16(v, p4);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + t] = p4[p];
+}
 
 // ---- host-side launchers implemented in the kernel sources (internal C++ linkage)
 namespace sra {
@@ -125,7 +133,19 @@ struct Epilogue {
   const uint16_t* E = nullptr;  // bf16, element (row, j) at E[row*e_row_stride + j*e_j_stride]
   int64_t e_row_stride = 0, e_j_stride = 0;
   int r = 0;
+  // When G is set the SpMM computes U = Act G^T itself (G: r rows of C bf16, row j at G + j*g_ld)
+  // and does not read U; its first row tile then writes U to u_out ([T][r] fp32) and, when vt is
+  // set, U^T in four bf16 parts (vt[p][j][t], vt_rp rows, vt_tp columns, zeros for t >= T).
+  const uint16_t* G = nullptr;
+  int64_t g_ld = 0;
+  float* u_out = nullptr;
+  uint16_t* vt = nullptr;
+  int vt_rp = 0;
+  int64_t vt_tp = 0;
 };
+// True when launch_spmm24_bf16 for this shape computes the adapter rows U itself (Epilogue::G);
+// the caller then skips the separate U kernel.
+bool spmm24_fuses_adapter(int64_t R, int64_t C, int64_t T, int r);
 size_t spmm24_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,

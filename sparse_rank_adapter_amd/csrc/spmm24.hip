@@ -60,6 +60,22 @@ SRA_DEV void tile_coords(int L, int n_rt, int n_tt, int& rt, int& tt) {
 }
 
 
+// Eight consecutive adapter entries E(row, jb .. jb+7) as an MFMA operand (zero past r or R).
+SRA_DEV bf16x8 load_e8(const sra::Epilogue& ep, int64_t row, int64_t R, int jb) {
+  union { u32x4 v; uint16_t h[8]; bf16x8 b; } x;
+  x.v = u32x4{0, 0, 0, 0};
+  if (row < R) {
+    if (ep.e_j_stride == 1 && (ep.r & 7) == 0 && jb + 8 <= ep.r) {
+      x.v = *reinterpret_cast<const u32x4*>(ep.E + row * ep.e_row_stride + jb);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (jb + q < ep.r) x.h[q] = ep.E[row * ep.e_row_stride + (int64_t)(jb + q) * ep.e_j_stride];
+    }
+  }
+  return x.b;
+}
+
 // Output tile staged through LDS so that global stores are whole 16-byte vectors along a token's
 // row of Y (consecutive weight rows): the MFMA accumulator layout gives each lane 4 rows of one
 // token, which written directly would be 8-byte pieces 2R bytes apart.  Layout [token][row] with a
@@ -350,12 +366,17 @@ __global__ __launch_bounds__(256, (Tile<FR, FT, WR, WT>::OCC)) void k_spmm24(
 // (chunk ^ f(row)) instead of padded, and the 128-bit fragment reads of 16 consecutive lanes
 // still hit 16 distinct bank groups.  Rows / tokens past the edge read a clamped valid address
 // and their results are never stored.
-template <int FR, int FT, int WR, int WT, int NS>
+// UG > 0: UG adapter rows G (Epilogue::G) ride along as rows BT .. BT+UG-1 of each stage's
+// activation region (same 128-byte rows and swizzle as the tokens), in GT 1 KB transfers per
+// stage spread over the waves (GW each, one more for the first GX waves).
+template <int FR, int FT, int WR, int WT, int NS, int UG = 0>
 struct PTile {
   static constexpr int BR = 32 * FR * WR, BT = 32 * FT * WT;
   static constexpr int LA = BR / 64, LM = BR / 128, LB = BT / 32;  // transfers per wave per stage
-  static constexpr int L = LA + LM + LB;
-  static constexpr int A_BYTES = BR * 64, M_BYTES = BR * 8, B_BYTES = BT * 128;
+  static constexpr int GT = UG / 8, GW = GT / 4, GX = GT % 4;
+  static constexpr int L = LA + LM + LB + GW;  // waves >= GX
+  static constexpr int L1 = L + (GX ? 1 : 0);  // waves < GX
+  static constexpr int A_BYTES = BR * 64, M_BYTES = BR * 8, B_BYTES = (BT + UG) * 128;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
   static constexpr int LDS = NS * STAGE;
   static constexpr int OCC = (FR * FT >= 8 || 2 * LDS > 160 * 1024) ? 1 : 2;
@@ -375,20 +396,135 @@ SRA_DEV void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// With `in_flight` stages issued (the oldest is the one about to be computed) and L transfers per
+// stage, wait until at most the newer stages' transfers are outstanding.
+template <int L>
+SRA_DEV void wait_stages(int in_flight) {
+  if (in_flight >= 4) wait_vm<(3 * L < 63 ? 3 * L : 63)>();
+  else if (in_flight == 3) wait_vm<2 * L>();
+  else if (in_flight == 2) wait_vm<L>();
+  else wait_vm<0>();
+}
 
-template <int FR, int FT, int WR, int WT, int NS>
-__global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm24_pipe(
+// In-kernel adapter rows (UG > 0): per stage, U^T[j][t] += G[j][c] Act[t][c] over the stage's 64
+// columns for the 16-token fragments f = wave, wave + NW, ..., with dense v_mfma_f32_16x16x32_bf16
+// (A = G rows j, lane: j = l%16, columns 8(l/16)..+7; B = tokens, lane: token l%16, same columns)
+// from the stage's activation region `rows` (128-byte rows, chunk c of row x at (c ^ ((x>>1)&7))).
+// Each stage's fp32 result is added to fp64 sums one stage later (so the wave never waits on these
+// MFMAs), and U keeps full fp32 accuracy over long C.
+template <int BT, int UG, int NW>
+struct AdapterRows {
+  static constexpr int NTF = BT / 16, NFW = (NTF + NW - 1) / NW, NJ = UG / 16;
+  static constexpr int ULD = UG + 4;  // floats per token row of the U tile handed over in LDS
+  double u[NFW][NJ][4];
+  f32x4 d[NFW][NJ];  // the last stage's products, not yet in u
+  SRA_DEV void zero() {
+#pragma unroll
+    for (int i = 0; i < NFW; ++i)
+#pragma unroll
+      for (int jf = 0; jf < NJ; ++jf) {
+        d[i][jf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[i][jf][e] = 0.0;
+      }
+  }
+  SRA_DEV void flush() {
+#pragma unroll
+    for (int i = 0; i < NFW; ++i)
+#pragma unroll
+      for (int jf = 0; jf < NJ; ++jf)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[i][jf][e] += (double)d[i][jf][e];
+  }
+  bf16x8 tb0[NFW], tb1[NFW], g0[NJ], g1[NJ];  // the stage's operand fragments
+  // fragment reads of one stage (issued together with the main product's reads)
+  SRA_DEV void read(const uint8_t* rows, int wave, int lane) {
+    const int q4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) {
+      const int f = min(wave + NW * i, NTF - 1);
+      const int tk = f * 16 + l16, sw = (tk >> 1) & 7;
+      tb0[i] = *reinterpret_cast<const bf16x8*>(rows + tk * 128 + ((q4 ^ sw) << 4));
+      tb1[i] = *reinterpret_cast<const bf16x8*>(rows + tk * 128 + (((4 + q4) ^ sw) << 4));
+    }
+#pragma unroll
+    for (int jf = 0; jf < NJ; ++jf) {
+      const int gr = BT + jf * 16 + l16, sg = (gr >> 1) & 7;
+      g0[jf] = *reinterpret_cast<const bf16x8*>(rows + gr * 128 + ((q4 ^ sg) << 4));
+      g1[jf] = *reinterpret_cast<const bf16x8*>(rows + gr * 128 + (((4 + q4) ^ sg) << 4));
+    }
+  }
+  SRA_DEV void mma(int wave) {
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) {
+      if (NTF % NW != 0 && wave + NW * i >= NTF) continue;
+#pragma unroll
+      for (int jf = 0; jf < NJ; ++jf) {
+        const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g0[jf], tb0[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        d[i][jf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g1[jf], tb1[i], x, 0, 0, 0);
+      }
+    }
+  }
+  // U tile -> LDS ut[t][j] (fp32); the first row tile also writes U and its V^T parts out.
+  SRA_DEV void hand_over(float* ut, int wave, int lane, bool first_row_tile, int64_t t0, int64_t T,
+                         const sra::Epilogue& ep) const {
+    const int q4 = lane >> 4, l16 = lane & 15;
+    const bool u_vec = (ep.r & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) {
+      const int f = wave + NW * i;
+      if (NTF % NW != 0 && f >= NTF) continue;
+      const int tl = f * 16 + l16;
+      const int64_t tg = t0 + tl;
+#pragma unroll
+      for (int jf = 0; jf < NJ; ++jf) {
+        const int j = jf * 16 + 4 * q4;
+        const f32x4 v = f32x4{(float)u[i][jf][0], (float)u[i][jf][1], (float)u[i][jf][2],
+                              (float)u[i][jf][3]};
+        *reinterpret_cast<f32x4*>(ut + tl * ULD + j) = v;
+        if (!first_row_tile) continue;
+        if (tg < T) {
+          if (ep.u_out) {
+            if (u_vec && j + 4 <= ep.r) {
+              *reinterpret_cast<f32x4*>(ep.u_out + tg * ep.r + j) = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (j + e < ep.r) ep.u_out[tg * ep.r + j + e] = v[e];
+            }
+          }
+          if (ep.vt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j + e < ep.r) write_vt4(ep.vt, ep.vt_rp, ep.vt_tp, j + e, tg, u[i][jf][e]);
+          }
+        } else if (ep.vt && tg < ep.vt_tp) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < ep.r)
+#pragma unroll
+              for (int p = 0; p < 4; ++p) ep.vt[((int64_t)p * ep.vt_rp + j + e) * ep.vt_tp + tg] = 0;
+        }
+      }
+    }
+  }
+};
+
+template <int FR, int FT, int WR, int WT, int NS, int UG = 0>
+__global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_spmm24_pipe(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
     float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
-  using TL = PTile<FR, FT, WR, WT, NS>;
+  using TL = PTile<FR, FT, WR, WT, NS, UG>;
+  using AD = AdapterRows<TL::BT, (UG > 0 ? UG : 16), 4>;
+  static_assert(UG == 0 || AD::ULD * 4 * TL::BT <= TL::LDS, "U tile fits in LDS");
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   static_assert(WR * WT == 4, "4 waves");
   static_assert(BR % 128 == 0 && BT % 32 == 0, "transfer counts must be whole per wave");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   int rt, tt;
   tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
   const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT;
@@ -428,6 +564,19 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
     b_src[k] = act + gt * C + ch * 8;
     b_dst[k] = TL::A_BYTES + TL::M_BYTES + b * 1024;
   }
+  // adapter rows: transfer k*4 + wave (< GT) moves rows BT + 8(k*4 + wave) .. +7 (G rows past r
+  // repeat row r-1: finite, and their products meet zero E entries)
+  constexpr int NG = TL::GW + (TL::GX ? 1 : 0);
+  const uint16_t* g_src[NG ? NG : 1];
+  int g_dst[NG ? NG : 1];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int b = k * 4 + wave, tk = BT + 8 * b + (lane >> 3), pos = lane & 7;
+    const int ch = pos ^ ((tk >> 1) & 7);
+    const int jr = min(tk - BT, ep.r - 1);
+    g_src[k] = ep.G + (int64_t)jr * ep.g_ld + ch * 8;
+    g_dst[k] = TL::A_BYTES + TL::M_BYTES + (BT / 8 + b) * 1024;
+  }
   auto issue = [&](int c, int buf) {
     uint8_t* base = smem + buf * TL::STAGE;
 #pragma unroll
@@ -436,7 +585,12 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
     for (int k = 0; k < TL::LM; ++k) dma4(m_src[k] + (int64_t)c * 2, base + m_dst[k]);
 #pragma unroll
     for (int k = 0; k < TL::LB; ++k) dma16(b_src[k] + (int64_t)c * BC, base + b_dst[k]);
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      if (k < TL::GW || wave < TL::GX) dma16(g_src[k] + (int64_t)c * BC, base + g_dst[k]);
   };
+  AD ad;
+  if constexpr (UG > 0) ad.zero();
 
   f32x16 acc[FR][FT];
 #pragma unroll
@@ -447,34 +601,42 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int wr = wave / WT, wt = wave % WT;
+  // One stage: every fragment read first (one LDS round trip), then the adapter-row MFMAs (which
+  // do not depend on the accumulators), then the sparse products.
   auto compute = [&](int buf) {
     const uint8_t* A = smem + buf * TL::STAGE;
     const uint32_t* M = reinterpret_cast<const uint32_t*>(A + TL::A_BYTES);
     const uint8_t* B = A + TL::A_BYTES + TL::M_BYTES;
+    if constexpr (UG > 0) ad.flush();
+    bf16x8 af[2][FR];
+    int idx[2][FR];
+    bf16x16 bfr[2][FT];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 af[FR];
-      int idx[FR];
 #pragma unroll
       for (int i = 0; i < FR; ++i) {
         const int r = wr * 32 * FR + i * 32 + li;
-        af[i] = *reinterpret_cast<const bf16x8*>(A + r * 64 + (((2 * s + g) ^ ((r >> 2) & 3)) << 4));
-        idx[i] = (int)(M[r * 2 + s] >> (16 * g));
+        af[s][i] = *reinterpret_cast<const bf16x8*>(A + r * 64 + (((2 * s + g) ^ ((r >> 2) & 3)) << 4));
+        idx[s][i] = (int)(M[r * 2 + s] >> (16 * g));
       }
-      bf16x16 bfr[FT];
 #pragma unroll
       for (int j = 0; j < FT; ++j) {
         const int tk = wt * 32 * FT + j * 32 + li, sw = (tk >> 1) & 7;
         const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 * s + g) ^ sw) << 4));
         const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 * s + 2 + g) ^ sw) << 4));
-        bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        bfr[s][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       }
+    }
+    if constexpr (UG > 0) ad.read(B, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+    if constexpr (UG > 0) ad.mma(wave);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int i = 0; i < FR; ++i)
 #pragma unroll
         for (int j = 0; j < FT; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[i], bfr[j], acc[i][j], idx[i], 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[s][i], bfr[s][j], acc[i][j], idx[s][i], 0, 0);
   };
 
   constexpr int D = NS - 1;  // stages in flight ahead of the one being computed
@@ -483,45 +645,42 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
     if (c_beg + d < c_end) issue(c_beg + d, d);
   for (int c = c_beg; c < c_end; ++c) {
     const int in_flight = min(D, c_end - c);  // stages c .. c+in_flight-1 were issued
-    if (in_flight >= 4) wait_vm<(3 * L < 63 ? 3 * L : 63)>();
-    else if (in_flight == 3) wait_vm<2 * L>();
-    else if (in_flight == 2) wait_vm<L>();
-    else wait_vm<0>();
+    if (TL::GX && wave < TL::GX) wait_stages<TL::L1>(in_flight);
+    else wait_stages<L>(in_flight);
     __builtin_amdgcn_s_barrier();  // stage c visible to all waves; stage c-1 fully consumed
     if (c + D < c_end) issue(c + D, (c - c_beg + D) % NS);
     compute((c - c_beg) % NS);
   }
+  if constexpr (UG > 0) ad.flush();
+
+  // ---- in-kernel U: hand the tile over through LDS (and write U / V^T from the first row tile)
+  float* const ut = reinterpret_cast<float*>(smem);
+  if constexpr (UG > 0) {
+    __syncthreads();  // every wave is done with the operand ring
+    ad.hand_over(ut, wave, lane, rt == 0, t0, T, ep);
+    __syncthreads();
+  }
 
   // ---- fused low-rank epilogue (first split only): acc += E(rows, :) U(tokens, :)^T
   if (ep.r > 0 && z == 0) {
-    const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0;
     const bool u_vec = (ep.r & 7) == 0;
     for (int jj = 0; jj < ep.r; jj += 16) {
       const int jb = jj + 8 * g;
       bf16x8 ef[FR];
 #pragma unroll
-      for (int i = 0; i < FR; ++i) {
-        const int64_t row = row0 + wr * 32 * FR + i * 32 + li;
-        union { u32x4 v; uint16_t h[8]; bf16x8 b; } x;
-        x.v = u32x4{0, 0, 0, 0};
-        if (row < R) {
-          if (e_vec && jb + 8 <= ep.r) {
-            x.v = *reinterpret_cast<const u32x4*>(ep.E + row * ep.e_row_stride + jb);
-          } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (jb + q < ep.r) x.h[q] = ep.E[row * ep.e_row_stride + (int64_t)(jb + q) * ep.e_j_stride];
-          }
-        }
-        ef[i] = x.b;
-      }
+      for (int i = 0; i < FR; ++i) ef[i] = load_e8(ep, row0 + wr * 32 * FR + i * 32 + li, R, jb);
 #pragma unroll
       for (int j = 0; j < FT; ++j) {
-        const int64_t t = t0 + wt * 32 * FT + j * 32 + li;
+        const int tl = wt * 32 * FT + j * 32 + li;
+        const int64_t t = t0 + tl;
         float u[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) u[q] = 0.f;
-        if (t < T) {
+        if (UG > 0 && t < T) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (jb + q < ep.r) u[q] = ut[tl * AD::ULD + jb + q];
+        } else if (t < T) {
           const float* up = ep.U + t * ep.r + jb;
           if (u_vec && jb + 8 <= ep.r) {
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
@@ -620,13 +779,16 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS>::OCC)) void k_spmm2
 // MS > 0: metadata is not part of a stage but fetched in super-stages of MS stages (8 B per row per
 // stage, so MS = 8 gives 64-byte runs instead of 8-byte ones, which LDS-DMA moves ~7x faster per
 // byte) into a double buffer of its own, one super-stage ahead; needs C % 128 == 0 and no split.
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0>
+// UG > 0: adapter rows in the activation region as in PTile (GT transfers over NW waves).
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0>
 struct QTile {
   static constexpr int NW = WR * WT;  // waves per workgroup: 4 or 8
   static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
   static constexpr int LA = BR / (16 * NW), LM = MS ? 0 : BR / (32 * NW), LB = BT / (8 * NW);
-  static constexpr int L = LA + LM + LB;
-  static constexpr int A_BYTES = BR * 64, M_BYTES = MS ? 0 : BR * 8, B_BYTES = BT * 128;
+  static constexpr int GT = UG / 8, GW = GT / NW, GX = GT % NW;
+  static constexpr int L = LA + LM + LB + GW;  // waves >= GX
+  static constexpr int L1 = L + (GX ? 1 : 0);  // waves < GX
+  static constexpr int A_BYTES = BR * 64, M_BYTES = MS ? 0 : BR * 8, B_BYTES = (BT + UG) * 128;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
   static constexpr int MSB = MS ? BR * MS * 8 : 0;            // one metadata super-stage buffer
   static constexpr int LMS = MS ? MSB / (1024 * NW) : 0;      // its 1 KB transfers per wave
@@ -634,21 +796,23 @@ struct QTile {
   static constexpr int OCC = (NW == 8 || FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
 };
 
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0>
-__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC)) void k_spmm24_q(
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0>
+__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
     float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
-  using TL = QTile<FR, FT, WR, WT, NS, MS>;
+  using TL = QTile<FR, FT, WR, WT, NS, MS, UG>;
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   constexpr int NW = TL::NW;
+  using AD = AdapterRows<BT, (UG > 0 ? UG : 16), NW>;
+  static_assert(UG == 0 || AD::ULD * 4 * BT <= TL::LDS, "U tile fits in LDS");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(BR % (32 * NW) == 0 && BT % (8 * NW) == 0, "transfer counts must be whole per wave");
   static_assert(MS == 0 || (MS == 8 && TL::MSB % (1024 * NW) == 0), "metadata super-stages of 8");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, q4 = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q4 = lane >> 4, l16 = lane & 15;
   int rt, tt;
   tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
   const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT;
@@ -709,6 +873,17 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
     b_src[k] = act + gt * C + ch * 8;
     b_dst[k] = TL::A_BYTES + TL::M_BYTES + b * 1024;
   }
+  constexpr int NG = TL::GW + (TL::GX ? 1 : 0);
+  const uint16_t* g_src[NG ? NG : 1];
+  int g_dst[NG ? NG : 1];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int b = k * NW + wave, tk = BT + 8 * b + (lane >> 3), pos = lane & 7;
+    const int ch = pos ^ ((tk >> 1) & 7);
+    const int jr = min(tk - BT, ep.r - 1);
+    g_src[k] = ep.G + (int64_t)jr * ep.g_ld + ch * 8;
+    g_dst[k] = TL::A_BYTES + TL::M_BYTES + (BT / 8 + b) * 1024;
+  }
   auto issue = [&](int c, int buf) {
     uint8_t* base = smem + buf * TL::STAGE;
 #pragma unroll
@@ -717,7 +892,12 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
     for (int k = 0; k < TL::LM; ++k) dma4(m_src[k] + (int64_t)c * 2, base + m_dst[k]);
 #pragma unroll
     for (int k = 0; k < TL::LB; ++k) dma16(b_src[k] + (int64_t)c * BC, base + b_dst[k]);
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      if (k < TL::GW || wave < TL::GX) dma16(g_src[k] + (int64_t)c * BC, base + g_dst[k]);
   };
+  AD ad;
+  if constexpr (UG > 0) ad.zero();
 
   f32x4 acc[FR][FT];
 #pragma unroll
@@ -732,6 +912,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
     const uint8_t* MS_buf = msbuf + (MS ? ((rel / (MS ? MS : 1)) & 1) * TL::MSB : 0);
     const int u = MS ? rel % (MS ? MS : 1) : 0;
     const uint8_t* B = A + TL::A_BYTES + TL::M_BYTES;
+    if constexpr (UG > 0) ad.flush();
     bf16x16 bfr[FT];
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
@@ -740,22 +921,29 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
       const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
       bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     }
+    bf16x8 af[FR];
+    uint32_t mword[FR];
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
       const int r = wr * 16 * FR + i * 16 + l16;
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + r * 64 + ((q4 ^ ((r >> 2) & 3)) << 4));
-      uint32_t mword;
+      af[i] = *reinterpret_cast<const bf16x8*>(A + r * 64 + ((q4 ^ ((r >> 2) & 3)) << 4));
       if constexpr (MS > 0) {
         const int chunk = (u >> 1) ^ ((r >> 2) & 3);
-        mword = *reinterpret_cast<const uint32_t*>(MS_buf + r * (MS * 8) + (chunk << 4) +
-                                                   4 * (2 * (u & 1) + (q4 >> 1)));
+        mword[i] = *reinterpret_cast<const uint32_t*>(MS_buf + r * (MS * 8) + (chunk << 4) +
+                                                      4 * (2 * (u & 1) + (q4 >> 1)));
       } else {
-        mword = M[r * 2 + (q4 >> 1)];
+        mword[i] = M[r * 2 + (q4 >> 1)];
       }
-      const int idx = (int)(mword >> (16 * (q4 & 1)));
+    }
+    if constexpr (UG > 0) ad.read(B, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+    if constexpr (UG > 0) ad.mma(wave);
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      const int idx = (int)(mword[i] >> (16 * (q4 & 1)));
 #pragma unroll
       for (int j = 0; j < FT; ++j)
-        acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af, bfr[j], acc[i][j], idx, 0, 0);
+        acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bfr[j], acc[i][j], idx, 0, 0);
     }
   };
 
@@ -770,10 +958,8 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
     // waiting for at most (in_flight-1)*L outstanding transfers completes stage c and every older
     // one, including the metadata of stage c's super-stage (issued before stage c's own loads)
     const int in_flight = min(D, c_end - c);
-    if (in_flight >= 4) wait_vm<(3 * L < 63 ? 3 * L : 63)>();
-    else if (in_flight == 3) wait_vm<2 * L>();
-    else if (in_flight == 2) wait_vm<L>();
-    else wait_vm<0>();
+    if (TL::GX && wave < TL::GX) wait_stages<TL::L1>(in_flight);
+    else wait_stages<L>(in_flight);
     __builtin_amdgcn_s_barrier();
     const int rel = c - c_beg;
     if constexpr (MS > 0) {
@@ -781,6 +967,15 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
     }
     if (c + D < c_end) issue(c + D, (rel + D) % NS);
     compute(rel % NS, rel);
+  }
+  if constexpr (UG > 0) ad.flush();
+
+  // ---- in-kernel U: hand the tile over through LDS (and write U / V^T from the first row tile)
+  float* const ut = reinterpret_cast<float*>(smem);
+  if constexpr (UG > 0) {
+    __syncthreads();  // every wave is done with the operand ring
+    ad.hand_over(ut, wave, lane, rt == 0, t0, T, ep);
+    __syncthreads();
   }
 
   // ---- fused low-rank epilogue (first split only), dense v_mfma_f32_16x16x32_bf16:
@@ -794,11 +989,16 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
       UH uhi[FT], ulo[FT];
 #pragma unroll
       for (int j = 0; j < FT; ++j) {
-        const int64_t t = t0 + wt * 16 * FT + j * 16 + l16;
+        const int tl = wt * 16 * FT + j * 16 + l16;
+        const int64_t t = t0 + tl;
         float u[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) u[q] = 0.f;
-        if (t < T) {
+        if (UG > 0 && t < T) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (jb + q < ep.r) u[q] = ut[tl * AD::ULD + jb + q];
+        } else if (t < T) {
           const float* up = ep.U + t * ep.r + jb;
           if (u_vec && jb + 8 <= ep.r) {
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
@@ -831,10 +1031,11 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS>::OCC))
               if (jb + q < ep.r) x.h[q] = ep.E[row * ep.e_row_stride + (int64_t)(jb + q) * ep.e_j_stride];
           }
         }
+        const bf16x8 e = x.b;
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, uhi[j].b, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, ulo[j].b, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e, uhi[j].b, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e, ulo[j].b, acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -1242,16 +1443,16 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
     const char* comma = strchr(env, ',');
     p.splits = comma ? atoi(comma + 1) : 1;
   } else {
-    // Measured on MI355X (2:4, bf16): eight-wave 256x256 tiles win once there are enough of them
-    // to fill the GPU twice, eight-wave 256x128 once those fill it (both with metadata in
-    // super-stages when C % 128 == 0), 128x64 for long reductions that would otherwise need a
-    // split; otherwise 128x128 (two workgroups per CU), splitting the reduction when even those
-    // leave CUs idle.
+    // Measured on MI355X (2:4, bf16): once 256x256 tiles fill the GPU twice, eight-wave 256x256
+    // tiles with three stages win unless the reduction is long (C >= 2R), where eight-wave 256x128
+    // tiles with four stages and metadata super-stages do; eight-wave 256x128 once those fill the
+    // GPU; 128x64 for long reductions that would otherwise need a split; otherwise 128x128 (two
+    // workgroups per CU), splitting the reduction when even those leave CUs idle.
     auto tiles = [&](int br, int bt) { return ((R + br - 1) / br) * ((T + bt - 1) / bt); };
     if (T <= 16) {
       p.cfg = cfg_by_id(30);  // few tokens: bound by reading the weight once
     } else if (pipe_ok && tiles(256, 256) >= 512) {
-      p.cfg = cfg_by_id(wide_ok ? 58 : 51);
+      p.cfg = cfg_by_id(C >= 2 * R ? (wide_ok ? 55 : 50) : 51);
     } else if (pipe_ok && tiles(256, 128) >= 240) {
       p.cfg = cfg_by_id(wide_ok ? 55 : 50);
     } else if (pipe_ok && tiles(128, 64) >= 240 && C >= 2048) {
@@ -1275,13 +1476,13 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
   return p;
 }
 
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0>
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0>
 void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
               const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
               const Plan& p, hipStream_t s) {
-  using TL = QTile<FR, FT, WR, WT, NS, MS>;
+  using TL = QTile<FR, FT, WR, WT, NS, MS, UG>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
-  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_q<FR, FT, WR, WT, NS, MS>,
+  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG>,
               dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(64 * TL::NW), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
@@ -1308,20 +1509,37 @@ void launch_w(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
 
-template <int FR, int FT, int WR, int WT, int NS>
+template <int FR, int FT, int WR, int WT, int NS, int UG = 0>
 void launch_pipe(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                  const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out,
                  float* part, const Plan& p, hipStream_t s) {
-  using TL = PTile<FR, FT, WR, WT, NS>;
+  using TL = PTile<FR, FT, WR, WT, NS, UG>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
-  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_pipe<FR, FT, WR, WT, NS>,
+  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_pipe<FR, FT, WR, WT, NS, UG>,
               dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(256), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
+}
+
+// In-kernel adapter rows (Epilogue::G): ranks up to 16, one reduction pass (no split), and the
+// configurations that keep their occupancy and registers with the 2 KB of adapter rows added to
+// each stage (the 256x128 eight-wave tile drops to 3 stages for it; the 256x256 one would spill).
+// SRA_SPMM24_FUSE=0 turns it off.
+constexpr int kFuseRank = 16;
+bool fuse_ok(const Plan& p, int64_t C, int r) {
+  if (r <= 0 || r > kFuseRank || C % 64 != 0 || p.splits != 1) return false;
+  const char* env = getenv("SRA_SPMM24_FUSE");
+  if (env && env[0] == '0') return false;
+  return p.cfg.id == 14 || p.cfg.id == 55;
 }
 
 }  // namespace
 
 namespace sra {
+
+bool spmm24_fuses_adapter(int64_t R, int64_t C, int64_t T, int r) {
+  if (T <= 0 || R <= 0) return false;
+  return fuse_ok(plan_for(R, C, T), C, r);
+}
 
 size_t spmm24_ws(int64_t R, int64_t C, int64_t T) {
   const Plan p = plan_for(R, C, T);
@@ -1334,6 +1552,16 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
   if (T == 0 || R == 0) return hipSuccess;
   const Plan p = plan_for(R, C, T);
   float* part = p.splits > 1 ? (float*)ws : nullptr;
+  const bool fuse = ep.G != nullptr;
+  if (fuse && (!fuse_ok(p, C, ep.r) || ep.g_ld % 8 != 0)) return hipErrorInvalidValue;
+  if (fuse) {
+    switch (p.cfg.id) {
+      case 14: launch_pipe<2, 1, 2, 2, 4, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+      case 55: launch_q<4, 4, 4, 2, 3, 8, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (p.cfg.id) {
     case 30: return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s);
     case 55: launch_q<4, 4, 4, 2, 4, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
