@@ -173,6 +173,26 @@ sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flag
   return SRA_OK;
 }
 
+// dB (over dY, V = U in three parts) and dA (over X, V = dU in four parts, stored transposed) as
+// jobs of the merged adapter-gradient launch; pointers are filled in by the caller.
+int grad_jobs(sra::AdapterGrad* jobs, bool db, bool da, int64_t N, int64_t K) {
+  int n = 0;
+  if (db) {
+    jobs[n] = sra::AdapterGrad{};
+    jobs[n].M = N;
+    jobs[n].parts = 3;
+    ++n;
+  }
+  if (da) {
+    jobs[n] = sra::AdapterGrad{};
+    jobs[n].M = K;
+    jobs[n].parts = 4;
+    jobs[n].out_t = true;
+    ++n;
+  }
+  return n;
+}
+
 size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool have_u,
                  bool have_du, BwdPlan* plan) {
   BwdPlan p;
@@ -202,6 +222,9 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
     if (p.need_du) g = std::max(g, sra::adapter_rows_ws(T, N, r));
     if (db) g = std::max(g, sra::adapter_cols_ws(T, N, r));
     if (da) g = std::max(g, sra::adapter_cols_ws(T, K, r));
+    sra::AdapterGrad jobs[2];
+    const int nj = grad_jobs(jobs, db, da, N, K);
+    g = std::max(g, sra::adapter_grads_ws(jobs, nj, T, r));
     p.gemm_off = a.take(g);
   }
   if (P->dtype == SRA_BF16 && P->format == SRA_FMT_NM && dx)
@@ -533,6 +556,19 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                                  P->row_ptr, 0, K, N, (const uint16_t*)dY, T, ep,
                                                  (uint16_t*)dX, s),
                        s, "bwd dX ffi"));
+  }
+  // dB and dA: one merged launch (and one slice reduction) when the shapes allow
+  sra::AdapterGrad jobs[2];
+  const int nj = grad_jobs(jobs, fdb, fda, N, K);
+  for (int i = 0; i < nj; ++i) {
+    const bool is_db = fdb && i == 0;
+    jobs[i].act = (const uint16_t*)(is_db ? dY : X);
+    jobs[i].vt = is_db ? vtU : vtdU;
+    jobs[i].out = is_db ? dB : dA;
+  }
+  if (nj > 0 && sra::adapter_grads_ok(jobs, nj, T, r)) {
+    SRA_TRY(hip_done(sra::launch_adapter_grads(jobs, nj, T, r, gws, s), s, "bwd dB, dA"));
+    return SRA_OK;
   }
   if (fdb)
     SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)dY, T, N, vtU, 3, r, false, dB, gws, s),

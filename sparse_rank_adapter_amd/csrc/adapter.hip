@@ -23,6 +23,8 @@
 // Both use v_mfma_f32_16x16x32_bf16 and move every 32-step MFMA partial into fp64 registers (fp32
 // rounding only acts inside one 32-term dot product); slices write fp64 partials that one more
 // kernel sums in a fixed order, so results are independent of scheduling.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace {
@@ -34,6 +36,27 @@ union Frag {
   uint16_t h[8];
   bf16x8v b;
 };
+
+// s_waitcnt vmcnt(N) only (expcnt / lgkmcnt left at their maxima), gfx9 encoding
+template <int N>
+SRA_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// With n stages of L transfers each in flight (1 <= n <= D), wait for the oldest stage.
+template <int L, int D>
+SRA_DEV void wait_inflight(int n) {
+  if constexpr (D > 1) {
+    if (n >= D) {
+      wait_vm<((D - 1) * L < 63 ? (D - 1) * L : 63)>();
+      return;
+    }
+    wait_inflight<L, D - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
+}
 
 template <int N>
 SRA_DEV void flush(f32x4 (&acc)[N], double (&acc64)[N][4]) {
@@ -447,6 +470,203 @@ void cols_launch(dim3 grid, hipStream_t s, const uint16_t* act, int64_t T, int64
               r, rp, Tp, t_per, out_t, part, out);
 }
 
+
+// ------------------------------------------------------------------------------------ grads
+// Both adapter gradients of the backward in one launch: each "job" is a cols product
+// Out[m][j] = sum_t Act[t][m] V[t][j] (dB: Act = dY, V = U; dA: Act = X, V = dU, transposed out).
+// A workgroup owns 64 columns m x 16*JT adapter rows j x one slice of tokens; grid.x runs over the
+// column blocks of the first job, then the second.  Tokens stream through an LDS ring of NS stages
+// of ST = 32*KG tokens, filled by buffer -> LDS DMA: every token row of the Act tile (128 bytes)
+// and every V^T row (part p, row j; 2*ST bytes) of a stage is one run, and rows past the slice or
+// past T read as zeros.  The 4*KG waves split a stage into 4 column fragments x KG 32-token groups,
+// so each wave's MFMA chain per stage is short and every SIMD holds KG waves; the KG partial sums
+// of a fragment are added in a fixed order through LDS at the end.
+// Swizzles (16-byte chunk c of LDS row x holds source chunk c ^ s(x)): Act rows s = 2((x>>3)&3), so
+// the four 8-token groups of a transposed 2-byte read fall on different banks; V^T rows
+// s = x & (2*KG*... ) as below, so 16 consecutive rows of a 16-byte fragment read do.
+template <int JT, int KG>
+struct GradTile {
+  static constexpr int JR = 16 * JT, NW = 4 * KG, ST = 32 * KG;
+  static constexpr int VROW = 2 * ST, VCH = VROW / 16;           // V^T row bytes, 16-byte chunks
+  static constexpr int A_BYTES = ST * 128, V_BYTES = 4 * JR * VROW, STAGE = A_BYTES + V_BYTES;
+  static constexpr int NS = (160 * 1024 - 4096) / STAGE < 8 ? (160 * 1024 - 4096) / STAGE : 8;
+  static constexpr int LA = A_BYTES / 1024 / NW, LV = V_BYTES / 1024 / NW, L = LA + LV;
+  static_assert(A_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0, "whole transfers per wave");
+  static_assert(NS >= 2, "two stages fit");
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int JT, int KG>
+SRA_DEV void adapter_grads_body(const sra::AdapterGradArgs& ga) {
+  using GT = GradTile<JT, KG>;
+  constexpr int JR = GT::JR, NS = GT::NS, L = GT::L, ST = GT::ST, VCH = GT::VCH;
+  constexpr int RED = (KG - 1) * 4 * JT * 4 * 64 * 8;  // k-group partials handed over at the end
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * GT::STAGE > RED ? NS * GT::STAGE : RED];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), cf = w & 3, kg = w >> 2;
+  const bool second = (int)blockIdx.x >= ga.job[0].nmb;
+  const sra::AdapterGrad job = second ? ga.job[1] : ga.job[0];
+  const int mb = (int)blockIdx.x - (second ? ga.job[0].nmb : 0);
+  const int64_t M = job.M, m0 = (int64_t)mb * 64;
+  const int j0 = blockIdx.y * JR;
+  const int64_t tb = (int64_t)blockIdx.z * ga.t_per, te = min(ga.T, tb + ga.t_per);
+  const int n_st = (int)((te - tb + ST - 1) / ST);
+
+  // Act rows [tb, te) seen from column m0; V^T parts whole
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(job.act + tb * M + m0), 0, (int)((te - tb) * M * 2 - m0 * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)job.vt, 0, (int)((int64_t)job.parts * ga.rp * ga.Tp * 2), 0x00020000);
+  uint32_t a_off[GT::LA], v_off[GT::LV];
+  int a_dst[GT::LA], v_dst[GT::LV];
+#pragma unroll
+  for (int k = 0; k < GT::LA; ++k) {  // 1 KB = 8 token rows of 128 bytes
+    const int b = k * GT::NW + w, x = 8 * b + (lane >> 3), c = (lane & 7) ^ (((x >> 3) & 3) << 1);
+    a_off[k] = (uint32_t)((x * M + c * 8) * 2);
+    a_dst[k] = b * 1024;
+  }
+#pragma unroll
+  for (int k = 0; k < GT::LV; ++k) {  // 1 KB = 64 / VCH rows of 2 ST bytes
+    const int b = k * GT::NW + w, x = b * (64 / VCH) + lane / VCH;
+    const int c = (lane % VCH) ^ ((x >> (VCH == 8 ? 1 : 0)) & (VCH - 1));
+    const int p = min(x / JR, job.parts - 1), jj = x % JR;  // parts past the job's repeat its last
+    v_off[k] = (uint32_t)((((int64_t)p * ga.rp + j0 + jj) * ga.Tp + tb + c * 8) * 2);
+    v_dst[k] = GT::A_BYTES + b * 1024;
+  }
+  auto issue = [&](int st, int buf) {
+    uint8_t* base = smem + buf * GT::STAGE;
+#pragma unroll
+    for (int k = 0; k < GT::LA; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + a_dst[k]), 16,
+                                               a_off[k] + (uint32_t)(st * ST * M * 2), 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < GT::LV; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(base + v_dst[k]), 16,
+                                               v_off[k] + (uint32_t)(st * ST * 2), 0, 0, 0);
+  };
+
+  // two accumulator sets, alternating by stage: the other (previous stage's) set moves to fp64
+  // while this stage's MFMAs run
+  f32x4 acc[2][JT];
+  double acc64[JT][4];
+#pragma unroll
+  for (int a = 0; a < JT; ++a) {
+    acc[0][a] = acc[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc64[a][e] = 0.0;
+  }
+  auto to64 = [&](f32x4 (&x)[JT]) {
+#pragma unroll
+    for (int a = 0; a < JT; ++a) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc64[a][e] += (double)x[a][e];
+      x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  const int m = 16 * cf + l16, mc = m >> 3, mo = m & 7;
+  auto compute = [&](int buf, f32x4 (&cur)[JT], f32x4 (&prev)[JT]) {
+    const uint8_t* A = smem + buf * GT::STAGE;
+    const uint8_t* V = A + GT::A_BYTES;
+    // B: Act[t][m] for this wave's 32 tokens t = 32kg + 8(l/16) .. +7 (one column per lane);
+    // A: V^T rows, the same 8 tokens
+    Frag bf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = 32 * kg + 8 * q4 + e, c = mc ^ (((t >> 3) & 3) << 1);
+      bf.h[e] = *reinterpret_cast<const uint16_t*>(A + t * 128 + c * 16 + mo * 2);
+    }
+    bf16x8v af[JT][4];
+#pragma unroll
+    for (int a = 0; a < JT; ++a)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int x = p * JR + 16 * a + l16;
+        const int c = (4 * kg + q4) ^ ((x >> (VCH == 8 ? 1 : 0)) & (VCH - 1));
+        af[a][p] = *reinterpret_cast<const bf16x8v*>(V + x * GT::VROW + c * 16);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int a = 0; a < JT; ++a)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (p < job.parts) cur[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a][p], bf.b, cur[a], 0, 0, 0);
+    to64(prev);
+  };
+
+  constexpr int D = NS - 1;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < n_st) issue(d, d);
+  for (int st = 0; st < n_st; ++st) {
+    wait_inflight<L, D>(min(D, n_st - st));
+    __builtin_amdgcn_s_barrier();
+    if (st + D < n_st) issue(st + D, (st + D) % NS);
+    if (st & 1) compute(st % NS, acc[1], acc[0]);
+    else compute(st % NS, acc[0], acc[1]);
+  }
+  to64(acc[0]);
+  to64(acc[1]);
+
+  // k-groups 1 .. KG-1 hand their sums to k-group 0, which adds them in k-group order
+  if constexpr (KG > 1) {
+    __syncthreads();  // the ring is no longer read
+    double* red = reinterpret_cast<double*>(smem);
+    if (kg > 0) {
+#pragma unroll
+      for (int a = 0; a < JT; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((((kg - 1) * 4 + cf) * JT + a) * 4 + e) * 64 + lane] = acc64[a][e];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g)
+#pragma unroll
+      for (int a = 0; a < JT; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc64[a][e] += red[((((g - 1) * 4 + cf) * JT + a) * 4 + e) * 64 + lane];
+  }
+
+  // D layout: rows j = 4(l/16) + e of adapter tile a, column m = l%16 of this fragment
+  const int64_t mg = m0 + m;
+  if (mg >= M) return;
+#pragma unroll
+  for (int a = 0; a < JT; ++a)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = j0 + 16 * a + 4 * q4 + e;
+      if (j >= ga.r) continue;
+      const int64_t o = job.out_t ? (int64_t)j * M + mg : mg * ga.r + j;
+      if (ga.S > 1)
+        job.part[(int64_t)blockIdx.z * M * ga.r + o] = acc64[a][e];
+      else
+        job.out[o] = (float)acc64[a][e];
+    }
+}
+
+// one kernel per adapter-row tile width (the body is a device template: the buffer-resource
+// builtins it uses have no host form)
+constexpr int kGradKG[3] = {4, 4, 2};  // k-groups (waves / 4) for 16, 32, 64 adapter rows
+__global__ __launch_bounds__(256 * kGradKG[0]) void k_adapter_grads16(sra::AdapterGradArgs ga) { adapter_grads_body<1, kGradKG[0]>(ga); }
+__global__ __launch_bounds__(256 * kGradKG[1]) void k_adapter_grads32(sra::AdapterGradArgs ga) { adapter_grads_body<2, kGradKG[1]>(ga); }
+__global__ __launch_bounds__(256 * kGradKG[2]) void k_adapter_grads64(sra::AdapterGradArgs ga) { adapter_grads_body<4, kGradKG[2]>(ga); }
+
+// out = sum over the S slices of each job's partials, in slice order (one thread per element of
+// the first job's output, then of the second's)
+__global__ void k_reduce_grads(sra::AdapterGradArgs ga) {
+  const int64_t n0 = ga.job[0].M * ga.r;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool second = i >= n0;
+  const sra::AdapterGrad job = second ? ga.job[1] : ga.job[0];
+  if (second) i -= n0;
+  const int64_t n = job.M * ga.r;
+  if (i >= n) return;
+  double s = 0.0;
+  for (int z = 0; z < ga.S; ++z) s += job.part[(int64_t)z * n + i];
+  job.out[i] = (float)s;
+}
+
 }  // namespace
 
 namespace sra {
@@ -528,6 +748,91 @@ hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const 
     const int64_t n = M * r;
     hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, p.S,
                        n, out, nullptr, r, nullptr, 0, 0);
+  }
+  return hipGetLastError();
+}
+
+
+// ---- merged adapter gradients
+namespace {
+struct GradsPlan {
+  int jt, njb, S;
+  int64_t t_per;
+};
+GradsPlan grads_plan(const AdapterGrad* g, int n, int64_t T, int r) {
+  GradsPlan p;
+  p.jt = pick_jt(r);
+  p.njb = (int)cdiv(r, 16 * p.jt);
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) blocks += cdiv(g[i].M, 64) * p.njb;
+  // one workgroup per CU (the ring takes most of the LDS): as many slices as keep the grid within
+  // 256 workgroups, each slice at least 256 tokens
+  int64_t S = 256 / (blocks < 1 ? 1 : blocks);
+  const char* env = getenv("SRA_GRADS_S");  // tuning override
+  if (env && *env) S = atoi(env);
+  const int64_t max_s = cdiv(T, 256);
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  p.t_per = round_up(cdiv(T, S), 64);
+  p.S = (int)cdiv(T, p.t_per);
+  return p;
+}
+}  // namespace
+
+bool adapter_grads_ok(const AdapterGrad* g, int n, int64_t T, int r) {
+  if (n < 1 || n > 2 || T <= 0 || r <= 0) return false;
+  const int64_t Tp = vt_cols(T), rp = vt_rows(r);
+  for (int i = 0; i < n; ++i) {
+    if (g[i].M <= 0 || g[i].M % 8 != 0 || g[i].parts < 1 || g[i].parts > 4) return false;
+    // 32-bit buffer offsets
+    if (T * g[i].M * 2 >= (int64_t)1 << 31 || (int64_t)g[i].parts * (rp + 64) * (Tp + 64) * 2 >= (int64_t)1 << 31)
+      return false;
+  }
+  return true;
+}
+
+size_t adapter_grads_ws(const AdapterGrad* g, int n, int64_t T, int r) {
+  if (!adapter_grads_ok(g, n, T, r)) return 0;
+  const GradsPlan p = grads_plan(g, n, T, r);
+  if (p.S <= 1) return 0;
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b += align256((size_t)p.S * g[i].M * r * sizeof(double));
+  return b;
+}
+
+hipError_t launch_adapter_grads(const AdapterGrad* g, int n, int64_t T, int r, void* ws,
+                                hipStream_t s) {
+  if (!adapter_grads_ok(g, n, T, r)) return hipErrorInvalidValue;
+  const GradsPlan p = grads_plan(g, n, T, r);
+  AdapterGradArgs ga{};
+  uint8_t* w = (uint8_t*)ws;
+  int nmb = 0;
+  for (int i = 0; i < n; ++i) {
+    ga.job[i] = g[i];
+    ga.job[i].nmb = (int)cdiv(g[i].M, 64);
+    nmb += ga.job[i].nmb;
+    if (p.S > 1) {
+      ga.job[i].part = (double*)w;
+      w += align256((size_t)p.S * g[i].M * r * sizeof(double));
+    }
+  }
+  if (n == 1) ga.job[1] = ga.job[0], ga.job[1].M = 0;  // no second job: never reached
+  ga.T = T;
+  ga.Tp = vt_cols(T);
+  ga.t_per = p.t_per;
+  ga.r = r;
+  ga.rp = (int)vt_rows(r);
+  ga.S = p.S;
+  const dim3 grid((unsigned)nmb, (unsigned)p.njb, (unsigned)p.S);
+  switch (p.jt) {
+    case 1: launch(SRA_KERNEL_ADAPTER, k_adapter_grads16, grid, dim3(256 * kGradKG[0]), 0, s, ga); break;
+    case 2: launch(SRA_KERNEL_ADAPTER, k_adapter_grads32, grid, dim3(256 * kGradKG[1]), 0, s, ga); break;
+    default: launch(SRA_KERNEL_ADAPTER, k_adapter_grads64, grid, dim3(256 * kGradKG[2]), 0, s, ga); break;
+  }
+  if (p.S > 1) {
+    int64_t tot = 0;
+    for (int i = 0; i < n; ++i) tot += g[i].M * r;
+    hipLaunchKernelGGL(k_reduce_grads, dim3((unsigned)cdiv(tot, 256)), dim3(256), 0, s, ga);
   }
   return hipGetLastError();
 }

@@ -182,5 +182,26 @@ size_t adapter_cols_ws(int64_t T, int64_t M, int r);
 hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const uint16_t* vt,
                                int parts, int r, bool out_transposed, float* out, void* ws,
                                hipStream_t s);
+// One or two cols products in one launch (dB and dA of the backward), each
+//   out[m][j] (or out[j][m] when out_t) = sum_t act[t][m] V[t][j],  V^T as `parts` bf16 parts;
+// needs M % 8 == 0 (adapter_grads_ok).  nmb and part are filled in by the launcher.
+struct AdapterGrad {
+  const uint16_t* act = nullptr;
+  const uint16_t* vt = nullptr;
+  float* out = nullptr;
+  double* part = nullptr;
+  int64_t M = 0;
+  int parts = 0, nmb = 0;
+  bool out_t = false;
+};
+struct AdapterGradArgs {
+  AdapterGrad job[2];
+  int64_t T, Tp, t_per;
+  int r, rp, S;
+};
+bool adapter_grads_ok(const AdapterGrad* g, int n, int64_t T, int r);
+size_t adapter_grads_ws(const AdapterGrad* g, int n, int64_t T, int r);
+hipError_t launch_adapter_grads(const AdapterGrad* g, int n, int64_t T, int r, void* ws,
+                                hipStream_t s);
 
 }  // namespace sra
