@@ -2,11 +2,12 @@
 // pass": a fixed N:M mask chosen at initialisation, then the pruned weight is transposed and
 // N:M-pruned again for the backward product; §2.3 keeps compressed forms of both).
 //
-// Both kernels are memory-bound one-pass rewrites.  Each lane owns whole 4-element groups, so the
-// top-2 selection is a rank-by-count over four magnitude keys held in registers (six compares per
-// group); no cross-lane traffic is needed for the first prune.  The second prune groups along the
-// output dimension, which is strided in memory, so a 128 x 64 tile of the compressed weight is
-// decompressed into LDS and each lane then ranks one column's groups.
+// All kernels are memory-bound one-pass rewrites.  Each lane owns whole 4-element groups, so the
+// top-2 selection needs no cross-lane traffic for the first prune.  The second prune groups along
+// the output dimension, which is strided in memory, so a tile of the first prune's output is
+// expanded into LDS and each lane then ranks one column's groups.  bf16 (the training path) runs
+// on 128 x 128 tiles with a branch-free selection (top2_net, gather2); fp32 keeps the
+// rank-by-count selection on 128 x 64 tiles.
 #include "common.h"
 
 namespace {
@@ -26,6 +27,35 @@ SRA_DEV void top2_of4(const uint32_t k[4], int& p0, int& p1) {
   p1 = kept[1];
 }
 
+// bf16 selection without branches or indexed registers: with the position folded into the low bits of
+// each key (lower position = larger tiebreak), the four keys are distinct, a max/min network gives
+// the largest and the second largest, their low bits give the positions, and one byte permute
+// gathers both kept bf16 values from the group's two 32-bit words.  Same choice as top2_of4.
+constexpr uint32_t kPrunedMark = 0xFFFFu;
+
+// positions p0 < p1 of the two largest keys (k < 2^30; ties: the lower position wins)
+SRA_DEV void top2_net(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3, uint32_t& p0, uint32_t& p1) {
+  const uint32_t K0 = (k0 << 2) | 3u, K1 = (k1 << 2) | 2u, K2 = (k2 << 2) | 1u, K3 = k3 << 2;
+  const uint32_t a = max(K0, K1), b = min(K0, K1), c = max(K2, K3), d = min(K2, K3);
+  const uint32_t first = max(a, c), second = max(min(a, c), max(b, d));
+  const uint32_t pa = 3u - (first & 3u), pb = 3u - (second & 3u);
+  p0 = min(pa, pb);
+  p1 = max(pa, pb);
+}
+// the bf16 values at positions p0, p1 of a group held as words lo = (x0, x1), hi = (x2, x3)
+SRA_DEV uint32_t gather2(uint32_t lo, uint32_t hi, uint32_t p0, uint32_t p1) {
+  const uint32_t sel = (p0 * 0x0202u + 0x0100u) | ((p1 * 0x0202u + 0x0100u) << 16);
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// the group's words with pruned halves replaced by the mark (kept: positions p0, p1)
+SRA_DEV void mark_pruned(uint32_t& lo, uint32_t& hi, uint32_t p0, uint32_t p1) {
+  const uint32_t m = (1u << p0) | (1u << p1);
+  lo |= ((m & 1u) ? 0u : 0x0000FFFFu) | ((m & 2u) ? 0u : 0xFFFF0000u);
+  hi |= ((m & 4u) ? 0u : 0x0000FFFFu) | ((m & 8u) ? 0u : 0xFFFF0000u);
+}
+SRA_DEV uint32_t second_key(uint32_t v) { return v == kPrunedMark ? 0u : (v & 0x7FFFu) + 1u; }
+
+
 // One lane per 32-column block of a row: 8 groups -> 16 kept values + one metadata word.
 template <typename T>
 __global__ __launch_bounds__(256) void k_compress24(const T* __restrict__ W, int64_t rows,
@@ -40,18 +70,26 @@ __global__ __launch_bounds__(256) void k_compress24(const T* __restrict__ W, int
   const u32x4* src = reinterpret_cast<const u32x4*>(W + row * cols + w * 32);
 #pragma unroll
   for (int i = 0; i < 32 / VEC; ++i) x.v[i] = src[i];
-  union { u32x4 v[16 / VEC]; T e[16]; } o;
+  union { u32x4 v[16 / VEC]; T e[16]; uint32_t w[8]; } o;
   uint32_t word = 0;
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
-    uint32_t k[4];
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t lo = x.v[g / 2][2 * (g & 1)], hi = x.v[g / 2][2 * (g & 1) + 1];
+      uint32_t p0, p1;
+      top2_net(lo & 0x7FFFu, (lo >> 16) & 0x7FFFu, hi & 0x7FFFu, (hi >> 16) & 0x7FFFu, p0, p1);
+      o.w[g] = gather2(lo, hi, p0, p1);
+      word |= (p0 | (p1 << 2)) << (4 * g);
+    } else {
+      uint32_t k[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) k[a] = mag_key(x.e[4 * g + a]);
-    int p0, p1;
-    top2_of4(k, p0, p1);
-    o.e[2 * g] = x.e[4 * g + p0];
-    o.e[2 * g + 1] = x.e[4 * g + p1];
-    word |= (uint32_t)(p0 | (p1 << 2)) << (4 * g);
+      for (int a = 0; a < 4; ++a) k[a] = mag_key(x.e[4 * g + a]);
+      int p0, p1;
+      top2_of4(k, p0, p1);
+      o.e[2 * g] = x.e[4 * g + p0];
+      o.e[2 * g + 1] = x.e[4 * g + p1];
+      word |= (uint32_t)(p0 | (p1 << 2)) << (4 * g);
+    }
   }
   u32x4* dst = reinterpret_cast<u32x4*>(vals + row * (cols / 2) + w * 16);
 #pragma unroll
@@ -125,7 +163,8 @@ __global__ __launch_bounds__(256) void k_double_prune24(const T* __restrict__ va
 }
 
 // Both prunes in one pass over W, for training loops that refresh Ws and P together after each
-// weight update: a 128 x 64 tile of W is read once; each lane ranks one row's 32-column block (the
+// weight update (fp32 weights; bf16 has the 128 x 128 tile kernel below): a 128 x 64 tile of W is
+// read once; each lane ranks one row's 32-column block (the
 // first prune, written to Ws as in k_compress24) and drops the survivors' keys and values into the
 // LDS tiles the second prune reads (as k_double_prune24 builds them from Ws), then each lane ranks
 // one column's 32-row block and writes P.  Same selection code, so the bits match the two-kernel
@@ -200,6 +239,153 @@ __global__ __launch_bounds__(256) void k_compress_pair24(const T* __restrict__ W
   pm[prow * (rows / 32) + ostart / 32] = word;
 }
 
+
+// bf16 pair on 128 x 128 tiles, so that both outputs leave as whole 128-byte row segments: Ws rows
+// (64 kept values of the tile's 128 columns) and P rows (64 kept values of its 128 rows).  The LDS
+// tile holds the first prune's output in place -- kept values as they are, pruned positions as the
+// NaN pattern 0xFFFF (weights are finite) -- and the second prune derives its magnitude keys from
+// it (pruned: 0, kept: |w| key + 1), which is what the two-kernel path ranks.
+//
+// Second prune of a 128 x 128 LDS tile of the first prune's output (kept values, pruned positions
+// marked): lane = (column, 64-row half), two 32-row blocks of 8 groups each; writes one 16-value
+// slice and one metadata word of P's row per block.
+constexpr int kTileLD = 128 + 8;  // LDS row stride (elements), 16-byte multiple
+SRA_DEV void second_prune_tile(const uint16_t* tile, int64_t c0, int64_t r0, int64_t rows,
+                               int64_t cols, uint16_t* __restrict__ pv, uint32_t* __restrict__ pm) {
+  constexpr int LD = kTileLD;
+  const int tid = threadIdx.x;
+  const int c = tid & 127, b = tid >> 7;
+  const int64_t prow = c0 + c;
+  if (prow >= cols) return;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int lr0 = 64 * b + 32 * q;
+    const int64_t ostart = r0 + lr0;
+    if (ostart >= rows) break;
+    union { u32x4 v[2]; uint32_t w[8]; } o;
+    uint32_t word = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      uint32_t v[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) v[a] = tile[(lr0 + 4 * g + a) * LD + c];
+      uint32_t p0, p1;
+      top2_net(second_key(v[0]), second_key(v[1]), second_key(v[2]), second_key(v[3]), p0, p1);
+      uint32_t y = gather2(v[0] | (v[1] << 16), v[2] | (v[3] << 16), p0, p1);
+      // a group with fewer than two survivors pads with +0.0
+      if ((y & 0xFFFFu) == kPrunedMark) y &= 0xFFFF0000u;
+      if ((y >> 16) == kPrunedMark) y &= 0x0000FFFFu;
+      o.w[g] = y;
+      word |= (p0 | (p1 << 2)) << (4 * g);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(pv + prow * (rows / 2) + ostart / 2);
+    dst[0] = o.v[0];
+    dst[1] = o.v[1];
+    pm[prow * (rows / 32) + ostart / 32] = word;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __restrict__ W,
+                                                          int64_t rows, int64_t cols,
+                                                          uint16_t* __restrict__ vals,
+                                                          uint32_t* __restrict__ meta,
+                                                          uint16_t* __restrict__ pv,
+                                                          uint32_t* __restrict__ pm) {
+  constexpr int LD = kTileLD;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * LD];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 128, r0 = (int64_t)blockIdx.y * 128;
+  {
+    // first prune: lane = (row, 64-column half), two 32-column blocks
+    const int lr = tid >> 1, h = tid & 1;
+    const int64_t row = r0 + lr;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int lc = 64 * h + 32 * q;
+      const int64_t cb = c0 + lc;
+      union { u32x4 v[4]; uint32_t w[16]; } x;
+      if (row < rows && cb < cols) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(W + row * cols + cb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x.v[i] = src[i];
+        union { u32x4 v[2]; uint32_t w[8]; } o;
+        uint32_t word = 0;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          uint32_t lo = x.w[2 * g], hi = x.w[2 * g + 1], p0, p1;
+          top2_net(lo & 0x7FFFu, (lo >> 16) & 0x7FFFu, hi & 0x7FFFu, (hi >> 16) & 0x7FFFu, p0, p1);
+          o.w[g] = gather2(lo, hi, p0, p1);
+          word |= (p0 | (p1 << 2)) << (4 * g);
+          mark_pruned(lo, hi, p0, p1);
+          x.w[2 * g] = lo;
+          x.w[2 * g + 1] = hi;
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(vals + row * (cols / 2) + cb / 2);
+        dst[0] = o.v[0];
+        dst[1] = o.v[1];
+        meta[row * (cols / 32) + cb / 32] = word;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x.v[i] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&tile[lr * LD + lc + 8 * i]) = x.v[i];
+    }
+  }
+  __syncthreads();
+  second_prune_tile(tile, c0, r0, rows, cols, pv, pm);
+}
+
+
+// bf16 double prune on 128 x 128 tiles of Ws (128 rows x 128 logical columns = 64 stored values,
+// one 128-byte run per row): each lane expands one row's 64-column half into the LDS tile (kept
+// values at their positions, the mark elsewhere, one byte permute per two positions), then the
+// tile goes through the same second prune as the pair kernel.
+__global__ __launch_bounds__(256) void k_double_prune24t(const uint16_t* __restrict__ vals,
+                                                         const uint32_t* __restrict__ meta,
+                                                         int64_t rows, int64_t cols,
+                                                         uint16_t* __restrict__ pv,
+                                                         uint32_t* __restrict__ pm) {
+  constexpr int LD = kTileLD;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * LD];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 128, r0 = (int64_t)blockIdx.y * 128;
+  {
+    const int lr = tid >> 1, h = tid & 1;
+    const int64_t row = r0 + lr;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int lc = 64 * h + 32 * q;
+      const int64_t cb = c0 + lc;
+      union { u32x4 v[4]; uint32_t w[16]; } x;
+      if (row < rows && cb < cols) {
+        union { u32x4 v[2]; uint32_t w[8]; } in;
+        const u32x4* src = reinterpret_cast<const u32x4*>(vals + row * (cols / 2) + cb / 2);
+        in.v[0] = src[0];
+        in.v[1] = src[1];
+        const uint32_t word = meta[row * (cols / 32) + cb / 32];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          const uint32_t p0 = (word >> (4 * g)) & 3u, p1 = (word >> (4 * g + 2)) & 3u;
+          // byte pairs of {mark, mark : v1, v0}: v0 = 0x0100, v1 = 0x0302, mark = 0x0504
+          uint32_t sel[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) sel[a] = a == (int)p0 ? 0x0100u : a == (int)p1 ? 0x0302u : 0x0504u;
+          x.w[2 * g] = __builtin_amdgcn_perm(0xFFFFFFFFu, in.w[g], sel[0] | (sel[1] << 16));
+          x.w[2 * g + 1] = __builtin_amdgcn_perm(0xFFFFFFFFu, in.w[g], sel[2] | (sel[3] << 16));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x.v[i] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&tile[lr * LD + lc + 8 * i]) = x.v[i];
+    }
+  }
+  __syncthreads();
+  second_prune_tile(tile, c0, r0, rows, cols, pv, pm);
+}
+
 }  // namespace
 
 namespace sra {
@@ -207,13 +393,15 @@ namespace sra {
 hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
                                   uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
+  if (dtype == SRA_BF16) {
+    const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+    launch(SRA_KERNEL_COMPRESS, k_compress_pair24t, grid, dim3(256), 0, s, (const uint16_t*)W, rows,
+           cols, (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
-  if (dtype == SRA_BF16)
-    launch(SRA_KERNEL_COMPRESS, k_compress_pair24<uint16_t>, grid, dim3(256), 0, s,
-           (const uint16_t*)W, rows, cols, (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
-  else
-    launch(SRA_KERNEL_COMPRESS, k_compress_pair24<uint32_t>, grid, dim3(256), 0, s,
-           (const uint32_t*)W, rows, cols, (uint32_t*)vals, meta, (uint32_t*)p_vals, p_meta);
+  launch(SRA_KERNEL_COMPRESS, k_compress_pair24<uint32_t>, grid, dim3(256), 0, s,
+         (const uint32_t*)W, rows, cols, (uint32_t*)vals, meta, (uint32_t*)p_vals, p_meta);
   return hipGetLastError();
 }
 
@@ -234,13 +422,15 @@ hipError_t launch_compress24(int dtype, const void* W, int64_t rows, int64_t col
 hipError_t launch_double_prune24(int dtype, const void* vals, const uint32_t* meta, int64_t rows,
                                  int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
+  if (dtype == SRA_BF16) {
+    const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+    launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune24t, grid, dim3(256), 0, s, (const uint16_t*)vals,
+           meta, rows, cols, (uint16_t*)p_vals, p_meta);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
-  if (dtype == SRA_BF16)
-    launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune24<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)vals,
-                       meta, rows, cols, (uint16_t*)p_vals, p_meta);
-  else
-    launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune24<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)vals,
-                       meta, rows, cols, (uint32_t*)p_vals, p_meta);
+  launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune24<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)vals,
+         meta, rows, cols, (uint32_t*)p_vals, p_meta);
   return hipGetLastError();
 }
 
