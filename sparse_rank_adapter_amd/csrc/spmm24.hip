@@ -390,6 +390,13 @@ SRA_DEV void dma16(const void* g, uint8_t* lds_block) {
 SRA_DEV void dma4(const void* g, uint8_t* lds_block) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_block, 4, 0, 0);
 }
+// buffer -> LDS transfer of `size` bytes per lane at lane offset `voff` + wave-uniform `soff`
+SRA_DEV void bdma(__amdgpu_buffer_rsrc_t rs, uint8_t* lds_block, int size, uint32_t voff, int soff) {
+  if (size == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds_block, 16, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds_block, 4, voff, soff, 0, 0);
+}
 // s_waitcnt vmcnt(N) only (expcnt / lgkmcnt left at their maxima), gfx9 encoding
 template <int N>
 SRA_DEV void wait_vm() {
@@ -534,60 +541,63 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_s
   const int c_beg = z * stages_per_split;
   const int c_end = min(nC_all, c_beg + stages_per_split);
 
-  // Per-lane source pointers for stage 0; stage c adds c*32 values / c*64 activations / 2c words.
-  const uint16_t* a_src[TL::LA];
-  int a_dst[TL::LA];
+  // Operands through buffer resources based at the tile: each lane's offset is fixed and the stage
+  // moves an SGPR offset (c*64 bytes of values, c*8 of metadata, c*128 of activations and adapter
+  // rows), so issuing a stage costs no vector address arithmetic; rows past R, T or r are out of
+  // range and read as zeros.
+  const int rows_here = (int)min((int64_t)BR, R - row0), toks_here = (int)min((int64_t)BT, T - t0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s_vals + row0 * cv), 0, rows_here * (int)C, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s_meta + row0 * cm), 0, rows_here * (int)cm * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(act + t0 * C), 0, toks_here * (int)C * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ep.G, 0, UG > 0 ? ep.r * (int)ep.g_ld * 2 : 0, 0x00020000);
+  uint32_t a_off[TL::LA], m_off[TL::LM], b_off[TL::LB];
+  int a_dst[TL::LA], m_dst[TL::LM], b_dst[TL::LB];
 #pragma unroll
   for (int k = 0; k < TL::LA; ++k) {
     const int b = k * 4 + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
     const int ch = pos ^ ((row >> 2) & 3);
-    const int64_t grow = min(row0 + row, R - 1);
-    a_src[k] = s_vals + grow * cv + ch * 8;
+    a_off[k] = (uint32_t)(row * C + ch * 16);
     a_dst[k] = b * 1024;
   }
-  const uint32_t* m_src[TL::LM];
-  int m_dst[TL::LM];
 #pragma unroll
   for (int k = 0; k < TL::LM; ++k) {
     const int b = k * 4 + wave, row = 32 * b + (lane >> 1);
-    const int64_t grow = min(row0 + row, R - 1);
-    m_src[k] = s_meta + grow * cm + (lane & 1);
+    m_off[k] = (uint32_t)((row * cm + (lane & 1)) * 4);
     m_dst[k] = TL::A_BYTES + b * 256;
   }
-  const uint16_t* b_src[TL::LB];
-  int b_dst[TL::LB];
 #pragma unroll
   for (int k = 0; k < TL::LB; ++k) {
     const int b = k * 4 + wave, tk = 8 * b + (lane >> 3), pos = lane & 7;
     const int ch = pos ^ ((tk >> 1) & 7);
-    const int64_t gt = min(t0 + tk, T - 1);
-    b_src[k] = act + gt * C + ch * 8;
+    b_off[k] = (uint32_t)((tk * C + ch * 8) * 2);
     b_dst[k] = TL::A_BYTES + TL::M_BYTES + b * 1024;
   }
-  // adapter rows: transfer k*4 + wave (< GT) moves rows BT + 8(k*4 + wave) .. +7 (G rows past r
-  // repeat row r-1: finite, and their products meet zero E entries)
+  // adapter rows: transfer k*4 + wave (< GT) moves rows BT + 8(k*4 + wave) .. +7 of the region
   constexpr int NG = TL::GW + (TL::GX ? 1 : 0);
-  const uint16_t* g_src[NG ? NG : 1];
+  uint32_t g_off[NG ? NG : 1];
   int g_dst[NG ? NG : 1];
 #pragma unroll
   for (int k = 0; k < NG; ++k) {
     const int b = k * 4 + wave, tk = BT + 8 * b + (lane >> 3), pos = lane & 7;
     const int ch = pos ^ ((tk >> 1) & 7);
-    const int jr = min(tk - BT, ep.r - 1);
-    g_src[k] = ep.G + (int64_t)jr * ep.g_ld + ch * 8;
+    g_off[k] = (uint32_t)(((tk - BT) * ep.g_ld + ch * 8) * 2);
     g_dst[k] = TL::A_BYTES + TL::M_BYTES + (BT / 8 + b) * 1024;
   }
   auto issue = [&](int c, int buf) {
     uint8_t* base = smem + buf * TL::STAGE;
 #pragma unroll
-    for (int k = 0; k < TL::LA; ++k) dma16(a_src[k] + (int64_t)c * 32, base + a_dst[k]);
+    for (int k = 0; k < TL::LA; ++k) bdma(ra, base + a_dst[k], 16, a_off[k], c * 64);
 #pragma unroll
-    for (int k = 0; k < TL::LM; ++k) dma4(m_src[k] + (int64_t)c * 2, base + m_dst[k]);
+    for (int k = 0; k < TL::LM; ++k) bdma(rm, base + m_dst[k], 4, m_off[k], c * 8);
 #pragma unroll
-    for (int k = 0; k < TL::LB; ++k) dma16(b_src[k] + (int64_t)c * BC, base + b_dst[k]);
+    for (int k = 0; k < TL::LB; ++k) bdma(rb, base + b_dst[k], 16, b_off[k], c * 128);
 #pragma unroll
     for (int k = 0; k < NG; ++k)
-      if (k < TL::GW || wave < TL::GX) dma16(g_src[k] + (int64_t)c * BC, base + g_dst[k]);
+      if (k < TL::GW || wave < TL::GX) bdma(rg, base + g_dst[k], 16, g_off[k], c * 128);
   };
   AD ad;
   if constexpr (UG > 0) ad.zero();
@@ -643,11 +653,24 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_s
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (c_beg + d < c_end) issue(c_beg + d, d);
-  for (int c = c_beg; c < c_end; ++c) {
+  // Steady state, unrolled by the ring depth so that every buffer index (LDS addresses, DMA
+  // destinations) is a constant: D stages in flight at each wait.
+  int c = c_beg;
+  for (; c + NS + D <= c_end; c += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      if (TL::GX && wave < TL::GX) wait_vm<((D - 1) * TL::L1 < 63 ? (D - 1) * TL::L1 : 63)>();
+      else wait_vm<((D - 1) * L < 63 ? (D - 1) * L : 63)>();
+      __builtin_amdgcn_s_barrier();  // stage c+u visible to all waves; stage c+u-1 consumed
+      issue(c + u + D, (u + D) % NS);
+      compute(u);
+    }
+  }
+  for (; c < c_end; ++c) {
     const int in_flight = min(D, c_end - c);  // stages c .. c+in_flight-1 were issued
     if (TL::GX && wave < TL::GX) wait_stages<TL::L1>(in_flight);
     else wait_stages<L>(in_flight);
-    __builtin_amdgcn_s_barrier();  // stage c visible to all waves; stage c-1 fully consumed
+    __builtin_amdgcn_s_barrier();
     if (c + D < c_end) issue(c + D, (c - c_beg + D) % NS);
     compute((c - c_beg) % NS);
   }
