@@ -160,6 +160,7 @@ struct BwdPlan {
   bool need_du = false, need_u = false, own_du = false, own_u = false;
   size_t u_off = 0, du_off = 0, u64_off = 0, du64_off = 0, gemm_off = 0, spmm_off = 0, total = 0;
   size_t wt_off = 0, vtu_off = 0, vtdu_off = 0;  // packed B^T, split U^T (dB), split dU^T (dA)
+  size_t at_off = 0;                             // packed A^T (dX epilogue)
 };
 
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
@@ -214,6 +215,7 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   if (p.own_u) p.u_off = a.take((size_t)T * r * 4);
   if (p.own_du) p.du_off = a.take((size_t)T * r * 4);
   if (p.need_du) p.wt_off = a.take(sra::adapter_wt_bytes(N, r));
+  if (dx_ad) p.at_off = a.take(sra::adapter_at_bytes(K, r));
   if (db && r > 0) p.vtu_off = a.take(sra::adapter_vt_bytes(T, r, 3));
   if (da && r > 0) p.vtdu_off = a.take(sra::adapter_vt_bytes(T, r, 4));  // dU (fp64 sum) split for dA
   if (P->dtype == SRA_BF16 && r > 0) {
@@ -523,8 +525,9 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
   if (plan.own_u)
     SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, r,
                                               (float*)Uv, nullptr, nullptr, gws, s), s, "bwd U"));
-  SRA_TRY(hip_done(sra::launch_adapter_bwd_prep((const uint16_t*)B, N, r, wt, Uv, T, vtU, s), s,
-                   "bwd prep"));
+  uint16_t* at = dx_ad ? (uint16_t*)(wsb + plan.at_off) : nullptr;
+  SRA_TRY(hip_done(sra::launch_adapter_bwd_prep((const uint16_t*)B, N, r, wt, (const uint16_t*)A, K,
+                                                at, Uv, T, vtU, s), s, "bwd prep"));
   // dU = dY B: computed inside the dX SpMM (which also writes dU_out and dU^T's parts for dA)
   // when its plan allows, else by the adapter kernel first
   const bool fuse = dx_ad && P->format == SRA_FMT_NM && sra::spmm24_fuses_adapter(K, N, T, r);
@@ -534,9 +537,9 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
   if (fdx) {
     sra::Epilogue ep;
     ep.U = dU;
-    ep.E = (const uint16_t*)A;
-    ep.e_row_stride = 1;
-    ep.e_j_stride = K;
+    ep.E = at;  // A^T rows: E(k, j) = A[j][k]
+    ep.e_row_stride = sra::packed_at_ld(r);
+    ep.e_j_stride = 1;
     ep.r = dx_ad ? r : 0;
     if (fuse) {
       ep.G = wt;

@@ -207,45 +207,68 @@ __global__ __launch_bounds__(256) void k_adapter_rows(const uint16_t* __restrict
   }
 }
 
-// Backward prep, one launch for two independent inputs of the adapter gradients:
-//   blocks [0, n_pack):  wt[j][c] = B[c][j] (c < C, j < r; rows of stride ldw), a 64 x 64 tile per
-//                        block transposed through LDS so reads and writes are coalesced;
-//   blocks [n_pack, ..): vt[p][j][t], U^T split into three bf16 parts (j < rp, t < Tp, zero
-//                        outside r x T), 256 entries per block.
-__global__ void k_bwd_prep(const uint16_t* __restrict__ B, int64_t C, int r, int64_t ldw,
-                           uint16_t* __restrict__ wt, int n_pack, int pack_cx,
-                           const float* __restrict__ U, int64_t T, int rp, int64_t Tp,
-                           uint16_t* __restrict__ vt) {
+// dst[y][x] = src[x][y] for a 64 x 64 tile (src rows x < X of Y elements, dst rows of stride ld),
+// transposed through LDS so reads and writes are coalesced; 256 threads.
+SRA_DEV void transpose_tile(const uint16_t* __restrict__ src, int64_t X, int64_t Y,
+                            uint16_t* __restrict__ dst, int64_t ld, int64_t x0, int64_t y0,
+                            uint16_t (*tile)[65]) {
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 4 rows at a time
+  uint16_t v[16];  // all loads issued before the first LDS store
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int64_t x = x0 + ty + 4 * k, y = y0 + tx;
+    v[k] = (x < X && y < Y) ? src[x * Y + y] : (uint16_t)0;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) tile[ty + 4 * k][tx] = v[k];
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t y = y0 + i, x = x0 + tx;
+    if (y < Y && x < X) dst[y * ld + x] = tile[tx][i];
+  }
+}
+
+// Backward prep, one launch for the independent inputs of the adapter products:
+//   blocks [0, nb):        wt[j][c] = B[c][j] (c < C, j < r; rows of stride ldw), the dU operand;
+//   blocks [nb, nb + na):  at[k][j] = A[j][k] (k < K, j < r; rows of stride lda), the dX epilogue's
+//                          E operand as 16-byte rows;
+//   blocks [nb + na, ..):  vt[p][j][t], U^T split into three bf16 parts (j < rp, t < Tp, zero
+//                          outside r x T), 256 entries per block.
+struct PrepArgs {
+  const uint16_t* B;
+  int64_t C, ldw;
+  uint16_t* wt;
+  int nb, b_cx;  // B^T tiles, tiles along C
+  const uint16_t* A;
+  int64_t K, lda;
+  uint16_t* at;
+  int na, a_cx;  // A^T tiles, tiles along K
+  const float* U;
+  int64_t T, Tp;
+  int r, rp;
+  uint16_t* vt;
+};
+__global__ void k_bwd_prep(PrepArgs pa) {
   __shared__ uint16_t tile[64][65];
   const int bid = blockIdx.x;
-  if (bid < n_pack) {
-    const int64_t c0 = (int64_t)(bid % pack_cx) * 64;
-    const int j0 = (bid / pack_cx) * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 256 threads: 4 rows at a time
-    uint16_t v[16];  // all loads issued before the first LDS store
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int64_t c = c0 + ty + 4 * k;
-      const int j = j0 + tx;
-      v[k] = (c < C && j < r) ? B[c * r + j] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) tile[ty + 4 * k][tx] = v[k];
-    __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-      const int j = j0 + i;
-      const int64_t c = c0 + tx;
-      if (j < r && c < C) wt[(int64_t)j * ldw + c] = tile[tx][i];
-    }
+  if (bid < pa.nb) {
+    transpose_tile(pa.B, pa.C, pa.r, pa.wt, pa.ldw, (int64_t)(bid % pa.b_cx) * 64,
+                   (int64_t)(bid / pa.b_cx) * 64, tile);
     return;
   }
-  const int64_t i = (int64_t)(bid - n_pack) * 256 + threadIdx.x;  // i = j * Tp + t
-  if (i >= (int64_t)rp * Tp) return;
-  const int j = (int)(i / Tp);
-  const int64_t t = i - (int64_t)j * Tp;
+  if (bid < pa.nb + pa.na) {
+    const int b = bid - pa.nb;
+    transpose_tile(pa.A, pa.r, pa.K, pa.at, pa.lda, (int64_t)(b / pa.a_cx) * 64,
+                   (int64_t)(b % pa.a_cx) * 64, tile);
+    return;
+  }
+  const int64_t i = (int64_t)(bid - pa.nb - pa.na) * 256 + threadIdx.x;  // i = j * Tp + t
+  if (i >= (int64_t)pa.rp * pa.Tp) return;
+  const int j = (int)(i / pa.Tp);
+  const int64_t t = i - (int64_t)j * pa.Tp;
   uint16_t p[3] = {0, 0, 0};
-  if (j < r && t < T) split3_bf16(U[t * r + j], p[0], p[1], p[2]);
-  for (int q = 0; q < 3; ++q) vt[((int64_t)q * rp + j) * Tp + t] = p[q];
+  if (j < pa.r && t < pa.T) split3_bf16(pa.U[t * pa.r + j], p[0], p[1], p[2]);
+  for (int q = 0; q < 3; ++q) pa.vt[((int64_t)q * pa.rp + j) * pa.Tp + t] = p[q];
 }
 
 // ------------------------------------------------------------------------------------ cols
@@ -600,7 +623,7 @@ SRA_DEV void adapter_grads_body(const sra::AdapterGradArgs& ga) {
     if (d < n_st) issue(d, d);
   for (int st = 0; st < n_st; ++st) {
     wait_inflight<L, D>(min(D, n_st - st));
-    __builtin_amdgcn_s_barrier();
+    ring_barrier();
     if (st + D < n_st) issue(st + D, (st + D) % NS);
     if (st & 1) compute(st % NS, acc[1], acc[0]);
     else compute(st % NS, acc[0], acc[1]);
@@ -677,19 +700,37 @@ size_t adapter_vt_bytes(int64_t T, int r, int parts) {
   return align256((size_t)parts * vt_rows(r) * vt_cols(T) * 2);
 }
 int64_t packed_wt_ld(int64_t C) { return round_up(C, 8); }
+int64_t packed_at_ld(int r) { return round_up(r, 8); }
+size_t adapter_at_bytes(int64_t K, int r) { return align256((size_t)K * packed_at_ld(r) * 2); }
 size_t adapter_wt_bytes(int64_t C, int r) { return align256((size_t)r * packed_wt_ld(C) * 2); }
 
 hipError_t launch_adapter_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* wt,
-                                   const float* U, int64_t T, uint16_t* vtU, hipStream_t s) {
-  if (r == 0 || (!wt && !vtU)) return hipSuccess;
-  const int pack_cx = wt ? (int)cdiv(N, 64) : 0;
-  const int n_pack = wt ? pack_cx * (int)cdiv(r, 64) : 0;
-  const int rp = (int)vt_rows(r);
-  const int64_t Tp = vt_cols(T);
-  const int n_split = vtU ? (int)cdiv((int64_t)rp * Tp, 256) : 0;
-  if (n_pack + n_split == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)(n_pack + n_split)), dim3(256), 0, s, B, N, r,
-                     packed_wt_ld(N), wt, n_pack, pack_cx > 0 ? pack_cx : 1, U, T, rp, Tp, vtU);
+                                   const uint16_t* A, int64_t K, uint16_t* at, const float* U,
+                                   int64_t T, uint16_t* vtU, hipStream_t s) {
+  if (r == 0 || (!wt && !at && !vtU)) return hipSuccess;
+  PrepArgs pa{};
+  pa.B = B;
+  pa.C = N;
+  pa.ldw = packed_wt_ld(N);
+  pa.wt = wt;
+  pa.b_cx = (int)cdiv(N, 64);
+  pa.nb = wt ? pa.b_cx * (int)cdiv(r, 64) : 0;
+  pa.A = A;
+  pa.K = K;
+  pa.lda = packed_at_ld(r);
+  pa.at = at;
+  pa.a_cx = (int)cdiv(K, 64);
+  pa.na = at ? pa.a_cx * (int)cdiv(r, 64) : 0;
+  pa.U = U;
+  pa.T = T;
+  pa.r = r;
+  pa.rp = (int)vt_rows(r);
+  pa.Tp = vt_cols(T);
+  pa.vt = vtU;
+  const int n_split = vtU ? (int)cdiv((int64_t)pa.rp * pa.Tp, 256) : 0;
+  const int blocks = pa.nb + pa.na + n_split;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)blocks), dim3(256), 0, s, pa);
   return hipGetLastError();
 }
 

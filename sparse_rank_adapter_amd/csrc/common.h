@@ -72,6 +72,15 @@ SRA_DEV void write_vt4(uint16_t* __restrict__ vt, int rp, int64_t Tp, int j, int
   for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + t] = p4[p];
 }
 
+// Workgroup barrier of the LDS-DMA rings: a bare s_barrier (no memory fence, so it does not wait
+// for the transfers still in flight), fenced for the compiler's scheduler on both sides, so that
+// no LDS read of the next stage is hoisted above it (nor one of the previous stage sunk below it).
+SRA_DEV void ring_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- host-side launchers implemented in the kernel sources (internal C++ linkage)
 namespace sra {
 
@@ -165,15 +174,19 @@ hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t*
 //   cols: out[m][j] = sum_t act[t][m] * V[t][j], written as [m][j] or transposed [j][m] (dB, dA)
 // rows also writes an fp64 copy (out64) and/or V^T split into four bf16 parts (vt) when non-null;
 // cols reads V^T as `parts` bf16 parts vt[p][j][t], rows vt_rows(r), columns vt_cols(T), zero past
-// T.  The backward prep kernel packs B^T for the dU product (wt [r][packed_wt_ld(N)]) and splits
-// U^T into three parts for dB; either output may be null.
+// T.  The backward prep kernel packs B^T for the dU product (wt [r][packed_wt_ld(N)]) and A^T for
+// the dX epilogue, and splits U^T into three parts for dB; any output may be null.
 int64_t vt_rows(int r);
 int64_t vt_cols(int64_t T);
 size_t adapter_vt_bytes(int64_t T, int r, int parts);
 int64_t packed_wt_ld(int64_t C);
 size_t adapter_wt_bytes(int64_t C, int r);
+// at [K][packed_at_ld(r)] = A^T, rows of r adapter entries (16-byte aligned) for the dX epilogue
+int64_t packed_at_ld(int r);
+size_t adapter_at_bytes(int64_t K, int r);
 hipError_t launch_adapter_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* wt,
-                                   const float* U, int64_t T, uint16_t* vtU, hipStream_t s);
+                                   const uint16_t* A, int64_t K, uint16_t* at, const float* U,
+                                   int64_t T, uint16_t* vtU, hipStream_t s);
 size_t adapter_rows_ws(int64_t T, int64_t C, int r);
 hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const uint16_t* wt,
                                int64_t ldw, int r, float* out, double* out64, uint16_t* vt,

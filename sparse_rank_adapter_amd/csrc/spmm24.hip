@@ -661,7 +661,7 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_s
     for (int u = 0; u < NS; ++u) {
       if (TL::GX && wave < TL::GX) wait_vm<((D - 1) * TL::L1 < 63 ? (D - 1) * TL::L1 : 63)>();
       else wait_vm<((D - 1) * L < 63 ? (D - 1) * L : 63)>();
-      __builtin_amdgcn_s_barrier();  // stage c+u visible to all waves; stage c+u-1 consumed
+      ring_barrier();  // stage c+u visible to all waves; stage c+u-1 consumed
       issue(c + u + D, (u + D) % NS);
       compute(u);
     }
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_s
     const int in_flight = min(D, c_end - c);  // stages c .. c+in_flight-1 were issued
     if (TL::GX && wave < TL::GX) wait_stages<TL::L1>(in_flight);
     else wait_stages<L>(in_flight);
-    __builtin_amdgcn_s_barrier();
+    ring_barrier();
     if (c + D < c_end) issue(c + D, (c - c_beg + D) % NS);
     compute((c - c_beg) % NS);
   }
@@ -845,35 +845,43 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::O
   const int c_beg = z * stages_per_split;
   const int c_end = min(nC_all, c_beg + stages_per_split);
 
-  const uint16_t* a_src[TL::LA];
+  // operands through buffer resources based at the tile (fixed lane offsets, the stage offset in
+  // an SGPR; rows past R, T or r read as zeros), as in k_spmm24_pipe
+  const int rows_here = (int)min((int64_t)BR, R - row0), toks_here = (int)min((int64_t)BT, T - t0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s_vals + row0 * cv), 0, rows_here * (int)C, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s_meta + row0 * cm), 0, rows_here * (int)cm * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(act + t0 * C), 0, toks_here * (int)C * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ep.G, 0, UG > 0 ? ep.r * (int)ep.g_ld * 2 : 0, 0x00020000);
+  uint32_t a_off[TL::LA];
   int a_dst[TL::LA];
 #pragma unroll
   for (int k = 0; k < TL::LA; ++k) {
     const int b = k * NW + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
     const int ch = pos ^ ((row >> 2) & 3);
-    const int64_t grow = min(row0 + row, R - 1);
-    a_src[k] = s_vals + grow * cv + ch * 8;
+    a_off[k] = (uint32_t)(row * C + ch * 16);
     a_dst[k] = b * 1024;
   }
-  const uint32_t* m_src[TL::LM ? TL::LM : 1];
+  uint32_t m_off[TL::LM ? TL::LM : 1];
   int m_dst[TL::LM ? TL::LM : 1];
 #pragma unroll
   for (int k = 0; k < TL::LM; ++k) {
     const int b = k * NW + wave, row = 32 * b + (lane >> 1);
-    const int64_t grow = min(row0 + row, R - 1);
-    m_src[k] = s_meta + grow * cm + (lane & 1);
+    m_off[k] = (uint32_t)((row * cm + (lane & 1)) * 4);
     m_dst[k] = TL::A_BYTES + b * 256;
   }
   // super-stage metadata: 1 KB block b = 16 rows x 64 B; slot lane%4 holds 16-byte chunk
   // slot^((row>>2)&3), chunk ch = stages 2ch and 2ch+1 of the super-stage
-  const uint32_t* ms_row[TL::LMS ? TL::LMS : 1];
+  uint32_t ms_row[TL::LMS ? TL::LMS : 1];
   int ms_ch[TL::LMS ? TL::LMS : 1], ms_dst[TL::LMS ? TL::LMS : 1];
 #pragma unroll
   for (int k = 0; k < TL::LMS; ++k) {
     const int b = k * NW + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
     ms_ch[k] = pos ^ ((row >> 2) & 3);
-    const int64_t grow = min(row0 + row, R - 1);
-    ms_row[k] = s_meta + grow * cm;
+    ms_row[k] = (uint32_t)(row * cm * 4);
     ms_dst[k] = b * 1024;
   }
   uint8_t* const msbuf = smem + NS * TL::STAGE;
@@ -881,43 +889,41 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::O
     uint8_t* base = msbuf + (g & 1) * TL::MSB;
 #pragma unroll
     for (int k = 0; k < TL::LMS; ++k) {
-      int64_t w = 2 * ((int64_t)c_beg + MS * g) + 4 * ms_ch[k];  // two words per stage
-      if (w > cm - 4) w = cm - 4;  // past the row's end: clamped, never read
-      dma16(ms_row[k] + w, base + ms_dst[k]);
+      int w = 2 * (c_beg + MS * g) + 4 * ms_ch[k];  // two words per stage
+      if (w > (int)cm - 4) w = (int)cm - 4;  // past the row's end: clamped, never read
+      bdma(rm, base + ms_dst[k], 16, ms_row[k] + (uint32_t)w * 4, 0);
     }
   };
-  const uint16_t* b_src[TL::LB];
+  uint32_t b_off[TL::LB];
   int b_dst[TL::LB];
 #pragma unroll
   for (int k = 0; k < TL::LB; ++k) {
     const int b = k * NW + wave, tk = 8 * b + (lane >> 3), pos = lane & 7;
     const int ch = pos ^ ((tk >> 1) & 7);
-    const int64_t gt = min(t0 + tk, T - 1);
-    b_src[k] = act + gt * C + ch * 8;
+    b_off[k] = (uint32_t)((tk * C + ch * 8) * 2);
     b_dst[k] = TL::A_BYTES + TL::M_BYTES + b * 1024;
   }
   constexpr int NG = TL::GW + (TL::GX ? 1 : 0);
-  const uint16_t* g_src[NG ? NG : 1];
+  uint32_t g_off[NG ? NG : 1];
   int g_dst[NG ? NG : 1];
 #pragma unroll
   for (int k = 0; k < NG; ++k) {
     const int b = k * NW + wave, tk = BT + 8 * b + (lane >> 3), pos = lane & 7;
     const int ch = pos ^ ((tk >> 1) & 7);
-    const int jr = min(tk - BT, ep.r - 1);
-    g_src[k] = ep.G + (int64_t)jr * ep.g_ld + ch * 8;
+    g_off[k] = (uint32_t)(((tk - BT) * ep.g_ld + ch * 8) * 2);
     g_dst[k] = TL::A_BYTES + TL::M_BYTES + (BT / 8 + b) * 1024;
   }
   auto issue = [&](int c, int buf) {
     uint8_t* base = smem + buf * TL::STAGE;
 #pragma unroll
-    for (int k = 0; k < TL::LA; ++k) dma16(a_src[k] + (int64_t)c * 32, base + a_dst[k]);
+    for (int k = 0; k < TL::LA; ++k) bdma(ra, base + a_dst[k], 16, a_off[k], c * 64);
 #pragma unroll
-    for (int k = 0; k < TL::LM; ++k) dma4(m_src[k] + (int64_t)c * 2, base + m_dst[k]);
+    for (int k = 0; k < TL::LM; ++k) bdma(rm, base + m_dst[k], 4, m_off[k], c * 8);
 #pragma unroll
-    for (int k = 0; k < TL::LB; ++k) dma16(b_src[k] + (int64_t)c * BC, base + b_dst[k]);
+    for (int k = 0; k < TL::LB; ++k) bdma(rb, base + b_dst[k], 16, b_off[k], c * 128);
 #pragma unroll
     for (int k = 0; k < NG; ++k)
-      if (k < TL::GW || wave < TL::GX) dma16(g_src[k] + (int64_t)c * BC, base + g_dst[k]);
+      if (k < TL::GW || wave < TL::GX) bdma(rg, base + g_dst[k], 16, g_off[k], c * 128);
   };
   AD ad;
   if constexpr (UG > 0) ad.zero();
@@ -977,13 +983,31 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::O
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (c_beg + d < c_end) issue(c_beg + d, d);
-  for (int c = c_beg; c < c_end; ++c) {
-    // waiting for at most (in_flight-1)*L outstanding transfers completes stage c and every older
-    // one, including the metadata of stage c's super-stage (issued before stage c's own loads)
+  // waiting for at most (in_flight-1)*L outstanding transfers completes stage c and every older
+  // one, including the metadata of stage c's super-stage (issued before stage c's own loads).
+  // Steady state unrolled by the ring depth: constant buffer indices, D stages in flight (not for
+  // the largest wave tiles, whose registers are spoken for).
+  constexpr bool kUnroll = FR * FT < 32;
+  int c = c_beg;
+  for (; kUnroll && c + NS + D <= c_end; c += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      if (TL::GX && wave < TL::GX) wait_vm<((D - 1) * TL::L1 < 63 ? (D - 1) * TL::L1 : 63)>();
+      else wait_vm<((D - 1) * L < 63 ? (D - 1) * L : 63)>();
+      ring_barrier();
+      const int rel = c + u - c_beg;
+      if constexpr (MS > 0) {
+        if (rel % MS == 0 && c + u + MS < c_end) issue_meta(rel / MS + 1);
+      }
+      issue(c + u + D, (u + D) % NS);
+      compute(u, rel);
+    }
+  }
+  for (; c < c_end; ++c) {
     const int in_flight = min(D, c_end - c);
     if (TL::GX && wave < TL::GX) wait_stages<TL::L1>(in_flight);
     else wait_stages<L>(in_flight);
-    __builtin_amdgcn_s_barrier();
+    ring_barrier();
     const int rel = c - c_beg;
     if constexpr (MS > 0) {
       if (rel % MS == 0 && c + MS < c_end) issue_meta(rel / MS + 1);
@@ -1264,7 +1288,7 @@ __global__ __launch_bounds__(256, 1) void k_spmm24_w(
     if (in_flight >= 3) wait_vm<(2 * L < 63 ? 2 * L : 63)>();
     else if (in_flight == 2) wait_vm<L>();
     else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();  // stage c visible; stage c-1 and its super-stage reads done
+    ring_barrier();  // stage c visible; stage c-1 and its super-stage reads done
     const int rel = c - c_beg;
     if (rel % MS == 0 && c + MS < c_end) issue_meta(rel / MS + 1);
     if (c + D < c_end) issue(c + D, (rel + D) % NS);
@@ -1552,7 +1576,7 @@ bool fuse_ok(const Plan& p, int64_t C, int r) {
   if (r <= 0 || r > kFuseRank || C % 64 != 0 || p.splits != 1) return false;
   const char* env = getenv("SRA_SPMM24_FUSE");
   if (env && env[0] == '0') return false;
-  return p.cfg.id == 14 || p.cfg.id == 55;
+  return p.cfg.id == 14 || p.cfg.id == 55 || p.cfg.id == 56;
 }
 
 }  // namespace
@@ -1581,6 +1605,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
     switch (p.cfg.id) {
       case 14: launch_pipe<2, 1, 2, 2, 4, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
       case 55: launch_q<4, 4, 4, 2, 3, 8, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+      case 56: launch_q<4, 2, 2, 2, 3, 8, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -100,11 +100,12 @@ def test_ragged_shapes(gpu, T, K, N, r, dtype):
     run_nm(wl, seed=T + K)
 
 
-@pytest.mark.parametrize("cfg", [14, 55])
+@pytest.mark.parametrize("cfg", [14, 55, 56])
 @pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (77, 384, 640, 5), (130, 256, 128, 1)])
 def test_in_kernel_adapter_rows(gpu, monkeypatch, cfg, T, K, N, r):
-    """Ranks <= 16 on the 128x64 and eight-wave 256x128 tiles: U (forward) and dU (backward, with
-    dU^T's parts for dA and the zero columns past T) are computed inside the SpMM."""
+    """Ranks <= 16 on the 128x64 tiles (32x32 and 16x16x64 forms) and the eight-wave 256x128 tiles:
+    U (forward) and dU (backward, with dU^T's parts for dA and the zero columns past T) are
+    computed inside the SpMM."""
     monkeypatch.setenv("SRA_SPMM24_CFG", str(cfg))
     wl = Workload("fused", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
     run_nm(wl, seed=T + r)
