@@ -39,8 +39,8 @@ PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the kernel configuration the planner picks for
 # that call; a key missing here (kernel changed since the counters were taken) reports null.
 TRAFFIC_BYTES = {
-    "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27355.7 * 1024 * 2.0 + 4352.0 * 1024,
-    "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13826.3 * 1024 * 2.0 + 16512.0 * 1024,
+    "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
+    "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
     "opt66b_ffn_decode/T16/k_decode24": 196310.1 * 1024 * 2.0 + 1152.5 * 1024,
 }
 
