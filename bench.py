@@ -343,7 +343,7 @@ def bench_ffi(args, wl):
     import torch
 
     import sparse_rank_adapter_amd as sra
-    from sparse_rank_adapter_amd._abi import SRA_KERNEL_SPMM_FFI
+    from sparse_rank_adapter_amd._abi import SRA_KERNEL_FFI_DENSIFY, SRA_KERNEL_SPMM_FFI
     from sra_inputs import layer_inputs
 
     dev = torch.device("cuda:0")
@@ -370,8 +370,11 @@ def bench_ffi(args, wl):
     ms_fwd = time_graph(fwd, args.steps, args.warmup, graph)
     ms_bwd = time_graph(bwd, args.steps, args.warmup, graph)
     reps = max(10, args.steps)
+    # the product kernel (densified weight on dense MFMA for these shapes) and the densify pass
     k_fwd = time_kernel(SRA_KERNEL_SPMM_FFI, fwd, reps)
     k_bwd = time_kernel(SRA_KERNEL_SPMM_FFI, bwd, reps)
+    k_dens_f = time_kernel(SRA_KERNEL_FFI_DENSIFY, fwd, reps)
+    k_dens_b = time_kernel(SRA_KERNEL_FFI_DENSIFY, bwd, reps)
     Wd = W.contiguous()
     d_fwd = time_graph(lambda: torch.nn.functional.linear(X, Wd), args.steps, args.warmup, graph)
     d_bwd = time_graph(lambda: torch.matmul(dY, Wd), args.steps, args.warmup, graph)
@@ -381,8 +384,10 @@ def bench_ffi(args, wl):
             "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5),
             "dense_eq_tflops": round(dense_eq / ((ms_fwd + ms_bwd) * 1e-3) / 1e12, 2),
             "spmm_fwd_kernel_ms": round(k_fwd, 5), "spmm_bwd_kernel_ms": round(k_bwd, 5),
-            "spmm_fwd_tflops": round(sparse_flops / (k_fwd * 1e-3) / 1e12, 2),
-            "spmm_fwd_frac_fp32_valu": round(sparse_flops / (k_fwd * 1e-3) / PEAK_FP32_VALU, 4),
+            "densify_fwd_ms": round(k_dens_f, 5), "densify_bwd_ms": round(k_dens_b, 5),
+            "spmm_fwd_stored_tflops": round(sparse_flops / (k_fwd * 1e-3) / 1e12, 2),
+            # the densified product runs the dense flops on bf16 MFMA
+            "spmm_fwd_frac_bf16_mfma": round(2 * T * wl.N * wl.K / (k_fwd * 1e-3) / PEAK_BF16_FLOPS, 4),
             "dense_fwd_ms": round(d_fwd, 5), "dense_dx_ms": round(d_bwd, 5),
             "speedup_vs_dense": round((d_fwd + d_bwd) / (ms_fwd + ms_bwd), 3),
             "compress_ffi_ms": round(ms_setup, 5)}

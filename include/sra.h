@@ -207,7 +207,8 @@ enum {
   SRA_KERNEL_SPMM24 = 3,       /* bf16 2:4 SpMM + fused adapter epilogue (forward Y, backward dX) */
   SRA_KERNEL_ADAPTER = 4,      /* adapter products U, dU, dB, dA (one launch each) */
   SRA_KERNEL_DECODE24 = 5,     /* bf16 2:4 decode SpMM (forward with T <= 16) */
-  SRA_KERNEL_SPMM_FFI = 6      /* bf16 fixed fan-in SpMM (forward Y, backward dX) */
+  SRA_KERNEL_SPMM_FFI = 6,     /* bf16 fixed fan-in SpMM (forward Y, backward dX) */
+  SRA_KERNEL_FFI_DENSIFY = 7   /* bf16 fixed fan-in weight expanded to dense rows before the SpMM */
 };
 
 /*

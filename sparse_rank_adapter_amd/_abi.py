@@ -23,6 +23,7 @@ EXPORTS = (
 )
 SRA_KERNEL_COMPRESS, SRA_KERNEL_DOUBLE_PRUNE, SRA_KERNEL_SPMM24 = 1, 2, 3
 SRA_KERNEL_ADAPTER, SRA_KERNEL_DECODE24, SRA_KERNEL_SPMM_FFI = 4, 5, 6
+SRA_KERNEL_FFI_DENSIFY = 7
 
 
 class SraSparse(ctypes.Structure):

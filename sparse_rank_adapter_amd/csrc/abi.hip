@@ -124,7 +124,7 @@ sra::F32Sparse f32_view(const sra_sparse* S) {
 
 // ---------------------------------------------------------------- forward plan
 struct FwdPlan {
-  size_t u_off = 0, u64_off = 0, gemm_off = 0, total = 0;
+  size_t u_off = 0, u64_off = 0, gemm_off = 0, ffi_off = 0, total = 0;
   bool own_u = false;
 };
 
@@ -148,6 +148,7 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
     size_t g = r > 0 ? sra::adapter_rows_ws(T, Ws->cols, r) : 0;
     if (Ws->format == SRA_FMT_NM) g = std::max(g, sra::spmm24_ws(Ws->rows, Ws->cols, T));
     p.gemm_off = a.take(g);
+    if (Ws->format == SRA_FMT_ELL) p.ffi_off = a.take(sra::spmm_ffi_ws(Ws->rows, Ws->cols, T));
   }
 
   p.total = a.used;
@@ -231,6 +232,8 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   }
   if (P->dtype == SRA_BF16 && P->format == SRA_FMT_NM && dx)
     p.spmm_off = a.take(sra::spmm24_ws(K, N, T));
+  if (P->dtype == SRA_BF16 && P->format == SRA_FMT_CSR && dx)
+    p.spmm_off = a.take(sra::spmm_ffi_ws(K, N, T));
   p.total = a.used;
   if (plan) *plan = p;
   return p.total;
@@ -255,7 +258,7 @@ sra_status sra_time_next_kernel(int32_t which, void* start, void* stop) {
     g_time_which = 0;
     return SRA_OK;
   }
-  if (which < SRA_KERNEL_COMPRESS || which > SRA_KERNEL_SPMM_FFI)
+  if (which < SRA_KERNEL_COMPRESS || which > SRA_KERNEL_FFI_DENSIFY)
     return fail(SRA_ERR_INVALID_ARG, "unknown kernel class %d", which);
   if (!start || !stop) return fail(SRA_ERR_INVALID_ARG, "start and stop events are required");
   g_time_which = which;
@@ -451,7 +454,7 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
                     s, "fwd spmm 2:4");
   return hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_ELL, (const uint16_t*)Ws->values, Ws->index,
                                             nullptr, Ws->k, N, K, (const uint16_t*)X, T, ep,
-                                            (uint16_t*)Y, s),
+                                            (uint16_t*)Y, wsb ? wsb + plan.ffi_off : nullptr, s),
                   s, "fwd spmm ffi");
 }
 
@@ -557,7 +560,7 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     else
       SRA_TRY(hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_CSR, (const uint16_t*)P->values, P->index,
                                                  P->row_ptr, 0, K, N, (const uint16_t*)dY, T, ep,
-                                                 (uint16_t*)dX, s),
+                                                 (uint16_t*)dX, wsb ? wsb + plan.spmm_off : nullptr, s),
                        s, "bwd dX ffi"));
   }
   // dB and dA: one merged launch (and one slice reduction) when the shapes allow

@@ -163,11 +163,16 @@ size_t spmm24_decode_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
                                 uint16_t* out, hipStream_t s);
-// fixed fan-in bf16 SpMM (ELL forward / CSR backward) with the same epilogue
+// Out[t][row] = sum_c Act[t][c] Wd[row][c] + epilogue, Wd dense bf16 [R][C] (C % 64 == 0)
+hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uint16_t* act, int64_t T,
+                             const Epilogue& ep, uint16_t* out, hipStream_t s);
+// fixed fan-in bf16 SpMM (ELL forward / CSR backward) with the same epilogue; with enough tokens
+// it densifies the weight into the workspace (spmm_ffi_ws bytes) and runs the dense MFMA kernel
+size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t* idx,
                                 const int32_t* row_ptr, int k, int64_t R, int64_t C,
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
-                                hipStream_t s);
+                                void* ws, hipStream_t s);
 
 // Adapter products (fp32 results):
 //   rows: out[t][j] = sum_c act[t][c] * wt[j*ldw + c]                              (U, dU)

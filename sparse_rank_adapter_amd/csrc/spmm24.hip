@@ -803,15 +803,21 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_s
 // stage, so MS = 8 gives 64-byte runs instead of 8-byte ones, which LDS-DMA moves ~7x faster per
 // byte) into a double buffer of its own, one super-stage ahead; needs C % 128 == 0 and no split.
 // UG > 0: adapter rows in the activation region as in PTile (GT transfers over NW waves).
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0>
+// DN: the weight is dense (rows of C bf16, 128 bytes per row and stage, no metadata) and the
+// products are pairs of dense v_mfma_f32_16x16x32_bf16 -- the fixed fan-in layer's densified
+// weight.
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false>
 struct QTile {
+  static_assert(!(DN && (MS || UG)), "dense weights have no metadata or adapter rows");
   static constexpr int NW = WR * WT;  // waves per workgroup: 4 or 8
   static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
-  static constexpr int LA = BR / (16 * NW), LM = MS ? 0 : BR / (32 * NW), LB = BT / (8 * NW);
+  static constexpr int LA = BR / ((DN ? 8 : 16) * NW), LM = (MS || DN) ? 0 : BR / (32 * NW);
+  static constexpr int LB = BT / (8 * NW);
   static constexpr int GT = UG / 8, GW = GT / NW, GX = GT % NW;
   static constexpr int L = LA + LM + LB + GW;  // waves >= GX
   static constexpr int L1 = L + (GX ? 1 : 0);  // waves < GX
-  static constexpr int A_BYTES = BR * 64, M_BYTES = MS ? 0 : BR * 8, B_BYTES = (BT + UG) * 128;
+  static constexpr int A_BYTES = BR * (DN ? 128 : 64), M_BYTES = (MS || DN) ? 0 : BR * 8;
+  static constexpr int B_BYTES = (BT + UG) * 128;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
   static constexpr int MSB = MS ? BR * MS * 8 : 0;            // one metadata super-stage buffer
   static constexpr int LMS = MS ? MSB / (1024 * NW) : 0;      // its 1 KB transfers per wave
@@ -819,12 +825,12 @@ struct QTile {
   static constexpr int OCC = (NW == 8 || FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
 };
 
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0>
-__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::OCC)) void k_spmm24_q(
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false>
+__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
     float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
-  using TL = QTile<FR, FT, WR, WT, NS, MS, UG>;
+  using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN>;
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   constexpr int NW = TL::NW;
   using AD = AdapterRows<BT, (UG > 0 ? UG : 16), NW>;
@@ -848,10 +854,11 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::O
   // operands through buffer resources based at the tile (fixed lane offsets, the stage offset in
   // an SGPR; rows past R, T or r read as zeros), as in k_spmm24_pipe
   const int rows_here = (int)min((int64_t)BR, R - row0), toks_here = (int)min((int64_t)BT, T - t0);
+  constexpr int A_ROW = DN ? 128 : 64;  // weight bytes per row and stage
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(s_vals + row0 * cv), 0, rows_here * (int)C, 0x00020000);
+      (void*)(s_vals + row0 * (DN ? C : cv)), 0, rows_here * (int)C * (DN ? 2 : 1), 0x00020000);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(s_meta + row0 * cm), 0, rows_here * (int)cm * 4, 0x00020000);
+      (void*)(DN ? nullptr : s_meta + row0 * cm), 0, DN ? 0 : rows_here * (int)cm * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(act + t0 * C), 0, toks_here * (int)C * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
@@ -860,9 +867,14 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::O
   int a_dst[TL::LA];
 #pragma unroll
   for (int k = 0; k < TL::LA; ++k) {
-    const int b = k * NW + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
-    const int ch = pos ^ ((row >> 2) & 3);
-    a_off[k] = (uint32_t)(row * C + ch * 16);
+    const int b = k * NW + wave;
+    if constexpr (DN) {  // 8 rows of 128 bytes, chunk swizzle (row >> 1) & 7 as for tokens
+      const int row = 8 * b + (lane >> 3), ch = (lane & 7) ^ ((row >> 1) & 7);
+      a_off[k] = (uint32_t)((row * C + ch * 8) * 2);
+    } else {             // 16 rows of 64 bytes
+      const int row = 16 * b + (lane >> 2), ch = (lane & 3) ^ ((row >> 2) & 3);
+      a_off[k] = (uint32_t)(row * C + ch * 16);
+    }
     a_dst[k] = b * 1024;
   }
   uint32_t m_off[TL::LM ? TL::LM : 1];
@@ -916,7 +928,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::O
   auto issue = [&](int c, int buf) {
     uint8_t* base = smem + buf * TL::STAGE;
 #pragma unroll
-    for (int k = 0; k < TL::LA; ++k) bdma(ra, base + a_dst[k], 16, a_off[k], c * 64);
+    for (int k = 0; k < TL::LA; ++k) bdma(ra, base + a_dst[k], 16, a_off[k], c * A_ROW);
 #pragma unroll
     for (int k = 0; k < TL::LM; ++k) bdma(rm, base + m_dst[k], 4, m_off[k], c * 8);
 #pragma unroll
@@ -949,6 +961,27 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG>::O
       const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + ((q4 ^ sw) << 4));
       const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
       bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    }
+    if constexpr (DN) {
+      // dense weight rows: columns 8(l/16)..+7 and 32+8(l/16)..+7 of the stage, one dense MFMA each
+      bf16x8 alo[FR], ahi[FR];
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int r = wr * 16 * FR + i * 16 + l16, sw = (r >> 1) & 7;
+        alo[i] = *reinterpret_cast<const bf16x8*>(A + r * 128 + ((q4 ^ sw) << 4));
+        ahi[i] = *reinterpret_cast<const bf16x8*>(A + r * 128 + (((4 + q4) ^ sw) << 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+          const bf16x8 blo = __builtin_shufflevector(bfr[j], bfr[j], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 bhi = __builtin_shufflevector(bfr[j], bfr[j], 8, 9, 10, 11, 12, 13, 14, 15);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[i], blo, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[i], bhi, acc[i][j], 0, 0, 0);
+        }
+      return;
     }
     bf16x8 af[FR];
     uint32_t mword[FR];
@@ -1523,13 +1556,13 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
   return p;
 }
 
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0>
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false>
 void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
               const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
-              const Plan& p, hipStream_t s) {
-  using TL = QTile<FR, FT, WR, WT, NS, MS, UG>;
+              const Plan& p, hipStream_t s, int which = SRA_KERNEL_SPMM24) {
+  using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
-  sra::launch(SRA_KERNEL_SPMM24, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG>,
+  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN>,
               dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(64 * TL::NW), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
@@ -1582,6 +1615,19 @@ bool fuse_ok(const Plan& p, int64_t C, int r) {
 }  // namespace
 
 namespace sra {
+
+hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uint16_t* act, int64_t T,
+                             const Epilogue& ep, uint16_t* out, hipStream_t s) {
+  if (T == 0 || R == 0) return hipSuccess;
+  if (C % 64 != 0 || ep.G) return hipErrorInvalidValue;
+  Plan p{cfg_by_id(13), 1, (int)(C / 64)};
+  const int64_t big = ((R + 255) / 256) * ((T + 127) / 128);
+  if (big >= 240)  // eight waves, 256x128 tiles, 3 stages of 48 KB
+    launch_q<4, 4, 4, 2, 3, 0, 0, true>(Wd, nullptr, R, C, act, T, ep, out, nullptr, p, s, SRA_KERNEL_SPMM_FFI);
+  else             // four waves, 128x64 tiles, 4 stages of 24 KB
+    launch_q<4, 2, 2, 2, 4, 0, 0, true>(Wd, nullptr, R, C, act, T, ep, out, nullptr, p, s, SRA_KERNEL_SPMM_FFI);
+  return hipGetLastError();
+}
 
 bool spmm24_fuses_adapter(int64_t R, int64_t C, int64_t T, int r) {
   if (T <= 0 || R <= 0) return false;

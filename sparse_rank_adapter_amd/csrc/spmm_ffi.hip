@@ -170,15 +170,51 @@ __global__ __launch_bounds__(256) void k_spmm_ffi(int format, const uint16_t* __
   }
 }
 
+// Densify one sparse row per workgroup: the row is cleared and its (index, value) pairs scattered
+// in LDS, then written out as C contiguous bf16 (C % 8 == 0; indices within a row are distinct).
+__global__ __launch_bounds__(256) void k_ffi_densify(int format, const uint16_t* __restrict__ vals,
+                                                     const int16_t* __restrict__ idx,
+                                                     const int32_t* __restrict__ row_ptr, int k,
+                                                     int64_t C, uint16_t* __restrict__ Wd) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t rowbuf[];  // C elements
+  const int64_t n = blockIdx.x;
+  for (int64_t c = threadIdx.x * 8; c < C; c += 256 * 8)
+    *reinterpret_cast<u32x4*>(&rowbuf[c]) = u32x4{0, 0, 0, 0};
+  __syncthreads();
+  const int64_t b = format == SRA_FMT_ELL ? n * k : row_ptr[n];
+  const int64_t e = format == SRA_FMT_ELL ? b + k : row_ptr[n + 1];
+  for (int64_t i = b + threadIdx.x; i < e; i += 256) rowbuf[idx[i]] = vals[i];
+  __syncthreads();
+  for (int64_t c = threadIdx.x * 8; c < C; c += 256 * 8)
+    *reinterpret_cast<u32x4*>(&Wd[n * C + c]) = *reinterpret_cast<const u32x4*>(&rowbuf[c]);
+}
+
+// The densified product pays one pass writing R x C bf16 and then runs at dense MFMA rate; worth
+// it once the token tile is wide enough to reuse each weight row many times.
+bool use_dense(int64_t R, int64_t C, int64_t T) { return T >= 128 && C % 64 == 0 && C * 2 <= 65536 && R > 0; }
+
 }  // namespace
 
 namespace sra {
 
+size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T) {
+  return use_dense(R, C, T) ? (size_t)R * C * 2 : 0;
+}
+
 hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t* idx,
                                 const int32_t* row_ptr, int k, int64_t R, int64_t C,
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
-                                hipStream_t s) {
+                                void* ws, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
+  if (use_dense(R, C, T)) {
+    if (!ws) return hipErrorInvalidValue;
+    uint16_t* Wd = (uint16_t*)ws;
+    launch(SRA_KERNEL_FFI_DENSIFY, k_ffi_densify, dim3((unsigned)R), dim3(256), (size_t)C * 2, s,
+           format, vals, idx, row_ptr, k, C, Wd);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_dense_bf16(Wd, R, C, act, T, ep, out, s);
+  }
   const dim3 grid((unsigned)((T + TT - 1) / TT), (unsigned)((R + RB - 1) / RB));
   launch(SRA_KERNEL_SPMM_FFI, k_spmm_ffi, grid, dim3(256), 0, s, format, vals, idx, row_ptr, k, R,
          C, act, T, ep, out);

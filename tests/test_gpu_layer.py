@@ -210,7 +210,10 @@ def run_ffi(wl: Workload, T=None, seed=0, rows=None, cols_n=None, kcols=None):
     rep.check()
 
 
-@pytest.mark.parametrize("T,K,N,k,r", [(3, 37, 5, 7, 2), (130, 300, 64, 17, 16), (64, 512, 200, 64, 0)])
+# (T >= 128 with the reduction a multiple of 64 runs the densified MFMA path: (257, 192, 320) in
+# both directions, (130, 300, 64) in the backward, (300, 640, 200) in the forward)
+@pytest.mark.parametrize("T,K,N,k,r", [(3, 37, 5, 7, 2), (130, 300, 64, 17, 16), (64, 512, 200, 64, 0),
+                                       (257, 192, 320, 20, 16), (300, 640, 200, 40, 8)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ffi_ragged(gpu, T, K, N, k, r, dtype):
     wl = Workload("ffi_ragged", T=T, K=K, N=N, r=r, dtype=dtype, fmt="ffi", ffi_k=k)
