@@ -690,6 +690,171 @@ __global__ void k_reduce_grads(sra::AdapterGradArgs ga) {
   job.out[i] = (float)s;
 }
 
+// ------------------------------------------------------------------------------ rows, ring
+// The rows product for ranks above 32 at training token counts.  The small-tile rows kernel reads
+// the whole weight operand once per 16 tokens, which at r = 128 and C = 20480 (dU = dY B) is
+// gigabytes of L2 / Infinity Cache traffic; here a workgroup owns 128 tokens x JR = 16 JT adapter
+// columns over a slice of c, and both operands stream through an NS-deep LDS ring of 64-column
+// stages filled by buffer -> LDS DMA (one 128-byte run per row; token rows past T and adapter rows
+// past r read as zeros through the buffer range checks).  Wave w owns tokens 16w .. 16w+15 and all
+// JR columns: per stage 2 x JT mfma_f32_16x16x32_bf16 into one of two fp32 accumulator sets, the
+// other (previous stage's) set moving into fp64 meanwhile, so fp32 rounding only acts inside one
+// stage's 64-term dot products.
+// LDS rows are 128 bytes; 16-byte chunk k of row x sits in slot k ^ ((x >> 1) & 7), so the 16 rows
+// of one fragment read spread over the banks.
+// Requires C % 64 == 0, c_per % 64 == 0, ldw % 8 == 0 and 16-byte aligned act / wt.
+template <int JT>
+struct RowsRing {
+  static constexpr int TT = 128, JR = 16 * JT, NW = 8;
+  static constexpr int A_BYTES = TT * 128, G_BYTES = JR * 128, STAGE = A_BYTES + G_BYTES;
+  static constexpr int NS = 4;
+  static constexpr int LA = A_BYTES / 1024 / NW, LG = G_BYTES / 1024 / NW, L = LA + LG;
+  static_assert(A_BYTES % (1024 * NW) == 0 && G_BYTES % (1024 * NW) == 0, "whole transfers per wave");
+  static_assert(NS * STAGE <= 160 * 1024, "ring fits in LDS");
+};
+
+SRA_DEV int rows_swz(int x) { return (x >> 1) & 7; }
+
+template <int JT>
+SRA_DEV void adapter_rows_ring_body(const uint16_t* __restrict__ act, int64_t T, int64_t C,
+                                    const uint16_t* __restrict__ wt, int64_t ldw, int r,
+                                    int64_t c_per, double* __restrict__ part,
+                                    float* __restrict__ out, double* __restrict__ out64,
+                                    uint16_t* __restrict__ vt, int rp, int64_t Tp) {
+  using RR = RowsRing<JT>;
+  constexpr int NS = RR::NS, L = RR::L, NW = RR::NW;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * RR::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = (int64_t)blockIdx.x * RR::TT;
+  const int j0 = blockIdx.y * RR::JR;
+  const int64_t cb = (int64_t)blockIdx.z * c_per, ce = min(C, cb + c_per);
+  const int n_st = (int)((ce - cb) / 64);
+
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(act + t0 * C + cb), 0, (int)(((T - t0) * C - cb) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wt + (int64_t)j0 * ldw + cb), 0, (int)(((int64_t)(r - j0) * ldw - cb) * 2), 0x00020000);
+  uint32_t a_off[RR::LA], g_off[RR::LG];
+  int a_dst[RR::LA], g_dst[RR::LG];
+#pragma unroll
+  for (int k = 0; k < RR::LA; ++k) {  // 1 KB = 8 rows of 128 bytes
+    const int b = k * NW + w, x = 8 * b + (lane >> 3), c = (lane & 7) ^ rows_swz(x);
+    a_off[k] = (uint32_t)((x * C + c * 8) * 2);
+    a_dst[k] = b * 1024;
+  }
+#pragma unroll
+  for (int k = 0; k < RR::LG; ++k) {
+    const int b = k * NW + w, x = 8 * b + (lane >> 3), c = (lane & 7) ^ rows_swz(x);
+    g_off[k] = (uint32_t)((x * ldw + c * 8) * 2);
+    g_dst[k] = RR::A_BYTES + b * 1024;
+  }
+  auto issue = [&](int st, int buf) {
+    uint8_t* base = smem + buf * RR::STAGE;
+#pragma unroll
+    for (int k = 0; k < RR::LA; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + a_dst[k]), 16,
+                                               a_off[k] + (uint32_t)(st * 128), 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < RR::LG; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_ptr_t)(base + g_dst[k]), 16,
+                                               g_off[k] + (uint32_t)(st * 128), 0, 0, 0);
+  };
+
+  f32x4 acc[2][JT];
+  double acc64[JT][4];
+#pragma unroll
+  for (int a = 0; a < JT; ++a) {
+    acc[0][a] = acc[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc64[a][e] = 0.0;
+  }
+  auto to64 = [&](f32x4 (&x)[JT]) {
+#pragma unroll
+    for (int a = 0; a < JT; ++a) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc64[a][e] += (double)x[a][e];
+      x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  const int xa = 16 * w + l16;  // this lane's token row of the stage
+  auto compute = [&](int buf, f32x4 (&cur)[JT], f32x4 (&prev)[JT]) {
+    const uint8_t* Ab = smem + buf * RR::STAGE;
+    const uint8_t* Gb = Ab + RR::A_BYTES;
+    bf16x8v af[2], gf[2][JT];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k = 4 * ks + q4;
+      af[ks] = *reinterpret_cast<const bf16x8v*>(Ab + xa * 128 + ((k ^ rows_swz(xa)) << 4));
+#pragma unroll
+      for (int a = 0; a < JT; ++a) {
+        const int x = 16 * a + l16;
+        gf[ks][a] = *reinterpret_cast<const bf16x8v*>(Gb + x * 128 + ((k ^ rows_swz(x)) << 4));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < JT; ++a)
+        cur[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], gf[ks][a], cur[a], 0, 0, 0);
+    to64(prev);
+  };
+
+  constexpr int D = NS - 1;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < n_st) issue(d, d);
+  for (int st = 0; st < n_st; ++st) {
+    wait_inflight<L, D>(min(D, n_st - st));
+    ring_barrier();
+    if (st + D < n_st) issue(st + D, (st + D) % NS);
+    if (st & 1) compute(st % NS, acc[1], acc[0]);
+    else compute(st % NS, acc[0], acc[1]);
+  }
+  to64(acc[0]);
+  to64(acc[1]);
+
+  // D layout: tokens 16w + 4(l/16) + e, column j = 16a + l%16
+#pragma unroll
+  for (int a = 0; a < JT; ++a) {
+    const int j = j0 + 16 * a + l16;
+    if (j >= r) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t tt = t0 + 16 * w + 4 * q4 + e;
+      if (tt >= T) {
+        // V^T columns T .. Tp-1 (padding to a multiple of 8) must read as zero in the cols kernel
+        if (vt && blockIdx.z == 0 && tt < Tp)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + tt] = 0;
+        continue;
+      }
+      const double s = acc64[a][e];
+      if (part) {
+        part[(int64_t)blockIdx.z * T * r + tt * r + j] = s;
+      } else {
+        if (out) out[tt * r + j] = (float)s;
+        if (out64) out64[tt * r + j] = s;
+        if (vt) write_vt4(vt, rp, Tp, j, tt, s);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(512) void k_adapter_rows_ring64(
+    const uint16_t* __restrict__ act, int64_t T, int64_t C, const uint16_t* __restrict__ wt,
+    int64_t ldw, int r, int64_t c_per, double* __restrict__ part, float* __restrict__ out,
+    double* __restrict__ out64, uint16_t* __restrict__ vt, int rp, int64_t Tp) {
+  adapter_rows_ring_body<4>(act, T, C, wt, ldw, r, c_per, part, out, out64, vt, rp, Tp);
+}
+__global__ __launch_bounds__(512) void k_adapter_rows_ring128(
+    const uint16_t* __restrict__ act, int64_t T, int64_t C, const uint16_t* __restrict__ wt,
+    int64_t ldw, int r, int64_t c_per, double* __restrict__ part, float* __restrict__ out,
+    double* __restrict__ out64, uint16_t* __restrict__ vt, int rp, int64_t Tp) {
+  adapter_rows_ring_body<8>(act, T, C, wt, ldw, r, c_per, part, out, out64, vt, rp, Tp);
+}
+
 }  // namespace
 
 namespace sra {
@@ -734,9 +899,44 @@ hipError_t launch_adapter_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t
   return hipGetLastError();
 }
 
+namespace {
+// The ring kernel: ranks above 32 with at least two 128-token tiles, whole 64-column stages and
+// 32-bit buffer offsets; the grid gets as many reduction slices (of whole stages, at least 4 per
+// slice) as keep it near 256 workgroups, one per CU.
+struct RingPlan {
+  bool ok;
+  int jr, S;
+  int64_t c_per;
+  size_t part_bytes;
+};
+RingPlan ring_plan(int64_t T, int64_t C, int r) {
+  RingPlan p{};
+  if (r <= 32 || T < 256 || C % 64 != 0 || T * C * 2 >= ((int64_t)1 << 31)) return p;
+  p.ok = true;
+  p.jr = r <= 64 ? 64 : 128;
+  const int64_t blocks = cdiv(T, 128) * cdiv(r, p.jr);
+  int64_t S = cdiv(256, blocks);
+  const char* env = getenv("SRA_ROWS_S");  // tuning override
+  if (env && *env) S = atoi(env);
+  const int64_t max_s = C / 256 > 0 ? C / 256 : 1;
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  p.c_per = round_up(cdiv(C, S), 64);
+  p.S = (int)cdiv(C, p.c_per);
+  p.part_bytes = p.S > 1 ? (size_t)p.S * T * r * sizeof(double) : 0;
+  return p;
+}
+bool ring_usable(const RingPlan& p, const uint16_t* act, const uint16_t* wt, int64_t ldw, int r) {
+  return p.ok && ldw % 8 == 0 && (int64_t)r * ldw * 2 < ((int64_t)1 << 31) &&
+         ((uintptr_t)act & 15) == 0 && ((uintptr_t)wt & 15) == 0;
+}
+}  // namespace
+
 size_t adapter_rows_ws(int64_t T, int64_t C, int r) {
   if (T <= 0 || C <= 0 || r <= 0) return 0;
-  return rows_plan(T, C, r).part_bytes;
+  // the ring kernel may fall back to the register kernel at launch (operand alignment): room for both
+  const size_t a = rows_plan(T, C, r).part_bytes, b = ring_plan(T, C, r).part_bytes;
+  return a > b ? a : b;
 }
 
 hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const uint16_t* wt,
@@ -747,10 +947,27 @@ hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const 
     if (out64 || vt) return hipErrorInvalidValue;  // callers never ask for fp64 with an empty reduction
     return launch_fill_f32(out, T * r, 0.f, s);
   }
-  const RowsPlan p = rows_plan(T, C, r);
-  double* part = p.S > 1 ? (double*)ws : nullptr;
   const int rp = (int)vt_rows(r);
   const int64_t Tp = vt_cols(T);
+  const RingPlan q = ring_plan(T, C, r);
+  if (ring_usable(q, act, wt, ldw, r)) {
+    double* part = q.S > 1 ? (double*)ws : nullptr;
+    const dim3 grid((unsigned)cdiv(T, 128), (unsigned)cdiv(r, q.jr), (unsigned)q.S);
+    if (q.jr == 64)
+      launch(SRA_KERNEL_ADAPTER, k_adapter_rows_ring64, grid, dim3(512), 0, s, act, T, C, wt, ldw,
+             r, q.c_per, part, out, out64, vt, rp, Tp);
+    else
+      launch(SRA_KERNEL_ADAPTER, k_adapter_rows_ring128, grid, dim3(512), 0, s, act, T, C, wt, ldw,
+             r, q.c_per, part, out, out64, vt, rp, Tp);
+    if (q.S > 1) {
+      const int64_t n = T * r;
+      hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, q.S,
+                         n, out, out64, r, vt, rp, Tp);
+    }
+    return hipGetLastError();
+  }
+  const RowsPlan p = rows_plan(T, C, r);
+  double* part = p.S > 1 ? (double*)ws : nullptr;
   const dim3 grid((unsigned)cdiv(T, 16), (unsigned)cdiv(r, 16 * p.jt), (unsigned)p.S);
   switch (p.jt) {
     case 1: rows_launch<1, 4>(grid, s, act, T, C, wt, ldw, r, p.c_per, part, out, out64, vt, rp, Tp); break;

@@ -111,6 +111,17 @@ def test_in_kernel_adapter_rows(gpu, monkeypatch, cfg, T, K, N, r):
     run_nm(wl, seed=T + r)
 
 
+@pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 40), (257, 512, 1024, 128), (520, 1280, 256, 100),
+                                     (384, 256, 640, 136), (256, 64, 128, 64), (1030, 2048, 1536, 128)])
+def test_adapter_rows_ring(gpu, T, K, N, r):
+    """Ranks above 32 with at least 256 tokens and whole 64-column stages take the LDS-ring rows
+    kernel for U and dU: ragged last token tile, adapter rows past r, two adapter-column blocks
+    (r = 136), a single-stage reduction (K = 64), one to several reduction slices, and dU^T's
+    parts with their zero columns past T."""
+    wl = Workload("ring", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
+    run_nm(wl, seed=T + r)
+
+
 def test_no_adapter_flag(gpu):
     wl = Workload("noad", T=96, K=128, N=64, r=8, dtype="bf16", fmt="nm")
     run_nm(wl, seed=5, flags_adapter=False)
