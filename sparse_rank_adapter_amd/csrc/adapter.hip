@@ -675,6 +675,180 @@ __global__ __launch_bounds__(256 * kGradKG[0]) void k_adapter_grads16(sra::Adapt
 __global__ __launch_bounds__(256 * kGradKG[1]) void k_adapter_grads32(sra::AdapterGradArgs ga) { adapter_grads_body<2, kGradKG[1]>(ga); }
 __global__ __launch_bounds__(256 * kGradKG[2]) void k_adapter_grads64(sra::AdapterGradArgs ga) { adapter_grads_body<4, kGradKG[2]>(ga); }
 
+// Wide tiles of the merged gradients, for ranks above 32.  With 64 x 64 tiles the V^T parts of a
+// stage (4 parts x 64 rows) are four times the Act tile and are re-read by every column block, and
+// Act itself is re-read once per 64 adapter rows.  Here each of the 8 waves owns 2 column
+// fragments x 4 adapter-row fragments, and the waves tile either 128 columns x 128 adapter rows
+// (WJ = 2) or 256 columns x 64 adapter rows (WJ = 1).  Stages are 32 tokens: the Act tile as
+// 2*MW-byte token rows, the V^T tile as P*JR rows of 64 bytes, both by buffer -> LDS DMA with the
+// same zero-reads past the slice and past T as the narrow kernel.  P (3 for dB, 4 for dA) is a
+// template parameter so no DMA or MFMA is spent on absent parts.
+// Swizzles: Act row t keeps 16-byte chunk c in slot c ^ 2((t >> 3) & 3) (the four 8-token groups
+// of a transposed 2-byte read land on different banks); V^T row x keeps chunk c in slot
+// c ^ ((x >> 2) & 3) (16 consecutive 64-byte rows of a 16-byte fragment read cover all banks once).
+template <int WJ, int P>
+struct GradWide {
+  static constexpr int WM = 8 / WJ, MW = 32 * WM, JR = 64 * WJ, ST = 32, NW = 8;
+  static constexpr int CPR = MW / 8;                            // 16-byte chunks per Act row
+  static constexpr int A_BYTES = ST * MW * 2, V_BYTES = P * JR * 64, STAGE = A_BYTES + V_BYTES;
+  static constexpr int NS = (150 * 1024) / STAGE < 4 ? (150 * 1024) / STAGE : 4;
+  static constexpr int LA = A_BYTES / 1024 / NW;                // Act transfers per wave
+  static constexpr int NV = V_BYTES / 1024, LVM = (NV + NW - 1) / NW;
+  static_assert(A_BYTES % (1024 * NW) == 0, "whole Act transfers per wave");
+  static_assert(NS >= 3, "three stages fit");
+};
+constexpr int kGradWideLds = 128 * 1024;
+
+template <int WJ, int P>
+SRA_DEV void adapter_grads_wide_body(const sra::AdapterGradArgs& ga, const sra::AdapterGrad& job,
+                                     int mb, uint8_t* smem) {
+  using GW = GradWide<WJ, P>;
+  static_assert(GW::NS * GW::STAGE <= kGradWideLds, "ring fits the shared buffer");
+  constexpr int NS = GW::NS, NW = GW::NW, ST = GW::ST, JR = GW::JR, MW = GW::MW;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w % GW::WM, wj = w / GW::WM;
+  const int64_t M = job.M, m0 = (int64_t)mb * MW;
+  const int j0 = blockIdx.y * JR;
+  const int64_t tb = (int64_t)blockIdx.z * ga.t_per, te = min(ga.T, tb + ga.t_per);
+  const int n_st = (int)((te - tb + ST - 1) / ST);
+
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(job.act + tb * M + m0), 0, (int)((te - tb) * M * 2 - m0 * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)job.vt, 0, (int)((int64_t)P * ga.rp * ga.Tp * 2), 0x00020000);
+  uint32_t a_off[GW::LA], v_off[GW::LVM];
+  int a_dst[GW::LA], v_dst[GW::LVM];
+#pragma unroll
+  for (int k = 0; k < GW::LA; ++k) {  // 1 KB = 64 / CPR token rows of 2 MW bytes
+    const int b = k * NW + w, x = b * (64 / GW::CPR) + lane / GW::CPR;
+    const int c = (lane % GW::CPR) ^ (((x >> 3) & 3) << 1);
+    a_off[k] = (uint32_t)((x * M + c * 8) * 2);
+    a_dst[k] = b * 1024;
+  }
+  // waves w < NV - NW (LVM - 1) issue LVM V^T transfers per stage, the others LVM - 1
+  const bool full_v = w < GW::NV - NW * (GW::LVM - 1);
+#pragma unroll
+  for (int k = 0; k < GW::LVM; ++k) {  // 1 KB = 16 rows of 64 bytes
+    const int b = min(k * NW + w, GW::NV - 1), x = 16 * b + (lane >> 2);
+    const int c = (lane & 3) ^ ((x >> 2) & 3);
+    const int p = x / JR, jj = x % JR;
+    v_off[k] = (uint32_t)((((int64_t)p * ga.rp + j0 + jj) * ga.Tp + tb + c * 8) * 2);
+    v_dst[k] = GW::A_BYTES + b * 1024;
+  }
+  auto issue = [&](int st, int buf) {
+    uint8_t* base = smem + buf * GW::STAGE;
+#pragma unroll
+    for (int k = 0; k < GW::LA; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + a_dst[k]), 16,
+                                               a_off[k] + (uint32_t)(st * ST * M * 2), 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < GW::LVM; ++k)
+      if (k < GW::LVM - 1 || full_v)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(base + v_dst[k]), 16,
+                                                 v_off[k] + (uint32_t)(st * ST * 2), 0, 0, 0);
+  };
+
+  f32x4 acc[2][2][4];
+  double acc64[2][4][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      acc[0][f][a] = acc[1][f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc64[f][a][e] = 0.0;
+    }
+  auto to64 = [&](f32x4 (&x)[2][4]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc64[f][a][e] += (double)x[f][a][e];
+        x[f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  };
+  auto compute = [&](int buf, f32x4 (&cur)[2][4], f32x4 (&prev)[2][4]) {
+    const uint8_t* A = smem + buf * GW::STAGE;
+    const uint8_t* V = A + GW::A_BYTES;
+    // B operand: Act[t][m] for tokens t = 8(l/16) .. +7 of the stage, one column m per lane
+    Frag bf[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int m = 32 * wm + 16 * f + l16, mc = m >> 3, mo = m & 7;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = 8 * q4 + e, c = mc ^ (((t >> 3) & 3) << 1);
+        bf[f].h[e] = *reinterpret_cast<const uint16_t*>(A + t * (2 * MW) + c * 16 + mo * 2);
+      }
+    }
+    // A operand: V^T rows (part p, adapter row 64 wj + 16 a + l%16), the same 8 tokens
+    bf16x8v vf[4][P];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int x = p * JR + 64 * wj + 16 * a + l16;
+        vf[a][p] = *reinterpret_cast<const bf16x8v*>(V + x * 64 + ((q4 ^ ((x >> 2) & 3)) << 4));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+          cur[f][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[a][p], bf[f].b, cur[f][a], 0, 0, 0);
+    to64(prev);
+  };
+
+  constexpr int D = NS - 1;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < n_st) issue(d, d);
+  for (int st = 0; st < n_st; ++st) {
+    if (full_v) wait_inflight<GW::LA + GW::LVM, D>(min(D, n_st - st));
+    else wait_inflight<GW::LA + GW::LVM - 1, D>(min(D, n_st - st));
+    ring_barrier();
+    if (st + D < n_st) issue(st + D, (st + D) % NS);
+    if (st & 1) compute(st % NS, acc[1], acc[0]);
+    else compute(st % NS, acc[0], acc[1]);
+  }
+  to64(acc[0]);
+  to64(acc[1]);
+
+  // D layout: adapter rows 4(l/16) + e of fragment (wj, a), column l%16 of fragment (wm, f)
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int64_t mg = m0 + 32 * wm + 16 * f + l16;
+    if (mg >= M) continue;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + 64 * wj + 16 * a + 4 * q4 + e;
+        if (j >= ga.r) continue;
+        const int64_t o = job.out_t ? (int64_t)j * M + mg : mg * ga.r + j;
+        if (ga.S > 1)
+          job.part[(int64_t)blockIdx.z * M * ga.r + o] = acc64[f][a][e];
+        else
+          job.out[o] = (float)acc64[f][a][e];
+      }
+  }
+}
+
+template <int WJ>
+SRA_DEV void adapter_grads_wide(const sra::AdapterGradArgs& ga) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGradWideLds];
+  const bool second = (int)blockIdx.x >= ga.job[0].nmb;
+  const sra::AdapterGrad job = second ? ga.job[1] : ga.job[0];
+  const int mb = (int)blockIdx.x - (second ? ga.job[0].nmb : 0);
+  if (job.parts == 4) adapter_grads_wide_body<WJ, 4>(ga, job, mb, smem);
+  else adapter_grads_wide_body<WJ, 3>(ga, job, mb, smem);
+}
+__global__ __launch_bounds__(512) void k_adapter_grads_w64(sra::AdapterGradArgs ga) { adapter_grads_wide<1>(ga); }
+__global__ __launch_bounds__(512) void k_adapter_grads_w128(sra::AdapterGradArgs ga) { adapter_grads_wide<2>(ga); }
+
 // out = sum over the S slices of each job's partials, in slice order (one thread per element of
 // the first job's output, then of the second's)
 __global__ void k_reduce_grads(sra::AdapterGradArgs ga) {
@@ -1015,17 +1189,34 @@ hipError_t launch_adapter_cols(const uint16_t* act, int64_t T, int64_t M, const 
 namespace {
 struct GradsPlan {
   int jt, njb, S;
+  int wj;   // wide tiles: 1 (256 columns x 64 adapter rows) or 2 (128 x 128); 0 for 64 x 64
+  int mw;   // columns per workgroup
   int64_t t_per;
 };
 GradsPlan grads_plan(const AdapterGrad* g, int n, int64_t T, int r) {
   GradsPlan p;
   p.jt = pick_jt(r);
-  p.njb = (int)cdiv(r, 16 * p.jt);
+  bool wide = r > 32;
+  // (parts 3 or 4; the per-lane offsets of a 32-token stage stay below 2^31)
+  for (int i = 0; i < n; ++i)
+    wide = wide && (g[i].parts == 3 || g[i].parts == 4) && g[i].M * 64 < ((int64_t)1 << 31);
+  p.wj = wide ? (r <= 64 ? 1 : 2) : 0;
+  p.mw = wide ? 256 / p.wj : 64;
+  p.njb = (int)cdiv(r, wide ? 64 * p.wj : 16 * p.jt);
   int64_t blocks = 0;
-  for (int i = 0; i < n; ++i) blocks += cdiv(g[i].M, 64) * p.njb;
-  // one workgroup per CU (the ring takes most of the LDS): as many slices as keep the grid within
-  // 256 workgroups, each slice at least 256 tokens
+  for (int i = 0; i < n; ++i) blocks += cdiv(g[i].M, p.mw) * p.njb;
+  // one workgroup per CU (the ring takes most of the LDS).  Narrow tiles: as many slices as keep
+  // the grid within 256 workgroups.  Wide tiles: the slice count (<= 8) that minimises whole
+  // waves of 256 workgroups per slice plus about 4% per extra slice for the partials' traffic.
+  // Each slice is at least 256 tokens.
   int64_t S = 256 / (blocks < 1 ? 1 : blocks);
+  if (wide) {
+    double best = 1e30;
+    for (int64_t c = 1; c <= 8; ++c) {
+      const double cost = (double)cdiv(blocks * c, 256) / (double)c + 0.04 * (double)(c - 1);
+      if (cost < best - 1e-9) best = cost, S = c;
+    }
+  }
   const char* env = getenv("SRA_GRADS_S");  // tuning override
   if (env && *env) S = atoi(env);
   const int64_t max_s = cdiv(T, 256);
@@ -1067,7 +1258,7 @@ hipError_t launch_adapter_grads(const AdapterGrad* g, int n, int64_t T, int r, v
   int nmb = 0;
   for (int i = 0; i < n; ++i) {
     ga.job[i] = g[i];
-    ga.job[i].nmb = (int)cdiv(g[i].M, 64);
+    ga.job[i].nmb = (int)cdiv(g[i].M, p.mw);
     nmb += ga.job[i].nmb;
     if (p.S > 1) {
       ga.job[i].part = (double*)w;
@@ -1082,7 +1273,9 @@ hipError_t launch_adapter_grads(const AdapterGrad* g, int n, int64_t T, int r, v
   ga.rp = (int)vt_rows(r);
   ga.S = p.S;
   const dim3 grid((unsigned)nmb, (unsigned)p.njb, (unsigned)p.S);
-  switch (p.jt) {
+  switch (p.wj ? 4 + p.wj : p.jt) {
+    case 5: launch(SRA_KERNEL_ADAPTER, k_adapter_grads_w64, grid, dim3(512), 0, s, ga); break;
+    case 6: launch(SRA_KERNEL_ADAPTER, k_adapter_grads_w128, grid, dim3(512), 0, s, ga); break;
     case 1: launch(SRA_KERNEL_ADAPTER, k_adapter_grads16, grid, dim3(256 * kGradKG[0]), 0, s, ga); break;
     case 2: launch(SRA_KERNEL_ADAPTER, k_adapter_grads32, grid, dim3(256 * kGradKG[1]), 0, s, ga); break;
     default: launch(SRA_KERNEL_ADAPTER, k_adapter_grads64, grid, dim3(256 * kGradKG[2]), 0, s, ga); break;
