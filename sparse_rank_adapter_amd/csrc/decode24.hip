@@ -7,11 +7,11 @@
 // Design: one pass over S straight from HBM into registers, no LDS staging.  All tokens fit in
 // one v_smfmac_f32_16x16x64_bf16 column tile (tokens past T are zero), so the instruction's
 // B operand (Act, 295 KB at the largest shape, L2-resident) is shared by every weight row tile.
-// A workgroup owns 64 weight rows (four 16-row tiles per wave) and its four waves split the
-// reduction: batch b covers 64-column steps 8b .. 8b+7 and wave w takes steps 8b+2w and
+// A workgroup owns 16 FR weight rows (FR 16-row tiles per wave, FR = 3 or 4 picked per shape so
+// the workgroups split evenly over the CUs) and its four waves split the reduction: batch b covers 64-column steps 8b .. 8b+7 and wave w takes steps 8b+2w and
 // 8b+2w+1, so the workgroup reads each row in 512-byte runs.  Each wave loads batch b+1 while
 // multiplying batch b.  The four partial tiles are summed through LDS in wave order (deterministic), and
-// wave w finishes row tile w: adapter epilogue on v_mfma_f32_16x16x32_bf16 (U as bf16 hi + lo)
+// wave w < FR finishes row tile w: adapter epilogue on v_mfma_f32_16x16x32_bf16 (U as bf16 hi + lo)
 // and a bf16 store.
 //
 // Operand layouts (gfx950, lane l, l16 = l % 16, q = l / 16):
@@ -19,12 +19,12 @@
 //               metadata = half (q & 1) of word 2s + (q >> 1) of the row
 //   B (tokens)  token l16, columns 8q .. 8q+7 and 32+8q .. 32+8q+7 of the step
 //   D           rows 4q .. 4q+3 of token l16
+#include <cstdlib>
+
 #include "common.h"
 
 namespace {
 
-constexpr int FR = 4;         // 16-row tiles per wave
-constexpr int RB = 16 * FR;   // weight rows per workgroup
 // Buffer resource word 3 for untyped loads on gfx9-family GPUs (32-bit data format, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
 // Offsets stay below 2^31 (every resource is smaller), so setting bit 31 moves an access past the
@@ -32,6 +32,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 // unconditional.
 SRA_DEV uint32_t oob_unless(bool in, uint32_t off) { return off | ((uint32_t)!in << 31); }
 
+template <int FR>
 struct Batch {
   u32x4 a[FR][2];  // this wave's stored values, per row tile and step
   u32x4 m;         // cooperative share of the workgroup's metadata for the batch
@@ -41,13 +42,15 @@ struct Batch {
 constexpr int MLD = 20;       // LDS row of the metadata block: 16 words + 4 (16-byte rows, reads spread over banks)
 constexpr int XLD = 512 + 8;  // LDS row of the Act block: 512 columns + 8 (bank spread)
 
+template <int FR>
 __global__ __launch_bounds__(256, 3) void k_decode24(const uint16_t* __restrict__ vals,
                                                      const uint32_t* __restrict__ meta, int64_t R,
                                                      int64_t C, const uint16_t* __restrict__ act,
                                                      int64_t T, sra::Epilogue ep,
                                                      uint16_t* __restrict__ out) {
+  constexpr int RB = 16 * FR;  // weight rows per workgroup
   // Per batch (eight 64-column steps = 512 logical columns) the workgroup stages the metadata of
-  // its 64 rows (64 B per row) and the Act block (T x 512) in LDS with one coalesced 16-byte
+  // its RB rows (64 B per row) and the Act block (T x 512) in LDS with one coalesced 16-byte
   // load per thread and vector; each wave streams its own rows' values into registers.
   __shared__ __attribute__((aligned(16))) uint32_t ml[2][RB * MLD];
   __shared__ __attribute__((aligned(16))) uint16_t xl[2][16 * XLD];
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(256, 3) void k_decode24(const uint16_t* __restrict_
   const int m_row = tid >> 2, m_chunk = tid & 3;
   const uint32_t m_lane = (uint32_t)((m_row * mstride + 4 * m_chunk) * 4);
 
-  auto load = [&](int b, Batch& B) {
+  auto load = [&](int b, Batch<FR>& B) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int s = 8 * b + 2 * w + u;                // this wave's step
@@ -91,8 +94,8 @@ __global__ __launch_bounds__(256, 3) void k_decode24(const uint16_t* __restrict_
       B.x[k] = __builtin_amdgcn_raw_buffer_load_b128(xres, oob_unless(in, (uint32_t)((tok * C + col) * 2)), 0, 0);
     }
   };
-  auto stage = [&](int buf, const Batch& B) {
-    *reinterpret_cast<u32x4*>(&ml[buf][m_row * MLD + 4 * m_chunk]) = B.m;
+  auto stage = [&](int buf, const Batch<FR>& B) {
+    if (m_row < RB) *reinterpret_cast<u32x4*>(&ml[buf][m_row * MLD + 4 * m_chunk]) = B.m;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int v = tid + 256 * k, tok = v >> 6, c = 8 * (v & 63);
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(256, 3) void k_decode24(const uint16_t* __restrict_
 #pragma unroll
   for (int i = 0; i < FR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int hsh = 16 * (q & 1);
-  auto compute = [&](int buf, const Batch& B) {
+  auto compute = [&](int buf, const Batch<FR>& B) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int j = 2 * w + u;  // step within the batch
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(256, 3) void k_decode24(const uint16_t* __restrict_
 
   // Ping-pong over register batches; batches past the end are all-zero loads.  sched_barrier
   // keeps the compiler from sinking a batch's loads down to their first use.
-  Batch b0, b1;
+  Batch<FR> b0, b1;
   load(0, b0);
   for (int b = 0; b < nb; b += 2) {
     load(b + 1, b1);
@@ -145,6 +148,7 @@ __global__ __launch_bounds__(256, 3) void k_decode24(const uint16_t* __restrict_
 #pragma unroll
   for (int i = 0; i < FR; ++i) red[(w * FR + i) * 64 + l] = acc[i];
   __syncthreads();
+  if (w >= FR) return;  // FR row tiles, one per finishing wave
   f32x4 y = red[(0 * FR + w) * 64 + l];
 #pragma unroll
   for (int k = 1; k < 4; ++k) y += red[(k * FR + w) * 64 + l];
@@ -207,8 +211,21 @@ hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, 
                                 uint16_t* out, hipStream_t s) {
   if (T <= 0 || R <= 0) return hipSuccess;
   if (T > 16 || (C & 31) != 0) return hipErrorInvalidValue;
-  launch(SRA_KERNEL_DECODE24, k_decode24, dim3((unsigned)((R + RB - 1) / RB)), dim3(256), 0, s,
-         s_vals, s_meta, R, C, act, T, ep, out);
+  // Rows per workgroup: the CU with the most workgroups sets the time of a weight-streaming pass,
+  // so pick the tile count whose busiest CU streams the fewest rows (ties: the larger tile).
+  int fr = 4;
+  int64_t best = -1;
+  for (int f = 4; f >= 3; --f) {
+    const int64_t nwg = (R + 16 * f - 1) / (16 * f), per_cu = (nwg + 255) / 256 * 16 * f;
+    if (best < 0 || per_cu < best) best = per_cu, fr = f;
+  }
+  const char* env = getenv("SRA_DECODE_FR");  // tuning override
+  if (env && (*env == '3' || *env == '4')) fr = *env - '0';
+  const unsigned grid = (unsigned)((R + 16 * fr - 1) / (16 * fr));
+  if (fr == 3)
+    launch(SRA_KERNEL_DECODE24, k_decode24<3>, dim3(grid), dim3(256), 0, s, s_vals, s_meta, R, C, act, T, ep, out);
+  else
+    launch(SRA_KERNEL_DECODE24, k_decode24<4>, dim3(grid), dim3(256), 0, s, s_vals, s_meta, R, C, act, T, ep, out);
   return hipGetLastError();
 }
 

@@ -122,6 +122,16 @@ def test_adapter_rows_ring(gpu, T, K, N, r):
     run_nm(wl, seed=T + r)
 
 
+@pytest.mark.parametrize("fr", ["3", "4"])
+@pytest.mark.parametrize("T,K,N,r", [(16, 512, 200, 64), (5, 96, 100, 8), (1, 160, 3000, 0)])
+def test_decode_row_tiles(gpu, monkeypatch, fr, T, K, N, r):
+    """The streaming decode kernel with 48- and 64-row workgroups: a ragged last row tile, waves
+    without a row tile of their own (48 rows, four waves), and the adapter epilogue."""
+    monkeypatch.setenv("SRA_DECODE_FR", fr)
+    wl = Workload("decode_tiles", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
+    run_nm(wl, seed=N + T, check_bwd=False)
+
+
 def test_no_adapter_flag(gpu):
     wl = Workload("noad", T=96, K=128, N=64, r=8, dtype="bf16", fmt="nm")
     run_nm(wl, seed=5, flags_adapter=False)
