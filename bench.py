@@ -41,7 +41,9 @@ PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 TRAFFIC_BYTES = {
     "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
     "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
-    "opt66b_ffn_decode/T16/k_decode24": 196310.1 * 1024 * 2.0 + 1152.5 * 1024,
+    # 48-row decode workgroups: the tile the library picks at this shape
+    "opt66b_ffn_decode/T16/k_decode24<3>": 196910.3 * 1024 * 2.0 + 1152.4 * 1024,
+    "opt66b_ffn_decode/T1/k_decode24<3>": 194047.5 * 1024 * 2.0 + 72.1 * 1024,
 }
 
 
@@ -457,7 +459,7 @@ def main():
                "roofline": {"kernel": "k_decode24", "bound": "hbm", "achieved": d["kernel_GBps"],
                             "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                             "frac": d["kernel_frac_hbm"],
-                            "traffic": TRAFFIC_BYTES.get(f"{wl.name}/T{args.decode_t}/k_decode24")}}
+                            "traffic": TRAFFIC_BYTES.get(f"{wl.name}/T{args.decode_t}/k_decode24<3>")}}
         print(json.dumps(out), flush=True)
         return
     if wl.fmt != "nm":
