@@ -42,8 +42,8 @@ TRAFFIC_BYTES = {
     "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
     "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
     # 48-row decode workgroups: the tile the library picks at this shape
-    "opt66b_ffn_decode/T16/k_decode24<3>": 196910.3 * 1024 * 2.0 + 1152.4 * 1024,
-    "opt66b_ffn_decode/T1/k_decode24<3>": 194047.5 * 1024 * 2.0 + 72.1 * 1024,
+    "opt66b_ffn_decode/T16/canonical/k_decode24<3>": 196910.3 * 1024 * 2.0 + 1152.4 * 1024,
+    "opt66b_ffn_decode/T1/canonical/k_decode24<3>": 194047.5 * 1024 * 2.0 + 72.1 * 1024,
 }
 
 
@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--workload", default="opt350m_fc1",
                     choices=["opt350m_fc1", "opt13b_fc1", "opt13b_fc2", "ffi90_4096", "opt66b_ffn_decode"])
     ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
+    ap.add_argument("--decode-layout", choices=["streaming", "canonical"], default="streaming",
+                    help="weight layout of the decode forward (streaming = sra_nm_tile)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle sampling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -293,9 +295,10 @@ def decode_bytes(wl, T, kernel_only=False):
 
 
 def bench_decode(args, wl, Ts):
-    """Forward at decode token counts.  Two compressed copies of the weight (2 x 382 MB) are
-    alternated so that the 256 MB Infinity Cache cannot serve a repeated read; the dense
-    comparator alternates two dense copies the same way."""
+    """Forward at decode token counts on the streaming layout of the weight (sra_nm_tile), with
+    the decode kernel on the canonical arrays timed beside it.  Two compressed copies of the
+    weight (2 x 382 MB) are alternated so that the 256 MB Infinity Cache cannot serve a repeated
+    read; the dense comparator alternates two dense copies the same way."""
     import torch
 
     import sparse_rank_adapter_amd as sra
@@ -306,36 +309,44 @@ def bench_decode(args, wl, Ts):
     inp = layer_inputs(wl, seed=0, T=max(Ts), with_dy=False)
     X, W, A, B = (inp[k].to(dev) for k in ("X", "W", "A", "B"))
     r = wl.r
-    copies = (sra.compress(W), sra.compress(W))
+    canon = (sra.compress(W), sra.compress(W))
+    streaming = tuple(sra.nm_tile(S) for S in canon)
+    main, other = (streaming, canon) if args.decode_layout == "streaming" else (canon, streaming)
     dense = (W, W.clone())
     rows = []
     for T in Ts:
         Xt = X[:T].contiguous()
         Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
         U = torch.empty((T, r), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(1, sra.fwd_workspace(copies[0], T, r)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(1, sra.fwd_workspace(canon[0], T, r)), dtype=torch.uint8, device=dev)
 
         def both():
-            for S in copies:
+            for S in main:
                 sra.sparse_lora_fwd(S, Xt, A, B, Y=Y, U=U, ws=ws)
 
-        flip = [0]
+        def alternate(copies):
+            flip = [0]
 
-        def one():
-            S = copies[flip[0] & 1]
-            flip[0] += 1
-            sra.sparse_lora_fwd(S, Xt, A, B, Y=Y, U=U, ws=ws)
+            def one():
+                S = copies[flip[0] & 1]
+                flip[0] += 1
+                sra.sparse_lora_fwd(S, Xt, A, B, Y=Y, U=U, ws=ws)
+            return one
 
         call_ms = time_graph(both, args.steps, args.warmup, not args.no_graph) / 2
-        k_ms = time_kernel(SRA_KERNEL_DECODE24, one, max(20, args.steps))
+        k_ms = time_kernel(SRA_KERNEL_DECODE24, alternate(main), max(20, args.steps))
+        k2_ms = time_kernel(SRA_KERNEL_DECODE24, alternate(other), max(20, args.steps))
         d_ms = time_graph(lambda: [torch.nn.functional.linear(Xt, Wd) for Wd in dense], args.steps,
                           args.warmup, not args.no_graph) / 2
         kb = decode_bytes(wl, T, kernel_only=True)
-        rows.append({"T": T, "call_us": round(call_ms * 1e3, 2), "kernel_us": round(k_ms * 1e3, 2),
+        rows.append({"T": T, "layout": args.decode_layout,
+                     "call_us": round(call_ms * 1e3, 2), "kernel_us": round(k_ms * 1e3, 2),
                      "kernel_GBps": round(kb / (k_ms * 1e-3) / 1e9, 1),
                      "kernel_frac_hbm": round(kb / (k_ms * 1e-3) / PEAK_HBM_BPS, 4),
                      "call_GBps": round(decode_bytes(wl, T) / (call_ms * 1e-3) / 1e9, 1),
-                     "dense_us": round(d_ms * 1e3, 2), "speedup_vs_dense": round(d_ms / call_ms, 3)})
+                     "dense_us": round(d_ms * 1e3, 2), "speedup_vs_dense": round(d_ms / call_ms, 3),
+                     "other_layout_kernel_us": round(k2_ms * 1e3, 2),
+                     "other_layout_frac_hbm": round(kb / (k2_ms * 1e-3) / PEAK_HBM_BPS, 4)})
     return rows
 
 
@@ -417,6 +428,8 @@ def loop_calls(args):
     inp = layer_inputs(wl, seed=0, T=T, with_dy=args.loop == "spmm_bwd")
     X, W, A, B = (inp[k].to(dev) for k in ("X", "W", "A", "B"))
     S = sra.compress(W)
+    if args.loop == "decode" and args.decode_layout == "streaming":
+        S = sra.nm_tile(S)
     Y, U = sra.sparse_lora_fwd(S, X, A, B)
     if args.loop == "spmm_bwd":
         P = sra.double_prune(S)
@@ -454,12 +467,14 @@ def main():
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                "data": "synthetic",
                "config": {"workload": wl.name, "T": args.decode_t, "K": wl.K, "N": wl.N, "r": wl.r,
-                          "sparsity": "2:4", "step": "forward (U = X A^T, Y = X Ws^T + U B^T)"},
+                          "sparsity": "2:4", "layout": args.decode_layout,
+                          "step": "forward (U = X A^T, Y = X Ws^T + U B^T)"},
                "decode": rows,
                "roofline": {"kernel": "k_decode24", "bound": "hbm", "achieved": d["kernel_GBps"],
                             "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                             "frac": d["kernel_frac_hbm"],
-                            "traffic": TRAFFIC_BYTES.get(f"{wl.name}/T{args.decode_t}/k_decode24<3>")}}
+                            "traffic": TRAFFIC_BYTES.get(
+                                f"{wl.name}/T{args.decode_t}/{args.decode_layout}/k_decode24<3>")}}
         print(json.dumps(out), flush=True)
         return
     if wl.fmt != "nm":

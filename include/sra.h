@@ -56,8 +56,9 @@ typedef enum { SRA_BF16 = 0, SRA_F32 = 1 } sra_dtype;
 typedef enum {
   SRA_FMT_NM = 0,  /* N:M along cols: values [rows, cols*n/m], meta [rows, sra_nm_meta_words] */
   SRA_FMT_ELL = 1, /* fixed fan-in: values [rows, k], index int16 [rows, k], columns ascending */
-  SRA_FMT_CSR = 2  /* transpose of an ELL matrix: row_ptr int32 [rows+1], index int16 [nnz],
+  SRA_FMT_CSR = 2, /* transpose of an ELL matrix: row_ptr int32 [rows+1], index int16 [nnz],
                       values [nnz], column ids ascending inside each row */
+  SRA_FMT_NM_TILED = 3 /* 2:4 bf16 in the streaming layout of sra_nm_tile (forwards of T <= 16) */
 } sra_format;
 
 /*
@@ -132,6 +133,27 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
                              void* stream);
 
 /*
+ * nm_tile -- the same 2:4 weight in a streaming layout for memory-bound forwards of few tokens
+ * (SLoPe §3 inference results: with few tokens the layer is bound by reading the compressed
+ * weight once; the compressed form is prepared once and reused, SLoPe §2.3).  The content is that
+ * of the canonical arrays, permuted so that the decode kernel reads every block contiguously:
+ *   values: for row tile t (16 rows) and step s (64 columns = 32 stored values), a 1 KB block at
+ *           byte (t * ceil(cols/64) + s) * 1024; its 16-byte chunk l = 16 q + i holds stored values
+ *           32 s + 8 q .. 32 s + 8 q + 7 of row 16 t + i.
+ *   meta:   for row tile t and batch b (512 columns = 16 words), a 1 KB block at byte
+ *           (t * ceil(cols/512) + b) * 1024; bytes 64 i .. 64 i + 63 hold words 16 b .. 16 b + 15
+ *           of row 16 t + i.
+ * Entries past the last row or column are zero.  Sizes: sra_nm_tile_bytes.
+ * Ws: canonical SRA_FMT_NM, bf16, 2:4.  out: the caller sets values and meta (16-byte aligned,
+ * value_bytes and meta_bytes long); the call fills the other fields (format SRA_FMT_NM_TILED, same
+ * dtype, rows, cols, n, m).  An SRA_FMT_NM_TILED weight is accepted by sra_sparse_lora_fwd for
+ * T <= 16 (larger T: SRA_ERR_UNSUPPORTED) and by no other call.
+ */
+sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m,
+                             size_t* value_bytes /* host */, size_t* meta_bytes /* host */);
+sra_status sra_nm_tile(const sra_sparse* Ws /* host */, sra_sparse* out /* host */, void* stream);
+
+/*
  * compress_ffi(W, k) -- fixed fan-in selection (SQuAsh project update): every row of W
  * [rows, cols] keeps its k largest-magnitude entries.  out->values [rows, k] and out->index
  * (int16) [rows, k] with columns ascending; set by the caller, other fields filled by the call.
@@ -160,7 +182,8 @@ sra_status sra_fwd_workspace(const sra_sparse* Ws /* host */, int64_t T, int32_t
 /*
  * sparse_lora_fwd -- Y = X Ws^T + (X A^T) B^T (SLoPe §2.2; the adapter product is fused into the
  * sparse product's epilogue, cf. SLoPe §2.4 and App. D, so Y is written once).
- * Ws: SRA_FMT_NM (2:4) or SRA_FMT_ELL, rows = N, cols = K.  X [T,K], A [r,K], B [N,r], Y [T,N].
+ * Ws: SRA_FMT_NM (2:4), SRA_FMT_NM_TILED (2:4, T <= 16) or SRA_FMT_ELL, rows = N, cols = K.
+ * X [T,K], A [r,K], B [N,r], Y [T,N].
  * U_out [T,r] fp32 receives U = X A^T when non-NULL (keep it for the backward).
  * r = 0 means no adapter (A, B, U_out ignored).  T = 0 is a no-op.  Y has dtype Ws->dtype.
  * bf16 accumulates in fp32 (U is kept in fp32); fp32 accumulates in fp64.

@@ -5,5 +5,5 @@ this package only marshals torch tensors into those calls.  Importing it does no
 library; the first call does, and raises if it has not been built.
 """
 from .api import (SparseMatrix, bwd_workspace, compress, compress_ffi, compress_pair,  # noqa: F401
-                  double_prune, ffi_transpose, fwd_workspace, meta_words, sparse_lora_bwd,
+                  double_prune, ffi_transpose, fwd_workspace, meta_words, nm_tile, sparse_lora_bwd,
                   sparse_lora_fwd, time_next_kernel)

@@ -12,6 +12,7 @@ import torch
 
 from . import _abi
 from ._abi import (SRA_BF16, SRA_DX_NO_ADAPTER, SRA_F32, SRA_FMT_CSR, SRA_FMT_ELL, SRA_FMT_NM,
+                   SRA_FMT_NM_TILED,
                    SRA_GRAD_DA, SRA_GRAD_DB, SRA_GRAD_DX, SraSparse, check, load)
 
 _DT = {torch.bfloat16: SRA_BF16, torch.float32: SRA_F32}
@@ -121,6 +122,21 @@ def compress_pair(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | None = N
     check("sra_compress_pair", lib.sra_compress_pair(_p(W), _dt(W), rows, cols, n, m, ctypes.byref(dw),
                                                      ctypes.byref(dp), _stream(W.device)))
     return Ws, P
+
+
+def nm_tile(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMatrix:
+    """The 2:4 weight Ws in the streaming layout for forwards of at most 16 tokens (sra_nm_tile)."""
+    lib = load()
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    check("sra_nm_tile_bytes", lib.sra_nm_tile_bytes(Ws.rows, Ws.cols, Ws.n, Ws.m, ctypes.byref(vb),
+                                                     ctypes.byref(mb)))
+    if out is None:
+        vals = torch.empty(max(1, vb.value // 2), dtype=Ws.dtype, device=Ws.device)
+        meta = torch.empty(max(1, mb.value // 4), dtype=torch.int32, device=Ws.device)
+        out = SparseMatrix(SRA_FMT_NM_TILED, Ws.dtype, Ws.rows, Ws.cols, vals, meta=meta, n=Ws.n, m=Ws.m)
+    dw, do = Ws.desc(), out.desc()
+    check("sra_nm_tile", lib.sra_nm_tile(ctypes.byref(dw), ctypes.byref(do), _stream(Ws.device)))
+    return out
 
 
 def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:

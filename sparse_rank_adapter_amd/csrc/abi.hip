@@ -80,6 +80,11 @@ sra_status check_sparse(const sra_sparse* S, const char* name) {
     SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
     SRA_TRY(check_ptr(S->values, any, "values"));
     SRA_TRY(check_ptr(S->meta, any, "meta"));
+  } else if (S->format == SRA_FMT_NM_TILED) {
+    SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
+    if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "%s: the streaming 2:4 layout is bf16 only", name);
+    SRA_TRY(check_ptr(S->values, any, "values"));
+    SRA_TRY(check_ptr(S->meta, any, "meta"));
   } else if (S->format == SRA_FMT_ELL) {
     if (S->cols > 32767) return fail(SRA_ERR_INVALID_ARG, "%s: ELL needs cols <= 32767", name);
     if (S->k < 1 || S->k > S->cols) return fail(SRA_ERR_INVALID_ARG, "%s: need 1 <= k <= cols", name);
@@ -132,6 +137,10 @@ sra_status validate_fwd(const sra_sparse* Ws, int64_t T, int32_t r) {
   SRA_TRY(check_sparse(Ws, "Ws"));
   if (Ws->format == SRA_FMT_CSR) return fail(SRA_ERR_INVALID_ARG, "forward takes an N:M or ELL weight, not CSR");
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
+  if (Ws->format == SRA_FMT_NM_TILED && T > 16)
+    return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout serves forwards of at most 16 tokens (T = %lld)", (long long)T);
+  if (Ws->format == SRA_FMT_NM_TILED && Ws->cols == 0)
+    return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 forward needs K > 0");
   if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
   if (Ws->format == SRA_FMT_NM && Ws->dtype == SRA_BF16 && Ws->cols == 0)
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 forward needs K > 0");
@@ -166,7 +175,8 @@ struct BwdPlan {
 
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
   SRA_TRY(check_sparse(P, "P"));
-  if (P->format == SRA_FMT_ELL) return fail(SRA_ERR_INVALID_ARG, "backward takes the double-pruned N:M weight or the CSR transpose, not ELL");
+  if (P->format == SRA_FMT_ELL || P->format == SRA_FMT_NM_TILED)
+    return fail(SRA_ERR_INVALID_ARG, "backward takes the double-pruned N:M weight or the CSR transpose");
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
   if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
   if (flags & ~15u) return fail(SRA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
@@ -343,6 +353,33 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
                   s, "compress_pair");
 }
 
+sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m, size_t* value_bytes,
+                             size_t* meta_bytes) {
+  SRA_TRY(check_nm(rows, cols, n, m));
+  if (!value_bytes || !meta_bytes) return fail(SRA_ERR_INVALID_ARG, "size pointers are NULL");
+  sra::nm_tile_bytes(rows, cols, value_bytes, meta_bytes);
+  return SRA_OK;
+}
+
+sra_status sra_nm_tile(const sra_sparse* Ws, sra_sparse* out, void* stream) {
+  SRA_TRY(check_sparse(Ws, "Ws"));
+  if (Ws->format != SRA_FMT_NM) return fail(SRA_ERR_INVALID_ARG, "nm_tile needs a canonical N:M weight");
+  if (Ws->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout is bf16 only");
+  if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
+  const bool any = Ws->rows > 0 && Ws->cols > 0;
+  SRA_TRY(check_ptr(out->values, any, "out values"));
+  SRA_TRY(check_ptr(out->meta, any, "out meta"));
+  out->format = SRA_FMT_NM_TILED;
+  out->dtype = Ws->dtype;
+  out->rows = Ws->rows;
+  out->cols = Ws->cols;
+  out->n = Ws->n;
+  out->m = Ws->m;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_nm_tile_bf16((const uint16_t*)Ws->values, Ws->meta, Ws->rows, Ws->cols,
+                                           out->values, out->meta, s), s, "nm_tile");
+}
+
 sra_status sra_compress_ffi(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t k,
                             sra_sparse* out, void* stream) {
   SRA_TRY(check_dtype(dtype));
@@ -447,6 +484,10 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     ep.g_ld = K;
     ep.u_out = U_out;
   }
+  if (Ws->format == SRA_FMT_NM_TILED)
+    return hip_done(sra::launch_decode24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
+                                              (const uint16_t*)X, T, ep, (uint16_t*)Y, s, /*tiled=*/true),
+                    s, "fwd decode 2:4 (streaming layout)");
   if (Ws->format == SRA_FMT_NM)
     return hip_done(sra::launch_spmm24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
                                             (const uint16_t*)X, T, ep, (uint16_t*)Y,

@@ -162,7 +162,12 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
 size_t spmm24_decode_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
-                                uint16_t* out, hipStream_t s);
+                                uint16_t* out, hipStream_t s, bool tiled = false);
+// canonical 2:4 bf16 arrays -> the decode kernel's streaming layout (1 KB blocks per 16-row tile
+// and 64-column step, metadata per tile and 512-column batch)
+void nm_tile_bytes(int64_t R, int64_t C, size_t* value_bytes, size_t* meta_bytes);
+hipError_t launch_nm_tile_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+                               void* t_vals, void* t_meta, hipStream_t s);
 // Out[t][row] = sum_c Act[t][c] Wd[row][c] + epilogue, Wd dense bf16 [R][C] (C % 64 == 0)
 hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uint16_t* act, int64_t T,
                              const Epilogue& ep, uint16_t* out, hipStream_t s);

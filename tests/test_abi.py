@@ -12,7 +12,8 @@ import pytest
 from sparse_rank_adapter_amd import _abi
 from sparse_rank_adapter_amd._abi import (SRA_BF16, SRA_ERR_INVALID_ARG, SRA_ERR_UNSUPPORTED,
                                           SRA_ERR_WORKSPACE, SRA_F32, SRA_FMT_CSR, SRA_FMT_ELL,
-                                          SRA_FMT_NM, SRA_OK, SraSparse)
+                                          SRA_FMT_NM, SRA_FMT_NM_TILED, SRA_GRAD_DX, SRA_OK,
+                                          SraSparse)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 1 << 20  # aligned, never dereferenced
@@ -160,6 +161,29 @@ def test_workspace_queries_any_size(lib, T, r, shape):
         assert lib.sra_fwd_workspace(ctypes.byref(d), T, r, ctypes.byref(n)) == SRA_OK
         for flags in (1, 2, 4, 7, 15):
             assert lib.sra_bwd_workspace(ctypes.byref(d), T, r, flags, ctypes.byref(n)) == SRA_OK
+
+
+def test_nm_tile_validation(lib):
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sra_nm_tile_bytes(36864, 9216, 2, 4, ctypes.byref(vb), ctypes.byref(mb)) == SRA_OK
+    assert vb.value == 36864 * 9216 and mb.value == 36864 * 9216 // 8   # same bytes as canonical
+    assert lib.sra_nm_tile_bytes(100, 96, 2, 4, ctypes.byref(vb), ctypes.byref(mb)) == SRA_OK
+    assert vb.value == 7 * 2 * 1024 and mb.value == 7 * 1 * 1024          # padded 16-row tiles
+    assert lib.sra_nm_tile_bytes(64, 48, 2, 4, ctypes.byref(vb), ctypes.byref(mb)) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_nm_tile_bytes(64, 64, 1, 4, ctypes.byref(vb), ctypes.byref(mb)) == SRA_ERR_UNSUPPORTED
+    f32 = nm_desc(rows=64, cols=64, dtype=SRA_F32)
+    out = nm_desc(rows=64, cols=64)
+    assert lib.sra_nm_tile(ctypes.byref(f32), ctypes.byref(out), None) == SRA_ERR_UNSUPPORTED
+    tiled = nm_desc(rows=64, cols=64)
+    tiled.format = SRA_FMT_NM_TILED
+    assert lib.sra_nm_tile(ctypes.byref(tiled), ctypes.byref(out), None) == SRA_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert lib.sra_fwd_workspace(ctypes.byref(tiled), 16, 64, ctypes.byref(n)) == SRA_OK
+    assert lib.sra_fwd_workspace(ctypes.byref(tiled), 17, 64, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    assert "16 tokens" in err(lib)
+    assert lib.sra_bwd_workspace(ctypes.byref(tiled), 16, 64, SRA_GRAD_DX, ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    tiled.dtype = SRA_F32
+    assert lib.sra_fwd_workspace(ctypes.byref(tiled), 16, 64, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
 
 
 def test_bwd_validation(lib):

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import sparse_rank_adapter_amd as sra
+from sparse_rank_adapter_amd._abi import SraError
 from oracle import ffi as offi
 from oracle import layer as olayer
 from oracle import nm as onm
@@ -29,9 +30,10 @@ def nm_oracle_weights(W64, k_groups=None):
 
 
 def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, r=None,
-           check_bwd=True, flags_adapter=True):
+           check_bwd=True, flags_adapter=True, tiled=False):
     """Runs fwd + bwd on the GPU and compares (optionally on sampled token rows, output columns
-    of Y / dB and 4-column groups of K for dX / dA)."""
+    of Y / dB and 4-column groups of K for dX / dA).  tiled: the forward also runs on the
+    streaming layout of the weight (sra_nm_tile), whose Y must equal the canonical one bit for bit."""
     inp = layer_inputs(wl, seed=seed, T=T)
     dtype = inp["X"].dtype
     if r is not None and r != wl.r:
@@ -40,6 +42,7 @@ def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, 
     X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
     S = sra.compress(W)
     Y, U = sra.sparse_lora_fwd(S, X, A if rr else None, B if rr else None)
+    Yt = sra.sparse_lora_fwd(sra.nm_tile(S), X, A if rr else None, B if rr else None)[0] if tiled else None
     g = {}
     if check_bwd:
         P = sra.double_prune(S)
@@ -56,6 +59,9 @@ def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, 
     Yo, Uo = olayer.forward(X64[rows], Ws_n, A64, B64[cols_n])
     rep = Report(dtype)
     rep.add("Y", f64(Y[rows][:, cols_n]), Yo)
+    if tiled:
+        assert np.array_equal(bits(Yt), bits(Y)), "streaming-layout Y differs from the canonical Y"
+        rep.add("Y (streaming layout)", f64(Yt[rows][:, cols_n]), Yo)
     if rr:
         rep.add("U", U[rows].cpu().numpy(), Uo)
     if not check_bwd:
@@ -122,14 +128,54 @@ def test_adapter_rows_ring(gpu, T, K, N, r):
     run_nm(wl, seed=T + r)
 
 
-@pytest.mark.parametrize("fr", ["3", "4"])
-@pytest.mark.parametrize("T,K,N,r", [(16, 512, 200, 64), (5, 96, 100, 8), (1, 160, 3000, 0)])
+@pytest.mark.parametrize("fr", ["3", "4", "9"])
+@pytest.mark.parametrize("T,K,N,r", [(16, 512, 200, 64), (5, 96, 100, 8), (1, 160, 3000, 0),
+                                     (3, 1056, 52, 20), (16, 608, 300, 64)])
 def test_decode_row_tiles(gpu, monkeypatch, fr, T, K, N, r):
-    """The streaming decode kernel with 48- and 64-row workgroups: a ragged last row tile, waves
-    without a row tile of their own (48 rows, four waves), and the adapter epilogue."""
+    """The decode kernel with 48-, 64- and 144-row workgroups: a ragged last row tile, waves
+    without a row tile of their own (48 rows, four waves), half steps and batches past K, and the
+    adapter epilogue; on the canonical arrays and on the streaming layout."""
     monkeypatch.setenv("SRA_DECODE_FR", fr)
     wl = Workload("decode_tiles", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
-    run_nm(wl, seed=N + T, check_bwd=False)
+    run_nm(wl, seed=N + T, check_bwd=False, tiled=True)
+
+
+def tile_layout_np(vals, meta, R, C):
+    """The streaming layout as the header defines it, written with numpy reshapes: value block
+    (t, s) holds in chunk 16q + i the stored values 32s + 8q .. +7 of row 16t + i; metadata block
+    (t, b) holds at 64i the words 16b .. 16b + 15 of row 16t + i; zero past the edges."""
+    nt, ns, nb = (R + 15) // 16, (C + 63) // 64, (C + 511) // 512
+    vp = np.zeros((nt * 16, ns * 32), np.uint16)
+    vp[:R, :C // 2] = vals.reshape(R, C // 2)
+    mp = np.zeros((nt * 16, nb * 16), np.uint32)
+    mp[:R, :C // 32] = meta.reshape(R, C // 32)
+    tv = vp.reshape(nt, 16, ns, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    tm = mp.reshape(nt, 16, nb, 16).transpose(0, 2, 1, 3).reshape(-1)
+    return tv, tm
+
+
+@pytest.mark.parametrize("R,C", [(16, 64), (100, 96), (37, 608), (300, 2048), (48, 1056), (4096, 9216)])
+def test_nm_tile_layout(gpu, R, C):
+    """sra_nm_tile is a pure permutation of the canonical arrays (bit-exact, zero padding)."""
+    wl = Workload("tile", T=1, K=C, N=R, r=0, dtype="bf16", fmt="nm")
+    W = layer_inputs(wl, seed=R + C, with_dy=False)["W"].cuda()
+    S = sra.compress(W)
+    St = sra.nm_tile(S)
+    torch.cuda.synchronize()
+    tv, tm = tile_layout_np(S.values.view(torch.int16).cpu().numpy().view(np.uint16),
+                            S.meta.cpu().numpy().view(np.uint32), R, C)
+    gv = St.values.view(torch.int16).cpu().numpy().view(np.uint16)
+    gm = St.meta.cpu().numpy().view(np.uint32)
+    assert gv.size == tv.size and gm.size == tm.size
+    assert np.array_equal(gv, tv) and np.array_equal(gm, tm)
+
+
+def test_nm_tile_rejects_large_t(gpu):
+    wl = Workload("tile", T=17, K=64, N=32, r=0, dtype="bf16", fmt="nm")
+    inp = layer_inputs(wl, seed=0, with_dy=False)
+    St = sra.nm_tile(sra.compress(inp["W"].cuda()))
+    with pytest.raises(SraError, match="16 tokens"):
+        sra.sparse_lora_fwd(St, inp["X"].cuda(), None, None)
 
 
 def test_no_adapter_flag(gpu):
@@ -156,7 +202,7 @@ def test_opt66b_decode_sampled(gpu, T):
     wl = WORKLOADS["opt66b_ffn_decode"]
     rng = np.random.default_rng(T)
     cols_n = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 510, replace=False)]))
-    run_nm(wl, T=T, cols_n=cols_n, check_bwd=False)
+    run_nm(wl, T=T, cols_n=cols_n, check_bwd=False, tiled=True)
 
 
 def test_deterministic_and_t0(gpu):
@@ -219,6 +265,9 @@ def run_ffi(wl: Workload, T=None, seed=0, rows=None, cols_n=None, kcols=None):
     Yo, _ = olayer.forward(X64[rows], Ws[cols_n], A64, B64[cols_n])
     rep = Report(dtype)
     rep.add("Y", f64(Y[rows][:, cols_n]), Yo)
+    if tiled:
+        assert np.array_equal(bits(Yt), bits(Y)), "streaming-layout Y differs from the canonical Y"
+        rep.add("Y (streaming layout)", f64(Yt[rows][:, cols_n]), Yo)
     gx = olayer.backward(dY64[rows], X64[rows][:, kcols], Ws[:, kcols], A64[:, kcols], B64,
                          want=("dX", "dU"))
     rep.add("dX", f64(g["dX"][rows][:, kcols]), gx["dX"])
