@@ -172,6 +172,43 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode24(const uint16_t* __res
     }
   };
 
+  // Adapter operands of the epilogue: lane (l16, q) takes E(row rt + l16, j = jb .. jb+7) and
+  // U(token l16, j = jb .. jb+7) for jb = jj + 8q.  The first 64 adapter columns of the first row
+  // tile this wave finishes are loaded here, before the weight stream, so their latency is hidden
+  // behind it instead of following it.
+  const bool tok_ok = l16 < T;
+  const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0 && (ep.e_row_stride & 7) == 0;
+  auto load_e = [&](int64_t erow, int jb) {
+    union { u32x4 v; uint16_t h[8]; } x;
+    x.v = u32x4{0, 0, 0, 0};
+    if (erow < R) {
+      if (e_vec && jb + 8 <= ep.r) {
+        x.v = *reinterpret_cast<const u32x4*>(ep.E + erow * ep.e_row_stride + jb);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (jb + e < ep.r) x.h[e] = ep.E[erow * ep.e_row_stride + (int64_t)(jb + e) * ep.e_j_stride];
+      }
+    }
+    return x.v;
+  };
+  auto load_u = [&](int jb, float (&u)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = tok_ok && jb + e < ep.r ? ep.U[(int64_t)l16 * ep.r + jb + e] : 0.f;
+  };
+  // prefetched 32-column adapter blocks (none for 64-row tiles, which have no registers to spare)
+  constexpr int PF = FR == 4 ? 0 : 2;
+  u32x4 pf_e[2];
+  float pf_u[2][8];
+  const bool pf = PF > 0 && ep.r > 0 && w < FR && row0 + 16 * w < R;
+  if (pf) {
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+      pf_e[c] = load_e(row0 + 16 * w + l16, 32 * c + 8 * q);
+      load_u(32 * c + 8 * q, pf_u[c]);
+    }
+  }
+
   // Ping-pong over register batches; batches past the end are all-zero loads.  sched_barrier
   // keeps the compiler from sinking a batch's loads down to their first use.
   BT b0, b1;
@@ -196,7 +233,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode24(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < FR; ++i) red[(w * FR + i) * 64 + l] = acc[i];
   __syncthreads();
-  const bool tok_ok = l16 < T;
   // row tile i is finished by wave i % NW: partials summed in wave order (deterministic), adapter
   // epilogue, bf16 store
   for (int i = w; i < FR; i += NW) {
@@ -208,27 +244,23 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode24(const uint16_t* __res
 
     // ---- adapter epilogue: A operand = E rows (row l16, j = 8q..), B operand = U^T (token l16)
     if (ep.r > 0) {
-      const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0 && (ep.e_row_stride & 7) == 0;
-      const int64_t erow = rt + l16;
+      const bool first = pf && i == w;  // the prefetched tile
       for (int jj = 0; jj < ep.r; jj += 32) {
         const int jb = jj + 8 * q;
+        union { u32x4 v; bf16x8 b; } x;
+        float u[8];
+        if (first && jj < 32 * PF) {
+          const int c = jj / 32;
+          x.v = c == 0 ? pf_e[0] : pf_e[1];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) u[e] = c == 0 ? pf_u[0][e] : pf_u[1][e];
+        } else {
+          x.v = load_e(rt + l16, jb);
+          load_u(jb, u);
+        }
         union UH { uint16_t h[8]; bf16x8 b; } uhi, ulo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float u = tok_ok && jb + e < ep.r ? ep.U[(int64_t)l16 * ep.r + jb + e] : 0.f;
-          split_bf16(u, uhi.h[e], ulo.h[e]);
-        }
-        union { u32x4 v; uint16_t h[8]; bf16x8 b; } x;
-        x.v = u32x4{0, 0, 0, 0};
-        if (erow < R) {
-          if (e_vec && jb + 8 <= ep.r) {
-            x.v = *reinterpret_cast<const u32x4*>(ep.E + erow * ep.e_row_stride + jb);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (jb + e < ep.r) x.h[e] = ep.E[erow * ep.e_row_stride + (int64_t)(jb + e) * ep.e_j_stride];
-          }
-        }
+        for (int e = 0; e < 8; ++e) split_bf16(u[e], uhi.h[e], ulo.h[e]);
         y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, uhi.b, y, 0, 0, 0);
         y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, ulo.b, y, 0, 0, 0);
       }
