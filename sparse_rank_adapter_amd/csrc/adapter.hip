@@ -395,6 +395,66 @@ __global__ __launch_bounds__(256) void k_adapter_cols(const uint16_t* __restrict
 }
 
 // out[i] = sum_k part[k][i], summed in slice order
+// U = Act G^T for a few tokens (T <= 16), in one launch: workgroup (t, j0) computes
+// U[t][j0 .. j0+3] over the whole reduction.  Each thread takes 16-byte chunks c = tid, tid + 256,
+// ... of the token's row and of the four G rows, accumulates exact products in fp64, and the
+// workgroup sums the 256 partials through LDS in a fixed tree order (deterministic).  Columns
+// j0 + jj >= r accumulate a clamped row and are never written.  A split of
+// the reduction over workgroups would need a second launch for the sum; with few tokens both
+// launches are latency-bound, so this one reads the token row once per four adapter columns
+// instead.  Needs C % 8 == 0, 16-byte aligned rows (ldw % 8 == 0).
+constexpr int kFewJ = 4;
+__global__ __launch_bounds__(256) void k_adapter_rows_few(const uint16_t* __restrict__ act, int64_t C,
+                                                         const uint16_t* __restrict__ wt, int64_t ldw,
+                                                         int r, float* __restrict__ out) {
+  __shared__ double red[kFewJ][256];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int j0 = blockIdx.y * kFewJ;
+  const uint16_t* xrow = act + t * C;
+  double acc[kFewJ] = {0.0, 0.0, 0.0, 0.0};
+  // every load of a block of NCH chunks is issued before the first product, so the reduction
+  // costs one memory round trip per 256 * NCH chunks instead of one per chunk
+  constexpr int NCH = 5;
+  const int64_t nch = C / 8;
+  for (int64_t base = 0; base < nch; base += 256 * NCH) {
+    u32x4 xv[NCH], gv[NCH][kFewJ];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int64_t c = base + tid + 256 * k;
+      const bool in = c < nch;
+      xv[k] = in ? *reinterpret_cast<const u32x4*>(xrow + 8 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int jj = 0; jj < kFewJ; ++jj) {
+        const int j = min(j0 + jj, r - 1);  // columns past r: a valid row, never accumulated
+        gv[k][jj] = in ? *reinterpret_cast<const u32x4*>(wt + (int64_t)j * ldw + 8 * c) : u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+#pragma unroll
+      for (int jj = 0; jj < kFewJ; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = __uint_as_float(xv[k][e] << 16), x1 = __uint_as_float(xv[k][e] & 0xffff0000u);
+          const float g0 = __uint_as_float(gv[k][jj][e] << 16), g1 = __uint_as_float(gv[k][jj][e] & 0xffff0000u);
+          acc[jj] += (double)(x0 * g0);  // bf16 x bf16 is exact in fp32
+          acc[jj] += (double)(x1 * g1);
+        }
+  }
+#pragma unroll
+  for (int jj = 0; jj < kFewJ; ++jj) red[jj][tid] = acc[jj];
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (tid < h) {
+#pragma unroll
+      for (int jj = 0; jj < kFewJ; ++jj) red[jj][tid] += red[jj][tid + h];
+    }
+    __syncthreads();
+  }
+  if (tid < kFewJ && j0 + tid < r) out[t * r + j0 + tid] = (float)red[tid][0];
+}
+
 __global__ void k_reduce_parts(const double* __restrict__ part, int S, int64_t n,
                                float* __restrict__ out, double* __restrict__ out64, int r,
                                uint16_t* __restrict__ vt, int rp, int64_t Tp) {
@@ -1120,6 +1180,11 @@ hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const 
   if (C == 0) {
     if (out64 || vt) return hipErrorInvalidValue;  // callers never ask for fp64 with an empty reduction
     return launch_fill_f32(out, T * r, 0.f, s);
+  }
+  if (T <= 16 && !out64 && !vt && C % 8 == 0 && ldw % 8 == 0 && (((uintptr_t)act | (uintptr_t)wt) & 15) == 0) {
+    launch(SRA_KERNEL_ADAPTER, k_adapter_rows_few, dim3((unsigned)T, (unsigned)cdiv(r, kFewJ)),
+           dim3(256), 0, s, act, C, wt, ldw, r, out);
+    return hipGetLastError();
   }
   const int rp = (int)vt_rows(r);
   const int64_t Tp = vt_cols(T);
