@@ -41,9 +41,9 @@ PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 TRAFFIC_BYTES = {
     "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
     "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
-    # 48-row decode workgroups: the tile the library picks at this shape
-    "opt66b_ffn_decode/T16/canonical/k_decode24<3>": 196910.3 * 1024 * 2.0 + 1152.4 * 1024,
-    "opt66b_ffn_decode/T1/canonical/k_decode24<3>": 194047.5 * 1024 * 2.0 + 72.1 * 1024,
+    # streaming layout (sra_nm_tile), 48-row workgroups of four waves
+    "opt66b_ffn_decode/T16/streaming/k_decode24<3>": 192608.7 * 1024 * 2.0 + 1152.1 * 1024,
+    "opt66b_ffn_decode/T1/streaming/k_decode24<3>": 189201.6 * 1024 * 2.0 + 72.0 * 1024,
 }
 
 
@@ -415,8 +415,8 @@ def loop_calls(args):
 
     dev = torch.device("cuda:0")
     if args.loop == "copy":
-        # a plain elementwise kernel that reads 256 MiB and writes 256 MiB
-        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        # a plain elementwise kernel that reads 256 MiB (a ramp, no constant data) and writes 256 MiB
+        a = torch.arange(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(args.steps):
             torch.neg(a, out=b)

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256) void k_adapter_cols(const uint16_t* __restrict
 }
 
 // out[i] = sum_k part[k][i], summed in slice order
-// U = Act G^T for a few tokens (T <= 16), in one launch: workgroup (t, j0) computes
+// U = Act G^T for a few tokens (T <= 16), in one launch: workgroup (j0 / 4, t) computes
 // U[t][j0 .. j0+3] over the whole reduction.  Each thread takes 16-byte chunks c = tid, tid + 256,
 // ... of the token's row and of the four G rows, accumulates exact products in fp64, and the
 // workgroup sums the 256 partials through LDS in a fixed tree order (deterministic).  Columns
@@ -409,8 +409,11 @@ __global__ __launch_bounds__(256) void k_adapter_rows_few(const uint16_t* __rest
                                                          int r, float* __restrict__ out) {
   __shared__ double red[kFewJ][256];
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;
-  const int j0 = blockIdx.y * kFewJ;
+  // grid (column groups, tokens): consecutive workgroup ids go to different XCDs, so with a
+  // multiple of 8 column groups every token of one group runs on the same XCD and its G rows
+  // come from that XCD's L2 after the first read
+  const int64_t t = blockIdx.y;
+  const int j0 = blockIdx.x * kFewJ;
   const uint16_t* xrow = act + t * C;
   double acc[kFewJ] = {0.0, 0.0, 0.0, 0.0};
   // every load of a block of NCH chunks is issued before the first product, so the reduction
@@ -1182,7 +1185,7 @@ hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const 
     return launch_fill_f32(out, T * r, 0.f, s);
   }
   if (T <= 16 && !out64 && !vt && C % 8 == 0 && ldw % 8 == 0 && (((uintptr_t)act | (uintptr_t)wt) & 15) == 0) {
-    launch(SRA_KERNEL_ADAPTER, k_adapter_rows_few, dim3((unsigned)T, (unsigned)cdiv(r, kFewJ)),
+    launch(SRA_KERNEL_ADAPTER, k_adapter_rows_few, dim3((unsigned)cdiv(r, kFewJ), (unsigned)T),
            dim3(256), 0, s, act, C, wt, ldw, r, out);
     return hipGetLastError();
   }
