@@ -58,7 +58,7 @@ typedef enum {
   SRA_FMT_ELL = 1, /* fixed fan-in: values [rows, k], index int16 [rows, k], columns ascending */
   SRA_FMT_CSR = 2, /* transpose of an ELL matrix: row_ptr int32 [rows+1], index int16 [nnz],
                       values [nnz], column ids ascending inside each row */
-  SRA_FMT_NM_TILED = 3 /* 2:4 bf16 in the streaming layout of sra_nm_tile (forwards of T <= 16) */
+  SRA_FMT_NM_TILED = 3 /* 2:4 bf16 in the streaming layout of sra_nm_tile */
 } sra_format;
 
 /*
@@ -146,12 +146,27 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
  * Entries past the last row or column are zero.  Sizes: sra_nm_tile_bytes.
  * Ws: canonical SRA_FMT_NM, bf16, 2:4.  out: the caller sets values and meta (16-byte aligned,
  * value_bytes and meta_bytes long); the call fills the other fields (format SRA_FMT_NM_TILED, same
- * dtype, rows, cols, n, m).  An SRA_FMT_NM_TILED weight is accepted by sra_sparse_lora_fwd for
- * T <= 16 (larger T: SRA_ERR_UNSUPPORTED) and by no other call.
+ * dtype, rows, cols, n, m).  An SRA_FMT_NM_TILED weight is accepted by sra_sparse_lora_fwd (as
+ * Ws) and sra_sparse_lora_bwd (as P) for T <= 16, and for any T when cols % 128 == 0 (else
+ * SRA_ERR_UNSUPPORTED); the results equal the canonical arrays' bit for bit when neither path
+ * splits the reduction.
  */
 sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m,
                              size_t* value_bytes /* host */, size_t* meta_bytes /* host */);
 sra_status sra_nm_tile(const sra_sparse* Ws /* host */, sra_sparse* out /* host */, void* stream);
+
+/*
+ * compress_pair_tiled -- sra_compress_pair with both outputs written in the streaming layout of
+ * sra_nm_tile (SLoPe §2.3: a training loop refreshes both compressed forms after every update; in
+ * this layout the forward and backward products read their sparse operand in 1 KB runs).  The
+ * content equals sra_nm_tile applied to sra_compress_pair's outputs, bit for bit.
+ * Ws: values / meta of sra_nm_tile_bytes(rows, cols) bytes; P: of sra_nm_tile_bytes(cols, rows).
+ * The call fills the other fields (format SRA_FMT_NM_TILED, dtype, shapes, n, m).
+ * Supported: bf16, 2:4, rows % 128 == 0, cols % 128 == 0 (else SRA_ERR_UNSUPPORTED).
+ */
+sra_status sra_compress_pair_tiled(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
+                                   int32_t m, sra_sparse* Ws /* host */, sra_sparse* P /* host */,
+                                   void* stream);
 
 /*
  * compress_ffi(W, k) -- fixed fan-in selection (SQuAsh project update): every row of W
@@ -182,7 +197,7 @@ sra_status sra_fwd_workspace(const sra_sparse* Ws /* host */, int64_t T, int32_t
 /*
  * sparse_lora_fwd -- Y = X Ws^T + (X A^T) B^T (SLoPe §2.2; the adapter product is fused into the
  * sparse product's epilogue, cf. SLoPe §2.4 and App. D, so Y is written once).
- * Ws: SRA_FMT_NM (2:4), SRA_FMT_NM_TILED (2:4, T <= 16) or SRA_FMT_ELL, rows = N, cols = K.
+ * Ws: SRA_FMT_NM (2:4), SRA_FMT_NM_TILED (2:4, see sra_nm_tile) or SRA_FMT_ELL, rows = N, cols = K.
  * X [T,K], A [r,K], B [N,r], Y [T,N].
  * U_out [T,r] fp32 receives U = X A^T when non-NULL (keep it for the backward).
  * r = 0 means no adapter (A, B, U_out ignored).  T = 0 is a no-op.  Y has dtype Ws->dtype.
@@ -207,7 +222,8 @@ sra_status sra_bwd_workspace(const sra_sparse* P /* host */, int64_t T, int32_t 
 /*
  * sparse_lora_bwd -- double-pruned backward (SLoPe §1, §2.1; the output gradient dY is never
  * pruned, SLoPe App. J).
- * P: for N:M weights the output of sra_double_prune (rows = K, cols = N); for fixed fan-in weights
+ * P: for N:M weights the output of sra_double_prune (rows = K, cols = N; canonical, or in the
+ * streaming layout of sra_nm_tile / sra_compress_pair_tiled); for fixed fan-in weights
  * the CSR of sra_ffi_transpose (rows = K, cols = N).
  * dY [T,N], X [T,K], A [r,K], B [N,r] (dtype P->dtype); T tokens.  U [T,r] fp32 from the forward, or NULL
  * to recompute it from X and A.  Outputs (each only if its flag is set): dX [T,K] (dtype),

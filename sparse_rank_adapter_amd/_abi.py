@@ -17,7 +17,7 @@ SRA_GRAD_DX, SRA_GRAD_DA, SRA_GRAD_DB, SRA_DX_NO_ADAPTER = 1, 2, 4, 8
 # every symbol include/sra.h declares
 EXPORTS = (
     "sra_abi_version", "sra_last_error", "sra_nm_meta_words", "sra_compress", "sra_double_prune",
-    "sra_compress_pair", "sra_nm_tile_bytes", "sra_nm_tile",
+    "sra_compress_pair", "sra_compress_pair_tiled", "sra_nm_tile_bytes", "sra_nm_tile",
     "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
     "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_time_next_kernel",
 )
@@ -55,6 +55,7 @@ def load(path: str = LIB_PATH):
         "sra_compress": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32, P, c_void_p]),
         "sra_double_prune": (c_int32, [P, P, c_void_p]),
         "sra_compress_pair": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32, P, P, c_void_p]),
+        "sra_compress_pair_tiled": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32, P, P, c_void_p]),
         "sra_nm_tile_bytes": (c_int32, [c_int64, c_int64, c_int32, c_int32, POINTER(c_size_t), POINTER(c_size_t)]),
         "sra_nm_tile": (c_int32, [P, P, c_void_p]),
         "sra_compress_ffi": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, P, c_void_p]),

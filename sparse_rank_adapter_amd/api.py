@@ -139,6 +139,34 @@ def nm_tile(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMatrix:
     return out
 
 
+def tile_bytes(rows: int, cols: int, n: int = 2, m: int = 4) -> tuple:
+    """(value bytes, metadata bytes) of the streaming layout of a rows x cols N:M matrix."""
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    check("sra_nm_tile_bytes", load().sra_nm_tile_bytes(rows, cols, n, m, ctypes.byref(vb), ctypes.byref(mb)))
+    return vb.value, mb.value
+
+
+def compress_pair_tiled(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | None = None):
+    """compress_pair with both outputs in the streaming layout (sra_compress_pair_tiled)."""
+    lib = load()
+    _dev(W)
+    rows, cols = W.shape
+    if out is None:
+        def mk(r, c):
+            vb, mb = tile_bytes(r, c, n, m)
+            return SparseMatrix(SRA_FMT_NM_TILED, W.dtype, r, c,
+                                torch.empty(max(1, vb // 2), dtype=W.dtype, device=W.device),
+                                meta=torch.empty(max(1, mb // 4), dtype=torch.int32, device=W.device), n=n, m=m)
+        Ws, P = mk(rows, cols), mk(cols, rows)
+    else:
+        Ws, P = out
+    dw, dp = Ws.desc(), P.desc()
+    check("sra_compress_pair_tiled", lib.sra_compress_pair_tiled(_p(W), _dt(W), rows, cols, n, m,
+                                                                 ctypes.byref(dw), ctypes.byref(dp),
+                                                                 _stream(W.device)))
+    return Ws, P
+
+
 def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:
     """compress_ffi(W, k): keep the k largest-magnitude entries of every row (ELL, int16 columns)."""
     lib = load()

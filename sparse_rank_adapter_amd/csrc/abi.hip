@@ -137,8 +137,8 @@ sra_status validate_fwd(const sra_sparse* Ws, int64_t T, int32_t r) {
   SRA_TRY(check_sparse(Ws, "Ws"));
   if (Ws->format == SRA_FMT_CSR) return fail(SRA_ERR_INVALID_ARG, "forward takes an N:M or ELL weight, not CSR");
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
-  if (Ws->format == SRA_FMT_NM_TILED && T > 16)
-    return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout serves forwards of at most 16 tokens (T = %lld)", (long long)T);
+  if (Ws->format == SRA_FMT_NM_TILED && !sra::spmm24_tiled_ok(Ws->cols, T))
+    return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout needs K %% 128 == 0 above 16 tokens (T = %lld)", (long long)T);
   if (Ws->format == SRA_FMT_NM_TILED && Ws->cols == 0)
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 forward needs K > 0");
   if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
@@ -175,8 +175,12 @@ struct BwdPlan {
 
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
   SRA_TRY(check_sparse(P, "P"));
-  if (P->format == SRA_FMT_ELL || P->format == SRA_FMT_NM_TILED)
+  if (P->format == SRA_FMT_ELL)
     return fail(SRA_ERR_INVALID_ARG, "backward takes the double-pruned N:M weight or the CSR transpose");
+  if (P->format == SRA_FMT_NM_TILED && (flags & SRA_GRAD_DX) && !sra::spmm24_tiled_ok(P->cols, T))
+    return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout needs N %% 128 == 0 above 16 tokens (T = %lld)", (long long)T);
+  if (P->format == SRA_FMT_NM_TILED && P->cols == 0 && (flags & SRA_GRAD_DX))
+    return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 backward needs N > 0");
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
   if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
   if (flags & ~15u) return fail(SRA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
@@ -353,6 +357,35 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
                   s, "compress_pair");
 }
 
+sra_status sra_compress_pair_tiled(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
+                                   int32_t m, sra_sparse* Ws, sra_sparse* P, void* stream) {
+  SRA_TRY(check_dtype(dtype));
+  SRA_TRY(check_nm(rows, cols, n, m));
+  SRA_TRY(check_nm(cols, rows, n, m));
+  if (dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout is bf16 only");
+  if (rows % 128 || cols % 128)
+    return fail(SRA_ERR_UNSUPPORTED, "compress_pair_tiled needs rows and cols that are multiples of 128");
+  if (!Ws || !P) return fail(SRA_ERR_INVALID_ARG, "output descriptor is NULL");
+  const bool any = rows > 0 && cols > 0;
+  SRA_TRY(check_ptr(W, any, "W"));
+  SRA_TRY(check_ptr(Ws->values, any, "Ws->values"));
+  SRA_TRY(check_ptr(Ws->meta, any, "Ws->meta"));
+  SRA_TRY(check_ptr(P->values, any, "P->values"));
+  SRA_TRY(check_ptr(P->meta, any, "P->meta"));
+  Ws->format = P->format = SRA_FMT_NM_TILED;
+  Ws->dtype = P->dtype = dtype;
+  Ws->rows = rows;
+  Ws->cols = cols;
+  P->rows = cols;
+  P->cols = rows;
+  Ws->n = P->n = n;
+  Ws->m = P->m = m;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_compress_pair24_tiled((const uint16_t*)W, rows, cols, Ws->values, Ws->meta,
+                                                    P->values, P->meta, s),
+                  s, "compress_pair_tiled");
+}
+
 sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m, size_t* value_bytes,
                              size_t* meta_bytes) {
   SRA_TRY(check_nm(rows, cols, n, m));
@@ -469,7 +502,8 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
                                          (float*)Y, s), s, "fwd spmm f32");
   }
   // U = X A^T: computed inside the SpMM when its plan allows, else by the adapter kernel first
-  const bool fuse = r > 0 && Ws->format == SRA_FMT_NM && sra::spmm24_fuses_adapter(N, K, T, r);
+  const bool nm24 = Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED;
+  const bool fuse = r > 0 && nm24 && sra::spmm24_fuses_adapter(N, K, T, r);
   if (r > 0 && !fuse)
     SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, r, U,
                                               nullptr, nullptr, wsb + plan.gemm_off, s), s, "fwd U"));
@@ -485,9 +519,9 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     ep.u_out = U_out;
   }
   if (Ws->format == SRA_FMT_NM_TILED)
-    return hip_done(sra::launch_decode24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
-                                              (const uint16_t*)X, T, ep, (uint16_t*)Y, s, /*tiled=*/true),
-                    s, "fwd decode 2:4 (streaming layout)");
+    return hip_done(sra::launch_spmm24_tiled_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
+                                                  (const uint16_t*)X, T, ep, (uint16_t*)Y, s),
+                    s, "fwd spmm 2:4 (streaming layout)");
   if (Ws->format == SRA_FMT_NM)
     return hip_done(sra::launch_spmm24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
                                             (const uint16_t*)X, T, ep, (uint16_t*)Y,
@@ -574,7 +608,8 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                                 at, Uv, T, vtU, s), s, "bwd prep"));
   // dU = dY B: computed inside the dX SpMM (which also writes dU_out and dU^T's parts for dA)
   // when its plan allows, else by the adapter kernel first
-  const bool fuse = dx_ad && P->format == SRA_FMT_NM && sra::spmm24_fuses_adapter(K, N, T, r);
+  const bool nm24 = P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED;
+  const bool fuse = dx_ad && nm24 && sra::spmm24_fuses_adapter(K, N, T, r);
   if (plan.need_du && !fuse)
     SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)dY, T, N, wt, sra::packed_wt_ld(N), r,
                                               dU, nullptr, vtdU, gws, s), s, "bwd dU"));
@@ -593,7 +628,11 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
       ep.vt_rp = (int)sra::vt_rows(r);
       ep.vt_tp = sra::vt_cols(T);
     }
-    if (P->format == SRA_FMT_NM)
+    if (P->format == SRA_FMT_NM_TILED)
+      SRA_TRY(hip_done(sra::launch_spmm24_tiled_bf16((const uint16_t*)P->values, P->meta, K, N,
+                                                     (const uint16_t*)dY, T, ep, (uint16_t*)dX, s),
+                       s, "bwd dX 2:4 (streaming layout)"));
+    else if (P->format == SRA_FMT_NM)
       SRA_TRY(hip_done(sra::launch_spmm24_bf16((const uint16_t*)P->values, P->meta, K, N,
                                                (const uint16_t*)dY, T, ep, (uint16_t*)dX,
                                                wsb ? wsb + plan.spmm_off : nullptr, s),

@@ -103,6 +103,9 @@ hipError_t launch_compress24(int dtype, const void* W, int64_t rows, int64_t col
                              uint32_t* meta, hipStream_t s);
 hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
                                   uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s);
+// bf16 compress + double prune with both outputs in the streaming layout (rows, cols % 128 == 0)
+hipError_t launch_compress_pair24_tiled(const uint16_t* W, int64_t rows, int64_t cols, void* vals,
+                                        uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s);
 hipError_t launch_double_prune24(int dtype, const void* vals, const uint32_t* meta, int64_t rows,
                                  int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s);
 hipError_t launch_compress_ffi(int dtype, const void* W, int64_t rows, int64_t cols, int k,
@@ -159,6 +162,12 @@ size_t spmm24_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                               void* ws, hipStream_t s);
+// the same product with the weight in the streaming layout (sra_nm_tile): any T when C % 128 == 0,
+// else T <= 16 only; no workspace (never split)
+bool spmm24_tiled_ok(int64_t C, int64_t T);
+hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
+                                    int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
+                                    uint16_t* out, hipStream_t s);
 size_t spmm24_decode_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,

@@ -250,6 +250,20 @@ __global__ __launch_bounds__(256) void k_compress_pair24(const T* __restrict__ W
 // marked): lane = (column, 64-row half), two 32-row blocks of 8 groups each; writes one 16-value
 // slice and one metadata word of P's row per block.
 constexpr int kTileLD = 128 + 8;  // LDS row stride (elements), 16-byte multiple
+
+// Streaming 2:4 layout (the decode and streaming SpMM kernels' operand order): 1 KB value blocks per
+// (16-row group, 64-column step), chunk 16q + i = stored values 32s + 8q .. +7 of row 16t + i;
+// 1 KB metadata blocks per (16-row group, 512-column batch), row i's 16 words at 64i.
+// Element offset of the 8 stored values from stored index j (j % 8 == 0) of `row`:
+SRA_DEV int64_t tl_val(int64_t row, int64_t j, int64_t nsteps) {
+  return (((row >> 4) * nsteps + (j >> 5)) * 64 + 16 * ((j & 31) >> 3) + (row & 15)) * 8;
+}
+// Word offset of metadata word w of `row`:
+SRA_DEV int64_t tl_meta(int64_t row, int64_t w, int64_t nbat) {
+  return ((row >> 4) * nbat + (w >> 4)) * 256 + (row & 15) * 16 + (w & 15);
+}
+
+template <bool TL>
 SRA_DEV void second_prune_tile(const uint16_t* tile, int64_t c0, int64_t r0, int64_t rows,
                                int64_t cols, uint16_t* __restrict__ pv, uint32_t* __restrict__ pm) {
   constexpr int LD = kTileLD;
@@ -278,13 +292,22 @@ SRA_DEV void second_prune_tile(const uint16_t* tile, int64_t c0, int64_t r0, int
       o.w[g] = y;
       word |= (p0 | (p1 << 2)) << (4 * g);
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(pv + prow * (rows / 2) + ostart / 2);
-    dst[0] = o.v[0];
-    dst[1] = o.v[1];
-    pm[prow * (rows / 32) + ostart / 32] = word;
+    if constexpr (TL) {  // P rows have `rows` columns
+      const int64_t ns = (rows + 63) / 64, nb = (rows + 511) / 512;
+      *reinterpret_cast<u32x4*>(pv + tl_val(prow, ostart / 2, ns)) = o.v[0];
+      *reinterpret_cast<u32x4*>(pv + tl_val(prow, ostart / 2 + 8, ns)) = o.v[1];
+      pm[tl_meta(prow, ostart / 32, nb)] = word;
+    } else {
+      u32x4* dst = reinterpret_cast<u32x4*>(pv + prow * (rows / 2) + ostart / 2);
+      dst[0] = o.v[0];
+      dst[1] = o.v[1];
+      pm[prow * (rows / 32) + ostart / 32] = word;
+    }
   }
 }
 
+// TL: both outputs in the streaming layout (rows and cols multiples of 128).
+template <bool TL>
 __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __restrict__ W,
                                                           int64_t rows, int64_t cols,
                                                           uint16_t* __restrict__ vals,
@@ -320,10 +343,17 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
           x.w[2 * g] = lo;
           x.w[2 * g + 1] = hi;
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(vals + row * (cols / 2) + cb / 2);
-        dst[0] = o.v[0];
-        dst[1] = o.v[1];
-        meta[row * (cols / 32) + cb / 32] = word;
+        if constexpr (TL) {
+          const int64_t ns = (cols + 63) / 64, nb = (cols + 511) / 512;
+          *reinterpret_cast<u32x4*>(vals + tl_val(row, cb / 2, ns)) = o.v[0];
+          *reinterpret_cast<u32x4*>(vals + tl_val(row, cb / 2 + 8, ns)) = o.v[1];
+          meta[tl_meta(row, cb / 32, nb)] = word;
+        } else {
+          u32x4* dst = reinterpret_cast<u32x4*>(vals + row * (cols / 2) + cb / 2);
+          dst[0] = o.v[0];
+          dst[1] = o.v[1];
+          meta[row * (cols / 32) + cb / 32] = word;
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x.v[i] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
@@ -333,7 +363,7 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
     }
   }
   __syncthreads();
-  second_prune_tile(tile, c0, r0, rows, cols, pv, pm);
+  second_prune_tile<TL>(tile, c0, r0, rows, cols, pv, pm);
 }
 
 
@@ -383,7 +413,7 @@ __global__ __launch_bounds__(256) void k_double_prune24t(const uint16_t* __restr
     }
   }
   __syncthreads();
-  second_prune_tile(tile, c0, r0, rows, cols, pv, pm);
+  second_prune_tile<false>(tile, c0, r0, rows, cols, pv, pm);
 }
 
 }  // namespace
@@ -395,13 +425,33 @@ hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_
   if (rows == 0 || cols == 0) return hipSuccess;
   if (dtype == SRA_BF16) {
     const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
-    launch(SRA_KERNEL_COMPRESS, k_compress_pair24t, grid, dim3(256), 0, s, (const uint16_t*)W, rows,
+    launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<false>, grid, dim3(256), 0, s, (const uint16_t*)W, rows,
            cols, (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
   launch(SRA_KERNEL_COMPRESS, k_compress_pair24<uint32_t>, grid, dim3(256), 0, s,
          (const uint32_t*)W, rows, cols, (uint32_t*)vals, meta, (uint32_t*)p_vals, p_meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_pair24_tiled(const uint16_t* W, int64_t rows, int64_t cols, void* vals,
+                                        uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (rows % 128 != 0 || cols % 128 != 0) return hipErrorInvalidValue;
+  // metadata words past a row's end inside its last 512-column batch are not written by the
+  // kernel: clear them first (only when a batch is partial)
+  if (cols % 512 != 0) {
+    const hipError_t e = launch_fill_f32((float*)meta, rows / 16 * ((cols + 511) / 512) * 256, 0.f, s);
+    if (e != hipSuccess) return e;
+  }
+  if (rows % 512 != 0) {
+    const hipError_t e = launch_fill_f32((float*)p_meta, cols / 16 * ((rows + 511) / 512) * 256, 0.f, s);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
+  launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<true>, grid, dim3(256), 0, s, W, rows, cols,
+         (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
   return hipGetLastError();
 }
 

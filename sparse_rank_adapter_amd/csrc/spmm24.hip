@@ -825,7 +825,11 @@ struct QTile {
   static constexpr int OCC = (NW == 8 || FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
 };
 
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false>
+// TLAY: the weight is in the streaming 2:4 layout (1 KB blocks per 16-row group and 64-column stage,
+// metadata in 1 KB blocks per 16-row group and 8-stage super-stage; see decode24.hip), so every
+// transfer of the sparse operand reads 1 KB contiguously instead of 64-byte (values) and 64-byte
+// (super-stage metadata) runs per row.  Same LDS layout and products; needs MS == 8.
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false>
 __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
@@ -834,9 +838,11 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   constexpr int NW = TL::NW;
   using AD = AdapterRows<BT, (UG > 0 ? UG : 16), NW>;
+  static_assert(!TLAY || (MS == 8 && !DN), "the streaming layout is read with metadata super-stages");
   static_assert(UG == 0 || AD::ULD * 4 * BT <= TL::LDS, "U tile fits in LDS");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static_assert(BR % (32 * NW) == 0 && BT % (8 * NW) == 0, "transfer counts must be whole per wave");
+  static_assert(BR % (16 * NW) == 0 && (MS || DN || BR % (32 * NW) == 0) && BT % (8 * NW) == 0,
+                "transfer counts must be whole per wave");
   static_assert(MS == 0 || (MS == 8 && TL::MSB % (1024 * NW) == 0), "metadata super-stages of 8");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
 
@@ -854,11 +860,19 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   // operands through buffer resources based at the tile (fixed lane offsets, the stage offset in
   // an SGPR; rows past R, T or r read as zeros), as in k_spmm24_pipe
   const int rows_here = (int)min((int64_t)BR, R - row0), toks_here = (int)min((int64_t)BT, T - t0);
-  constexpr int A_ROW = DN ? 128 : 64;  // weight bytes per row and stage
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(s_vals + row0 * (DN ? C : cv)), 0, rows_here * (int)C * (DN ? 2 : 1), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(DN ? nullptr : s_meta + row0 * cm), 0, DN ? 0 : rows_here * (int)cm * 4, 0x00020000);
+  constexpr int A_ROW = TLAY ? 1024 : DN ? 128 : 64;  // stage offset of the weight operand (bytes)
+  // streaming layout: 16-row groups of nsteps 1 KB value blocks and nbat 1 KB metadata blocks
+  const int nsteps = (int)((C + 63) / 64), nbat = (int)((C + 511) / 512), ngrp = (rows_here + 15) / 16;
+  const __amdgpu_buffer_rsrc_t ra =
+      TLAY ? __builtin_amdgcn_make_buffer_rsrc((void*)(s_vals + (row0 / 16) * nsteps * 512), 0,
+                                               ngrp * nsteps * 1024, 0x00020000)
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(s_vals + row0 * (DN ? C : cv)), 0,
+                                               rows_here * (int)C * (DN ? 2 : 1), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm =
+      TLAY ? __builtin_amdgcn_make_buffer_rsrc((void*)(s_meta + (row0 / 16) * nbat * 256), 0,
+                                               ngrp * nbat * 1024, 0x00020000)
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(DN ? nullptr : s_meta + row0 * cm), 0,
+                                               DN ? 0 : rows_here * (int)cm * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(act + t0 * C), 0, toks_here * (int)C * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
@@ -873,7 +887,9 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
       a_off[k] = (uint32_t)((row * C + ch * 8) * 2);
     } else {             // 16 rows of 64 bytes
       const int row = 16 * b + (lane >> 2), ch = (lane & 3) ^ ((row >> 2) & 3);
-      a_off[k] = (uint32_t)(row * C + ch * 16);
+      // streaming layout: chunk ch of row i of group b sits at (16 ch + i) * 16 in its block
+      a_off[k] = TLAY ? (uint32_t)(b * nsteps * 1024 + (16 * ch + (lane >> 2)) * 16)
+                      : (uint32_t)(row * C + ch * 16);
     }
     a_dst[k] = b * 1024;
   }
@@ -901,9 +917,16 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     uint8_t* base = msbuf + (g & 1) * TL::MSB;
 #pragma unroll
     for (int k = 0; k < TL::LMS; ++k) {
-      int w = 2 * (c_beg + MS * g) + 4 * ms_ch[k];  // two words per stage
-      if (w > (int)cm - 4) w = (int)cm - 4;  // past the row's end: clamped, never read
-      bdma(rm, base + ms_dst[k], 16, ms_row[k] + (uint32_t)w * 4, 0);
+      if constexpr (TLAY) {
+        // super-stage g is batch g (no split): block (group, g), row i's 64 bytes at 64 i
+        const int b = k * NW + wave;
+        bdma(rm, base + ms_dst[k], 16, (uint32_t)(b * nbat * 1024 + 64 * (lane >> 2) + 16 * ms_ch[k]),
+             g * 1024);
+      } else {
+        int w = 2 * (c_beg + MS * g) + 4 * ms_ch[k];  // two words per stage
+        if (w > (int)cm - 4) w = (int)cm - 4;  // past the row's end: clamped, never read
+        bdma(rm, base + ms_dst[k], 16, ms_row[k] + (uint32_t)w * 4, 0);
+      }
     }
   };
   uint32_t b_off[TL::LB];
@@ -1483,7 +1506,7 @@ struct Cfg {
 //   50 = 256x128 (4x2 waves of 64x64, 4 stages), 51 = 256x256 (4x2 waves of 64x128, 3)
 // the same with metadata in 8-stage super-stages (C % 128 == 0, no split):
 //   55 = 256x128 (8 waves, 4 stages), 56 = 128x64 (4 waves, 4), 57 = 128x128 (4 waves, 3),
-//   58 = 256x256 (8 waves, 2)
+//   58 = 256x256 (8 waves, 2), 60 = 128x64 (8 waves of 32x32, 4)
 // streaming decode kernel (T <= 16, one 16-token column tile, weight read once from HBM):
 //   30 = 64 weight rows per workgroup (decode24.hip)
 constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 256, false},
@@ -1495,7 +1518,8 @@ constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 25
                          {40, 256, 128, true, 128}, {41, 128, 128, true, 128},
                          {44, 256, 64, true, 128}, {50, 256, 128, true}, {51, 256, 256, true},
                          {55, 256, 128, true, 64, true}, {56, 128, 64, true, 64, true},
-                         {57, 128, 128, true, 64, true}, {58, 256, 256, true, 64, true}};
+                         {57, 128, 128, true, 64, true}, {58, 256, 256, true, 64, true},
+                         {60, 128, 64, true, 64, true}};
 
 Cfg cfg_by_id(int id) {
   for (const Cfg& c : kCfgs)
@@ -1556,13 +1580,13 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
   return p;
 }
 
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false>
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false>
 void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
               const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
               const Plan& p, hipStream_t s, int which = SRA_KERNEL_SPMM24) {
   using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
-  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN>,
+  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN, TLAY>,
               dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(64 * TL::NW), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
@@ -1609,7 +1633,7 @@ bool fuse_ok(const Plan& p, int64_t C, int r) {
   if (r <= 0 || r > kFuseRank || C % 64 != 0 || p.splits != 1) return false;
   const char* env = getenv("SRA_SPMM24_FUSE");
   if (env && env[0] == '0') return false;
-  return p.cfg.id == 14 || p.cfg.id == 55 || p.cfg.id == 56;
+  return p.cfg.id == 14 || p.cfg.id == 55 || p.cfg.id == 56 || p.cfg.id == 60;
 }
 
 }  // namespace
@@ -1639,6 +1663,38 @@ size_t spmm24_ws(int64_t R, int64_t C, int64_t T) {
   return p.splits > 1 ? (size_t)p.splits * T * R * sizeof(float) : 0;
 }
 
+// The same product on the streaming layout (sra_nm_tile).  T <= 16 goes to the decode kernel;
+// otherwise the metadata super-stage kernels read the 1 KB blocks: the tile shape follows the
+// canonical plan (256x256, 256x128 or a 128-row tile), never split, C % 128 == 0.
+bool spmm24_tiled_ok(int64_t C, int64_t T) { return T <= 16 || C % 128 == 0; }
+
+hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
+                                    int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
+                                    uint16_t* out, hipStream_t s) {
+  if (T == 0 || R == 0) return hipSuccess;
+  if (T <= 16) return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s, /*tiled=*/true);
+  if (C % 128 != 0) return hipErrorInvalidValue;
+  Plan p = plan_for(R, C, T);
+  const int id = p.cfg.id;
+  const bool fuse = ep.G != nullptr;
+  if (fuse && (!fuse_ok(p, C, ep.r) || ep.g_ld % 8 != 0)) return hipErrorInvalidValue;
+  p.splits = 1;
+  p.stages_per_split = (int)((C + 63) / 64);
+  const bool wide = id == 0 || id == 10 || id == 22 || id == 51 || id == 58;   // 256x256
+  const bool mid = id == 1 || id == 11 || id == 20 || id == 50 || id == 55;    // 256x128
+  if (fuse) {
+    if (id == 55) launch_q<4, 4, 4, 2, 3, 8, 16, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+    else launch_q<2, 2, 4, 2, 4, 8, 16, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+  } else if (wide) {
+    launch_q<4, 8, 4, 2, 2, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+  } else if (mid) {
+    launch_q<4, 4, 4, 2, 4, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+  } else {
+    launch_q<2, 2, 4, 2, 4, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                               void* ws, hipStream_t s) {
@@ -1652,6 +1708,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
       case 14: launch_pipe<2, 1, 2, 2, 4, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
       case 55: launch_q<4, 4, 4, 2, 3, 8, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
       case 56: launch_q<4, 2, 2, 2, 3, 8, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+      case 60: launch_q<2, 2, 4, 2, 4, 8, 16>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1660,6 +1717,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
     case 30: return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s);
     case 55: launch_q<4, 4, 4, 2, 4, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 56: launch_q<4, 2, 2, 2, 4, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 60: launch_q<2, 2, 4, 2, 4, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 57: launch_q<4, 4, 2, 2, 3, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 58: launch_q<4, 8, 4, 2, 2, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 50: launch_q<4, 4, 4, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;

@@ -181,9 +181,25 @@ def test_nm_tile_validation(lib):
     assert lib.sra_fwd_workspace(ctypes.byref(tiled), 16, 64, ctypes.byref(n)) == SRA_OK
     assert lib.sra_fwd_workspace(ctypes.byref(tiled), 17, 64, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
     assert "16 tokens" in err(lib)
-    assert lib.sra_bwd_workspace(ctypes.byref(tiled), 16, 64, SRA_GRAD_DX, ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    assert lib.sra_bwd_workspace(ctypes.byref(tiled), 16, 64, SRA_GRAD_DX, ctypes.byref(n)) == SRA_OK
+    assert lib.sra_bwd_workspace(ctypes.byref(tiled), 17, 64, SRA_GRAD_DX, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    wide = nm_desc(rows=256, cols=1024)
+    wide.format = SRA_FMT_NM_TILED
+    assert lib.sra_fwd_workspace(ctypes.byref(wide), 2048, 16, ctypes.byref(n)) == SRA_OK
+    assert lib.sra_bwd_workspace(ctypes.byref(wide), 2048, 16, SRA_GRAD_DX, ctypes.byref(n)) == SRA_OK
     tiled.dtype = SRA_F32
     assert lib.sra_fwd_workspace(ctypes.byref(tiled), 16, 64, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+
+
+def test_compress_pair_tiled_validation(lib):
+    a, b = nm_desc(rows=256, cols=256), nm_desc(rows=256, cols=256)
+    call = lambda dt, R, C, n=2, m=4: lib.sra_compress_pair_tiled(FAKE, dt, R, C, n, m, ctypes.byref(a),
+                                                                  ctypes.byref(b), None)
+    assert call(SRA_F32, 256, 256) == SRA_ERR_UNSUPPORTED
+    assert call(SRA_BF16, 64, 256) == SRA_ERR_UNSUPPORTED and "128" in err(lib)
+    assert call(SRA_BF16, 256, 96) == SRA_ERR_UNSUPPORTED
+    assert call(SRA_BF16, 256, 256, 1, 4) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_compress_pair_tiled(FAKE, SRA_BF16, 256, 256, 2, 4, None, ctypes.byref(b), None) == SRA_ERR_INVALID_ARG
 
 
 def test_bwd_validation(lib):

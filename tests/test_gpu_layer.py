@@ -32,11 +32,12 @@ def nm_oracle_weights(W64, k_groups=None):
 
 
 def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, r=None,
-           check_bwd=True, flags_adapter=True, tiled=False):
+           check_bwd=True, flags_adapter=True, tiled=False, streaming=False):
     """Runs fwd + bwd on the GPU and compares (optionally on sampled token rows, output columns
     of Y / dB and 4-column groups of K for dX / dA).  tiled: the forward also runs on the
     streaming layout of the weight (sra_nm_tile), whose Y must equal the canonical one bit for bit
-    when both run the same decode configuration (SRA_DECODE_FR set)."""
+    when both run the same decode configuration (SRA_DECODE_FR set).  streaming: forward and
+    backward run on the streaming layouts of Ws and P instead of the canonical arrays."""
     inp = layer_inputs(wl, seed=seed, T=T)
     dtype = inp["X"].dtype
     if r is not None and r != wl.r:
@@ -44,11 +45,14 @@ def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, 
     rr = inp["A"].shape[0]
     X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
     S = sra.compress(W)
-    Y, U = sra.sparse_lora_fwd(S, X, A if rr else None, B if rr else None)
+    Sf = sra.nm_tile(S) if streaming else S
+    Y, U = sra.sparse_lora_fwd(Sf, X, A if rr else None, B if rr else None)
     Yt = sra.sparse_lora_fwd(sra.nm_tile(S), X, A if rr else None, B if rr else None)[0] if tiled else None
     g = {}
     if check_bwd:
         P = sra.double_prune(S)
+        if streaming:
+            P = sra.nm_tile(P)
         g = sra.sparse_lora_bwd(P, dY, X, U, A if rr else None, B if rr else None,
                                 dx_adapter=flags_adapter, want_du=True)
     torch.cuda.synchronize()
@@ -113,7 +117,7 @@ def test_ragged_shapes(gpu, T, K, N, r, dtype):
     run_nm(wl, seed=T + K)
 
 
-@pytest.mark.parametrize("cfg", [14, 55, 56])
+@pytest.mark.parametrize("cfg", [14, 55, 56, 60])
 @pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (77, 384, 640, 5), (130, 256, 128, 1)])
 def test_in_kernel_adapter_rows(gpu, monkeypatch, cfg, T, K, N, r):
     """Ranks <= 16 on the 128x64 tiles (32x32 and 16x16x64 forms) and the eight-wave 256x128 tiles:
@@ -147,6 +151,35 @@ def test_decode_row_tiles(gpu, monkeypatch, fr, T, K, N, r):
     run_nm(wl, seed=N + T, check_bwd=False, tiled=True)
 
 
+@pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (77, 384, 640, 5), (130, 256, 128, 1),
+                                     (200, 512, 256, 64), (33, 1024, 512, 0), (16, 512, 256, 20),
+                                     (700, 1024, 640, 8)])
+def test_streaming_layout_layer(gpu, T, K, N, r):
+    """Forward and double-pruned backward on the streaming layouts of Ws and P (any T when K and N
+    are multiples of 128): fused and separate adapter rows, ragged tiles, the decode path."""
+    wl = Workload("streaming", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
+    run_nm(wl, seed=T + K + N, streaming=True)
+
+
+@pytest.mark.parametrize("name", ["opt350m_fc1", "opt13b_fc2"])
+def test_streaming_layout_bit_identical(gpu, name):
+    """The streaming-layout SpMM performs the canonical kernels' SMFMAC sequence per output element,
+    so Y, U, dX, dU, dA and dB equal the canonical path's bit for bit (where neither splits K)."""
+    wl = WORKLOADS[name]
+    T = min(wl.T, 2048)
+    inp = layer_inputs(wl, seed=3, T=T)
+    X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
+    S, P = sra.compress_pair(W)
+    out = []
+    for Sx, Px in ((S, P), (sra.nm_tile(S), sra.nm_tile(P))):
+        Y, U = sra.sparse_lora_fwd(Sx, X, A, B)
+        g = sra.sparse_lora_bwd(Px, dY, X, U, A, B, want_du=True)
+        out.append((Y, U, g["dX"], g["dU"], g["dA"], g["dB"]))
+    torch.cuda.synchronize()
+    for a, b, lab in zip(out[0], out[1], ("Y", "U", "dX", "dU", "dA", "dB")):
+        assert np.array_equal(bits(a), bits(b)), f"{lab} differs between layouts"
+
+
 def tile_layout_np(vals, meta, R, C):
     """The streaming layout as the header defines it, written with numpy reshapes: value block
     (t, s) holds in chunk 16q + i the stored values 32s + 8q .. +7 of row 16t + i; metadata block
@@ -177,8 +210,24 @@ def test_nm_tile_layout(gpu, R, C):
     assert np.array_equal(gv, tv) and np.array_equal(gm, tm)
 
 
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 640), (1024, 4096), (384, 1152)])
+def test_compress_pair_tiled(gpu, R, C):
+    """sra_compress_pair_tiled = sra_nm_tile of sra_compress_pair's outputs, bit for bit (partial
+    512-column metadata batches included: their unused words are zero)."""
+    wl = Workload("pair_tiled", T=1, K=C, N=R, r=0, dtype="bf16", fmt="nm")
+    W = layer_inputs(wl, seed=R * 7 + C, with_dy=False)["W"].cuda()
+    S, P = sra.compress_pair(W)
+    St, Pt = sra.compress_pair_tiled(W)
+    Se, Pe = sra.nm_tile(S), sra.nm_tile(P)
+    torch.cuda.synchronize()
+    for a, b in ((St, Se), (Pt, Pe)):
+        assert (a.rows, a.cols, a.fmt) == (b.rows, b.cols, b.fmt)
+        assert torch.equal(a.values.view(torch.int16), b.values.view(torch.int16))
+        assert torch.equal(a.meta, b.meta)
+
+
 def test_nm_tile_rejects_large_t(gpu):
-    wl = Workload("tile", T=17, K=64, N=32, r=0, dtype="bf16", fmt="nm")
+    wl = Workload("tile", T=17, K=96, N=32, r=0, dtype="bf16", fmt="nm")
     inp = layer_inputs(wl, seed=0, with_dy=False)
     St = sra.nm_tile(sra.compress(inp["W"].cuda()))
     with pytest.raises(SraError, match="16 tokens"):
