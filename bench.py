@@ -39,8 +39,8 @@ PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the kernel configuration the planner picks for
 # that call; a key missing here (kernel changed since the counters were taken) reports null.
 TRAFFIC_BYTES = {
-    "opt350m_fc1/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
-    "opt350m_fc1/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
+    "opt350m_fc1/canonical/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
+    "opt350m_fc1/canonical/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
     # streaming layout (sra_nm_tile), 48-row workgroups of four waves
     "opt66b_ffn_decode/T16/streaming/k_decode24<3>": 192608.7 * 1024 * 2.0 + 1152.1 * 1024,
     "opt66b_ffn_decode/T1/streaming/k_decode24<3>": 189201.6 * 1024 * 2.0 + 72.0 * 1024,
@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
     ap.add_argument("--decode-layout", choices=["streaming", "canonical"], default="streaming",
                     help="weight layout of the decode forward (streaming = sra_nm_tile)")
+    ap.add_argument("--layout", choices=["canonical", "streaming"], default="canonical",
+                    help="weight layout of the training step (streaming = sra_compress_pair_tiled)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle sampling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -186,8 +188,14 @@ def bench_nm_layer(args, wl):
     inp = layer_inputs(wl, seed=0)
     X, W, A, B, dY = (inp[k].to(dev) for k in ("X", "W", "A", "B", "dY"))
     T, r = wl.T, wl.r
-    S = sra.compress(W)
-    P = sra.double_prune(S)
+    tiled = args.layout == "streaming"
+    if tiled:
+        S, P = sra.compress_pair_tiled(W)
+        pair = lambda: sra.compress_pair_tiled(W, out=(S, P))  # noqa: E731
+    else:
+        S = sra.compress(W)
+        P = sra.double_prune(S)
+        pair = lambda: sra.compress_pair(W, out=(S, P))  # noqa: E731
     Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
     U = torch.empty((T, r), dtype=torch.float32, device=dev)
     ws_f = torch.empty(max(1, sra.fwd_workspace(S, T, r)), dtype=torch.uint8, device=dev)
@@ -203,7 +211,7 @@ def bench_nm_layer(args, wl):
         sra.sparse_lora_bwd(P, dY, X, U, A, B, ws=ws_b, out=grads)
 
     def step():
-        sra.compress_pair(W, out=(S, P))  # compress and double prune in one pass over W
+        pair()  # compress and double prune in one pass over W
         fwd()
         bwd()
 
@@ -211,7 +219,7 @@ def bench_nm_layer(args, wl):
     ms = time_graph(step, args.steps, args.warmup, graph)
     ms_fwd = time_graph(fwd, args.steps, args.warmup, graph)
     ms_bwd = time_graph(bwd, args.steps, args.warmup, graph)
-    ms_cmp = time_graph(lambda: sra.compress_pair(W, out=(S, P)), args.steps, args.warmup, graph)
+    ms_cmp = time_graph(pair, args.steps, args.warmup, graph)
     # dense bf16 baseline: the same layer's forward and input-gradient GEMMs (hipBLASLt)
     Wd = W.contiguous()
     d_fwd = time_graph(lambda: torch.nn.functional.linear(X, Wd), args.steps, args.warmup, graph)
@@ -234,9 +242,10 @@ def bench_nm_layer(args, wl):
     reps = max(10, args.steps)
     k_fwd = time_kernel(SRA_KERNEL_SPMM24, fwd, reps)
     k_bwd = time_kernel(SRA_KERNEL_SPMM24, lambda: sra.sparse_lora_bwd(P, dY, X, U, A, B, ws=ws_b, out=grads), reps)
-    k_pair = time_kernel(SRA_KERNEL_COMPRESS, lambda: sra.compress_pair(W, out=(S, P)), reps)
-    k_cmp = time_kernel(SRA_KERNEL_COMPRESS, lambda: sra.compress(W, out=S), reps)
-    k_dp = time_kernel(SRA_KERNEL_DOUBLE_PRUNE, lambda: sra.double_prune(S, out=P), reps)
+    k_pair = time_kernel(SRA_KERNEL_COMPRESS, pair, reps)
+    # the separate single passes exist for the canonical arrays only
+    k_cmp = None if tiled else time_kernel(SRA_KERNEL_COMPRESS, lambda: sra.compress(W, out=S), reps)
+    k_dp = None if tiled else time_kernel(SRA_KERNEL_DOUBLE_PRUNE, lambda: sra.double_prune(S, out=P), reps)
 
     dense_eq, algo, nbytes = step_model(wl, T)
     # dominant kernel: the slower of the two SpMM launches; algorithmic flops per launch are the
@@ -245,10 +254,10 @@ def bench_nm_layer(args, wl):
     spmm_flops_bwd = 2 * T * wl.K * (wl.N // 2) + 2 * T * r * wl.K
     if k_bwd >= k_fwd:
         kname, kms, kflops = "k_spmm24 (backward dX = dY P^T + dU A)", k_bwd, spmm_flops_bwd
-        tkey = f"{wl.name}/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>"
+        tkey = f"{wl.name}/{args.layout}/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>"
     else:
         kname, kms, kflops = "k_spmm24 (forward Y = X Ws^T + U B^T)", k_fwd, spmm_flops_fwd
-        tkey = f"{wl.name}/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>"
+        tkey = f"{wl.name}/{args.layout}/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>"
     traffic = TRAFFIC_BYTES.get(tkey)
     achieved = kflops / (kms * 1e-3) / 1e12
     out = {
@@ -260,6 +269,7 @@ def bench_nm_layer(args, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "K": wl.K, "N": wl.N, "r": r, "sparsity": "2:4",
+                   "layout": args.layout,
                    "step": "compress + double_prune (one pass) + fwd + bwd (dX, dA, dB)",
                    "graph": graph, "seed": 0},
         "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -275,8 +285,9 @@ def bench_nm_layer(args, wl):
         "speedup_fwd_vs_dense_fwd": round(d_fwd / ms_fwd, 3),
         "speedup_bwd_vs_dense_dx": round(d_bwd / ms_bwd, 3),
         "kernel_ms": {"spmm24_fwd": round(k_fwd, 5), "spmm24_bwd": round(k_bwd, 5),
-                      "compress_pair": round(k_pair, 5), "compress": round(k_cmp, 5),
-                      "double_prune": round(k_dp, 5)},
+                      "compress_pair": round(k_pair, 5),
+                      "compress": None if k_cmp is None else round(k_cmp, 5),
+                      "double_prune": None if k_dp is None else round(k_dp, 5)},
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4),
