@@ -153,7 +153,7 @@ def test_decode_row_tiles(gpu, monkeypatch, fr, T, K, N, r):
 
 @pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (77, 384, 640, 5), (130, 256, 128, 1),
                                      (200, 512, 256, 64), (33, 1024, 512, 0), (16, 512, 256, 20),
-                                     (700, 1024, 640, 8)])
+                                     (700, 1024, 640, 8), (1900, 1152, 2048, 8)])
 def test_streaming_layout_layer(gpu, T, K, N, r):
     """Forward and double-pruned backward on the streaming layouts of Ws and P (any T when K and N
     are multiples of 128): fused and separate adapter rows, ragged tiles, the decode path."""
