@@ -54,3 +54,23 @@ def rel_err(got, ref, floor=1e-3):
     if got.size == 0:
         return 0.0
     return float(np.max(np.abs(got - ref) / (np.abs(ref) + floor)))
+
+
+def masked_weight_grad(row_act, col_act, meta, n, m, cols):
+    """Gradient of a compressed N:M matrix's stored values -- SLoPe's sparse training backward.
+
+    Source (SLoPe paperlayer summary, §2.1 and §2.3): during sparse pretraining the N:M weight is
+    trained with its mask fixed, so only the stored entries receive a gradient, which is the
+    dense weight gradient dY^T X restricted to the mask and kept in the compressed value order.
+
+    For a rows x cols matrix pruned along cols with metadata ``meta``:
+        Out[row][i] = sum_t row_act[t][row] * col_act[t][c_i(row)]
+    where c_i(row) is the column of the row's i-th stored entry (ascending).  For Ws (rows = N
+    outputs, cols = K) row_act = dY [T,N] and col_act = X [T,K], so Out = (dY^T X) o mask1 in Ws's
+    value order.  Written out as the masked dense product; float64.
+    """
+    from . import nm as _nm
+    G = row_act.T @ col_act                         # rows x cols, dense
+    rows = G.shape[0]
+    _, stored = _nm.decompress(np.zeros((rows, cols // m * n)), meta, n, m, cols)
+    return G[stored].reshape(rows, cols // m * n)

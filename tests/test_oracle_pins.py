@@ -333,6 +333,52 @@ def test_double_pruned_dx_differs_from_true_gradient():
     assert not np.allclose(layer.backward(dY, X, Wdp, A, B)["dX"], dY @ Ws)
 
 
+# ----------------------------------------------------------------------------- masked weight gradient
+
+def test_masked_weight_grad_finite_differences():
+    """L(values) = sum(dY * (X Ws^T)) with Ws = decompress(values) is linear in the stored values,
+    so central differences are exact up to rounding: one probe per stored value, in stored order."""
+    rng = np.random.default_rng(11)
+    T, K, N = 3, 16, 8
+    X, dY = rng.standard_normal((T, K)), rng.standard_normal((T, N))
+    vals, meta, _ = nm.compress(rng.standard_normal((N, K)), 2, 4)
+    g = layer.masked_weight_grad(dY, X, meta, 2, 4, K)
+    assert g.shape == vals.shape
+
+    def loss(v):
+        Ws, _ = nm.decompress(v, meta, 2, 4, K)
+        return float(np.sum(dY * (X @ Ws.T)))
+
+    num = np.zeros_like(vals)
+    for idx in np.ndindex(vals.shape):
+        p, q = vals.copy(), vals.copy()
+        p[idx] += 0.5
+        q[idx] -= 0.5
+        num[idx] = loss(p) - loss(q)
+    assert np.allclose(g, num, rtol=1e-10, atol=1e-10)
+
+
+def test_masked_weight_grad_dense_and_identity():
+    """With N = M every entry is stored and the result is the plain product dY^T X (a library
+    matmul); for 2:4 the stored gradients satisfy sum(dW o Ws) = sum(dY o (X Ws^T)) (the loss is
+    linear, homogeneous of degree one in the stored values)."""
+    rng = np.random.default_rng(12)
+    T, K, N = 5, 32, 12
+    X, dY = rng.standard_normal((T, K)), rng.standard_normal((T, N))
+    W = rng.standard_normal((N, K))
+    _, meta44, _ = nm.compress(W, 4, 4)
+    assert np.allclose(layer.masked_weight_grad(dY, X, meta44, 4, 4, K), np.matmul(dY.T, X), rtol=1e-12)
+    vals, meta, _ = nm.compress(W, 2, 4)
+    g = layer.masked_weight_grad(dY, X, meta, 2, 4, K)
+    Ws, _ = nm.decompress(vals, meta, 2, 4, K)
+    assert np.isclose(np.sum(g * vals), np.sum(dY * (X @ Ws.T)), rtol=1e-12)
+    # and the transpose orientation: P's rows are K, its stored gradient is (X^T dY) o stored(P)
+    Pv, Pm, _, _ = nm.double_prune(vals, meta, 2, 4, K)
+    gP = layer.masked_weight_grad(X, dY, Pm, 2, 4, N)
+    _, storedP = nm.decompress(Pv, Pm, 2, 4, N)
+    assert np.allclose(gP, (X.T @ dY)[storedP].reshape(K, N // 2), rtol=1e-12)
+
+
 def test_rel_err_metric():
     assert layer.rel_err([1.0, 0.0], [1.0, 0.0]) == 0.0
     assert layer.rel_err([1.02], [1.0]) == pytest.approx(0.02 / 1.001)
