@@ -239,6 +239,22 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, c
                                uint32_t flags, void* dX, float* dA, float* dB, float* dU_out,
                                void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * masked_weight_grad -- gradient of the stored values of a compressed N:M matrix (SLoPe §2.1: in
+ * sparse training the mask is fixed and only the stored entries learn; §2.3 keeps compressed
+ * forms of the weight and its transpose).  For S (rows x cols, N:M along cols):
+ *     out_values[row][i] = sum_t row_act[t][row] * col_act[t][c_i(row)]
+ * with c_i(row) the column of the row's i-th stored entry (the order of S->values).  For the
+ * forward weight Ws (rows = N, cols = K): row_act = dY [T,N], col_act = X [T,K], giving
+ * dWs = (dY^T X) o mask1 in Ws's value order.  For P (rows = K, cols = N): row_act = X,
+ * col_act = dY (P's padding slots receive the dense gradient at their positions).
+ * S: SRA_FMT_NM canonical, bf16, 2:4 (S->values is not read; S->meta is).  out_values
+ * [rows, cols/2] bf16, caller-owned.  fp32 accumulation of 32-token partials summed in fp64, one
+ * rounding to bf16.  T = 0 writes zeros.  Supported: bf16, 2:4, rows % 8 == 0.
+ */
+sra_status sra_masked_weight_grad(const sra_sparse* S /* host */, const void* row_act,
+                                  const void* col_act, int64_t T, void* out_values, void* stream);
+
 /* Kernel classes for sra_time_next_kernel. */
 enum {
   SRA_KERNEL_COMPRESS = 1,     /* 2:4 compression (sra_compress, sra_compress_pair) */
@@ -247,7 +263,8 @@ enum {
   SRA_KERNEL_ADAPTER = 4,      /* adapter products U, dU, dB, dA (one launch each) */
   SRA_KERNEL_DECODE24 = 5,     /* bf16 2:4 decode SpMM (forward with T <= 16) */
   SRA_KERNEL_SPMM_FFI = 6,     /* bf16 fixed fan-in SpMM (forward Y, backward dX) */
-  SRA_KERNEL_FFI_DENSIFY = 7   /* bf16 fixed fan-in weight expanded to dense rows before the SpMM */
+  SRA_KERNEL_FFI_DENSIFY = 7,  /* bf16 fixed fan-in weight expanded to dense rows before the SpMM */
+  SRA_KERNEL_WEIGHT_GRAD = 8   /* bf16 masked weight gradient (sra_masked_weight_grad) */
 };
 
 /*

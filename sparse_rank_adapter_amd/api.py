@@ -167,6 +167,26 @@ def compress_pair_tiled(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | No
     return Ws, P
 
 
+def masked_weight_grad(S: SparseMatrix, row_act: torch.Tensor, col_act: torch.Tensor,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """Gradient of S's stored values: out[row][i] = sum_t row_act[t][row] col_act[t][c_i(row)].
+
+    For the forward weight Ws: masked_weight_grad(Ws, dY, X) = (dY^T X) o mask in Ws's value order.
+    """
+    lib = load()
+    _dev(row_act)
+    _dev(col_act)
+    T = row_act.shape[0]
+    if row_act.shape != (T, S.rows) or col_act.shape != (T, S.cols):
+        raise ValueError("row_act must be [T, S.rows] and col_act [T, S.cols]")
+    if out is None:
+        out = torch.empty((S.rows, S.cols // S.m * S.n), dtype=S.dtype, device=S.device)
+    d = S.desc()
+    check("sra_masked_weight_grad", lib.sra_masked_weight_grad(ctypes.byref(d), _p(row_act), _p(col_act), T,
+                                                               _p(out), _stream(S.device)))
+    return out
+
+
 def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:
     """compress_ffi(W, k): keep the k largest-magnitude entries of every row (ELL, int16 columns)."""
     lib = load()

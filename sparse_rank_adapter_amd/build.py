@@ -26,6 +26,7 @@ SOURCES = [
     "decode24.hip",
     "adapter.hip",
     "spmm_ffi.hip",
+    "weight_grad.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

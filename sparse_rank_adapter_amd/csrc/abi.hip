@@ -272,7 +272,7 @@ sra_status sra_time_next_kernel(int32_t which, void* start, void* stop) {
     g_time_which = 0;
     return SRA_OK;
   }
-  if (which < SRA_KERNEL_COMPRESS || which > SRA_KERNEL_FFI_DENSIFY)
+  if (which < SRA_KERNEL_COMPRESS || which > SRA_KERNEL_WEIGHT_GRAD)
     return fail(SRA_ERR_INVALID_ARG, "unknown kernel class %d", which);
   if (!start || !stop) return fail(SRA_ERR_INVALID_ARG, "start and stop events are required");
   g_time_which = which;
@@ -384,6 +384,26 @@ sra_status sra_compress_pair_tiled(const void* W, int32_t dtype, int64_t rows, i
   return hip_done(sra::launch_compress_pair24_tiled((const uint16_t*)W, rows, cols, Ws->values, Ws->meta,
                                                     P->values, P->meta, s),
                   s, "compress_pair_tiled");
+}
+
+sra_status sra_masked_weight_grad(const sra_sparse* S, const void* row_act, const void* col_act,
+                                  int64_t T, void* out_values, void* stream) {
+  if (!S) return fail(SRA_ERR_INVALID_ARG, "S descriptor is NULL");
+  SRA_TRY(check_dtype(S->dtype));
+  if (S->format != SRA_FMT_NM) return fail(SRA_ERR_INVALID_ARG, "masked_weight_grad needs a canonical N:M matrix");
+  SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
+  if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad is bf16 only");
+  if (S->rows % 8) return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad needs rows %% 8 == 0");
+  if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
+  const bool any = S->rows > 0 && S->cols > 0;
+  SRA_TRY(check_ptr(S->meta, any, "meta"));
+  SRA_TRY(check_ptr(out_values, any, "out_values"));
+  SRA_TRY(check_ptr(row_act, any && T > 0, "row_act"));
+  SRA_TRY(check_ptr(col_act, any && T > 0, "col_act"));
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_sddmm24_bf16((const uint16_t*)row_act, (const uint16_t*)col_act, S->meta,
+                                           S->rows, S->cols, T, (uint16_t*)out_values, s),
+                  s, "masked_weight_grad");
 }
 
 sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m, size_t* value_bytes,

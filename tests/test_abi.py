@@ -202,6 +202,20 @@ def test_compress_pair_tiled_validation(lib):
     assert lib.sra_compress_pair_tiled(FAKE, SRA_BF16, 256, 256, 2, 4, None, ctypes.byref(b), None) == SRA_ERR_INVALID_ARG
 
 
+def test_masked_weight_grad_validation(lib):
+    d = nm_desc(rows=64, cols=128)
+    assert lib.sra_masked_weight_grad(ctypes.byref(d), FAKE, FAKE, 16, None, None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_masked_weight_grad(ctypes.byref(d), FAKE, FAKE, -1, FAKE, None) == SRA_ERR_INVALID_ARG
+    f32 = nm_desc(rows=64, cols=128, dtype=SRA_F32)
+    assert lib.sra_masked_weight_grad(ctypes.byref(f32), FAKE, FAKE, 16, FAKE, None) == SRA_ERR_UNSUPPORTED
+    odd = nm_desc(rows=60, cols=128)
+    assert lib.sra_masked_weight_grad(ctypes.byref(odd), FAKE, FAKE, 16, FAKE, None) == SRA_ERR_UNSUPPORTED
+    tiled = nm_desc(rows=64, cols=128)
+    tiled.format = SRA_FMT_NM_TILED
+    assert lib.sra_masked_weight_grad(ctypes.byref(tiled), FAKE, FAKE, 16, FAKE, None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_masked_weight_grad(None, FAKE, FAKE, 16, FAKE, None) == SRA_ERR_INVALID_ARG
+
+
 def test_bwd_validation(lib):
     P = nm_desc(rows=1024, cols=4096)
     n = ctypes.c_size_t()
