@@ -247,6 +247,22 @@ def bench_nm_layer(args, wl):
     k_cmp = None if tiled else time_kernel(SRA_KERNEL_COMPRESS, lambda: sra.compress(W, out=S), reps)
     k_dp = None if tiled else time_kernel(SRA_KERNEL_DOUBLE_PRUNE, lambda: sra.double_prune(S, out=P), reps)
 
+    # masked weight gradient of the sparse weight (sparse training's weight update input):
+    # dWs = (dY^T X) o mask1 in Ws's value order, against the dense dY^T X GEMM
+    wg = None
+    if not tiled:
+        from sparse_rank_adapter_amd._abi import SRA_KERNEL_WEIGHT_GRAD
+        gW = torch.empty((wl.N, wl.K // 2), dtype=X.dtype, device=dev)
+        k_wg = time_kernel(SRA_KERNEL_WEIGHT_GRAD, lambda: sra.masked_weight_grad(S, dY, X, out=gW), reps)
+        dYt = dY.t().contiguous()
+        d_wg = time_graph(lambda: torch.matmul(dYt, X), args.steps, args.warmup, graph)
+        wg_flops = 2 * T * wl.N * wl.K   # the dense block product the kernel performs
+        wg = {"kernel_ms": round(k_wg, 5),
+              "dense_block_tflops": round(wg_flops / (k_wg * 1e-3) / 1e12, 2),
+              "frac_bf16_mfma": round(wg_flops / (k_wg * 1e-3) / PEAK_BF16_FLOPS, 4),
+              "dense_dW_gemm_ms": round(d_wg, 5),
+              "speedup_vs_dense_dW": round(d_wg / k_wg, 3)}
+
     dense_eq, algo, nbytes = step_model(wl, T)
     # dominant kernel: the slower of the two SpMM launches; algorithmic flops per launch are the
     # stored-half products plus the adapter epilogue (2 T N K/2 + 2 T r R)
@@ -288,6 +304,7 @@ def bench_nm_layer(args, wl):
                       "compress_pair": round(k_pair, 5),
                       "compress": None if k_cmp is None else round(k_cmp, 5),
                       "double_prune": None if k_dp is None else round(k_dp, 5)},
+        "masked_weight_grad": wg,
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4),

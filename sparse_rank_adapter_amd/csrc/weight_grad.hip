@@ -9,69 +9,71 @@
 //
 // Design: the dense 64 x 128 block of RowAct^T ColAct is computed with v_mfma_f32_16x16x32_bf16 and
 // only its stored half leaves.  The reduction (tokens) runs along the rows of both operands in
-// memory, while an MFMA lane needs 8 consecutive reduction elements, so each 32-token stage is
-// loaded coalesced along the rows (16-byte chunks) and written to LDS transposed ([row][t] and
-// [col][t], 2-byte stores); fragments are then single 16-byte LDS reads.  Stages are double
-// buffered with the next stage's global loads in flight during the products.  Each stage's MFMA
-// starts from zero and its fp32 result is added to fp64 sums one stage later, so fp32 rounding acts
-// only inside a 32-token partial (the outputs are sums of thousands of signed terms and can cancel
-// to near zero).  The epilogue stages the block in LDS (fp32) and each thread picks the 16 stored
-// values of one metadata word (2 of every 4 columns), rounds them to bf16 and writes 32 bytes.
+// memory, while an MFMA lane needs 8 consecutive reduction elements.  So a 64-token stage is
+// loaded as 8 x 8 blocks (8 tokens x 8 rows or columns, eight coalesced 16-byte loads), each
+// transposed in registers with byte permutes and written to LDS as eight 16-byte rows of 8
+// tokens ([row][t] and [col][t]); fragments are then single 16-byte LDS reads.  Stages are double
+// buffered with the next stage's loads in flight during the products.  Each stage's products start
+// from zero in fp32 and are added to fp64 sums one stage later, so fp32 rounding acts only inside
+// a 64-token partial (the outputs are sums of thousands of signed terms and can cancel to near
+// zero).  The epilogue stages the fp32 block in LDS (over the operand buffers) and each thread
+// picks the 16 stored values of one metadata word (2 of every 4 columns), rounds them to bf16 and
+// writes 32 bytes.
 #include "common.h"
 
 namespace {
 
-constexpr int SD_BM = 64, SD_BC = 128, SD_BT = 32;  // rows, logical columns, tokens per stage
+constexpr int SD_BM = 64, SD_BC = 128, SD_BT = 64;  // rows, logical columns, tokens per stage
 constexpr int SD_LD = SD_BT + 8;                    // LDS row stride of the transposed tiles (bf16)
 constexpr int SD_DLD = SD_BC + 4;                   // LDS row stride of the fp32 output block
+constexpr int SD_AB = SD_BM * SD_LD, SD_BB = SD_BC * SD_LD;  // elements per stage buffer
+constexpr int SD_LDS = 2 * (SD_AB + SD_BB) * 2;              // bytes: two stages of both operands
+static_assert(SD_BM * SD_DLD * 4 <= SD_LDS, "the output block fits over the operand buffers");
 
-__global__ __launch_bounds__(256) void k_sddmm24(const uint16_t* __restrict__ ra,
-                                                 const uint16_t* __restrict__ ca,
-                                                 const uint32_t* __restrict__ meta, int64_t R,
-                                                 int64_t C, int64_t T, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[2][SD_BM * SD_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2][SD_BC * SD_LD];
-  __shared__ __attribute__((aligned(16))) float ds[SD_BM * SD_DLD];
+// 8 x 8 bf16 transpose: in[i] holds row i (8 elements), out[j] receives column j.
+SRA_DEV void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      out[j][k] = __builtin_amdgcn_perm(in[2 * k + 1][j >> 1], in[2 * k][j >> 1],
+                                        (j & 1) ? 0x07060302u : 0x05040100u);
+}
+
+__global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__ ra,
+                                                    const uint16_t* __restrict__ ca,
+                                                    const uint32_t* __restrict__ meta, int64_t R,
+                                                    int64_t C, int64_t T, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[SD_LDS];
+  uint16_t* const as0 = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* const bs0 = as0 + 2 * SD_AB;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, q4 = l >> 4;
   const int64_t c0 = (int64_t)blockIdx.x * SD_BC, r0 = (int64_t)blockIdx.y * SD_BM;
   const int nst = (int)((T + SD_BT - 1) / SD_BT);
 
-  // staging shares: one 8-row chunk of RowAct and two 8-column chunks of ColAct per thread
-  const int a_t = tid >> 3, a_m = (tid & 7) * 8;
-  const bool a_in = r0 + a_m < R;
-  int b_t[2], b_c[2];
-  bool b_in[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int idx = tid + 256 * k;
-    b_t[k] = idx >> 4;
-    b_c[k] = (idx & 15) * 8;
-    b_in[k] = c0 + b_c[k] < C;
-  }
-  u32x4 ga, gb[2];
+  // staging: threads 0..127 own one 8 x 8 block of ColAct (16 column blocks x 8 token blocks),
+  // threads 128..191 one of RowAct (8 row blocks x 8 token blocks); consecutive threads take
+  // consecutive 16-byte chunks of a token row
+  const bool is_b = tid < 128, is_a = tid >= 128 && tid < 192;
+  const int blk = is_b ? tid : tid - 128;
+  const int bx = is_b ? (blk & 15) : (blk & 7), bt = is_b ? (blk >> 4) : (blk >> 3);
+  const uint16_t* src = is_b ? ca + c0 + 8 * bx : ra + r0 + 8 * bx;
+  const int64_t ld = is_b ? C : R;
+  const bool x_in = (is_b && c0 + 8 * bx < C) || (is_a && r0 + 8 * bx < R);
+  u32x4 g[8];
   auto load = [&](int s) {
-    const int64_t t = (int64_t)s * SD_BT;
-    ga = (a_in && t + a_t < T) ? *reinterpret_cast<const u32x4*>(ra + (t + a_t) * R + r0 + a_m)
-                               : u32x4{0, 0, 0, 0};
+    const int64_t t = (int64_t)s * SD_BT + 8 * bt;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      gb[k] = (b_in[k] && t + b_t[k] < T)
-                  ? *reinterpret_cast<const u32x4*>(ca + (t + b_t[k]) * C + c0 + b_c[k])
-                  : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < 8; ++i)
+      g[i] = (x_in && t + i < T) ? *reinterpret_cast<const u32x4*>(src + (t + i) * ld) : u32x4{0, 0, 0, 0};
   };
   auto store = [&](int buf) {
+    if (!is_a && !is_b) return;
+    u32x4 tr[8];
+    transpose8(g, tr);
+    uint16_t* dst = is_b ? bs0 + buf * SD_BB : as0 + buf * SD_AB;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      as[buf][(a_m + 2 * e) * SD_LD + a_t] = (uint16_t)(ga[e] & 0xffffu);
-      as[buf][(a_m + 2 * e + 1) * SD_LD + a_t] = (uint16_t)(ga[e] >> 16);
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bs[buf][(b_c[k] + 2 * e) * SD_LD + b_t[k]] = (uint16_t)(gb[k][e] & 0xffffu);
-        bs[buf][(b_c[k] + 2 * e + 1) * SD_LD + b_t[k]] = (uint16_t)(gb[k][e] >> 16);
-      }
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(dst + (8 * bx + j) * SD_LD + 8 * bt) = tr[j];
   };
 
   // wave w: rows 16w .. 16w+15 of the block against its 8 column fragments
@@ -84,16 +86,20 @@ __global__ __launch_bounds__(256) void k_sddmm24(const uint16_t* __restrict__ ra
     for (int e = 0; e < 4; ++e) acc[j][e] = 0.0;
   }
   auto compute = [&](int buf) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&as[buf][(16 * w + l16) * SD_LD + 8 * q4]);
-    bf16x8 b[8];
+    const uint16_t* as = as0 + buf * SD_AB;
+    const uint16_t* bs = bs0 + buf * SD_BB;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(&bs[buf][(16 * j + l16) * SD_LD + 8 * q4]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[j][e] += (double)d[j][e];  // the previous stage's partial
-      d[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < SD_BT / 32; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(as + (16 * w + l16) * SD_LD + 32 * kk + 8 * q4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(bs + (16 * j + l16) * SD_LD + 32 * kk + 8 * q4);
+        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, kk ? d[j] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
     }
   };
 
@@ -113,7 +119,9 @@ __global__ __launch_bounds__(256) void k_sddmm24(const uint16_t* __restrict__ ra
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[j][e] += (double)d[j][e];
 
-  // dense block -> LDS: lane holds rows 16w + 4 q4 + e of column 16 j + l16
+  // dense block -> LDS (over the operand buffers, free after the last barrier): lane holds rows
+  // 16w + 4 q4 + e of column 16 j + l16
+  float* const ds = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -127,10 +135,10 @@ __global__ __launch_bounds__(256) void k_sddmm24(const uint16_t* __restrict__ ra
   const uint32_t word = meta[row * (C / 32) + cg / 32];
   union { u32x4 v[2]; uint32_t w[8]; } o;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int p0 = (word >> (4 * g)) & 3, p1 = (word >> (4 * g + 2)) & 3;
-    const float v0 = ds[m * SD_DLD + 32 * q + 4 * g + p0], v1 = ds[m * SD_DLD + 32 * q + 4 * g + p1];
-    o.w[g] = pack_bf16x2(v0, v1);
+  for (int g8 = 0; g8 < 8; ++g8) {
+    const int p0 = (word >> (4 * g8)) & 3, p1 = (word >> (4 * g8 + 2)) & 3;
+    const float v0 = ds[m * SD_DLD + 32 * q + 4 * g8 + p0], v1 = ds[m * SD_DLD + 32 * q + 4 * g8 + p1];
+    o.w[g8] = pack_bf16x2(v0, v1);
   }
   u32x4* dst = reinterpret_cast<u32x4*>(out + row * (C / 2) + cg / 2);
   dst[0] = o.v[0];
