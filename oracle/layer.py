@@ -74,3 +74,11 @@ def masked_weight_grad(row_act, col_act, meta, n, m, cols):
     rows = G.shape[0]
     _, stored = _nm.decompress(np.zeros((rows, cols // m * n)), meta, n, m, cols)
     return G[stored].reshape(rows, cols // m * n)
+
+
+def nm_axpby(beta, a_vals, gamma, b_vals):
+    """beta * A + gamma * B for two compressed matrices that share one N:M pattern (same metadata),
+    computed on their value arrays -- SLoPe's optimizer-side sparse kernel for weight decay and
+    the update step (SLoPe paperlayer summary, §2.3: a sparse addition of two matrices with the
+    same pattern; §2.1: the mask stays fixed, so the metadata carries over unchanged).  float64."""
+    return beta * np.asarray(a_vals, dtype=np.float64) + gamma * np.asarray(b_vals, dtype=np.float64)

@@ -379,6 +379,25 @@ def test_masked_weight_grad_dense_and_identity():
     assert np.allclose(gP, (X.T @ dY)[storedP].reshape(K, N // 2), rtol=1e-12)
 
 
+def test_nm_axpby_against_library_and_dense():
+    """beta A + gamma B on shared-pattern values equals torch.add on the values (a library routine)
+    and, decompressed, the dense combination of the two decompressed matrices; with the update
+    B = dW it is the SGD step with decoupled weight decay on the stored entries only."""
+    rng = np.random.default_rng(13)
+    W = rng.standard_normal((8, 32))
+    vals, meta, mask = nm.compress(W, 2, 4)
+    dW = layer.masked_weight_grad(rng.standard_normal((4, 8)), rng.standard_normal((4, 32)), meta, 2, 4, 32)
+    beta, gamma = 0.999, -0.01
+    out = layer.nm_axpby(beta, vals, gamma, dW)
+    ref = torch.add(torch.from_numpy(vals) * beta, torch.from_numpy(dW), alpha=gamma).numpy()
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-14)
+    D, stored = nm.decompress(out, meta, 2, 4, 32)
+    Wa, _ = nm.decompress(vals, meta, 2, 4, 32)
+    Gd, _ = nm.decompress(dW, meta, 2, 4, 32)
+    assert np.allclose(D, beta * Wa + gamma * Gd, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(stored, mask)
+
+
 def test_rel_err_metric():
     assert layer.rel_err([1.0, 0.0], [1.0, 0.0]) == 0.0
     assert layer.rel_err([1.02], [1.0]) == pytest.approx(0.02 / 1.001)
