@@ -378,6 +378,35 @@ def bench_decode(args, wl, Ts):
     return rows
 
 
+def bench_update(args, wl):
+    """Sparse update step on the OPT-66B FFN weight's compressed values (339.7 MB): the decayed SGD
+    step Ws <- (1 - lr wd) Ws - lr dWs in place (sra_nm_axpby), HBM-bound: read Ws and dWs, write
+    Ws.  Synthetic dWs of the same size; two weight copies alternate against the Infinity Cache."""
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    from sparse_rank_adapter_amd._abi import SRA_KERNEL_NM_UPDATE
+
+    dev = torch.device("cuda:0")
+    n = wl.N * wl.K // 2
+    g = torch.Generator(device=dev).manual_seed(0)
+    ws = [torch.randn(n, device=dev, generator=g).to(torch.bfloat16) for _ in range(2)]
+    dw = [torch.randn(n, device=dev, generator=g).to(torch.bfloat16) for _ in range(2)]
+    flip = [0]
+
+    def one():
+        i = flip[0] & 1
+        flip[0] += 1
+        sra.nm_axpby(1.0 - 1e-4, ws[i], -1e-3, dw[i], out=ws[i])
+    for _ in range(4):
+        one()
+    k_ms = time_kernel(SRA_KERNEL_NM_UPDATE, one, max(20, args.steps))
+    nbytes = 3 * n * 2
+    return {"workload": f"{wl.name} weight values ({n} bf16)", "kernel_ms": round(k_ms, 5),
+            "GBps": round(nbytes / (k_ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (k_ms * 1e-3) / PEAK_HBM_BPS, 4)}
+
+
 def bench_ffi(args, wl):
     """Fixed fan-in layer: forward on the ELL weight, backward dX on the exact CSR transpose plus
     the adapter gradients.  Compression and the transpose are setup, timed apart."""
@@ -510,6 +539,7 @@ def main():
     out, inp, dense_eq = bench_nm_layer(args, wl)
     if not args.no_decode:
         out["decode_opt66b_ffn"] = bench_decode(args, WORKLOADS["opt66b_ffn_decode"], (1, 4, 16))
+        out["sparse_update_opt66b_ffn"] = bench_update(args, WORKLOADS["opt66b_ffn_decode"])
     if not args.no_ffi:
         out["ffi90_4096"] = bench_ffi(args, WORKLOADS["ffi90_4096"])
     if not args.no_cpu_baseline:

@@ -255,6 +255,20 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, c
 sra_status sra_masked_weight_grad(const sra_sparse* S /* host */, const void* row_act,
                                   const void* col_act, int64_t T, void* out_values, void* stream);
 
+/*
+ * nm_axpby -- out = beta * A + gamma * B for two compressed matrices that share one N:M pattern,
+ * on their value arrays (SLoPe §2.3: a sparse addition of matrices with the same pattern, for
+ * weight decay and the update step; §2.1: the mask is fixed, so the metadata stays valid and is
+ * not touched).  With B = the masked weight gradient (sra_masked_weight_grad) this is the sparse
+ * SGD step with decoupled weight decay, Ws <- (1 - lr wd) Ws - lr dWs; afterwards
+ * sra_double_prune (or sra_compress_pair from the dense weight) refreshes the transpose form.
+ * a_values, b_values, out_values: n_values elements of `dtype` (out may equal a or b).  fp32
+ * arithmetic (one fused multiply-add per element), one rounding to the storage type.
+ * The caller guarantees the shared pattern (the call sees values only).
+ */
+sra_status sra_nm_axpby(const void* a_values, float beta, const void* b_values, float gamma,
+                        void* out_values, int64_t n_values, int32_t dtype, void* stream);
+
 /* Kernel classes for sra_time_next_kernel. */
 enum {
   SRA_KERNEL_COMPRESS = 1,     /* 2:4 compression (sra_compress, sra_compress_pair) */
@@ -264,7 +278,8 @@ enum {
   SRA_KERNEL_DECODE24 = 5,     /* bf16 2:4 decode SpMM (forward with T <= 16) */
   SRA_KERNEL_SPMM_FFI = 6,     /* bf16 fixed fan-in SpMM (forward Y, backward dX) */
   SRA_KERNEL_FFI_DENSIFY = 7,  /* bf16 fixed fan-in weight expanded to dense rows before the SpMM */
-  SRA_KERNEL_WEIGHT_GRAD = 8   /* bf16 masked weight gradient (sra_masked_weight_grad) */
+  SRA_KERNEL_WEIGHT_GRAD = 8,  /* bf16 masked weight gradient (sra_masked_weight_grad) */
+  SRA_KERNEL_NM_UPDATE = 9     /* beta A + gamma B on shared-pattern values (sra_nm_axpby) */
 };
 
 /*

@@ -5,6 +5,6 @@ this package only marshals torch tensors into those calls.  Importing it does no
 library; the first call does, and raises if it has not been built.
 """
 from .api import (SparseMatrix, bwd_workspace, compress, compress_ffi, compress_pair,  # noqa: F401
-                  compress_pair_tiled, masked_weight_grad, tile_bytes,
+                  compress_pair_tiled, masked_weight_grad, nm_axpby, tile_bytes,
                   double_prune, ffi_transpose, fwd_workspace, meta_words, nm_tile, sparse_lora_bwd,
                   sparse_lora_fwd, time_next_kernel)

@@ -3,7 +3,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsra.so")
 
@@ -18,13 +18,13 @@ SRA_GRAD_DX, SRA_GRAD_DA, SRA_GRAD_DB, SRA_DX_NO_ADAPTER = 1, 2, 4, 8
 EXPORTS = (
     "sra_abi_version", "sra_last_error", "sra_nm_meta_words", "sra_compress", "sra_double_prune",
     "sra_compress_pair", "sra_compress_pair_tiled", "sra_nm_tile_bytes", "sra_nm_tile",
-    "sra_masked_weight_grad",
+    "sra_masked_weight_grad", "sra_nm_axpby",
     "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
     "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_time_next_kernel",
 )
 SRA_KERNEL_COMPRESS, SRA_KERNEL_DOUBLE_PRUNE, SRA_KERNEL_SPMM24 = 1, 2, 3
 SRA_KERNEL_ADAPTER, SRA_KERNEL_DECODE24, SRA_KERNEL_SPMM_FFI = 4, 5, 6
-SRA_KERNEL_FFI_DENSIFY, SRA_KERNEL_WEIGHT_GRAD = 7, 8
+SRA_KERNEL_FFI_DENSIFY, SRA_KERNEL_WEIGHT_GRAD, SRA_KERNEL_NM_UPDATE = 7, 8, 9
 
 
 class SraSparse(ctypes.Structure):
@@ -57,6 +57,7 @@ def load(path: str = LIB_PATH):
         "sra_double_prune": (c_int32, [P, P, c_void_p]),
         "sra_compress_pair": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32, P, P, c_void_p]),
         "sra_compress_pair_tiled": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32, P, P, c_void_p]),
+        "sra_nm_axpby": (c_int32, [c_void_p, c_float, c_void_p, c_float, c_void_p, c_int64, c_int32, c_void_p]),
         "sra_masked_weight_grad": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
         "sra_nm_tile_bytes": (c_int32, [c_int64, c_int64, c_int32, c_int32, POINTER(c_size_t), POINTER(c_size_t)]),
         "sra_nm_tile": (c_int32, [P, P, c_void_p]),

@@ -187,6 +187,22 @@ def masked_weight_grad(S: SparseMatrix, row_act: torch.Tensor, col_act: torch.Te
     return out
 
 
+def nm_axpby(beta: float, a: torch.Tensor, gamma: float, b: torch.Tensor,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = beta * a + gamma * b on value arrays sharing one N:M pattern (sra_nm_axpby);
+    ``out=a`` updates in place."""
+    lib = load()
+    _dev(a)
+    _dev(b)
+    if a.shape != b.shape or a.dtype != b.dtype:
+        raise ValueError("a and b must have the same shape and dtype")
+    if out is None:
+        out = torch.empty_like(a)
+    check("sra_nm_axpby", lib.sra_nm_axpby(_p(a), float(beta), _p(b), float(gamma), _p(out), a.numel(),
+                                           _dt(a), _stream(a.device)))
+    return out
+
+
 def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:
     """compress_ffi(W, k): keep the k largest-magnitude entries of every row (ELL, int16 columns)."""
     lib = load()

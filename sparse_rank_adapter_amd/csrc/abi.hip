@@ -272,7 +272,7 @@ sra_status sra_time_next_kernel(int32_t which, void* start, void* stop) {
     g_time_which = 0;
     return SRA_OK;
   }
-  if (which < SRA_KERNEL_COMPRESS || which > SRA_KERNEL_WEIGHT_GRAD)
+  if (which < SRA_KERNEL_COMPRESS || which > SRA_KERNEL_NM_UPDATE)
     return fail(SRA_ERR_INVALID_ARG, "unknown kernel class %d", which);
   if (!start || !stop) return fail(SRA_ERR_INVALID_ARG, "start and stop events are required");
   g_time_which = which;
@@ -404,6 +404,18 @@ sra_status sra_masked_weight_grad(const sra_sparse* S, const void* row_act, cons
   return hip_done(sra::launch_sddmm24_bf16((const uint16_t*)row_act, (const uint16_t*)col_act, S->meta,
                                            S->rows, S->cols, T, (uint16_t*)out_values, s),
                   s, "masked_weight_grad");
+}
+
+sra_status sra_nm_axpby(const void* a_values, float beta, const void* b_values, float gamma,
+                        void* out_values, int64_t n_values, int32_t dtype, void* stream) {
+  SRA_TRY(check_dtype(dtype));
+  if (n_values < 0) return fail(SRA_ERR_INVALID_ARG, "n_values < 0");
+  SRA_TRY(check_ptr(a_values, n_values > 0, "a_values"));
+  SRA_TRY(check_ptr(b_values, n_values > 0, "b_values"));
+  SRA_TRY(check_ptr(out_values, n_values > 0, "out_values"));
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_nm_axpby(dtype, a_values, beta, b_values, gamma, out_values, n_values, s),
+                  s, "nm_axpby");
 }
 
 sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m, size_t* value_bytes,

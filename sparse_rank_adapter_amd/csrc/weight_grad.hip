@@ -19,6 +19,8 @@
 // zero).  The epilogue stages the fp32 block in LDS (over the operand buffers) and each thread
 // picks the 16 stored values of one metadata word (2 of every 4 columns), rounds them to bf16 and
 // writes 32 bytes.
+#include <algorithm>
+
 #include "common.h"
 
 namespace {
@@ -145,6 +147,65 @@ __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__
   dst[1] = o.v[1];
 }
 
+// beta * A + gamma * B on the value arrays of two compressed matrices that share one N:M pattern
+// (SLoPe §2.3's sparse addition; §2.1: the mask is fixed, so the metadata is unchanged): weight
+// decay and the update step of sparse training, e.g. Ws <- (1 - lr wd) Ws - lr dWs with dWs from
+// k_sddmm24.  Bandwidth-bound: 16 bytes per lane and operand, fp32 arithmetic (one fma), one
+// rounding to the storage type.  `out` may be `a` (in place).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_nm_axpby(const void* __restrict__ a, float beta,
+                                                  const void* __restrict__ b, float gamma,
+                                                  void* out, int64_t n) {
+  constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int U = 4;             // chunks per thread and iteration, all loads issued first
+  const int64_t nch = n / E;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  auto combine = [&](const u32x4& va, const u32x4& vb) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (BF16) {
+        const float a0 = __uint_as_float(va[k] << 16), a1 = __uint_as_float(va[k] & 0xffff0000u);
+        const float b0 = __uint_as_float(vb[k] << 16), b1 = __uint_as_float(vb[k] & 0xffff0000u);
+        r[k] = pack_bf16x2(fmaf(beta, a0, gamma * b0), fmaf(beta, a1, gamma * b1));
+      } else {
+        r[k] = __float_as_uint(fmaf(beta, __uint_as_float(va[k]), gamma * __uint_as_float(vb[k])));
+      }
+    }
+    return r;
+  };
+  const u32x4* pa = reinterpret_cast<const u32x4*>(a);
+  const u32x4* pb = reinterpret_cast<const u32x4*>(b);
+  u32x4* po = reinterpret_cast<u32x4*>(out);
+  // workgroup tiles of U x 256 consecutive chunks: the U loads of a wave read adjacent 1 KB runs
+  const int64_t full = nch / (U * 256);
+  for (int64_t tile = blockIdx.x; tile < full; tile += gridDim.x) {
+    const int64_t i = tile * (U * 256) + threadIdx.x;
+    u32x4 va[U], vb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      va[u] = pa[i + 256 * u];
+      vb[u] = pb[i + 256 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) po[i + 256 * u] = combine(va[u], vb[u]);
+  }
+  for (int64_t i = full * (U * 256) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nch; i += stride)
+    po[i] = combine(pa[i], pb[i]);
+  // tail (n % E < E elements), one thread each
+  const int64_t t = nch * E + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) {
+    if constexpr (BF16) {
+      const float av = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a)[t] << 16);
+      const float bv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(b)[t] << 16);
+      reinterpret_cast<uint16_t*>(out)[t] = f32_to_bf16(fmaf(beta, av, gamma * bv));
+    } else {
+      reinterpret_cast<float*>(out)[t] =
+          fmaf(beta, reinterpret_cast<const float*>(a)[t], gamma * reinterpret_cast<const float*>(b)[t]);
+    }
+  }
+}
+
 }  // namespace
 
 namespace sra {
@@ -155,6 +216,18 @@ hipError_t launch_sddmm24_bf16(const uint16_t* row_act, const uint16_t* col_act,
   if (R % 8 != 0 || C % 32 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((C + SD_BC - 1) / SD_BC), (unsigned)((R + SD_BM - 1) / SD_BM));
   launch(SRA_KERNEL_WEIGHT_GRAD, k_sddmm24, grid, dim3(256), 0, s, row_act, col_act, meta, R, C, T, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nm_axpby(int dtype, const void* a, float beta, const void* b, float gamma, void* out,
+                          int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t nch = n / (dtype == SRA_BF16 ? 8 : 4);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((nch + 1023) / 1024, 2048));
+  if (dtype == SRA_BF16)
+    launch(SRA_KERNEL_NM_UPDATE, k_nm_axpby<true>, dim3(grid), dim3(256), 0, s, a, beta, b, gamma, out, n);
+  else
+    launch(SRA_KERNEL_NM_UPDATE, k_nm_axpby<false>, dim3(grid), dim3(256), 0, s, a, beta, b, gamma, out, n);
   return hipGetLastError();
 }
 

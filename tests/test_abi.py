@@ -216,6 +216,14 @@ def test_masked_weight_grad_validation(lib):
     assert lib.sra_masked_weight_grad(None, FAKE, FAKE, 16, FAKE, None) == SRA_ERR_INVALID_ARG
 
 
+def test_nm_axpby_validation(lib):
+    assert lib.sra_nm_axpby(FAKE, 1.0, FAKE, 1.0, FAKE, -1, SRA_BF16, None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_nm_axpby(None, 1.0, FAKE, 1.0, FAKE, 8, SRA_BF16, None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_nm_axpby(FAKE, 1.0, FAKE, 1.0, FAKE + 2, 8, SRA_BF16, None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_nm_axpby(FAKE, 1.0, FAKE, 1.0, FAKE, 8, 7, None) != SRA_OK
+    assert lib.sra_nm_axpby(None, 1.0, None, 1.0, None, 0, SRA_BF16, None) == SRA_OK  # nothing to do
+
+
 def test_bwd_validation(lib):
     P = nm_desc(rows=1024, cols=4096)
     n = ctypes.c_size_t()
