@@ -102,7 +102,11 @@ int64_t sra_nm_meta_words(int64_t cols, int32_t n, int32_t m);
  * compress(W, N, M) -- first N:M prune (SLoPe §2.1; the mask is chosen once and kept fixed).
  * W [rows, cols] dense (dtype) -> out->values [rows, cols*n/m], out->meta [rows, meta_words].
  * In each group of m consecutive columns the n entries of largest magnitude are kept.
- * Supported: n = 2, m = 4, cols % 32 == 0.  The caller sets out->values and out->meta; the call
+ * Supported: 2:4 and 1:2 (same format: one 2-bit in-group field per stored value), cols % 32 == 0.
+ * Every call that takes a canonical N:M matrix accepts 1:2 as well; the products run it on the
+ * 2:4 kernels (a 1:2 row keeps two entries of every four columns, one per pair), converting the
+ * metadata into the workspace.  The streaming layout (sra_nm_tile, sra_compress_pair_tiled) is
+ * 2:4 only.  The caller sets out->values and out->meta; the call
  * fills the remaining descriptor fields (format, dtype, rows, cols, n, m).
  */
 sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
@@ -116,7 +120,7 @@ sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols
  * In each group of m consecutive outputs of one input column, only entries kept by Ws are
  * eligible; the n largest eligible are kept.  A group with fewer than n eligible entries is padded
  * with its lowest unused positions holding +0.0, so every group stores exactly n.
- * Supported: 2:4, Ws->rows % 32 == 0, Ws->cols % 32 == 0.
+ * Supported: 2:4 and 1:2, Ws->rows % 32 == 0, Ws->cols % 32 == 0.
  */
 sra_status sra_double_prune(const sra_sparse* Ws /* host */, sra_sparse* P /* host */, void* stream);
 

@@ -66,9 +66,18 @@ sra_status check_ptr(const void* p, bool needed, const char* name) {
 sra_status check_nm(int64_t rows, int64_t cols, int n, int m) {
   if (rows < 0 || cols < 0) return fail(SRA_ERR_INVALID_ARG, "negative shape");
   if (n < 1 || m < n || m > 4) return fail(SRA_ERR_INVALID_ARG, "invalid N:M %d:%d", n, m);
-  if (n != 2 || m != 4) return fail(SRA_ERR_UNSUPPORTED, "only 2:4 is implemented (got %d:%d)", n, m);
+  if (!((n == 2 && m == 4) || (n == 1 && m == 2)))
+    return fail(SRA_ERR_UNSUPPORTED, "only 2:4 and 1:2 are implemented (got %d:%d)", n, m);
   if (cols % 32) return fail(SRA_ERR_UNSUPPORTED, "grouped dimension %lld is not a multiple of 32", (long long)cols);
   return SRA_OK;
+}
+
+// 1:2 weights run on the 2:4 kernels: each group of four columns holds one entry of each pair, and
+// the metadata becomes the 2:4 encoding when every odd field gains 2 (word | 0x88888888).
+constexpr uint32_t kMeta12To24 = 0x88888888u;
+bool is12(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 1 && S->m == 2; }
+size_t meta_bytes(const sra_sparse* S) {
+  return (size_t)S->rows * (size_t)sra_nm_meta_words(S->cols, S->n, S->m) * 4;
 }
 
 sra_status check_sparse(const sra_sparse* S, const char* name) {
@@ -82,6 +91,7 @@ sra_status check_sparse(const sra_sparse* S, const char* name) {
     SRA_TRY(check_ptr(S->meta, any, "meta"));
   } else if (S->format == SRA_FMT_NM_TILED) {
     SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
+    if (S->n != 2 || S->m != 4) return fail(SRA_ERR_UNSUPPORTED, "%s: the streaming layout is 2:4 only", name);
     if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "%s: the streaming 2:4 layout is bf16 only", name);
     SRA_TRY(check_ptr(S->values, any, "values"));
     SRA_TRY(check_ptr(S->meta, any, "meta"));
@@ -129,7 +139,7 @@ sra::F32Sparse f32_view(const sra_sparse* S) {
 
 // ---------------------------------------------------------------- forward plan
 struct FwdPlan {
-  size_t u_off = 0, u64_off = 0, gemm_off = 0, ffi_off = 0, total = 0;
+  size_t u_off = 0, u64_off = 0, gemm_off = 0, ffi_off = 0, meta_off = 0, total = 0;
   bool own_u = false;
 };
 
@@ -159,6 +169,7 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
     p.gemm_off = a.take(g);
     if (Ws->format == SRA_FMT_ELL) p.ffi_off = a.take(sra::spmm_ffi_ws(Ws->rows, Ws->cols, T));
   }
+  if (is12(Ws)) p.meta_off = a.take(meta_bytes(Ws));  // the 2:4 encoding of the metadata
 
   p.total = a.used;
   if (plan) *plan = p;
@@ -171,6 +182,7 @@ struct BwdPlan {
   size_t u_off = 0, du_off = 0, u64_off = 0, du64_off = 0, gemm_off = 0, spmm_off = 0, total = 0;
   size_t wt_off = 0, vtu_off = 0, vtdu_off = 0;  // packed B^T, split U^T (dB), split dU^T (dA)
   size_t at_off = 0;                             // packed A^T (dX epilogue)
+  size_t meta_off = 0;                           // 1:2 metadata in the 2:4 encoding
 };
 
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
@@ -218,6 +230,7 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   p.need_du = r > 0 && (dx_ad || da || have_du);
   p.need_u = r > 0 && db;
   Arena a;
+  if (is12(P) && dx) p.meta_off = a.take(meta_bytes(P));
   if (P->dtype == SRA_F32) {  // fp32: U and dU stay fp64; U is always recomputed
     if (p.need_u) p.u64_off = a.take((size_t)T * r * 8);
     if (p.need_du) p.du64_off = a.take((size_t)T * r * 8);
@@ -308,6 +321,8 @@ sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols
   out->n = n;
   out->m = m;
   const hipStream_t s = (hipStream_t)stream;
+  if (n == 1)
+    return hip_done(sra::launch_compress12(dtype, W, rows, cols, out->values, out->meta, s), s, "compress 1:2");
   return hip_done(sra::launch_compress24(dtype, W, rows, cols, out->values, out->meta, s), s, "compress");
 }
 
@@ -326,6 +341,10 @@ sra_status sra_double_prune(const sra_sparse* Ws, sra_sparse* P, void* stream) {
   P->n = Ws->n;
   P->m = Ws->m;
   const hipStream_t s = (hipStream_t)stream;
+  if (is12(Ws))
+    return hip_done(sra::launch_double_prune12(Ws->dtype, Ws->values, Ws->meta, Ws->rows, Ws->cols,
+                                               P->values, P->meta, s),
+                    s, "double_prune 1:2");
   return hip_done(sra::launch_double_prune24(Ws->dtype, Ws->values, Ws->meta, Ws->rows, Ws->cols,
                                              P->values, P->meta, s),
                   s, "double_prune");
@@ -352,6 +371,11 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
   Ws->n = P->n = n;
   Ws->m = P->m = m;
   const hipStream_t s = (hipStream_t)stream;
+  if (n == 1) {  // 1:2: the two passes (the one-pass kernel ranks groups of four)
+    SRA_TRY(hip_done(sra::launch_compress12(dtype, W, rows, cols, Ws->values, Ws->meta, s), s, "compress 1:2"));
+    return hip_done(sra::launch_double_prune12(dtype, Ws->values, Ws->meta, rows, cols, P->values, P->meta, s),
+                    s, "double_prune 1:2");
+  }
   return hip_done(sra::launch_compress_pair24(dtype, W, rows, cols, Ws->values, Ws->meta, P->values,
                                               P->meta, s),
                   s, "compress_pair");
@@ -363,6 +387,7 @@ sra_status sra_compress_pair_tiled(const void* W, int32_t dtype, int64_t rows, i
   SRA_TRY(check_nm(rows, cols, n, m));
   SRA_TRY(check_nm(cols, rows, n, m));
   if (dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout is bf16 only");
+  if (n != 2 || m != 4) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 only");
   if (rows % 128 || cols % 128)
     return fail(SRA_ERR_UNSUPPORTED, "compress_pair_tiled needs rows and cols that are multiples of 128");
   if (!Ws || !P) return fail(SRA_ERR_INVALID_ARG, "output descriptor is NULL");
@@ -402,7 +427,8 @@ sra_status sra_masked_weight_grad(const sra_sparse* S, const void* row_act, cons
   SRA_TRY(check_ptr(col_act, any && T > 0, "col_act"));
   const hipStream_t s = (hipStream_t)stream;
   return hip_done(sra::launch_sddmm24_bf16((const uint16_t*)row_act, (const uint16_t*)col_act, S->meta,
-                                           S->rows, S->cols, T, (uint16_t*)out_values, s),
+                                           is12(S) ? kMeta12To24 : 0u, S->rows, S->cols, T,
+                                           (uint16_t*)out_values, s),
                   s, "masked_weight_grad");
 }
 
@@ -421,6 +447,7 @@ sra_status sra_nm_axpby(const void* a_values, float beta, const void* b_values, 
 sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m, size_t* value_bytes,
                              size_t* meta_bytes) {
   SRA_TRY(check_nm(rows, cols, n, m));
+  if (n != 2 || m != 4) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 only");
   if (!value_bytes || !meta_bytes) return fail(SRA_ERR_INVALID_ARG, "size pointers are NULL");
   sra::nm_tile_bytes(rows, cols, value_bytes, meta_bytes);
   return SRA_OK;
@@ -430,6 +457,7 @@ sra_status sra_nm_tile(const sra_sparse* Ws, sra_sparse* out, void* stream) {
   SRA_TRY(check_sparse(Ws, "Ws"));
   if (Ws->format != SRA_FMT_NM) return fail(SRA_ERR_INVALID_ARG, "nm_tile needs a canonical N:M weight");
   if (Ws->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout is bf16 only");
+  if (is12(Ws)) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 only");
   if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
   const bool any = Ws->rows > 0 && Ws->cols > 0;
   SRA_TRY(check_ptr(out->values, any, "out values"));
@@ -523,6 +551,16 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
   const hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)ws;
   float* U = r > 0 ? (U_out ? U_out : (float*)(wsb + plan.u_off)) : nullptr;
+  sra_sparse w24;
+  if (is12(Ws)) {  // run on the 2:4 kernels with the converted metadata
+    w24 = *Ws;
+    w24.meta = (uint32_t*)(wsb + plan.meta_off);
+    w24.n = 2;
+    w24.m = 4;
+    SRA_TRY(hip_done(sra::launch_meta_or(Ws->meta, w24.meta, (int64_t)(meta_bytes(Ws) / 4), kMeta12To24, s),
+                     s, "fwd 1:2 metadata"));
+    Ws = &w24;
+  }
 
   if (Ws->dtype == SRA_F32) {
     double* U64 = r > 0 ? (double*)(wsb + plan.u64_off) : nullptr;
@@ -605,6 +643,16 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     return SRA_OK;
   }
   uint8_t* wsb = (uint8_t*)ws;
+  sra_sparse p24;
+  if (is12(P) && fdx) {  // run on the 2:4 kernels with the converted metadata
+    p24 = *P;
+    p24.meta = (uint32_t*)(wsb + plan.meta_off);
+    p24.n = 2;
+    p24.m = 4;
+    SRA_TRY(hip_done(sra::launch_meta_or(P->meta, p24.meta, (int64_t)(meta_bytes(P) / 4), kMeta12To24, s),
+                     s, "bwd 1:2 metadata"));
+    P = &p24;
+  }
   const float* Uv = plan.need_u ? (plan.own_u ? (const float*)(wsb + plan.u_off) : U) : nullptr;
   float* dU = plan.need_du ? (plan.own_du ? (float*)(wsb + plan.du_off) : dU_out) : nullptr;
   void* gws = wsb ? wsb + plan.gemm_off : nullptr;

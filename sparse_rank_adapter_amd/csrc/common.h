@@ -105,11 +105,20 @@ hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_
                                   uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s);
 // Out[row][i] = sum_t row_act[t][row] col_act[t][c_i(row)] over the stored slots of a 2:4 matrix
 // (canonical metadata), bf16 out; R % 8 == 0, C % 32 == 0
+// (meta_or = 0x88888888 reads 1:2 metadata as its 2:4 encoding)
 hipError_t launch_sddmm24_bf16(const uint16_t* row_act, const uint16_t* col_act, const uint32_t* meta,
-                               int64_t R, int64_t C, int64_t T, uint16_t* out, hipStream_t s);
+                               uint32_t meta_or, int64_t R, int64_t C, int64_t T, uint16_t* out,
+                               hipStream_t s);
 // out = beta a + gamma b over n values (bf16 or fp32), out may alias a
 hipError_t launch_nm_axpby(int dtype, const void* a, float beta, const void* b, float gamma, void* out,
                           int64_t n, hipStream_t s);
+// 1:2 compress and double prune (canonical format), and the metadata conversion to the 2:4
+// encoding the SpMM kernels read (word | 0x88888888)
+hipError_t launch_compress12(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
+                             uint32_t* meta, hipStream_t s);
+hipError_t launch_double_prune12(int dtype, const void* vals, const uint32_t* meta, int64_t rows,
+                                 int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s);
+hipError_t launch_meta_or(const uint32_t* in, uint32_t* out, int64_t n, uint32_t bits, hipStream_t s);
 // bf16 compress + double prune with both outputs in the streaming layout (rows, cols % 128 == 0)
 hipError_t launch_compress_pair24_tiled(const uint16_t* W, int64_t rows, int64_t cols, void* vals,
                                         uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s);

@@ -8,6 +8,8 @@
 // expanded into LDS and each lane then ranks one column's groups.  bf16 (the training path) runs
 // on 128 x 128 tiles with a branch-free selection (top2_net, gather2); fp32 keeps the
 // rank-by-count selection on 128 x 64 tiles.
+#include <algorithm>
+
 #include "common.h"
 
 namespace {
@@ -416,6 +418,87 @@ __global__ __launch_bounds__(256) void k_double_prune24t(const uint16_t* __restr
   second_prune_tile<false>(tile, c0, r0, rows, cols, pv, pm);
 }
 
+// ------------------------------------------------------------------------------------------------
+// 1:2 (SLoPe §2.1 N:M pruning with N = 1, M = 2; its Lemma 2.1 figures cover 1:2).  Same canonical
+// format: values [rows, cols/2] in ascending column order, one 2-bit field (the in-pair index) per
+// stored value.  A 1:2 row keeps one entry of every column pair, so each group of four columns
+// holds exactly two: the 2:4 SMFMAC kernels take it once each odd field gains 2 (the in-quad index
+// of the pair's second half), i.e. metadata word | 0x88888888.
+
+// One lane per 32-column block of a row: 16 pairs -> 16 kept values + one metadata word.
+template <typename T>
+__global__ __launch_bounds__(256) void k_compress12(const T* __restrict__ W, int64_t rows,
+                                                    int64_t words_per_row, T* __restrict__ vals,
+                                                    uint32_t* __restrict__ meta) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows * words_per_row) return;
+  const int64_t row = id / words_per_row, w = id - row * words_per_row;
+  const int64_t cols = words_per_row * 32;
+  union { u32x4 v[32 / VEC]; T e[32]; } x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(W + row * cols + w * 32);
+#pragma unroll
+  for (int i = 0; i < 32 / VEC; ++i) x.v[i] = src[i];
+  union { u32x4 v[16 / VEC]; T e[16]; } o;
+  uint32_t word = 0;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    // larger magnitude first; equal magnitudes keep the lower index
+    const uint32_t p = mag_key(x.e[2 * g + 1]) > mag_key(x.e[2 * g]) ? 1u : 0u;
+    o.e[g] = x.e[2 * g + p];
+    word |= p << (2 * g);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(vals + row * (cols / 2) + w * 16);
+#pragma unroll
+  for (int i = 0; i < 16 / VEC; ++i) dst[i] = o.v[i];
+  meta[id] = word;
+}
+
+// Double prune of a 1:2 Ws (rows = N outputs, cols = K): P row k, pairs of output rows
+// (2g, 2g+1): the eligible entries are those Ws keeps at column k (in-pair field == k & 1, value
+// at stored index k/2); the larger eligible magnitude is kept (the lower row on ties); a pair with
+// none eligible stores its first position with +0.0.  One lane per (k, 32 output rows).
+template <typename T>
+__global__ __launch_bounds__(256) void k_double_prune12(const T* __restrict__ vals,
+                                                        const uint32_t* __restrict__ meta,
+                                                        int64_t rows, int64_t cols,
+                                                        T* __restrict__ pv, uint32_t* __restrict__ pm) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= cols) return;
+  const int64_t n0 = (int64_t)blockIdx.y * 32;
+  const int64_t mw = cols / 32, vk = k >> 1;
+  const int shift = (int)(2 * (vk & 15)), want = (int)(k & 1);
+  union { u32x4 v[16 / VEC]; T e[16]; } o;
+  uint32_t word = 0;
+#pragma unroll 4
+  for (int g = 0; g < 16; ++g) {
+    bool kept[2];
+    T v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int64_t n = n0 + 2 * g + e;
+      kept[e] = (int)((meta[n * mw + (vk >> 4)] >> shift) & 3u) == want;
+      v[e] = vals[n * (cols / 2) + vk];
+    }
+    uint32_t p = 0;
+    if (kept[0] && kept[1]) p = mag_key(v[1]) > mag_key(v[0]) ? 1u : 0u;
+    else if (kept[1]) p = 1;
+    o.e[g] = kept[p] ? v[p] : (T)0;
+    word |= p << (2 * g);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(pv + k * (rows / 2) + n0 / 2);
+#pragma unroll
+  for (int i = 0; i < 16 / VEC; ++i) dst[i] = o.v[i];
+  pm[k * (rows / 32) + n0 / 32] = word;
+}
+
+__global__ void k_meta_or(const uint32_t* __restrict__ in, uint32_t* __restrict__ out, int64_t n,
+                          uint32_t bits) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    out[i] = in[i] | bits;
+}
+
 }  // namespace
 
 namespace sra {
@@ -481,6 +564,41 @@ hipError_t launch_double_prune24(int dtype, const void* vals, const uint32_t* me
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
   launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune24<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)vals,
          meta, rows, cols, (uint32_t*)p_vals, p_meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress12(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
+                             uint32_t* meta, hipStream_t s) {
+  const int64_t wpr = cols / 32, total = rows * wpr;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == SRA_BF16)
+    launch(SRA_KERNEL_COMPRESS, k_compress12<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, rows,
+           wpr, (uint16_t*)vals, meta);
+  else
+    launch(SRA_KERNEL_COMPRESS, k_compress12<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)W, rows,
+           wpr, (uint32_t*)vals, meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_prune12(int dtype, const void* vals, const uint32_t* meta, int64_t rows,
+                                 int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (rows % 32 || cols % 32) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((cols + 255) / 256), (unsigned)(rows / 32));
+  if (dtype == SRA_BF16)
+    launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune12<uint16_t>, grid, dim3(256), 0, s,
+           (const uint16_t*)vals, meta, rows, cols, (uint16_t*)p_vals, p_meta);
+  else
+    launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune12<uint32_t>, grid, dim3(256), 0, s,
+           (const uint32_t*)vals, meta, rows, cols, (uint32_t*)p_vals, p_meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_meta_or(const uint32_t* in, uint32_t* out, int64_t n, uint32_t bits, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_meta_or, dim3(grid), dim3(256), 0, s, in, out, n, bits);
   return hipGetLastError();
 }
 

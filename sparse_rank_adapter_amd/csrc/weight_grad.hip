@@ -44,8 +44,9 @@ SRA_DEV void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
 
 __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__ ra,
                                                     const uint16_t* __restrict__ ca,
-                                                    const uint32_t* __restrict__ meta, int64_t R,
-                                                    int64_t C, int64_t T, uint16_t* __restrict__ out) {
+                                                    const uint32_t* __restrict__ meta, uint32_t meta_or,
+                                                    int64_t R, int64_t C, int64_t T,
+                                                    uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[SD_LDS];
   uint16_t* const as0 = reinterpret_cast<uint16_t*>(lds);
   uint16_t* const bs0 = as0 + 2 * SD_AB;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__
   const int m = tid >> 2, q = tid & 3;
   const int64_t row = r0 + m, cg = c0 + 32 * q;
   if (row >= R || cg >= C) return;
-  const uint32_t word = meta[row * (C / 32) + cg / 32];
+  const uint32_t word = meta[row * (C / 32) + cg / 32] | meta_or;  // 1:2 read as its 2:4 encoding
   union { u32x4 v[2]; uint32_t w[8]; } o;
 #pragma unroll
   for (int g8 = 0; g8 < 8; ++g8) {
@@ -211,11 +212,13 @@ __global__ __launch_bounds__(256) void k_nm_axpby(const void* __restrict__ a, fl
 namespace sra {
 
 hipError_t launch_sddmm24_bf16(const uint16_t* row_act, const uint16_t* col_act, const uint32_t* meta,
-                               int64_t R, int64_t C, int64_t T, uint16_t* out, hipStream_t s) {
+                               uint32_t meta_or, int64_t R, int64_t C, int64_t T, uint16_t* out,
+                               hipStream_t s) {
   if (R <= 0 || C <= 0) return hipSuccess;
   if (R % 8 != 0 || C % 32 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((C + SD_BC - 1) / SD_BC), (unsigned)((R + SD_BM - 1) / SD_BM));
-  launch(SRA_KERNEL_WEIGHT_GRAD, k_sddmm24, grid, dim3(256), 0, s, row_act, col_act, meta, R, C, T, out);
+  launch(SRA_KERNEL_WEIGHT_GRAD, k_sddmm24, grid, dim3(256), 0, s, row_act, col_act, meta, meta_or, R, C,
+         T, out);
   return hipGetLastError();
 }
 

@@ -224,6 +224,23 @@ def test_nm_axpby_validation(lib):
     assert lib.sra_nm_axpby(None, 1.0, None, 1.0, None, 0, SRA_BF16, None) == SRA_OK  # nothing to do
 
 
+def test_nm12_validation(lib):
+    """1:2 is accepted by the canonical paths and refused by the streaming layout."""
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sra_nm_tile_bytes(256, 256, 1, 2, ctypes.byref(vb), ctypes.byref(mb)) == SRA_ERR_UNSUPPORTED
+    a, b = nm_desc(rows=256, cols=256), nm_desc(rows=256, cols=256)
+    assert lib.sra_compress_pair_tiled(FAKE, SRA_BF16, 256, 256, 1, 2, ctypes.byref(a), ctypes.byref(b),
+                                       None) == SRA_ERR_UNSUPPORTED
+    d12 = nm_desc(rows=4096, cols=1024, n=1, m=2)
+    d24 = nm_desc(rows=4096, cols=1024)
+    n12, n24 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sra_fwd_workspace(ctypes.byref(d12), 2048, 16, ctypes.byref(n12)) == SRA_OK
+    assert lib.sra_fwd_workspace(ctypes.byref(d24), 2048, 16, ctypes.byref(n24)) == SRA_OK
+    assert n12.value >= n24.value + 4096 * 1024 // 32 * 4   # the converted metadata
+    assert lib.sra_nm_tile(ctypes.byref(d12), ctypes.byref(a), None) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_nm_meta_words(1024, 1, 2) == 1024 // 32
+
+
 def test_bwd_validation(lib):
     P = nm_desc(rows=1024, cols=4096)
     n = ctypes.c_size_t()
