@@ -39,8 +39,8 @@ PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the kernel configuration the planner picks for
 # that call; a key missing here (kernel changed since the counters were taken) reports null.
 TRAFFIC_BYTES = {
-    "opt350m_fc1/canonical/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
-    "opt350m_fc1/canonical/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
+    "opt350m_fc1/2:4/canonical/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
+    "opt350m_fc1/2:4/canonical/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
     # streaming layout (sra_nm_tile), 48-row workgroups of four waves
     "opt66b_ffn_decode/T16/streaming/k_decode24<3>": 192608.7 * 1024 * 2.0 + 1152.1 * 1024,
     "opt66b_ffn_decode/T1/streaming/k_decode24<3>": 189201.6 * 1024 * 2.0 + 72.0 * 1024,
@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
     ap.add_argument("--decode-layout", choices=["streaming", "canonical"], default="streaming",
                     help="weight layout of the decode forward (streaming = sra_nm_tile)")
+    ap.add_argument("--nm", choices=["2:4", "1:2"], default="2:4",
+                    help="N:M pattern of the training step's weight (1:2 runs on the 2:4 kernels)")
     ap.add_argument("--layout", choices=["canonical", "streaming"], default="canonical",
                     help="weight layout of the training step (streaming = sra_compress_pair_tiled)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph")
@@ -189,13 +191,16 @@ def bench_nm_layer(args, wl):
     X, W, A, B, dY = (inp[k].to(dev) for k in ("X", "W", "A", "B", "dY"))
     T, r = wl.T, wl.r
     tiled = args.layout == "streaming"
+    n_, m_ = (int(x) for x in args.nm.split(":"))
+    if tiled and (n_, m_) != (2, 4):
+        raise SystemExit("the streaming layout is 2:4 only")
     if tiled:
         S, P = sra.compress_pair_tiled(W)
         pair = lambda: sra.compress_pair_tiled(W, out=(S, P))  # noqa: E731
     else:
-        S = sra.compress(W)
+        S = sra.compress(W, n_, m_)
         P = sra.double_prune(S)
-        pair = lambda: sra.compress_pair(W, out=(S, P))  # noqa: E731
+        pair = lambda: sra.compress_pair(W, n_, m_, out=(S, P))  # noqa: E731
     Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
     U = torch.empty((T, r), dtype=torch.float32, device=dev)
     ws_f = torch.empty(max(1, sra.fwd_workspace(S, T, r)), dtype=torch.uint8, device=dev)
@@ -244,7 +249,7 @@ def bench_nm_layer(args, wl):
     k_bwd = time_kernel(SRA_KERNEL_SPMM24, lambda: sra.sparse_lora_bwd(P, dY, X, U, A, B, ws=ws_b, out=grads), reps)
     k_pair = time_kernel(SRA_KERNEL_COMPRESS, pair, reps)
     # the separate single passes exist for the canonical arrays only
-    k_cmp = None if tiled else time_kernel(SRA_KERNEL_COMPRESS, lambda: sra.compress(W, out=S), reps)
+    k_cmp = None if tiled else time_kernel(SRA_KERNEL_COMPRESS, lambda: sra.compress(W, n_, m_, out=S), reps)
     k_dp = None if tiled else time_kernel(SRA_KERNEL_DOUBLE_PRUNE, lambda: sra.double_prune(S, out=P), reps)
 
     # masked weight gradient of the sparse weight (sparse training's weight update input):
@@ -270,10 +275,10 @@ def bench_nm_layer(args, wl):
     spmm_flops_bwd = 2 * T * wl.K * (wl.N // 2) + 2 * T * r * wl.K
     if k_bwd >= k_fwd:
         kname, kms, kflops = "k_spmm24 (backward dX = dY P^T + dU A)", k_bwd, spmm_flops_bwd
-        tkey = f"{wl.name}/{args.layout}/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>"
+        tkey = f"{wl.name}/{args.nm}/{args.layout}/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>"
     else:
         kname, kms, kflops = "k_spmm24 (forward Y = X Ws^T + U B^T)", k_fwd, spmm_flops_fwd
-        tkey = f"{wl.name}/{args.layout}/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>"
+        tkey = f"{wl.name}/{args.nm}/{args.layout}/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>"
     traffic = TRAFFIC_BYTES.get(tkey)
     achieved = kflops / (kms * 1e-3) / 1e12
     out = {
@@ -284,7 +289,7 @@ def bench_nm_layer(args, wl):
         "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "T": T, "K": wl.K, "N": wl.N, "r": r, "sparsity": "2:4",
+        "config": {"workload": wl.name, "T": T, "K": wl.K, "N": wl.N, "r": r, "sparsity": args.nm,
                    "layout": args.layout,
                    "step": "compress + double_prune (one pass) + fwd + bwd (dX, dA, dB)",
                    "graph": graph, "seed": 0},
