@@ -457,40 +457,50 @@ __global__ __launch_bounds__(256) void k_compress12(const T* __restrict__ W, int
 // Double prune of a 1:2 Ws (rows = N outputs, cols = K): P row k, pairs of output rows
 // (2g, 2g+1): the eligible entries are those Ws keeps at column k (in-pair field == k & 1, value
 // at stored index k/2); the larger eligible magnitude is kept (the lower row on ties); a pair with
-// none eligible stores its first position with +0.0.  One lane per (k, 32 output rows).
+// none eligible stores its first position with +0.0.  One lane per (stored index j, 32 output
+// rows) writes both P rows k = 2j and 2j+1: a row's stored value at j belongs to exactly one of
+// them, so each row is read once, 2 bytes per lane (128 bytes per wave load).
 template <typename T>
 __global__ __launch_bounds__(256) void k_double_prune12(const T* __restrict__ vals,
                                                         const uint32_t* __restrict__ meta,
                                                         int64_t rows, int64_t cols,
                                                         T* __restrict__ pv, uint32_t* __restrict__ pm) {
   constexpr int VEC = 16 / sizeof(T);
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k >= cols) return;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= cols / 2) return;
   const int64_t n0 = (int64_t)blockIdx.y * 32;
-  const int64_t mw = cols / 32, vk = k >> 1;
-  const int shift = (int)(2 * (vk & 15)), want = (int)(k & 1);
-  union { u32x4 v[16 / VEC]; T e[16]; } o;
-  uint32_t word = 0;
+  const int64_t mw = cols / 32;
+  const int shift = (int)(2 * (j & 15));
+  union { u32x4 v[16 / VEC]; T e[16]; } o[2];
+  uint32_t word[2] = {0, 0};
 #pragma unroll 4
   for (int g = 0; g < 16; ++g) {
-    bool kept[2];
+    int f[2];
     T v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int64_t n = n0 + 2 * g + e;
-      kept[e] = (int)((meta[n * mw + (vk >> 4)] >> shift) & 3u) == want;
-      v[e] = vals[n * (cols / 2) + vk];
+      f[e] = (int)((meta[n * mw + (j >> 4)] >> shift) & 3u);  // 0: row keeps column 2j, 1: 2j+1
+      v[e] = vals[n * (cols / 2) + j];
     }
-    uint32_t p = 0;
-    if (kept[0] && kept[1]) p = mag_key(v[1]) > mag_key(v[0]) ? 1u : 0u;
-    else if (kept[1]) p = 1;
-    o.e[g] = kept[p] ? v[p] : (T)0;
-    word |= p << (2 * g);
-  }
-  u32x4* dst = reinterpret_cast<u32x4*>(pv + k * (rows / 2) + n0 / 2);
 #pragma unroll
-  for (int i = 0; i < 16 / VEC; ++i) dst[i] = o.v[i];
-  pm[k * (rows / 32) + n0 / 32] = word;
+    for (int h = 0; h < 2; ++h) {  // P row k = 2j + h
+      const bool k0 = f[0] == h, k1 = f[1] == h;
+      uint32_t p = 0;
+      if (k0 && k1) p = mag_key(v[1]) > mag_key(v[0]) ? 1u : 0u;
+      else if (k1) p = 1;
+      o[h].e[g] = (p ? k1 : k0) ? v[p] : (T)0;
+      word[h] |= p << (2 * g);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = 2 * j + h;
+    u32x4* dst = reinterpret_cast<u32x4*>(pv + k * (rows / 2) + n0 / 2);
+#pragma unroll
+    for (int i = 0; i < 16 / VEC; ++i) dst[i] = o[h].v[i];
+    pm[k * (rows / 32) + n0 / 32] = word[h];
+  }
 }
 
 __global__ void k_meta_or(const uint32_t* __restrict__ in, uint32_t* __restrict__ out, int64_t n,
@@ -585,7 +595,7 @@ hipError_t launch_double_prune12(int dtype, const void* vals, const uint32_t* me
                                  int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (rows % 32 || cols % 32) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((cols + 255) / 256), (unsigned)(rows / 32));
+  const dim3 grid((unsigned)((cols / 2 + 255) / 256), (unsigned)(rows / 32));
   if (dtype == SRA_BF16)
     launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune12<uint16_t>, grid, dim3(256), 0, s,
            (const uint16_t*)vals, meta, rows, cols, (uint16_t*)p_vals, p_meta);
