@@ -254,7 +254,8 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, c
  * col_act = dY (P's padding slots receive the dense gradient at their positions).
  * S: SRA_FMT_NM canonical, bf16, 2:4 (S->values is not read; S->meta is).  out_values
  * [rows, cols/2] bf16, caller-owned.  fp32 accumulation of 32-token partials summed in fp64, one
- * rounding to bf16.  T = 0 writes zeros.  Supported: bf16, 2:4, rows % 8 == 0.
+ * rounding to bf16.  T = 0 writes zeros.  Supported: bf16, 2:4 or 1:2, rows % 8 == 0,
+ * T*rows and T*cols below 2^30 elements (else SRA_ERR_UNSUPPORTED).
  */
 sra_status sra_masked_weight_grad(const sra_sparse* S /* host */, const void* row_act,
                                   const void* col_act, int64_t T, void* out_values, void* stream);

@@ -420,6 +420,8 @@ sra_status sra_masked_weight_grad(const sra_sparse* S, const void* row_act, cons
   if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad is bf16 only");
   if (S->rows % 8) return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad needs rows %% 8 == 0");
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
+  if (!sra::sddmm24_fits(S->rows, S->cols, T))
+    return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad needs T*rows and T*cols below 2^30 elements");
   const bool any = S->rows > 0 && S->cols > 0;
   SRA_TRY(check_ptr(S->meta, any, "meta"));
   SRA_TRY(check_ptr(out_values, any, "out_values"));

@@ -105,7 +105,8 @@ hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_
                                   uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s);
 // Out[row][i] = sum_t row_act[t][row] col_act[t][c_i(row)] over the stored slots of a 2:4 matrix
 // (canonical metadata), bf16 out; R % 8 == 0, C % 32 == 0
-// (meta_or = 0x88888888 reads 1:2 metadata as its 2:4 encoding)
+// (meta_or = 0x88888888 reads 1:2 metadata as its 2:4 encoding); needs T*R and T*C below 2^30
+bool sddmm24_fits(int64_t R, int64_t C, int64_t T);
 hipError_t launch_sddmm24_bf16(const uint16_t* row_act, const uint16_t* col_act, const uint32_t* meta,
                                uint32_t meta_or, int64_t R, int64_t C, int64_t T, uint16_t* out,
                                hipStream_t s);

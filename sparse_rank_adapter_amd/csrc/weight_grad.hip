@@ -9,16 +9,18 @@
 //
 // Design: the dense 64 x 128 block of RowAct^T ColAct is computed with v_mfma_f32_16x16x32_bf16 and
 // only its stored half leaves.  The reduction (tokens) runs along the rows of both operands in
-// memory, while an MFMA lane needs 8 consecutive reduction elements.  So a 64-token stage is
-// loaded as 8 x 8 blocks (8 tokens x 8 rows or columns, eight coalesced 16-byte loads), each
-// transposed in registers with byte permutes and written to LDS as eight 16-byte rows of 8
-// tokens ([row][t] and [col][t]); fragments are then single 16-byte LDS reads.  Stages are double
-// buffered with the next stage's loads in flight during the products.  Each stage's products start
-// from zero in fp32 and are added to fp64 sums one stage later, so fp32 rounding acts only inside
-// a 64-token partial (the outputs are sums of thousands of signed terms and can cancel to near
-// zero).  The epilogue stages the fp32 block in LDS (over the operand buffers) and each thread
-// picks the 16 stored values of one metadata word (2 of every 4 columns), rounds them to bf16 and
-// writes 32 bytes.
+// memory, while an MFMA lane needs 8 consecutive reduction elements.  Each 64-token stage is copied
+// as it lies (rows of tokens) from global memory to LDS by buffer -> LDS transfers into a three-
+// stage ring, and the fragments are read with ds_read_b64_tr_b16, gfx950's transposing LDS read:
+// within a group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// i / 4 + 4 r (r = 0..3).  So lane j (r = j / 4, s = j % 4) of lane group g addresses row
+// t = 8 g + 4 h + r and columns m0 + 4 s .. +3, and lane i gets column m0 + i at tokens
+// 8 g + 4 h .. +3: half (h) of an MFMA fragment.  Rows are XOR-swizzled by 16-byte chunk so the 16
+// rows of one read spread over the LDS banks.  Each stage's products start from zero in fp32 and are
+// added to fp64 sums one stage later, so fp32 rounding acts only inside a 64-token partial (the
+// outputs are sums of thousands of signed terms and can cancel to near zero).  The epilogue stages
+// the fp32 block in LDS (over the ring) and each thread picks the 16 stored values of one metadata
+// word (2 of every 4 columns), rounds them to bf16 and writes 32 bytes.
 #include <algorithm>
 
 #include "common.h"
@@ -26,20 +28,33 @@
 namespace {
 
 constexpr int SD_BM = 64, SD_BC = 128, SD_BT = 64;  // rows, logical columns, tokens per stage
-constexpr int SD_LD = SD_BT + 8;                    // LDS row stride of the transposed tiles (bf16)
-constexpr int SD_DLD = SD_BC + 4;                   // LDS row stride of the fp32 output block
-constexpr int SD_AB = SD_BM * SD_LD, SD_BB = SD_BC * SD_LD;  // elements per stage buffer
-constexpr int SD_LDS = 2 * (SD_AB + SD_BB) * 2;              // bytes: two stages of both operands
-static_assert(SD_BM * SD_DLD * 4 <= SD_LDS, "the output block fits over the operand buffers");
+constexpr int SD_NS = 3;                            // ring stages
+constexpr int SD_AROW = SD_BM * 2, SD_BROW = SD_BC * 2;        // bytes per token row of each tile
+constexpr int SD_ASTG = SD_BT * SD_AROW, SD_BSTG = SD_BT * SD_BROW;
+constexpr int SD_STAGE = SD_ASTG + SD_BSTG;                    // 24 KB
+constexpr int SD_DLD = SD_BC + 4;                              // LDS row stride of the fp32 block
+constexpr int SD_LA = SD_ASTG / (1024 * 4), SD_LB = SD_BSTG / (1024 * 4);  // 1 KB transfers per wave
+static_assert(SD_BM * SD_DLD * 4 <= SD_NS * SD_STAGE, "the output block fits over the ring");
 
-// 8 x 8 bf16 transpose: in[i] holds row i (8 elements), out[j] receives column j.
-SRA_DEV void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      out[j][k] = __builtin_amdgcn_perm(in[2 * k + 1][j >> 1], in[2 * k][j >> 1],
-                                        (j & 1) ? 0x07060302u : 0x05040100u);
+typedef __attribute__((address_space(3))) void* sd_lds_t;
+typedef short sd_v4s __attribute__((ext_vector_type(4)));
+
+// chunk swizzles (16-byte chunks, even values keep chunk pairs together): over the 16 rows one
+// transposing read touches, the 32-byte windows land in 8 distinct bank windows, twice each
+SRA_DEV int swz_a(int t) { return 2 * (((t >> 1) ^ (t >> 3)) & 3); }
+SRA_DEV int swz_b(int t) { return 2 * ((t & 3) | (((t >> 3) & 1) << 2)); }
+
+SRA_DEV void sd_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* lds_block, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (sd_lds_t)lds_block, 16, voff, soff, 0, 0);
+}
+template <int N>
+SRA_DEV void sd_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// half of an MFMA fragment (4 tokens of 16 rows or columns) by one transposing read
+SRA_DEV sd_v4s sd_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) sd_v4s*)p);
 }
 
 __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__ ra,
@@ -47,36 +62,53 @@ __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__
                                                     const uint32_t* __restrict__ meta, uint32_t meta_or,
                                                     int64_t R, int64_t C, int64_t T,
                                                     uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[SD_LDS];
-  uint16_t* const as0 = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* const bs0 = as0 + 2 * SD_AB;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[SD_NS * SD_STAGE];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, q4 = l >> 4;
   const int64_t c0 = (int64_t)blockIdx.x * SD_BC, r0 = (int64_t)blockIdx.y * SD_BM;
   const int nst = (int)((T + SD_BT - 1) / SD_BT);
 
-  // staging: threads 0..127 own one 8 x 8 block of ColAct (16 column blocks x 8 token blocks),
-  // threads 128..191 one of RowAct (8 row blocks x 8 token blocks); consecutive threads take
-  // consecutive 16-byte chunks of a token row
-  const bool is_b = tid < 128, is_a = tid >= 128 && tid < 192;
-  const int blk = is_b ? tid : tid - 128;
-  const int bx = is_b ? (blk & 15) : (blk & 7), bt = is_b ? (blk >> 4) : (blk >> 3);
-  const uint16_t* src = is_b ? ca + c0 + 8 * bx : ra + r0 + 8 * bx;
-  const int64_t ld = is_b ? C : R;
-  const bool x_in = (is_b && c0 + 8 * bx < C) || (is_a && r0 + 8 * bx < R);
-  u32x4 g[8];
-  auto load = [&](int s) {
-    const int64_t t = (int64_t)s * SD_BT + 8 * bt;
+  // buffer resources based at the tile's first column; rows past T are past the range (zeros),
+  // columns past R or C get an offset with bit 31 set (past the range too)
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ra + r0), (short)0, (int)((T * R - r0) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ca + c0), (short)0, (int)((T * C - c0) * 2), 0x00020000);
+  // transfer k of this wave: A block q = k * 4 + w covers tile rows 8q .. 8q+7 (lane: row 8q + l/8,
+  // physical chunk l % 8); B block q covers rows 4q .. 4q+3 (row 4q + l/16, chunk l % 16).  The
+  // lane fetches the logical chunk that its slot holds under the swizzle.
+  uint32_t a_off[SD_LA], b_off[SD_LB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      g[i] = (x_in && t + i < T) ? *reinterpret_cast<const u32x4*>(src + (t + i) * ld) : u32x4{0, 0, 0, 0};
+  for (int k = 0; k < SD_LA; ++k) {
+    const int q = k * 4 + w, t = 8 * q + (l >> 3), lc = (l & 7) ^ swz_a(t);
+    const bool in = r0 + 8 * lc < R;
+    a_off[k] = (uint32_t)((t * R + 8 * lc) * 2) | ((uint32_t)!in << 31);
+  }
+#pragma unroll
+  for (int k = 0; k < SD_LB; ++k) {
+    const int q = k * 4 + w, t = 4 * q + (l >> 4), lc = (l & 15) ^ swz_b(t);
+    const bool in = c0 + 8 * lc < C;
+    b_off[k] = (uint32_t)((t * C + 8 * lc) * 2) | ((uint32_t)!in << 31);
+  }
+  auto issue = [&](int st, int buf) {
+    uint8_t* base = lds + buf * SD_STAGE;
+    const int soff_a = (int)((int64_t)st * SD_BT * R * 2), soff_b = (int)((int64_t)st * SD_BT * C * 2);
+#pragma unroll
+    for (int k = 0; k < SD_LA; ++k) sd_dma(rsa, base + (k * 4 + w) * 1024, a_off[k], soff_a);
+#pragma unroll
+    for (int k = 0; k < SD_LB; ++k) sd_dma(rsb, base + SD_ASTG + (k * 4 + w) * 1024, b_off[k], soff_b);
   };
-  auto store = [&](int buf) {
-    if (!is_a && !is_b) return;
-    u32x4 tr[8];
-    transpose8(g, tr);
-    uint16_t* dst = is_b ? bs0 + buf * SD_BB : as0 + buf * SD_AB;
+
+  // fragment read addresses: lane (group g = q4, j = l16: r = j/4, s = j%4), half h, K-step kk
+  const int fr = l16 >> 2, fs = l16 & 3;
+  auto frag = [&](const uint8_t* tile, int rowb, bool is_a, int m0, int kk) {
+    union { sd_v4s h[2]; bf16x8 v; } u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(dst + (8 * bx + j) * SD_LD + 8 * bt) = tr[j];
+    for (int h = 0; h < 2; ++h) {
+      const int t = 32 * kk + 8 * q4 + 4 * h + fr, col = m0 + 4 * fs;
+      const int pc = (col >> 3) ^ (is_a ? swz_a(t) : swz_b(t));
+      u.h[h] = sd_tr(tile + t * rowb + pc * 16 + (col & 7) * 2);
+    }
+    return u.v;
   };
 
   // wave w: rows 16w .. 16w+15 of the block against its 8 column fragments
@@ -89,41 +121,44 @@ __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__
     for (int e = 0; e < 4; ++e) acc[j][e] = 0.0;
   }
   auto compute = [&](int buf) {
-    const uint16_t* as = as0 + buf * SD_AB;
-    const uint16_t* bs = bs0 + buf * SD_BB;
+    const uint8_t* at = lds + buf * SD_STAGE;
+    const uint8_t* bt = at + SD_ASTG;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[j][e] += (double)d[j][e];  // the previous stage's partial
 #pragma unroll
     for (int kk = 0; kk < SD_BT / 32; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(as + (16 * w + l16) * SD_LD + 32 * kk + 8 * q4);
+      const bf16x8 a = frag(at, SD_AROW, true, 16 * w, kk);
+      bf16x8 b[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(bs + (16 * j + l16) * SD_LD + 32 * kk + 8 * q4);
-        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, kk ? d[j] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      }
+      for (int j = 0; j < 8; ++j) b[j] = frag(bt, SD_BROW, false, 16 * j, kk);
+      __builtin_amdgcn_sched_barrier(0);  // every read of the step ahead of its products
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], kk ? d[j] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
   };
 
-  if (nst > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    if (s + 1 < nst) load(s + 1);
-    compute(s & 1);
-    if (s + 1 < nst) store((s + 1) & 1);
-    __syncthreads();
+  // ring: stage c sits in buffer c % NS; NS - 1 stages are in flight ahead of the products
+  constexpr int L = SD_LA + SD_LB;
+#pragma unroll
+  for (int c = 0; c < SD_NS - 1; ++c)
+    if (c < nst) issue(c, c);
+  for (int c = 0; c < nst; ++c) {
+    if (c + 1 < nst) sd_wait_vm<L>();  // stage c + 1's transfers may still be in flight
+    else sd_wait_vm<0>();
+    ring_barrier();                    // every wave's stage c is in LDS; stage c - 1 is consumed
+    if (c + SD_NS - 1 < nst) issue(c + SD_NS - 1, (c + SD_NS - 1) % SD_NS);
+    compute(c % SD_NS);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[j][e] += (double)d[j][e];
+  __syncthreads();  // the ring is free
 
-  // dense block -> LDS (over the operand buffers, free after the last barrier): lane holds rows
-  // 16w + 4 q4 + e of column 16 j + l16
+  // dense block -> LDS: lane holds rows 16w + 4 q4 + e of column 16 j + l16
   float* const ds = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -211,11 +246,16 @@ __global__ __launch_bounds__(256) void k_nm_axpby(const void* __restrict__ a, fl
 
 namespace sra {
 
+bool sddmm24_fits(int64_t R, int64_t C, int64_t T) {
+  return T * R * 2 < ((int64_t)1 << 31) && T * C * 2 < ((int64_t)1 << 31);
+}
+
 hipError_t launch_sddmm24_bf16(const uint16_t* row_act, const uint16_t* col_act, const uint32_t* meta,
                                uint32_t meta_or, int64_t R, int64_t C, int64_t T, uint16_t* out,
                                hipStream_t s) {
   if (R <= 0 || C <= 0) return hipSuccess;
   if (R % 8 != 0 || C % 32 != 0) return hipErrorInvalidValue;
+  if (!sddmm24_fits(R, C, T)) return hipErrorInvalidValue;  // 32-bit buffer offsets
   const dim3 grid((unsigned)((C + SD_BC - 1) / SD_BC), (unsigned)((R + SD_BM - 1) / SD_BM));
   launch(SRA_KERNEL_WEIGHT_GRAD, k_sddmm24, grid, dim3(256), 0, s, row_act, col_act, meta, meta_or, R, C,
          T, out);
