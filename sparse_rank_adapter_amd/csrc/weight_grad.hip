@@ -111,32 +111,45 @@ __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__
     return u.v;
   };
 
-  // wave w: rows 16w .. 16w+15 of the block against its 8 column fragments
-  f32x4 d[8];
-  double acc[8][4];
+  // wave w: rows 32 (w / 2) .. +31 (two row fragments) against columns 64 (w % 2) .. +63 (four
+  // column fragments): six fragment reads per 32-token step for eight products
+  const int wr = 32 * (w >> 1), wc = 64 * (w & 1);
+  f32x4 d[2][4];
+  double acc[2][4][4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    d[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[j][e] = 0.0;
-  }
+    for (int j = 0; j < 4; ++j) {
+      d[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0;
+    }
+  auto flush = [&]() {  // the previous stage's partials into the fp64 sums
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] += (double)d[i][j][e];
+  };
   auto compute = [&](int buf) {
     const uint8_t* at = lds + buf * SD_STAGE;
     const uint8_t* bt = at + SD_ASTG;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[j][e] += (double)d[j][e];  // the previous stage's partial
+    flush();
 #pragma unroll
     for (int kk = 0; kk < SD_BT / 32; ++kk) {
-      const bf16x8 a = frag(at, SD_AROW, true, 16 * w, kk);
-      bf16x8 b[8];
+      bf16x8 a[2], b[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = frag(bt, SD_BROW, false, 16 * j, kk);
+      for (int i = 0; i < 2; ++i) a[i] = frag(at, SD_AROW, true, wr + 16 * i, kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = frag(bt, SD_BROW, false, wc + 16 * j, kk);
       __builtin_amdgcn_sched_barrier(0);  // every read of the step ahead of its products
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], kk ? d[j] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], kk ? d[i][j] : f32x4{0.f, 0.f, 0.f, 0.f},
+                                                            0, 0, 0);
     }
   };
 
@@ -152,18 +165,18 @@ __global__ __launch_bounds__(256, 2) void k_sddmm24(const uint16_t* __restrict__
     if (c + SD_NS - 1 < nst) issue(c + SD_NS - 1, (c + SD_NS - 1) % SD_NS);
     compute(c % SD_NS);
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[j][e] += (double)d[j][e];
+  flush();
   __syncthreads();  // the ring is free
 
-  // dense block -> LDS: lane holds rows 16w + 4 q4 + e of column 16 j + l16
+  // dense block -> LDS: lane holds rows wr + 16 i + 4 q4 + e of column wc + 16 j + l16
   float* const ds = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ds[(16 * w + 4 * q4 + e) * SD_DLD + 16 * j + l16] = (float)acc[j][e];
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ds[(wr + 16 * i + 4 * q4 + e) * SD_DLD + wc + 16 * j + l16] = (float)acc[i][j][e];
   __syncthreads();
 
   // stored values: thread = (row m, 32-column group q) -> one metadata word, 16 values
