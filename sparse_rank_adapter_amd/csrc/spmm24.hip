@@ -801,7 +801,8 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_s
 // holds rows 4(l/16)..+3 of token l%16.
 // MS > 0: metadata is not part of a stage but fetched in super-stages of MS stages (8 B per row per
 // stage, so MS = 8 gives 64-byte runs instead of 8-byte ones, which LDS-DMA moves ~7x faster per
-// byte) into a double buffer of its own, one super-stage ahead; needs C % 128 == 0 and no split.
+// byte; MS = 4 gives 32-byte runs in half the LDS) into a double buffer of its own, one
+// super-stage ahead; needs C % 128 == 0 and no split.
 // UG > 0: adapter rows in the activation region as in PTile (GT transfers over NW waves).
 // DN: the weight is dense (rows of C bf16, 128 bytes per row and stage, no metadata) and the
 // products are pairs of dense v_mfma_f32_16x16x32_bf16 -- the fixed fan-in layer's densified
@@ -826,10 +827,12 @@ struct QTile {
 };
 
 // TLAY: the weight is in the streaming 2:4 layout (1 KB blocks per 16-row group and 64-column stage,
-// metadata in 1 KB blocks per 16-row group and 8-stage super-stage; see decode24.hip), so every
-// transfer of the sparse operand reads 1 KB contiguously instead of 64-byte (values) and 64-byte
-// (super-stage metadata) runs per row.  Same LDS layout and products; needs MS == 8.
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false>
+// metadata in 1 KB blocks per 16-row group and 512 columns; see decode24.hip), so every transfer of
+// the values reads 1 KB contiguously instead of 64-byte runs per row, and a super-stage of
+// metadata reads 64-byte (MS = 8) or 32-byte (MS = 4) pieces of those blocks.  Same LDS layout and
+// products; needs MS > 0.
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false,
+          bool PP = false>
 __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
@@ -838,12 +841,14 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   constexpr int NW = TL::NW;
   using AD = AdapterRows<BT, (UG > 0 ? UG : 16), NW>;
-  static_assert(!TLAY || (MS == 8 && !DN), "the streaming layout is read with metadata super-stages");
+  static_assert(!TLAY || (MS > 0 && !DN), "the streaming layout is read with metadata super-stages");
   static_assert(UG == 0 || AD::ULD * 4 * BT <= TL::LDS, "U tile fits in LDS");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(BR % (16 * NW) == 0 && (MS || DN || BR % (32 * NW) == 0) && BT % (8 * NW) == 0,
                 "transfer counts must be whole per wave");
-  static_assert(MS == 0 || (MS == 8 && TL::MSB % (1024 * NW) == 0), "metadata super-stages of 8");
+  static_assert(MS == 0 || ((MS == 8 || MS == 4) && TL::MSB % (1024 * NW) == 0),
+                "metadata super-stages of 4 or 8");
+  static_assert(!PP || (NW == 8 && MS > 0 && UG == 0 && !DN), "ping-pong: eight waves, super-stages");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
 
   const int tid = threadIdx.x;
@@ -901,15 +906,19 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     m_off[k] = (uint32_t)((row * cm + (lane & 1)) * 4);
     m_dst[k] = TL::A_BYTES + b * 256;
   }
-  // super-stage metadata: 1 KB block b = 16 rows x 64 B; slot lane%4 holds 16-byte chunk
-  // slot^((row>>2)&3), chunk ch = stages 2ch and 2ch+1 of the super-stage
+  // super-stage metadata: row r holds MS*8 bytes, 16-byte chunk ch = stages 2ch and 2ch+1 of the
+  // super-stage, stored in slot ch ^ ms_swz(r); a 1 KB transfer b covers 16 rows (MS = 8, lane:
+  // row lane/4, slot lane%4) or 32 rows (MS = 4, lane: row lane/2, slot lane%2)
+  // slot swizzle of a super-stage row: the 16 rows of a fragment's 4-byte reads spread over the banks
+  auto ms_swz = [](int r) { return MS == 4 ? (r >> 2) & 1 : (r >> 2) & 3; };
   uint32_t ms_row[TL::LMS ? TL::LMS : 1];
   int ms_ch[TL::LMS ? TL::LMS : 1], ms_dst[TL::LMS ? TL::LMS : 1];
 #pragma unroll
   for (int k = 0; k < TL::LMS; ++k) {
-    const int b = k * NW + wave, row = 16 * b + (lane >> 2), pos = lane & 3;
-    ms_ch[k] = pos ^ ((row >> 2) & 3);
-    ms_row[k] = (uint32_t)(row * cm * 4);
+    constexpr int SL = MS / 2;  // 16-byte slots per row
+    const int b = k * NW + wave, row = (1024 / (8 * MS)) * b + lane / SL, pos = lane % SL;
+    ms_ch[k] = pos ^ ms_swz(row);
+    ms_row[k] = (uint32_t)row;
     ms_dst[k] = b * 1024;
   }
   uint8_t* const msbuf = smem + NS * TL::STAGE;
@@ -918,14 +927,16 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
 #pragma unroll
     for (int k = 0; k < TL::LMS; ++k) {
       if constexpr (TLAY) {
-        // super-stage g is batch g (no split): block (group, g), row i's 64 bytes at 64 i
-        const int b = k * NW + wave;
-        bdma(rm, base + ms_dst[k], 16, (uint32_t)(b * nbat * 1024 + 64 * (lane >> 2) + 16 * ms_ch[k]),
-             g * 1024);
+        // super-stage g (no split) covers columns 64 MS g ..: block (row / 16, 64 MS g / 512), row
+        // (row % 16)'s 64 bytes at 64 (row % 16), this super-stage's MS*8 of them from 8 MS (g % (8/MS))
+        const int row = (int)ms_row[k];
+        bdma(rm, base + ms_dst[k], 16,
+             (uint32_t)((row >> 4) * nbat * 1024 + 64 * (row & 15) + 16 * ms_ch[k]),
+             (g / (8 / MS)) * 1024 + 8 * MS * (g % (8 / MS)));
       } else {
         int w = 2 * (c_beg + MS * g) + 4 * ms_ch[k];  // two words per stage
         if (w > (int)cm - 4) w = (int)cm - 4;  // past the row's end: clamped, never read
-        bdma(rm, base + ms_dst[k], 16, ms_row[k] + (uint32_t)w * 4, 0);
+        bdma(rm, base + ms_dst[k], 16, ms_row[k] * (uint32_t)cm * 4 + (uint32_t)w * 4, 0);
       }
     }
   };
@@ -1013,7 +1024,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
       const int r = wr * 16 * FR + i * 16 + l16;
       af[i] = *reinterpret_cast<const bf16x8*>(A + r * 64 + ((q4 ^ ((r >> 2) & 3)) << 4));
       if constexpr (MS > 0) {
-        const int chunk = (u >> 1) ^ ((r >> 2) & 3);
+        const int chunk = (u >> 1) ^ ms_swz(r);
         mword[i] = *reinterpret_cast<const uint32_t*>(MS_buf + r * (MS * 8) + (chunk << 4) +
                                                       4 * (2 * (u & 1) + (q4 >> 1)));
       } else {
@@ -1033,6 +1044,75 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   };
 
   constexpr int D = NS - 1;
+  if constexpr (PP) {
+    // Ping-pong: waves 0-3 and 4-7 (one of each per SIMD) run the same read / multiply sequence
+    // half a stage apart: the late group passes one extra barrier first (and the early group one
+    // at the end), so between two workgroup barriers one group reads fragments from LDS while the
+    // other runs the SMFMACs on the fragments it read in the previous phase, and each SIMD's
+    // matrix core and the LDS work at once instead of in turn.  Barriers k -> k+1: early reads
+    // stage c at k = 2(c - c_beg), multiplies it at k + 1; late reads it at k + 1, multiplies at
+    // k + 2.  Stage c+1 must be visible at barrier 2(c - c_beg) + 2, so each wave waits for its own
+    // transfers of it before that barrier (the late group's is the one after its read phase).  A
+    // stage's buffer is free once the late group's read phase ends (reads drained by lgkmcnt(0)),
+    // so each group issues stage c + D into the buffer of stage c-1 as it starts stage c.
+    struct Frags {
+      bf16x16 b[FT];
+      bf16x8 a[FR];
+      uint32_t m[FR];
+    };
+    auto pp_read = [&](int buf, int rel, Frags& f) {
+      const uint8_t* A = smem + buf * TL::STAGE;
+      const uint8_t* B = A + TL::A_BYTES;
+      const uint8_t* MS_buf = msbuf + ((rel / MS) & 1) * TL::MSB;
+      const int u = rel % MS;
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int tk = wt * 16 * FT + j * 16 + l16, sw = (tk >> 1) & 7;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + ((q4 ^ sw) << 4));
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
+        f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int r = wr * 16 * FR + i * 16 + l16;
+        f.a[i] = *reinterpret_cast<const bf16x8*>(A + r * 64 + ((q4 ^ ((r >> 2) & 3)) << 4));
+        const int chunk = (u >> 1) ^ ms_swz(r);
+        f.m[i] = *reinterpret_cast<const uint32_t*>(MS_buf + r * (MS * 8) + (chunk << 4) +
+                                                    4 * (2 * (u & 1) + (q4 >> 1)));
+      }
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0): the reads are done
+    };
+    auto pp_mma = [&](const Frags& f) {
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int idx = (int)(f.m[i] >> (16 * (q4 & 1)));
+#pragma unroll
+        for (int j = 0; j < FT; ++j)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], f.b[j], acc[i][j], idx, 0, 0);
+      }
+    };
+    const bool late = wave >= NW / 2;
+    Frags f;
+    if (c_beg < c_end) issue_meta(0);
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (c_beg + d < c_end) issue(c_beg + d, d);
+    wait_stages<L>(min(D, c_end - c_beg));
+    ring_barrier();  // stage c_beg visible
+    if (late) ring_barrier();
+    for (int c = c_beg; c < c_end; ++c) {
+      const int rel = c - c_beg;
+      if (rel % MS == 0 && c + MS < c_end) issue_meta(rel / MS + 1);
+      if (c + D < c_end) issue(c + D, (rel + D) % NS);
+      pp_read(rel % NS, rel, f);
+      if (late && c + 1 < c_end) wait_stages<L>(min(D, c_end - (c + 1)));
+      ring_barrier();
+      pp_mma(f);
+      if (!late && c + 1 < c_end) wait_stages<L>(min(D, c_end - (c + 1)));
+      ring_barrier();
+    }
+    if (!late) ring_barrier();
+  } else {
   if constexpr (MS > 0) {
     if (c_beg < c_end) issue_meta(0);
   }
@@ -1070,6 +1150,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     }
     if (c + D < c_end) issue(c + D, (rel + D) % NS);
     compute(rel % NS, rel);
+  }
   }
   if constexpr (UG > 0) ad.flush();
 
@@ -1507,6 +1588,10 @@ struct Cfg {
 // the same with metadata in 8-stage super-stages (C % 128 == 0, no split):
 //   55 = 256x128 (8 waves, 4 stages), 56 = 128x64 (4 waves, 4), 57 = 128x128 (4 waves, 3),
 //   58 = 256x256 (8 waves, 2), 60 = 128x64 (8 waves of 32x32, 4)
+// metadata in 4-stage super-stages (32-byte runs, half the LDS), so 256x256 keeps three stages:
+//   61 = 256x256 (8 waves, 3)
+// ping-pong (waves 0-3 and 4-7 half a stage apart, reads of one group beside the products of the
+// other): 62 = 61 so scheduled
 // streaming decode kernel (T <= 16, one 16-token column tile, weight read once from HBM):
 //   30 = 64 weight rows per workgroup (decode24.hip)
 constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 256, false},
@@ -1519,7 +1604,8 @@ constexpr Cfg kCfgs[] = {{0, 256, 256, false}, {1, 256, 128, false}, {2, 128, 25
                          {44, 256, 64, true, 128}, {50, 256, 128, true}, {51, 256, 256, true},
                          {55, 256, 128, true, 64, true}, {56, 128, 64, true, 64, true},
                          {57, 128, 128, true, 64, true}, {58, 256, 256, true, 64, true},
-                         {60, 128, 64, true, 64, true}};
+                         {60, 128, 64, true, 64, true}, {61, 256, 256, true, 64, true},
+                         {62, 256, 256, true, 64, true}};
 
 Cfg cfg_by_id(int id) {
   for (const Cfg& c : kCfgs)
@@ -1548,15 +1634,16 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
     p.splits = comma ? atoi(comma + 1) : 1;
   } else {
     // Measured on MI355X (2:4, bf16): once 256x256 tiles fill the GPU twice, eight-wave 256x256
-    // tiles with three stages win unless the reduction is long (C >= 2R), where eight-wave 256x128
-    // tiles with four stages and metadata super-stages do; eight-wave 256x128 once those fill the
-    // GPU; 128x64 for long reductions that would otherwise need a split; otherwise 128x128 (two
-    // workgroups per CU), splitting the reduction when even those leave CUs idle.
+    // tiles with three stages and 4-stage metadata super-stages (C % 128 == 0; else per-stage
+    // metadata, or 256x128 with four stages for long reductions, C >= 2R); eight-wave 256x128
+    // once those fill the GPU; 128x64 for long reductions that would otherwise need a split;
+    // otherwise 128x128 (two workgroups per CU), splitting the reduction when even those leave
+    // CUs idle.
     auto tiles = [&](int br, int bt) { return ((R + br - 1) / br) * ((T + bt - 1) / bt); };
     if (T <= 16) {
       p.cfg = cfg_by_id(30);  // few tokens: bound by reading the weight once
     } else if (pipe_ok && tiles(256, 256) >= 512) {
-      p.cfg = cfg_by_id(C >= 2 * R ? (wide_ok ? 55 : 50) : 51);
+      p.cfg = cfg_by_id(wide_ok ? 61 : C >= 2 * R ? 50 : 51);
     } else if (pipe_ok && tiles(256, 128) >= 240) {
       p.cfg = cfg_by_id(wide_ok ? 55 : 50);
     } else if (pipe_ok && tiles(128, 64) >= 240 && C >= 2048) {
@@ -1580,13 +1667,14 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
   return p;
 }
 
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false>
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false,
+          bool PP = false>
 void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
               const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
               const Plan& p, hipStream_t s, int which = SRA_KERNEL_SPMM24) {
   using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
-  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN, TLAY>,
+  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN, TLAY, PP>,
               dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(64 * TL::NW), 0, s, s_vals, s_meta, R,
               C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
 }
@@ -1680,13 +1768,15 @@ hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_me
   if (fuse && (!fuse_ok(p, C, ep.r) || ep.g_ld % 8 != 0)) return hipErrorInvalidValue;
   p.splits = 1;
   p.stages_per_split = (int)((C + 63) / 64);
-  const bool wide = id == 0 || id == 10 || id == 22 || id == 51 || id == 58;   // 256x256
+  const bool wide = id == 0 || id == 10 || id == 22 || id == 51 || id == 58 || id == 61;  // 256x256
   const bool mid = id == 1 || id == 11 || id == 20 || id == 50 || id == 55;    // 256x128
   if (fuse) {
     if (id == 55) launch_q<4, 4, 4, 2, 3, 8, 16, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
     else launch_q<2, 2, 4, 2, 4, 8, 16, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+  } else if (id == 62) {
+    launch_q<4, 8, 4, 2, 3, 4, 0, false, true, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
   } else if (wide) {
-    launch_q<4, 8, 4, 2, 2, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+    launch_q<4, 8, 4, 2, 3, 4, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
   } else if (mid) {
     launch_q<4, 4, 4, 2, 4, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
   } else {
@@ -1720,6 +1810,8 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
     case 60: launch_q<2, 2, 4, 2, 4, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 57: launch_q<4, 4, 2, 2, 3, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 58: launch_q<4, 8, 4, 2, 2, 8>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 61: launch_q<4, 8, 4, 2, 3, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
+    case 62: launch_q<4, 8, 4, 2, 3, 4, 0, false, false, true>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 50: launch_q<4, 4, 4, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 51: launch_q<4, 8, 4, 2, 3>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     case 40: launch_w<8, 4, 2, 4>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;

@@ -161,6 +161,19 @@ def test_streaming_layout_layer(gpu, T, K, N, r):
     run_nm(wl, seed=T + K + N, streaming=True)
 
 
+@pytest.mark.parametrize("cfg", ["61", "62"])
+@pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (700, 1152, 640, 8)])
+def test_streaming_layout_three_stage_wide(gpu, monkeypatch, cfg, T, K, N, r):
+    """The 256x256 tile with three stages and 4-stage metadata super-stages (32-byte pieces of the
+    streaming layout's metadata blocks; K and N not multiples of 512, so a last super-stage is
+    half past the end), also in the ping-pong schedule (62), on both layouts, forward and
+    backward."""
+    monkeypatch.setenv("SRA_SPMM24_CFG", cfg)
+    wl = Workload("wide3", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
+    run_nm(wl, seed=T + K, streaming=True)
+    run_nm(wl, seed=T + K, streaming=False)
+
+
 @pytest.mark.parametrize("name", ["opt350m_fc1", "opt13b_fc2"])
 def test_streaming_layout_bit_identical(gpu, name):
     """The streaming-layout SpMM performs the canonical kernels' SMFMAC sequence per output element,

@@ -18,7 +18,7 @@ from tests._util import Report, bits, f64
 
 pytestmark = pytest.mark.gpu
 
-CFGS = [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 20, 21, 22, 23, 24, 40, 41, 44, 50, 51, 55, 56, 57, 58, 60]
+CFGS = [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 20, 21, 22, 23, 24, 40, 41, 44, 50, 51, 55, 56, 57, 58, 60, 61, 62]
 
 
 @pytest.fixture(scope="module")
