@@ -160,6 +160,7 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 struct Epilogue {
   const float* U = nullptr;     // [T][r] fp32
   const uint16_t* E = nullptr;  // bf16, element (row, j) at E[row*e_row_stride + j*e_j_stride]
+                                // (the bf16 2:4 and dense SpMM launchers require e_j_stride == 1)
   int64_t e_row_stride = 0, e_j_stride = 0;
   int r = 0;
   // When G is set the SpMM computes U = Act G^T itself (G: r rows of C bf16, row j at G + j*g_ld)

@@ -1164,6 +1164,87 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
 
   // ---- fused low-rank epilogue (first split only), dense v_mfma_f32_16x16x32_bf16:
   //      A operand = E rows (lane: row l%16, j = 8(l/16)..+7), B operand = U^T (token l%16)
+  // With U from memory, the tile's U rows go through LDS once per 128 adapter columns (LDS-DMA
+  // when r % 4 == 0, no registers held), so each U element crosses from L2 once per workgroup
+  // and all of a block's transfers are in flight together, instead of every wave reading its
+  // tokens' U in four dependent rounds per block (the WR waves of one token column read the same
+  // rows).  Staged fp32 rows of 512 bytes, 16-byte chunk c of token t at slot c ^ (t % 32) so the
+  // 16 tokens of a fragment read spread over the banks; each wave splits its fragments into bf16
+  // hi + lo itself.
+  constexpr bool kStageU = UG == 0 && BT * 512 <= TL::LDS && BT % (2 * NW) == 0;
+  if constexpr (kStageU) {
+  if (ep.r > 0 && z == 0) {
+    // E rows are contiguous in j (e_j_stride == 1, checked by the launchers): one 16-byte load
+    // per fragment (eight 2-byte ones when rows are not 16-byte aligned) through a resource over
+    // E's rows R, so rows past R read as zero; entries past r (the next row's, or padding) are
+    // cleared after the load.
+    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)ep.E, 0, (int)(R * ep.e_row_stride * 2), 0x00020000);
+    const bool e_al = (ep.e_row_stride & 7) == 0;  // 16-byte aligned fragments
+    auto load_e = [&](int64_t row, int j0) {
+      union { u32x4 v; uint16_t h[8]; } x;
+      const uint32_t off = (uint32_t)((row * ep.e_row_stride + j0) * 2);
+      if (e_al) {
+        x.v = __builtin_amdgcn_raw_buffer_load_b128(re, off, 0, 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x.h[q] = __builtin_amdgcn_raw_buffer_load_b16(re, off + 2 * q, 0, 0);
+      }
+      if (j0 + 8 > ep.r) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (j0 + q >= ep.r) x.h[q] = 0;
+      }
+      return x.v;
+    };
+    const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ep.U + t0 * ep.r), 0, toks_here * ep.r * 4, 0x00020000);
+    for (int jb0 = 0; jb0 < ep.r; jb0 += 128) {
+      __syncthreads();  // the operand ring (or the previous block's U) is no longer read
+      if ((ep.r & 3) == 0) {
+#pragma unroll
+        for (int k = 0; k < BT / (2 * NW); ++k) {  // 1 KB = two token rows per transfer
+          const int b = k * NW + wave, tok = 2 * b + (lane >> 5), c = (lane & 31) ^ (tok & 31);
+          const int j = jb0 + 4 * c;
+          bdma(ru, smem + b * 1024, 16, j < ep.r ? (uint32_t)((tok * ep.r + j) * 4) : 0x80000000u, 0);
+        }
+      } else {  // U rows not 16-byte aligned: 4-byte transfers, 64 floats (256 B) each
+#pragma unroll 1
+        for (int k = 0; k < 2 * BT / NW; ++k) {
+          const int b = k * NW + wave, f = 64 * b + lane, tok = f >> 7, p = f & 127;
+          const int j = jb0 + 4 * ((p >> 2) ^ (tok & 31)) + (p & 3);
+          bdma(ru, smem + b * 256, 4, j < ep.r ? (uint32_t)((tok * ep.r + j) * 4) : 0x80000000u, 0);
+        }
+      }
+      wait_vm<0>();
+      __syncthreads();
+      const int nj = min(128, ep.r - jb0);
+      for (int jj = 0; jj < nj; jj += 32) {
+        const int c0 = (jj + 8 * q4) >> 2;
+        union { u32x4 v; bf16x8 b; } e[FR];
+#pragma unroll
+        for (int i = 0; i < FR; ++i) e[i].v = load_e(row0 + wr * 16 * FR + i * 16 + l16, jb0 + jj + 8 * q4);
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+          const int tl = wt * 16 * FT + j * 16 + l16, sw = tl & 31;
+          const f32x4 u0 = *reinterpret_cast<const f32x4*>(smem + tl * 512 + 16 * (c0 ^ sw));
+          const f32x4 u1 = *reinterpret_cast<const f32x4*>(smem + tl * 512 + 16 * ((c0 + 1) ^ sw));
+          union { uint16_t h[8]; bf16x8 b; } uhi, ulo;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            split_bf16(u0[q], uhi.h[q], ulo.h[q]);
+            split_bf16(u1[q], uhi.h[4 + q], ulo.h[4 + q]);
+          }
+#pragma unroll
+          for (int i = 0; i < FR; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e[i].b, uhi.b, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e[i].b, ulo.b, acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  } else {
   if (ep.r > 0 && z == 0) {
     const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0;
     const bool u_vec = (ep.r & 7) == 0;
@@ -1223,6 +1304,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
         }
       }
     }
+  }
   }
 
   // ---- store: lane holds rows 4(l/16)..+3 of token l%16
@@ -1731,7 +1813,7 @@ namespace sra {
 hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uint16_t* act, int64_t T,
                              const Epilogue& ep, uint16_t* out, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
-  if (C % 64 != 0 || ep.G) return hipErrorInvalidValue;
+  if (C % 64 != 0 || ep.G || (ep.r > 0 && ep.e_j_stride != 1)) return hipErrorInvalidValue;
   Plan p{cfg_by_id(13), 1, (int)(C / 64)};
   const int64_t big = ((R + 255) / 256) * ((T + 127) / 128);
   if (big >= 240)  // eight waves, 256x128 tiles, 3 stages of 48 KB
@@ -1761,7 +1843,7 @@ hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_me
                                     uint16_t* out, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
   if (T <= 16) return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s, /*tiled=*/true);
-  if (C % 128 != 0) return hipErrorInvalidValue;
+  if (C % 128 != 0 || (ep.r > 0 && ep.e_j_stride != 1)) return hipErrorInvalidValue;
   Plan p = plan_for(R, C, T);
   const int id = p.cfg.id;
   const bool fuse = ep.G != nullptr;
@@ -1789,6 +1871,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                               void* ws, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
+  if (ep.r > 0 && ep.e_j_stride != 1) return hipErrorInvalidValue;  // E rows contiguous in j
   const Plan p = plan_for(R, C, T);
   float* part = p.splits > 1 ? (float*)ws : nullptr;
   const bool fuse = ep.G != nullptr;
