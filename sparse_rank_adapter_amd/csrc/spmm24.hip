@@ -1799,6 +1799,11 @@ void launch_pipe(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int6
 // each stage (the 256x128 eight-wave tile drops to 3 stages for it; the 256x256 one would spill).
 // SRA_SPMM24_FUSE=0 turns it off.
 constexpr int kFuseRank = 16;
+// The adapter epilogue reads E through a buffer resource: rows contiguous in j, and R rows of
+// e_row_stride elements addressable with 32-bit byte offsets.
+bool epilogue_ok(const sra::Epilogue& ep, int64_t R) {
+  return ep.r <= 0 || (ep.e_j_stride == 1 && R * ep.e_row_stride * 2 < ((int64_t)1 << 31));
+}
 bool fuse_ok(const Plan& p, int64_t C, int r) {
   if (r <= 0 || r > kFuseRank || C % 64 != 0 || p.splits != 1) return false;
   const char* env = getenv("SRA_SPMM24_FUSE");
@@ -1813,7 +1818,7 @@ namespace sra {
 hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uint16_t* act, int64_t T,
                              const Epilogue& ep, uint16_t* out, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
-  if (C % 64 != 0 || ep.G || (ep.r > 0 && ep.e_j_stride != 1)) return hipErrorInvalidValue;
+  if (C % 64 != 0 || ep.G || !epilogue_ok(ep, R)) return hipErrorInvalidValue;
   Plan p{cfg_by_id(13), 1, (int)(C / 64)};
   const int64_t big = ((R + 255) / 256) * ((T + 127) / 128);
   if (big >= 240)  // eight waves, 256x128 tiles, 3 stages of 48 KB
@@ -1843,7 +1848,7 @@ hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_me
                                     uint16_t* out, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
   if (T <= 16) return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s, /*tiled=*/true);
-  if (C % 128 != 0 || (ep.r > 0 && ep.e_j_stride != 1)) return hipErrorInvalidValue;
+  if (C % 128 != 0 || !epilogue_ok(ep, R)) return hipErrorInvalidValue;
   Plan p = plan_for(R, C, T);
   const int id = p.cfg.id;
   const bool fuse = ep.G != nullptr;
@@ -1871,7 +1876,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                               void* ws, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
-  if (ep.r > 0 && ep.e_j_stride != 1) return hipErrorInvalidValue;  // E rows contiguous in j
+  if (!epilogue_ok(ep, R)) return hipErrorInvalidValue;
   const Plan p = plan_for(R, C, T);
   float* part = p.splits > 1 ? (float*)ws : nullptr;
   const bool fuse = ep.G != nullptr;
