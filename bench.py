@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="opt350m_fc1",
-                    choices=["opt350m_fc1", "opt13b_fc1", "opt13b_fc2", "ffi90_4096", "opt66b_ffn_decode"])
+                    choices=["opt350m_fc1", "opt13b_fc1", "opt13b_fc2", "opt13b_mlp", "ffi90_4096",
+                             "opt66b_ffn_decode"])
     ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
     ap.add_argument("--decode-layout", choices=["streaming", "canonical"], default="streaming",
                     help="weight layout of the decode forward (streaming = sra_nm_tile)")
@@ -318,6 +319,94 @@ def bench_nm_layer(args, wl):
     return out, inp, dense_eq
 
 
+def bench_mlp_chain(args):
+    """OPT-13B MLP step with both layers chained: fc1 forward on X, fc2 forward on fc1's Y, fc2
+    backward on dY2, fc1 backward on fc2's dX (no activation between the layers), each layer's
+    compress + double prune first; against the four dense GEMMs of the same chain."""
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    from sra_inputs import WORKLOADS, layer_inputs
+
+    dev = torch.device("cuda:0")
+    w1, w2 = WORKLOADS["opt13b_fc1"], WORKLOADS["opt13b_fc2"]
+    i1 = layer_inputs(w1, seed=0, with_dy=False)
+    i2 = layer_inputs(w2, seed=0)
+    X, W1, A1, B1 = (i1[k].to(dev) for k in ("X", "W", "A", "B"))
+    W2, A2, B2, dY2 = (i2[k].to(dev) for k in ("W", "A", "B", "dY"))
+    T = w1.T
+    tiled = args.layout == "streaming"
+    layers = []
+    for wl, W, A, B in ((w1, W1, A1, B1), (w2, W2, A2, B2)):
+        S, P = sra.compress_pair_tiled(W) if tiled else sra.compress_pair(W)
+        r = wl.r
+        layers.append(dict(
+            wl=wl, W=W, A=A, B=B, S=S, P=P,
+            Y=torch.empty((T, wl.N), dtype=X.dtype, device=dev),
+            U=torch.empty((T, r), dtype=torch.float32, device=dev),
+            ws_f=torch.empty(max(1, sra.fwd_workspace(S, T, r)), dtype=torch.uint8, device=dev),
+            ws_b=torch.empty(max(1, sra.bwd_workspace(P, T, r)), dtype=torch.uint8, device=dev),
+            g={"dX": torch.empty((T, wl.K), dtype=X.dtype, device=dev),
+               "dA": torch.empty((r, wl.K), dtype=torch.float32, device=dev),
+               "dB": torch.empty((wl.N, r), dtype=torch.float32, device=dev)}))
+    l1, l2 = layers
+
+    def pairs():
+        for L in layers:
+            if tiled:
+                sra.compress_pair_tiled(L["W"], out=(L["S"], L["P"]))
+            else:
+                sra.compress_pair(L["W"], out=(L["S"], L["P"]))
+
+    def fwd():
+        sra.sparse_lora_fwd(l1["S"], X, l1["A"], l1["B"], Y=l1["Y"], U=l1["U"], ws=l1["ws_f"])
+        sra.sparse_lora_fwd(l2["S"], l1["Y"], l2["A"], l2["B"], Y=l2["Y"], U=l2["U"], ws=l2["ws_f"])
+
+    def bwd():
+        sra.sparse_lora_bwd(l2["P"], dY2, l1["Y"], l2["U"], l2["A"], l2["B"], ws=l2["ws_b"], out=l2["g"])
+        sra.sparse_lora_bwd(l1["P"], l2["g"]["dX"], X, l1["U"], l1["A"], l1["B"], ws=l1["ws_b"],
+                            out=l1["g"])
+
+    def step():
+        pairs()
+        fwd()
+        bwd()
+
+    graph = not args.no_graph
+    ms = time_graph(step, args.steps, args.warmup, graph)
+    ms_fwd = time_graph(fwd, args.steps, args.warmup, graph)
+    ms_bwd = time_graph(bwd, args.steps, args.warmup, graph)
+    W1d, W2d = W1.contiguous(), W2.contiguous()
+    Y1d = torch.nn.functional.linear(X, W1d)
+    dX2d = torch.matmul(dY2, W2d)
+    d_fwd = time_graph(lambda: (torch.nn.functional.linear(X, W1d), torch.nn.functional.linear(Y1d, W2d)),
+                       args.steps, args.warmup, graph)
+    d_bwd = time_graph(lambda: (torch.matmul(dY2, W2d), torch.matmul(dX2d, W1d)),
+                       args.steps, args.warmup, graph)
+    dense_eq = sum(step_model(L["wl"], T, with_compress=False)[0] for L in layers)
+    return {
+        "metric": METRIC,
+        "value": round(dense_eq / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "opt13b_mlp", "T": T, "hidden": w1.K, "ffn": w1.N, "r": w1.r,
+                   "sparsity": "2:4", "layout": args.layout,
+                   "step": "per layer compress + double_prune; fc1 fwd, fc2 fwd, fc2 bwd, fc1 bwd",
+                   "graph": graph, "seed": 0},
+        # fwd + bwd of both layers against the chain's four dense GEMMs (X W1^T, Y1 W2^T, dY2 W2,
+        # dX2 W1); compress and double prune are the method's setup and are timed apart
+        "speedup_vs_dense": round((d_fwd + d_bwd) / (ms_fwd + ms_bwd), 3),
+        "speedup_step_incl_compress_vs_dense": round((d_fwd + d_bwd) / ms, 3),
+        "speedup_fwd_vs_dense_fwd": round(d_fwd / ms_fwd, 3),
+        "speedup_bwd_vs_dense_dx": round(d_bwd / ms_bwd, 3),
+        "detail_ms": {"step": round(ms, 5), "fwd": round(ms_fwd, 5), "bwd": round(ms_bwd, 5),
+                      "dense_fwd_gemms": round(d_fwd, 5), "dense_dx_gemms": round(d_bwd, 5)},
+    }
+
+
 def decode_bytes(wl, T, kernel_only=False):
     """Algorithmic HBM bytes of one decode forward call (or of the decode kernel alone: the
     down-projection U = X A^T reads A in its own launch, the kernel reads U instead)."""
@@ -520,6 +609,9 @@ def main():
         loop_calls(args)
         return
     from sra_inputs import WORKLOADS
+    if args.workload == "opt13b_mlp":
+        print(json.dumps(bench_mlp_chain(args)), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     if wl.name == "opt66b_ffn_decode":
         rows = bench_decode(args, wl, (args.decode_t,))

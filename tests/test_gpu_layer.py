@@ -362,3 +362,40 @@ def test_ffi90_sampled(gpu):
     rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 126, replace=False)]))
     cols = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 254, replace=False)]))
     run_ffi(wl, rows=rows, cols_n=cols, kcols=cols)
+
+
+@pytest.mark.parametrize("layout", ["canonical", "streaming"])
+def test_mlp_chain(gpu, layout):
+    """The OPT-13B MLP chain at a reduced size (hidden 256, FFN 1024, rank 16, 300 tokens): fc1
+    forward on X, fc2 forward on fc1's bf16 Y, fc2 backward on dY2, fc1 backward on fc2's bf16 dX,
+    no activation between the layers.  Each call is held to the tolerance against the oracle fed
+    that call's actual GPU inputs (Y1 and dX2 as the GPU produced them), so one-ulp bf16
+    differences upstream do not count against the next layer."""
+    T, H, F, r = 300, 256, 1024, 16
+    w1 = Workload("mlp_fc1", T=T, K=H, N=F, r=r, dtype="bf16", fmt="nm")
+    w2 = Workload("mlp_fc2", T=T, K=F, N=H, r=r, dtype="bf16", fmt="nm")
+    i1, i2 = layer_inputs(w1, seed=5, with_dy=False), layer_inputs(w2, seed=6)
+    X, W1, A1, B1 = (i1[k].cuda() for k in ("X", "W", "A", "B"))
+    W2, A2, B2, dY2 = (i2[k].cuda() for k in ("W", "A", "B", "dY"))
+    tiled = layout == "streaming"
+    S1, P1 = sra.compress_pair_tiled(W1) if tiled else sra.compress_pair(W1)
+    S2, P2 = sra.compress_pair_tiled(W2) if tiled else sra.compress_pair(W2)
+    Y1, U1 = sra.sparse_lora_fwd(S1, X, A1, B1)
+    Y2, U2 = sra.sparse_lora_fwd(S2, Y1, A2, B2)
+    g2 = sra.sparse_lora_bwd(P2, dY2, Y1, U2, A2, B2)
+    g1 = sra.sparse_lora_bwd(P1, g2["dX"], X, U1, A1, B1)
+    torch.cuda.synchronize()
+
+    rep = Report(torch.bfloat16)
+    for name, Win, Xin, Ain, Bin, Yg, Ug, dYin, g in (
+            ("fc1", W1, X, A1, B1, Y1, U1, g2["dX"], g1),
+            ("fc2", W2, Y1, A2, B2, Y2, U2, dY2, g2)):
+        W64, X64, A64, B64, dY64 = (f64(t.cpu()) for t in (Win, Xin, Ain, Bin, dYin))
+        Ws, Wdp = nm_oracle_weights(W64)
+        Yo, Uo = olayer.forward(X64, Ws, A64, B64)
+        rep.add(f"{name} Y", f64(Yg), Yo)
+        rep.add(f"{name} U", Ug.cpu().numpy(), Uo)
+        go = olayer.backward(dY64, X64, Wdp, A64, B64, want=("dX", "dA", "dB"))
+        for k in ("dX", "dA", "dB"):
+            rep.add(f"{name} {k}", f64(g[k]) if k == "dX" else g[k].cpu().numpy(), go[k])
+    rep.check()
