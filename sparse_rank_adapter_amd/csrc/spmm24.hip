@@ -1726,6 +1726,12 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
       p.cfg = cfg_by_id(30);  // few tokens: bound by reading the weight once
     } else if (pipe_ok && tiles(256, 256) >= 512) {
       p.cfg = cfg_by_id(wide_ok ? 61 : C >= 2 * R ? 50 : 51);
+      // long reductions whose tiles leave the last wave of 256 workgroups mostly empty: two
+      // splits of the reduction fill it (each split 8-stage aligned; the fp32 partials and their
+      // sum cost about a tenth of what the fuller waves save)
+      const int64_t t = tiles(256, 256);
+      auto fill = [](int64_t n) { return (double)n / (256.0 * (double)((n + 255) / 256)); };
+      if (wide_ok && C >= 2 * R && C % 1024 == 0 && fill(2 * t) - fill(t) >= 0.1) p.splits = 2;
     } else if (pipe_ok && tiles(256, 128) >= 240) {
       p.cfg = cfg_by_id(wide_ok ? 55 : 50);
     } else if (pipe_ok && tiles(128, 64) >= 240 && C >= 2048) {
@@ -1742,7 +1748,10 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
     }
   }
   const int nC = (int)((C + p.cfg.width - 1) / p.cfg.width);
-  if (p.splits < 1 || p.cfg.id == 30 || p.cfg.super) p.splits = 1;
+  // Metadata super-stages allow a split of the reduction when every split starts on a
+  // super-stage boundary (the 256x256 tile's 4-stage super-stages, 8-stage splits).
+  const bool super_split = p.cfg.id == 61 && p.splits > 1 && nC % (8 * p.splits) == 0;
+  if (p.splits < 1 || p.cfg.id == 30 || (p.cfg.super && !super_split)) p.splits = 1;
   if (p.splits > nC) p.splits = nC;
   p.stages_per_split = (nC + p.splits - 1) / p.splits;
   p.splits = (nC + p.stages_per_split - 1) / p.stages_per_split;

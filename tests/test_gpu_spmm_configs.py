@@ -50,3 +50,24 @@ def test_config(problem, cfg, splits):
     rep.check()
     if splits == 1:
         assert np.array_equal(bits(Y), bits(problem["Y0"]))
+
+
+def test_super_stage_split(gpu, monkeypatch):
+    """The 256x256 tile with 4-stage metadata super-stages split over the reduction (two splits of
+    8 stages each, fp32 partials summed in a fixed order) on a ragged problem: within tolerance of
+    the oracle, and the same bits on a second call."""
+    wl = Workload("split", T=300, K=1024, N=544, r=24, dtype="bf16", fmt="nm")
+    inp = layer_inputs(wl, seed=22)
+    X, W, A, B = (inp[k].cuda() for k in ("X", "W", "A", "B"))
+    S = sra.compress(W)
+    monkeypatch.setenv("SRA_SPMM24_CFG", "61,2")
+    Y, _ = sra.sparse_lora_fwd(S, X, A, B)
+    Y2, _ = sra.sparse_lora_fwd(S, X, A, B)
+    torch.cuda.synchronize()
+    W64 = f64(inp["W"])
+    _, _, mask1 = onm.compress(W64, 2, 4)
+    Yo, _ = olayer.forward(f64(inp["X"]), np.where(mask1, W64, 0.0), f64(inp["A"]), f64(inp["B"]))
+    rep = Report(torch.bfloat16)
+    rep.add("Y", f64(Y), Yo)
+    rep.check()
+    assert np.array_equal(bits(Y), bits(Y2))
