@@ -165,7 +165,8 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
   if (Ws->dtype == SRA_F32 && r > 0) p.u64_off = a.take((size_t)T * r * 8);
   if (Ws->dtype == SRA_BF16) {
     size_t g = r > 0 ? sra::adapter_rows_ws(T, Ws->cols, r) : 0;
-    if (Ws->format == SRA_FMT_NM) g = std::max(g, sra::spmm24_ws(Ws->rows, Ws->cols, T));
+    if (Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED)
+      g = std::max(g, sra::spmm24_ws(Ws->rows, Ws->cols, T));
     p.gemm_off = a.take(g);
     if (Ws->format == SRA_FMT_ELL) p.ffi_off = a.take(sra::spmm_ffi_ws(Ws->rows, Ws->cols, T));
   }
@@ -257,7 +258,7 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
     g = std::max(g, sra::adapter_grads_ws(jobs, nj, T, r));
     p.gemm_off = a.take(g);
   }
-  if (P->dtype == SRA_BF16 && P->format == SRA_FMT_NM && dx)
+  if (P->dtype == SRA_BF16 && (P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED) && dx)
     p.spmm_off = a.take(sra::spmm24_ws(K, N, T));
   if (P->dtype == SRA_BF16 && P->format == SRA_FMT_CSR && dx)
     p.spmm_off = a.take(sra::spmm_ffi_ws(K, N, T));
@@ -592,7 +593,8 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
   }
   if (Ws->format == SRA_FMT_NM_TILED)
     return hip_done(sra::launch_spmm24_tiled_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
-                                                  (const uint16_t*)X, T, ep, (uint16_t*)Y, s),
+                                                  (const uint16_t*)X, T, ep, (uint16_t*)Y,
+                                                  wsb ? wsb + plan.gemm_off : nullptr, s),
                     s, "fwd spmm 2:4 (streaming layout)");
   if (Ws->format == SRA_FMT_NM)
     return hip_done(sra::launch_spmm24_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
@@ -712,7 +714,8 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     }
     if (P->format == SRA_FMT_NM_TILED)
       SRA_TRY(hip_done(sra::launch_spmm24_tiled_bf16((const uint16_t*)P->values, P->meta, K, N,
-                                                     (const uint16_t*)dY, T, ep, (uint16_t*)dX, s),
+                                                     (const uint16_t*)dY, T, ep, (uint16_t*)dX,
+                                                     wsb ? wsb + plan.spmm_off : nullptr, s),
                        s, "bwd dX 2:4 (streaming layout)"));
     else if (P->format == SRA_FMT_NM)
       SRA_TRY(hip_done(sra::launch_spmm24_bf16((const uint16_t*)P->values, P->meta, K, N,

@@ -181,11 +181,12 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                               void* ws, hipStream_t s);
 // the same product with the weight in the streaming layout (sra_nm_tile): any T when C % 128 == 0,
-// else T <= 16 only; no workspace (never split)
+// else T <= 16 only; ws holds the fp32 partials when the plan splits the reduction (spmm24_ws
+// bytes; without it the product runs unsplit)
 bool spmm24_tiled_ok(int64_t C, int64_t T);
 hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                     int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
-                                    uint16_t* out, hipStream_t s);
+                                    uint16_t* out, void* ws, hipStream_t s);
 size_t spmm24_decode_ws(int64_t R, int64_t C, int64_t T);
 hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,

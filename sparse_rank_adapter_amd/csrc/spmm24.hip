@@ -927,12 +927,13 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
 #pragma unroll
     for (int k = 0; k < TL::LMS; ++k) {
       if constexpr (TLAY) {
-        // super-stage g (no split) covers columns 64 MS g ..: block (row / 16, 64 MS g / 512), row
-        // (row % 16)'s 64 bytes at 64 (row % 16), this super-stage's MS*8 of them from 8 MS (g % (8/MS))
+        // super-stage g covers columns 64 (c_beg + MS g) ..: block (row / 16, that / 512), row
+        // (row % 16)'s 64 bytes at 64 (row % 16), this super-stage's MS*8 of them from 8 MS (g % (8/MS));
+        // a split starts on a 512-column batch (c_beg % 8 == 0)
         const int row = (int)ms_row[k];
         bdma(rm, base + ms_dst[k], 16,
              (uint32_t)((row >> 4) * nbat * 1024 + 64 * (row & 15) + 16 * ms_ch[k]),
-             (g / (8 / MS)) * 1024 + 8 * MS * (g % (8 / MS)));
+             (c_beg / 8 + g / (8 / MS)) * 1024 + 8 * MS * (g % (8 / MS)));
       } else {
         int w = 2 * (c_beg + MS * g) + 4 * ms_ch[k];  // two words per stage
         if (w > (int)cm - 4) w = (int)cm - 4;  // past the row's end: clamped, never read
@@ -1854,7 +1855,7 @@ bool spmm24_tiled_ok(int64_t C, int64_t T) { return T <= 16 || C % 128 == 0; }
 
 hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                     int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
-                                    uint16_t* out, hipStream_t s) {
+                                    uint16_t* out, void* ws, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
   if (T <= 16) return launch_decode24_bf16(s_vals, s_meta, R, C, act, T, ep, out, s, /*tiled=*/true);
   if (C % 128 != 0 || !epilogue_ok(ep, R)) return hipErrorInvalidValue;
@@ -1862,8 +1863,12 @@ hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_me
   const int id = p.cfg.id;
   const bool fuse = ep.G != nullptr;
   if (fuse && (!fuse_ok(p, C, ep.r) || ep.g_ld % 8 != 0)) return hipErrorInvalidValue;
-  p.splits = 1;
-  p.stages_per_split = (int)((C + 63) / 64);
+  // only the 256x256 tile splits (8-stage aligned, the plan's own split); others run whole
+  if (!(id == 61 && p.splits > 1 && !fuse && ws)) {
+    p.splits = 1;
+    p.stages_per_split = (int)((C + 63) / 64);
+  }
+  float* part = p.splits > 1 ? (float*)ws : nullptr;
   const bool wide = id == 0 || id == 10 || id == 22 || id == 51 || id == 58 || id == 61;  // 256x256
   const bool mid = id == 1 || id == 11 || id == 20 || id == 50 || id == 55;    // 256x128
   if (fuse) {
@@ -1872,11 +1877,16 @@ hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_me
   } else if (id == 62) {
     launch_q<4, 8, 4, 2, 3, 4, 0, false, true, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
   } else if (wide) {
-    launch_q<4, 8, 4, 2, 3, 4, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+    launch_q<4, 8, 4, 2, 3, 4, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s);
   } else if (mid) {
     launch_q<4, 4, 4, 2, 4, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
   } else {
     launch_q<2, 2, 4, 2, 4, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
+  }
+  if (part) {
+    const int64_t n = T * R;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, s,
+                       part, p.splits, n, out);
   }
   return hipGetLastError();
 }

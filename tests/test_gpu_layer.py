@@ -174,6 +174,16 @@ def test_streaming_layout_three_stage_wide(gpu, monkeypatch, cfg, T, K, N, r):
     run_nm(wl, seed=T + K, streaming=False)
 
 
+def test_split_reduction_both_layouts(gpu, monkeypatch):
+    """The 256x256 tile with its reduction split in two (8-stage aligned splits, fp32 partials
+    summed in a fixed order) for the forward (K = 1024) and dX (N = 2048), on the canonical arrays
+    and on the streaming layout, whose split starts its metadata at a 512-column batch."""
+    monkeypatch.setenv("SRA_SPMM24_CFG", "61,2")
+    wl = Workload("split2", T=300, K=1024, N=2048, r=8, dtype="bf16", fmt="nm")
+    run_nm(wl, seed=31, streaming=True)
+    run_nm(wl, seed=31, streaming=False)
+
+
 @pytest.mark.parametrize("name", ["opt350m_fc1", "opt13b_fc2"])
 def test_streaming_layout_bit_identical(gpu, name):
     """The streaming-layout SpMM performs the canonical kernels' SMFMAC sequence per output element,
