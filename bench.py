@@ -598,8 +598,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X and has no "
-              "multi-GPU path (sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library runs the layer on a single MI355X and has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
