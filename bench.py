@@ -70,6 +70,9 @@ def parse():
                          "rocprofv3 counter runs); 'copy' copies 256 MiB (counter calibration)")
     ap.add_argument("--no-ffi", action="store_true",
                     help="skip the fixed fan-in (90% sparse) layer measured beside the main line")
+    ap.add_argument("--no-mlp", action="store_true",
+                    help="skip the chained OPT-13B MLP step (streaming layout) appended to the "
+                         "default opt350m_fc1 line")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the OPT-66B decode measurements appended to the training-step line")
     return ap.parse_args()
@@ -639,6 +642,15 @@ def main():
         out["sparse_update_opt66b_ffn"] = bench_update(args, WORKLOADS["opt66b_ffn_decode"])
     if not args.no_ffi:
         out["ffi90_4096"] = bench_ffi(args, WORKLOADS["ffi90_4096"])
+    if not args.no_mlp and args.nm == "2:4" and wl.name == "opt350m_fc1":
+        import copy
+        margs = copy.copy(args)
+        margs.layout = "streaming"
+        m = bench_mlp_chain(margs)
+        out["opt13b_mlp_streaming"] = {k: m[k] for k in (
+            "value", "unit", "ms_per_step", "speedup_vs_dense", "speedup_step_incl_compress_vs_dense",
+            "speedup_fwd_vs_dense_fwd", "speedup_bwd_vs_dense_dx", "detail_ms")}
+        out["opt13b_mlp_streaming"]["config"] = m["config"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget, dense_eq)
     print(json.dumps(out), flush=True)
