@@ -836,7 +836,7 @@ template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool D
 __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
-    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split) {
+    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split, int n_whole) {
   using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN>;
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   constexpr int NW = TL::NW;
@@ -853,14 +853,29 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q4 = lane >> 4, l16 = lane & 15;
-  int rt, tt;
-  tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
+  // n_whole < 0: blockIdx.x is the tile, blockIdx.y the split of the reduction.  n_whole >= 0
+  // (tail split): the first n_whole workgroups run whole tiles and store bf16; each remaining
+  // tile is split in two (workgroups n_whole + 2i + z) into fp32 partials.
+  int rt, tt, z = blockIdx.y;
+  float* part_w = part;  // where this workgroup's partial goes (nullptr: the output itself)
+  bool whole = false;
+  if (n_whole < 0) {
+    tile_coords(xcd_remap(blockIdx.x, n_rt * n_tt), n_rt, n_tt, rt, tt);
+  } else if ((int)blockIdx.x < n_whole) {
+    tile_coords(xcd_remap(blockIdx.x, n_whole), n_rt, n_tt, rt, tt);
+    z = 0;
+    part_w = nullptr;
+    whole = true;
+  } else {
+    const int k = (int)blockIdx.x - n_whole;
+    tile_coords(n_whole + (k >> 1), n_rt, n_tt, rt, tt);
+    z = k & 1;
+  }
   const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT;
   const int64_t cv = C / 2, cm = C / 32;
   const int nC_all = (int)(C / BC);
-  const int z = blockIdx.y;
   const int c_beg = z * stages_per_split;
-  const int c_end = min(nC_all, c_beg + stages_per_split);
+  const int c_end = whole ? nC_all : min(nC_all, c_beg + stages_per_split);
 
   // operands through buffer resources based at the tile (fixed lane offsets, the stage offset in
   // an SGPR; rows past R, T or r read as zeros), as in k_spmm24_pipe
@@ -1313,7 +1328,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   using OP = OutStage<BR, true>;
   constexpr bool stage_bf16 = OB::template bytes<BT>() <= TL::LDS;
   constexpr bool stage_f32 = OP::template bytes<BT>() <= TL::LDS;
-  if ((part && stage_f32) || (!part && stage_bf16)) {
+  if ((part_w && stage_f32) || (!part_w && stage_bf16)) {
     __syncthreads();  // every wave is done with the operand ring
 #pragma unroll
     for (int i = 0; i < FR; ++i)
@@ -1321,11 +1336,11 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
       for (int j = 0; j < FT; ++j) {
         const int tok = wt * 16 * FT + j * 16 + l16, row = wr * 16 * FR + i * 16 + 4 * q4;
         const f32x4& c = acc[i][j];
-        if (part) OP::put(smem, tok, row, c[0], c[1], c[2], c[3]);
+        if (part_w) OP::put(smem, tok, row, c[0], c[1], c[2], c[3]);
         else OB::put(smem, tok, row, c[0], c[1], c[2], c[3]);
       }
     __syncthreads();
-    if (part) OP::template flush<BT>(smem, part + (int64_t)z * T * R, row0, t0, R, T);
+    if (part_w) OP::template flush<BT>(smem, part_w + (int64_t)z * T * R, row0, t0, R, T);
     else OB::template flush<BT>(smem, out, row0, t0, R, T);
     return;
   }
@@ -1337,8 +1352,8 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
       const int64_t t = t0 + wt * 16 * FT + j * 16 + l16;
       if (t >= T) continue;
       const int64_t rb = row0 + wr * 16 * FR + i * 16 + 4 * q4;
-      if (part) {
-        float* o = part + ((int64_t)z * T + t) * R + rb;
+      if (part_w) {
+        float* o = part_w + ((int64_t)z * T + t) * R + rb;
         if (r4 && rb + 3 < R) {
           *reinterpret_cast<f32x4*>(o) = acc[i][j];
         } else {
@@ -1627,6 +1642,31 @@ __global__ __launch_bounds__(256, 1) void k_spmm24_w(
 }
 
 // Fixed-order sum of the S fp32 partials, rounded once to bf16.
+// The two fp32 partials of each tail-split tile (tiles n_whole .. of a BR x BT tiling, in the
+// SpMM's tile order) summed in split order and stored as bf16: one workgroup per tile.
+__global__ void k_tail_reduce(const float* __restrict__ part, int64_t T, int64_t R, int n_whole,
+                              int n_rt, int n_tt, int BR, int BT, uint16_t* __restrict__ out) {
+  int rt, tt;
+  tile_coords(n_whole + (int)blockIdx.x, n_rt, n_tt, rt, tt);
+  const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT, n = T * R;
+  const bool vec = (R & 3) == 0;
+  for (int v = threadIdx.x; v < BT * (BR / 4); v += blockDim.x) {
+    const int tok = v / (BR / 4), c = v - tok * (BR / 4);
+    const int64_t t = t0 + tok, row = row0 + 4 * c;
+    if (t >= T || row >= R) continue;
+    const int64_t i = t * R + row;
+    if (vec && row + 4 <= R) {
+      const f32x4 s = *reinterpret_cast<const f32x4*>(part + i) + *reinterpret_cast<const f32x4*>(part + n + i);
+      u32x2 o;
+      o[0] = pack_bf16x2(s[0], s[1]);
+      o[1] = pack_bf16x2(s[2], s[3]);
+      *reinterpret_cast<u32x2*>(out + i) = o;
+    } else {
+      for (int e = 0; e < 4 && row + e < R; ++e) out[i + e] = f32_to_bf16(part[i + e] + part[n + i + e]);
+    }
+  }
+}
+
 __global__ void k_splitk_reduce(const float* __restrict__ part, int S, int64_t n,
                                 uint16_t* __restrict__ out) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -1700,6 +1740,7 @@ struct Plan {
   Cfg cfg;
   int splits;
   int stages_per_split;
+  bool tail = false;  // splits == 2 for the tiles past the last whole wave of 256 only
 };
 
 Plan plan_for(int64_t R, int64_t C, int64_t T) {
@@ -1715,6 +1756,7 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
     p.cfg = c;
     const char* comma = strchr(env, ',');
     p.splits = comma ? atoi(comma + 1) : 1;
+    p.tail = comma && strchr(comma, 't') != nullptr;  // "61,2t": split only the last wave's tiles
   } else {
     // Measured on MI355X (2:4, bf16): once 256x256 tiles fill the GPU twice, eight-wave 256x256
     // tiles with three stages and 4-stage metadata super-stages (C % 128 == 0; else per-stage
@@ -1727,12 +1769,14 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
       p.cfg = cfg_by_id(30);  // few tokens: bound by reading the weight once
     } else if (pipe_ok && tiles(256, 256) >= 512) {
       p.cfg = cfg_by_id(wide_ok ? 61 : C >= 2 * R ? 50 : 51);
-      // long reductions whose tiles leave the last wave of 256 workgroups mostly empty: two
-      // splits of the reduction fill it (each split 8-stage aligned; the fp32 partials and their
-      // sum cost about a tenth of what the fuller waves save)
+      // long reductions whose tiles leave the last wave of 256 workgroups at most half full: the
+      // tiles of that wave are split in two over the reduction (8-stage aligned), which fills it
+      // with half-length workgroups; the others run whole
       const int64_t t = tiles(256, 256);
-      auto fill = [](int64_t n) { return (double)n / (256.0 * (double)((n + 255) / 256)); };
-      if (wide_ok && C >= 2 * R && C % 1024 == 0 && fill(2 * t) - fill(t) >= 0.1) p.splits = 2;
+      if (wide_ok && C >= 2 * R && C % 1024 == 0 && t % 256 != 0 && t % 256 <= 128) {
+        p.splits = 2;
+        p.tail = true;
+      }
     } else if (pipe_ok && tiles(256, 128) >= 240) {
       p.cfg = cfg_by_id(wide_ok ? 55 : 50);
     } else if (pipe_ok && tiles(128, 64) >= 240 && C >= 2048) {
@@ -1753,6 +1797,7 @@ Plan plan_for(int64_t R, int64_t C, int64_t T) {
   // super-stage boundary (the 256x256 tile's 4-stage super-stages, 8-stage splits).
   const bool super_split = p.cfg.id == 61 && p.splits > 1 && nC % (8 * p.splits) == 0;
   if (p.splits < 1 || p.cfg.id == 30 || (p.cfg.super && !super_split)) p.splits = 1;
+  if (p.splits != 2 || p.cfg.id != 61) p.tail = false;  // the 256x256 tiling of finish_split
   if (p.splits > nC) p.splits = nC;
   p.stages_per_split = (nC + p.splits - 1) / p.splits;
   p.splits = (nC + p.stages_per_split - 1) / p.stages_per_split;
@@ -1766,9 +1811,10 @@ void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t
               const Plan& p, hipStream_t s, int which = SRA_KERNEL_SPMM24) {
   using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
-  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN, TLAY, PP>,
-              dim3((unsigned)(n_rt * n_tt), (unsigned)p.splits), dim3(64 * TL::NW), 0, s, s_vals, s_meta, R,
-              C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split);
+  const int n = n_rt * n_tt, n_whole = p.tail ? n - n % 256 : -1;
+  const dim3 grid = p.tail ? dim3((unsigned)(n_whole + 2 * (n - n_whole))) : dim3((unsigned)n, (unsigned)p.splits);
+  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN, TLAY, PP>, grid, dim3(64 * TL::NW), 0, s,
+              s_vals, s_meta, R, C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split, n_whole);
 }
 
 template <int FR, int FT, int WR, int WT>
@@ -1809,6 +1855,21 @@ void launch_pipe(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int6
 // each stage (the 256x128 eight-wave tile drops to 3 stages for it; the 256x256 one would spill).
 // SRA_SPMM24_FUSE=0 turns it off.
 constexpr int kFuseRank = 16;
+// Sum of a split product's fp32 partials into bf16 out: every element (k_splitk_reduce), or only
+// the tail-split tiles of the 256x256 tiling (k_tail_reduce; the rest was stored whole).
+void finish_split(const Plan& p, const float* part, int64_t R, int64_t T, uint16_t* out, hipStream_t s) {
+  if (p.tail) {
+    const int n_rt = (int)((R + 255) / 256), n_tt = (int)((T + 255) / 256), n = n_rt * n_tt;
+    const int n_whole = n - n % 256;
+    hipLaunchKernelGGL(k_tail_reduce, dim3((unsigned)(n - n_whole)), dim3(256), 0, s, part, T, R, n_whole,
+                       n_rt, n_tt, 256, 256, out);
+    return;
+  }
+  const int64_t n = T * R;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, s,
+                     part, p.splits, n, out);
+}
+
 // The adapter epilogue reads E through a buffer resource: rows contiguous in j, and R rows of
 // e_row_stride elements addressable with 32-bit byte offsets.
 bool epilogue_ok(const sra::Epilogue& ep, int64_t R) {
@@ -1866,6 +1927,7 @@ hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_me
   // only the 256x256 tile splits (8-stage aligned, the plan's own split); others run whole
   if (!(id == 61 && p.splits > 1 && !fuse && ws)) {
     p.splits = 1;
+    p.tail = false;
     p.stages_per_split = (int)((C + 63) / 64);
   }
   float* part = p.splits > 1 ? (float*)ws : nullptr;
@@ -1883,11 +1945,7 @@ hipError_t launch_spmm24_tiled_bf16(const uint16_t* s_vals, const uint32_t* s_me
   } else {
     launch_q<2, 2, 4, 2, 4, 8, 0, false, true>(s_vals, s_meta, R, C, act, T, ep, out, nullptr, p, s);
   }
-  if (part) {
-    const int64_t n = T * R;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, s,
-                       part, p.splits, n, out);
-  }
+  if (part) finish_split(p, part, R, T, out, s);
   return hipGetLastError();
 }
 
@@ -1941,11 +1999,7 @@ hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, in
     case 5: launch_cfg<1, 2, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
     default: launch_cfg<2, 2, 2, 2>(s_vals, s_meta, R, C, act, T, ep, out, part, p, s); break;
   }
-  if (p.splits > 1) {
-    const int64_t n = T * R;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, s,
-                       part, p.splits, n, out);
-  }
+  if (p.splits > 1) finish_split(p, part, R, T, out, s);
   return hipGetLastError();
 }
 

@@ -52,15 +52,17 @@ def test_config(problem, cfg, splits):
         assert np.array_equal(bits(Y), bits(problem["Y0"]))
 
 
-def test_super_stage_split(gpu, monkeypatch):
+@pytest.mark.parametrize("mode", ["61,2", "61,2t"])
+def test_super_stage_split(gpu, monkeypatch, mode):
     """The 256x256 tile with 4-stage metadata super-stages split over the reduction (two splits of
-    8 stages each, fp32 partials summed in a fixed order) on a ragged problem: within tolerance of
-    the oracle, and the same bits on a second call."""
+    8 stages each, fp32 partials summed in a fixed order; "t": only the tiles past the last whole
+    wave of 256 split, here all six) on a ragged problem: within tolerance of the oracle, and the
+    same bits on a second call."""
     wl = Workload("split", T=300, K=1024, N=544, r=24, dtype="bf16", fmt="nm")
     inp = layer_inputs(wl, seed=22)
     X, W, A, B = (inp[k].cuda() for k in ("X", "W", "A", "B"))
     S = sra.compress(W)
-    monkeypatch.setenv("SRA_SPMM24_CFG", "61,2")
+    monkeypatch.setenv("SRA_SPMM24_CFG", mode)
     Y, _ = sra.sparse_lora_fwd(S, X, A, B)
     Y2, _ = sra.sparse_lora_fwd(S, X, A, B)
     torch.cuda.synchronize()
