@@ -1643,15 +1643,17 @@ __global__ __launch_bounds__(256, 1) void k_spmm24_w(
 
 // Fixed-order sum of the S fp32 partials, rounded once to bf16.
 // The two fp32 partials of each tail-split tile (tiles n_whole .. of a BR x BT tiling, in the
-// SpMM's tile order) summed in split order and stored as bf16: one workgroup per tile.
+// SpMM's tile order) summed in split order and stored as bf16: gridDim.y workgroups per tile,
+// each over its share of the tile's tokens.
 __global__ void k_tail_reduce(const float* __restrict__ part, int64_t T, int64_t R, int n_whole,
                               int n_rt, int n_tt, int BR, int BT, uint16_t* __restrict__ out) {
   int rt, tt;
   tile_coords(n_whole + (int)blockIdx.x, n_rt, n_tt, rt, tt);
   const int64_t row0 = (int64_t)rt * BR, t0 = (int64_t)tt * BT, n = T * R;
   const bool vec = (R & 3) == 0;
-  for (int v = threadIdx.x; v < BT * (BR / 4); v += blockDim.x) {
-    const int tok = v / (BR / 4), c = v - tok * (BR / 4);
+  const int tpw = BT / (int)gridDim.y;  // tokens per workgroup
+  for (int v = threadIdx.x; v < tpw * (BR / 4); v += blockDim.x) {
+    const int tok = (int)blockIdx.y * tpw + v / (BR / 4), c = v % (BR / 4);
     const int64_t t = t0 + tok, row = row0 + 4 * c;
     if (t >= T || row >= R) continue;
     const int64_t i = t * R + row;
@@ -1861,8 +1863,8 @@ void finish_split(const Plan& p, const float* part, int64_t R, int64_t T, uint16
   if (p.tail) {
     const int n_rt = (int)((R + 255) / 256), n_tt = (int)((T + 255) / 256), n = n_rt * n_tt;
     const int n_whole = n - n % 256;
-    hipLaunchKernelGGL(k_tail_reduce, dim3((unsigned)(n - n_whole)), dim3(256), 0, s, part, T, R, n_whole,
-                       n_rt, n_tt, 256, 256, out);
+    hipLaunchKernelGGL(k_tail_reduce, dim3((unsigned)(n - n_whole), 8), dim3(256), 0, s, part, T, R,
+                       n_whole, n_rt, n_tt, 256, 256, out);
     return;
   }
   const int64_t n = T * R;
