@@ -184,15 +184,16 @@ def test_split_reduction_both_layouts(gpu, monkeypatch):
     run_nm(wl, seed=31, streaming=False)
 
 
-@pytest.mark.parametrize("streaming", [False, True])
-def test_tail_split(gpu, monkeypatch, streaming):
+@pytest.mark.parametrize("T,N,streaming", [(10240, 2048, False), (10240, 2048, True), (10000, 2016, False)])
+def test_tail_split(gpu, monkeypatch, T, N, streaming):
     """Tail split: of the forward's 320 tiles of 256 x 256 the first 256 run whole (bf16 stores)
     and the last 64 (tokens 8192 on) split over the reduction into fp32 partials that a second
-    kernel sums; the backward's 160 tiles are all tail.  Sampled token rows on both sides of the
+    kernel sums; the backward's tiles are all tail where it splits.  The ragged case ends in
+    partial row and token tiles inside the tail.  Sampled token rows on both sides of the
     boundary, every output column."""
     monkeypatch.setenv("SRA_SPMM24_CFG", "61,2t")
-    wl = Workload("tail", T=10240, K=1024, N=2048, r=8, dtype="bf16", fmt="nm")
-    rows = np.array([0, 1, 255, 4097, 8191, 8192, 8500, 9999, 10239])
+    wl = Workload("tail", T=T, K=1024, N=N, r=8, dtype="bf16", fmt="nm")
+    rows = np.array([0, 1, 255, 4097, 8191, 8192, 8500, 9983, T - 1])
     run_nm(wl, seed=41, rows=rows, streaming=streaming)
 
 
