@@ -321,6 +321,17 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * 128, r0 = (int64_t)blockIdx.y * 128;
   {
+    // the W tile into LDS with coalesced 16-byte loads (a wave reads four 256-byte row runs);
+    // positions past the matrix hold the pruned mark
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int v = tid + 256 * k, lr = v >> 4, ch = v & 15;
+      const int64_t row = r0 + lr, col = c0 + 8 * ch;
+      u32x4 x = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+      if (row < rows && col < cols) x = *reinterpret_cast<const u32x4*>(W + row * cols + col);
+      *reinterpret_cast<u32x4*>(&tile[lr * LD + 8 * ch]) = x;
+    }
+    __syncthreads();
     // first prune: lane = (row, 64-column half), two 32-column blocks
     const int lr = tid >> 1, h = tid & 1;
     const int64_t row = r0 + lr;
@@ -330,9 +341,8 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
       const int64_t cb = c0 + lc;
       union { u32x4 v[4]; uint32_t w[16]; } x;
       if (row < rows && cb < cols) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(W + row * cols + cb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x.v[i] = src[i];
+        for (int i = 0; i < 4; ++i) x.v[i] = *reinterpret_cast<const u32x4*>(&tile[lr * LD + lc + 8 * i]);
         union { u32x4 v[2]; uint32_t w[8]; } o;
         uint32_t word = 0;
 #pragma unroll
@@ -356,12 +366,9 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
           dst[1] = o.v[1];
           meta[row * (cols / 32) + cb / 32] = word;
         }
-      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x.v[i] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&tile[lr * LD + lc + 8 * i]) = x.v[i];
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&tile[lr * LD + lc + 8 * i]) = x.v[i];
     }
   }
   __syncthreads();
