@@ -802,7 +802,8 @@ __global__ __launch_bounds__(256, (PTile<FR, FT, WR, WT, NS, UG>::OCC)) void k_s
 // MS > 0: metadata is not part of a stage but fetched in super-stages of MS stages (8 B per row per
 // stage, so MS = 8 gives 64-byte runs instead of 8-byte ones, which LDS-DMA moves ~7x faster per
 // byte; MS = 4 gives 32-byte runs in half the LDS) into a double buffer of its own, one
-// super-stage ahead; needs C % 128 == 0 and no split.
+// super-stage ahead; needs C % 128 == 0, and a split of the reduction must start on an 8-stage
+// boundary (the planner splits only the 256x256 tile, so).
 // UG > 0: adapter rows in the activation region as in PTile (GT transfers over NW waves).
 // DN: the weight is dense (rows of C bf16, 128 bytes per row and stage, no metadata) and the
 // products are pairs of dense v_mfma_f32_16x16x32_bf16 -- the fixed fan-in layer's densified
