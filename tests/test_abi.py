@@ -265,3 +265,21 @@ def test_binding_fails_loudly_when_library_missing(tmp_path):
             _abi.load(str(tmp_path / "libsra.so"))
     finally:
         _abi._lib = saved
+
+
+def test_long_reduction_tail_split_workspace(lib):
+    """The planner splits the reduction of long-C products whose 256 x 256 tiles leave the last
+    wave of 256 workgroups at most half full (OPT-13B fc2 forward: 640 tiles), on both layouts, so
+    their workspace holds two fp32 partial arrays; the short-C product (fc1 forward, 2560 tiles)
+    needs none.  Rank 0, so only the product's share of the workspace counts."""
+    n = ctypes.c_size_t()
+    T, partials = 8192, 2 * 8192 * 5120 * 4
+    for fmt in (SRA_FMT_NM, SRA_FMT_NM_TILED):
+        fc2 = nm_desc(rows=5120, cols=20480)
+        fc2.format = fmt
+        assert lib.sra_fwd_workspace(ctypes.byref(fc2), T, 0, ctypes.byref(n)) == SRA_OK
+        assert n.value >= partials
+        fc1 = nm_desc(rows=20480, cols=5120)
+        fc1.format = fmt
+        assert lib.sra_fwd_workspace(ctypes.byref(fc1), T, 0, ctypes.byref(n)) == SRA_OK
+        assert n.value < partials
