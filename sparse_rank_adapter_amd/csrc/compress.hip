@@ -308,8 +308,10 @@ SRA_DEV void second_prune_tile(const uint16_t* tile, int64_t c0, int64_t r0, int
   }
 }
 
-// TL: both outputs in the streaming layout (rows and cols multiples of 128).
-template <bool TL>
+// TL: both outputs in the streaming layout (rows and cols multiples of 128).  ST: the W tile first
+// crosses into LDS with coalesced row-run loads (faster for large W; for small W the extra pass
+// adds latency, so lanes load their blocks directly).
+template <bool TL, bool ST>
 __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __restrict__ W,
                                                           int64_t rows, int64_t cols,
                                                           uint16_t* __restrict__ vals,
@@ -323,15 +325,17 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
   {
     // the W tile into LDS with coalesced 16-byte loads (a wave reads four 256-byte row runs);
     // positions past the matrix hold the pruned mark
+    if constexpr (ST) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int v = tid + 256 * k, lr = v >> 4, ch = v & 15;
-      const int64_t row = r0 + lr, col = c0 + 8 * ch;
-      u32x4 x = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-      if (row < rows && col < cols) x = *reinterpret_cast<const u32x4*>(W + row * cols + col);
-      *reinterpret_cast<u32x4*>(&tile[lr * LD + 8 * ch]) = x;
+      for (int k = 0; k < 8; ++k) {
+        const int v = tid + 256 * k, lr = v >> 4, ch = v & 15;
+        const int64_t row = r0 + lr, col = c0 + 8 * ch;
+        u32x4 x = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+        if (row < rows && col < cols) x = *reinterpret_cast<const u32x4*>(W + row * cols + col);
+        *reinterpret_cast<u32x4*>(&tile[lr * LD + 8 * ch]) = x;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // first prune: lane = (row, 64-column half), two 32-column blocks
     const int lr = tid >> 1, h = tid & 1;
     const int64_t row = r0 + lr;
@@ -341,8 +345,14 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
       const int64_t cb = c0 + lc;
       union { u32x4 v[4]; uint32_t w[16]; } x;
       if (row < rows && cb < cols) {
+        if constexpr (ST) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x.v[i] = *reinterpret_cast<const u32x4*>(&tile[lr * LD + lc + 8 * i]);
+          for (int i = 0; i < 4; ++i) x.v[i] = *reinterpret_cast<const u32x4*>(&tile[lr * LD + lc + 8 * i]);
+        } else {
+          const u32x4* src = reinterpret_cast<const u32x4*>(W + row * cols + cb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x.v[i] = src[i];
+        }
         union { u32x4 v[2]; uint32_t w[8]; } o;
         uint32_t word = 0;
 #pragma unroll
@@ -368,6 +378,11 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&tile[lr * LD + lc + 8 * i]) = x.v[i];
+      } else if constexpr (!ST) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x4*>(&tile[lr * LD + lc + 8 * i]) =
+              u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
       }
     }
   }
@@ -520,13 +535,21 @@ __global__ void k_meta_or(const uint32_t* __restrict__ in, uint32_t* __restrict_
 
 namespace sra {
 
+// W elements from which the pair kernel stages its tile through LDS first (OPT-13B-sized weights,
+// 105M elements, gain; OPT-350M-sized ones, 4M, do not)
+constexpr int64_t kPairStageElems = (int64_t)1 << 25;
+
 hipError_t launch_compress_pair24(int dtype, const void* W, int64_t rows, int64_t cols, void* vals,
                                   uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (dtype == SRA_BF16) {
     const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
-    launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<false>, grid, dim3(256), 0, s, (const uint16_t*)W, rows,
-           cols, (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
+    if (rows * cols >= kPairStageElems)
+      launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<false, true>, grid, dim3(256), 0, s, (const uint16_t*)W,
+             rows, cols, (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
+    else
+      launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<false, false>, grid, dim3(256), 0, s, (const uint16_t*)W,
+             rows, cols, (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
@@ -550,8 +573,12 @@ hipError_t launch_compress_pair24_tiled(const uint16_t* W, int64_t rows, int64_t
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
-  launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<true>, grid, dim3(256), 0, s, W, rows, cols,
-         (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
+  if (rows * cols < kPairStageElems)
+    launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<true, false>, grid, dim3(256), 0, s, W, rows, cols,
+           (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
+  else
+    launch(SRA_KERNEL_COMPRESS, k_compress_pair24t<true, true>, grid, dim3(256), 0, s, W, rows, cols,
+           (uint16_t*)vals, meta, (uint16_t*)p_vals, p_meta);
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ import torch
 import sparse_rank_adapter_amd as sra
 from oracle import ffi as offi
 from oracle import nm as onm
-from sra_inputs import WORKLOADS, layer_inputs
+from sra_inputs import WORKLOADS, Workload, layer_inputs
 from tests._util import bits, f64, meta_u32, np_bits, tie_heavy
 
 pytestmark = pytest.mark.gpu
@@ -91,6 +91,30 @@ def test_compress_pair_opt350m_fc1(gpu):
         assert np.array_equal(bits(a), bits(b))
     for a, b in ((S2.meta, S.meta), (P2.meta, P.meta)):
         assert np.array_equal(meta_u32(a), meta_u32(b))
+
+
+@pytest.mark.parametrize("shape", [(8192, 4096), (4224, 8000)])
+def test_compress_pair_large_matches_two_kernels(gpu, shape):
+    """At 2^25 elements and above the pair kernel stages each W tile through LDS before pruning
+    (a ragged shape included): both outputs bit-identical to compress then double_prune, on the
+    canonical arrays and, for the 128-aligned shape, in the streaming layout."""
+    wl = Workload("pair_large", T=1, K=shape[1], N=shape[0], r=0, dtype="bf16", fmt="nm")
+    W = layer_inputs(wl, seed=shape[0] + shape[1], with_dy=False)["W"].cuda()
+    S = sra.compress(W)
+    P = sra.double_prune(S)
+    S2, P2 = sra.compress_pair(W)
+    torch.cuda.synchronize()
+    for a, b in ((S2.values, S.values), (P2.values, P.values)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for a, b in ((S2.meta, S.meta), (P2.meta, P.meta)):
+        assert torch.equal(a, b)
+    if shape[0] % 128 == 0 and shape[1] % 128 == 0:
+        St, Pt = sra.compress_pair_tiled(W)
+        Se, Pe = sra.nm_tile(S), sra.nm_tile(P)
+        torch.cuda.synchronize()
+        for a, b in ((St, Se), (Pt, Pe)):
+            assert torch.equal(a.values.view(torch.int16), b.values.view(torch.int16))
+            assert torch.equal(a.meta, b.meta)
 
 
 def test_double_prune_tiny_f32(gpu):
