@@ -20,7 +20,7 @@ _DT = {torch.bfloat16: SRA_BF16, torch.float32: SRA_F32}
 
 def _dt(t: torch.Tensor) -> int:
     if t.dtype not in _DT:
-        raise TypeError(f"dtype {t.dtype} is not bfloat16 or float32")
+        raise ValueError(f"dtype {t.dtype} is not bfloat16 or float32")
     return _DT[t.dtype]
 
 
@@ -28,12 +28,60 @@ def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t: torch.Tensor):
+def _dev(t: torch.Tensor, name: str = "tensor", device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
-        raise ValueError("tensors must live on the GPU")
+        raise ValueError(f"{name} must live on the GPU")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
-        raise ValueError("tensors must be contiguous")
+        raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _arg(t, name: str, shape: tuple, dtype: torch.dtype, device=None, min_numel: bool = False):
+    """Check one tensor argument before anything reaches the library: shape (or, with
+    ``min_numel``, at least that many elements), dtype, device and contiguity.  Shape and dtype
+    are checked first so that a wrong call is reported the same way with or without a GPU."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if min_numel:
+        need = 1
+        for d in shape:
+            need *= int(d)
+        if t.numel() < need:
+            raise ValueError(f"{name} holds {t.numel()} elements, needs at least {need}")
+    elif tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return _dev(t, name, device)
+
+
+def _check_sparse(S: "SparseMatrix", name: str):
+    """Buffers of a compressed matrix: dtype, device, contiguity and sizes for its format."""
+    if S.dtype not in _DT:
+        raise ValueError(f"{name}: dtype {S.dtype} is not bfloat16 or float32")
+    dev = S.values.device if S.values is not None else None
+    if S.fmt == SRA_FMT_NM:
+        _arg(S.values, f"{name}.values", (S.rows, S.cols // S.m * S.n), S.dtype, dev)
+        _arg(S.meta, f"{name}.meta", (S.rows, meta_words(S.cols, S.n, S.m)), torch.int32, dev,
+             min_numel=True)
+    elif S.fmt == SRA_FMT_NM_TILED:
+        vb, mb = tile_bytes(S.rows, S.cols, S.n, S.m)
+        _arg(S.values, f"{name}.values", (vb // S.values.element_size(),), S.dtype, dev, min_numel=True)
+        _arg(S.meta, f"{name}.meta", (mb // 4,), torch.int32, dev, min_numel=True)
+    elif S.fmt == SRA_FMT_ELL:
+        _arg(S.values, f"{name}.values", (S.rows, S.k), S.dtype, dev)
+        _arg(S.index, f"{name}.index", (S.rows, S.k), torch.int16, dev)
+    elif S.fmt == SRA_FMT_CSR:
+        _arg(S.values, f"{name}.values", (S.nnz,), S.dtype, dev, min_numel=True)
+        _arg(S.index, f"{name}.index", (S.nnz,), torch.int16, dev, min_numel=True)
+        _arg(S.row_ptr, f"{name}.row_ptr", (S.rows + 1,), torch.int32, dev)
+    else:
+        raise ValueError(f"{name}: unknown format {S.fmt}")
+    return dev
 
 
 def _stream(dev) -> ctypes.c_void_p:
@@ -75,15 +123,46 @@ def meta_words(cols: int, n: int = 2, m: int = 4) -> int:
     return int(load().sra_nm_meta_words(cols, n, m))
 
 
+def _mat(W, name: str):
+    """A dense 2-D input matrix (bf16 or fp32, on the GPU, contiguous); returns its shape."""
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    _dt(W)
+    _dev(W, name)
+    return tuple(int(x) for x in W.shape)
+
+
+def _check_out_nm(S: "SparseMatrix", name: str, like: torch.Tensor, rows: int, cols: int, n: int, m: int):
+    """An output descriptor in the canonical N:M format of a rows x cols matrix."""
+    if S.fmt != SRA_FMT_NM or S.rows != rows or S.cols != cols or (S.n, S.m) != (n, m):
+        raise ValueError(f"{name} must describe a canonical {n}:{m} matrix of {rows} x {cols}")
+    if S.dtype != like.dtype:
+        raise ValueError(f"{name} has dtype {S.dtype}, expected {like.dtype}")
+    _check_sparse(S, name)
+    if S.values.device != like.device:
+        raise ValueError(f"{name} is on {S.values.device}, expected {like.device}")
+
+
+def _check_out_tiled(S: "SparseMatrix", name: str, like: torch.Tensor, rows: int, cols: int, n: int, m: int):
+    """An output descriptor in the streaming layout of a rows x cols matrix."""
+    if S.fmt != SRA_FMT_NM_TILED or S.rows != rows or S.cols != cols or (S.n, S.m) != (n, m):
+        raise ValueError(f"{name} must describe a streaming-layout {n}:{m} matrix of {rows} x {cols}")
+    if S.dtype != like.dtype:
+        raise ValueError(f"{name} has dtype {S.dtype}, expected {like.dtype}")
+    _check_sparse(S, name)
+    if S.values.device != like.device:
+        raise ValueError(f"{name} is on {S.values.device}, expected {like.device}")
+
+
 def compress(W: torch.Tensor, n: int = 2, m: int = 4, out: SparseMatrix | None = None) -> SparseMatrix:
     """compress(W, N, M): first N:M prune along W's columns (into `out`'s buffers if given)."""
     lib = load()
-    _dev(W)
-    rows, cols = W.shape
+    rows, cols = _mat(W, "W")
     if out is None:
         vals = torch.empty((rows, cols // m * n), dtype=W.dtype, device=W.device)
         meta = torch.empty((rows, meta_words(cols, n, m)), dtype=torch.int32, device=W.device)
         out = SparseMatrix(SRA_FMT_NM, W.dtype, rows, cols, vals, meta=meta, n=n, m=m)
+    _check_out_nm(out, "out", W, rows, cols, n, m)
     d = out.desc()
     check("sra_compress", lib.sra_compress(_p(W), _dt(W), rows, cols, n, m, ctypes.byref(d), _stream(W.device)))
     return out
@@ -92,11 +171,13 @@ def compress(W: torch.Tensor, n: int = 2, m: int = 4, out: SparseMatrix | None =
 def double_prune(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMatrix:
     """P = prune_NM(Ws^T): rows = Ws.cols, cols = Ws.rows (into `out`'s buffers if given)."""
     lib = load()
+    _check_sparse(Ws, "Ws")
     P = out
     if P is None:
         vals = torch.empty((Ws.cols, Ws.rows // Ws.m * Ws.n), dtype=Ws.dtype, device=Ws.device)
         meta = torch.empty((Ws.cols, meta_words(Ws.rows, Ws.n, Ws.m)), dtype=torch.int32, device=Ws.device)
         P = SparseMatrix(SRA_FMT_NM, Ws.dtype, Ws.cols, Ws.rows, vals, meta=meta, n=Ws.n, m=Ws.m)
+    _check_out_nm(P, "out", Ws.values, Ws.cols, Ws.rows, Ws.n, Ws.m)
     dw, dp = Ws.desc(), P.desc()
     check("sra_double_prune", lib.sra_double_prune(ctypes.byref(dw), ctypes.byref(dp), _stream(Ws.device)))
     return P
@@ -105,8 +186,7 @@ def double_prune(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMat
 def compress_pair(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | None = None):
     """(compress(W), double_prune(compress(W))) in one pass over W; `out` = (Ws, P) reuses buffers."""
     lib = load()
-    _dev(W)
-    rows, cols = W.shape
+    rows, cols = _mat(W, "W")
     if out is None:
         Ws = SparseMatrix(SRA_FMT_NM, W.dtype, rows, cols,
                           torch.empty((rows, cols // m * n), dtype=W.dtype, device=W.device),
@@ -118,6 +198,8 @@ def compress_pair(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | None = N
                          n=n, m=m)
     else:
         Ws, P = out
+    _check_out_nm(Ws, "out[0]", W, rows, cols, n, m)
+    _check_out_nm(P, "out[1]", W, cols, rows, n, m)
     dw, dp = Ws.desc(), P.desc()
     check("sra_compress_pair", lib.sra_compress_pair(_p(W), _dt(W), rows, cols, n, m, ctypes.byref(dw),
                                                      ctypes.byref(dp), _stream(W.device)))
@@ -127,6 +209,7 @@ def compress_pair(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | None = N
 def nm_tile(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMatrix:
     """The 2:4 weight Ws in the streaming layout for forwards of at most 16 tokens (sra_nm_tile)."""
     lib = load()
+    _check_sparse(Ws, "Ws")
     vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
     check("sra_nm_tile_bytes", lib.sra_nm_tile_bytes(Ws.rows, Ws.cols, Ws.n, Ws.m, ctypes.byref(vb),
                                                      ctypes.byref(mb)))
@@ -134,6 +217,7 @@ def nm_tile(Ws: SparseMatrix, out: SparseMatrix | None = None) -> SparseMatrix:
         vals = torch.empty(max(1, vb.value // 2), dtype=Ws.dtype, device=Ws.device)
         meta = torch.empty(max(1, mb.value // 4), dtype=torch.int32, device=Ws.device)
         out = SparseMatrix(SRA_FMT_NM_TILED, Ws.dtype, Ws.rows, Ws.cols, vals, meta=meta, n=Ws.n, m=Ws.m)
+    _check_out_tiled(out, "out", Ws.values, Ws.rows, Ws.cols, Ws.n, Ws.m)
     dw, do = Ws.desc(), out.desc()
     check("sra_nm_tile", lib.sra_nm_tile(ctypes.byref(dw), ctypes.byref(do), _stream(Ws.device)))
     return out
@@ -149,8 +233,7 @@ def tile_bytes(rows: int, cols: int, n: int = 2, m: int = 4) -> tuple:
 def compress_pair_tiled(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | None = None):
     """compress_pair with both outputs in the streaming layout (sra_compress_pair_tiled)."""
     lib = load()
-    _dev(W)
-    rows, cols = W.shape
+    rows, cols = _mat(W, "W")
     if out is None:
         def mk(r, c):
             vb, mb = tile_bytes(r, c, n, m)
@@ -160,6 +243,8 @@ def compress_pair_tiled(W: torch.Tensor, n: int = 2, m: int = 4, out: tuple | No
         Ws, P = mk(rows, cols), mk(cols, rows)
     else:
         Ws, P = out
+    _check_out_tiled(Ws, "out[0]", W, rows, cols, n, m)
+    _check_out_tiled(P, "out[1]", W, cols, rows, n, m)
     dw, dp = Ws.desc(), P.desc()
     check("sra_compress_pair_tiled", lib.sra_compress_pair_tiled(_p(W), _dt(W), rows, cols, n, m,
                                                                  ctypes.byref(dw), ctypes.byref(dp),
@@ -174,13 +259,17 @@ def masked_weight_grad(S: SparseMatrix, row_act: torch.Tensor, col_act: torch.Te
     For the forward weight Ws: masked_weight_grad(Ws, dY, X) = (dY^T X) o mask in Ws's value order.
     """
     lib = load()
-    _dev(row_act)
-    _dev(col_act)
+    if S.fmt != SRA_FMT_NM:
+        raise ValueError("masked_weight_grad takes a canonical N:M matrix")
+    dev = _check_sparse(S, "S")
+    if not isinstance(row_act, torch.Tensor) or row_act.dim() != 2:
+        raise ValueError("row_act must be a 2-D tensor [T, S.rows]")
     T = row_act.shape[0]
-    if row_act.shape != (T, S.rows) or col_act.shape != (T, S.cols):
-        raise ValueError("row_act must be [T, S.rows] and col_act [T, S.cols]")
+    _arg(row_act, "row_act", (T, S.rows), S.dtype, dev)
+    _arg(col_act, "col_act", (T, S.cols), S.dtype, dev)
     if out is None:
         out = torch.empty((S.rows, S.cols // S.m * S.n), dtype=S.dtype, device=S.device)
+    _arg(out, "out", (S.rows, S.cols // S.m * S.n), S.dtype, dev)
     d = S.desc()
     check("sra_masked_weight_grad", lib.sra_masked_weight_grad(ctypes.byref(d), _p(row_act), _p(col_act), T,
                                                                _p(out), _stream(S.device)))
@@ -192,12 +281,12 @@ def nm_axpby(beta: float, a: torch.Tensor, gamma: float, b: torch.Tensor,
     """out = beta * a + gamma * b on value arrays sharing one N:M pattern (sra_nm_axpby);
     ``out=a`` updates in place."""
     lib = load()
-    _dev(a)
-    _dev(b)
-    if a.shape != b.shape or a.dtype != b.dtype:
-        raise ValueError("a and b must have the same shape and dtype")
+    _dt(a)
+    _arg(a, "a", tuple(a.shape), a.dtype)
+    _arg(b, "b", tuple(a.shape), a.dtype, a.device)
     if out is None:
         out = torch.empty_like(a)
+    _arg(out, "out", tuple(a.shape), a.dtype, a.device)
     check("sra_nm_axpby", lib.sra_nm_axpby(_p(a), float(beta), _p(b), float(gamma), _p(out), a.numel(),
                                            _dt(a), _stream(a.device)))
     return out
@@ -206,8 +295,7 @@ def nm_axpby(beta: float, a: torch.Tensor, gamma: float, b: torch.Tensor,
 def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:
     """compress_ffi(W, k): keep the k largest-magnitude entries of every row (ELL, int16 columns)."""
     lib = load()
-    _dev(W)
-    rows, cols = W.shape
+    rows, cols = _mat(W, "W")
     vals = torch.empty((rows, k), dtype=W.dtype, device=W.device)
     idx = torch.empty((rows, k), dtype=torch.int16, device=W.device)
     out = SparseMatrix(SRA_FMT_ELL, W.dtype, rows, cols, vals, index=idx, k=k)
@@ -219,6 +307,9 @@ def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:
 def ffi_transpose(Ws: SparseMatrix) -> SparseMatrix:
     """Exact transpose of an ELL weight as CSR (rows = Ws.cols)."""
     lib = load()
+    if Ws.fmt != SRA_FMT_ELL:
+        raise ValueError("ffi_transpose takes an ELL matrix")
+    _check_sparse(Ws, "Ws")
     nnz = Ws.rows * Ws.k
     nbytes = ctypes.c_size_t()
     check("sra_ffi_transpose_workspace", lib.sra_ffi_transpose_workspace(Ws.rows, Ws.cols, Ws.k, ctypes.byref(nbytes)))
@@ -260,19 +351,31 @@ def sparse_lora_fwd(Ws: SparseMatrix, X: torch.Tensor, A: torch.Tensor | None = 
                     U: torch.Tensor | None = None, want_u: bool = True, ws: torch.Tensor | None = None):
     """Y = X Ws^T + (X A^T) B^T.  Returns (Y, U) with U fp32 [T, r] (None when r = 0 or not wanted)."""
     lib = load()
-    _dev(X)
+    dev = _check_sparse(Ws, "Ws")
+    N, K, dt = Ws.rows, Ws.cols, Ws.dtype
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError("X must be a 2-D tensor [T, K]")
     T = X.shape[0]
+    _arg(X, "X", (T, K), dt, dev)
+    if (A is None) != (B is None):
+        raise ValueError("A and B must both be given or both be None")
     r = 0 if A is None else A.shape[0]
-    dev = X.device
+    if r:
+        _arg(A, "A", (r, K), dt, dev)
+        _arg(B, "B", (N, r), dt, dev)
     if Y is None:
-        Y = torch.empty((T, Ws.rows), dtype=X.dtype, device=dev)
+        Y = torch.empty((T, N), dtype=dt, device=dev)
+    _arg(Y, "Y", (T, N), dt, dev)
     if U is None and want_u and r > 0:
         U = torch.empty((T, r), dtype=torch.float32, device=dev)
+    if U is not None and r:
+        _arg(U, "U", (T, r), torch.float32, dev)
     d = Ws.desc()
     nbytes = ctypes.c_size_t()
     check("sra_fwd_workspace", lib.sra_fwd_workspace(ctypes.byref(d), T, r, ctypes.byref(nbytes)))
     if ws is None or ws.numel() < nbytes.value:
         ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
+    _arg(ws, "ws", (ws.numel(),), torch.uint8, dev)
     check("sra_sparse_lora_fwd", lib.sra_sparse_lora_fwd(
         ctypes.byref(d), _p(X), T, _p(A) if r else None, _p(B) if r else None, r, _p(Y),
         _p(U) if r else None, _p(ws), ws.numel(), _stream(dev)))
@@ -286,28 +389,47 @@ def sparse_lora_bwd(P: SparseMatrix, dY: torch.Tensor, X: torch.Tensor | None = 
                     out: dict | None = None):
     """Double-pruned backward.  Returns dict with dX, dA, dB (and dU when want_du)."""
     lib = load()
-    _dev(dY)
+    dev = _check_sparse(P, "P")
+    K, N, dt = P.rows, P.cols, P.dtype
+    if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
+        raise ValueError("dY must be a 2-D tensor [T, N]")
     T = dY.shape[0]
+    _arg(dY, "dY", (T, N), dt, dev)
+    if (A is None) != (B is None):
+        raise ValueError("A and B must both be given or both be None")
     r = 0 if A is None else A.shape[0]
-    dev = dY.device
-    K, N = P.rows, P.cols
+    if r:
+        _arg(A, "A", (r, K), dt, dev)
+        _arg(B, "B", (N, r), dt, dev)
+    if U is not None and r:
+        _arg(U, "U", (T, r), torch.float32, dev)
+    # X feeds dA, and U when U is not given
+    if X is not None:
+        _arg(X, "X", (T, K), dt, dev)
+    elif r and (da or (db and U is None) or dt == torch.float32):
+        raise ValueError("X is needed for dA, and for dB when U is not given")
     flags = (SRA_GRAD_DX if dx else 0) | (SRA_GRAD_DA if da else 0) | (SRA_GRAD_DB if db else 0)
     if not dx_adapter:
         flags |= SRA_DX_NO_ADAPTER
     out = dict(out or {})
     if dx and out.get("dX") is None:
-        out["dX"] = torch.empty((T, K), dtype=dY.dtype, device=dev)
+        out["dX"] = torch.empty((T, K), dtype=dt, device=dev)
     if da and r and out.get("dA") is None:
         out["dA"] = torch.empty((r, K), dtype=torch.float32, device=dev)
     if db and r and out.get("dB") is None:
         out["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev)
     if want_du and r and out.get("dU") is None:
         out["dU"] = torch.empty((T, r), dtype=torch.float32, device=dev)
+    for key, shape, odt in (("dX", (T, K), dt), ("dA", (r, K), torch.float32),
+                            ("dB", (N, r), torch.float32), ("dU", (T, r), torch.float32)):
+        if out.get(key) is not None:
+            _arg(out[key], f"out['{key}']", shape, odt, dev)
     d = P.desc()
     nbytes = ctypes.c_size_t()
     check("sra_bwd_workspace", lib.sra_bwd_workspace(ctypes.byref(d), T, r, flags, ctypes.byref(nbytes)))
     if ws is None or ws.numel() < nbytes.value:
         ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
+    _arg(ws, "ws", (ws.numel(),), torch.uint8, dev)
     check("sra_sparse_lora_bwd", lib.sra_sparse_lora_bwd(
         ctypes.byref(d), _p(dY), _p(X), T, _p(U) if r else None, _p(A) if r else None,
         _p(B) if r else None, r, flags, _p(out.get("dX")), _p(out.get("dA")), _p(out.get("dB")),
