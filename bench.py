@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the structured-sparse plus low-rank linear layer on one MI355X.
 
-A step is one pass of the hot path over one batch of seeded synthetic input, on the OPT-350M fc1
-shape by default (X 2048 x 1024, W 4096 x 1024 pruned 2:4, rank-16 adapter, bf16 / fp32 accum):
+A step is one pass of the hot path over one batch of seeded synthetic input.  By default it is
+the OPT-13B-shaped MLP training step (hidden 5120, FFN 20480, T = 8192 tokens, both layers 2:4
+bf16 with fp32 accumulation, rank-128 adapters), both layers chained:
 
-    compress(W) + double_prune (one pass, sra_compress_pair) -> forward (U, Y)
-        -> backward (dU, dX, dB, dA)
+    per layer: compress(W) + double_prune (one pass, in the streaming layout)
+    fc1 forward (U1, Y1) -> fc2 forward on Y1 (U2, Y2)
+        -> fc2 backward on dY2 (dU2, dX2, dB2, dA2) -> fc1 backward on dX2 (dU1, dX1, dB1, dA1)
 
-Re-compressing every step mirrors SLoPe's training loop, which refreshes both compressed forms
-after each optimizer update (SLoPe paperlayer summary §2.3).  The step is captured once in a HIP
-graph and replayed.  Prints ONE JSON line with the throughput (dense-equivalent TFLOP/s), the
-speedup over the dense bf16 GEMMs of the same layer (hipBLASLt through torch, same protocol), the
-roofline of the dominant kernel (timed live with HIP events around that kernel alone) and the CPU
-oracle timed on a bounded sample as a reported baseline.
+Re-compressing every step mirrors a training loop that refreshes both compressed forms after each
+optimizer update (SLoPe paperlayer summary §2.3).  The step is captured once in a HIP graph and
+replayed.  Prints ONE JSON line with the throughput (dense-equivalent TFLOP/s), the speedup over
+the dense bf16 GEMMs of the same chain (hipBLASLt through torch, same protocol), the roofline of
+the dominant kernel (the 2:4 SpMM, timed live with HIP events around each launch alone), the
+distribution of per-replay times, the smaller workloads as extras, and the CPU oracle timed on a
+bounded sample as a reported baseline.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload opt350m_fc1]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload opt13b_mlp]
 """
 from __future__ import annotations
 
@@ -47,12 +50,18 @@ TRAFFIC_BYTES = {
 }
 
 
+# The 256x256 SMFMAC SpMM instantiation the planner picks for all four products of the OPT-13B
+# MLP step (fc1 Y, fc2 Y, fc2 dX, fc1 dX), by weight layout.
+SPMM_MLP_KERNELS = {"streaming": "k_spmm24_q<4, 8, 4, 2, 3, 4, 0, false, true, false>",
+                    "canonical": "k_spmm24_q<4, 8, 4, 2, 3, 4, 0, false, false, false>"}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="opt350m_fc1",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="opt13b_mlp",
                     choices=["opt350m_fc1", "opt13b_fc1", "opt13b_fc2", "opt13b_mlp", "ffi90_4096",
                              "opt66b_ffn_decode"])
     ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
@@ -60,22 +69,28 @@ def parse():
                     help="weight layout of the decode forward (streaming = sra_nm_tile)")
     ap.add_argument("--nm", choices=["2:4", "1:2"], default="2:4",
                     help="N:M pattern of the training step's weight (1:2 runs on the 2:4 kernels)")
-    ap.add_argument("--layout", choices=["canonical", "streaming"], default="canonical",
-                    help="weight layout of the training step (streaming = sra_compress_pair_tiled)")
+    ap.add_argument("--layout", choices=["canonical", "streaming"], default=None,
+                    help="weight layout of the training step (streaming = sra_compress_pair_tiled); "
+                         "default: streaming for opt13b_*, canonical otherwise")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle sampling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--loop", choices=["spmm_fwd", "spmm_bwd", "decode", "copy"], default=None,
+    ap.add_argument("--loop", choices=["spmm_fwd", "spmm_bwd", "decode", "copy", "read", "mlp"],
+                    default=None,
                     help="run one call of the default workload --steps times and exit (for "
-                         "rocprofv3 counter runs); 'copy' copies 256 MiB (counter calibration)")
+                         "rocprofv3 counter runs); 'copy' copies 256 MiB and 'read' sums 256 MiB "
+                         "(counter calibration); "
+                         "'mlp' runs the chained OPT-13B MLP step's calls")
     ap.add_argument("--no-ffi", action="store_true",
                     help="skip the fixed fan-in (90% sparse) layer measured beside the main line")
-    ap.add_argument("--no-mlp", action="store_true",
-                    help="skip the chained OPT-13B MLP step (streaming layout) appended to the "
-                         "default opt350m_fc1 line")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the OPT-350M fc1 step measured beside the headline MLP step")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the OPT-66B decode measurements appended to the training-step line")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.layout is None:
+        args.layout = "streaming" if args.workload.startswith("opt13b") else "canonical"
+    return args
 
 
 # ----------------------------------------------------------------------------- work / bytes model
@@ -105,8 +120,11 @@ def step_model(wl, T, with_bwd=True, with_compress=True):
 
 # ----------------------------------------------------------------------------- GPU timing helpers
 
-def time_graph(fn, steps, warmup, use_graph=True):
-    """Wall-clock ms per call of fn over `steps` calls (graph replays), sync on both sides."""
+def time_graph(fn, steps, warmup, use_graph=True, dist=None):
+    """Wall-clock ms per call of fn over `steps` calls (graph replays), sync on both sides.
+
+    With a dict as ``dist``, a second timed pass records a HIP event after every replay on the
+    current stream and fills ``dist`` with the mean, median, p10 and p90 of the per-replay times."""
     import torch
     if use_graph:
         side = torch.cuda.Stream()
@@ -129,7 +147,26 @@ def time_graph(fn, steps, warmup, use_graph=True):
     for _ in range(steps):
         run()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    if dist is not None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        dist.update(replay_stats([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    return ms
+
+
+def replay_stats(ts):
+    """mean, median, p10, p90 (ms) of a list of per-replay times."""
+    import numpy as np
+    a = np.asarray(ts, dtype=np.float64)
+    return {"n": int(a.size), "mean_ms": round(float(a.mean()), 5),
+            "median_ms": round(float(np.median(a)), 5),
+            "p10_ms": round(float(np.percentile(a, 10)), 5),
+            "p90_ms": round(float(np.percentile(a, 90)), 5)}
 
 
 def time_kernel(which, call, reps):
@@ -149,36 +186,145 @@ def time_kernel(which, call, reps):
     return sum(ts) / len(ts)
 
 
+def time_kernel_dist(which, call, reps):
+    """time_kernel, returning the per-launch times as well (mean, distribution)."""
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sra.time_next_kernel(which, e0, e1)
+        call()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in pairs]
+    return sum(ts) / len(ts), ts
+
+
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
-def cpu_baseline(wl, inp, budget_s, dense_eq_per_step):
-    """The oracle (float64, numpy) on the same step, repeated within a time budget."""
+def host_info():
+    """Host CPU facts for the CPU baseline: model, logical CPUs, the process's CPU share and the
+    threads the oracle's numpy BLAS actually runs."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the host's view
+        threads = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "blas_threads": int(threads)}
+
+
+def _oracle_layer_step(X, W, A, B, dY, K):
+    """compress + double prune + forward + backward of one layer with the oracle (float64)."""
     import numpy as np
 
     from oracle import layer as olayer
     from oracle import nm as onm
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: report the host's view
-        cores = os.cpu_count() or 1
-    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    v, m, mask1 = onm.compress(W, 2, 4)
+    _, _, _, Wdp = onm.double_prune(v, m, 2, 4, K)
+    Y, U = olayer.forward(X, np.where(mask1, W, 0.0), A, B)
+    olayer.backward(dY, X, Wdp, A, B, U)
+
+
+def cpu_baseline(wl, inp, budget_s, dense_eq_per_step, threads=None):
+    """The oracle (float64 numpy) on full steps of a single-layer workload within a time budget;
+    ``threads`` limits numpy's BLAS pool (None: as the process runs it)."""
+    import contextlib
+
+    import numpy as np
+    ctx = contextlib.nullcontext()
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(threads)
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
     X, W, A, B, dY = (f64(inp[k]) for k in ("X", "W", "A", "B", "dY"))
+    reps, t_total = 0, 0.0
+    with ctx:
+        used = host_info()["blas_threads"]
+        while t_total < budget_s or reps == 0:
+            t0 = time.perf_counter()
+            _oracle_layer_step(X, W, A, B, dY, wl.K)
+            t_total += time.perf_counter() - t0
+            reps += 1
+            if reps >= 20000:
+                break
+    return {"value": round(dense_eq_per_step * reps / t_total / 1e12, 5), "unit": "TFLOP/s",
+            "cores": int(used), "kind": "oracle",
+            "sample": f"{reps} full {wl.name} steps (compress + double_prune + fwd + bwd) in float64 "
+                      f"numpy, {t_total:.2f} s"}
+
+
+def cpu_baseline_mlp(i1, i2, budget_s, ffn_slice=1280):
+    """The oracle on a bounded sample of the chained OPT-13B MLP step: the chain restricted to the
+    FFN features [0, ffn_slice) (fc1's first output rows, fc2's first input columns; 1/16 of the
+    20480 at the default), all 8192 tokens.  Every part of the step (both weights' compress and
+    double prune, the four products and the adapter terms) is linear in the FFN width, so the
+    sample is 1/16 of the step's work; its rate is reported on its own dense-equivalent flops."""
+    import numpy as np
+
+    from oracle import layer as olayer
+    from oracle import nm as onm
+    from sra_inputs import WORKLOADS
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    X, A1, dY2, B2 = f64(i1["X"]), f64(i1["A"]), f64(i2["dY"]), f64(i2["B"])
+    W1 = f64(i1["W"][:ffn_slice])
+    B1 = f64(i1["B"][:ffn_slice])
+    W2 = f64(i2["W"][:, :ffn_slice].contiguous())
+    A2 = f64(i2["A"][:, :ffn_slice].contiguous())
+    w1, w2 = WORKLOADS["opt13b_fc1"], WORKLOADS["opt13b_fc2"]
+    T, H = X.shape
+    sub1 = type(w1)("fc1_slice", T=T, K=H, N=ffn_slice, r=w1.r, dtype="bf16", fmt="nm")
+    sub2 = type(w2)("fc2_slice", T=T, K=ffn_slice, N=H, r=w2.r, dtype="bf16", fmt="nm")
+    flops = step_model(sub1, T, with_compress=False)[0] + step_model(sub2, T, with_compress=False)[0]
     reps, t_total = 0, 0.0
     while t_total < budget_s or reps == 0:
         t0 = time.perf_counter()
-        v, m, mask1 = onm.compress(W, 2, 4)
-        _, _, _, Wdp = onm.double_prune(v, m, 2, 4, wl.K)
-        Y, U = olayer.forward(X, np.where(mask1, W, 0.0), A, B)
-        olayer.backward(dY, X, Wdp, A, B, U)
+        v1, m1, mask1 = onm.compress(W1, 2, 4)
+        _, _, _, Wdp1 = onm.double_prune(v1, m1, 2, 4, H)
+        v2, m2, mask2 = onm.compress(W2, 2, 4)
+        _, _, _, Wdp2 = onm.double_prune(v2, m2, 2, 4, ffn_slice)
+        Y1, U1 = olayer.forward(X, np.where(mask1, W1, 0.0), A1, B1)
+        _, U2 = olayer.forward(Y1, np.where(mask2, W2, 0.0), A2, B2)
+        g2 = olayer.backward(dY2, Y1, Wdp2, A2, B2, U2)
+        olayer.backward(g2["dX"], X, Wdp1, A1, B1, U1)
         t_total += time.perf_counter() - t0
         reps += 1
-        if reps >= 50:
-            break
-    return {"value": round(dense_eq_per_step * reps / t_total / 1e12, 4), "unit": "TFLOP/s",
-            "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} full {wl.name} steps (compress + double_prune + fwd + bwd) in float64 "
-                      f"numpy, {t_total:.1f} s"}
+    info = host_info()
+    return {"value": round(flops * reps / t_total / 1e12, 5), "unit": "TFLOP/s",
+            "cores": info["blas_threads"], "kind": "oracle",
+            "sample": f"{reps} x the chained opt13b_mlp step restricted to FFN features "
+                      f"[0, {ffn_slice}) of 20480 (1/{20480 // ffn_slice} of every part: both "
+                      f"weights' compress + double_prune on their slices, fc1 -> fc2 -> fc2 bwd -> "
+                      f"fc1 bwd over all {T} tokens) in float64 numpy, {t_total:.1f} s; rate on "
+                      f"the sample's own dense-equivalent flops",
+            "host": info}
+
+
+def cpu_one_thread(budget_s=4.0):
+    """1-thread oracle figures on the tiny fp32 workload and the OPT-350M fc1 step."""
+    from sra_inputs import WORKLOADS, layer_inputs
+    out = {}
+    for name, b in (("tiny_f32", 1.0), ("opt350m_fc1", budget_s)):
+        wl = WORKLOADS[name]
+        inp = layer_inputs(wl, seed=0)
+        dense_eq = step_model(wl, wl.T, with_compress=False)[0]
+        out[name] = cpu_baseline(wl, inp, b, dense_eq, threads=1)
+    return out
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -225,7 +371,8 @@ def bench_nm_layer(args, wl):
         bwd()
 
     graph = not args.no_graph
-    ms = time_graph(step, args.steps, args.warmup, graph)
+    dist = {}
+    ms = time_graph(step, args.steps, args.warmup, graph, dist=dist)
     ms_fwd = time_graph(fwd, args.steps, args.warmup, graph)
     ms_bwd = time_graph(bwd, args.steps, args.warmup, graph)
     ms_cmp = time_graph(pair, args.steps, args.warmup, graph)
@@ -297,6 +444,7 @@ def bench_nm_layer(args, wl):
                    "layout": args.layout,
                    "step": "compress + double_prune (one pass) + fwd + bwd (dX, dA, dB)",
                    "graph": graph, "seed": 0},
+        "replay_ms": dist,
         "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
         # fwd + bwd against the dense layer's two GEMMs; compress and double prune are the
         # method's one-time setup (the mask is fixed) and are timed separately
@@ -322,19 +470,22 @@ def bench_nm_layer(args, wl):
     return out, inp, dense_eq
 
 
-def bench_mlp_chain(args):
+def bench_mlp_chain(args, inputs=None):
     """OPT-13B MLP step with both layers chained: fc1 forward on X, fc2 forward on fc1's Y, fc2
     backward on dY2, fc1 backward on fc2's dX (no activation between the layers), each layer's
-    compress + double prune first; against the four dense GEMMs of the same chain."""
+    compress + double prune first; against the four dense GEMMs of the same chain.
+
+    Returns (line, (i1, i2)) with the CPU inputs of both layers for the CPU baseline."""
     import torch
 
     import sparse_rank_adapter_amd as sra
+    from sparse_rank_adapter_amd._abi import SRA_KERNEL_SPMM24
     from sra_inputs import WORKLOADS, layer_inputs
 
     dev = torch.device("cuda:0")
     w1, w2 = WORKLOADS["opt13b_fc1"], WORKLOADS["opt13b_fc2"]
-    i1 = layer_inputs(w1, seed=0, with_dy=False)
-    i2 = layer_inputs(w2, seed=0)
+    i1, i2 = inputs if inputs is not None else (layer_inputs(w1, seed=0, with_dy=False),
+                                                layer_inputs(w2, seed=0))
     X, W1, A1, B1 = (i1[k].to(dev) for k in ("X", "W", "A", "B"))
     W2, A2, B2, dY2 = (i2[k].to(dev) for k in ("W", "A", "B", "dY"))
     T = w1.T
@@ -361,14 +512,26 @@ def bench_mlp_chain(args):
             else:
                 sra.compress_pair(L["W"], out=(L["S"], L["P"]))
 
-    def fwd():
+    def fwd1():
         sra.sparse_lora_fwd(l1["S"], X, l1["A"], l1["B"], Y=l1["Y"], U=l1["U"], ws=l1["ws_f"])
+
+    def fwd2():
         sra.sparse_lora_fwd(l2["S"], l1["Y"], l2["A"], l2["B"], Y=l2["Y"], U=l2["U"], ws=l2["ws_f"])
 
-    def bwd():
+    def bwd2():
         sra.sparse_lora_bwd(l2["P"], dY2, l1["Y"], l2["U"], l2["A"], l2["B"], ws=l2["ws_b"], out=l2["g"])
+
+    def bwd1():
         sra.sparse_lora_bwd(l1["P"], l2["g"]["dX"], X, l1["U"], l1["A"], l1["B"], ws=l1["ws_b"],
                             out=l1["g"])
+
+    def fwd():
+        fwd1()
+        fwd2()
+
+    def bwd():
+        bwd2()
+        bwd1()
 
     def step():
         pairs()
@@ -376,18 +539,44 @@ def bench_mlp_chain(args):
         bwd()
 
     graph = not args.no_graph
-    ms = time_graph(step, args.steps, args.warmup, graph)
+    dist = {}
+    ms = time_graph(step, args.steps, args.warmup, graph, dist=dist)
     ms_fwd = time_graph(fwd, args.steps, args.warmup, graph)
     ms_bwd = time_graph(bwd, args.steps, args.warmup, graph)
+    ms_pairs = time_graph(pairs, args.steps, args.warmup, graph)
     W1d, W2d = W1.contiguous(), W2.contiguous()
     Y1d = torch.nn.functional.linear(X, W1d)
     dX2d = torch.matmul(dY2, W2d)
+    d_dist = {}
     d_fwd = time_graph(lambda: (torch.nn.functional.linear(X, W1d), torch.nn.functional.linear(Y1d, W2d)),
                        args.steps, args.warmup, graph)
     d_bwd = time_graph(lambda: (torch.matmul(dY2, W2d), torch.matmul(dX2d, W1d)),
                        args.steps, args.warmup, graph)
+    d_all = time_graph(lambda: (torch.nn.functional.linear(X, W1d), torch.nn.functional.linear(Y1d, W2d),
+                                torch.matmul(dY2, W2d), torch.matmul(dX2d, W1d)),
+                       args.steps, args.warmup, graph, dist=d_dist)
+
+    # the dominant kernel: the 2:4 SpMM with the fused adapter epilogue, four launches per step
+    # (fc1 Y, fc2 Y, fc2 dX, fc1 dX), each timed alone by the library's hook on its own stream.
+    # Algorithmic flops per launch: stored-half products 2 T R (C/2) plus the epilogue 2 T r R.
+    reps = max(10, args.steps)
+    launches = []
+    for name, call, R, C in (("fc1_fwd", fwd1, w1.N, w1.K), ("fc2_fwd", fwd2, w2.N, w2.K),
+                             ("fc2_dx", bwd2, w2.K, w2.N), ("fc1_dx", bwd1, w1.K, w1.N)):
+        mean, ts = time_kernel_dist(SRA_KERNEL_SPMM24, call, reps)
+        fl = 2 * T * R * (C // 2) + 2 * T * w1.r * R
+        launches.append({"call": name, "rows": R, "reduction": C, "flops": fl,
+                         "kernel_ms": round(mean, 5),
+                         "kernel_median_ms": round(float(sorted(ts)[len(ts) // 2]), 5),
+                         "tflops_stored": round(fl / (mean * 1e-3) / 1e12, 1)})
+    k_flops = sum(L["flops"] for L in launches) / len(launches)
+    k_ms = sum(L["kernel_ms"] for L in launches) / len(launches)
+    achieved = k_flops / (k_ms * 1e-3) / 1e12
+    kname = SPMM_MLP_KERNELS[args.layout]
+    traffic = TRAFFIC_BYTES.get(f"opt13b_mlp/{args.layout}/spmm24/{kname}")
+
     dense_eq = sum(step_model(L["wl"], T, with_compress=False)[0] for L in layers)
-    return {
+    line = {
         "metric": METRIC,
         "value": round(dense_eq / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
@@ -397,8 +586,11 @@ def bench_mlp_chain(args):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "opt13b_mlp", "T": T, "hidden": w1.K, "ffn": w1.N, "r": w1.r,
                    "sparsity": "2:4", "layout": args.layout,
-                   "step": "per layer compress + double_prune; fc1 fwd, fc2 fwd, fc2 bwd, fc1 bwd",
+                   "step": "per layer compress + double_prune; fc1 fwd, fc2 fwd, fc2 bwd (dX, dA, dB), "
+                           "fc1 bwd (dX, dA, dB)",
                    "graph": graph, "seed": 0},
+        # per-replay HIP-event times of the timed step (a second pass of the same replays)
+        "replay_ms": dist,
         # fwd + bwd of both layers against the chain's four dense GEMMs (X W1^T, Y1 W2^T, dY2 W2,
         # dX2 W1); compress and double prune are the method's setup and are timed apart
         "speedup_vs_dense": round((d_fwd + d_bwd) / (ms_fwd + ms_bwd), 3),
@@ -406,8 +598,21 @@ def bench_mlp_chain(args):
         "speedup_fwd_vs_dense_fwd": round(d_fwd / ms_fwd, 3),
         "speedup_bwd_vs_dense_dx": round(d_bwd / ms_bwd, 3),
         "detail_ms": {"step": round(ms, 5), "fwd": round(ms_fwd, 5), "bwd": round(ms_bwd, 5),
-                      "dense_fwd_gemms": round(d_fwd, 5), "dense_dx_gemms": round(d_bwd, 5)},
+                      "compress+double_prune": round(ms_pairs, 5),
+                      "dense_fwd_gemms": round(d_fwd, 5), "dense_dx_gemms": round(d_bwd, 5),
+                      "dense_four_gemms": round(d_all, 5)},
+        "dense_replay_ms": d_dist,
+        "spmm_launches": launches,
+        "roofline": {"kernel": f"{kname} (2:4 SpMM + adapter epilogue; mean of the four "
+                               f"launches of a step)",
+                     "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4),
+                     "traffic": round(traffic) if traffic else None,
+                     "algorithmic_flops_per_launch": int(k_flops),
+                     "kernel_ms": round(k_ms, 5)},
     }
+    return line, (i1, i2)
 
 
 def decode_bytes(wl, T, kernel_only=False):
@@ -568,6 +773,15 @@ def loop_calls(args):
     from sra_inputs import WORKLOADS, layer_inputs
 
     dev = torch.device("cuda:0")
+    if args.loop == "read":
+        # a plain reduction that reads 256 MiB (a ramp) and writes one value (counter calibration)
+        a = torch.arange(64 << 20, dtype=torch.float32, device=dev)
+        out = torch.empty((), dtype=torch.float32, device=dev)
+        for _ in range(args.steps):
+            torch.sum(a, out=out)
+        torch.cuda.synchronize()
+        print(f"read 256 MiB x {args.steps}", flush=True)
+        return
     if args.loop == "copy":
         # a plain elementwise kernel that reads 256 MiB (a ramp, no constant data) and writes 256 MiB
         a = torch.arange(64 << 20, dtype=torch.float32, device=dev)
@@ -576,6 +790,26 @@ def loop_calls(args):
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         print(f"copy 256 MiB x {args.steps}", flush=True)
+        return
+    if args.loop == "mlp":
+        # the chained OPT-13B MLP step's four products (streaming layout unless --layout canonical)
+        w1, w2 = WORKLOADS["opt13b_fc1"], WORKLOADS["opt13b_fc2"]
+        i1 = layer_inputs(w1, seed=0, with_dy=False)
+        i2 = layer_inputs(w2, seed=0)
+        X = i1["X"].to(dev)
+        L = []
+        for w, i in ((w1, i1), (w2, i2)):
+            W, A, B = (i[k].to(dev) for k in ("W", "A", "B"))
+            S, P = sra.compress_pair_tiled(W) if args.layout == "streaming" else sra.compress_pair(W)
+            L.append((S, P, A, B))
+        dY2 = i2["dY"].to(dev)
+        for _ in range(args.steps):
+            Y1, U1 = sra.sparse_lora_fwd(L[0][0], X, L[0][2], L[0][3])
+            Y2, U2 = sra.sparse_lora_fwd(L[1][0], Y1, L[1][2], L[1][3])
+            g2 = sra.sparse_lora_bwd(L[1][1], dY2, Y1, U2, L[1][2], L[1][3])
+            sra.sparse_lora_bwd(L[0][1], g2["dX"], X, U1, L[0][2], L[0][3])
+        torch.cuda.synchronize()
+        print(f"mlp opt13b x {args.steps}", flush=True)
         return
     wl = WORKLOADS["opt66b_ffn_decode" if args.loop == "decode" else args.workload]
     T = args.decode_t if args.loop == "decode" else wl.T
@@ -613,7 +847,12 @@ def main():
         return
     from sra_inputs import WORKLOADS
     if args.workload == "opt13b_mlp":
-        print(json.dumps(bench_mlp_chain(args)), flush=True)
+        out, (i1, i2) = bench_mlp_chain(args)
+        extras(args, out, small=not args.no_small)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_mlp(i1, i2, args.cpu_budget)
+            out["cpu_baseline_1thread"] = cpu_one_thread()
+        print(json.dumps(out), flush=True)
         return
     wl = WORKLOADS[args.workload]
     if wl.name == "opt66b_ffn_decode":
@@ -637,23 +876,32 @@ def main():
     if wl.fmt != "nm":
         raise SystemExit(f"workload {wl.name} is not wired into bench.py yet")
     out, inp, dense_eq = bench_nm_layer(args, wl)
+    extras(args, out, small=False)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget, dense_eq)
+        out["cpu_baseline"]["host"] = host_info()
+    print(json.dumps(out), flush=True)
+
+
+def extras(args, out, small):
+    """The other workloads measured beside the headline line (each its own config)."""
+    import copy
+
+    from sra_inputs import WORKLOADS
+    if small:
+        sargs = copy.copy(args)
+        sargs.layout = "canonical"
+        s, _, _ = bench_nm_layer(sargs, WORKLOADS["opt350m_fc1"])
+        keep = ("value", "unit", "ms_per_step", "config", "speedup_vs_dense",
+                "speedup_step_incl_compress_vs_dense", "speedup_vs_dense_lora", "detail_ms",
+                "speedup_fwd_vs_dense_fwd", "speedup_bwd_vs_dense_dx", "kernel_ms",
+                "masked_weight_grad", "roofline", "replay_ms")
+        out["opt350m_fc1"] = {k: s[k] for k in keep if k in s}
     if not args.no_decode:
         out["decode_opt66b_ffn"] = bench_decode(args, WORKLOADS["opt66b_ffn_decode"], (1, 4, 16))
         out["sparse_update_opt66b_ffn"] = bench_update(args, WORKLOADS["opt66b_ffn_decode"])
     if not args.no_ffi:
         out["ffi90_4096"] = bench_ffi(args, WORKLOADS["ffi90_4096"])
-    if not args.no_mlp and args.nm == "2:4" and wl.name == "opt350m_fc1":
-        import copy
-        margs = copy.copy(args)
-        margs.layout = "streaming"
-        m = bench_mlp_chain(margs)
-        out["opt13b_mlp_streaming"] = {k: m[k] for k in (
-            "value", "unit", "ms_per_step", "speedup_vs_dense", "speedup_step_incl_compress_vs_dense",
-            "speedup_fwd_vs_dense_fwd", "speedup_bwd_vs_dense_dx", "detail_ms")}
-        out["opt13b_mlp_streaming"]["config"] = m["config"]
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget, dense_eq)
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
