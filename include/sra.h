@@ -20,6 +20,8 @@
  *     Device pointers must be 16-byte aligned.
  *   - Ownership: the caller allocates and frees every buffer, including outputs and the
  *     workspace; the library allocates no device memory and keeps no pointer after a call returns.
+ *     The one exception is the fixed per-GPU array of sra_sparse_lora_bwd_noalloc, which lives in
+ *     the library's code object (no allocating call) until the process ends.
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     asynchronously; a call returns after launching.  Calls on different streams may overlap.
  *   - Errors: every call returns an sra_status.  All argument checks happen on the host before any
@@ -242,6 +244,30 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, c
                                int64_t T, const float* U, const void* A, const void* B, int32_t r,
                                uint32_t flags, void* dX, float* dA, float* dB, float* dU_out,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_lora_bwd_noalloc -- sra_sparse_lora_bwd with no workspace argument and no allocation,
+ * for callers that cannot allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc).  Same arguments, same kernels and the same
+ * results as sra_sparse_lora_bwd bit for bit; the workspace that call would take is a fixed
+ * device array inside the library instead, SRA_NOALLOC_SCRATCH_BYTES long, one per GPU, held
+ * until the process ends.
+ *   - The GPU is the calling thread's current device; `stream` must belong to it.
+ *   - A call whose workspace (sra_bwd_workspace with the same U / dU_out choices) exceeds
+ *     SRA_NOALLOC_SCRATCH_BYTES returns SRA_ERR_WORKSPACE before any launch; use
+ *     sra_sparse_lora_bwd with a caller workspace for such shapes.
+ *   - Every call on one GPU shares that GPU's array: calls on one stream run one after another,
+ *     but calls that can overlap on one GPU (different streams, or different threads) race on it
+ *     and give undefined results.  Nothing in the array needs to start at zero; a call writes
+ *     every part it reads.
+ *   - The first call on a device looks up the array's device address (no allocation); errors
+ *     there return SRA_ERR_HIP.
+ */
+#define SRA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sra_status sra_sparse_lora_bwd_noalloc(const sra_sparse* P /* host */, const void* dY,
+                                       const void* X, int64_t T, const float* U, const void* A,
+                                       const void* B, int32_t r, uint32_t flags, void* dX,
+                                       float* dA, float* dB, float* dU_out, void* stream);
 
 /*
  * masked_weight_grad -- gradient of the stored values of a compressed N:M matrix (SLoPe §2.1: in

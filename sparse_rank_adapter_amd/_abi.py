@@ -13,6 +13,7 @@ STATUS_NAMES = {0: "SRA_OK", -1: "SRA_ERR_INVALID_ARG", -2: "SRA_ERR_UNSUPPORTED
 SRA_BF16, SRA_F32 = 0, 1
 SRA_FMT_NM, SRA_FMT_ELL, SRA_FMT_CSR, SRA_FMT_NM_TILED = 0, 1, 2, 3
 SRA_GRAD_DX, SRA_GRAD_DA, SRA_GRAD_DB, SRA_DX_NO_ADAPTER = 1, 2, 4, 8
+SRA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/sra.h declares
 EXPORTS = (
@@ -20,7 +21,8 @@ EXPORTS = (
     "sra_compress_pair", "sra_compress_pair_tiled", "sra_nm_tile_bytes", "sra_nm_tile",
     "sra_masked_weight_grad", "sra_nm_axpby",
     "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
-    "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_time_next_kernel",
+    "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_sparse_lora_bwd_noalloc",
+    "sra_time_next_kernel",
 )
 SRA_KERNEL_COMPRESS, SRA_KERNEL_DOUBLE_PRUNE, SRA_KERNEL_SPMM24 = 1, 2, 3
 SRA_KERNEL_ADAPTER, SRA_KERNEL_DECODE24, SRA_KERNEL_SPMM_FFI = 4, 5, 6
@@ -71,6 +73,9 @@ def load(path: str = LIB_PATH):
         "sra_sparse_lora_bwd": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                                           c_int32, c_uint32, c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_size_t, c_void_p]),
+        "sra_sparse_lora_bwd_noalloc": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                                  c_void_p, c_int32, c_uint32, c_void_p, c_void_p,
+                                                  c_void_p, c_void_p, c_void_p]),
         "sra_time_next_kernel": (c_int32, [c_int32, c_void_p, c_void_p]),
     }
     assert set(sig) == set(EXPORTS)

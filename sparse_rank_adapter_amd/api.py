@@ -386,8 +386,11 @@ def sparse_lora_bwd(P: SparseMatrix, dY: torch.Tensor, X: torch.Tensor | None = 
                     U: torch.Tensor | None = None, A: torch.Tensor | None = None,
                     B: torch.Tensor | None = None, dx: bool = True, da: bool = True, db: bool = True,
                     dx_adapter: bool = True, want_du: bool = False, ws: torch.Tensor | None = None,
-                    out: dict | None = None):
-    """Double-pruned backward.  Returns dict with dX, dA, dB (and dU when want_du)."""
+                    out: dict | None = None, noalloc: bool = False):
+    """Double-pruned backward.  Returns dict with dX, dA, dB (and dU when want_du).
+
+    ``noalloc=True`` calls sra_sparse_lora_bwd_noalloc: no workspace, the library's fixed per-GPU
+    array instead (outputs missing from ``out`` are still allocated here by torch)."""
     lib = load()
     dev = _check_sparse(P, "P")
     K, N, dt = P.rows, P.cols, P.dtype
@@ -425,11 +428,18 @@ def sparse_lora_bwd(P: SparseMatrix, dY: torch.Tensor, X: torch.Tensor | None = 
         if out.get(key) is not None:
             _arg(out[key], f"out['{key}']", shape, odt, dev)
     d = P.desc()
-    nbytes = ctypes.c_size_t()
-    check("sra_bwd_workspace", lib.sra_bwd_workspace(ctypes.byref(d), T, r, flags, ctypes.byref(nbytes)))
-    if ws is None or ws.numel() < nbytes.value:
-        ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
-    _arg(ws, "ws", (ws.numel(),), torch.uint8, dev)
+    if not noalloc:
+        nbytes = ctypes.c_size_t()
+        check("sra_bwd_workspace", lib.sra_bwd_workspace(ctypes.byref(d), T, r, flags, ctypes.byref(nbytes)))
+        if ws is None or ws.numel() < nbytes.value:
+            ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
+        _arg(ws, "ws", (ws.numel(),), torch.uint8, dev)
+    if noalloc:
+        check("sra_sparse_lora_bwd_noalloc", lib.sra_sparse_lora_bwd_noalloc(
+            ctypes.byref(d), _p(dY), _p(X), T, _p(U) if r else None, _p(A) if r else None,
+            _p(B) if r else None, r, flags, _p(out.get("dX")), _p(out.get("dA")), _p(out.get("dB")),
+            _p(out.get("dU")), _stream(dev)))
+        return out
     check("sra_sparse_lora_bwd", lib.sra_sparse_lora_bwd(
         ctypes.byref(d), _p(dY), _p(X), T, _p(U) if r else None, _p(A) if r else None,
         _p(B) if r else None, r, flags, _p(out.get("dX")), _p(out.get("dA")), _p(out.get("dB")),

@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -265,6 +266,32 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   p.total = a.used;
   if (plan) *plan = p;
   return p.total;
+}
+
+// Every host check of a backward call except the workspace: shapes, flags, pointers.  Fills the
+// workspace plan for the U / dU_out choices of the call.
+sra_status check_bwd_args(const sra_sparse* P, const void* dY, const void* X, int64_t T,
+                          const float* U, const void* A, const void* B, int32_t r, uint32_t flags,
+                          const void* dX, const float* dA, const float* dB, const float* dU_out,
+                          BwdPlan* plan) {
+  SRA_TRY(validate_bwd(P, T, r, flags));
+  const int64_t K = P->rows, N = P->cols;
+  const bool fdx = flags & SRA_GRAD_DX, fda = (flags & SRA_GRAD_DA) && r > 0,
+             fdb = (flags & SRA_GRAD_DB) && r > 0;
+  const bool dx_ad = fdx && !(flags & SRA_DX_NO_ADAPTER) && r > 0;
+  bwd_bytes(P, T, r, flags, U != nullptr, dU_out != nullptr, plan);
+  const bool any = T > 0;
+  SRA_TRY(check_ptr(dY, any && N > 0 && (fdx || plan->need_du || fdb), "dY"));
+  const bool recompute_u = plan->own_u || (P->dtype == SRA_F32 && plan->need_u);
+  SRA_TRY(check_ptr(X, any && K > 0 && (fda || recompute_u), "X"));
+  SRA_TRY(check_ptr(A, any && r > 0 && K > 0 && (dx_ad || recompute_u), "A"));
+  SRA_TRY(check_ptr(B, any && r > 0 && N > 0 && plan->need_du, "B"));
+  SRA_TRY(check_ptr(dX, fdx && any && K > 0, "dX"));
+  SRA_TRY(check_ptr(dA, fda && K > 0, "dA"));
+  SRA_TRY(check_ptr(dB, fdb && N > 0, "dB"));
+  if (U) SRA_TRY(check_ptr(U, true, "U"));
+  if (dU_out) SRA_TRY(check_ptr(dU_out, true, "dU_out"));
+  return SRA_OK;
 }
 
 }  // namespace
@@ -619,24 +646,12 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                const void* A, const void* B, int32_t r, uint32_t flags, void* dX,
                                float* dA, float* dB, float* dU_out, void* ws, size_t ws_bytes,
                                void* stream) {
-  SRA_TRY(validate_bwd(P, T, r, flags));
+  BwdPlan plan;
+  SRA_TRY(check_bwd_args(P, dY, X, T, U, A, B, r, flags, dX, dA, dB, dU_out, &plan));
   const int64_t K = P->rows, N = P->cols;
   const bool fdx = flags & SRA_GRAD_DX, fda = (flags & SRA_GRAD_DA) && r > 0,
              fdb = (flags & SRA_GRAD_DB) && r > 0;
   const bool dx_ad = fdx && !(flags & SRA_DX_NO_ADAPTER) && r > 0;
-  BwdPlan plan;
-  bwd_bytes(P, T, r, flags, U != nullptr, dU_out != nullptr, &plan);
-  const bool any = T > 0;
-  SRA_TRY(check_ptr(dY, any && N > 0 && (fdx || plan.need_du || fdb), "dY"));
-  const bool recompute_u = plan.own_u || (P->dtype == SRA_F32 && plan.need_u);
-  SRA_TRY(check_ptr(X, any && K > 0 && (fda || recompute_u), "X"));
-  SRA_TRY(check_ptr(A, any && r > 0 && K > 0 && (dx_ad || recompute_u), "A"));
-  SRA_TRY(check_ptr(B, any && r > 0 && N > 0 && plan.need_du, "B"));
-  SRA_TRY(check_ptr(dX, fdx && any && K > 0, "dX"));
-  SRA_TRY(check_ptr(dA, fda && K > 0, "dA"));
-  SRA_TRY(check_ptr(dB, fdb && N > 0, "dB"));
-  if (U) SRA_TRY(check_ptr(U, true, "U"));
-  if (dU_out) SRA_TRY(check_ptr(dU_out, true, "dU_out"));
   if (plan.total > 0 && (!ws || ws_bytes < plan.total))
     return fail(SRA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", plan.total, ws_bytes);
   if (plan.total > 0 && !al16(ws)) return fail(SRA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
@@ -748,6 +763,44 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)X, T, K, vtdU, 4, r, true, dA, gws, s),
                      s, "bwd dA"));
   return SRA_OK;
+}
+
+// Allocation-free backward: the workspace is this fixed device array.  In host code its name is
+// only a stand-in for the symbol; the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[SRA_NOALLOC_SCRATCH_BYTES];
+
+sra_status sra_sparse_lora_bwd_noalloc(const sra_sparse* P, const void* dY, const void* X, int64_t T,
+                                       const float* U, const void* A, const void* B, int32_t r,
+                                       uint32_t flags, void* dX, float* dA, float* dB,
+                                       float* dU_out, void* stream) {
+  BwdPlan plan;
+  SRA_TRY(check_bwd_args(P, dY, X, T, U, A, B, r, flags, dX, dA, dB, dU_out, &plan));
+  const size_t need = plan.total;
+  if (need > SRA_NOALLOC_SCRATCH_BYTES)
+    return fail(SRA_ERR_WORKSPACE, "this call needs %zu bytes of workspace, above the %zu of the "
+                "allocation-free entry point (use sra_sparse_lora_bwd)", need,
+                (size_t)SRA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    static std::mutex mu;
+    static void* dev_ptr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SRA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(SRA_ERR_UNSUPPORTED, "device ordinal %d above 63", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(SRA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      dev_ptr[dev] = p;
+    }
+    ws = dev_ptr[dev];
+  }
+  return sra_sparse_lora_bwd(P, dY, X, T, U, A, B, r, flags, dX, dA, dB, dU_out, ws,
+                             ws ? (size_t)SRA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 }  // extern "C"

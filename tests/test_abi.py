@@ -257,6 +257,23 @@ def test_bwd_validation(lib):
     assert st == SRA_ERR_WORKSPACE
 
 
+def test_bwd_noalloc_host_checks(lib):
+    """The allocation-free backward validates like sra_sparse_lora_bwd and refuses calls whose
+    workspace exceeds its fixed array, both before touching the GPU."""
+    P = nm_desc(rows=5120, cols=20480)
+    st = lib.sra_sparse_lora_bwd_noalloc(ctypes.byref(P), FAKE, FAKE, 8192, None, FAKE, FAKE, 128, 7,
+                                         FAKE, FAKE, FAKE, None, None)
+    assert st == SRA_ERR_WORKSPACE and "allocation-free" in err(lib)
+    st = lib.sra_sparse_lora_bwd_noalloc(ctypes.byref(P), FAKE, FAKE, 8192, None, FAKE, FAKE, 128, 16,
+                                         FAKE, FAKE, FAKE, None, None)
+    assert st == SRA_ERR_INVALID_ARG
+    small = nm_desc(rows=1024, cols=4096)
+    st = lib.sra_sparse_lora_bwd_noalloc(ctypes.byref(small), FAKE, FAKE, 2048, FAKE, FAKE, FAKE, 16,
+                                         7, None, FAKE, FAKE, None, None)
+    assert st == SRA_ERR_INVALID_ARG and "dX" in err(lib)
+    assert _abi.SRA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_binding_fails_loudly_when_library_missing(tmp_path):
     saved = _abi._lib
     _abi._lib = None
