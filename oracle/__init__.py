@@ -19,10 +19,15 @@ computes, in float64 over inputs that hold the exact storage-dtype values:
                    LoRA as described in "efficient training for the gpu-poor",
                    section PEFT).
 
+* ``oracle.layer`` also holds SQuAsh's variant, an adapter whose down-projection
+                   factor is itself fixed-fan-in sparse (SQuAsh project update,
+                   first paragraph), and the masked weight gradient and sparse
+                   update of SLoPe's sparse training (§2.1, §2.3).
+
 Every function is pinned by ``tests/test_oracle_pins.py`` against brute force,
 invariants, library routines (torch autograd, ``F.linear``) and the added
-sparsity that SLoPe's Lemma 2.1 (§2.1, proof in App. T.1) predicts.  The one
-unpinned figure is Lemma 2.1's 2:8 value (parity unpinned: the printed number
-does not follow from the binomial model the same appendix describes).
+sparsity that SLoPe's Lemma 2.1 (§2.1, proof in App. T.1) predicts, at 1:2,
+2:4 and 2:8.  The page's printed 2:8 figure itself is not reproduced by the
+binomial model the same appendix describes; it is recorded, not enforced.
 """
 from . import ffi, layer, nm  # noqa: F401

@@ -82,3 +82,29 @@ def nm_axpby(beta, a_vals, gamma, b_vals):
     the update step (SLoPe paperlayer summary, §2.3: a sparse addition of two matrices with the
     same pattern; §2.1: the mask stays fixed, so the metadata carries over unchanged).  float64."""
     return beta * np.asarray(a_vals, dtype=np.float64) + gamma * np.asarray(b_vals, dtype=np.float64)
+
+
+def ffi_adapter_forward(X, Ws, A_vals, A_cols, B):
+    """Forward with a fixed-fan-in adapter factor -- SQuAsh's variant (SQuAsh project update, first
+    paragraph: one factor of the low-rank product is pruned with fixed fan-in so that a higher rank
+    fits the same memory).  The pruned factor is the down-projection A [r,K]: row j keeps exactly k
+    inputs, given as ELL values ``A_vals[r,k]`` and ascending columns ``A_cols[r,k]``.  With
+    A_s = A_vals scattered to their columns,
+        U = X A_s^T,   Y = X Ws^T + U B^T.
+    Returns (Y, U).  float64."""
+    from . import ffi as _ffi
+    A = _ffi.to_dense(np.asarray(A_vals, dtype=np.float64), np.asarray(A_cols), X.shape[1])
+    return forward(X, Ws, A, B)
+
+
+def ffi_adapter_backward(dY, X, Wsub, A_vals, A_cols, B, U=None, dx_adapter=True):
+    """Backward of ffi_adapter_forward: dU = dY B, dB = dY^T U, dX = dY Wsub + dU A_s, and the
+    gradient of A's stored values only (the fixed fan-in mask is fixed, as the sparse weight's mask
+    is in SLoPe §2.1), i.e. the dense dA = dU^T X read at each row's stored columns, in the ELL
+    order: ``dA_vals[j][i] = sum_t dU[t][j] X[t][A_cols[j][i]]``.  Returns dict with dU, dB,
+    dA_vals, dX.  float64."""
+    from . import ffi as _ffi
+    A = _ffi.to_dense(np.asarray(A_vals, dtype=np.float64), np.asarray(A_cols), X.shape[1])
+    g = backward(dY, X, Wsub, A, B, U, dx_adapter)
+    g["dA_vals"] = np.take_along_axis(g.pop("dA"), np.asarray(A_cols).astype(np.int64), axis=1)
+    return g

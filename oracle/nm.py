@@ -21,9 +21,15 @@ Readings taken where the page is silent:
 
 Compressed format ("nm"): for a rows x cols matrix pruned along cols,
 ``values[rows, cols*N/M]`` holds the kept entries of each row in ascending
-column order; ``meta[rows, ceil(cols*N/M/16)]`` (uint32) holds each kept
-entry's in-group index as a 2-bit field, fields in kept order, packed
-least-significant first, 16 per word, unused high fields zero.  M <= 4.
+column order; ``meta`` (uint32 words) holds each kept entry's in-group index:
+* M <= 4: a 2-bit field per kept entry, fields in kept order, packed
+  least-significant first, 16 per word, unused high fields zero
+  (``ceil(cols*N/M/16)`` words per row);
+* M = 8 (N <= 2): a 3-bit field per kept entry; the N fields of one group share
+  one byte (field i at bits 3i, the rest zero), groups in column order, four
+  bytes per word least-significant first (``ceil(cols/32)`` words per row).
+  This layout is this library's reading: the pages give 2:8 only as a pattern
+  (SLoPe §2.1, Lemma 2.1) and no storage format for it.
 """
 from __future__ import annotations
 
@@ -31,16 +37,20 @@ import numpy as np
 
 FIELD_BITS = 2
 FIELDS_PER_WORD = 16
+GROUPS_PER_WORD_M8 = 4    # M = 8: one byte per group
 
 
 def meta_words_per_row(cols: int, n: int, m: int) -> int:
+    if m == 8:
+        groups = cols // m
+        return (groups + GROUPS_PER_WORD_M8 - 1) // GROUPS_PER_WORD_M8
     fields = cols // m * n
     return (fields + FIELDS_PER_WORD - 1) // FIELDS_PER_WORD
 
 
 def _check(cols: int, n: int, m: int):
-    if not (1 <= n <= m <= 4):
-        raise ValueError("oracle supports 1 <= n <= m <= 4")
+    if not (1 <= n <= m <= 4 or (m == 8 and 1 <= n <= 2)):
+        raise ValueError("oracle supports 1 <= n <= m <= 4, and 1:8 / 2:8")
     if cols % m:
         raise ValueError("grouped dimension must be a multiple of m")
 
@@ -73,8 +83,20 @@ def nm_mask(W: np.ndarray, n: int, m: int, chunk_rows: int = 2048) -> np.ndarray
     return out
 
 
-def pack_fields(fields: np.ndarray) -> np.ndarray:
-    """fields[rows, F] (values < 4) -> uint32 words[rows, ceil(F/16)], LSB-first."""
+def pack_fields(fields: np.ndarray, n: int = 2, m: int = 4) -> np.ndarray:
+    """fields[rows, F] (in-group indices, F = groups * n) -> uint32 words, LSB-first.
+
+    M <= 4: 2-bit fields, 16 per word.  M = 8: 3-bit fields, one byte per group, 4 per word."""
+    if m == 8:
+        rows, F = fields.shape
+        G = F // n
+        f = fields.reshape(rows, G, n).astype(np.uint64)
+        byte = (f << (np.arange(n, dtype=np.uint64) * 3)).sum(axis=-1)        # [rows, G]
+        words = (G + GROUPS_PER_WORD_M8 - 1) // GROUPS_PER_WORD_M8
+        padded = np.zeros((rows, words * GROUPS_PER_WORD_M8), dtype=np.uint64)
+        padded[:, :G] = byte
+        padded = padded.reshape(rows, words, GROUPS_PER_WORD_M8)
+        return (padded << (np.arange(GROUPS_PER_WORD_M8, dtype=np.uint64) * 8)).sum(-1).astype(np.uint32)
     rows, F = fields.shape
     words = (F + FIELDS_PER_WORD - 1) // FIELDS_PER_WORD
     padded = np.zeros((rows, words * FIELDS_PER_WORD), dtype=np.uint64)
@@ -84,8 +106,15 @@ def pack_fields(fields: np.ndarray) -> np.ndarray:
     return (padded << shifts).sum(axis=-1).astype(np.uint32)
 
 
-def unpack_fields(meta: np.ndarray, F: int) -> np.ndarray:
+def unpack_fields(meta: np.ndarray, F: int, n: int = 2, m: int = 4) -> np.ndarray:
+    """Inverse of pack_fields: the first F fields of every row."""
     rows, words = meta.shape
+    if m == 8:
+        G = F // n
+        byte = (meta.astype(np.uint64)[..., None] >> (np.arange(GROUPS_PER_WORD_M8, dtype=np.uint64) * 8)) & 255
+        byte = byte.reshape(rows, words * GROUPS_PER_WORD_M8)[:, :G]
+        f = (byte[..., None] >> (np.arange(n, dtype=np.uint64) * 3)) & 7
+        return f.reshape(rows, G * n).astype(np.int64)
     shifts = (np.arange(FIELDS_PER_WORD, dtype=np.uint64) * FIELD_BITS)
     f = (meta.astype(np.uint64)[..., None] >> shifts) & 3
     return f.reshape(rows, words * FIELDS_PER_WORD)[:, :F].astype(np.int64)
@@ -106,7 +135,7 @@ def encode(W: np.ndarray, keep: np.ndarray, n: int, m: int, pad_zero: bool = Fal
     if pad_zero is not False:
         vals[pad_zero[keep].reshape(rows, G * n)] = 0.0
     pos = np.nonzero(kg)[2].reshape(rows, G * n)   # ascending in-group positions, row-major order
-    return vals, pack_fields(pos)
+    return vals, pack_fields(pos, n, m)
 
 
 def compress(W: np.ndarray, n: int, m: int):
@@ -120,7 +149,7 @@ def decompress(vals: np.ndarray, meta: np.ndarray, n: int, m: int, cols: int):
     """Canonical arrays -> (dense matrix, stored-position bitmap)."""
     rows = vals.shape[0]
     G = cols // m
-    pos = unpack_fields(meta, G * n).reshape(rows, G, n)
+    pos = unpack_fields(meta, G * n, n, m).reshape(rows, G, n)
     col = (np.arange(G)[None, :, None] * m + pos).reshape(rows, G * n)
     dense = np.zeros((rows, cols), dtype=vals.dtype)
     stored = np.zeros((rows, cols), dtype=bool)

@@ -75,7 +75,7 @@ def tie_heavy(rng, shape, alphabet=(0.0, -0.0, 0.5, -0.5, 1.0, 2.0)):
     return np.array(rng.choice(np.array(alphabet), size=shape), dtype=np.float64)
 
 
-NM_CASES = [(1, 2), (2, 4), (1, 4), (3, 4), (2, 2), (4, 4)]
+NM_CASES = [(1, 2), (2, 4), (1, 4), (3, 4), (2, 2), (4, 4), (2, 8), (1, 8)]
 
 
 # ----------------------------------------------------------------------------- a1: N:M mask + format
@@ -98,6 +98,18 @@ def test_pack_golden_example():
     assert np.array_equal(np.signbit(vals), np.signbit(np.array(g["values"])))
     assert np.array_equal(nm.unpack_fields(meta, 8), np.array(g["fields"]))
     assert meta.dtype == np.uint32 and meta.tolist() == g["meta_words"]
+
+
+def test_pack_golden_example_2_8():
+    """The 2:8 format (3-bit fields, one byte per group) on a hand-worked row."""
+    g = json.load(open(os.path.join(GOLDEN, "nm28_pack_example.json")))
+    W = np.array(g["W"])
+    vals, meta, mask1 = nm.compress(W, g["n"], g["m"])
+    assert np.array_equal(vals, np.array(g["values"]))
+    assert np.array_equal(np.signbit(vals), np.signbit(np.array(g["values"])))
+    assert np.array_equal(nm.unpack_fields(meta, 10, 2, 8), np.array(g["fields"]))
+    assert meta.dtype == np.uint32 and meta.tolist() == g["meta_words"]
+    assert nm.meta_words_per_row(40, 2, 8) == 2 and nm.meta_words_per_row(4096, 2, 8) == 128
 
 
 @pytest.mark.parametrize("n,m", NM_CASES)
@@ -194,6 +206,26 @@ def test_lemma_2_1_statistics(n, m, tol):
     _, _, mask2, _ = nm.double_prune(vals, meta, n, m, 1024)
     frac = (mask1 & ~mask2).sum() / W.size
     assert abs(frac - g["printed"][f"{n}:{m}"]) < tol
+
+
+def test_lemma_2_1_statistics_2_8():
+    """2:8 on Gaussian weights: the oracle's double prune removes the binomial model's fraction
+    (about 5.84%; within 4 standard errors of the model's own variance), not the 3.39% the page
+    prints.  The mask-1 survivors of one 8-row column group are 8 independent rows each keeping
+    the column with probability 1/4, so the model is exact for iid weights."""
+    g = json.load(open(os.path.join(GOLDEN, "lemma_2_1.json")))
+    rng = np.random.default_rng(1)
+    W = rng.standard_normal((4096, 1024)).astype(np.float32).astype(np.float64)
+    vals, meta, mask1 = nm.compress(W, 2, 8)
+    _, _, mask2, _ = nm.double_prune(vals, meta, 2, 8, 1024)
+    frac = (mask1 & ~mask2).sum() / W.size
+    model = _binomial_added_zeros(2, 8)
+    p = 0.25
+    pmf = [math.comb(8, y) * p ** y * (1 - p) ** (8 - y) for y in range(9)]
+    var = sum(((max(y - 2, 0) / 8) - model) ** 2 * pmf[y] for y in range(9))
+    se = math.sqrt(var / (W.size / 8))
+    assert abs(frac - model) < 4 * se
+    assert abs(frac - g["printed"]["2:8"]) > 100 * se
 
 
 # ----------------------------------------------------------------------------- a3: fixed fan-in
@@ -396,6 +428,66 @@ def test_nm_axpby_against_library_and_dense():
     Gd, _ = nm.decompress(dW, meta, 2, 4, 32)
     assert np.allclose(D, beta * Wa + gamma * Gd, rtol=1e-14, atol=1e-14)
     assert np.array_equal(stored, mask)
+
+
+# ----------------------------------------------------------------------------- fixed-fan-in adapter factor
+
+def _squash_problem(seed, T=6, K=20, N=8, r=3, k=5):
+    rng = np.random.default_rng(seed)
+    X, dY = rng.standard_normal((T, K)), rng.standard_normal((T, N))
+    Ws = rng.standard_normal((N, K)) * 0.1
+    A_full, B = rng.standard_normal((r, K)) * 0.1, rng.standard_normal((N, r)) * 0.1
+    A_vals, A_cols = ffi.select(A_full, k)
+    return X, dY, Ws, A_vals, A_cols, B
+
+
+def test_ffi_adapter_against_autograd():
+    """SQuAsh's fixed-fan-in adapter factor: gradients of sum(dY * Y) with respect to B, X and the
+    stored values of A, by torch autograd in float64 (A rebuilt by index_put from its values)."""
+    X, dY, Ws, A_vals, A_cols, B = _squash_problem(0)
+    Y, U = layer.ffi_adapter_forward(X, Ws, A_vals, A_cols, B)
+    g = layer.ffi_adapter_backward(dY, X, Ws, A_vals, A_cols, B, U)
+    tX = torch.tensor(X, requires_grad=True)
+    tv = torch.tensor(A_vals, requires_grad=True)
+    tB = torch.tensor(B, requires_grad=True)
+    rows = torch.arange(A_vals.shape[0]).repeat_interleave(A_vals.shape[1])
+    tA = torch.zeros(A_vals.shape[0], X.shape[1], dtype=torch.float64).index_put(
+        (rows, torch.tensor(A_cols.astype(np.int64)).reshape(-1)), tv.reshape(-1))
+    tY = F.linear(tX, torch.tensor(Ws)) + F.linear(F.linear(tX, tA), tB)
+    (tY * torch.tensor(dY)).sum().backward()
+    assert np.allclose(Y, tY.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dA_vals"], tv.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dB"], tB.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dX"], tX.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dU"], dY @ B, rtol=1e-12, atol=1e-12)
+
+
+def test_ffi_adapter_finite_differences():
+    """The loss is linear in each stored value of A: a central difference is exact up to rounding."""
+    X, dY, Ws, A_vals, A_cols, B = _squash_problem(1)
+    g = layer.ffi_adapter_backward(dY, X, Ws, A_vals, A_cols, B)
+    h = 1e-3
+    for j in range(A_vals.shape[0]):
+        for i in range(A_vals.shape[1]):
+            ap, am = A_vals.copy(), A_vals.copy()
+            ap[j, i] += h
+            am[j, i] -= h
+            lp = (dY * layer.ffi_adapter_forward(X, Ws, ap, A_cols, B)[0]).sum()
+            lm = (dY * layer.ffi_adapter_forward(X, Ws, am, A_cols, B)[0]).sum()
+            assert (lp - lm) / (2 * h) == pytest.approx(g["dA_vals"][j, i], rel=1e-8, abs=1e-10)
+
+
+def test_ffi_adapter_full_fan_in_is_the_dense_adapter():
+    """With k = K nothing is pruned: the dense adapter's forward and gradients."""
+    X, dY, Ws, _, _, B = _squash_problem(2, k=20)
+    A = np.random.default_rng(9).standard_normal((3, 20)) * 0.1
+    A_vals, A_cols = ffi.select(A, 20)
+    assert np.array_equal(A_vals, A)
+    Y, _ = layer.ffi_adapter_forward(X, Ws, A_vals, A_cols, B)
+    Yd = X @ Ws.T + X @ A.T @ B.T
+    assert np.allclose(Y, Yd, rtol=1e-13, atol=1e-13)
+    g = layer.ffi_adapter_backward(dY, X, Ws, A_vals, A_cols, B)
+    assert np.allclose(g["dA_vals"], (dY @ B).T @ X, rtol=1e-12, atol=1e-12)
 
 
 def test_rel_err_metric():
