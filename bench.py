@@ -36,14 +36,22 @@ PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA (published); 2:4 work is pri
 PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E (published)
 PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector (published)
 
-# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of `bench.py --loop
-# <call>` (profiles/opt350m_fc1_spmm24_traffic.md, profiles/opt66b_ffn_decode_traffic.md), each
-# counter scaled by the factor that makes a plain 256 MiB elementwise copy read and write 256 MiB
-# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the kernel configuration the planner picks for
-# that call; a key missing here (kernel changed since the counters were taken) reports null.
+# Bytes between L2 and the fabric per launch (an upper bound on HBM bytes: the Infinity Cache may
+# serve part of them) from rocprofv3 --pmc runs of `bench.py --loop <call>`
+# (profiles/opt13b_mlp_spmm24_traffic.md, profiles/opt350m_fc1_spmm24_traffic.md,
+# profiles/opt66b_ffn_decode_traffic.md).  Calibration: on gfx950 every read request counted by
+# TCC_EA0_RDREQ moves a 128-byte line (TCC_BUBBLE and RDREQ_32B stay 0), so FETCH_SIZE, whose
+# formula prices these at 64 bytes, reads half of a plain 256 MiB read or copy: FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0.  Keyed by the kernel configuration the planner picks for that call; a key
+# missing here (kernel changed since the counters were taken) reports null.
 TRAFFIC_BYTES = {
     "opt350m_fc1/2:4/canonical/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>": 27366.7 * 1024 * 2.0 + 4352.0 * 1024,
     "opt350m_fc1/2:4/canonical/spmm24_fwd/k_spmm24_q<4,4,4,2,3,8,16>": 13840.2 * 1024 * 2.0 + 16512.0 * 1024,
+    # chained OPT-13B MLP step, streaming layout: mean per launch of the four 256x256 SpMM
+    # products (profiles/opt13b_mlp_spmm24_traffic.md: TCC_EA0_RDREQ x 128 B + TCC_EA0_WRREQ x
+    # 64 B, which equal FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 on gfx950)
+    "opt13b_mlp/streaming/spmm24/k_spmm24_q<4, 8, 4, 2, 3, 4, 0, false, true, false>":
+        18336626 * 128 + 3815806 * 64,
     # streaming layout (sra_nm_tile), 48-row workgroups of four waves
     "opt66b_ffn_decode/T16/streaming/k_decode24<3>": 192608.7 * 1024 * 2.0 + 1152.1 * 1024,
     "opt66b_ffn_decode/T1/streaming/k_decode24<3>": 189201.6 * 1024 * 2.0 + 72.0 * 1024,
@@ -778,7 +786,7 @@ def loop_calls(args):
         a = torch.arange(64 << 20, dtype=torch.float32, device=dev)
         out = torch.empty((), dtype=torch.float32, device=dev)
         for _ in range(args.steps):
-            torch.sum(a, out=out)
+            torch.sum(a, dim=0, out=out)
         torch.cuda.synchronize()
         print(f"read 256 MiB x {args.steps}", flush=True)
         return
