@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b_mlp",
                     choices=["opt350m_fc1", "opt13b_fc1", "opt13b_fc2", "opt13b_mlp", "ffi90_4096",
-                             "opt66b_ffn_decode"])
+                             "opt66b_ffn_decode", "squash_opt350m_fc2"])
     ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
     ap.add_argument("--decode-layout", choices=["streaming", "canonical"], default="streaming",
                     help="weight layout of the decode forward (streaming = sra_nm_tile)")
@@ -773,6 +773,74 @@ def bench_ffi(args, wl):
             "compress_ffi_ms": round(ms_setup, 5)}
 
 
+def bench_squash(args, wl):
+    """SQuAsh's variant: the 2:4 layer with a rank-r adapter whose A keeps wl.adapter_k inputs per
+    row (fixed fan-in, ELL values + int16 columns), against the same layer with a dense adapter of
+    the same bytes (rank r_dense = adapter bytes / 2 (K + N)) and against the dense GEMMs."""
+    import torch
+
+    import sparse_rank_adapter_amd as sra
+    from sra_inputs import layer_inputs
+
+    dev = torch.device("cuda:0")
+    inp = layer_inputs(wl, seed=0)
+    X, W, Af, B, dY = (inp[k].to(dev) for k in ("X", "W", "A", "B", "dY"))
+    T, r, k = wl.T, wl.r, wl.adapter_k
+    graph = not args.no_graph
+    S, P = sra.compress_pair(W)
+    A = sra.compress_ffi(Af, k)
+    ffa_bytes = r * k * (2 + 2) + wl.N * r * 2
+    r_d = ffa_bytes // (2 * (wl.K + wl.N))
+    Ad, Bd = Af[:r_d].contiguous(), B[:, :r_d].contiguous()
+    Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
+    U = torch.empty((T, r), dtype=torch.float32, device=dev)
+    Ud = torch.empty((T, r_d), dtype=torch.float32, device=dev)
+    g = {"dX": torch.empty((T, wl.K), dtype=X.dtype, device=dev),
+         "dA_values": torch.empty((r, k), dtype=torch.float32, device=dev),
+         "dB": torch.empty((wl.N, r), dtype=torch.float32, device=dev)}
+    gd = {"dX": torch.empty((T, wl.K), dtype=X.dtype, device=dev),
+          "dA": torch.empty((r_d, wl.K), dtype=torch.float32, device=dev),
+          "dB": torch.empty((wl.N, r_d), dtype=torch.float32, device=dev)}
+    ws_f = torch.empty(max(1, sra.ffa_fwd_workspace(S, T, A), sra.fwd_workspace(S, T, r_d)),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, sra.ffa_bwd_workspace(P, T, A), sra.bwd_workspace(P, T, r_d)),
+                       dtype=torch.uint8, device=dev)
+
+    def fwd():
+        sra.sparse_lora_fwd_ffa(S, X, A, B, Y=Y, U=U, ws=ws_f)
+
+    def bwd():
+        sra.sparse_lora_bwd_ffa(P, dY, X, U, A, B, ws=ws_b, out=g)
+
+    def fwd_d():
+        sra.sparse_lora_fwd(S, X, Ad, Bd, Y=Y, U=Ud, ws=ws_f)
+
+    def bwd_d():
+        sra.sparse_lora_bwd(P, dY, X, Ud, Ad, Bd, ws=ws_b, out=gd)
+    fwd()
+    bwd()
+    fwd_d()
+    bwd_d()
+    ms_f = time_graph(fwd, args.steps, args.warmup, graph)
+    ms_b = time_graph(bwd, args.steps, args.warmup, graph)
+    ms_fd = time_graph(fwd_d, args.steps, args.warmup, graph)
+    ms_bd = time_graph(bwd_d, args.steps, args.warmup, graph)
+    Wd = W.contiguous()
+    d_f = time_graph(lambda: torch.nn.functional.linear(X, Wd), args.steps, args.warmup, graph)
+    d_b = time_graph(lambda: torch.matmul(dY, Wd), args.steps, args.warmup, graph)
+    dense_eq = step_model(wl, T, with_compress=False)[0]
+    return {"workload": wl.name, "T": T, "K": wl.K, "N": wl.N, "r": r, "adapter_k": k,
+            "adapter_bytes": ffa_bytes, "dense_adapter_rank_same_bytes": r_d,
+            "dense_adapter_bytes": r_d * 2 * (wl.K + wl.N),
+            "fwd_ms": round(ms_f, 5), "bwd_ms": round(ms_b, 5),
+            "dense_eq_tflops": round(dense_eq / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
+            "same_bytes_dense_adapter_fwd_ms": round(ms_fd, 5),
+            "same_bytes_dense_adapter_bwd_ms": round(ms_bd, 5),
+            "time_vs_same_bytes_dense_adapter": round((ms_f + ms_b) / (ms_fd + ms_bd), 3),
+            "dense_fwd_gemm_ms": round(d_f, 5), "dense_dx_gemm_ms": round(d_b, 5),
+            "speedup_vs_dense": round((d_f + d_b) / (ms_f + ms_b), 3)}
+
+
 def loop_calls(args):
     """Repeat one call for counter collection: no timing, no output but a last line."""
     import torch
@@ -863,6 +931,9 @@ def main():
         print(json.dumps(out), flush=True)
         return
     wl = WORKLOADS[args.workload]
+    if wl.name == "squash_opt350m_fc2":
+        print(json.dumps(bench_squash(args, wl)), flush=True)
+        return
     if wl.name == "opt66b_ffn_decode":
         rows = bench_decode(args, wl, (args.decode_t,))
         d = rows[0]
@@ -910,6 +981,7 @@ def extras(args, out, small):
         out["sparse_update_opt66b_ffn"] = bench_update(args, WORKLOADS["opt66b_ffn_decode"])
     if not args.no_ffi:
         out["ffi90_4096"] = bench_ffi(args, WORKLOADS["ffi90_4096"])
+    out["squash_opt350m_fc2"] = bench_squash(args, WORKLOADS["squash_opt350m_fc2"])
 
 
 if __name__ == "__main__":

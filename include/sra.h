@@ -246,6 +246,36 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P /* host */, const void* dY, c
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Fixed-fan-in adapter factor (SQuAsh project update, first paragraph: one factor of the low-rank
+ * product is itself pruned with fixed fan-in, so that a higher-rank adapter fits the memory of a
+ * lower-rank dense one).  The pruned factor is the down-projection A [r,K], given as an ELL matrix
+ * (SRA_FMT_ELL, rows = r, cols = K, k entries per row at ascending columns, as sra_compress_ffi
+ * writes it); B [N,r] stays dense.  With A_s = A scattered to its columns:
+ *     forward   U = X A_s^T,  Y = X Ws^T + U B^T
+ *     backward  dU = dY B,  dB = dY^T U,  dX = dY P^T + dU A_s,
+ *               dA_values[j][i] = sum_t dU[t][j] X[t][col(j, i)]   (fp32, A's ELL order: only the
+ *               stored entries learn, their mask is fixed)
+ * Ws / P as for sra_sparse_lora_fwd / sra_sparse_lora_bwd (N:M or its streaming layout); bf16 only;
+ * A->dtype == the weight's dtype, A->cols == K, 1 <= A->rows <= 256, K % 8 == 0.  The workspace
+ * holds A_s densified (r x K bf16) and, for dA, the dense fp32 r x K gradient before its gather;
+ * sizes from sra_ffa_fwd_workspace / sra_ffa_bwd_workspace.  Flags as for sra_sparse_lora_bwd
+ * (SRA_GRAD_DA selects dA_values).  Errors as for the dense-adapter calls.
+ */
+sra_status sra_ffa_fwd_workspace(const sra_sparse* Ws /* host */, int64_t T,
+                                 const sra_sparse* A /* host */, size_t* bytes /* host */);
+sra_status sra_sparse_lora_fwd_ffa(const sra_sparse* Ws /* host */, const void* X, int64_t T,
+                                   const sra_sparse* A /* host */, const void* B, void* Y,
+                                   float* U_out, void* ws, size_t ws_bytes, void* stream);
+sra_status sra_ffa_bwd_workspace(const sra_sparse* P /* host */, int64_t T,
+                                 const sra_sparse* A /* host */, uint32_t flags,
+                                 size_t* bytes /* host */);
+sra_status sra_sparse_lora_bwd_ffa(const sra_sparse* P /* host */, const void* dY, const void* X,
+                                   int64_t T, const float* U, const sra_sparse* A /* host */,
+                                   const void* B, uint32_t flags, void* dX, float* dA_values,
+                                   float* dB, float* dU_out, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/*
  * sparse_lora_bwd_noalloc -- sra_sparse_lora_bwd with no workspace argument and no allocation,
  * for callers that cannot allocate device memory (code under HIP graph capture, tight serving or
  * training loops, harnesses that forbid hipMalloc).  Same arguments, same kernels and the same

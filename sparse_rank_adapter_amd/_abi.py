@@ -22,6 +22,7 @@ EXPORTS = (
     "sra_masked_weight_grad", "sra_nm_axpby",
     "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
     "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_sparse_lora_bwd_noalloc",
+    "sra_ffa_fwd_workspace", "sra_sparse_lora_fwd_ffa", "sra_ffa_bwd_workspace", "sra_sparse_lora_bwd_ffa",
     "sra_time_next_kernel",
 )
 SRA_KERNEL_COMPRESS, SRA_KERNEL_DOUBLE_PRUNE, SRA_KERNEL_SPMM24 = 1, 2, 3
@@ -76,6 +77,13 @@ def load(path: str = LIB_PATH):
         "sra_sparse_lora_bwd_noalloc": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                                   c_void_p, c_int32, c_uint32, c_void_p, c_void_p,
                                                   c_void_p, c_void_p, c_void_p]),
+        "sra_ffa_fwd_workspace": (c_int32, [P, c_int64, P, POINTER(c_size_t)]),
+        "sra_sparse_lora_fwd_ffa": (c_int32, [P, c_void_p, c_int64, P, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_size_t, c_void_p]),
+        "sra_ffa_bwd_workspace": (c_int32, [P, c_int64, P, c_uint32, POINTER(c_size_t)]),
+        "sra_sparse_lora_bwd_ffa": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, P, c_void_p,
+                                              c_uint32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_size_t, c_void_p]),
         "sra_time_next_kernel": (c_int32, [c_int32, c_void_p, c_void_p]),
     }
     assert set(sig) == set(EXPORTS)

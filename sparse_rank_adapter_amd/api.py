@@ -445,3 +445,117 @@ def sparse_lora_bwd(P: SparseMatrix, dY: torch.Tensor, X: torch.Tensor | None = 
         _p(B) if r else None, r, flags, _p(out.get("dX")), _p(out.get("dA")), _p(out.get("dB")),
         _p(out.get("dU")), _p(ws), ws.numel(), _stream(dev)))
     return out
+
+
+def _check_ffa_factor(A: SparseMatrix, K: int, dt, dev):
+    if not isinstance(A, SparseMatrix) or A.fmt != SRA_FMT_ELL:
+        raise ValueError("A must be an ELL SparseMatrix (compress_ffi of the dense factor)")
+    if A.cols != K or A.dtype != dt:
+        raise ValueError(f"A must be [r, {K}] of dtype {dt}, got [{A.rows}, {A.cols}] {A.dtype}")
+    d = _check_sparse(A, "A")
+    if d != dev:
+        raise ValueError(f"A is on {d}, expected {dev}")
+    return A.rows
+
+
+def sparse_lora_fwd_ffa(Ws: SparseMatrix, X: torch.Tensor, A: SparseMatrix, B: torch.Tensor,
+                        Y: torch.Tensor | None = None, U: torch.Tensor | None = None,
+                        want_u: bool = True, ws: torch.Tensor | None = None):
+    """Y = X Ws^T + (X A_s^T) B^T with a fixed-fan-in adapter factor A (ELL [r, K]).
+    Returns (Y, U) with U fp32 [T, r] (None when not wanted)."""
+    lib = load()
+    dev = _check_sparse(Ws, "Ws")
+    N, K, dt = Ws.rows, Ws.cols, Ws.dtype
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError("X must be a 2-D tensor [T, K]")
+    T = X.shape[0]
+    _arg(X, "X", (T, K), dt, dev)
+    r = _check_ffa_factor(A, K, dt, dev)
+    _arg(B, "B", (N, r), dt, dev)
+    if Y is None:
+        Y = torch.empty((T, N), dtype=dt, device=dev)
+    _arg(Y, "Y", (T, N), dt, dev)
+    if U is None and want_u:
+        U = torch.empty((T, r), dtype=torch.float32, device=dev)
+    if U is not None:
+        _arg(U, "U", (T, r), torch.float32, dev)
+    dw, da = Ws.desc(), A.desc()
+    nbytes = ctypes.c_size_t()
+    check("sra_ffa_fwd_workspace", lib.sra_ffa_fwd_workspace(ctypes.byref(dw), T, ctypes.byref(da),
+                                                             ctypes.byref(nbytes)))
+    if ws is None or ws.numel() < nbytes.value:
+        ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
+    _arg(ws, "ws", (ws.numel(),), torch.uint8, dev)
+    check("sra_sparse_lora_fwd_ffa", lib.sra_sparse_lora_fwd_ffa(
+        ctypes.byref(dw), _p(X), T, ctypes.byref(da), _p(B), _p(Y), _p(U), _p(ws), ws.numel(),
+        _stream(dev)))
+    return Y, U
+
+
+def sparse_lora_bwd_ffa(P: SparseMatrix, dY: torch.Tensor, X: torch.Tensor | None,
+                        U: torch.Tensor | None, A: SparseMatrix, B: torch.Tensor, dx: bool = True,
+                        da: bool = True, db: bool = True, dx_adapter: bool = True,
+                        want_du: bool = False, ws: torch.Tensor | None = None,
+                        out: dict | None = None):
+    """Double-pruned backward with a fixed-fan-in adapter factor A (ELL [r, K]).  Returns dict with
+    dX, dA_values (fp32 [r, k], A's ELL order), dB (and dU when want_du)."""
+    lib = load()
+    dev = _check_sparse(P, "P")
+    K, N, dt = P.rows, P.cols, P.dtype
+    if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
+        raise ValueError("dY must be a 2-D tensor [T, N]")
+    T = dY.shape[0]
+    _arg(dY, "dY", (T, N), dt, dev)
+    r = _check_ffa_factor(A, K, dt, dev)
+    _arg(B, "B", (N, r), dt, dev)
+    if U is not None:
+        _arg(U, "U", (T, r), torch.float32, dev)
+    if X is not None:
+        _arg(X, "X", (T, K), dt, dev)
+    elif da or (db and U is None):
+        raise ValueError("X is needed for dA, and for dB when U is not given")
+    flags = (SRA_GRAD_DX if dx else 0) | (SRA_GRAD_DA if da else 0) | (SRA_GRAD_DB if db else 0)
+    if not dx_adapter:
+        flags |= SRA_DX_NO_ADAPTER
+    out = dict(out or {})
+    if dx and out.get("dX") is None:
+        out["dX"] = torch.empty((T, K), dtype=dt, device=dev)
+    if da and out.get("dA_values") is None:
+        out["dA_values"] = torch.empty((r, A.k), dtype=torch.float32, device=dev)
+    if db and out.get("dB") is None:
+        out["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev)
+    if want_du and out.get("dU") is None:
+        out["dU"] = torch.empty((T, r), dtype=torch.float32, device=dev)
+    for key, shape, odt in (("dX", (T, K), dt), ("dA_values", (r, A.k), torch.float32),
+                            ("dB", (N, r), torch.float32), ("dU", (T, r), torch.float32)):
+        if out.get(key) is not None:
+            _arg(out[key], f"out['{key}']", shape, odt, dev)
+    dp, da_ = P.desc(), A.desc()
+    nbytes = ctypes.c_size_t()
+    check("sra_ffa_bwd_workspace", lib.sra_ffa_bwd_workspace(ctypes.byref(dp), T, ctypes.byref(da_),
+                                                             flags, ctypes.byref(nbytes)))
+    if ws is None or ws.numel() < nbytes.value:
+        ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
+    _arg(ws, "ws", (ws.numel(),), torch.uint8, dev)
+    check("sra_sparse_lora_bwd_ffa", lib.sra_sparse_lora_bwd_ffa(
+        ctypes.byref(dp), _p(dY), _p(X), T, _p(U), ctypes.byref(da_), _p(B), flags,
+        _p(out.get("dX")), _p(out.get("dA_values")), _p(out.get("dB")), _p(out.get("dU")), _p(ws),
+        ws.numel(), _stream(dev)))
+    return out
+
+
+def ffa_fwd_workspace(Ws: SparseMatrix, T: int, A: SparseMatrix) -> int:
+    n = ctypes.c_size_t()
+    dw, da = Ws.desc(), A.desc()
+    check("sra_ffa_fwd_workspace", load().sra_ffa_fwd_workspace(ctypes.byref(dw), T, ctypes.byref(da),
+                                                                ctypes.byref(n)))
+    return n.value
+
+
+def ffa_bwd_workspace(P: SparseMatrix, T: int, A: SparseMatrix,
+                      flags: int = SRA_GRAD_DX | SRA_GRAD_DA | SRA_GRAD_DB) -> int:
+    n = ctypes.c_size_t()
+    dp, da = P.desc(), A.desc()
+    check("sra_ffa_bwd_workspace", load().sra_ffa_bwd_workspace(ctypes.byref(dp), T, ctypes.byref(da),
+                                                                flags, ctypes.byref(n)))
+    return n.value

@@ -765,6 +765,99 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
   return SRA_OK;
 }
 
+// ---------------------------------------------------------------- fixed-fan-in adapter factor
+// A [r, K] as ELL: densified into the workspace, then the dense-adapter path; dA is gathered at
+// A's stored columns from the dense fp32 gradient.
+static sra_status check_ffa(const sra_sparse* A, const sra_sparse* S, int64_t K) {
+  SRA_TRY(check_sparse(A, "A"));
+  if (A->format != SRA_FMT_ELL) return fail(SRA_ERR_INVALID_ARG, "A must be an ELL matrix (fixed fan-in)");
+  if (A->dtype != SRA_BF16 || S->dtype != SRA_BF16)
+    return fail(SRA_ERR_UNSUPPORTED, "the fixed-fan-in adapter factor is bf16 only");
+  if (A->cols != K) return fail(SRA_ERR_INVALID_ARG, "A has %lld columns, the layer has K = %lld",
+                                (long long)A->cols, (long long)K);
+  if (A->rows < 1 || A->rows > 256) return fail(SRA_ERR_UNSUPPORTED, "adapter rank %lld outside [1, 256]", (long long)A->rows);
+  if (K % 8) return fail(SRA_ERR_UNSUPPORTED, "K %% 8 != 0");
+  return SRA_OK;
+}
+
+static size_t ffa_dense_bytes(const sra_sparse* A) { return ((size_t)A->rows * A->cols * 2 + 255) & ~(size_t)255; }
+static size_t ffa_grad_bytes(const sra_sparse* A) { return ((size_t)A->rows * A->cols * 4 + 255) & ~(size_t)255; }
+
+sra_status sra_ffa_fwd_workspace(const sra_sparse* Ws, int64_t T, const sra_sparse* A, size_t* bytes) {
+  SRA_TRY(validate_fwd(Ws, T, A ? (int32_t)std::min<int64_t>(A->rows, 256) : 0));
+  SRA_TRY(check_ffa(A, Ws, Ws->cols));
+  if (!bytes) return fail(SRA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ffa_dense_bytes(A) + fwd_bytes(Ws, T, (int32_t)A->rows, /*own_u=*/true, nullptr);
+  return SRA_OK;
+}
+
+sra_status sra_sparse_lora_fwd_ffa(const sra_sparse* Ws, const void* X, int64_t T, const sra_sparse* A,
+                                   const void* B, void* Y, float* U_out, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  SRA_TRY(validate_fwd(Ws, T, A ? (int32_t)std::min<int64_t>(A->rows, 256) : 0));
+  SRA_TRY(check_ffa(A, Ws, Ws->cols));
+  const int32_t r = (int32_t)A->rows;
+  const size_t head = ffa_dense_bytes(A);
+  const size_t need = head + fwd_bytes(Ws, T, r, U_out == nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(SRA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (!al16(ws)) return fail(SRA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const int64_t N = Ws->rows, K = Ws->cols;
+  SRA_TRY(check_ptr(X, T > 0 && K > 0, "X"));
+  SRA_TRY(check_ptr(Y, T > 0 && N > 0, "Y"));
+  SRA_TRY(check_ptr(B, T > 0 && N > 0, "B"));
+  if (U_out) SRA_TRY(check_ptr(U_out, true, "U_out"));
+  if (T == 0) return SRA_OK;
+  const hipStream_t s = (hipStream_t)stream;
+  uint16_t* Ad = (uint16_t*)ws;
+  SRA_TRY(hip_done(sra::launch_ffi_densify(SRA_FMT_ELL, (const uint16_t*)A->values, A->index, nullptr,
+                                           A->k, r, K, Ad, s), s, "fwd A densify"));
+  return sra_sparse_lora_fwd(Ws, X, T, Ad, B, r, Y, U_out, (uint8_t*)ws + head, ws_bytes - head, stream);
+}
+
+sra_status sra_ffa_bwd_workspace(const sra_sparse* P, int64_t T, const sra_sparse* A, uint32_t flags,
+                                 size_t* bytes) {
+  SRA_TRY(validate_bwd(P, T, A ? (int32_t)std::min<int64_t>(A->rows, 256) : 0, flags));
+  SRA_TRY(check_ffa(A, P, P->rows));
+  if (!bytes) return fail(SRA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ffa_dense_bytes(A) + ((flags & SRA_GRAD_DA) ? ffa_grad_bytes(A) : 0) +
+           bwd_bytes(P, T, (int32_t)A->rows, flags, /*have_u=*/false, /*have_du=*/false, nullptr);
+  return SRA_OK;
+}
+
+sra_status sra_sparse_lora_bwd_ffa(const sra_sparse* P, const void* dY, const void* X, int64_t T,
+                                   const float* U, const sra_sparse* A, const void* B, uint32_t flags,
+                                   void* dX, float* dA_values, float* dB, float* dU_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  SRA_TRY(validate_bwd(P, T, A ? (int32_t)std::min<int64_t>(A->rows, 256) : 0, flags));
+  SRA_TRY(check_ffa(A, P, P->rows));
+  const int32_t r = (int32_t)A->rows;
+  const int64_t K = P->rows;
+  const bool fda = flags & SRA_GRAD_DA;
+  const size_t head = ffa_dense_bytes(A), gbytes = fda ? ffa_grad_bytes(A) : 0;
+  uint16_t* Ad = ws ? (uint16_t*)ws : nullptr;
+  float* dA_dense = (ws && fda) ? (float*)((uint8_t*)ws + head) : nullptr;
+  BwdPlan plan;
+  // every check of the dense-adapter call, with the densified factor and the dense dA in place
+  SRA_TRY(check_bwd_args(P, dY, X, T, U, Ad ? Ad : (const void*)16, B, r, flags, dX,
+                         fda ? (dA_dense ? dA_dense : (const float*)16) : nullptr, dB, dU_out, &plan));
+  SRA_TRY(check_ptr(dA_values, fda, "dA_values"));
+  const size_t need = head + gbytes + plan.total;
+  if (!ws || ws_bytes < need)
+    return fail(SRA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (!al16(ws)) return fail(SRA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  if (T > 0)
+    SRA_TRY(hip_done(sra::launch_ffi_densify(SRA_FMT_ELL, (const uint16_t*)A->values, A->index, nullptr,
+                                             A->k, r, K, Ad, s), s, "bwd A densify"));
+  SRA_TRY(sra_sparse_lora_bwd(P, dY, X, T, U, Ad, B, r, flags, dX, dA_dense, dB, dU_out,
+                              (uint8_t*)ws + head + gbytes, ws_bytes - head - gbytes, stream));
+  if (fda)
+    SRA_TRY(hip_done(sra::launch_ell_gather_f32(dA_dense, A->index, A->k, r, K, dA_values, s), s,
+                     "bwd dA gather"));
+  return SRA_OK;
+}
+
 // Allocation-free backward: the workspace is this fixed device array.  In host code its name is
 // only a stand-in for the symbol; the device address comes from hipGetSymbolAddress, once per
 // device, and only that address is ever handed to kernels.

@@ -202,6 +202,13 @@ hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uin
 // fixed fan-in bf16 SpMM (ELL forward / CSR backward) with the same epilogue; with enough tokens
 // it densifies the weight into the workspace (spmm_ffi_ws bytes) and runs the dense MFMA kernel
 size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T);
+// An ELL (or CSR) matrix written out as R dense bf16 rows of C (C % 8 == 0, C <= 32767).
+hipError_t launch_ffi_densify(int format, const uint16_t* vals, const int16_t* idx,
+                              const int32_t* row_ptr, int k, int64_t R, int64_t C, uint16_t* out,
+                              hipStream_t s);
+// out[e] = dense[(e / k) * C + idx[e]] for the R * k entries of an ELL pattern (fp32).
+hipError_t launch_ell_gather_f32(const float* dense, const int16_t* idx, int k, int64_t R, int64_t C,
+                                 float* out, hipStream_t s);
 hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t* idx,
                                 const int32_t* row_ptr, int k, int64_t R, int64_t C,
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,

@@ -189,6 +189,15 @@ __global__ __launch_bounds__(256) void k_ffi_densify(int format, const uint16_t*
     *reinterpret_cast<u32x4*>(&Wd[n * C + c]) = *reinterpret_cast<const u32x4*>(&rowbuf[c]);
 }
 
+// The stored entries of an ELL pattern read out of a dense fp32 matrix, one thread per entry.
+__global__ __launch_bounds__(256) void k_ell_gather_f32(const float* __restrict__ dense,
+                                                        const int16_t* __restrict__ idx, int k,
+                                                        int64_t C, int64_t n, float* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  out[e] = dense[(e / k) * C + idx[e]];
+}
+
 // The densified product pays one pass writing R x C bf16 and then runs at dense MFMA rate; worth
 // it once the token tile is wide enough to reuse each weight row many times.
 bool use_dense(int64_t R, int64_t C, int64_t T) { return T >= 128 && C % 64 == 0 && C * 2 <= 65536 && R > 0; }
@@ -199,6 +208,24 @@ namespace sra {
 
 size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T) {
   return use_dense(R, C, T) ? (size_t)R * C * 2 : 0;
+}
+
+hipError_t launch_ffi_densify(int format, const uint16_t* vals, const int16_t* idx,
+                              const int32_t* row_ptr, int k, int64_t R, int64_t C, uint16_t* out,
+                              hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  launch(SRA_KERNEL_FFI_DENSIFY, k_ffi_densify, dim3((unsigned)R), dim3(256), (size_t)C * 2, s,
+         format, vals, idx, row_ptr, k, C, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ell_gather_f32(const float* dense, const int16_t* idx, int k, int64_t R, int64_t C,
+                                 float* out, hipStream_t s) {
+  const int64_t n = R * k;
+  if (n == 0) return hipSuccess;
+  launch(0, k_ell_gather_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dense, idx, k, C,
+         n, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t* idx,

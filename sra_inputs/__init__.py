@@ -38,6 +38,7 @@ class Workload:
     n: int = 2
     m: int = 4
     ffi_k: int = 0
+    adapter_k: int = 0   # > 0: the adapter's A keeps this many inputs per row (fixed fan-in)
     decode_T: tuple = field(default_factory=tuple)
     note: str = ""
 
@@ -52,6 +53,10 @@ WORKLOADS = {
     "opt66b_ffn_decode": Workload("opt66b_ffn_decode", T=16, K=9216, N=36864, r=64, dtype="bf16",
                                   fmt="nm", decode_T=(1, 4, 16),
                                   note="OPT-66B FFN up-projection, 2:4, rank 64, decode T=1,4,16"),
+    "squash_opt350m_fc2": Workload("squash_opt350m_fc2", T=2048, K=4096, N=1024, r=32, dtype="bf16",
+                                   fmt="nm", adapter_k=768,
+                                   note="OPT-350M fc2, 2:4, rank-32 adapter whose A keeps 768 of 4096 "
+                                        "inputs per row: the adapter bytes of a dense rank-16 one"),
     "opt13b_fc1": Workload("opt13b_fc1", T=8192, K=5120, N=20480, r=128, dtype="bf16", fmt="nm",
                            note="OPT-13B MLP fc1, 2:4, rank 128"),
     "opt13b_fc2": Workload("opt13b_fc2", T=8192, K=20480, N=5120, r=128, dtype="bf16", fmt="nm",

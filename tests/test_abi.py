@@ -274,6 +274,36 @@ def test_bwd_noalloc_host_checks(lib):
     assert _abi.SRA_NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
+def test_ffa_validation(lib):
+    """Fixed-fan-in adapter factor: A must be a bf16 ELL matrix over the layer's K."""
+    W = nm_desc(rows=1024, cols=4096)
+    A = ell_desc(rows=32, cols=4096, k=768)
+    n = ctypes.c_size_t()
+    assert lib.sra_ffa_fwd_workspace(ctypes.byref(W), 2048, ctypes.byref(A), ctypes.byref(n)) == SRA_OK
+    assert n.value >= 32 * 4096 * 2
+    bad = ell_desc(rows=32, cols=2048, k=768)
+    assert lib.sra_ffa_fwd_workspace(ctypes.byref(W), 2048, ctypes.byref(bad), ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    assert "columns" in err(lib)
+    assert lib.sra_ffa_fwd_workspace(ctypes.byref(W), 2048, ctypes.byref(nm_desc(rows=32, cols=4096)),
+                                     ctypes.byref(n)) == SRA_ERR_INVALID_ARG
+    big = ell_desc(rows=300, cols=4096, k=8)
+    assert lib.sra_ffa_fwd_workspace(ctypes.byref(W), 2048, ctypes.byref(big), ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    f32 = ell_desc(rows=32, cols=4096, k=768, dtype=SRA_F32)
+    assert lib.sra_ffa_fwd_workspace(ctypes.byref(W), 2048, ctypes.byref(f32), ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    lib.sra_ffa_fwd_workspace(ctypes.byref(W), 2048, ctypes.byref(A), ctypes.byref(n))
+    st = lib.sra_sparse_lora_fwd_ffa(ctypes.byref(W), FAKE, 2048, ctypes.byref(A), FAKE, FAKE, None,
+                                     FAKE, n.value - 256, None)
+    assert st == SRA_ERR_WORKSPACE
+    P = nm_desc(rows=4096, cols=1024)
+    assert lib.sra_ffa_bwd_workspace(ctypes.byref(P), 2048, ctypes.byref(A), 7, ctypes.byref(n)) == SRA_OK
+    st = lib.sra_sparse_lora_bwd_ffa(ctypes.byref(P), FAKE, FAKE, 2048, FAKE, ctypes.byref(A), FAKE, 7,
+                                     FAKE, None, FAKE, None, FAKE, n.value, None)
+    assert st == SRA_ERR_INVALID_ARG and "dA_values" in err(lib)
+    st = lib.sra_sparse_lora_bwd_ffa(ctypes.byref(P), FAKE, None, 2048, FAKE, ctypes.byref(A), FAKE, 7,
+                                     FAKE, FAKE, FAKE, None, FAKE, n.value, None)
+    assert st == SRA_ERR_INVALID_ARG and "X" in err(lib)
+
+
 def test_binding_fails_loudly_when_library_missing(tmp_path):
     saved = _abi._lib
     _abi._lib = None
