@@ -330,6 +330,43 @@ sra_status sra_masked_weight_grad(const sra_sparse* S /* host */, const void* ro
 sra_status sra_nm_axpby(const void* a_values, float beta, const void* b_values, float gamma,
                         void* out_values, int64_t n_values, int32_t dtype, void* stream);
 
+/*
+ * Tuning knobs of the calling thread, for benchmarks and tests (not needed for computing anything;
+ * every knob's default is the library's own choice, and results stay within the stated tolerance
+ * under any setting).  Returns SRA_ERR_INVALID_ARG for an unknown key or a value out of range.
+ *   SRA_TUNE_RESET         every knob back to its default (value ignored)
+ *   SRA_TUNE_SPMM_CONFIG   bf16 2:4 SpMM tile configuration for T > 16 (0 = the planner's); the
+ *                          decode path (T <= 16) ignores it.  Ids: 3 register-staged 128x128;
+ *                          13 and 14 LDS-DMA 128x128 and 128x64 (32x32x32 SMFMAC); 50, 51 eight-wave
+ *                          256x128, 256x256; 55 and 61 the same with metadata super-stages
+ *                          (C % 128 == 0); 62 = 61 in a ping-pong schedule.  A configuration the
+ *                          shape cannot take falls back to one it can.
+ *   SRA_TUNE_SPMM_SPLITS   splits of the reduction for a forced configuration (0 or 1: none;
+ *                          -2: only the 256x256 tiles past the last whole wave of 256, in two)
+ *   SRA_TUNE_SPMM_FUSE     1 (default): U / dU of ranks <= 16 inside the SpMM where the plan
+ *                          allows; 0: always in a separate kernel
+ *   SRA_TUNE_ENGINE        SRA_ENGINE_SMFMAC (default): 2:4 products on the structured-sparse
+ *                          matrix instructions; SRA_ENGINE_DENSE_MFMA: the same pipeline with each
+ *                          weight fragment expanded to dense bf16 (zeros at the pruned positions)
+ *                          for dense MFMA, the path 2:8 weights always take (bf16, K % 128 == 0
+ *                          for the forward, N % 128 == 0 for the backward)
+ *   SRA_TUNE_DECODE_ROWS   decode workgroup row tiles of 16 rows: 3, 4 or 9 (0 = the planner's)
+ *   SRA_TUNE_ROWS_SLICES   reduction slices of the rank > 32 U / dU kernel (0 = the planner's)
+ *   SRA_TUNE_GRADS_SLICES  token slices of the dA / dB kernel (0 = the planner's)
+ */
+enum {
+  SRA_TUNE_RESET = 0,
+  SRA_TUNE_SPMM_CONFIG = 1,
+  SRA_TUNE_SPMM_SPLITS = 2,
+  SRA_TUNE_SPMM_FUSE = 3,
+  SRA_TUNE_ENGINE = 4,
+  SRA_TUNE_DECODE_ROWS = 5,
+  SRA_TUNE_ROWS_SLICES = 6,
+  SRA_TUNE_GRADS_SLICES = 7
+};
+enum { SRA_ENGINE_SMFMAC = 0, SRA_ENGINE_DENSE_MFMA = 1 };
+sra_status sra_set_tuning(int32_t key, int32_t value);
+
 /* Kernel classes for sra_time_next_kernel. */
 enum {
   SRA_KERNEL_COMPRESS = 1,     /* 2:4 compression (sra_compress, sra_compress_pair) */

@@ -14,6 +14,9 @@ SRA_BF16, SRA_F32 = 0, 1
 SRA_FMT_NM, SRA_FMT_ELL, SRA_FMT_CSR, SRA_FMT_NM_TILED = 0, 1, 2, 3
 SRA_GRAD_DX, SRA_GRAD_DA, SRA_GRAD_DB, SRA_DX_NO_ADAPTER = 1, 2, 4, 8
 SRA_NOALLOC_SCRATCH_BYTES = 64 << 20
+SRA_TUNE_KEYS = {"spmm_config": 1, "spmm_splits": 2, "spmm_fuse": 3, "engine": 4, "decode_rows": 5,
+                 "rows_slices": 6, "grads_slices": 7}
+SRA_ENGINE_SMFMAC, SRA_ENGINE_DENSE_MFMA = 0, 1
 
 # every symbol include/sra.h declares
 EXPORTS = (
@@ -23,7 +26,7 @@ EXPORTS = (
     "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
     "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_sparse_lora_bwd_noalloc",
     "sra_ffa_fwd_workspace", "sra_sparse_lora_fwd_ffa", "sra_ffa_bwd_workspace", "sra_sparse_lora_bwd_ffa",
-    "sra_time_next_kernel",
+    "sra_time_next_kernel", "sra_set_tuning",
 )
 SRA_KERNEL_COMPRESS, SRA_KERNEL_DOUBLE_PRUNE, SRA_KERNEL_SPMM24 = 1, 2, 3
 SRA_KERNEL_ADAPTER, SRA_KERNEL_DECODE24, SRA_KERNEL_SPMM_FFI = 4, 5, 6
@@ -85,6 +88,7 @@ def load(path: str = LIB_PATH):
                                               c_uint32, c_void_p, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_size_t, c_void_p]),
         "sra_time_next_kernel": (c_int32, [c_int32, c_void_p, c_void_p]),
+        "sra_set_tuning": (c_int32, [c_int32, c_int32]),
     }
     assert set(sig) == set(EXPORTS)
     for name, (res, args) in sig.items():

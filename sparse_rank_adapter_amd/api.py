@@ -6,6 +6,7 @@ kernels.  Nothing here computes a result on the host.
 from __future__ import annotations
 
 import ctypes
+from contextlib import contextmanager
 from dataclasses import dataclass
 
 import torch
@@ -559,3 +560,32 @@ def ffa_bwd_workspace(P: SparseMatrix, T: int, A: SparseMatrix,
     check("sra_ffa_bwd_workspace", load().sra_ffa_bwd_workspace(ctypes.byref(dp), T, ctypes.byref(da),
                                                                 flags, ctypes.byref(n)))
     return n.value
+
+
+_ENGINES = {"smfmac": 0, "dense_mfma": 1}
+
+
+def set_tuning(**knobs) -> None:
+    """Tuning knobs of the calling thread (sra_set_tuning): spmm_config, spmm_splits, spmm_fuse,
+    engine ("smfmac" or "dense_mfma"), decode_rows, rows_slices, grads_slices."""
+    lib = load()
+    for k, v in knobs.items():
+        if k not in _abi.SRA_TUNE_KEYS:
+            raise ValueError(f"unknown tuning knob {k}")
+        if k == "engine" and isinstance(v, str):
+            v = _ENGINES[v]
+        check("sra_set_tuning", lib.sra_set_tuning(_abi.SRA_TUNE_KEYS[k], int(v)))
+
+
+def reset_tuning() -> None:
+    check("sra_set_tuning", load().sra_set_tuning(0, 0))
+
+
+@contextmanager
+def tuned(**knobs):
+    """Run a block with the given tuning knobs, then restore every knob to its default."""
+    set_tuning(**knobs)
+    try:
+        yield
+    finally:
+        reset_tuning()

@@ -23,6 +23,7 @@ SOURCES = [
     "ffi_format.hip",
     "f32_path.hip",
     "spmm24.hip",
+    "spmm_xp.hip",
     "decode24.hip",
     "adapter.hip",
     "spmm_ffi.hip",

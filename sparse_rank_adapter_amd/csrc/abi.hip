@@ -14,6 +14,7 @@ namespace {
 thread_local std::string g_err;
 thread_local int g_time_which = 0;
 thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+thread_local sra::Tuning g_tune;
 
 sra_status fail(sra_status st, const char* fmt, ...) {
   char buf[512];
@@ -66,9 +67,9 @@ sra_status check_ptr(const void* p, bool needed, const char* name) {
 
 sra_status check_nm(int64_t rows, int64_t cols, int n, int m) {
   if (rows < 0 || cols < 0) return fail(SRA_ERR_INVALID_ARG, "negative shape");
-  if (n < 1 || m < n || m > 4) return fail(SRA_ERR_INVALID_ARG, "invalid N:M %d:%d", n, m);
-  if (!((n == 2 && m == 4) || (n == 1 && m == 2)))
-    return fail(SRA_ERR_UNSUPPORTED, "only 2:4 and 1:2 are implemented (got %d:%d)", n, m);
+  if (n < 1 || m < n || (m > 4 && m != 8)) return fail(SRA_ERR_INVALID_ARG, "invalid N:M %d:%d", n, m);
+  if (!((n == 2 && m == 4) || (n == 1 && m == 2) || (n == 2 && m == 8)))
+    return fail(SRA_ERR_UNSUPPORTED, "only 2:4, 1:2 and 2:8 are implemented (got %d:%d)", n, m);
   if (cols % 32) return fail(SRA_ERR_UNSUPPORTED, "grouped dimension %lld is not a multiple of 32", (long long)cols);
   return SRA_OK;
 }
@@ -77,6 +78,12 @@ sra_status check_nm(int64_t rows, int64_t cols, int n, int m) {
 // the metadata becomes the 2:4 encoding when every odd field gains 2 (word | 0x88888888).
 constexpr uint32_t kMeta12To24 = 0x88888888u;
 bool is12(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 1 && S->m == 2; }
+bool is28(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 2 && S->m == 8; }
+// 2:8 weights, and bf16 2:4 weights on the dense-MFMA engine, run the expanded-fragment products
+bool use_xp(const sra_sparse* S) {
+  if (S->format != SRA_FMT_NM && S->format != SRA_FMT_NM_TILED) return false;
+  return is28(S) || (S->dtype == SRA_BF16 && sra::tuning().engine == SRA_ENGINE_DENSE_MFMA);
+}
 size_t meta_bytes(const sra_sparse* S) {
   return (size_t)S->rows * (size_t)sra_nm_meta_words(S->cols, S->n, S->m) * 4;
 }
@@ -88,6 +95,7 @@ sra_status check_sparse(const sra_sparse* S, const char* name) {
   const bool any = S->rows > 0 && S->cols > 0;
   if (S->format == SRA_FMT_NM) {
     SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
+    if (S->m == 8 && S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "%s: 2:8 is bf16 only", name);
     SRA_TRY(check_ptr(S->values, any, "values"));
     SRA_TRY(check_ptr(S->meta, any, "meta"));
   } else if (S->format == SRA_FMT_NM_TILED) {
@@ -155,6 +163,9 @@ sra_status validate_fwd(const sra_sparse* Ws, int64_t T, int32_t r) {
   if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
   if (Ws->format == SRA_FMT_NM && Ws->dtype == SRA_BF16 && Ws->cols == 0)
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 forward needs K > 0");
+  if (use_xp(Ws) && T > 0 && !sra::spmm_xp_ok(Ws->cols))
+    return fail(SRA_ERR_UNSUPPORTED, "%s products need K %% 128 == 0 (K = %lld)",
+                is28(Ws) ? "2:8" : "dense-MFMA 2:4", (long long)Ws->cols);
   return SRA_OK;
 }
 
@@ -166,7 +177,9 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
   if (Ws->dtype == SRA_F32 && r > 0) p.u64_off = a.take((size_t)T * r * 8);
   if (Ws->dtype == SRA_BF16) {
     size_t g = r > 0 ? sra::adapter_rows_ws(T, Ws->cols, r) : 0;
-    if (Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED)
+    if (use_xp(Ws))
+      g = std::max(g, sra::spmm_xp_ws(Ws->rows, Ws->cols, T));
+    else if (Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED)
       g = std::max(g, sra::spmm24_ws(Ws->rows, Ws->cols, T));
     p.gemm_off = a.take(g);
     if (Ws->format == SRA_FMT_ELL) p.ffi_off = a.take(sra::spmm_ffi_ws(Ws->rows, Ws->cols, T));
@@ -200,6 +213,9 @@ sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flag
   if (flags & ~15u) return fail(SRA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (P->format == SRA_FMT_NM && P->dtype == SRA_BF16 && (flags & SRA_GRAD_DX) && P->cols == 0)
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 dX needs N > 0");
+  if (use_xp(P) && (flags & SRA_GRAD_DX) && T > 0 && !sra::spmm_xp_ok(P->cols))
+    return fail(SRA_ERR_UNSUPPORTED, "%s dX needs N %% 128 == 0 (N = %lld)",
+                is28(P) ? "2:8" : "dense-MFMA 2:4", (long long)P->cols);
   return SRA_OK;
 }
 
@@ -259,7 +275,9 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
     g = std::max(g, sra::adapter_grads_ws(jobs, nj, T, r));
     p.gemm_off = a.take(g);
   }
-  if (P->dtype == SRA_BF16 && (P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED) && dx)
+  if (P->dtype == SRA_BF16 && use_xp(P) && dx)
+    p.spmm_off = a.take(sra::spmm_xp_ws(K, N, T));
+  else if (P->dtype == SRA_BF16 && (P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED) && dx)
     p.spmm_off = a.take(sra::spmm24_ws(K, N, T));
   if (P->dtype == SRA_BF16 && P->format == SRA_FMT_CSR && dx)
     p.spmm_off = a.take(sra::spmm_ffi_ws(K, N, T));
@@ -297,6 +315,8 @@ sra_status check_bwd_args(const sra_sparse* P, const void* dY, const void* X, in
 }  // namespace
 
 namespace sra {
+const Tuning& tuning() { return g_tune; }
+
 bool take_timing(int which, hipEvent_t* start, hipEvent_t* stop) {
   if (g_time_which == 0 || g_time_which != which) return false;
   *start = g_time_start;
@@ -323,12 +343,47 @@ sra_status sra_time_next_kernel(int32_t which, void* start, void* stop) {
 }
 
 
+sra_status sra_set_tuning(int32_t key, int32_t value) {
+  switch (key) {
+    case SRA_TUNE_RESET: g_tune = sra::Tuning{}; return SRA_OK;
+    case SRA_TUNE_SPMM_CONFIG:
+      if (value < 0 || value > 99) return fail(SRA_ERR_INVALID_ARG, "SpMM configuration %d out of range", value);
+      g_tune.spmm_cfg = value;
+      return SRA_OK;
+    case SRA_TUNE_SPMM_SPLITS:
+      if (value < -2 || value == -1 || value > 64) return fail(SRA_ERR_INVALID_ARG, "splits %d out of range", value);
+      g_tune.spmm_splits = value;
+      return SRA_OK;
+    case SRA_TUNE_SPMM_FUSE:
+      if (value != 0 && value != 1) return fail(SRA_ERR_INVALID_ARG, "fuse must be 0 or 1");
+      g_tune.spmm_fuse = value;
+      return SRA_OK;
+    case SRA_TUNE_ENGINE:
+      if (value != SRA_ENGINE_SMFMAC && value != SRA_ENGINE_DENSE_MFMA)
+        return fail(SRA_ERR_INVALID_ARG, "unknown engine %d", value);
+      g_tune.engine = value;
+      return SRA_OK;
+    case SRA_TUNE_DECODE_ROWS:
+      if (value != 0 && value != 3 && value != 4 && value != 9)
+        return fail(SRA_ERR_INVALID_ARG, "decode row tiles must be 0, 3, 4 or 9");
+      g_tune.decode_rows = value;
+      return SRA_OK;
+    case SRA_TUNE_ROWS_SLICES:
+    case SRA_TUNE_GRADS_SLICES:
+      if (value < 0 || value > 1024) return fail(SRA_ERR_INVALID_ARG, "slices %d out of range", value);
+      (key == SRA_TUNE_ROWS_SLICES ? g_tune.rows_slices : g_tune.grads_slices) = value;
+      return SRA_OK;
+    default: return fail(SRA_ERR_INVALID_ARG, "unknown tuning key %d", key);
+  }
+}
+
 int32_t sra_abi_version(void) { return SRA_ABI_VERSION; }
 
 const char* sra_last_error(void) { return g_err.c_str(); }
 
 int64_t sra_nm_meta_words(int64_t cols, int32_t n, int32_t m) {
   if (m <= 0 || n <= 0 || cols < 0) return 0;
+  if (m == 8) return (cols / 8 + 3) / 4;  // one byte per 8-column group
   const int64_t fields = cols / m * n;
   return (fields + 15) / 16;
 }
@@ -349,6 +404,11 @@ sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols
   out->n = n;
   out->m = m;
   const hipStream_t s = (hipStream_t)stream;
+  if (m == 8) {
+    if (dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "2:8 is bf16 only");
+    return hip_done(sra::launch_compress28((const uint16_t*)W, rows, cols, (uint16_t*)out->values,
+                                           out->meta, s), s, "compress 2:8");
+  }
   if (n == 1)
     return hip_done(sra::launch_compress12(dtype, W, rows, cols, out->values, out->meta, s), s, "compress 1:2");
   return hip_done(sra::launch_compress24(dtype, W, rows, cols, out->values, out->meta, s), s, "compress");
@@ -369,6 +429,10 @@ sra_status sra_double_prune(const sra_sparse* Ws, sra_sparse* P, void* stream) {
   P->n = Ws->n;
   P->m = Ws->m;
   const hipStream_t s = (hipStream_t)stream;
+  if (is28(Ws))
+    return hip_done(sra::launch_double_prune28((const uint16_t*)Ws->values, Ws->meta, Ws->rows, Ws->cols,
+                                               (uint16_t*)P->values, P->meta, s),
+                    s, "double_prune 2:8");
   if (is12(Ws))
     return hip_done(sra::launch_double_prune12(Ws->dtype, Ws->values, Ws->meta, Ws->rows, Ws->cols,
                                                P->values, P->meta, s),
@@ -383,6 +447,7 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
   SRA_TRY(check_dtype(dtype));
   SRA_TRY(check_nm(rows, cols, n, m));
   SRA_TRY(check_nm(cols, rows, n, m));  // the second prune groups along rows
+  if (m == 8) return fail(SRA_ERR_UNSUPPORTED, "compress_pair: 2:8 runs as sra_compress + sra_double_prune");
   if (!Ws || !P) return fail(SRA_ERR_INVALID_ARG, "output descriptor is NULL");
   const bool any = rows > 0 && cols > 0;
   SRA_TRY(check_ptr(W, any, "W"));
@@ -446,6 +511,7 @@ sra_status sra_masked_weight_grad(const sra_sparse* S, const void* row_act, cons
   if (S->format != SRA_FMT_NM) return fail(SRA_ERR_INVALID_ARG, "masked_weight_grad needs a canonical N:M matrix");
   SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
   if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad is bf16 only");
+  if (is28(S)) return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad is 2:4 and 1:2 only");
   if (S->rows % 8) return fail(SRA_ERR_UNSUPPORTED, "masked_weight_grad needs rows %% 8 == 0");
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
   if (!sra::sddmm24_fits(S->rows, S->cols, T))
@@ -487,7 +553,7 @@ sra_status sra_nm_tile(const sra_sparse* Ws, sra_sparse* out, void* stream) {
   SRA_TRY(check_sparse(Ws, "Ws"));
   if (Ws->format != SRA_FMT_NM) return fail(SRA_ERR_INVALID_ARG, "nm_tile needs a canonical N:M weight");
   if (Ws->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout is bf16 only");
-  if (is12(Ws)) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 only");
+  if (is12(Ws) || is28(Ws)) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 only");
   if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
   const bool any = Ws->rows > 0 && Ws->cols > 0;
   SRA_TRY(check_ptr(out->values, any, "out values"));
@@ -603,7 +669,9 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
   }
   // U = X A^T: computed inside the SpMM when its plan allows, else by the adapter kernel first
   const bool nm24 = Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED;
-  const bool fuse = r > 0 && nm24 && sra::spmm24_fuses_adapter(N, K, T, r);
+  const bool xp = use_xp(Ws);
+  const bool fuse = r > 0 && nm24 && (xp ? sra::spmm_xp_fuses_adapter(N, K, T, r)
+                                         : sra::spmm24_fuses_adapter(N, K, T, r));
   if (r > 0 && !fuse)
     SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)X, T, K, (const uint16_t*)A, K, r, U,
                                               nullptr, nullptr, wsb + plan.gemm_off, s), s, "fwd U"));
@@ -618,6 +686,12 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     ep.g_ld = K;
     ep.u_out = U_out;
   }
+  if (xp)
+    return hip_done(sra::launch_spmm_xp_bf16(is28(Ws) ? 28 : 24, Ws->format == SRA_FMT_NM_TILED,
+                                             (const uint16_t*)Ws->values, Ws->meta, N, K,
+                                             (const uint16_t*)X, T, ep, (uint16_t*)Y,
+                                             wsb ? wsb + plan.gemm_off : nullptr, s),
+                    s, is28(Ws) ? "fwd spmm 2:8" : "fwd spmm 2:4 (dense MFMA)");
   if (Ws->format == SRA_FMT_NM_TILED)
     return hip_done(sra::launch_spmm24_tiled_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
                                                   (const uint16_t*)X, T, ep, (uint16_t*)Y,
@@ -708,7 +782,9 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
   // dU = dY B: computed inside the dX SpMM (which also writes dU_out and dU^T's parts for dA)
   // when its plan allows, else by the adapter kernel first
   const bool nm24 = P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED;
-  const bool fuse = dx_ad && nm24 && sra::spmm24_fuses_adapter(K, N, T, r);
+  const bool xp = use_xp(P);
+  const bool fuse = dx_ad && nm24 && (xp ? sra::spmm_xp_fuses_adapter(K, N, T, r)
+                                         : sra::spmm24_fuses_adapter(K, N, T, r));
   if (plan.need_du && !fuse)
     SRA_TRY(hip_done(sra::launch_adapter_rows((const uint16_t*)dY, T, N, wt, sra::packed_wt_ld(N), r,
                                               dU, nullptr, vtdU, gws, s), s, "bwd dU"));
@@ -727,7 +803,13 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
       ep.vt_rp = (int)sra::vt_rows(r);
       ep.vt_tp = sra::vt_cols(T);
     }
-    if (P->format == SRA_FMT_NM_TILED)
+    if (xp)
+      SRA_TRY(hip_done(sra::launch_spmm_xp_bf16(is28(P) ? 28 : 24, P->format == SRA_FMT_NM_TILED,
+                                                (const uint16_t*)P->values, P->meta, K, N,
+                                                (const uint16_t*)dY, T, ep, (uint16_t*)dX,
+                                                wsb ? wsb + plan.spmm_off : nullptr, s),
+                       s, is28(P) ? "bwd dX 2:8" : "bwd dX 2:4 (dense MFMA)"));
+    else if (P->format == SRA_FMT_NM_TILED)
       SRA_TRY(hip_done(sra::launch_spmm24_tiled_bf16((const uint16_t*)P->values, P->meta, K, N,
                                                      (const uint16_t*)dY, T, ep, (uint16_t*)dX,
                                                      wsb ? wsb + plan.spmm_off : nullptr, s),

@@ -1153,8 +1153,7 @@ RingPlan ring_plan(int64_t T, int64_t C, int r) {
   p.jr = r <= 64 ? 64 : 128;
   const int64_t blocks = cdiv(T, 128) * cdiv(r, p.jr);
   int64_t S = cdiv(256, blocks);
-  const char* env = getenv("SRA_ROWS_S");  // tuning override
-  if (env && *env) S = atoi(env);
+  if (tuning().rows_slices > 0) S = tuning().rows_slices;
   const int64_t max_s = C / 256 > 0 ? C / 256 : 1;
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;
@@ -1285,8 +1284,7 @@ GradsPlan grads_plan(const AdapterGrad* g, int n, int64_t T, int r) {
       if (cost < best - 1e-9) best = cost, S = c;
     }
   }
-  const char* env = getenv("SRA_GRADS_S");  // tuning override
-  if (env && *env) S = atoi(env);
+  if (tuning().grads_slices > 0) S = tuning().grads_slices;
   const int64_t max_s = cdiv(T, 256);
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;

@@ -84,6 +84,19 @@ SRA_DEV void ring_barrier() {
 // ---- host-side launchers implemented in the kernel sources (internal C++ linkage)
 namespace sra {
 
+// Tuning knobs of the calling thread (sra_set_tuning); zero / default values mean the planners'
+// own choices.
+struct Tuning {
+  int spmm_cfg = 0;     // forced 2:4 SpMM configuration id (T > 16)
+  int spmm_splits = 0;  // its reduction splits; -2 = tail split in two
+  int spmm_fuse = 1;    // in-kernel U / dU allowed
+  int engine = 0;       // SRA_ENGINE_SMFMAC or SRA_ENGINE_DENSE_MFMA
+  int decode_rows = 0;  // decode row tiles per workgroup (3, 4 or 9)
+  int rows_slices = 0;  // reduction slices of the rank > 32 rows kernel
+  int grads_slices = 0; // token slices of the adapter gradient kernel
+};
+const Tuning& tuning();
+
 // Profiling hook (sra_time_next_kernel): returns true, and the events, exactly once after the
 // calling thread armed kernel class `which`.
 bool take_timing(int which, hipEvent_t* start, hipEvent_t* stop);
@@ -120,6 +133,11 @@ hipError_t launch_compress12(int dtype, const void* W, int64_t rows, int64_t col
 hipError_t launch_double_prune12(int dtype, const void* vals, const uint32_t* meta, int64_t rows,
                                  int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s);
 hipError_t launch_meta_or(const uint32_t* in, uint32_t* out, int64_t n, uint32_t bits, hipStream_t s);
+// 2:8 (bf16): one 3-bit field per kept value, the two of a group in one byte, 4 groups per word
+hipError_t launch_compress28(const uint16_t* W, int64_t rows, int64_t cols, uint16_t* vals, uint32_t* meta,
+                             hipStream_t s);
+hipError_t launch_double_prune28(const uint16_t* vals, const uint32_t* meta, int64_t rows, int64_t cols,
+                                 uint16_t* p_vals, uint32_t* p_meta, hipStream_t s);
 // bf16 compress + double prune with both outputs in the streaming layout (rows, cols % 128 == 0)
 hipError_t launch_compress_pair24_tiled(const uint16_t* W, int64_t rows, int64_t cols, void* vals,
                                         uint32_t* meta, void* p_vals, uint32_t* p_meta, hipStream_t s);
@@ -177,6 +195,14 @@ struct Epilogue {
 // the caller then skips the separate U kernel.
 bool spmm24_fuses_adapter(int64_t R, int64_t C, int64_t T, int r);
 size_t spmm24_ws(int64_t R, int64_t C, int64_t T);
+// The same products with the weight fragments expanded to dense bf16 for dense MFMA (spmm_xp.hip):
+// nm = 28 (2:8, canonical arrays) or 24 (2:4, canonical or streaming layout); C % 128 == 0.
+bool spmm_xp_ok(int64_t C);
+bool spmm_xp_fuses_adapter(int64_t R, int64_t C, int64_t T, int r);
+size_t spmm_xp_ws(int64_t R, int64_t C, int64_t T);
+hipError_t launch_spmm_xp_bf16(int nm, bool tiled, const uint16_t* s_vals, const uint32_t* s_meta,
+                               int64_t R, int64_t C, const uint16_t* act, int64_t T,
+                               const Epilogue& ep, uint16_t* out, void* ws, hipStream_t s);
 hipError_t launch_spmm24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                               const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
                               void* ws, hipStream_t s);

@@ -531,9 +531,146 @@ __global__ void k_meta_or(const uint32_t* __restrict__ in, uint32_t* __restrict_
     out[i] = in[i] | bits;
 }
 
+// ---------------------------------------------------------------- 2:8 (bf16)
+// Each 8-column group keeps its two largest magnitudes (ties: the lower position); positions are
+// 3-bit fields, the two of a group in one byte (first at bits 0-2, second at 3-5), 4 groups per
+// metadata word, values in ascending position order.
+
+// positions p0 < p1 of the two largest of eight keys (k < 2^28; ties: the lower position wins)
+SRA_DEV void top2_of8(const uint32_t k[8], uint32_t& p0, uint32_t& p1) {
+  uint32_t K[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) K[j] = (k[j] << 3) | (uint32_t)(7 - j);  // distinct folded keys
+  uint32_t first = K[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) first = max(first, K[j]);
+  uint32_t second = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) second = max(second, K[j] == first ? 0u : K[j]);
+  const uint32_t pa = 7u - (first & 7u), pb = 7u - (second & 7u);
+  p0 = min(pa, pb);
+  p1 = max(pa, pb);
+}
+
+// the word of a group's four words w[0..3] that holds position p (branch-free select)
+SRA_DEV uint32_t word_at(const uint32_t w[4], uint32_t p) {
+  const uint32_t q = p >> 1;
+  const uint32_t a = (q & 1u) ? w[1] : w[0], b = (q & 1u) ? w[3] : w[2];
+  return (q & 2u) ? b : a;
+}
+
+// One lane per 32-column block of a row: 4 groups -> 8 kept values (16 bytes) + one metadata word.
+__global__ __launch_bounds__(256) void k_compress28(const uint16_t* __restrict__ W, int64_t rows,
+                                                    int64_t words_per_row, uint16_t* __restrict__ vals,
+                                                    uint32_t* __restrict__ meta) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows * words_per_row) return;
+  const int64_t row = id / words_per_row, w = id - row * words_per_row;
+  const int64_t cols = words_per_row * 32;
+  union { u32x4 v[4]; uint32_t w[16]; } x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(W + row * cols + w * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x.v[i] = src[i];
+  union { u32x4 v; uint32_t w[4]; } o;
+  uint32_t word = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t* gw = &x.w[4 * g];
+    uint32_t key[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) key[a] = (gw[a >> 1] >> (16 * (a & 1))) & 0x7FFFu;
+    uint32_t p0, p1;
+    top2_of8(key, p0, p1);
+    const uint32_t lo = word_at(gw, p0), hi = word_at(gw, p1);
+    const uint32_t sel = ((p0 & 1u) * 0x0202u + 0x0100u) | (((p1 & 1u) * 0x0202u + 0x0504u) << 16);
+    o.w[g] = __builtin_amdgcn_perm(hi, lo, sel);
+    word |= (p0 | (p1 << 3)) << (8 * g);
+  }
+  *reinterpret_cast<u32x4*>(vals + row * (cols / 4) + w * 8) = o.v;
+  meta[row * words_per_row + w] = word;
+}
+
+// The second prune at 2:8 on 128-row x 64-column tiles of Ws: the tile's first-prune output is
+// expanded into LDS (positions the first prune dropped hold the mark 0xFFFF), then each lane ranks
+// four 8-row groups of one input column.  Keys: 0 for a dropped position, |w| + 1 for a kept one,
+// with the position folded in as for the first prune, so the two largest are the kept entries by
+// (|w| desc, row asc) and, when fewer than two were kept, the lowest unused positions (stored as
+// +0.0).  P row k receives, per tile, 4 lanes x (8 values, 1 metadata word).
+constexpr int kDp28Rows = 128, kDp28Cols = 64, kDp28Ld = kDp28Cols + 2;
+__global__ __launch_bounds__(256) void k_double_prune28(const uint16_t* __restrict__ vals,
+                                                        const uint32_t* __restrict__ meta, int64_t rows,
+                                                        int64_t cols, uint16_t* __restrict__ p_vals,
+                                                        uint32_t* __restrict__ p_meta) {
+  __shared__ uint16_t t[kDp28Rows * kDp28Ld];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * kDp28Rows, c0 = (int64_t)blockIdx.x * kDp28Cols;
+  {  // expand: lane -> (row r0 + tid / 2, 32 columns from c0 + 32 (tid & 1))
+    const int lr = tid >> 1, h = tid & 1;
+    uint16_t* dst = t + lr * kDp28Ld + 32 * h;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) dst[e] = (uint16_t)kPrunedMark;
+    const int64_t row = r0 + lr, cb = c0 + 32 * h;
+    if (row < rows && cb < cols) {
+      union { u32x4 v; uint16_t h[8]; } x;
+      x.v = *reinterpret_cast<const u32x4*>(vals + row * (cols / 4) + cb / 4);
+      const uint32_t mw = meta[row * (cols / 32) + cb / 32];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t b = (mw >> (8 * g)) & 0xFFu;
+        dst[8 * g + (b & 7u)] = x.h[2 * g];
+        dst[8 * g + ((b >> 3) & 7u)] = x.h[2 * g + 1];
+      }
+    }
+  }
+  __syncthreads();
+  const int lc = tid >> 2, q = tid & 3;
+  const int64_t k = c0 + lc, g0 = r0 + 32 * q;  // input column; first output row of 4 groups
+  if (k >= cols || g0 >= rows) return;
+  union { u32x4 v; uint16_t h[8]; } o;
+  uint32_t word = 0;
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg) {
+    const uint16_t* col = t + (32 * q + 8 * gg) * kDp28Ld + lc;
+    uint32_t key[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const uint32_t v = col[a * kDp28Ld];
+      key[a] = v == kPrunedMark ? 0u : (v & 0x7FFFu) + 1u;
+    }
+    uint32_t p0, p1;
+    top2_of8(key, p0, p1);
+    const uint32_t v0 = col[p0 * kDp28Ld], v1 = col[p1 * kDp28Ld];
+    o.h[2 * gg] = (uint16_t)(v0 == kPrunedMark ? 0u : v0);
+    o.h[2 * gg + 1] = (uint16_t)(v1 == kPrunedMark ? 0u : v1);
+    word |= (p0 | (p1 << 3)) << (8 * gg);
+  }
+  *reinterpret_cast<u32x4*>(p_vals + k * (rows / 4) + g0 / 4) = o.v;
+  p_meta[k * (rows / 32) + g0 / 32] = word;
+}
+
 }  // namespace
 
 namespace sra {
+
+hipError_t launch_compress28(const uint16_t* W, int64_t rows, int64_t cols, uint16_t* vals, uint32_t* meta,
+                             hipStream_t s) {
+  const int64_t wpr = cols / 32, total = rows * wpr;
+  if (total == 0) return hipSuccess;
+  if (cols % 32) return hipErrorInvalidValue;
+  launch(SRA_KERNEL_COMPRESS, k_compress28, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W,
+         rows, wpr, vals, meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_prune28(const uint16_t* vals, const uint32_t* meta, int64_t rows, int64_t cols,
+                                 uint16_t* p_vals, uint32_t* p_meta, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (rows % 32 || cols % 32) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((cols + kDp28Cols - 1) / kDp28Cols), (unsigned)((rows + kDp28Rows - 1) / kDp28Rows));
+  launch(SRA_KERNEL_DOUBLE_PRUNE, k_double_prune28, grid, dim3(256), 0, s, vals, meta, rows, cols, p_vals,
+         p_meta);
+  return hipGetLastError();
+}
 
 // W elements from which the pair kernel stages its tile through LDS first (OPT-13B-sized weights,
 // 105M elements, gain; OPT-350M-sized ones, 4M, do not)

@@ -358,8 +358,7 @@ hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, 
     const int64_t nwg = (R + 16 * f - 1) / (16 * f), per_cu = (nwg + 255) / 256 * 16 * f;
     if (best < 0 || per_cu < best) best = per_cu, fr = f;
   }
-  const char* env = getenv("SRA_DECODE_FR");  // tuning override: 3, 4 or 9 row tiles
-  if (env && (*env == '3' || *env == '4' || *env == '9')) fr = *env - '0';
+  if (tuning().decode_rows) fr = tuning().decode_rows;  // 3, 4 or 9 row tiles
   const unsigned grid = (unsigned)((R + 16 * fr - 1) / (16 * fr));
 #define SRA_DECODE_LAUNCH(F, NW, OCC, TLV)                                                     \
   launch(SRA_KERNEL_DECODE24, k_decode24<F, NW, OCC, TLV>, dim3(grid), dim3(64 * NW), 0, s, s_vals, \

@@ -65,7 +65,9 @@ def err(lib):
     return lib.sra_last_error().decode()
 
 
-@pytest.mark.parametrize("n,m,code", [(1, 4, SRA_ERR_UNSUPPORTED), (2, 8, SRA_ERR_INVALID_ARG),
+@pytest.mark.parametrize("n,m,code", [(1, 4, SRA_ERR_UNSUPPORTED), (1, 8, SRA_ERR_UNSUPPORTED),
+                                      (4, 8, SRA_ERR_UNSUPPORTED), (2, 16, SRA_ERR_INVALID_ARG),
+                                      (2, 6, SRA_ERR_INVALID_ARG),
                                       (3, 2, SRA_ERR_INVALID_ARG), (0, 4, SRA_ERR_INVALID_ARG)])
 def test_compress_rejects_patterns(lib, n, m, code):
     d = SraSparse()
@@ -255,6 +257,50 @@ def test_bwd_validation(lib):
     st = lib.sra_sparse_lora_bwd(ctypes.byref(P), FAKE, FAKE, 2048, FAKE, FAKE, FAKE, 16, 7,
                                  FAKE, FAKE, FAKE, None, None, 0, None)
     assert st == SRA_ERR_WORKSPACE
+
+
+def test_nm28_validation(lib):
+    """2:8: bf16 only, 32-column multiples, no pair or streaming forms; products need K % 128."""
+    d = SraSparse()
+    d.values, d.meta = FAKE, FAKE
+    assert lib.sra_compress(FAKE, SRA_F32, 64, 64, 2, 8, ctypes.byref(d), None) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_compress(FAKE, SRA_BF16, 64, 48, 2, 8, ctypes.byref(d), None) == SRA_ERR_UNSUPPORTED
+    P = SraSparse()
+    P.values, P.meta = FAKE, FAKE
+    assert lib.sra_compress_pair(FAKE, SRA_BF16, 64, 64, 2, 8, ctypes.byref(d), ctypes.byref(P),
+                                 None) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_nm_meta_words(1024, 2, 8) == 32 and lib.sra_nm_meta_words(40, 2, 8) == 2
+    W = nm_desc(rows=256, cols=192, n=2, m=8)
+    n = ctypes.c_size_t()
+    assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    assert "128" in err(lib)
+    W = nm_desc(rows=256, cols=256, n=2, m=8)
+    assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_OK
+    W.dtype = SRA_F32
+    assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    out = SraSparse()
+    out.values, out.meta = FAKE, FAKE
+    assert lib.sra_nm_tile(ctypes.byref(nm_desc(rows=256, cols=256, n=2, m=8)), ctypes.byref(out),
+                           None) == SRA_ERR_UNSUPPORTED
+
+
+def test_tuning_knobs(lib):
+    """sra_set_tuning: validated keys and values; a dense-engine 2:4 product needs K % 128."""
+    from sparse_rank_adapter_amd._abi import SRA_TUNE_KEYS
+    assert lib.sra_set_tuning(99, 0) == SRA_ERR_INVALID_ARG
+    assert lib.sra_set_tuning(SRA_TUNE_KEYS["engine"], 5) == SRA_ERR_INVALID_ARG
+    assert lib.sra_set_tuning(SRA_TUNE_KEYS["decode_rows"], 5) == SRA_ERR_INVALID_ARG
+    assert lib.sra_set_tuning(SRA_TUNE_KEYS["spmm_splits"], -1) == SRA_ERR_INVALID_ARG
+    W = nm_desc(rows=256, cols=192)
+    n = ctypes.c_size_t()
+    assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_OK
+    try:
+        assert lib.sra_set_tuning(SRA_TUNE_KEYS["engine"], 1) == SRA_OK
+        assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+        assert lib.sra_fwd_workspace(ctypes.byref(W), 16, 8, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    finally:
+        assert lib.sra_set_tuning(0, 0) == SRA_OK
+    assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_OK
 
 
 def test_bwd_noalloc_host_checks(lib):

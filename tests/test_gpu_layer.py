@@ -3,7 +3,6 @@
 Floats: max |gpu - oracle| / (|oracle| + 1e-3) <= 2e-2 for bf16 and <= 1e-5 for fp32.  Full-size
 workloads compare sampled token rows / output columns that the oracle computes one by one.
 """
-import os
 
 import numpy as np
 import pytest
@@ -32,11 +31,12 @@ def nm_oracle_weights(W64, k_groups=None):
 
 
 def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, r=None,
-           check_bwd=True, flags_adapter=True, tiled=False, streaming=False):
+           check_bwd=True, flags_adapter=True, tiled=False, streaming=False, same_decode=False):
     """Runs fwd + bwd on the GPU and compares (optionally on sampled token rows, output columns
     of Y / dB and 4-column groups of K for dX / dA).  tiled: the forward also runs on the
     streaming layout of the weight (sra_nm_tile), whose Y must equal the canonical one bit for bit
-    when both run the same decode configuration (SRA_DECODE_FR set).  streaming: forward and
+    when both run the same decode configuration (same_decode: the decode row tiles are forced
+    by the caller's tuning).  streaming: forward and
     backward run on the streaming layouts of Ws and P instead of the canonical arrays."""
     inp = layer_inputs(wl, seed=seed, T=T)
     dtype = inp["X"].dtype
@@ -70,7 +70,7 @@ def run_nm(wl: Workload, T=None, seed=0, rows=None, cols_n=None, k_groups=None, 
         # the same decode configuration on both layouts sums in the same order: equal bits; the
         # planner may give the layouts different workgroup shapes (another split of K), then
         # both are held to the tolerance only
-        if os.environ.get("SRA_DECODE_FR"):
+        if same_decode:
             assert np.array_equal(bits(Yt), bits(Y)), "streaming-layout Y differs from the canonical Y"
         rep.add("Y (streaming layout)", f64(Yt[rows][:, cols_n]), Yo)
     if rr:
@@ -117,15 +117,15 @@ def test_ragged_shapes(gpu, T, K, N, r, dtype):
     run_nm(wl, seed=T + K)
 
 
-@pytest.mark.parametrize("cfg", [14, 55, 56, 60])
+@pytest.mark.parametrize("cfg", [14, 55])
 @pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (77, 384, 640, 5), (130, 256, 128, 1)])
-def test_in_kernel_adapter_rows(gpu, monkeypatch, cfg, T, K, N, r):
+def test_in_kernel_adapter_rows(gpu, cfg, T, K, N, r):
     """Ranks <= 16 on the 128x64 tiles (32x32 and 16x16x64 forms) and the eight-wave 256x128 tiles:
     U (forward) and dU (backward, with dU^T's parts for dA and the zero columns past T) are
     computed inside the SpMM."""
-    monkeypatch.setenv("SRA_SPMM24_CFG", str(cfg))
     wl = Workload("fused", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
-    run_nm(wl, seed=T + r)
+    with sra.tuned(spmm_config=cfg):
+        run_nm(wl, seed=T + r)
 
 
 @pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 40), (257, 512, 1024, 128), (520, 1280, 256, 100),
@@ -142,13 +142,13 @@ def test_adapter_rows_ring(gpu, T, K, N, r):
 @pytest.mark.parametrize("fr", ["3", "4", "9"])
 @pytest.mark.parametrize("T,K,N,r", [(16, 512, 200, 64), (5, 96, 100, 8), (1, 160, 3000, 0),
                                      (3, 1056, 52, 20), (16, 608, 300, 64)])
-def test_decode_row_tiles(gpu, monkeypatch, fr, T, K, N, r):
+def test_decode_row_tiles(gpu, fr, T, K, N, r):
     """The decode kernel with 48-, 64- and 144-row workgroups: a ragged last row tile, waves
     without a row tile of their own (48 rows, four waves), half steps and batches past K, and the
     adapter epilogue; on the canonical arrays and on the streaming layout."""
-    monkeypatch.setenv("SRA_DECODE_FR", fr)
     wl = Workload("decode_tiles", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
-    run_nm(wl, seed=N + T, check_bwd=False, tiled=True)
+    with sra.tuned(decode_rows=int(fr)):
+        run_nm(wl, seed=N + T, check_bwd=False, tiled=True, same_decode=True)
 
 
 @pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (77, 384, 640, 5), (130, 256, 128, 1),
@@ -163,38 +163,38 @@ def test_streaming_layout_layer(gpu, T, K, N, r):
 
 @pytest.mark.parametrize("cfg", ["61", "62"])
 @pytest.mark.parametrize("T,K,N,r", [(300, 640, 384, 16), (700, 1152, 640, 8)])
-def test_streaming_layout_three_stage_wide(gpu, monkeypatch, cfg, T, K, N, r):
+def test_streaming_layout_three_stage_wide(gpu, cfg, T, K, N, r):
     """The 256x256 tile with three stages and 4-stage metadata super-stages (32-byte pieces of the
     streaming layout's metadata blocks; K and N not multiples of 512, so a last super-stage is
     half past the end), also in the ping-pong schedule (62), on both layouts, forward and
     backward."""
-    monkeypatch.setenv("SRA_SPMM24_CFG", cfg)
     wl = Workload("wide3", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm")
-    run_nm(wl, seed=T + K, streaming=True)
-    run_nm(wl, seed=T + K, streaming=False)
+    with sra.tuned(spmm_config=int(cfg)):
+        run_nm(wl, seed=T + K, streaming=True)
+        run_nm(wl, seed=T + K, streaming=False)
 
 
-def test_split_reduction_both_layouts(gpu, monkeypatch):
+def test_split_reduction_both_layouts(gpu):
     """The 256x256 tile with its reduction split in two (8-stage aligned splits, fp32 partials
     summed in a fixed order) for the forward (K = 1024) and dX (N = 2048), on the canonical arrays
     and on the streaming layout, whose split starts its metadata at a 512-column batch."""
-    monkeypatch.setenv("SRA_SPMM24_CFG", "61,2")
     wl = Workload("split2", T=300, K=1024, N=2048, r=8, dtype="bf16", fmt="nm")
-    run_nm(wl, seed=31, streaming=True)
-    run_nm(wl, seed=31, streaming=False)
+    with sra.tuned(spmm_config=61, spmm_splits=2):
+        run_nm(wl, seed=31, streaming=True)
+        run_nm(wl, seed=31, streaming=False)
 
 
 @pytest.mark.parametrize("T,N,streaming", [(10240, 2048, False), (10240, 2048, True), (10000, 2016, False)])
-def test_tail_split(gpu, monkeypatch, T, N, streaming):
+def test_tail_split(gpu, T, N, streaming):
     """Tail split: of the forward's 320 tiles of 256 x 256 the first 256 run whole (bf16 stores)
     and the last 64 (tokens 8192 on) split over the reduction into fp32 partials that a second
     kernel sums; the backward's tiles are all tail where it splits.  The ragged case ends in
     partial row and token tiles inside the tail.  Sampled token rows on both sides of the
     boundary, every output column."""
-    monkeypatch.setenv("SRA_SPMM24_CFG", "61,2t")
     wl = Workload("tail", T=T, K=1024, N=N, r=8, dtype="bf16", fmt="nm")
     rows = np.array([0, 1, 255, 4097, 8191, 8192, 8500, 9983, T - 1])
-    run_nm(wl, seed=41, rows=rows, streaming=streaming)
+    with sra.tuned(spmm_config=61, spmm_splits=-2):
+        run_nm(wl, seed=41, rows=rows, streaming=streaming)
 
 
 @pytest.mark.parametrize("name", ["opt350m_fc1", "opt13b_fc2"])
