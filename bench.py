@@ -75,8 +75,9 @@ def parse():
     ap.add_argument("--decode-t", type=int, default=16, help="tokens for the decode workload")
     ap.add_argument("--decode-layout", choices=["streaming", "canonical"], default="streaming",
                     help="weight layout of the decode forward (streaming = sra_nm_tile)")
-    ap.add_argument("--nm", choices=["2:4", "1:2"], default="2:4",
-                    help="N:M pattern of the training step's weight (1:2 runs on the 2:4 kernels)")
+    ap.add_argument("--nm", choices=["2:4", "1:2", "2:8"], default="2:4",
+                    help="N:M pattern of the training step's weight (1:2 runs on the 2:4 kernels, "
+                         "2:8 on dense MFMA with expanded fragments)")
     ap.add_argument("--layout", choices=["canonical", "streaming"], default=None,
                     help="weight layout of the training step (streaming = sra_compress_pair_tiled); "
                          "default: streaming for opt13b_*, canonical otherwise")
@@ -358,11 +359,21 @@ def bench_nm_layer(args, wl):
     else:
         S = sra.compress(W, n_, m_)
         P = sra.double_prune(S)
-        pair = lambda: sra.compress_pair(W, n_, m_, out=(S, P))  # noqa: E731
+        if m_ == 8:  # no one-pass pair kernel for 2:8
+            def pair():
+                sra.compress(W, n_, m_, out=S)
+                sra.double_prune(S, out=P)
+        else:
+            pair = lambda: sra.compress_pair(W, n_, m_, out=(S, P))  # noqa: E731
     Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
     U = torch.empty((T, r), dtype=torch.float32, device=dev)
-    ws_f = torch.empty(max(1, sra.fwd_workspace(S, T, r)), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(1, sra.bwd_workspace(P, T, r)), dtype=torch.uint8, device=dev)
+
+    def ws_max(fn, M):  # a workspace large enough for both engines
+        with sra.tuned(engine="dense_mfma"):
+            b = fn(M, T, r)
+        return max(1, b, fn(M, T, r))
+    ws_f = torch.empty(ws_max(sra.fwd_workspace, S), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(ws_max(sra.bwd_workspace, P), dtype=torch.uint8, device=dev)
     grads = {"dX": torch.empty((T, wl.K), dtype=X.dtype, device=dev),
              "dA": torch.empty((r, wl.K), dtype=torch.float32, device=dev),
              "dB": torch.empty((wl.N, r), dtype=torch.float32, device=dev)}
@@ -414,7 +425,7 @@ def bench_nm_layer(args, wl):
     # masked weight gradient of the sparse weight (sparse training's weight update input):
     # dWs = (dY^T X) o mask1 in Ws's value order, against the dense dY^T X GEMM
     wg = None
-    if not tiled:
+    if not tiled and m_ != 8:
         from sparse_rank_adapter_amd._abi import SRA_KERNEL_WEIGHT_GRAD
         gW = torch.empty((wl.N, wl.K // 2), dtype=X.dtype, device=dev)
         k_wg = time_kernel(SRA_KERNEL_WEIGHT_GRAD, lambda: sra.masked_weight_grad(S, dY, X, out=gW), reps)
@@ -427,11 +438,28 @@ def bench_nm_layer(args, wl):
               "dense_dW_gemm_ms": round(d_wg, 5),
               "speedup_vs_dense_dW": round(d_wg / k_wg, 3)}
 
+    ev = None
+    if args.nm == "2:4":
+        # the same layer with its 2:4 products on the dense-MFMA engine (expanded fragments)
+        with sra.tuned(engine="dense_mfma"):
+            e_fwd = time_graph(fwd, args.steps, args.warmup, graph)
+            e_bwd = time_graph(bwd, args.steps, args.warmup, graph)
+            ek_fwd = time_kernel(SRA_KERNEL_SPMM24, fwd, reps)
+            ek_bwd = time_kernel(SRA_KERNEL_SPMM24, lambda: sra.sparse_lora_bwd(P, dY, X, U, A, B, ws=ws_b,
+                                                                                out=grads), reps)
+        ev = {"what": "2:4 products on SMFMAC (the default) against the same pipeline with each weight "
+                      "fragment expanded to dense bf16 for dense MFMA",
+              "smfmac": {"fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5),
+                         "spmm_fwd_kernel_ms": round(k_fwd, 5), "spmm_bwd_kernel_ms": round(k_bwd, 5)},
+              "dense_mfma": {"fwd_ms": round(e_fwd, 5), "bwd_ms": round(e_bwd, 5),
+                             "spmm_fwd_kernel_ms": round(ek_fwd, 5), "spmm_bwd_kernel_ms": round(ek_bwd, 5)},
+              "smfmac_speedup_fwd_bwd": round((e_fwd + e_bwd) / (ms_fwd + ms_bwd), 3)}
+
     dense_eq, algo, nbytes = step_model(wl, T)
     # dominant kernel: the slower of the two SpMM launches; algorithmic flops per launch are the
-    # stored-half products plus the adapter epilogue (2 T N K/2 + 2 T r R)
-    spmm_flops_fwd = 2 * T * wl.N * (wl.K // 2) + 2 * T * r * wl.N
-    spmm_flops_bwd = 2 * T * wl.K * (wl.N // 2) + 2 * T * r * wl.K
+    # stored products plus the adapter epilogue (2 T N K n/m + 2 T r R)
+    spmm_flops_fwd = 2 * T * wl.N * (wl.K * n_ // m_) + 2 * T * r * wl.N
+    spmm_flops_bwd = 2 * T * wl.K * (wl.N * n_ // m_) + 2 * T * r * wl.K
     if k_bwd >= k_fwd:
         kname, kms, kflops = "k_spmm24 (backward dX = dY P^T + dU A)", k_bwd, spmm_flops_bwd
         tkey = f"{wl.name}/{args.nm}/{args.layout}/spmm24_bwd/k_spmm24_pipe<2,1,2,2,4,16>"
@@ -470,6 +498,11 @@ def bench_nm_layer(args, wl):
                       "compress": None if k_cmp is None else round(k_cmp, 5),
                       "double_prune": None if k_dp is None else round(k_dp, 5)},
         "masked_weight_grad": wg,
+        "engine_eval": ev,
+        # Lemma 2.1's quantity on the GPU's own compressed forms: entries the second prune removed,
+        # over all N K entries (Gaussian weights: every kept value is nonzero)
+        "added_zeros_frac": None if tiled else round(
+            (int((S.values != 0).sum()) - int((P.values != 0).sum())) / (wl.N * wl.K), 5),
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4),
@@ -478,10 +511,13 @@ def bench_nm_layer(args, wl):
     return out, inp, dense_eq
 
 
-def bench_mlp_chain(args, inputs=None):
+def bench_mlp_chain(args, inputs=None, nm="2:4", engine_eval=True):
     """OPT-13B MLP step with both layers chained: fc1 forward on X, fc2 forward on fc1's Y, fc2
     backward on dY2, fc1 backward on fc2's dX (no activation between the layers), each layer's
-    compress + double prune first; against the four dense GEMMs of the same chain.
+    compress + double prune first; against the four dense GEMMs of the same chain.  nm = "2:8"
+    runs both weights at 2:8 (canonical arrays, dense-MFMA products); for 2:4, engine_eval also
+    times the same step with the 2:4 products on the dense-MFMA engine (weight fragments expanded
+    to dense bf16) beside the SMFMAC one.
 
     Returns (line, (i1, i2)) with the CPU inputs of both layers for the CPU baseline."""
     import torch
@@ -497,17 +533,29 @@ def bench_mlp_chain(args, inputs=None):
     X, W1, A1, B1 = (i1[k].to(dev) for k in ("X", "W", "A", "B"))
     W2, A2, B2, dY2 = (i2[k].to(dev) for k in ("W", "A", "B", "dY"))
     T = w1.T
-    tiled = args.layout == "streaming"
+    n_, m_ = (int(x) for x in nm.split(":"))
+    tiled = args.layout == "streaming" and nm == "2:4"
     layers = []
+
+    def ws_max(fn, M):  # a workspace large enough for both engines
+        with sra.tuned(engine="dense_mfma"):
+            b = fn(M, T, r)
+        return max(1, b, fn(M, T, r))
     for wl, W, A, B in ((w1, W1, A1, B1), (w2, W2, A2, B2)):
-        S, P = sra.compress_pair_tiled(W) if tiled else sra.compress_pair(W)
+        if tiled:
+            S, P = sra.compress_pair_tiled(W)
+        elif nm == "2:4":
+            S, P = sra.compress_pair(W)
+        else:
+            S = sra.compress(W, n_, m_)
+            P = sra.double_prune(S)
         r = wl.r
         layers.append(dict(
             wl=wl, W=W, A=A, B=B, S=S, P=P,
             Y=torch.empty((T, wl.N), dtype=X.dtype, device=dev),
             U=torch.empty((T, r), dtype=torch.float32, device=dev),
-            ws_f=torch.empty(max(1, sra.fwd_workspace(S, T, r)), dtype=torch.uint8, device=dev),
-            ws_b=torch.empty(max(1, sra.bwd_workspace(P, T, r)), dtype=torch.uint8, device=dev),
+            ws_f=torch.empty(ws_max(sra.fwd_workspace, S), dtype=torch.uint8, device=dev),
+            ws_b=torch.empty(ws_max(sra.bwd_workspace, P), dtype=torch.uint8, device=dev),
             g={"dX": torch.empty((T, wl.K), dtype=X.dtype, device=dev),
                "dA": torch.empty((r, wl.K), dtype=torch.float32, device=dev),
                "dB": torch.empty((wl.N, r), dtype=torch.float32, device=dev)}))
@@ -517,8 +565,11 @@ def bench_mlp_chain(args, inputs=None):
         for L in layers:
             if tiled:
                 sra.compress_pair_tiled(L["W"], out=(L["S"], L["P"]))
-            else:
+            elif nm == "2:4":
                 sra.compress_pair(L["W"], out=(L["S"], L["P"]))
+            else:
+                sra.compress(L["W"], n_, m_, out=L["S"])
+                sra.double_prune(L["S"], out=L["P"])
 
     def fwd1():
         sra.sparse_lora_fwd(l1["S"], X, l1["A"], l1["B"], Y=l1["Y"], U=l1["U"], ws=l1["ws_f"])
@@ -568,20 +619,45 @@ def bench_mlp_chain(args, inputs=None):
     # (fc1 Y, fc2 Y, fc2 dX, fc1 dX), each timed alone by the library's hook on its own stream.
     # Algorithmic flops per launch: stored-half products 2 T R (C/2) plus the epilogue 2 T r R.
     reps = max(10, args.steps)
-    launches = []
-    for name, call, R, C in (("fc1_fwd", fwd1, w1.N, w1.K), ("fc2_fwd", fwd2, w2.N, w2.K),
-                             ("fc2_dx", bwd2, w2.K, w2.N), ("fc1_dx", bwd1, w1.K, w1.N)):
-        mean, ts = time_kernel_dist(SRA_KERNEL_SPMM24, call, reps)
-        fl = 2 * T * R * (C // 2) + 2 * T * w1.r * R
-        launches.append({"call": name, "rows": R, "reduction": C, "flops": fl,
-                         "kernel_ms": round(mean, 5),
-                         "kernel_median_ms": round(float(sorted(ts)[len(ts) // 2]), 5),
-                         "tflops_stored": round(fl / (mean * 1e-3) / 1e12, 1)})
+
+    def spmm_launches():
+        out = []
+        for name, call, R, C in (("fc1_fwd", fwd1, w1.N, w1.K), ("fc2_fwd", fwd2, w2.N, w2.K),
+                                 ("fc2_dx", bwd2, w2.K, w2.N), ("fc1_dx", bwd1, w1.K, w1.N)):
+            mean, ts = time_kernel_dist(SRA_KERNEL_SPMM24, call, reps)
+            fl = 2 * T * R * (C * n_ // m_) + 2 * T * w1.r * R   # stored products + epilogue
+            fd = 2 * T * R * C + 2 * T * w1.r * R                 # the same on the dense weight
+            out.append({"call": name, "rows": R, "reduction": C, "flops": fl,
+                        "kernel_ms": round(mean, 5),
+                        "kernel_median_ms": round(float(sorted(ts)[len(ts) // 2]), 5),
+                        "tflops_stored": round(fl / (mean * 1e-3) / 1e12, 1),
+                        "tflops_dense_eq": round(fd / (mean * 1e-3) / 1e12, 1)})
+        return out
+    launches = spmm_launches()
     k_flops = sum(L["flops"] for L in launches) / len(launches)
     k_ms = sum(L["kernel_ms"] for L in launches) / len(launches)
     achieved = k_flops / (k_ms * 1e-3) / 1e12
-    kname = SPMM_MLP_KERNELS[args.layout]
-    traffic = TRAFFIC_BYTES.get(f"opt13b_mlp/{args.layout}/spmm24/{kname}")
+    kname = SPMM_MLP_KERNELS[args.layout] if nm == "2:4" else "k_spmm24_q<..., NM = 28> (2:8, dense MFMA)"
+    traffic = TRAFFIC_BYTES.get(f"opt13b_mlp/{args.layout}/spmm24/{kname}") if nm == "2:4" else None
+    ev = None
+    if engine_eval and nm == "2:4":
+        # the same step with the 2:4 products on the dense-MFMA engine (graphs captured under it)
+        with sra.tuned(engine="dense_mfma"):
+            e_ms = time_graph(step, args.steps, args.warmup, graph)
+            e_fwd = time_graph(fwd, args.steps, args.warmup, graph)
+            e_bwd = time_graph(bwd, args.steps, args.warmup, graph)
+            e_launches = spmm_launches()
+        e_k = sum(L["kernel_ms"] for L in e_launches) / len(e_launches)
+        ev = {"what": "2:4 products on SMFMAC (the default) against the same pipeline with each "
+                      "weight fragment expanded to dense bf16 for dense MFMA",
+              "smfmac": {"step_ms": round(ms, 5), "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5),
+                         "spmm_kernel_ms_mean": round(k_ms, 5)},
+              "dense_mfma": {"step_ms": round(e_ms, 5), "fwd_ms": round(e_fwd, 5), "bwd_ms": round(e_bwd, 5),
+                             "spmm_kernel_ms_mean": round(e_k, 5),
+                             "spmm_launches": [{k: L[k] for k in ("call", "kernel_ms", "tflops_dense_eq")}
+                                               for L in e_launches]},
+              "smfmac_speedup_spmm": round(e_k / k_ms, 3),
+              "smfmac_speedup_fwd_bwd": round((e_fwd + e_bwd) / (ms_fwd + ms_bwd), 3)}
 
     dense_eq = sum(step_model(L["wl"], T, with_compress=False)[0] for L in layers)
     line = {
@@ -593,7 +669,7 @@ def bench_mlp_chain(args, inputs=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "opt13b_mlp", "T": T, "hidden": w1.K, "ffn": w1.N, "r": w1.r,
-                   "sparsity": "2:4", "layout": args.layout,
+                   "sparsity": nm, "layout": "streaming" if tiled else "canonical",
                    "step": "per layer compress + double_prune; fc1 fwd, fc2 fwd, fc2 bwd (dX, dA, dB), "
                            "fc1 bwd (dX, dA, dB)",
                    "graph": graph, "seed": 0},
@@ -611,7 +687,7 @@ def bench_mlp_chain(args, inputs=None):
                       "dense_four_gemms": round(d_all, 5)},
         "dense_replay_ms": d_dist,
         "spmm_launches": launches,
-        "roofline": {"kernel": f"{kname} (2:4 SpMM + adapter epilogue; mean of the four "
+        "roofline": {"kernel": f"{kname} ({nm} SpMM + adapter epilogue; mean of the four "
                                f"launches of a step)",
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
@@ -620,6 +696,8 @@ def bench_mlp_chain(args, inputs=None):
                      "algorithmic_flops_per_launch": int(k_flops),
                      "kernel_ms": round(k_ms, 5)},
     }
+    if ev:
+        line["engine_eval"] = ev
     return line, (i1, i2)
 
 
@@ -925,6 +1003,10 @@ def main():
     if args.workload == "opt13b_mlp":
         out, (i1, i2) = bench_mlp_chain(args)
         extras(args, out, small=not args.no_small)
+        m28, _ = bench_mlp_chain(args, inputs=(i1, i2), nm="2:8", engine_eval=False)
+        out["nm28_opt13b_mlp"] = {k: m28[k] for k in (
+            "value", "unit", "ms_per_step", "config", "speedup_vs_dense", "speedup_fwd_vs_dense_fwd",
+            "speedup_bwd_vs_dense_dx", "detail_ms", "spmm_launches", "roofline")}
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_mlp(i1, i2, args.cpu_budget)
             out["cpu_baseline_1thread"] = cpu_one_thread()
@@ -974,8 +1056,11 @@ def extras(args, out, small):
         keep = ("value", "unit", "ms_per_step", "config", "speedup_vs_dense",
                 "speedup_step_incl_compress_vs_dense", "speedup_vs_dense_lora", "detail_ms",
                 "speedup_fwd_vs_dense_fwd", "speedup_bwd_vs_dense_dx", "kernel_ms",
-                "masked_weight_grad", "roofline", "replay_ms")
+                "masked_weight_grad", "roofline", "replay_ms", "engine_eval", "added_zeros_frac")
         out["opt350m_fc1"] = {k: s[k] for k in keep if k in s}
+        sargs.nm = "2:8"
+        s8, _, _ = bench_nm_layer(sargs, WORKLOADS["opt350m_fc1"])
+        out["nm28_opt350m_fc1"] = {k: s8[k] for k in keep if k in s8}
     if not args.no_decode:
         out["decode_opt66b_ffn"] = bench_decode(args, WORKLOADS["opt66b_ffn_decode"], (1, 4, 16))
         out["sparse_update_opt66b_ffn"] = bench_update(args, WORKLOADS["opt66b_ffn_decode"])
