@@ -392,6 +392,7 @@ sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols
                         int32_t m, sra_sparse* out, void* stream) {
   SRA_TRY(check_dtype(dtype));
   SRA_TRY(check_nm(rows, cols, n, m));
+  if (m == 8 && dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "2:8 is bf16 only");
   if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
   const bool any = rows > 0 && cols > 0;
   SRA_TRY(check_ptr(W, any, "W"));
@@ -405,7 +406,6 @@ sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols
   out->m = m;
   const hipStream_t s = (hipStream_t)stream;
   if (m == 8) {
-    if (dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "2:8 is bf16 only");
     return hip_done(sra::launch_compress28((const uint16_t*)W, rows, cols, (uint16_t*)out->values,
                                            out->meta, s), s, "compress 2:8");
   }

@@ -415,8 +415,8 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   int ms_ch[TL::LMS ? TL::LMS : 1], ms_dst[TL::LMS ? TL::LMS : 1];
 #pragma unroll
   for (int k = 0; k < TL::LMS; ++k) {
-    constexpr int SL = MS / 2;  // 16-byte slots per row
-    const int b = k * NW + wave, row = (1024 / (8 * MS)) * b + lane / SL, pos = lane % SL;
+    constexpr int SL = MS ? MS / 2 : 1;  // 16-byte slots per row
+    const int b = k * NW + wave, row = (1024 / (8 * (MS ? MS : 1))) * b + lane / SL, pos = lane % SL;
     ms_ch[k] = pos ^ ms_swz(row);
     ms_row[k] = (uint32_t)row;
     ms_dst[k] = b * 1024;

@@ -430,6 +430,29 @@ def test_nm_axpby_against_library_and_dense():
     assert np.array_equal(stored, mask)
 
 
+def test_sparse_sgd_step_against_torch_optimizer():
+    """The sparse update as an optimizer step: nm_axpby(1 - lr wd, Ws, -lr, dWs) on the stored values
+    equals torch.optim.SGD(lr, weight_decay=wd) stepping the dense masked weight with its masked
+    gradient (the dense gradient dY^T X at the stored positions, zero elsewhere; the optimizer adds
+    wd W to the gradient and subtracts lr times the sum), read back at the stored positions, with
+    the pruned entries left at zero."""
+    rng = np.random.default_rng(17)
+    T, N, K = 6, 8, 32
+    W = rng.standard_normal((N, K))
+    dY, X = rng.standard_normal((T, N)), rng.standard_normal((T, K))
+    vals, meta, mask = nm.compress(W, 2, 4)
+    dW = layer.masked_weight_grad(dY, X, meta, 2, 4, K)
+    lr, wd = 0.05, 0.1
+    new_vals = layer.nm_axpby(1.0 - lr * wd, vals, -lr, dW)
+    w = torch.nn.Parameter(torch.from_numpy(np.where(mask, W, 0.0)))
+    opt = torch.optim.SGD([w], lr=lr, weight_decay=wd)
+    w.grad = torch.from_numpy(np.where(mask, dY.T @ X, 0.0))
+    opt.step()
+    ref = w.detach().numpy()
+    assert np.allclose(ref[mask].reshape(N, -1), new_vals, rtol=1e-13, atol=1e-13)
+    assert np.all(ref[~mask] == 0.0)
+
+
 # ----------------------------------------------------------------------------- fixed-fan-in adapter factor
 
 def _squash_problem(seed, T=6, K=20, N=8, r=3, k=5):
