@@ -219,7 +219,7 @@ sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flag
   return SRA_OK;
 }
 
-// dB (over dY, V = U in three parts) and dA (over X, V = dU in four parts, stored transposed) as
+// dB (over dY, V = U in three parts) and dA (over X, V = dU in three parts, stored transposed) as
 // jobs of the merged adapter-gradient launch; pointers are filled in by the caller.
 int grad_jobs(sra::AdapterGrad* jobs, bool db, bool da, int64_t N, int64_t K) {
   int n = 0;
@@ -232,7 +232,7 @@ int grad_jobs(sra::AdapterGrad* jobs, bool db, bool da, int64_t N, int64_t K) {
   if (da) {
     jobs[n] = sra::AdapterGrad{};
     jobs[n].M = K;
-    jobs[n].parts = 4;
+    jobs[n].parts = 3;
     jobs[n].out_t = true;
     ++n;
   }
@@ -263,7 +263,7 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   if (p.need_du) p.wt_off = a.take(sra::adapter_wt_bytes(N, r));
   if (dx_ad) p.at_off = a.take(sra::adapter_at_bytes(K, r));
   if (db && r > 0) p.vtu_off = a.take(sra::adapter_vt_bytes(T, r, 3));
-  if (da && r > 0) p.vtdu_off = a.take(sra::adapter_vt_bytes(T, r, 4));  // dU (fp64 sum) split for dA
+  if (da && r > 0) p.vtdu_off = a.take(sra::adapter_vt_bytes(T, r, 3));  // dU (fp32) split for dA
   if (P->dtype == SRA_BF16 && r > 0) {
     size_t g = 0;
     if (p.own_u) g = std::max(g, sra::adapter_rows_ws(T, K, r));
@@ -842,7 +842,7 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)dY, T, N, vtU, 3, r, false, dB, gws, s),
                      s, "bwd dB"));
   if (fda)
-    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)X, T, K, vtdU, 4, r, true, dA, gws, s),
+    SRA_TRY(hip_done(sra::launch_adapter_cols((const uint16_t*)X, T, K, vtdU, 3, r, true, dA, gws, s),
                      s, "bwd dA"));
   return SRA_OK;
 }

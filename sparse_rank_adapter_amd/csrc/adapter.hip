@@ -17,9 +17,9 @@
 //   so each 64-token x 64-column Act tile is staged in LDS as [t][m] and a lane gathers its 8
 //   tokens of one column from there.  dB and dA sum thousands of token products whose total can
 //   cancel by orders of magnitude, so V's rounding is amplified ~sqrt(T) times: V^T arrives as
-//   bf16 parts [part][j][t] -- three parts for fp32 V (U, split by the backward prep kernel; split
-//   error below fp32 rounding), four for fp64 dU (written by the rows kernel that produces it) --
-//   which read as contiguous 16-byte fragments.
+//   bf16 parts [part][j][t] -- three parts of an fp32 V, an exact split (U, split by the backward
+//   prep kernel; dU, summed in fp64 by the rows kernel that produces it and rounded once to fp32,
+//   the dU the call returns) -- which read as contiguous 16-byte fragments.
 // Both use v_mfma_f32_16x16x32_bf16 and move every 32-step MFMA partial into fp64 registers (fp32
 // rounding only acts inside one 32-term dot product); slices write fp64 partials that one more
 // kernel sums in a fixed order, so results are independent of scheduling.
@@ -86,7 +86,7 @@ SRA_DEV u32x4 load8(const uint16_t* __restrict__ p, int64_t i, int64_t lim, bool
 // ------------------------------------------------------------------------------------ rows
 // grid: (ceil(T/16), ceil(r/(16 JT)), S); slice z covers c in [z*c_per, min(C, (z+1)*c_per)).
 // Wave w takes the 32-column steps w, w+4, w+8, ... of its slice, UB steps per batch.
-// When vt is non-null the result is also written as V^T split into four bf16 parts (write_vt4),
+// When vt is non-null the result is also written as V^T split into three bf16 parts (write_vt3),
 // vt[p][j][t] (rows rp, columns Tp; the zero padding is the caller's), ready for the cols kernel.
 
 template <int JT, int UB>
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void k_adapter_rows(const uint16_t* __restrict
       for (int e = 0; e < 4; ++e)
         if (j < r && tt + e >= T && tt + e < Tp)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + tt + e] = 0;
+          for (int p = 0; p < 3; ++p) vt[((int64_t)p * rp + j) * Tp + tt + e] = 0;
     }
   }
   // waves 1..3 hand their sums to wave 0, which adds them in wave order
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void k_adapter_rows(const uint16_t* __restrict
       } else {
         if (out) out[tt * r + j] = (float)s;
         if (out64) out64[tt * r + j] = s;
-        if (vt) write_vt4(vt, rp, Tp, j, tt, s);
+        if (vt) write_vt3(vt, rp, Tp, j, tt, s);
       }
     }
   }
@@ -277,8 +277,8 @@ constexpr int ALD = 64 + 8;   // LDS row of the Act tile [t][m] (elements; 144 B
 constexpr int VLD = CS + 8;   // LDS row of the V^T tile [j][t]
 
 // V^T parts: vt[p][j][t] for j < rp (r rounded up to 16) and t < Tp (T rounded up to 8; columns
-// past T are 0).  fp32 V (U) -> 3 parts written by the backward prep kernel, fp64 V (dU) -> 4 parts
-// written by the rows kernel (or its slice reduction).
+// past T are 0).  U -> 3 parts written by the backward prep kernel, dU -> 3 parts of its fp32 value
+// written by the rows kernel (or its slice reduction).  The kernels take 1 to 4 parts.
 
 // grid: (ceil(M/64), ceil(r/(16 JT)), S); slice z covers tokens [z*t_per, min(T, (z+1)*t_per)),
 // t_per % CS == 0.  Wave w owns columns m0 + 16w .. +15.
@@ -475,7 +475,7 @@ __global__ void k_reduce_parts(const double* __restrict__ part, int S, int64_t n
   for (; k < S; ++k) s += part[(int64_t)k * n + i];
   if (out) out[i] = (float)s;
   if (out64) out64[i] = s;
-  if (vt) write_vt4(vt, rp, Tp, (int)(i % r), i / r, s);  // rows output [T][r]
+  if (vt) write_vt3(vt, rp, Tp, (int)(i % r), i / r, s);  // rows output [T][r]
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -739,13 +739,13 @@ __global__ __launch_bounds__(256 * kGradKG[1]) void k_adapter_grads32(sra::Adapt
 __global__ __launch_bounds__(256 * kGradKG[2]) void k_adapter_grads64(sra::AdapterGradArgs ga) { adapter_grads_body<4, kGradKG[2]>(ga); }
 
 // Wide tiles of the merged gradients, for ranks above 32.  With 64 x 64 tiles the V^T parts of a
-// stage (4 parts x 64 rows) are four times the Act tile and are re-read by every column block, and
+// stage (3 parts x 64 rows) are three times the Act tile and are re-read by every column block, and
 // Act itself is re-read once per 64 adapter rows.  Here each of the 8 waves owns 2 column
 // fragments x 4 adapter-row fragments, and the waves tile either 128 columns x 128 adapter rows
 // (WJ = 2) or 256 columns x 64 adapter rows (WJ = 1).  Stages are 32 tokens: the Act tile as
 // 2*MW-byte token rows, the V^T tile as P*JR rows of 64 bytes, both by buffer -> LDS DMA with the
-// same zero-reads past the slice and past T as the narrow kernel.  P (3 for dB, 4 for dA) is a
-// template parameter so no DMA or MFMA is spent on absent parts.
+// same zero-reads past the slice and past T as the narrow kernel.  P is the part count of V^T (3:
+// U for dB and dU for dA, both fp32 split exactly).
 // Swizzles: Act row t keeps 16-byte chunk c in slot c ^ 2((t >> 3) & 3) (the four 8-token groups
 // of a transposed 2-byte read land on different banks); V^T row x keeps chunk c in slot
 // c ^ ((x >> 2) & 3) (16 consecutive 64-byte rows of a 16-byte fragment read cover all banks once).
@@ -906,8 +906,7 @@ SRA_DEV void adapter_grads_wide(const sra::AdapterGradArgs& ga) {
   const bool second = (int)blockIdx.x >= ga.job[0].nmb;
   const sra::AdapterGrad job = second ? ga.job[1] : ga.job[0];
   const int mb = (int)blockIdx.x - (second ? ga.job[0].nmb : 0);
-  if (job.parts == 4) adapter_grads_wide_body<WJ, 4>(ga, job, mb, smem);
-  else adapter_grads_wide_body<WJ, 3>(ga, job, mb, smem);
+  adapter_grads_wide_body<WJ, 3>(ga, job, mb, smem);
 }
 __global__ __launch_bounds__(512) void k_adapter_grads_w64(sra::AdapterGradArgs ga) { adapter_grads_wide<1>(ga); }
 __global__ __launch_bounds__(512) void k_adapter_grads_w128(sra::AdapterGradArgs ga) { adapter_grads_wide<2>(ga); }
@@ -1064,7 +1063,7 @@ SRA_DEV void adapter_rows_ring_body(const uint16_t* __restrict__ act, int64_t T,
         // V^T columns T .. Tp-1 (padding to a multiple of 8) must read as zero in the cols kernel
         if (vt && blockIdx.z == 0 && tt < Tp)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + tt] = 0;
+          for (int p = 0; p < 3; ++p) vt[((int64_t)p * rp + j) * Tp + tt] = 0;
         continue;
       }
       const double s = acc64[a][e];
@@ -1073,7 +1072,7 @@ SRA_DEV void adapter_rows_ring_body(const uint16_t* __restrict__ act, int64_t T,
       } else {
         if (out) out[tt * r + j] = (float)s;
         if (out64) out64[tt * r + j] = s;
-        if (vt) write_vt4(vt, rp, Tp, j, tt, s);
+        if (vt) write_vt3(vt, rp, Tp, j, tt, s);
       }
     }
   }
@@ -1264,9 +1263,9 @@ GradsPlan grads_plan(const AdapterGrad* g, int n, int64_t T, int r) {
   GradsPlan p;
   p.jt = pick_jt(r);
   bool wide = r > 32;
-  // (parts 3 or 4; the per-lane offsets of a 32-token stage stay below 2^31)
+  // (three parts; the per-lane offsets of a 32-token stage stay below 2^31)
   for (int i = 0; i < n; ++i)
-    wide = wide && (g[i].parts == 3 || g[i].parts == 4) && g[i].M * 64 < ((int64_t)1 << 31);
+    wide = wide && g[i].parts == 3 && g[i].M * 64 < ((int64_t)1 << 31);
   p.wj = wide ? (r <= 64 ? 1 : 2) : 0;
   p.mw = wide ? 256 / p.wj : 64;
   p.njb = (int)cdiv(r, wide ? 64 * p.wj : 16 * p.jt);

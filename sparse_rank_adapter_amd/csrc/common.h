@@ -53,23 +53,14 @@ SRA_DEV void split3_bf16(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   mid = f32_to_bf16(r1);
   lo = f32_to_bf16(r1 - bf16_to_f32(mid));
 }
-// Four-way split of an fp64 value into bf16 parts (error about 2^-33 |x|); the remainders are
-// formed in fp64, so each part is the correctly rounded bf16 of what is left.
-SRA_DEV void split4_bf16(double x, uint16_t p[4]) {
-  double rem = x;
+// V^T in three bf16 parts, vt[p][j][t] (rp rows per part, Tp columns), the operand layout of the
+// adapter-gradient kernel: v (an fp64 sum) is rounded once to fp32, the value the call returns,
+// and split exactly (hi + mid + lo carry all 24 bits of the fp32 significand).
+SRA_DEV void write_vt3(uint16_t* __restrict__ vt, int rp, int64_t Tp, int j, int64_t t, double v) {
+  uint16_t p3[3];
+  split3_bf16((float)v, p3[0], p3[1], p3[2]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = f32_to_bf16((float)rem);
-    rem -= (double)bf16_to_f32(p[i]);
-  }
-}
-// V^T in four bf16 parts, vt[p][j][t] (rp rows per part, Tp columns), the operand layout of the
-// adapter-gradient kernel for an fp64 V.
-SRA_DEV void write_vt4(uint16_t* __restrict__ vt, int rp, int64_t Tp, int j, int64_t t, double v) {
-  uint16_t p4[4];
-  split4_bf16(v, p4);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) vt[((int64_t)p * rp + j) * Tp + t] = p4[p];
+  for (int p = 0; p < 3; ++p) vt[((int64_t)p * rp + j) * Tp + t] = p3[p];
 }
 
 // Workgroup barrier of the LDS-DMA rings: a bare s_barrier (no memory fence, so it does not wait
@@ -183,7 +174,7 @@ struct Epilogue {
   int r = 0;
   // When G is set the SpMM computes U = Act G^T itself (G: r rows of C bf16, row j at G + j*g_ld)
   // and does not read U; its first row tile then writes U to u_out ([T][r] fp32) and, when vt is
-  // set, U^T in four bf16 parts (vt[p][j][t], vt_rp rows, vt_tp columns, zeros for t >= T).
+  // set, U^T in three bf16 parts (vt[p][j][t], vt_rp rows, vt_tp columns, zeros for t >= T).
   const uint16_t* G = nullptr;
   int64_t g_ld = 0;
   float* u_out = nullptr;
@@ -243,7 +234,7 @@ hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t*
 // Adapter products (fp32 results):
 //   rows: out[t][j] = sum_c act[t][c] * wt[j*ldw + c]                              (U, dU)
 //   cols: out[m][j] = sum_t act[t][m] * V[t][j], written as [m][j] or transposed [j][m] (dB, dA)
-// rows also writes an fp64 copy (out64) and/or V^T split into four bf16 parts (vt) when non-null;
+// rows also writes an fp64 copy (out64) and/or V^T split into three bf16 parts (vt) when non-null;
 // cols reads V^T as `parts` bf16 parts vt[p][j][t], rows vt_rows(r), columns vt_cols(T), zero past
 // T.  The backward prep kernel packs B^T for the dU product (wt [r][packed_wt_ld(N)]) and A^T for
 // the dX epilogue, and splits U^T into three parts for dB; any output may be null.

@@ -206,14 +206,14 @@ struct AdapterRows {
           if (ep.vt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (j + e < ep.r) write_vt4(ep.vt, ep.vt_rp, ep.vt_tp, j + e, tg, u[i][jf][e]);
+              if (j + e < ep.r) write_vt3(ep.vt, ep.vt_rp, ep.vt_tp, j + e, tg, u[i][jf][e]);
           }
         } else if (ep.vt && tg < ep.vt_tp) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (j + e < ep.r)
 #pragma unroll
-              for (int p = 0; p < 4; ++p) ep.vt[((int64_t)p * ep.vt_rp + j + e) * ep.vt_tp + tg] = 0;
+              for (int p = 0; p < 3; ++p) ep.vt[((int64_t)p * ep.vt_rp + j + e) * ep.vt_tp + tg] = 0;
         }
       }
     }
@@ -482,7 +482,12 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int wr = wave / WT, wt = wave % WT;
-  auto compute = [&](int buf, int rel) {
+  constexpr bool kIlv = UG == 0 && NM == 0 && !DN && !PP;
+  constexpr int kIlvAhead = 2;  // column fragments read ahead of their products
+  // compute(buf, rel, post): the products of the stage in buffer buf; post() issues the transfers
+  // of a later stage and runs before the products, or between them in the interleaved schedule
+  auto compute = [&](int buf, int rel, auto&& post) {
+    if constexpr (!kIlv) post();
     const uint8_t* A = smem + buf * TL::STAGE;
     const uint32_t* M = reinterpret_cast<const uint32_t*>(A + TL::A_BYTES);
     const uint8_t* MS_buf = msbuf + (MS ? ((rel / (MS ? MS : 1)) & 1) * TL::MSB : 0);
@@ -490,6 +495,46 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     const uint8_t* B = A + TL::A_BYTES + TL::M_BYTES;
     if constexpr (UG > 0) ad.flush();
     bf16x16 bfr[FT];
+    if constexpr (kIlv) {
+      // Interleaved schedule (SMFMAC, no in-kernel adapter rows): the wave's row fragments and
+      // their metadata first, then one column fragment at a time, each used by the FR products of
+      // its column before the next is needed; column fragments are read two columns ahead and the
+      // later stage's transfers are issued after the second column's first product.  The LDS reads
+      // spread evenly over the stage's products instead of coming all at once, and a product waits
+      // only for its own operands.
+      bf16x8 af[FR];
+      uint32_t mword[FR];
+      auto read_row = [&](int i) {
+        const int r = wr * 16 * FR + i * 16 + l16;
+        af[i] = *reinterpret_cast<const bf16x8*>(A + r * 64 + ((q4 ^ ((r >> 2) & 3)) << 4));
+        const int chunk = (u >> 1) ^ ms_swz(r);
+        mword[i] = MS > 0 ? *reinterpret_cast<const uint32_t*>(MS_buf + r * (MS * 8) + (chunk << 4) +
+                                                                4 * (2 * (u & 1) + (q4 >> 1)))
+                          : M[r * 2 + (q4 >> 1)];
+      };
+      auto read_col = [&](int j) {
+        const int tk = wt * 16 * FT + j * 16 + l16, sw = (tk >> 1) & 7;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + ((q4 ^ sw) << 4));
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
+        bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      };
+      constexpr int CA = kIlvAhead < FT ? kIlvAhead : FT;  // column fragments read ahead
+#pragma unroll
+      for (int i = 0; i < FR; ++i) read_row(i);
+#pragma unroll
+      for (int j = 0; j < CA; ++j) read_col(j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < FR * FT; ++k) {
+        const int j = k / FR, i = k % FR;
+        const int idx = (int)(mword[i] >> (16 * (q4 & 1)));
+        acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bfr[j], acc[i][j], idx, 0, 0);
+        if (i == 0 && j + CA < FT) read_col(j + CA);
+        if (k == (FT > 1 ? FR : 0)) post();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
       const int tk = wt * 16 * FT + j * 16 + l16, sw = (tk >> 1) & 7;
@@ -670,17 +715,17 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     }
     if (!late) ring_barrier();
   } else {
+  // waiting for at most (in_flight-1)*L outstanding transfers completes stage c and every older
+  // one, including the metadata of stage c's super-stage (issued before stage c's own loads).
+  // Steady state unrolled by the ring depth: constant buffer indices, D stages in flight (not for
+  // the largest wave tiles, whose registers are spoken for).
+  constexpr bool kUnroll = FR * FT < 32;
   if constexpr (MS > 0) {
     if (c_beg < c_end) issue_meta(0);
   }
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (c_beg + d < c_end) issue(c_beg + d, d);
-  // waiting for at most (in_flight-1)*L outstanding transfers completes stage c and every older
-  // one, including the metadata of stage c's super-stage (issued before stage c's own loads).
-  // Steady state unrolled by the ring depth: constant buffer indices, D stages in flight (not for
-  // the largest wave tiles, whose registers are spoken for).
-  constexpr bool kUnroll = FR * FT < 32;
   int c = c_beg;
   for (; kUnroll && c + NS + D <= c_end; c += NS) {
 #pragma unroll
@@ -689,11 +734,12 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
       else wait_vm<((D - 1) * L < 63 ? (D - 1) * L : 63)>();
       ring_barrier();
       const int rel = c + u - c_beg;
-      if constexpr (MS > 0) {
-        if (rel % MS == 0 && c + u + MS < c_end) issue_meta(rel / MS + 1);
-      }
-      issue(c + u + D, (u + D) % NS);
-      compute(u, rel);
+      compute(u, rel, [&] {
+        if constexpr (MS > 0) {
+          if (rel % MS == 0 && c + u + MS < c_end) issue_meta(rel / MS + 1);
+        }
+        issue(c + u + D, (u + D) % NS);
+      });
     }
   }
   for (; c < c_end; ++c) {
@@ -702,11 +748,12 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     else wait_stages<L>(in_flight);
     ring_barrier();
     const int rel = c - c_beg;
-    if constexpr (MS > 0) {
-      if (rel % MS == 0 && c + MS < c_end) issue_meta(rel / MS + 1);
-    }
-    if (c + D < c_end) issue(c + D, (rel + D) % NS);
-    compute(rel % NS, rel);
+    compute(rel % NS, rel, [&] {
+      if constexpr (MS > 0) {
+        if (rel % MS == 0 && c + MS < c_end) issue_meta(rel / MS + 1);
+      }
+      if (c + D < c_end) issue(c + D, (rel + D) % NS);
+    });
   }
   }
   if constexpr (UG > 0) ad.flush();
