@@ -35,6 +35,12 @@
 
 namespace {
 
+// Cache policy of the weight stream's loads on the streaming layout: non-temporal (gfx950's nt
+// bit), since every weight byte is read once, so the activation block, which every workgroup
+// re-reads, stays cached.  Measured at OPT-66B FFN: 67.3 -> 59.5 us at T = 1, 70.0 -> 62.8 us at
+// T = 16.  The canonical arrays keep the default: there a 128-byte line is read as two 64-byte
+// pieces by different loads, and a non-temporal line is dropped between them (72.9 -> 82.1 us).
+constexpr int kStreamPolicy = 2;
 // Buffer resource word 3 for untyped loads on gfx9-family GPUs (32-bit data format, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
 // Offsets stay below 2^31 (every resource is smaller), so setting bit 31 moves an access past the
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode24(const uint16_t* __res
       for (int i = 0; i < FR; ++i) {
         const uint32_t off = TL ? oob_unless(a_in, v_lane + (uint32_t)((i * nsteps + s) * 1024))
                                 : oob_unless(a_in, v_lane + (uint32_t)((16 * i * vstride + 32 * s) * 2));
-        B.a[i][u] = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
+        B.a[i][u] = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, TL ? kStreamPolicy : 0);
       }
     }
     // words past the row's end belong to steps whose values are zero; only the buffer end matters
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode24(const uint16_t* __res
       const bool m_in = c < 4 * RB && (TL ? b < nb : 16 * b + 4 * m_chunk < (int)mstride);
       const uint32_t off = TL ? (uint32_t)((c >> 6) * nb * 1024 + 16 * (c & 63) + 1024 * b)
                               : (uint32_t)((m_row * mstride + 4 * m_chunk) * 4 + 64 * b);
-      B.m[k] = __builtin_amdgcn_raw_buffer_load_b128(mres, oob_unless(m_in, off), 0, 0);
+      B.m[k] = __builtin_amdgcn_raw_buffer_load_b128(mres, oob_unless(m_in, off), 0, TL ? kStreamPolicy : 0);
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {

@@ -226,18 +226,19 @@ __global__ __launch_bounds__(256) void k_nm_axpby(const void* __restrict__ a, fl
   const u32x4* pa = reinterpret_cast<const u32x4*>(a);
   const u32x4* pb = reinterpret_cast<const u32x4*>(b);
   u32x4* po = reinterpret_cast<u32x4*>(out);
-  // workgroup tiles of U x 256 consecutive chunks: the U loads of a wave read adjacent 1 KB runs
+  // workgroup tiles of U x 256 consecutive chunks: the U loads of a wave read adjacent 1 KB runs;
+  // every byte is read or written once, so the loads and stores are non-temporal
   const int64_t full = nch / (U * 256);
   for (int64_t tile = blockIdx.x; tile < full; tile += gridDim.x) {
     const int64_t i = tile * (U * 256) + threadIdx.x;
     u32x4 va[U], vb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      va[u] = pa[i + 256 * u];
-      vb[u] = pb[i + 256 * u];
+      va[u] = __builtin_nontemporal_load(pa + i + 256 * u);
+      vb[u] = __builtin_nontemporal_load(pb + i + 256 * u);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) po[i + 256 * u] = combine(va[u], vb[u]);
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(combine(va[u], vb[u]), po + i + 256 * u);
   }
   for (int64_t i = full * (U * 256) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nch; i += stride)
     po[i] = combine(pa[i], pb[i]);
