@@ -821,15 +821,15 @@ SRA_DEV void adapter_grads_wide_body(const sra::AdapterGradArgs& ga, const sra::
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc64[f][a][e] = 0.0;
     }
-  auto to64 = [&](f32x4 (&x)[2][4]) {
+  // the set's next stage starts its products from zero (the first MFMA's accumulator input), so
+  // a flushed set needs no clearing
+  auto to64 = [&](const f32x4 (&x)[2][4]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc64[f][a][e] += (double)x[f][a][e];
-        x[f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
   };
   auto compute = [&](int buf, f32x4 (&cur)[2][4], f32x4 (&prev)[2][4]) {
     const uint8_t* A = smem + buf * GW::STAGE;
@@ -861,7 +861,8 @@ SRA_DEV void adapter_grads_wide_body(const sra::AdapterGradArgs& ga, const sra::
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int p = 0; p < P; ++p)
-          cur[f][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[a][p], bf[f].b, cur[f][a], 0, 0, 0);
+          cur[f][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[a][p], bf[f].b,
+                                                              p == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cur[f][a], 0, 0, 0);
     to64(prev);
   };
 
@@ -869,16 +870,27 @@ SRA_DEV void adapter_grads_wide_body(const sra::AdapterGradArgs& ga, const sra::
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < n_st) issue(d, d);
-  for (int st = 0; st < n_st; ++st) {
+  auto step = [&](int st, f32x4 (&cur)[2][4], f32x4 (&prev)[2][4]) {
     if (full_v) wait_inflight<GW::LA + GW::LVM, D>(min(D, n_st - st));
     else wait_inflight<GW::LA + GW::LVM - 1, D>(min(D, n_st - st));
     ring_barrier();
     if (st + D < n_st) issue(st + D, (st + D) % NS);
-    if (st & 1) compute(st % NS, acc[1], acc[0]);
-    else compute(st % NS, acc[0], acc[1]);
+    compute(st % NS, cur, prev);
+  };
+  // two stages per iteration, so each accumulator set keeps its registers (alternating the roles
+  // inside one loop body made the compiler copy both sets every stage)
+  // (stage 0 flushes the zero-initialised second set)
+  int st = 0;
+  for (; st + 1 < n_st; st += 2) {
+    step(st, acc[0], acc[1]);
+    step(st + 1, acc[1], acc[0]);
   }
-  to64(acc[0]);
-  to64(acc[1]);
+  if (st < n_st) {
+    step(st, acc[0], acc[1]);
+    to64(acc[0]);
+  } else if (n_st > 0) {
+    to64(acc[1]);
+  }
 
   // D layout: adapter rows 4(l/16) + e of fragment (wj, a), column l%16 of fragment (wm, f)
 #pragma unroll
