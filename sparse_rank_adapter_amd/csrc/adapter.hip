@@ -642,13 +642,13 @@ SRA_DEV void adapter_grads_body(const sra::AdapterGradArgs& ga) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc64[a][e] = 0.0;
   }
-  auto to64 = [&](f32x4 (&x)[JT]) {
+  // the set's next stage starts its products from zero (the first MFMA's accumulator input), so
+  // a flushed set needs no clearing
+  auto to64 = [&](const f32x4 (&x)[JT]) {
 #pragma unroll
-    for (int a = 0; a < JT; ++a) {
+    for (int a = 0; a < JT; ++a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc64[a][e] += (double)x[a][e];
-      x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
   };
   const int m = 16 * cf + l16, mc = m >> 3, mo = m & 7;
   auto compute = [&](int buf, f32x4 (&cur)[JT], f32x4 (&prev)[JT]) {
@@ -676,7 +676,9 @@ SRA_DEV void adapter_grads_body(const sra::AdapterGradArgs& ga) {
     for (int a = 0; a < JT; ++a)
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        if (p < job.parts) cur[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a][p], bf.b, cur[a], 0, 0, 0);
+        if (p < job.parts)
+          cur[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a][p], bf.b,
+                                                           p == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cur[a], 0, 0, 0);
     to64(prev);
   };
 
@@ -684,15 +686,25 @@ SRA_DEV void adapter_grads_body(const sra::AdapterGradArgs& ga) {
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < n_st) issue(d, d);
-  for (int st = 0; st < n_st; ++st) {
+  auto step = [&](int st, f32x4 (&cur)[JT], f32x4 (&prev)[JT]) {
     wait_inflight<L, D>(min(D, n_st - st));
     ring_barrier();
     if (st + D < n_st) issue(st + D, (st + D) % NS);
-    if (st & 1) compute(st % NS, acc[1], acc[0]);
-    else compute(st % NS, acc[0], acc[1]);
+    compute(st % NS, cur, prev);
+  };
+  // two stages per iteration, so each accumulator set keeps its registers; stage 0 flushes the
+  // zero-initialised second set
+  int st = 0;
+  for (; st + 1 < n_st; st += 2) {
+    step(st, acc[0], acc[1]);
+    step(st + 1, acc[1], acc[0]);
   }
-  to64(acc[0]);
-  to64(acc[1]);
+  if (st < n_st) {
+    step(st, acc[0], acc[1]);
+    to64(acc[0]);
+  } else if (n_st > 0) {
+    to64(acc[1]);
+  }
 
   // k-groups 1 .. KG-1 hand their sums to k-group 0, which adds them in k-group order
   if constexpr (KG > 1) {
@@ -1017,13 +1029,13 @@ SRA_DEV void adapter_rows_ring_body(const uint16_t* __restrict__ act, int64_t T,
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc64[a][e] = 0.0;
   }
-  auto to64 = [&](f32x4 (&x)[JT]) {
+  // the set's next stage starts its products from zero (the first MFMA's accumulator input), so
+  // a flushed set needs no clearing
+  auto to64 = [&](const f32x4 (&x)[JT]) {
 #pragma unroll
-    for (int a = 0; a < JT; ++a) {
+    for (int a = 0; a < JT; ++a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc64[a][e] += (double)x[a][e];
-      x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
   };
   const int xa = 16 * w + l16;  // this lane's token row of the stage
   auto compute = [&](int buf, f32x4 (&cur)[JT], f32x4 (&prev)[JT]) {
@@ -1045,7 +1057,8 @@ SRA_DEV void adapter_rows_ring_body(const uint16_t* __restrict__ act, int64_t T,
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int a = 0; a < JT; ++a)
-        cur[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], gf[ks][a], cur[a], 0, 0, 0);
+        cur[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], gf[ks][a],
+                                                         ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cur[a], 0, 0, 0);
     to64(prev);
   };
 
@@ -1053,15 +1066,25 @@ SRA_DEV void adapter_rows_ring_body(const uint16_t* __restrict__ act, int64_t T,
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < n_st) issue(d, d);
-  for (int st = 0; st < n_st; ++st) {
+  auto step = [&](int st, f32x4 (&cur)[JT], f32x4 (&prev)[JT]) {
     wait_inflight<L, D>(min(D, n_st - st));
     ring_barrier();
     if (st + D < n_st) issue(st + D, (st + D) % NS);
-    if (st & 1) compute(st % NS, acc[1], acc[0]);
-    else compute(st % NS, acc[0], acc[1]);
+    compute(st % NS, cur, prev);
+  };
+  // two stages per iteration, so each accumulator set keeps its registers; stage 0 flushes the
+  // zero-initialised second set
+  int st = 0;
+  for (; st + 1 < n_st; st += 2) {
+    step(st, acc[0], acc[1]);
+    step(st + 1, acc[1], acc[0]);
   }
-  to64(acc[0]);
-  to64(acc[1]);
+  if (st < n_st) {
+    step(st, acc[0], acc[1]);
+    to64(acc[0]);
+  } else if (n_st > 0) {
+    to64(acc[1]);
+  }
 
   // D layout: tokens 16w + 4(l/16) + e, column j = 16a + l%16
 #pragma unroll
