@@ -51,10 +51,11 @@ TRAFFIC_BYTES = {
     # products (profiles/opt13b_mlp_spmm24_traffic.md: TCC_EA0_RDREQ x 128 B + TCC_EA0_WRREQ x
     # 64 B, which equal FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 on gfx950)
     "opt13b_mlp/streaming/spmm24/k_spmm24_q<4, 8, 4, 2, 3, 4, 0, false, true, false>":
-        18336626 * 128 + 3815806 * 64,
-    # streaming layout (sra_nm_tile), 48-row workgroups of four waves
-    "opt66b_ffn_decode/T16/streaming/k_decode24<3>": 192608.7 * 1024 * 2.0 + 1152.1 * 1024,
-    "opt66b_ffn_decode/T1/streaming/k_decode24<3>": 189201.6 * 1024 * 2.0 + 72.0 * 1024,
+        18336572 * 128 + 3809929 * 64,
+    # streaming layout (sra_nm_tile), 48-row workgroups of four waves, non-temporal weight loads
+    # (profiles/opt66b_ffn_decode_traffic.md: read requests x 128 B + 64-byte and 32-byte writes)
+    "opt66b_ffn_decode/T16/streaming/k_decode24<3>": 3042927 * 128 + 12288 * 64 + 12289 * 32,
+    "opt66b_ffn_decode/T1/streaming/k_decode24<3>": 3025411 * 128 + 768 * 64 + 768 * 32,
 }
 
 
