@@ -323,15 +323,15 @@ __global__ __launch_bounds__(256) void k_compress_pair24t(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * 128, r0 = (int64_t)blockIdx.y * 128;
   {
-    // the W tile into LDS with coalesced 16-byte loads (a wave reads four 256-byte row runs);
-    // positions past the matrix hold the pruned mark
+    // the W tile into LDS with coalesced 16-byte loads (a wave reads four 256-byte row runs;
+    // non-temporal, every byte of W is read once); positions past the matrix hold the pruned mark
     if constexpr (ST) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int v = tid + 256 * k, lr = v >> 4, ch = v & 15;
         const int64_t row = r0 + lr, col = c0 + 8 * ch;
         u32x4 x = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-        if (row < rows && col < cols) x = *reinterpret_cast<const u32x4*>(W + row * cols + col);
+        if (row < rows && col < cols) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + row * cols + col));
         *reinterpret_cast<u32x4*>(&tile[lr * LD + 8 * ch]) = x;
       }
       __syncthreads();
