@@ -797,12 +797,14 @@ def bench_update(args, wl):
 
 
 def bench_ffi(args, wl):
-    """Fixed fan-in layer: forward on the ELL weight, backward dX on the exact CSR transpose plus
-    the adapter gradients.  Compression and the transpose are setup, timed apart."""
+    """Fixed fan-in layer: forward on the tiled ELL weight, backward dX on the tiled CSR transpose
+    plus the adapter gradients.  Compression, the transpose and the tiling are setup, timed apart
+    (once per mask).  The same calls on the untiled ELL / CSR forms, which tile into the workspace
+    on every call, are timed beside them."""
     import torch
 
     import sparse_rank_adapter_amd as sra
-    from sparse_rank_adapter_amd._abi import SRA_KERNEL_FFI_DENSIFY, SRA_KERNEL_SPMM_FFI
+    from sparse_rank_adapter_amd._abi import SRA_KERNEL_SPMM_FFI
     from sra_inputs import layer_inputs
 
     dev = torch.device("cuda:0")
@@ -812,44 +814,54 @@ def bench_ffi(args, wl):
     graph = not args.no_graph
     S = sra.compress_ffi(W, wl.ffi_k)
     ST = sra.ffi_transpose(S)
+    St, STt = sra.ffi_tile(S), sra.ffi_tile(ST)
     ms_setup = time_graph(lambda: sra.compress_ffi(W, wl.ffi_k), max(5, args.steps // 5), 2, False)
+    ms_tile = time_graph(lambda: (sra.ffi_tile(S), sra.ffi_tile(ST)), max(5, args.steps // 5), 2, False)
     Y = torch.empty((T, wl.N), dtype=X.dtype, device=dev)
     U = torch.empty((T, r), dtype=torch.float32, device=dev)
-    ws_f = torch.empty(max(1, sra.fwd_workspace(S, T, r)), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(1, sra.bwd_workspace(ST, T, r)), dtype=torch.uint8, device=dev)
     grads = {"dX": torch.empty((T, wl.K), dtype=X.dtype, device=dev),
              "dA": torch.empty((r, wl.K), dtype=torch.float32, device=dev),
              "dB": torch.empty((wl.N, r), dtype=torch.float32, device=dev)}
 
-    def fwd():
-        sra.sparse_lora_fwd(S, X, A, B, Y=Y, U=U, ws=ws_f)
+    def calls(fw, bw):
+        ws_f = torch.empty(max(1, sra.fwd_workspace(fw, T, r)), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(max(1, sra.bwd_workspace(bw, T, r)), dtype=torch.uint8, device=dev)
 
-    def bwd():
-        sra.sparse_lora_bwd(ST, dY, X, U, A, B, ws=ws_b, out=grads)
+        def fwd():
+            sra.sparse_lora_fwd(fw, X, A, B, Y=Y, U=U, ws=ws_f)
+
+        def bwd():
+            sra.sparse_lora_bwd(bw, dY, X, U, A, B, ws=ws_b, out=grads)
+        return fwd, bwd, ws_f.numel(), ws_b.numel()
+    fwd, bwd, wsf_t, wsb_t = calls(St, STt)
     ms_fwd = time_graph(fwd, args.steps, args.warmup, graph)
     ms_bwd = time_graph(bwd, args.steps, args.warmup, graph)
     reps = max(10, args.steps)
-    # the product kernel (densified weight on dense MFMA for these shapes) and the densify pass
+    # the product kernel: each stage's A tile written from the entry lists, dense MFMA
     k_fwd = time_kernel(SRA_KERNEL_SPMM_FFI, fwd, reps)
     k_bwd = time_kernel(SRA_KERNEL_SPMM_FFI, bwd, reps)
-    k_dens_f = time_kernel(SRA_KERNEL_FFI_DENSIFY, fwd, reps)
-    k_dens_b = time_kernel(SRA_KERNEL_FFI_DENSIFY, bwd, reps)
+    fwd_u, bwd_u, wsf_u, wsb_u = calls(S, ST)
+    ms_fwd_u = time_graph(fwd_u, args.steps, args.warmup, graph)
+    ms_bwd_u = time_graph(bwd_u, args.steps, args.warmup, graph)
     Wd = W.contiguous()
     d_fwd = time_graph(lambda: torch.nn.functional.linear(X, Wd), args.steps, args.warmup, graph)
     d_bwd = time_graph(lambda: torch.matmul(dY, Wd), args.steps, args.warmup, graph)
     sparse_flops = 2 * T * wl.N * wl.ffi_k
     dense_eq = 2 * (2 * T * wl.N * wl.K) + 2 * T * r * (wl.K + wl.N) + 4 * T * r * (wl.N + wl.K)
     return {"workload": wl.name, "T": T, "K": wl.K, "N": wl.N, "k": wl.ffi_k, "r": r,
+            "format": "tiled (sra_ffi_tile)",
             "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5),
             "dense_eq_tflops": round(dense_eq / ((ms_fwd + ms_bwd) * 1e-3) / 1e12, 2),
             "spmm_fwd_kernel_ms": round(k_fwd, 5), "spmm_bwd_kernel_ms": round(k_bwd, 5),
-            "densify_fwd_ms": round(k_dens_f, 5), "densify_bwd_ms": round(k_dens_b, 5),
             "spmm_fwd_stored_tflops": round(sparse_flops / (k_fwd * 1e-3) / 1e12, 2),
-            # the densified product runs the dense flops on bf16 MFMA
+            # the product runs the dense flops of each stage's A tile on bf16 MFMA
             "spmm_fwd_frac_bf16_mfma": round(2 * T * wl.N * wl.K / (k_fwd * 1e-3) / PEAK_BF16_FLOPS, 4),
             "dense_fwd_ms": round(d_fwd, 5), "dense_dx_ms": round(d_bwd, 5),
             "speedup_vs_dense": round((d_fwd + d_bwd) / (ms_fwd + ms_bwd), 3),
-            "compress_ffi_ms": round(ms_setup, 5)}
+            "workspace_bytes": {"fwd": wsf_t, "bwd": wsb_t, "fwd_untiled": wsf_u, "bwd_untiled": wsb_u},
+            "untiled_fwd_ms": round(ms_fwd_u, 5), "untiled_bwd_ms": round(ms_bwd_u, 5),
+            "speedup_vs_dense_untiled": round((d_fwd + d_bwd) / (ms_fwd_u + ms_bwd_u), 3),
+            "compress_ffi_ms": round(ms_setup, 5), "ffi_tile_both_ms": round(ms_tile, 5)}
 
 
 def bench_squash(args, wl):
@@ -1016,6 +1028,9 @@ def main():
     wl = WORKLOADS[args.workload]
     if wl.name == "squash_opt350m_fc2":
         print(json.dumps(bench_squash(args, wl)), flush=True)
+        return
+    if wl.name == "ffi90_4096":
+        print(json.dumps(bench_ffi(args, wl)), flush=True)
         return
     if wl.name == "opt66b_ffn_decode":
         rows = bench_decode(args, wl, (args.decode_t,))

@@ -60,7 +60,8 @@ typedef enum {
   SRA_FMT_ELL = 1, /* fixed fan-in: values [rows, k], index int16 [rows, k], columns ascending */
   SRA_FMT_CSR = 2, /* transpose of an ELL matrix: row_ptr int32 [rows+1], index int16 [nnz],
                       values [nnz], column ids ascending inside each row */
-  SRA_FMT_NM_TILED = 3 /* 2:4 bf16 in the streaming layout of sra_nm_tile */
+  SRA_FMT_NM_TILED = 3, /* 2:4 bf16 in the streaming layout of sra_nm_tile */
+  SRA_FMT_FFI_TILED = 4 /* fixed fan-in bf16 in the tiled entry lists of sra_ffi_tile */
 } sra_format;
 
 /*
@@ -196,6 +197,30 @@ sra_status sra_ffi_transpose_workspace(int64_t rows, int64_t cols, int32_t k, si
 sra_status sra_ffi_transpose(const sra_sparse* Ws /* host */, sra_sparse* WsT /* host */, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* Buffer sizes of sra_ffi_tile for a matrix of `rows` x `cols` with nnz stored entries:
+ * *entry_bytes for out->values, *offset_bytes for out->meta.  1 <= cols <= 32767. */
+sra_status sra_ffi_tile_size(int64_t rows, int64_t cols, int64_t nnz, size_t* entry_bytes /* host */,
+                             size_t* offset_bytes /* host */);
+
+/*
+ * ffi_tile -- the products' layout of a fixed fan-in matrix (SQuAsh project update: fixed fan-in
+ * weights; SLoPe paperlayer summary §2.3: a format for the weight and one for its transpose),
+ * built once per mask like sra_nm_tile.  S: SRA_FMT_ELL (the forward weight) or SRA_FMT_CSR (its
+ * transpose from sra_ffi_transpose), bf16.  Rows are cut into 32-row groups and columns into
+ * 64-column stages; list (g, x) holds the entries of group g in stage x as uint32 words, the
+ * bf16 value in the low 16 bits and (row - 32 g) * 64 + (column - 64 x) in the high 16 bits,
+ * ordered by row, then column, padded to a multiple of 4 words with 0xffffffff.  Lists follow
+ * each other by group, then stage.  out->values: the words (entry_bytes of sra_ffi_tile_size,
+ * 16-byte aligned); out->meta: uint32 offsets, meta[g * stages + x] = first word of list (g, x),
+ * then the total word count 4 times (offset_bytes).  The caller sets out->values and out->meta;
+ * the call fills format (SRA_FMT_FFI_TILED), dtype, rows, cols and nnz (the capacity of
+ * out->values in words).  sra_sparse_lora_fwd takes the tiled ELL weight, sra_sparse_lora_bwd the
+ * tiled CSR transpose; both need the reduction (cols) to be a multiple of 64 and use no
+ * workspace for the product.  Errors: SRA_ERR_INVALID_ARG (format, shapes, pointers),
+ * SRA_ERR_UNSUPPORTED (fp32, over 2 GiB of entries).
+ */
+sra_status sra_ffi_tile(const sra_sparse* S /* host */, sra_sparse* out /* host */, void* stream);
+
 /* Workspace bytes for sra_sparse_lora_fwd (T tokens, rank r). */
 sra_status sra_fwd_workspace(const sra_sparse* Ws /* host */, int64_t T, int32_t r,
                              size_t* bytes /* host */);
@@ -203,7 +228,9 @@ sra_status sra_fwd_workspace(const sra_sparse* Ws /* host */, int64_t T, int32_t
 /*
  * sparse_lora_fwd -- Y = X Ws^T + (X A^T) B^T (SLoPe §2.2; the adapter product is fused into the
  * sparse product's epilogue, cf. SLoPe §2.4 and App. D, so Y is written once).
- * Ws: SRA_FMT_NM (2:4), SRA_FMT_NM_TILED (2:4, see sra_nm_tile) or SRA_FMT_ELL, rows = N, cols = K.
+ * Ws: SRA_FMT_NM (2:4), SRA_FMT_NM_TILED (2:4, see sra_nm_tile), SRA_FMT_ELL or SRA_FMT_FFI_TILED
+ * (fixed fan-in, see sra_ffi_tile; K % 64 == 0), rows = N, cols = K.  With 128 or more tokens an
+ * ELL weight is first tiled into the workspace (O(nnz) bytes).
  * X [T,K], A [r,K], B [N,r], Y [T,N].
  * U_out [T,r] fp32 receives U = X A^T when non-NULL (keep it for the backward).
  * r = 0 means no adapter (A, B, U_out ignored).  T = 0 is a no-op.  Y has dtype Ws->dtype.
@@ -230,7 +257,7 @@ sra_status sra_bwd_workspace(const sra_sparse* P /* host */, int64_t T, int32_t 
  * pruned, SLoPe App. J).
  * P: for N:M weights the output of sra_double_prune (rows = K, cols = N; canonical, or in the
  * streaming layout of sra_nm_tile / sra_compress_pair_tiled); for fixed fan-in weights
- * the CSR of sra_ffi_transpose (rows = K, cols = N).
+ * the CSR of sra_ffi_transpose (rows = K, cols = N) or its sra_ffi_tile form (N % 64 == 0).
  * dY [T,N], X [T,K], A [r,K], B [N,r] (dtype P->dtype); T tokens.  U [T,r] fp32 from the forward, or NULL
  * to recompute it from X and A.  Outputs (each only if its flag is set): dX [T,K] (dtype),
  * dA [r,K] fp32, dB [N,r] fp32.  dU_out [T,r] fp32 receives dU = dY B when non-NULL and r > 0.
@@ -375,7 +402,7 @@ enum {
   SRA_KERNEL_ADAPTER = 4,      /* adapter products U, dU, dB, dA (one launch each) */
   SRA_KERNEL_DECODE24 = 5,     /* bf16 2:4 decode SpMM (forward with T <= 16) */
   SRA_KERNEL_SPMM_FFI = 6,     /* bf16 fixed fan-in SpMM (forward Y, backward dX) */
-  SRA_KERNEL_FFI_DENSIFY = 7,  /* bf16 fixed fan-in weight expanded to dense rows before the SpMM */
+  SRA_KERNEL_FFI_DENSIFY = 7,  /* bf16 fixed fan-in adapter factor expanded to dense rows */
   SRA_KERNEL_WEIGHT_GRAD = 8,  /* bf16 masked weight gradient (sra_masked_weight_grad) */
   SRA_KERNEL_NM_UPDATE = 9     /* beta A + gamma B on shared-pattern values (sra_nm_axpby) */
 };

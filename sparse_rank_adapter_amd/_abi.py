@@ -11,7 +11,7 @@ SRA_OK, SRA_ERR_INVALID_ARG, SRA_ERR_UNSUPPORTED, SRA_ERR_WORKSPACE, SRA_ERR_HIP
 STATUS_NAMES = {0: "SRA_OK", -1: "SRA_ERR_INVALID_ARG", -2: "SRA_ERR_UNSUPPORTED",
                 -3: "SRA_ERR_WORKSPACE", -4: "SRA_ERR_HIP"}
 SRA_BF16, SRA_F32 = 0, 1
-SRA_FMT_NM, SRA_FMT_ELL, SRA_FMT_CSR, SRA_FMT_NM_TILED = 0, 1, 2, 3
+SRA_FMT_NM, SRA_FMT_ELL, SRA_FMT_CSR, SRA_FMT_NM_TILED, SRA_FMT_FFI_TILED = 0, 1, 2, 3, 4
 SRA_GRAD_DX, SRA_GRAD_DA, SRA_GRAD_DB, SRA_DX_NO_ADAPTER = 1, 2, 4, 8
 SRA_NOALLOC_SCRATCH_BYTES = 64 << 20
 SRA_TUNE_KEYS = {"spmm_config": 1, "spmm_splits": 2, "spmm_fuse": 3, "engine": 4, "decode_rows": 5,
@@ -23,7 +23,8 @@ EXPORTS = (
     "sra_abi_version", "sra_last_error", "sra_nm_meta_words", "sra_compress", "sra_double_prune",
     "sra_compress_pair", "sra_compress_pair_tiled", "sra_nm_tile_bytes", "sra_nm_tile",
     "sra_masked_weight_grad", "sra_nm_axpby",
-    "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_fwd_workspace",
+    "sra_compress_ffi", "sra_ffi_transpose_workspace", "sra_ffi_transpose", "sra_ffi_tile_size",
+    "sra_ffi_tile", "sra_fwd_workspace",
     "sra_sparse_lora_fwd", "sra_bwd_workspace", "sra_sparse_lora_bwd", "sra_sparse_lora_bwd_noalloc",
     "sra_ffa_fwd_workspace", "sra_sparse_lora_fwd_ffa", "sra_ffa_bwd_workspace", "sra_sparse_lora_bwd_ffa",
     "sra_time_next_kernel", "sra_set_tuning",
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH):
         "sra_compress_ffi": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, P, c_void_p]),
         "sra_ffi_transpose_workspace": (c_int32, [c_int64, c_int64, c_int32, POINTER(c_size_t)]),
         "sra_ffi_transpose": (c_int32, [P, P, c_void_p, c_size_t, c_void_p]),
+        "sra_ffi_tile_size": (c_int32, [c_int64, c_int64, c_int64, POINTER(c_size_t), POINTER(c_size_t)]),
+        "sra_ffi_tile": (c_int32, [P, P, c_void_p]),
         "sra_fwd_workspace": (c_int32, [P, c_int64, c_int32, POINTER(c_size_t)]),
         "sra_sparse_lora_fwd": (c_int32, [P, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p,
                                           c_void_p, c_void_p, c_size_t, c_void_p]),

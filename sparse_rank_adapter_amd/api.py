@@ -13,7 +13,7 @@ import torch
 
 from . import _abi
 from ._abi import (SRA_BF16, SRA_DX_NO_ADAPTER, SRA_F32, SRA_FMT_CSR, SRA_FMT_ELL, SRA_FMT_NM,
-                   SRA_FMT_NM_TILED,
+                   SRA_FMT_NM_TILED, SRA_FMT_FFI_TILED,
                    SRA_GRAD_DA, SRA_GRAD_DB, SRA_GRAD_DX, SraSparse, check, load)
 
 _DT = {torch.bfloat16: SRA_BF16, torch.float32: SRA_F32}
@@ -80,6 +80,11 @@ def _check_sparse(S: "SparseMatrix", name: str):
         _arg(S.values, f"{name}.values", (S.nnz,), S.dtype, dev, min_numel=True)
         _arg(S.index, f"{name}.index", (S.nnz,), torch.int16, dev, min_numel=True)
         _arg(S.row_ptr, f"{name}.row_ptr", (S.rows + 1,), torch.int32, dev)
+    elif S.fmt == SRA_FMT_FFI_TILED:
+        if S.dtype != torch.bfloat16:
+            raise ValueError(f"{name}: the tiled fixed fan-in format is bfloat16 only")
+        _arg(S.values, f"{name}.values", (S.nnz,), torch.int32, dev, min_numel=True)
+        _arg(S.meta, f"{name}.meta", (ffi_tile_lists(S.rows, S.cols) + 4,), torch.int32, dev, min_numel=True)
     else:
         raise ValueError(f"{name}: unknown format {S.fmt}")
     return dev
@@ -302,6 +307,30 @@ def compress_ffi(W: torch.Tensor, k: int) -> SparseMatrix:
     out = SparseMatrix(SRA_FMT_ELL, W.dtype, rows, cols, vals, index=idx, k=k)
     d = out.desc()
     check("sra_compress_ffi", lib.sra_compress_ffi(_p(W), _dt(W), rows, cols, k, ctypes.byref(d), _stream(W.device)))
+    return out
+
+
+def ffi_tile_lists(rows: int, cols: int) -> int:
+    """Entry lists of the tiled fixed fan-in format: one per 32-row group and 64-column stage."""
+    return -(-rows // 32) * -(-cols // 64)
+
+
+def ffi_tile(S: SparseMatrix) -> SparseMatrix:
+    """The products' tiled layout of an ELL weight or of its CSR transpose (bf16): per 32-row group
+    and 64-column stage, a list of packed (value, position) words; values are int32 words."""
+    lib = load()
+    if S.fmt not in (SRA_FMT_ELL, SRA_FMT_CSR):
+        raise ValueError("ffi_tile takes an ELL or CSR matrix")
+    _check_sparse(S, "S")
+    nnz = S.rows * S.k if S.fmt == SRA_FMT_ELL else S.nnz
+    eb, ob = ctypes.c_size_t(), ctypes.c_size_t()
+    check("sra_ffi_tile_size", lib.sra_ffi_tile_size(S.rows, S.cols, nnz, ctypes.byref(eb), ctypes.byref(ob)))
+    ent = torch.empty(max(1, eb.value // 4), dtype=torch.int32, device=S.device)
+    offs = torch.empty(ob.value // 4, dtype=torch.int32, device=S.device)
+    out = SparseMatrix(SRA_FMT_FFI_TILED, S.dtype, S.rows, S.cols, ent, meta=offs, nnz=eb.value // 4)
+    ds, do = S.desc(), out.desc()
+    check("sra_ffi_tile", lib.sra_ffi_tile(ctypes.byref(ds), ctypes.byref(do), _stream(S.device)))
+    out.nnz = int(do.nnz)
     return out
 
 

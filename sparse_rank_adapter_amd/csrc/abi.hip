@@ -116,6 +116,12 @@ sra_status check_sparse(const sra_sparse* S, const char* name) {
     SRA_TRY(check_ptr(S->row_ptr, S->rows > 0, "row_ptr"));
     SRA_TRY(check_ptr(S->values, S->nnz > 0, "values"));
     SRA_TRY(check_ptr(S->index, S->nnz > 0, "index"));
+  } else if (S->format == SRA_FMT_FFI_TILED) {
+    if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "%s: the tiled fixed fan-in format is bf16 only", name);
+    if (S->cols > 32767) return fail(SRA_ERR_INVALID_ARG, "%s: tiled fixed fan-in needs cols <= 32767", name);
+    if (S->nnz < 0 || S->nnz >= ((int64_t)1 << 29)) return fail(SRA_ERR_INVALID_ARG, "%s: bad entry capacity (nnz)", name);
+    SRA_TRY(check_ptr(S->values, S->nnz > 0, "values"));
+    SRA_TRY(check_ptr(S->meta, true, "meta"));
   } else {
     return fail(SRA_ERR_INVALID_ARG, "%s: unknown format %d", name, S->format);
   }
@@ -155,6 +161,9 @@ struct FwdPlan {
 sra_status validate_fwd(const sra_sparse* Ws, int64_t T, int32_t r) {
   SRA_TRY(check_sparse(Ws, "Ws"));
   if (Ws->format == SRA_FMT_CSR) return fail(SRA_ERR_INVALID_ARG, "forward takes an N:M or ELL weight, not CSR");
+  if (Ws->format == SRA_FMT_FFI_TILED && T > 0 && (Ws->cols == 0 || Ws->cols % 64 != 0))
+    return fail(SRA_ERR_UNSUPPORTED, "the tiled fixed fan-in product needs K %% 64 == 0 and K > 0 (K = %lld)",
+                (long long)Ws->cols);
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
   if (Ws->format == SRA_FMT_NM_TILED && !sra::spmm24_tiled_ok(Ws->cols, T))
     return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout needs K %% 128 == 0 above 16 tokens (T = %lld)", (long long)T);
@@ -182,7 +191,8 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
     else if (Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED)
       g = std::max(g, sra::spmm24_ws(Ws->rows, Ws->cols, T));
     p.gemm_off = a.take(g);
-    if (Ws->format == SRA_FMT_ELL) p.ffi_off = a.take(sra::spmm_ffi_ws(Ws->rows, Ws->cols, T));
+    if (Ws->format == SRA_FMT_ELL)
+      p.ffi_off = a.take(sra::spmm_ffi_ws(Ws->rows, Ws->cols, T, Ws->rows * Ws->k));
   }
   if (is12(Ws)) p.meta_off = a.take(meta_bytes(Ws));  // the 2:4 encoding of the metadata
 
@@ -203,11 +213,14 @@ struct BwdPlan {
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
   SRA_TRY(check_sparse(P, "P"));
   if (P->format == SRA_FMT_ELL)
-    return fail(SRA_ERR_INVALID_ARG, "backward takes the double-pruned N:M weight or the CSR transpose");
+    return fail(SRA_ERR_INVALID_ARG, "backward takes the double-pruned N:M weight, the CSR transpose or its tiled form");
   if (P->format == SRA_FMT_NM_TILED && (flags & SRA_GRAD_DX) && !sra::spmm24_tiled_ok(P->cols, T))
     return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout needs N %% 128 == 0 above 16 tokens (T = %lld)", (long long)T);
   if (P->format == SRA_FMT_NM_TILED && P->cols == 0 && (flags & SRA_GRAD_DX))
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 backward needs N > 0");
+  if (P->format == SRA_FMT_FFI_TILED && (flags & SRA_GRAD_DX) && T > 0 && (P->cols == 0 || P->cols % 64 != 0))
+    return fail(SRA_ERR_UNSUPPORTED, "the tiled fixed fan-in dX needs N %% 64 == 0 and N > 0 (N = %lld)",
+                (long long)P->cols);
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
   if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
   if (flags & ~15u) return fail(SRA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
@@ -280,7 +293,7 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   else if (P->dtype == SRA_BF16 && (P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED) && dx)
     p.spmm_off = a.take(sra::spmm24_ws(K, N, T));
   if (P->dtype == SRA_BF16 && P->format == SRA_FMT_CSR && dx)
-    p.spmm_off = a.take(sra::spmm_ffi_ws(K, N, T));
+    p.spmm_off = a.take(sra::spmm_ffi_ws(K, N, T, P->nnz));
   p.total = a.used;
   if (plan) *plan = p;
   return p.total;
@@ -620,6 +633,39 @@ sra_status sra_ffi_transpose(const sra_sparse* Ws, sra_sparse* WsT, void* ws, si
                   s, "ffi_transpose");
 }
 
+sra_status sra_ffi_tile_size(int64_t rows, int64_t cols, int64_t nnz, size_t* entry_bytes,
+                             size_t* offset_bytes) {
+  if (!entry_bytes || !offset_bytes) return fail(SRA_ERR_INVALID_ARG, "entry_bytes / offset_bytes is NULL");
+  if (rows < 0 || cols < 1 || cols > 32767 || nnz < 0 || nnz > rows * cols)
+    return fail(SRA_ERR_INVALID_ARG, "need rows >= 0, 1 <= cols <= 32767, 0 <= nnz <= rows * cols");
+  sra::ffi_tile_bytes(rows, cols, nnz, entry_bytes, offset_bytes);
+  if (*entry_bytes >= ((size_t)1 << 31)) return fail(SRA_ERR_UNSUPPORTED, "tiled format over 2 GiB of entries");
+  return SRA_OK;
+}
+
+sra_status sra_ffi_tile(const sra_sparse* S, sra_sparse* out, void* stream) {
+  SRA_TRY(check_sparse(S, "S"));
+  if (S->format != SRA_FMT_ELL && S->format != SRA_FMT_CSR)
+    return fail(SRA_ERR_INVALID_ARG, "ffi_tile needs an ELL or CSR matrix");
+  if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "ffi_tile: the tiled format is bf16 only");
+  if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
+  const int64_t nnz = S->format == SRA_FMT_ELL ? S->rows * S->k : S->nnz;
+  size_t eb, ob;
+  SRA_TRY(sra_ffi_tile_size(S->rows, S->cols, nnz, &eb, &ob));
+  SRA_TRY(check_ptr(out->values, eb > 0, "out->values"));
+  SRA_TRY(check_ptr(out->meta, true, "out->meta"));
+  out->format = SRA_FMT_FFI_TILED;
+  out->dtype = S->dtype;
+  out->rows = S->rows;
+  out->cols = S->cols;
+  out->nnz = (int64_t)(eb / 4);
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_done(sra::launch_ffi_tile((const uint16_t*)S->values, S->index,
+                                       S->format == SRA_FMT_CSR ? S->row_ptr : nullptr, S->k, S->rows,
+                                       S->cols, (uint32_t*)out->values, out->meta, out->nnz, s),
+                  s, "ffi_tile");
+}
+
 sra_status sra_fwd_workspace(const sra_sparse* Ws, int64_t T, int32_t r, size_t* bytes) {
   SRA_TRY(validate_fwd(Ws, T, r));
   if (!bytes) return fail(SRA_ERR_INVALID_ARG, "bytes is NULL");
@@ -702,9 +748,14 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
                                             (const uint16_t*)X, T, ep, (uint16_t*)Y,
                                             wsb ? wsb + plan.gemm_off : nullptr, s),
                     s, "fwd spmm 2:4");
+  if (Ws->format == SRA_FMT_FFI_TILED)
+    return hip_done(sra::launch_ffi_tiled_bf16((const uint32_t*)Ws->values, Ws->meta, (size_t)Ws->nnz * 4,
+                                               N, K, (const uint16_t*)X, T, ep, (uint16_t*)Y, s),
+                    s, "fwd spmm ffi (tiled)");
   return hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_ELL, (const uint16_t*)Ws->values, Ws->index,
                                             nullptr, Ws->k, N, K, (const uint16_t*)X, T, ep,
-                                            (uint16_t*)Y, wsb ? wsb + plan.ffi_off : nullptr, s),
+                                            (uint16_t*)Y, wsb ? wsb + plan.ffi_off : nullptr, s,
+                                            Ws->rows * Ws->k),
                   s, "fwd spmm ffi");
 }
 
@@ -819,10 +870,15 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
                                                (const uint16_t*)dY, T, ep, (uint16_t*)dX,
                                                wsb ? wsb + plan.spmm_off : nullptr, s),
                        s, "bwd dX 2:4"));
+    else if (P->format == SRA_FMT_FFI_TILED)
+      SRA_TRY(hip_done(sra::launch_ffi_tiled_bf16((const uint32_t*)P->values, P->meta, (size_t)P->nnz * 4,
+                                                  K, N, (const uint16_t*)dY, T, ep, (uint16_t*)dX, s),
+                       s, "bwd dX ffi (tiled)"));
     else
       SRA_TRY(hip_done(sra::launch_spmm_ffi_bf16(SRA_FMT_CSR, (const uint16_t*)P->values, P->index,
                                                  P->row_ptr, 0, K, N, (const uint16_t*)dY, T, ep,
-                                                 (uint16_t*)dX, wsb ? wsb + plan.spmm_off : nullptr, s),
+                                                 (uint16_t*)dX, wsb ? wsb + plan.spmm_off : nullptr, s,
+                                                 P->nnz),
                        s, "bwd dX ffi"));
   }
   // dB and dA: one merged launch (and one slice reduction) when the shapes allow

@@ -213,13 +213,22 @@ hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, 
 void nm_tile_bytes(int64_t R, int64_t C, size_t* value_bytes, size_t* meta_bytes);
 hipError_t launch_nm_tile_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                                void* t_vals, void* t_meta, hipStream_t s);
-// Out[t][row] = sum_c Act[t][c] Wd[row][c] + epilogue, Wd dense bf16 [R][C] (C % 64 == 0)
-hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uint16_t* act, int64_t T,
-                             const Epilogue& ep, uint16_t* out, hipStream_t s);
+// The tiled fixed fan-in format (sra_ffi_tile) of an ELL matrix (row_ptr == nullptr, k entries
+// per row) or a CSR one: entry lists per 32-row group and 64-column stage, and their offsets.
+void ffi_tile_bytes(int64_t R, int64_t C, int64_t nnz, size_t* ent_bytes, size_t* off_bytes);
+hipError_t launch_ffi_tile(const uint16_t* vals, const int16_t* idx, const int32_t* row_ptr, int k,
+                           int64_t R, int64_t C, uint32_t* ent, uint32_t* offs, int64_t cap, hipStream_t s);
+// Out[t][row] = sum over the row's entries of Act[t][col] val + epilogue, from the tiled format
+// (C % 64 == 0, ent_bytes < 2^31); no workspace
+hipError_t launch_ffi_tiled_bf16(const uint32_t* ent, const uint32_t* offs, size_t ent_bytes, int64_t R,
+                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
+                                 uint16_t* out, hipStream_t s);
 // fixed fan-in bf16 SpMM (ELL forward / CSR backward) with the same epilogue; with enough tokens
-// it densifies the weight into the workspace (spmm_ffi_ws bytes) and runs the dense MFMA kernel
-size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T);
-// An ELL (or CSR) matrix written out as R dense bf16 rows of C (C % 8 == 0, C <= 32767).
+// it writes the weight's tiled format into the workspace (spmm_ffi_ws bytes, O(nnz)) and runs
+// the tiled product
+size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T, int64_t nnz);
+// An ELL (or CSR) matrix written out as R dense bf16 rows of C (C % 8 == 0, C <= 32767): the
+// fixed fan-in adapter factor's dense copy.
 hipError_t launch_ffi_densify(int format, const uint16_t* vals, const int16_t* idx,
                               const int32_t* row_ptr, int k, int64_t R, int64_t C, uint16_t* out,
                               hipStream_t s);
@@ -229,7 +238,7 @@ hipError_t launch_ell_gather_f32(const float* dense, const int16_t* idx, int k, 
 hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t* idx,
                                 const int32_t* row_ptr, int k, int64_t R, int64_t C,
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
-                                void* ws, hipStream_t s);
+                                void* ws, hipStream_t s, int64_t nnz);
 
 // Adapter products (fp32 results):
 //   rows: out[t][j] = sum_c act[t][c] * wt[j*ldw + c]                              (U, dU)

@@ -10,6 +10,16 @@
 // ffi_transpose: rows are cut into 64-row chunks.  Counting per (chunk, column) and a scan over
 // chunks give every chunk a private output cursor per column; a chunk's rows are then scattered
 // in row order by one workgroup, so CSR rows come out sorted by original row without a sort.
+//
+// ffi_tile: the product's layout of an ELL or CSR matrix.  Rows are cut into 32-row groups and
+// columns into 64-column stages; list (group g, stage x) holds the group's entries in that stage
+// as 32-bit words (bf16 value in the low half, (row - 32 g) * 64 + (column - 64 x) in the high
+// half), ordered by row and then column, and padded to a multiple of four words with 0xffffffff.
+// Lists follow each other group by group, stage by stage; offsets[g * stages + x] is the first
+// word of list (g, x), and the word count plus three more copies of it close the array.  Counting
+// per list, one scan over the lists, then per group a count per (row, stage) turns into each
+// entry's rank: the entries of earlier rows in the same stage plus the entry's place in its row's
+// run of that stage (a row's columns ascend, so a stage's entries are one run of the row).
 #include "common.h"
 
 namespace {
@@ -178,9 +188,146 @@ __global__ __launch_bounds__(256) void k_ffi_scatter(const T* __restrict__ vals,
   }
 }
 
+// list sizes of one 32-row group, padded to whole 16-byte words (row_ptr == nullptr: ELL)
+__global__ __launch_bounds__(256) void k_ffi_tile_count(const int16_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ row_ptr, int k,
+                                                        int64_t R, int nst, uint32_t* __restrict__ offs) {
+  extern __shared__ uint32_t cnt[];  // nst
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x, r0 = g * 32, r1 = min(R, r0 + 32);
+  for (int x = tid; x < nst; x += 256) cnt[x] = 0;
+  __syncthreads();
+  const int64_t b = row_ptr ? row_ptr[r0] : r0 * k, e = row_ptr ? row_ptr[r1] : r1 * k;
+  for (int64_t i = b + tid; i < e; i += 256) atomicAdd(&cnt[idx[i] >> 6], 1u);
+  __syncthreads();
+  for (int x = tid; x < nst; x += 256) offs[g * nst + x] = (cnt[x] + 3u) & ~3u;
+}
+
+// exclusive scan of the n list sizes in place; the total goes to offs[n .. n+3]
+__global__ __launch_bounds__(1024) void k_ffi_tile_scan(uint32_t* __restrict__ offs, int64_t n) {
+  __shared__ uint32_t sm[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024, b = min(n, tid * per), e = min(n, b + per);
+  uint32_t sum = 0;
+  for (int64_t i = b; i < e; ++i) sum += offs[i];
+  sm[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t add = tid >= off ? sm[tid - off] : 0u;
+    __syncthreads();
+    sm[tid] += add;
+    __syncthreads();
+  }
+  uint32_t run = sm[tid] - sum;
+  const uint32_t total = sm[1023];
+  for (int64_t i = b; i < e; ++i) {
+    const uint32_t v = offs[i];
+    offs[i] = run;
+    run += v;
+  }
+  if (tid < 4) offs[n + tid] = total;
+}
+
+// one 32-row group: every entry written at its list's offset plus its rank, then the padding
+__global__ __launch_bounds__(256) void k_ffi_tile_fill(const uint16_t* __restrict__ vals,
+                                                       const int16_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ row_ptr, int k,
+                                                       int64_t R, int nst, const uint32_t* __restrict__ offs,
+                                                       uint32_t* __restrict__ ent, int64_t cap) {
+  extern __shared__ uint32_t sm[];
+  // per half group of 16 rows: cnt[i][x] (entries of row i in stage x, then the entries of the
+  // group's earlier rows in stage x), pre[i][x] (entries of row i in earlier stages), both 16-bit;
+  // run[x] (entries of the group's rows so far in stage x), base[x] (list offset), part[256]
+  uint32_t* cntw = sm;
+  uint16_t* cnt = reinterpret_cast<uint16_t*>(cntw);
+  uint16_t* pre = cnt + 16 * nst;
+  uint32_t* run = sm + 16 * nst;
+  uint32_t* base = run + nst;
+  uint32_t* part = base + nst;
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  for (int x = tid; x < nst; x += 256) {
+    run[x] = 0;
+    base[x] = offs[g * nst + x];
+  }
+  auto row_beg = [&](int64_t row) -> int64_t { return row_ptr ? row_ptr[row] : row * k; };
+  for (int h = 0; h < 2; ++h) {
+    const int64_t r0 = g * 32 + 16 * h;
+    for (int w = tid; w < 8 * nst; w += 256) cntw[w] = 0;
+    __syncthreads();
+    for (int i = 0; i < 16 && r0 + i < R; ++i) {
+      const int64_t b = row_beg(r0 + i), e = row_beg(r0 + i + 1);
+      for (int64_t q = b + tid; q < e; q += 256) {
+        const int j = i * nst + (idx[q] >> 6);
+        atomicAdd(&cntw[j >> 1], 1u << (16 * (j & 1)));  // counts stay <= 64: no carry between halves
+      }
+    }
+    __syncthreads();
+    // pre: per row, an exclusive scan over the stages (16 lanes per row, each a run of stages)
+    {
+      const int i = tid >> 4, p = tid & 15, seg = (nst + 15) / 16;
+      const int xb = min(nst, p * seg), xe = min(nst, xb + seg);
+      uint32_t sum = 0;
+      for (int x = xb; x < xe; ++x) sum += cnt[i * nst + x];
+      part[tid] = sum;
+      __syncthreads();
+      uint32_t acc = 0;
+      for (int q = 0; q < p; ++q) acc += part[i * 16 + q];
+      for (int x = xb; x < xe; ++x) {
+        pre[i * nst + x] = (uint16_t)acc;
+        acc += cnt[i * nst + x];
+      }
+    }
+    __syncthreads();
+    // cnt -> entries of the group's earlier rows in the stage
+    for (int x = tid; x < nst; x += 256) {
+      uint32_t r = run[x];
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t c = cnt[i * nst + x];
+        cnt[i * nst + x] = (uint16_t)r;
+        r += c;
+      }
+      run[x] = r;
+    }
+    __syncthreads();
+    for (int i = 0; i < 16 && r0 + i < R; ++i) {
+      const int64_t b = row_beg(r0 + i), e = row_beg(r0 + i + 1);
+      for (int64_t q = b + tid; q < e; q += 256) {
+        const int col = idx[q], x = col >> 6;
+        const uint32_t pos = base[x] + cnt[i * nst + x] + ((uint32_t)(q - b) - pre[i * nst + x]);
+        if (pos < cap) ent[pos] = (uint32_t)vals[q] | ((uint32_t)((16 * h + i) * 64 + (col & 63)) << 16);
+      }
+    }
+    __syncthreads();
+  }
+  for (int x = tid; x < nst; x += 256) {
+    const uint32_t end = (uint32_t)min((int64_t)offs[g * nst + x + 1], cap);
+    for (uint32_t q = base[x] + run[x]; q < end; ++q) ent[q] = 0xffffffffu;
+  }
+}
+
 }  // namespace
 
 namespace sra {
+
+void ffi_tile_bytes(int64_t R, int64_t C, int64_t nnz, size_t* ent_bytes, size_t* off_bytes) {
+  const int64_t lists = ((R + 31) / 32) * ((C + 63) / 64);
+  *ent_bytes = (size_t)(nnz + 3 * lists) * 4;
+  *off_bytes = (size_t)(lists + 4) * 4;
+}
+
+hipError_t launch_ffi_tile(const uint16_t* vals, const int16_t* idx, const int32_t* row_ptr, int k,
+                           int64_t R, int64_t C, uint32_t* ent, uint32_t* offs, int64_t cap, hipStream_t s) {
+  const int64_t groups = (R + 31) / 32, nst = (C + 63) / 64, lists = groups * nst;
+  if (lists > 0)
+    hipLaunchKernelGGL(k_ffi_tile_count, dim3((unsigned)groups), dim3(256), (size_t)nst * 4, s, idx,
+                       row_ptr, k, R, (int)nst, offs);
+  hipLaunchKernelGGL(k_ffi_tile_scan, dim3(1), dim3(1024), 0, s, offs, lists);
+  if (lists > 0)
+    hipLaunchKernelGGL(k_ffi_tile_fill, dim3((unsigned)groups), dim3(256), (size_t)(18 * nst + 256) * 4, s,
+                       vals, idx, row_ptr, k, R, (int)nst, offs, ent, cap);
+  return hipGetLastError();
+}
 
 hipError_t launch_compress_ffi(int dtype, const void* W, int64_t rows, int64_t cols, int k,
                                void* vals, int16_t* idx, hipStream_t s) {

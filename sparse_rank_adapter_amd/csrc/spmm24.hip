@@ -698,16 +698,33 @@ bool fuse_ok(const Plan& p, int64_t C, int r) {
 
 namespace sra {
 
-hipError_t launch_dense_bf16(const uint16_t* Wd, int64_t R, int64_t C, const uint16_t* act, int64_t T,
-                             const Epilogue& ep, uint16_t* out, hipStream_t s) {
+// The fixed fan-in product on the tiled entry lists of sra_ffi_tile: the dense-weight (DN) tiles
+// of the SpMM kernel, with each stage's A tile written from the entries in LDS instead of
+// transferred (C % 64 == 0).
+// Lists of up to 256 entries per 32 rows and stage ride the ring (longer ones finish from memory);
+// denser weights (more than 216 words per list on average: at 10.5% density a list of 2048
+// cells holds 215 +- 14 entries, so 256 covers all but a few) take the four-wave tile with
+// 1024-entry slots.
+hipError_t launch_ffi_tiled_bf16(const uint32_t* ent, const uint32_t* offs, size_t ent_bytes, int64_t R,
+                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
+                                 uint16_t* out, hipStream_t s) {
   if (T == 0 || R == 0) return hipSuccess;
-  if (C % 64 != 0 || ep.G || !epilogue_ok(ep, R)) return hipErrorInvalidValue;
+  if (C <= 0 || C % 64 != 0 || ep.G || !epilogue_ok(ep, R) || ent_bytes >= ((size_t)1 << 31))
+    return hipErrorInvalidValue;
   Plan p{cfg_by_id(13), 1, (int)(C / 64)};
-  const int64_t big = ((R + 255) / 256) * ((T + 127) / 128);
-  if (big >= 240)  // eight waves, 256x128 tiles, 3 stages of 48 KB
-    launch_q<4, 4, 4, 2, 3, 0, 0, true>(Wd, nullptr, R, C, act, T, ep, out, nullptr, p, s, SRA_KERNEL_SPMM_FFI);
-  else             // four waves, 128x64 tiles, 4 stages of 24 KB
-    launch_q<4, 2, 2, 2, 4, 0, 0, true>(Wd, nullptr, R, C, act, T, ep, out, nullptr, p, s, SRA_KERNEL_SPMM_FFI);
+  const auto* v = reinterpret_cast<const uint16_t*>(ent);
+  const uint32_t eb = (uint32_t)ent_bytes;
+  const int64_t lists = ((R + 31) / 32) * (C / 64);
+  const int64_t huge = ((R + 255) / 256) * ((T + 255) / 256), big = ((R + 255) / 256) * ((T + 127) / 128);
+  constexpr int K = SRA_KERNEL_SPMM_FFI;
+  if ((int64_t)(ent_bytes / 4) > 216 * lists)  // four waves, 128x64 tiles, 3 stages, 1024-entry slots
+    launch_q<4, 2, 2, 2, 3, 0, 0, true, false, false, 0, 1024>(v, offs, R, C, act, T, ep, out, nullptr, p, s, K, eb);
+  else if (huge >= 240)  // eight waves, 256x256 tiles, 2 stages of 32 KB + 8 KB of entries
+    launch_q<4, 8, 4, 2, 2, 0, 0, true, false, false, 0, 256>(v, offs, R, C, act, T, ep, out, nullptr, p, s, K, eb);
+  else if (big >= 240)   // eight waves, 256x128 tiles, 3 stages of 16 KB + 8 KB
+    launch_q<4, 4, 4, 2, 3, 0, 0, true, false, false, 0, 256>(v, offs, R, C, act, T, ep, out, nullptr, p, s, K, eb);
+  else                   // four waves, 128x64 tiles, 3 stages of 8 KB + 4 KB, two workgroups per CU
+    launch_q<4, 2, 2, 2, 3, 0, 0, true, false, false, 0, 256>(v, offs, R, C, act, T, ep, out, nullptr, p, s, K, eb);
   return hipGetLastError();
 }
 

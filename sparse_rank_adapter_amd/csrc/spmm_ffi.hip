@@ -198,16 +198,20 @@ __global__ __launch_bounds__(256) void k_ell_gather_f32(const float* __restrict_
   out[e] = dense[(e / k) * C + idx[e]];
 }
 
-// The densified product pays one pass writing R x C bf16 and then runs at dense MFMA rate; worth
-// it once the token tile is wide enough to reuse each weight row many times.
-bool use_dense(int64_t R, int64_t C, int64_t T) { return T >= 128 && C % 64 == 0 && C * 2 <= 65536 && R > 0; }
+// The tiled product (matrix cores on a dense A tile written from the entries in LDS) pays one
+// pass building the tiled format; worth it once the token tile is wide enough to reuse each weight
+// row many times.
+bool use_tiled(int64_t R, int64_t C, int64_t T) { return T >= 128 && C % 64 == 0 && R > 0; }
 
 }  // namespace
 
 namespace sra {
 
-size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T) {
-  return use_dense(R, C, T) ? (size_t)R * C * 2 : 0;
+size_t spmm_ffi_ws(int64_t R, int64_t C, int64_t T, int64_t nnz) {
+  if (!use_tiled(R, C, T)) return 0;
+  size_t eb, ob;
+  ffi_tile_bytes(R, C, nnz, &eb, &ob);
+  return ((eb + 255) & ~(size_t)255) + ob;
 }
 
 hipError_t launch_ffi_densify(int format, const uint16_t* vals, const int16_t* idx,
@@ -231,16 +235,18 @@ hipError_t launch_ell_gather_f32(const float* dense, const int16_t* idx, int k, 
 hipError_t launch_spmm_ffi_bf16(int format, const uint16_t* vals, const int16_t* idx,
                                 const int32_t* row_ptr, int k, int64_t R, int64_t C,
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
-                                void* ws, hipStream_t s) {
+                                void* ws, hipStream_t s, int64_t nnz) {
   if (T == 0 || R == 0) return hipSuccess;
-  if (use_dense(R, C, T)) {
+  if (use_tiled(R, C, T)) {
     if (!ws) return hipErrorInvalidValue;
-    uint16_t* Wd = (uint16_t*)ws;
-    launch(SRA_KERNEL_FFI_DENSIFY, k_ffi_densify, dim3((unsigned)R), dim3(256), (size_t)C * 2, s,
-           format, vals, idx, row_ptr, k, C, Wd);
-    const hipError_t e = hipGetLastError();
+    size_t eb, ob;
+    ffi_tile_bytes(R, C, nnz, &eb, &ob);
+    uint32_t* ent = (uint32_t*)ws;
+    uint32_t* offs = (uint32_t*)((char*)ws + ((eb + 255) & ~(size_t)255));
+    hipError_t e = launch_ffi_tile(vals, idx, format == SRA_FMT_ELL ? nullptr : row_ptr, k, R, C, ent, offs,
+                                   (int64_t)(eb / 4), s);
     if (e != hipSuccess) return e;
-    return launch_dense_bf16(Wd, R, C, act, T, ep, out, s);
+    return launch_ffi_tiled_bf16(ent, offs, eb, R, C, act, T, ep, out, s);
   }
   const dim3 grid((unsigned)((T + TT - 1) / TT), (unsigned)((R + RB - 1) / RB));
   launch(SRA_KERNEL_SPMM_FFI, k_spmm_ffi, grid, dim3(256), 0, s, format, vals, idx, row_ptr, k, R,

@@ -278,31 +278,45 @@ SRA_DEV bf16x8 expand28(uint32_t s, uint32_t m) {
 // super-stage ahead; needs C % 128 == 0, and a split of the reduction must start on an 8-stage
 // boundary (the planner splits only the 256x256 tile, so).
 // UG > 0: adapter rows in the activation region as in PTile (GT transfers over NW waves).
-// DN: the weight is dense (rows of C bf16, 128 bytes per row and stage, no metadata) and the
-// products are pairs of dense v_mfma_f32_16x16x32_bf16 -- the fixed fan-in layer's densified
-// weight.
+// DN: the weight tile is dense (rows of 128 bytes per stage, no metadata) and the products are
+// pairs of dense v_mfma_f32_16x16x32_bf16; with FE > 0 (below) the tile is written in LDS from the
+// fixed fan-in entry lists, otherwise it is transferred from dense rows of C bf16.
 // NM = 24 / 28: the weight is 2:4 / 2:8 and each fragment is expanded to dense bf16 before the same
 // pairs of dense MFMAs (expand24 / expand28).  2:8 rows carry 32 bytes of stored values per
 // 64-column stage (two 16-byte chunks, slot = chunk ^ ((row >> 3) & 1)) and the same 8 bytes of
 // metadata per stage as 2:4 (one byte per 8-column group), so the metadata transfers are 2:4's.
-template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, int NM = 0>
+// FE > 0 (with DN): the fixed fan-in weight arrives in the tiled entry lists of sra_ffi_tile
+// instead of dense rows.  Each wave owns 32 rows of the tile; per 64-column stage it copies up to
+// FE of its rows' entries into LDS (LDS-DMA, with the activations), and one stage ahead of the
+// products it clears its 32 rows of a dense 128-byte-row A tile and writes each entry's value at
+// its (row, column).  The A tile is double-buffered apart from the ring (it is written with
+// ordinary LDS stores one stage ahead, not transferred); the entry lists ride the ring.
+template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, int NM = 0,
+          int FE = 0>
 struct QTile {
   static_assert(!(DN && (MS || UG)), "dense weights have no metadata or adapter rows");
   static_assert(NM == 0 || NM == 24 || NM == 28, "2:4 SMFMAC, or 2:4 / 2:8 expanded to dense");
+  static_assert(FE == 0 || (DN && FE % 256 == 0), "fixed fan-in entry lists: dense products, whole 1 KB transfers");
   static constexpr int NW = WR * WT;  // waves per workgroup: 4 or 8
   static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
+  static_assert(FE == 0 || BR == 32 * NW, "fixed fan-in: 32 weight rows per wave");
   static constexpr int VB = NM == 28 ? 32 : 64;  // stored-value bytes per weight row and stage
-  static constexpr int LA = BR / ((DN ? 8 : NM == 28 ? 32 : 16) * NW), LM = (MS || DN) ? 0 : BR / (32 * NW);
+  static constexpr int LA = FE ? 0 : BR / ((DN ? 8 : NM == 28 ? 32 : 16) * NW);
+  static constexpr int LM = (MS || DN) ? 0 : BR / (32 * NW);
   static constexpr int LB = BT / (8 * NW);
+  static constexpr int LE = FE / 256;  // 1 KB entry transfers per wave and stage
   static constexpr int GT = UG / 8, GW = GT / NW, GX = GT % NW;
-  static constexpr int L = LA + LM + LB + GW;  // waves >= GX
-  static constexpr int L1 = L + (GX ? 1 : 0);  // waves < GX
-  static constexpr int A_BYTES = BR * (DN ? 128 : VB), M_BYTES = (MS || DN) ? 0 : BR * 8;
+  static constexpr int L = LA + LM + LB + GW + LE;  // waves >= GX
+  static constexpr int L1 = L + (GX ? 1 : 0);       // waves < GX
+  static constexpr int A_BYTES = FE ? 0 : BR * (DN ? 128 : VB), M_BYTES = (MS || DN) ? 0 : BR * 8;
   static constexpr int B_BYTES = (BT + UG) * 128;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
   static constexpr int MSB = MS ? BR * MS * 8 : 0;            // one metadata super-stage buffer
   static constexpr int LMS = MS ? MSB / (1024 * NW) : 0;      // its 1 KB transfers per wave
-  static constexpr int LDS = NS * STAGE + 2 * MSB;
+  static constexpr int ABUF = FE ? 2 * BR * 128 : 0;          // the two scattered A tiles
+  static constexpr int EBUF = NS * NW * FE * 4;               // entry lists, one per wave and ring slot
+  static constexpr int OTAB = FE ? NW * 512 * 4 : 0;          // each wave's list offsets (<= 511 stages)
+  static constexpr int LDS = NS * STAGE + 2 * MSB + ABUF + EBUF + OTAB;
   static constexpr int OCC = (NW == 8 || FR * FT >= 32 || 2 * LDS > 160 * 1024) ? 1 : 2;
 };
 
@@ -311,13 +325,16 @@ struct QTile {
 // the values reads 1 KB contiguously instead of 64-byte runs per row, and a super-stage of
 // metadata reads 64-byte (MS = 8) or 32-byte (MS = 4) pieces of those blocks.  Same LDS layout and
 // products; needs MS > 0.
+// FE > 0: s_vals holds the tiled fixed fan-in entries (ent_bytes bytes) and s_meta their list
+// offsets (sra_ffi_tile); C % 64 == 0, no splits.
 template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false,
-          bool PP = false, int NM = 0>
-__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN, NM>::OCC)) void k_spmm24_q(
+          bool PP = false, int NM = 0, int FE = 0>
+__global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN, NM, FE>::OCC)) void k_spmm24_q(
     const uint16_t* __restrict__ s_vals, const uint32_t* __restrict__ s_meta, int64_t R, int64_t C,
     const uint16_t* __restrict__ act, int64_t T, sra::Epilogue ep, uint16_t* __restrict__ out,
-    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split, int n_whole) {
-  using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN, NM>;
+    float* __restrict__ part, int n_rt, int n_tt, int stages_per_split, int n_whole,
+    uint32_t ent_bytes) {
+  using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN, NM, FE>;
   constexpr int BR = TL::BR, BT = TL::BT, L = TL::L;
   constexpr int NW = TL::NW;
   using AD = AdapterRows<BT, (UG > 0 ? UG : 16), NW>;
@@ -331,6 +348,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   static_assert(!PP || (NW == 8 && MS > 0 && UG == 0 && !DN && NM == 0), "ping-pong: eight waves, super-stages");
   static_assert(NM == 0 || !DN, "an expanded N:M weight is not a dense one");
   static_assert(NM != 28 || (!TLAY && BR % (32 * NW) == 0), "2:8: canonical arrays, whole transfers");
+  static_assert(FE == 0 || (!TLAY && !PP), "fixed fan-in entry lists: their own schedule");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TL::LDS];
 
   const int tid = threadIdx.x;
@@ -379,8 +397,8 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
       (void*)(act + t0 * C), 0, toks_here * (int)C * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
       (void*)ep.G, 0, UG > 0 ? ep.r * (int)ep.g_ld * 2 : 0, 0x00020000);
-  uint32_t a_off[TL::LA];
-  int a_dst[TL::LA];
+  uint32_t a_off[TL::LA ? TL::LA : 1];
+  int a_dst[TL::LA ? TL::LA : 1];
 #pragma unroll
   for (int k = 0; k < TL::LA; ++k) {
     const int b = k * NW + wave;
@@ -460,8 +478,103 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     g_off[k] = (uint32_t)(((tk - BT) * ep.g_ld + ch * 8) * 2);
     g_dst[k] = TL::A_BYTES + TL::M_BYTES + (BT / 8 + b) * 1024;
   }
+  // fixed fan-in: this wave's 32-row group, the entry lists' ring slots, the two A tiles after the
+  // operand ring, and the group's list offsets (stage x: words otab[x] .. otab[x+1]) copied to LDS
+  // once, so that reading them waits only on the wave's own earlier LDS work
+  const int nst = (int)(C >> 6);
+  const int64_t g_w = (row0 >> 5) + wave;
+  const bool g_in = FE > 0 && g_w * 32 < R;
+  const __amdgpu_buffer_rsrc_t rent = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(FE ? s_vals : nullptr), 0, FE ? (int)ent_bytes : 0, 0x00020000);
+  uint8_t* const abuf = smem + NS * TL::STAGE + 2 * TL::MSB;
+  uint8_t* const ebuf = abuf + TL::ABUF;
+  uint32_t* const otab = reinterpret_cast<uint32_t*>(ebuf + TL::EBUF) + wave * 512;
+  if constexpr (FE > 0) {
+    const uint32_t* og = s_meta + (g_in ? g_w * nst : 0);
+    for (int i = lane; i <= nst; i += 64) otab[i] = g_in ? og[i] : 0u;
+  }
+  auto fe_start = [&](int x) -> uint32_t { return otab[x]; };
+  auto eslot = [&](int slot) { return ebuf + (slot * NW + wave) * FE * 4; };
+  auto fe_tile = [&](int rel) { return abuf + (rel & 1) * (TL::BR * 128); };
+  // one entry into the wave's rows of A tile `at`: bf16 value in the low half, (row in the group)
+  // * 64 + (column in the stage) in the high half; padding entries (position >= 2048) are skipped
+  auto fe_put = [&](uint8_t* at, uint32_t e) {
+    const uint32_t pos = e >> 16;
+    if (pos < 2048) {
+      const int r = wave * 32 + (int)(pos >> 6), col = (int)(pos & 63);
+      *reinterpret_cast<uint16_t*>(at + r * 128 + (((col >> 3) ^ ((r >> 1) & 7)) << 4) + (col & 7) * 2) =
+          (uint16_t)e;
+    }
+  };
+  auto fe_clear = [&](uint8_t* at) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(at + wave * 4096 + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+  };
+  // entries q .. n-1 of a list starting at word e0, straight from memory (four per lane at a time)
+  auto fe_from_memory = [&](uint8_t* at, uint32_t e0, uint32_t q, uint32_t n) {
+    for (; q < n; q += 256) {
+      const uint32_t q0 = q + (uint32_t)lane * 4;
+      if (q0 < n) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rent, (e0 + q0) * 4, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (q0 + i < n) fe_put(at, v[i]);
+      }
+    }
+  };
+  // the first stage's A tile, all from memory
+  auto fe_scatter_direct = [&](int rel) {
+    uint8_t* at = fe_tile(rel);
+    fe_clear(at);
+    const uint32_t e0 = __builtin_amdgcn_readfirstlane(fe_start(c_beg + rel));
+    const uint32_t n = min(__builtin_amdgcn_readfirstlane(fe_start(c_beg + rel + 1)) - e0, 2048u);
+    fe_from_memory(at, e0, 0, n);
+  };
+  // later stages in two steps between the products of the stage before: (1) clear the A tile's
+  // rows, read the list's bounds, its first FE words from the ring slot and the start of the list
+  // the next transfer brings in; (2) a few products later, write the entries (a list holds at most
+  // 32 * 64 words; past FE they come from memory)
+  u32x4 fe_ev[TL::LE ? TL::LE : 1];
+  uint32_t fe_lo = 0, fe_hi = 0, fe_dma = 0;
+  // (step 1 runs whether or not the stage exists, with its table reads clamped, so that nothing
+  // waits for these reads before step 2 uses them; the tile it clears is not read again)
+  auto fe_step1 = [&](int rel) {  // during the products of stage c_beg + rel
+    const int x = c_beg + rel + 1;
+    fe_clear(fe_tile(rel + 1));
+    fe_lo = fe_start(min(x, nst));
+    fe_hi = fe_start(min(x + 1, nst));
+    fe_dma = fe_start(min(x + NS - 1, nst));  // the list the next transfer brings in
+    const uint8_t* es = eslot((rel + 1) % NS);
+#pragma unroll
+    for (int k = 0; k < TL::LE; ++k) fe_ev[k] = *reinterpret_cast<const u32x4*>(es + (k * 256 + lane * 4) * 4);
+  };
+  auto fe_step2 = [&](int rel) {
+    const int x = c_beg + rel + 1;
+    if (x < c_end) {
+      uint8_t* at = fe_tile(rel + 1);
+      const uint32_t e0 = __builtin_amdgcn_readfirstlane(fe_lo);
+      const uint32_t n = min(__builtin_amdgcn_readfirstlane(fe_hi) - e0, 2048u);
+#pragma unroll
+      for (int k = 0; k < TL::LE; ++k) {
+        const uint32_t q0 = (uint32_t)(k * 256 + lane * 4);
+        if (q0 < n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (q0 + i < n) fe_put(at, fe_ev[k][i]);
+        }
+      }
+      if (n > (uint32_t)FE) fe_from_memory(at, e0, FE, n);
+    }
+  };
   auto issue = [&](int c, int buf) {
     uint8_t* base = smem + buf * TL::STAGE;
+    // the entry list of stage c + 1 goes first (ring slot buf + 1), so that waiting for stage c's
+    // transfers also covers it
+    const uint32_t e_start = FE ? __builtin_amdgcn_readfirstlane(fe_dma) : 0u;  // list of stage c + 1
+#pragma unroll
+    for (int k = 0; k < TL::LE; ++k)
+      bdma(rent, eslot((buf + 1) % NS) + k * 1024, 16, (uint32_t)(k * 1024 + lane * 16), e_start * 4);
 #pragma unroll
     for (int k = 0; k < TL::LA; ++k) bdma(ra, base + a_dst[k], 16, a_off[k], c * A_ROW);
 #pragma unroll
@@ -487,12 +600,12 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   // compute(buf, rel, post): the products of the stage in buffer buf; post() issues the transfers
   // of a later stage and runs before the products, or between them in the interleaved schedule
   auto compute = [&](int buf, int rel, auto&& post) {
-    if constexpr (!kIlv) post();
-    const uint8_t* A = smem + buf * TL::STAGE;
-    const uint32_t* M = reinterpret_cast<const uint32_t*>(A + TL::A_BYTES);
+    if constexpr (!kIlv && !DN) post();
+    const uint8_t* A = FE ? fe_tile(rel) : smem + buf * TL::STAGE;
+    const uint32_t* M = reinterpret_cast<const uint32_t*>(smem + buf * TL::STAGE + TL::A_BYTES);
     const uint8_t* MS_buf = msbuf + (MS ? ((rel / (MS ? MS : 1)) & 1) * TL::MSB : 0);
     const int u = MS ? rel % (MS ? MS : 1) : 0;
-    const uint8_t* B = A + TL::A_BYTES + TL::M_BYTES;
+    const uint8_t* B = smem + buf * TL::STAGE + TL::A_BYTES + TL::M_BYTES;
     if constexpr (UG > 0) ad.flush();
     bf16x16 bfr[FT];
     if constexpr (kIlv) {
@@ -535,33 +648,55 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
       }
       return;
     }
-#pragma unroll
-    for (int j = 0; j < FT; ++j) {
-      const int tk = wt * 16 * FT + j * 16 + l16, sw = (tk >> 1) & 7;
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + ((q4 ^ sw) << 4));
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
-      bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-    }
     if constexpr (DN) {
-      // dense weight rows: columns 8(l/16)..+7 and 32+8(l/16)..+7 of the stage, one dense MFMA each
+      // dense weight rows: columns 8(l/16)..+7 and 32+8(l/16)..+7 of the stage, one dense MFMA
+      // each.  The same interleaved order as the SMFMAC schedule: the wave's row fragments first,
+      // then one column fragment at a time (read two columns ahead), the later stage's transfers
+      // issued after the second column's first products.
       bf16x8 alo[FR], ahi[FR];
+      auto read_col = [&](int j) {
+        const int tk = wt * 16 * FT + j * 16 + l16, sw = (tk >> 1) & 7;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + ((q4 ^ sw) << 4));
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
+        bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      };
 #pragma unroll
       for (int i = 0; i < FR; ++i) {
         const int r = wr * 16 * FR + i * 16 + l16, sw = (r >> 1) & 7;
         alo[i] = *reinterpret_cast<const bf16x8*>(A + r * 128 + ((q4 ^ sw) << 4));
         ahi[i] = *reinterpret_cast<const bf16x8*>(A + r * 128 + (((4 + q4) ^ sw) << 4));
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+      constexpr int CA = kIlvAhead < FT ? kIlvAhead : FT;
 #pragma unroll
-      for (int i = 0; i < FR; ++i)
+      for (int j = 0; j < CA; ++j) read_col(j);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < FT; ++j) {
-          const bf16x8 blo = __builtin_shufflevector(bfr[j], bfr[j], 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 bhi = __builtin_shufflevector(bfr[j], bfr[j], 8, 9, 10, 11, 12, 13, 14, 15);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[i], blo, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[i], bhi, acc[i][j], 0, 0, 0);
+      for (int k = 0; k < FR * FT; ++k) {
+        const int j = k / FR, i = k % FR;
+        const bf16x8 blo = __builtin_shufflevector(bfr[j], bfr[j], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 bhi = __builtin_shufflevector(bfr[j], bfr[j], 8, 9, 10, 11, 12, 13, 14, 15);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[i], blo, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[i], bhi, acc[i][j], 0, 0, 0);
+        if (i == 0 && j + CA < FT) read_col(j + CA);
+        constexpr int kS1 = FT > 1 ? FR : 0, kS2 = 2 * FR < FR * FT - 1 ? 2 * FR : FR * FT - 1;
+        if (k == kS1) {
+          if constexpr (FE > 0) fe_step1(rel);
+          else post();
         }
+        if (FE > 0 && k == kS2) {
+          fe_step2(rel);
+          post();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       return;
+    }
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int tk = wt * 16 * FT + j * 16 + l16, sw = (tk >> 1) & 7;
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(B + tk * 128 + ((q4 ^ sw) << 4));
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(B + tk * 128 + (((4 + q4) ^ sw) << 4));
+      bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     }
     if constexpr (NM != 0) {
       // Expanded N:M: per weight fragment the stored values and both metadata words of the row's
@@ -723,16 +858,28 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   if constexpr (MS > 0) {
     if (c_beg < c_end) issue_meta(0);
   }
+  // fixed fan-in: the first stage's A tile from memory; later ones one stage ahead from the ring
+  if constexpr (FE > 0) {
+    if (c_beg < c_end) fe_scatter_direct(0);
+  }
+  // the scattered A tile is written with LDS stores, which the bare barrier does not wait for
+  auto stage_barrier = [&] {
+    if constexpr (FE > 0) __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+    ring_barrier();
+  };
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (c_beg + d < c_end) issue(c_beg + d, d);
+    if (c_beg + d < c_end) {
+      if constexpr (FE > 0) fe_dma = fe_start(c_beg + d + 1);
+      issue(c_beg + d, d);
+    }
   int c = c_beg;
   for (; kUnroll && c + NS + D <= c_end; c += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       if (TL::GX && wave < TL::GX) wait_vm<((D - 1) * TL::L1 < 63 ? (D - 1) * TL::L1 : 63)>();
       else wait_vm<((D - 1) * L < 63 ? (D - 1) * L : 63)>();
-      ring_barrier();
+      stage_barrier();
       const int rel = c + u - c_beg;
       compute(u, rel, [&] {
         if constexpr (MS > 0) {
@@ -746,7 +893,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
     const int in_flight = min(D, c_end - c);
     if (TL::GX && wave < TL::GX) wait_stages<TL::L1>(in_flight);
     else wait_stages<L>(in_flight);
-    ring_barrier();
+    stage_barrier();
     const int rel = c - c_beg;
     compute(rel % NS, rel, [&] {
       if constexpr (MS > 0) {
@@ -1031,16 +1178,17 @@ struct Plan {
 };
 
 template <int FR, int FT, int WR, int WT, int NS, int MS = 0, int UG = 0, bool DN = false, bool TLAY = false,
-          bool PP = false, int NM = 0>
+          bool PP = false, int NM = 0, int FE = 0>
 void launch_q(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
               const uint16_t* act, int64_t T, const sra::Epilogue& ep, uint16_t* out, float* part,
-              const Plan& p, hipStream_t s, int which = SRA_KERNEL_SPMM24) {
-  using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN, NM>;
+              const Plan& p, hipStream_t s, int which = SRA_KERNEL_SPMM24, uint32_t ent_bytes = 0) {
+  using TL = QTile<FR, FT, WR, WT, NS, MS, UG, DN, NM, FE>;
   const int n_rt = (int)((R + TL::BR - 1) / TL::BR), n_tt = (int)((T + TL::BT - 1) / TL::BT);
   const int n = n_rt * n_tt, n_whole = p.tail ? n - n % 256 : -1;
   const dim3 grid = p.tail ? dim3((unsigned)(n_whole + 2 * (n - n_whole))) : dim3((unsigned)n, (unsigned)p.splits);
-  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN, TLAY, PP, NM>, grid, dim3(64 * TL::NW), 0, s,
-              s_vals, s_meta, R, C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split, n_whole);
+  sra::launch(which, k_spmm24_q<FR, FT, WR, WT, NS, MS, UG, DN, TLAY, PP, NM, FE>, grid, dim3(64 * TL::NW), 0, s,
+              s_vals, s_meta, R, C, act, T, ep, out, part, n_rt, n_tt, p.stages_per_split, n_whole,
+              ent_bytes);
 }
 
 // Sum of a split product's fp32 partials into bf16 out: every element (k_splitk_reduce), or only

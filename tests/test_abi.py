@@ -12,7 +12,7 @@ import pytest
 from sparse_rank_adapter_amd import _abi
 from sparse_rank_adapter_amd._abi import (SRA_BF16, SRA_ERR_INVALID_ARG, SRA_ERR_UNSUPPORTED,
                                           SRA_ERR_WORKSPACE, SRA_F32, SRA_FMT_CSR, SRA_FMT_ELL,
-                                          SRA_FMT_NM, SRA_FMT_NM_TILED, SRA_GRAD_DX, SRA_OK,
+                                          SRA_FMT_FFI_TILED, SRA_FMT_NM, SRA_FMT_NM_TILED, SRA_GRAD_DX, SRA_OK,
                                           SraSparse)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -125,6 +125,38 @@ def test_ffi_validation(lib):
     e = ell_desc()
     assert lib.sra_ffi_transpose(ctypes.byref(e), ctypes.byref(T_), FAKE, 16, None) == SRA_ERR_WORKSPACE
     assert lib.sra_ffi_transpose(ctypes.byref(e), ctypes.byref(T_), None, 1 << 30, None) == SRA_ERR_WORKSPACE
+
+
+def test_ffi_tile_validation(lib):
+    eb, ob = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sra_ffi_tile_size(4096, 4096, 4096 * 410, ctypes.byref(eb), ctypes.byref(ob)) == SRA_OK
+    lists = 128 * 64
+    assert eb.value == (4096 * 410 + 3 * lists) * 4 and ob.value == (lists + 4) * 4
+    assert lib.sra_ffi_tile_size(4096, 40000, 10, ctypes.byref(eb), ctypes.byref(ob)) == SRA_ERR_INVALID_ARG
+    assert lib.sra_ffi_tile_size(4, 64, 257, ctypes.byref(eb), ctypes.byref(ob)) == SRA_ERR_INVALID_ARG
+    out = SraSparse()
+    out.values, out.meta = FAKE, FAKE
+    assert lib.sra_ffi_tile(ctypes.byref(nm_desc()), ctypes.byref(out), None) == SRA_ERR_INVALID_ARG
+    assert lib.sra_ffi_tile(ctypes.byref(ell_desc(dtype=SRA_F32)), ctypes.byref(out), None) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_ffi_tile(ctypes.byref(ell_desc()), None, None) == SRA_ERR_INVALID_ARG
+    out.meta = None
+    assert lib.sra_ffi_tile(ctypes.byref(ell_desc()), ctypes.byref(out), None) == SRA_ERR_INVALID_ARG
+    # the tiled products: bf16, reduction a multiple of 64, no product workspace
+    t = SraSparse()
+    t.format, t.dtype, t.rows, t.cols, t.nnz = SRA_FMT_FFI_TILED, SRA_BF16, 4096, 4096, 1 << 20
+    t.values, t.meta = FAKE, FAKE
+    n = ctypes.c_size_t()
+    assert lib.sra_fwd_workspace(ctypes.byref(t), 4096, 0, ctypes.byref(n)) == SRA_OK and n.value == 0
+    assert lib.sra_bwd_workspace(ctypes.byref(t), 4096, 0, SRA_GRAD_DX, ctypes.byref(n)) == SRA_OK and n.value == 0
+    t.cols = 4000
+    assert lib.sra_fwd_workspace(ctypes.byref(t), 4096, 0, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    assert lib.sra_bwd_workspace(ctypes.byref(t), 4096, 0, SRA_GRAD_DX, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    t.cols, t.dtype = 4096, SRA_F32
+    assert lib.sra_fwd_workspace(ctypes.byref(t), 4096, 0, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    # an ELL weight with 128 or more tokens tiles into the workspace: O(nnz), not R x C
+    e = ell_desc(rows=4096, cols=4096, k=410)
+    assert lib.sra_fwd_workspace(ctypes.byref(e), 4096, 0, ctypes.byref(n)) == SRA_OK
+    assert n.value <= (4096 * 410 + 4 * lists) * 4 + 1024 < 4096 * 4096 * 2 // 4
 
 
 def test_fwd_validation_and_workspace(lib):

@@ -9,7 +9,7 @@ import torch
 
 from sparse_rank_adapter_amd import _abi, api
 from sparse_rank_adapter_amd.api import SparseMatrix
-from sparse_rank_adapter_amd._abi import SRA_FMT_CSR, SRA_FMT_ELL, SRA_FMT_NM
+from sparse_rank_adapter_amd._abi import SRA_FMT_CSR, SRA_FMT_ELL, SRA_FMT_FFI_TILED, SRA_FMT_NM
 
 HOST_QUERIES = {"sra_nm_meta_words", "sra_nm_tile_bytes", "sra_fwd_workspace", "sra_bwd_workspace",
                 "sra_ffi_transpose_workspace", "sra_last_error", "sra_abi_version"}
@@ -160,3 +160,23 @@ def test_ffi_descriptors_checked(binding):
                        row_ptr=torch.zeros(K, dtype=torch.int32), nnz=N * 8)
     with pytest.raises(ValueError):
         binding.sparse_lora_bwd(csr, torch.zeros(T, N, dtype=bf), torch.zeros(T, K, dtype=bf))
+
+
+def test_ffi_tiled_descriptors_checked(binding):
+    nm = SparseMatrix(SRA_FMT_NM, bf, N, K, torch.zeros(N, K // 2, dtype=bf),
+                      meta=torch.zeros(N, K // 32, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        binding.ffi_tile(nm)                                     # not ELL or CSR
+    lists = binding.ffi_tile_lists(N, K)
+    short = SparseMatrix(SRA_FMT_FFI_TILED, bf, N, K, torch.zeros(64, dtype=torch.int32),
+                         meta=torch.zeros(lists, dtype=torch.int32), nnz=64)
+    with pytest.raises(ValueError):                              # offsets lack the 4 closing words
+        binding.sparse_lora_fwd(short, torch.zeros(T, K, dtype=bf))
+    f32 = SparseMatrix(SRA_FMT_FFI_TILED, torch.float32, N, K, torch.zeros(64, dtype=torch.int32),
+                       meta=torch.zeros(lists + 4, dtype=torch.int32), nnz=64)
+    with pytest.raises(ValueError):                              # bf16 only
+        binding.sparse_lora_fwd(f32, torch.zeros(T, K, dtype=torch.float32))
+    few = SparseMatrix(SRA_FMT_FFI_TILED, bf, N, K, torch.zeros(16, dtype=torch.int32),
+                       meta=torch.zeros(lists + 4, dtype=torch.int32), nnz=64)
+    with pytest.raises(ValueError):                              # fewer words than nnz says
+        binding.sparse_lora_fwd(few, torch.zeros(T, K, dtype=bf))

@@ -176,6 +176,62 @@ def test_ffi_gaussian(gpu, dtype):
     check_ffi(W, 205, dtype)
 
 
+def ffi_tile_expected(rows_of, cols_of, vbits, R, C):
+    """The tiled fixed fan-in layout (documented with sra_ffi_tile) of entries (row, column, value
+    bits): per 32-row group and 64-column stage a list of value | position << 16 words in (row,
+    column) order, padded to four words with 0xffffffff; lists by group, then stage."""
+    nst, groups = -(-C // 64), -(-R // 32)
+    r = np.asarray(rows_of, dtype=np.int64)
+    c = np.asarray(cols_of, dtype=np.int64)
+    g, x = r // 32, c // 64
+    lid = g * nst + x
+    order = np.lexsort((c, r, lid))
+    r, c, lid, vb = r[order], c[order], lid[order], np.asarray(vbits, dtype=np.uint32)[order]
+    counts = np.bincount(lid, minlength=groups * nst)
+    padded = (counts + 3) // 4 * 4
+    starts = np.concatenate([[0], np.cumsum(padded)])
+    first = np.concatenate([[0], np.cumsum(counts)])[:-1]
+    rank = np.arange(lid.size) - first[lid]
+    words = np.full(int(starts[-1]), 0xFFFFFFFF, dtype=np.uint32)
+    pos = ((r - 32 * (r // 32)) * 64 + (c - 64 * (c // 64))).astype(np.uint32)
+    words[starts[lid] + rank] = vb | (pos << 16)
+    offs = np.concatenate([starts[:-1], [starts[-1]] * 4]).astype(np.uint32)
+    return words, offs
+
+
+def check_ffi_tile(S, ST, vals, cols):
+    """ffi_tile of the ELL weight and of its CSR transpose against the layout above, built from
+    the oracle's selection and transpose."""
+    R, C = S.rows, S.cols
+    vb = np_bits(vals, torch.bfloat16).astype(np.uint32)
+    rows_of = np.repeat(np.arange(R), vals.shape[1])
+    for M, (ro, co, bb, RR, CC) in (
+            (sra.ffi_tile(S), (rows_of, cols.reshape(-1), vb.reshape(-1), R, C)),
+            (sra.ffi_tile(ST), _csr_entries(ST, vals, cols))):
+        torch.cuda.synchronize()
+        words, offs = ffi_tile_expected(ro, co, bb, RR, CC)
+        got_o = M.meta.cpu().numpy().view(np.uint32)
+        assert np.array_equal(got_o[:offs.size], offs)
+        got_w = M.values.cpu().numpy().view(np.uint32)
+        assert M.nnz >= words.size
+        assert np.array_equal(got_w[:words.size], words)
+
+
+def _csr_entries(ST, vals, cols):
+    rp, ids, tv = offi.transpose(vals, cols, ST.rows)
+    rows_of = np.repeat(np.arange(ST.rows), np.diff(rp))
+    return rows_of, ids, np_bits(tv, torch.bfloat16).astype(np.uint32), ST.rows, ST.cols
+
+
+@pytest.mark.parametrize("shape,k", [((1, 1), 1), ((5, 37), 3), ((64, 300), 17), ((100, 640), 600),
+                                     ((300, 200), 20), ((70, 4096), 410)])
+def test_ffi_tile_layout(gpu, shape, k):
+    W = tie_heavy(shape, seed=k + shape[0], dtype=torch.bfloat16)
+    S, ST = check_ffi(W, k, torch.bfloat16)
+    vals, cols = offi.select(f64(W), k)
+    check_ffi_tile(S, ST, vals, cols)
+
+
 def test_ffi90_full(gpu):
     wl = WORKLOADS["ffi90_4096"]
     inp = layer_inputs(wl, T=1, with_dy=False)

@@ -338,13 +338,15 @@ def test_u_recomputed_when_not_given(gpu):
 
 # ----------------------------------------------------------------------------- fixed fan-in
 
-def run_ffi(wl: Workload, T=None, seed=0, rows=None, cols_n=None, kcols=None):
+def run_ffi(wl: Workload, T=None, seed=0, rows=None, cols_n=None, kcols=None, tiled=False):
     inp = layer_inputs(wl, seed=seed, T=T)
     dtype = inp["X"].dtype
     X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
     rr = A.shape[0]
     S = sra.compress_ffi(W, wl.ffi_k)
     ST = sra.ffi_transpose(S)
+    if tiled:  # the products' tiled layout of both (sra_ffi_tile)
+        S, ST = sra.ffi_tile(S), sra.ffi_tile(ST)
     Y, U = sra.sparse_lora_fwd(S, X, A if rr else None, B if rr else None)
     g = sra.sparse_lora_bwd(ST, dY, X, U, A if rr else None, B if rr else None, want_du=True)
     torch.cuda.synchronize()
@@ -385,6 +387,46 @@ def test_ffi90_sampled(gpu):
     rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 126, replace=False)]))
     cols = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 254, replace=False)]))
     run_ffi(wl, rows=rows, cols_n=cols, kcols=cols)
+
+
+# the tiled format (K % 64 == 0 and N % 64 == 0): T = 1 and 5 on the four-wave tile, lists of
+# up to 256 entries, denser weights on the 1024-entry slots (k = 60 of 128: about 940 per list),
+# and lists longer than the slots (k = 250 of 256: about 2000 per list, the rest read from memory)
+@pytest.mark.parametrize("T,K,N,k,r", [(1, 64, 64, 5, 4), (5, 128, 192, 9, 4), (257, 192, 320, 20, 16),
+                                       (130, 640, 64, 40, 0), (300, 128, 256, 60, 8),
+                                       (200, 256, 320, 250, 8)])
+def test_ffi_tiled_ragged(gpu, T, K, N, k, r):
+    wl = Workload("ffi_tiled", T=T, K=K, N=N, r=r, dtype="bf16", fmt="ffi", ffi_k=k)
+    run_ffi(wl, seed=k, tiled=True)
+
+
+def test_ffi_tiled_wide_and_ffi90(gpu):
+    """The tiled format on the 256 x 256 and 256 x 128 tiles: the ragged wide case below, and the
+    90% fixed fan-in layer at full size on sampled outputs."""
+    wl = Workload("ffi_wide", T=3900, K=3904, N=3968, r=16, dtype="bf16", fmt="ffi", ffi_k=100)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([np.arange(3840, 3900), rng.choice(3840, 60, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(3840, 3968), rng.choice(3840, 64, replace=False)]))
+    kcols = np.unique(np.concatenate([np.arange(3840, 3904), rng.choice(3840, 64, replace=False)]))
+    run_ffi(wl, seed=4, rows=rows, cols_n=cols, kcols=kcols, tiled=True)
+    wl = WORKLOADS["ffi90_4096"]
+    rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 126, replace=False)]))
+    cols = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 254, replace=False)]))
+    run_ffi(wl, rows=rows, cols_n=cols, kcols=cols, tiled=True)
+    wl = Workload("ffi_mid", T=1500, K=1024, N=2048, r=8, dtype="bf16", fmt="ffi", ffi_k=96)
+    run_ffi(wl, seed=9, tiled=True)
+
+
+def test_ffi_ragged_wide_tiles(gpu):
+    """Token and row counts large enough for the densified product's 256 x 256 tiles in both
+    directions (forward rows N = 3968, backward rows K = 3904, T = 3900), each with a ragged last
+    tile; sampled outputs include every token, row and column of the ragged tails."""
+    wl = Workload("ffi_wide", T=3900, K=3904, N=3968, r=16, dtype="bf16", fmt="ffi", ffi_k=100)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([np.arange(3840, 3900), rng.choice(3840, 60, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(3840, 3968), rng.choice(3840, 64, replace=False)]))
+    kcols = np.unique(np.concatenate([np.arange(3840, 3904), rng.choice(3840, 64, replace=False)]))
+    run_ffi(wl, seed=3, rows=rows, cols_n=cols, kcols=kcols)
 
 
 @pytest.mark.parametrize("layout", ["canonical", "streaming"])
