@@ -208,8 +208,11 @@ sra_status sra_ffi_tile_size(int64_t rows, int64_t cols, int64_t nnz, size_t* en
  * built once per mask like sra_nm_tile.  S: SRA_FMT_ELL (the forward weight) or SRA_FMT_CSR (its
  * transpose from sra_ffi_transpose), bf16.  Rows are cut into 32-row groups and columns into
  * 64-column stages; list (g, x) holds the entries of group g in stage x as uint32 words, the
- * bf16 value in the low 16 bits and (row - 32 g) * 64 + (column - 64 x) in the high 16 bits,
- * ordered by row, then column, padded to a multiple of 4 words with 0xffffffff.  Lists follow
+ * bf16 value in the low 16 bits and in the high 16 bits the entry's byte offset in the group's
+ * 32 x 64 bf16 block as the products hold it in LDS: with i = row - 32 g and c = column - 64 x,
+ * i * 128 + ((c / 8) XOR ((i / 2) % 8)) * 16 + (c % 8) * 2 (128-byte rows, 16-byte chunks
+ * swizzled).  Words are ordered by row, then column, padded to a multiple of 4 words with
+ * 0xffffffff.  Lists follow
  * each other by group, then stage.  out->values: the words (entry_bytes of sra_ffi_tile_size,
  * 16-byte aligned); out->meta: uint32 offsets, meta[g * stages + x] = first word of list (g, x),
  * then the total word count 4 times (offset_bytes).  The caller sets out->values and out->meta;

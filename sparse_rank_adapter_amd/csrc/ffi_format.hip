@@ -13,8 +13,10 @@
 //
 // ffi_tile: the product's layout of an ELL or CSR matrix.  Rows are cut into 32-row groups and
 // columns into 64-column stages; list (group g, stage x) holds the group's entries in that stage
-// as 32-bit words (bf16 value in the low half, (row - 32 g) * 64 + (column - 64 x) in the high
-// half), ordered by row and then column, and padded to a multiple of four words with 0xffffffff.
+// as 32-bit words, ordered by row and then column, padded to a multiple of four words with
+// 0xffffffff.  A word holds the bf16 value in the low half and, in the high half, the entry's
+// byte offset in the group's 32 rows of 64 bf16 as the products lay them out in LDS: with
+// i = row - 32 g and c = column - 64 x, i * 128 + ((c / 8) ^ ((i / 2) % 8)) * 16 + (c % 8) * 2.
 // Lists follow each other group by group, stage by stage; offsets[g * stages + x] is the first
 // word of list (g, x), and the word count plus three more copies of it close the array.  Counting
 // per list, one scan over the lists, then per group a count per (row, stage) turns into each
@@ -295,7 +297,9 @@ __global__ __launch_bounds__(256) void k_ffi_tile_fill(const uint16_t* __restric
       for (int64_t q = b + tid; q < e; q += 256) {
         const int col = idx[q], x = col >> 6;
         const uint32_t pos = base[x] + cnt[i * nst + x] + ((uint32_t)(q - b) - pre[i * nst + x]);
-        if (pos < cap) ent[pos] = (uint32_t)vals[q] | ((uint32_t)((16 * h + i) * 64 + (col & 63)) << 16);
+        const int row = 16 * h + i, cc = col & 63;
+        const uint32_t off = (uint32_t)(row * 128 + (((cc >> 3) ^ ((row >> 1) & 7)) << 4) + (cc & 7) * 2);
+        if (pos < cap) ent[pos] = (uint32_t)vals[q] | (off << 16);
       }
     }
     __syncthreads();

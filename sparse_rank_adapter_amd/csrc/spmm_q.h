@@ -496,15 +496,13 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   auto fe_start = [&](int x) -> uint32_t { return otab[x]; };
   auto eslot = [&](int slot) { return ebuf + (slot * NW + wave) * FE * 4; };
   auto fe_tile = [&](int rel) { return abuf + (rel & 1) * (TL::BR * 128); };
-  // one entry into the wave's rows of A tile `at`: bf16 value in the low half, (row in the group)
-  // * 64 + (column in the stage) in the high half; padding entries (position >= 2048) are skipped
+  // one entry into the wave's rows of A tile `at`: bf16 value in the low half, in the high half
+  // its byte offset in the group's 32 rows of 128 bytes (the tile's swizzle, chunk c of row i at
+  // c ^ ((i >> 1) & 7), already applied; row 32 w + i of the tile has the same swizzle as row i);
+  // padding entries (offset >= 4096) are skipped
   auto fe_put = [&](uint8_t* at, uint32_t e) {
-    const uint32_t pos = e >> 16;
-    if (pos < 2048) {
-      const int r = wave * 32 + (int)(pos >> 6), col = (int)(pos & 63);
-      *reinterpret_cast<uint16_t*>(at + r * 128 + (((col >> 3) ^ ((r >> 1) & 7)) << 4) + (col & 7) * 2) =
-          (uint16_t)e;
-    }
+    const uint32_t off = e >> 16;
+    if (off < 4096) *reinterpret_cast<uint16_t*>(at + wave * 4096 + off) = (uint16_t)e;
   };
   auto fe_clear = [&](uint8_t* at) {
 #pragma unroll
@@ -552,7 +550,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   auto fe_step2 = [&](int rel) {
     const int x = c_beg + rel + 1;
     if (x < c_end) {
-      uint8_t* at = fe_tile(rel + 1);
+      uint8_t* at = fe_tile(rel + 1) + wave * 4096;
       const uint32_t e0 = __builtin_amdgcn_readfirstlane(fe_lo);
       const uint32_t n = min(__builtin_amdgcn_readfirstlane(fe_hi) - e0, 2048u);
 #pragma unroll
@@ -560,11 +558,13 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
         const uint32_t q0 = (uint32_t)(k * 256 + lane * 4);
         if (q0 < n) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (q0 + i < n) fe_put(at, fe_ev[k][i]);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t e = fe_ev[k][i], off = e >> 16;
+            if (q0 + i < n && off < 4096) *reinterpret_cast<uint16_t*>(at + off) = (uint16_t)e;
+          }
         }
       }
-      if (n > (uint32_t)FE) fe_from_memory(at, e0, FE, n);
+      if (n > (uint32_t)FE) fe_from_memory(fe_tile(rel + 1), e0, FE, n);
     }
   };
   auto issue = [&](int c, int buf) {
@@ -678,6 +678,9 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[i], blo, acc[i][j], 0, 0, 0);
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[i], bhi, acc[i][j], 0, 0, 0);
         if (i == 0 && j + CA < FT) read_col(j + CA);
+        // the later stage's transfers after the second column's first products; with entry lists,
+        // step 1 there and step 2 with the transfers (which need the list start step 1 read)
+        // four products later
         constexpr int kS1 = FT > 1 ? FR : 0, kS2 = 2 * FR < FR * FT - 1 ? 2 * FR : FR * FT - 1;
         if (k == kS1) {
           if constexpr (FE > 0) fe_step1(rel);

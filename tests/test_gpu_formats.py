@@ -178,8 +178,9 @@ def test_ffi_gaussian(gpu, dtype):
 
 def ffi_tile_expected(rows_of, cols_of, vbits, R, C):
     """The tiled fixed fan-in layout (documented with sra_ffi_tile) of entries (row, column, value
-    bits): per 32-row group and 64-column stage a list of value | position << 16 words in (row,
-    column) order, padded to four words with 0xffffffff; lists by group, then stage."""
+    bits): per 32-row group and 64-column stage a list of value | offset << 16 words in (row,
+    column) order, the offset being the entry's byte in the group's swizzled 32 x 128-byte block,
+    padded to four words with 0xffffffff; lists by group, then stage."""
     nst, groups = -(-C // 64), -(-R // 32)
     r = np.asarray(rows_of, dtype=np.int64)
     c = np.asarray(cols_of, dtype=np.int64)
@@ -193,7 +194,8 @@ def ffi_tile_expected(rows_of, cols_of, vbits, R, C):
     first = np.concatenate([[0], np.cumsum(counts)])[:-1]
     rank = np.arange(lid.size) - first[lid]
     words = np.full(int(starts[-1]), 0xFFFFFFFF, dtype=np.uint32)
-    pos = ((r - 32 * (r // 32)) * 64 + (c - 64 * (c // 64))).astype(np.uint32)
+    i, cc = r - 32 * (r // 32), c - 64 * (c // 64)
+    pos = (i * 128 + (((cc // 8) ^ ((i // 2) % 8)) * 16) + (cc % 8) * 2).astype(np.uint32)
     words[starts[lid] + rank] = vb | (pos << 16)
     offs = np.concatenate([starts[:-1], [starts[-1]] * 4]).astype(np.uint32)
     return words, offs
