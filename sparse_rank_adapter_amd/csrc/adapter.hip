@@ -478,6 +478,79 @@ __global__ void k_reduce_parts(const double* __restrict__ part, int S, int64_t n
   if (vt) write_vt3(vt, rp, Tp, (int)(i % r), i / r, s);  // rows output [T][r]
 }
 
+// The same sum for a block of 32 tokens x 64 ranks when V^T's parts are written too: the partials
+// are read and out / out64 written along the ranks, the fp32 sums go through LDS, and each part
+// row of V^T is written along the tokens (the per-element kernel above writes those parts
+// T columns apart, two bytes at a time).
+__global__ __launch_bounds__(256) void k_reduce_parts_vt(const double* __restrict__ part, int S, int64_t T,
+                                                         int r, float* __restrict__ out,
+                                                         double* __restrict__ out64,
+                                                         uint16_t* __restrict__ vt, int rp, int64_t Tp) {
+  __shared__ float tile[64][33];  // [rank][token]
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 32, n = T * r;
+  const int j0 = blockIdx.y * 64;
+  // eight elements per thread, all of their loads of four slices in flight before the adds (the
+  // sums keep the slice order of the per-element kernel)
+  const int jj = tid & 63, j = j0 + jj;
+  int64_t idx[8];
+  bool ok[8];
+  double sum[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t t = t0 + (tid >> 6) + 4 * q;
+    ok[q] = t < T && j < r;
+    idx[q] = ok[q] ? t * r + j : 0;
+    sum[q] = 0.0;
+  }
+  for (int k = 0; k < S; k += 4) {
+    double v[8][4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[q][u] = k + u < S ? part[(int64_t)(k + u) * n + idx[q]] : 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k + u < S) sum[q] += v[q][u];
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    if (ok[q]) {
+      if (out) out[idx[q]] = (float)sum[q];
+      if (out64) out64[idx[q]] = sum[q];
+      tile[jj][(tid >> 6) + 4 * q] = (float)sum[q];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int tt = tid & 31, jj = (tid >> 5) + 8 * q;
+    const int64_t t = t0 + tt;
+    const int j = j0 + jj;
+    if (t < T && j < r) {
+      uint16_t p3[3];
+      split3_bf16(tile[jj][tt], p3[0], p3[1], p3[2]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) vt[((int64_t)p * rp + j) * Tp + t] = p3[p];
+    }
+  }
+}
+
+// Sum of the S fp64 slice partials of a [T][r] adapter product: per element, or tiled when V^T's
+// parts are written as well.
+void reduce_parts(const double* part, int S, int64_t T, int r, float* out, double* out64, uint16_t* vt,
+                  int rp, int64_t Tp, hipStream_t s) {
+  const int64_t n = T * r;
+  if (vt)
+    hipLaunchKernelGGL(k_reduce_parts_vt, dim3((unsigned)((T + 31) / 32), (unsigned)((r + 63) / 64)), dim3(256),
+                       0, s, part, S, T, r, out, out64, vt, rp, Tp);
+  else
+    hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, S, n, out,
+                       out64, r, vt, rp, Tp);
+}
+
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1234,11 +1307,7 @@ hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const 
     else
       launch(SRA_KERNEL_ADAPTER, k_adapter_rows_ring128, grid, dim3(512), 0, s, act, T, C, wt, ldw,
              r, q.c_per, part, out, out64, vt, rp, Tp);
-    if (q.S > 1) {
-      const int64_t n = T * r;
-      hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, q.S,
-                         n, out, out64, r, vt, rp, Tp);
-    }
+    if (q.S > 1) reduce_parts(part, q.S, T, r, out, out64, vt, rp, Tp, s);
     return hipGetLastError();
   }
   const RowsPlan p = rows_plan(T, C, r);
@@ -1249,11 +1318,7 @@ hipError_t launch_adapter_rows(const uint16_t* act, int64_t T, int64_t C, const 
     case 2: rows_launch<2, 4>(grid, s, act, T, C, wt, ldw, r, p.c_per, part, out, out64, vt, rp, Tp); break;
     default: rows_launch<4, 2>(grid, s, act, T, C, wt, ldw, r, p.c_per, part, out, out64, vt, rp, Tp); break;
   }
-  if (p.S > 1) {
-    const int64_t n = T * r;
-    hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, p.S,
-                       n, out, out64, r, vt, rp, Tp);
-  }
+  if (p.S > 1) reduce_parts(part, p.S, T, r, out, out64, vt, rp, Tp, s);
   return hipGetLastError();
 }
 
