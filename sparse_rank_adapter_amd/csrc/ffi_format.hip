@@ -200,6 +200,7 @@ __global__ __launch_bounds__(256) void k_ffi_tile_count(const int16_t* __restric
   for (int x = tid; x < nst; x += 256) cnt[x] = 0;
   __syncthreads();
   const int64_t b = row_ptr ? row_ptr[r0] : r0 * k, e = row_ptr ? row_ptr[r1] : r1 * k;
+#pragma unroll 4
   for (int64_t i = b + tid; i < e; i += 256) atomicAdd(&cnt[idx[i] >> 6], 1u);
   __syncthreads();
   for (int x = tid; x < nst; x += 256) offs[g * nst + x] = (cnt[x] + 3u) & ~3u;
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(256) void k_ffi_tile_fill(const uint16_t* __restric
   uint32_t* run = sm + 16 * nst;
   uint32_t* base = run + nst;
   uint32_t* part = base + nst;
+  __shared__ int64_t rowb[17];  // the half group's row starts (entry indices) and its end
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x;
   for (int x = tid; x < nst; x += 256) {
@@ -253,16 +255,25 @@ __global__ __launch_bounds__(256) void k_ffi_tile_fill(const uint16_t* __restric
     base[x] = offs[g * nst + x];
   }
   auto row_beg = [&](int64_t row) -> int64_t { return row_ptr ? row_ptr[row] : row * k; };
+  // the row of an entry of the half group: the last row start at or before it (16 rows, 4 steps)
+  auto row_of = [&](int64_t q) {
+    int lo = 0;
+#pragma unroll
+    for (int step = 8; step >= 1; step >>= 1)
+      if (rowb[lo + step] <= q) lo += step;
+    return lo;
+  };
   for (int h = 0; h < 2; ++h) {
     const int64_t r0 = g * 32 + 16 * h;
     for (int w = tid; w < 8 * nst; w += 256) cntw[w] = 0;
+    if (tid <= 16) rowb[tid] = row_beg(min(r0 + tid, R));
     __syncthreads();
-    for (int i = 0; i < 16 && r0 + i < R; ++i) {
-      const int64_t b = row_beg(r0 + i), e = row_beg(r0 + i + 1);
-      for (int64_t q = b + tid; q < e; q += 256) {
-        const int j = i * nst + (idx[q] >> 6);
-        atomicAdd(&cntw[j >> 1], 1u << (16 * (j & 1)));  // counts stay <= 64: no carry between halves
-      }
+    // every entry of the half group's 16 rows in one pass (their entries are contiguous)
+    const int64_t hb = rowb[0], he = rowb[16];
+#pragma unroll 4
+    for (int64_t q = hb + tid; q < he; q += 256) {
+      const int j = row_of(q) * nst + (idx[q] >> 6);
+      atomicAdd(&cntw[j >> 1], 1u << (16 * (j & 1)));  // counts stay <= 64: no carry between halves
     }
     __syncthreads();
     // pre: per row, an exclusive scan over the stages (16 lanes per row, each a run of stages)
@@ -292,9 +303,11 @@ __global__ __launch_bounds__(256) void k_ffi_tile_fill(const uint16_t* __restric
       run[x] = r;
     }
     __syncthreads();
-    for (int i = 0; i < 16 && r0 + i < R; ++i) {
-      const int64_t b = row_beg(r0 + i), e = row_beg(r0 + i + 1);
-      for (int64_t q = b + tid; q < e; q += 256) {
+#pragma unroll 4
+    for (int64_t q = hb + tid; q < he; q += 256) {
+      {
+        const int i = row_of(q);
+        const int64_t b = rowb[i];
         const int col = idx[q], x = col >> 6;
         const uint32_t pos = base[x] + cnt[i * nst + x] + ((uint32_t)(q - b) - pre[i * nst + x]);
         const int row = 16 * h + i, cc = col & 63;
