@@ -279,8 +279,8 @@ SRA_DEV bf16x8 expand28(uint32_t s, uint32_t m) {
 // boundary (the planner splits only the 256x256 tile, so).
 // UG > 0: adapter rows in the activation region as in PTile (GT transfers over NW waves).
 // DN: the weight tile is dense (rows of 128 bytes per stage, no metadata) and the products are
-// pairs of dense v_mfma_f32_16x16x32_bf16; with FE > 0 (below) the tile is written in LDS from the
-// fixed fan-in entry lists, otherwise it is transferred from dense rows of C bf16.
+// pairs of dense v_mfma_f32_16x16x32_bf16; the tile is written in LDS from the fixed fan-in entry
+// lists (FE > 0, below).
 // NM = 24 / 28: the weight is 2:4 / 2:8 and each fragment is expanded to dense bf16 before the same
 // pairs of dense MFMAs (expand24 / expand28).  2:8 rows carry 32 bytes of stored values per
 // 64-column stage (two 16-byte chunks, slot = chunk ^ ((row >> 3) & 1)) and the same 8 bytes of
@@ -297,18 +297,19 @@ struct QTile {
   static_assert(!(DN && (MS || UG)), "dense weights have no metadata or adapter rows");
   static_assert(NM == 0 || NM == 24 || NM == 28, "2:4 SMFMAC, or 2:4 / 2:8 expanded to dense");
   static_assert(FE == 0 || (DN && FE % 256 == 0), "fixed fan-in entry lists: dense products, whole 1 KB transfers");
+  static_assert(!DN || FE > 0, "dense products take their weight tile from the entry lists");
   static constexpr int NW = WR * WT;  // waves per workgroup: 4 or 8
   static constexpr int BR = 16 * FR * WR, BT = 16 * FT * WT;
   static_assert(FE == 0 || BR == 32 * NW, "fixed fan-in: 32 weight rows per wave");
   static constexpr int VB = NM == 28 ? 32 : 64;  // stored-value bytes per weight row and stage
-  static constexpr int LA = FE ? 0 : BR / ((DN ? 8 : NM == 28 ? 32 : 16) * NW);
+  static constexpr int LA = FE ? 0 : BR / ((NM == 28 ? 32 : 16) * NW);
   static constexpr int LM = (MS || DN) ? 0 : BR / (32 * NW);
   static constexpr int LB = BT / (8 * NW);
   static constexpr int LE = FE / 256;  // 1 KB entry transfers per wave and stage
   static constexpr int GT = UG / 8, GW = GT / NW, GX = GT % NW;
   static constexpr int L = LA + LM + LB + GW + LE;  // waves >= GX
   static constexpr int L1 = L + (GX ? 1 : 0);       // waves < GX
-  static constexpr int A_BYTES = FE ? 0 : BR * (DN ? 128 : VB), M_BYTES = (MS || DN) ? 0 : BR * 8;
+  static constexpr int A_BYTES = FE ? 0 : BR * VB, M_BYTES = (MS || DN) ? 0 : BR * 8;
   static constexpr int B_BYTES = (BT + UG) * 128;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
   static constexpr int MSB = MS ? BR * MS * 8 : 0;            // one metadata super-stage buffer
@@ -380,14 +381,14 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
   // operands through buffer resources based at the tile (fixed lane offsets, the stage offset in
   // an SGPR; rows past R, T or r read as zeros), as in k_spmm24_pipe
   const int rows_here = (int)min((int64_t)BR, R - row0), toks_here = (int)min((int64_t)BT, T - t0);
-  constexpr int A_ROW = TLAY ? 1024 : DN ? 128 : TL::VB;  // stage offset of the weight operand (bytes)
+  constexpr int A_ROW = TLAY ? 1024 : TL::VB;  // stage offset of the weight operand (bytes)
   // streaming layout: 16-row groups of nsteps 1 KB value blocks and nbat 1 KB metadata blocks
   const int nsteps = (int)((C + 63) / 64), nbat = (int)((C + 511) / 512), ngrp = (rows_here + 15) / 16;
   const __amdgpu_buffer_rsrc_t ra =
       TLAY ? __builtin_amdgcn_make_buffer_rsrc((void*)(s_vals + (row0 / 16) * nsteps * 512), 0,
                                                ngrp * nsteps * 1024, 0x00020000)
-           : __builtin_amdgcn_make_buffer_rsrc((void*)(s_vals + row0 * (DN ? C : cv)), 0,
-                                               rows_here * (int)(DN ? C : cv) * 2, 0x00020000);
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(DN ? nullptr : s_vals + row0 * cv), 0,
+                                               DN ? 0 : rows_here * (int)cv * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rm =
       TLAY ? __builtin_amdgcn_make_buffer_rsrc((void*)(s_meta + (row0 / 16) * nbat * 256), 0,
                                                ngrp * nbat * 1024, 0x00020000)
@@ -402,10 +403,7 @@ __global__ __launch_bounds__(64 * WR * WT, (QTile<FR, FT, WR, WT, NS, MS, UG, DN
 #pragma unroll
   for (int k = 0; k < TL::LA; ++k) {
     const int b = k * NW + wave;
-    if constexpr (DN) {  // 8 rows of 128 bytes, chunk swizzle (row >> 1) & 7 as for tokens
-      const int row = 8 * b + (lane >> 3), ch = (lane & 7) ^ ((row >> 1) & 7);
-      a_off[k] = (uint32_t)((row * C + ch * 8) * 2);
-    } else if constexpr (NM == 28) {  // 32 rows of 32 bytes, chunk swizzle (row >> 3) & 1
+    if constexpr (NM == 28) {  // 32 rows of 32 bytes, chunk swizzle (row >> 3) & 1
       const int row = 32 * b + (lane >> 1), ch = (lane & 1) ^ ((row >> 3) & 1);
       a_off[k] = (uint32_t)(row * (C / 2) + ch * 16);
     } else {             // 16 rows of 64 bytes
