@@ -63,6 +63,12 @@ TRAFFIC_BYTES = {
 # MLP step (fc1 Y, fc2 Y, fc2 dX, fc1 dX), by weight layout.
 SPMM_MLP_KERNELS = {"streaming": "k_spmm24_q<4, 8, 4, 2, 3, 4, 0, false, true, false>",
                     "canonical": "k_spmm24_q<4, 8, 4, 2, 3, 4, 0, false, false, false>"}
+ENGINE_EVAL_WHAT = {
+    "2:4": "2:4 products on SMFMAC (the default) against the same pipeline with each weight fragment "
+           "expanded to dense bf16 for dense MFMA",
+    "2:8": "2:8 products on SMFMAC with the weight rewritten as 2:4 per call (the default above 16 "
+           "tokens: every four columns of a 2:8 row hold at most two kept entries) against the 2:8 "
+           "fragments expanded to dense bf16 for dense MFMA"}
 
 
 def parse():
@@ -78,7 +84,7 @@ def parse():
                     help="weight layout of the decode forward (streaming = sra_nm_tile)")
     ap.add_argument("--nm", choices=["2:4", "1:2", "2:8"], default="2:4",
                     help="N:M pattern of the training step's weight (1:2 runs on the 2:4 kernels, "
-                         "2:8 on dense MFMA with expanded fragments)")
+                         "2:8 on them too, rewritten as 2:4 per call)")
     ap.add_argument("--layout", choices=["canonical", "streaming"], default=None,
                     help="weight layout of the training step (streaming = sra_compress_pair_tiled); "
                          "default: streaming for opt13b_*, canonical otherwise")
@@ -440,16 +446,15 @@ def bench_nm_layer(args, wl):
               "speedup_vs_dense_dW": round(d_wg / k_wg, 3)}
 
     ev = None
-    if args.nm == "2:4":
-        # the same layer with its 2:4 products on the dense-MFMA engine (expanded fragments)
+    if args.nm in ("2:4", "2:8"):
+        # the same layer with its products on the dense-MFMA engine (expanded fragments)
         with sra.tuned(engine="dense_mfma"):
             e_fwd = time_graph(fwd, args.steps, args.warmup, graph)
             e_bwd = time_graph(bwd, args.steps, args.warmup, graph)
             ek_fwd = time_kernel(SRA_KERNEL_SPMM24, fwd, reps)
             ek_bwd = time_kernel(SRA_KERNEL_SPMM24, lambda: sra.sparse_lora_bwd(P, dY, X, U, A, B, ws=ws_b,
                                                                                 out=grads), reps)
-        ev = {"what": "2:4 products on SMFMAC (the default) against the same pipeline with each weight "
-                      "fragment expanded to dense bf16 for dense MFMA",
+        ev = {"what": ENGINE_EVAL_WHAT[args.nm],
               "smfmac": {"fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5),
                          "spmm_fwd_kernel_ms": round(k_fwd, 5), "spmm_bwd_kernel_ms": round(k_bwd, 5)},
               "dense_mfma": {"fwd_ms": round(e_fwd, 5), "bwd_ms": round(e_bwd, 5),
@@ -516,9 +521,9 @@ def bench_mlp_chain(args, inputs=None, nm="2:4", engine_eval=True):
     """OPT-13B MLP step with both layers chained: fc1 forward on X, fc2 forward on fc1's Y, fc2
     backward on dY2, fc1 backward on fc2's dX (no activation between the layers), each layer's
     compress + double prune first; against the four dense GEMMs of the same chain.  nm = "2:8"
-    runs both weights at 2:8 (canonical arrays, dense-MFMA products); for 2:4, engine_eval also
-    times the same step with the 2:4 products on the dense-MFMA engine (weight fragments expanded
-    to dense bf16) beside the SMFMAC one.
+    runs both weights at 2:8 (canonical arrays; the products rewrite them as 2:4 for SMFMAC);
+    engine_eval also times the same step with the products on the dense-MFMA engine (weight
+    fragments expanded to dense bf16) beside the SMFMAC one.
 
     Returns (line, (i1, i2)) with the CPU inputs of both layers for the CPU baseline."""
     import torch
@@ -638,19 +643,18 @@ def bench_mlp_chain(args, inputs=None, nm="2:4", engine_eval=True):
     k_flops = sum(L["flops"] for L in launches) / len(launches)
     k_ms = sum(L["kernel_ms"] for L in launches) / len(launches)
     achieved = k_flops / (k_ms * 1e-3) / 1e12
-    kname = SPMM_MLP_KERNELS[args.layout] if nm == "2:4" else "k_spmm24_q<..., NM = 28> (2:8, dense MFMA)"
+    kname = SPMM_MLP_KERNELS[args.layout] if nm == "2:4" else SPMM_MLP_KERNELS["canonical"]
     traffic = TRAFFIC_BYTES.get(f"opt13b_mlp/{args.layout}/spmm24/{kname}") if nm == "2:4" else None
     ev = None
-    if engine_eval and nm == "2:4":
-        # the same step with the 2:4 products on the dense-MFMA engine (graphs captured under it)
+    if engine_eval and nm in ("2:4", "2:8"):
+        # the same step with the products on the dense-MFMA engine (graphs captured under it)
         with sra.tuned(engine="dense_mfma"):
             e_ms = time_graph(step, args.steps, args.warmup, graph)
             e_fwd = time_graph(fwd, args.steps, args.warmup, graph)
             e_bwd = time_graph(bwd, args.steps, args.warmup, graph)
             e_launches = spmm_launches()
         e_k = sum(L["kernel_ms"] for L in e_launches) / len(e_launches)
-        ev = {"what": "2:4 products on SMFMAC (the default) against the same pipeline with each "
-                      "weight fragment expanded to dense bf16 for dense MFMA",
+        ev = {"what": ENGINE_EVAL_WHAT[nm],
               "smfmac": {"step_ms": round(ms, 5), "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5),
                          "spmm_kernel_ms_mean": round(k_ms, 5)},
               "dense_mfma": {"step_ms": round(e_ms, 5), "fwd_ms": round(e_fwd, 5), "bwd_ms": round(e_bwd, 5),
@@ -688,8 +692,8 @@ def bench_mlp_chain(args, inputs=None, nm="2:4", engine_eval=True):
                       "dense_four_gemms": round(d_all, 5)},
         "dense_replay_ms": d_dist,
         "spmm_launches": launches,
-        "roofline": {"kernel": f"{kname} ({nm} SpMM + adapter epilogue; mean of the four "
-                               f"launches of a step)",
+        "roofline": {"kernel": f"{kname} (" + ("2:4" if nm == "2:4" else "2:8 rewritten as 2:4")
+                               + " SpMM + adapter epilogue; mean of the four launches of a step)",
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved * 1e12 / PEAK_BF16_FLOPS, 4),
@@ -1016,10 +1020,11 @@ def main():
     if args.workload == "opt13b_mlp":
         out, (i1, i2) = bench_mlp_chain(args)
         extras(args, out, small=not args.no_small)
-        m28, _ = bench_mlp_chain(args, inputs=(i1, i2), nm="2:8", engine_eval=False)
+        m28, _ = bench_mlp_chain(args, inputs=(i1, i2), nm="2:8")
         out["nm28_opt13b_mlp"] = {k: m28[k] for k in (
             "value", "unit", "ms_per_step", "config", "speedup_vs_dense", "speedup_fwd_vs_dense_fwd",
-            "speedup_bwd_vs_dense_dx", "detail_ms", "spmm_launches", "roofline")}
+            "speedup_bwd_vs_dense_dx", "detail_ms", "spmm_launches", "roofline", "engine_eval")
+            if k in m28}
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_mlp(i1, i2, args.cpu_budget)
             out["cpu_baseline_1thread"] = cpu_one_thread()

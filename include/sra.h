@@ -108,7 +108,11 @@ int64_t sra_nm_meta_words(int64_t cols, int32_t n, int32_t m);
  * Supported: 2:4 and 1:2 (same format: one 2-bit in-group field per stored value), cols % 32 == 0.
  * Every call that takes a canonical N:M matrix accepts 1:2 as well; the products run it on the
  * 2:4 kernels (a 1:2 row keeps two entries of every four columns, one per pair), converting the
- * metadata into the workspace.  The streaming layout (sra_nm_tile, sra_compress_pair_tiled) is
+ * metadata into the workspace.  Also 2:8 (bf16, cols % 32 == 0): values [rows, cols/4] in
+ * ascending column order, and per 8-column group one metadata byte holding the two in-group
+ * positions (bits 0-2 and 3-5, the rest zero), four group bytes per uint32 word, so cols/32
+ * words per row.  The products rewrite a 2:8 weight as a 2:4 one in their workspace above 16
+ * tokens (see SRA_TUNE_ENGINE); 2:8 has no pair kernel, streaming layout or masked gradient.  The streaming layout (sra_nm_tile, sra_compress_pair_tiled) is
  * 2:4 only.  The caller sets out->values and out->meta; the call
  * fills the remaining descriptor fields (format, dtype, rows, cols, n, m).
  */
@@ -123,7 +127,7 @@ sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols
  * In each group of m consecutive outputs of one input column, only entries kept by Ws are
  * eligible; the n largest eligible are kept.  A group with fewer than n eligible entries is padded
  * with its lowest unused positions holding +0.0, so every group stores exactly n.
- * Supported: 2:4 and 1:2, Ws->rows % 32 == 0, Ws->cols % 32 == 0.
+ * Supported: 2:4, 1:2 and 2:8 (bf16), Ws->rows % 32 == 0, Ws->cols % 32 == 0.
  */
 sra_status sra_double_prune(const sra_sparse* Ws /* host */, sra_sparse* P /* host */, void* stream);
 
@@ -378,8 +382,11 @@ sra_status sra_nm_axpby(const void* a_values, float beta, const void* b_values, 
  *   SRA_TUNE_ENGINE        SRA_ENGINE_SMFMAC (default): 2:4 products on the structured-sparse
  *                          matrix instructions; SRA_ENGINE_DENSE_MFMA: the same pipeline with each
  *                          weight fragment expanded to dense bf16 (zeros at the pruned positions)
- *                          for dense MFMA, the path 2:8 weights always take (bf16, K % 128 == 0
- *                          for the forward, N % 128 == 0 for the backward)
+ *                          for dense MFMA (bf16, K % 128 == 0 for the forward, N % 128 == 0 for
+ *                          the backward), the path 2:8 weights take for 16 tokens or fewer; above
+ *                          that, on SMFMAC, a 2:8 weight is rewritten in the call's workspace as a
+ *                          2:4 one (each four columns of a 2:8 row hold at most two kept entries;
+ *                          +0.0 fills the rest) and runs on the 2:4 kernels
  *   SRA_TUNE_DECODE_ROWS   decode workgroup row tiles of 16 rows: 3, 4 or 9 (0 = the planner's)
  *   SRA_TUNE_ROWS_SLICES   reduction slices of the rank > 32 U / dU kernel (0 = the planner's)
  *   SRA_TUNE_GRADS_SLICES  token slices of the dA / dB kernel (0 = the planner's)

@@ -79,11 +79,16 @@ sra_status check_nm(int64_t rows, int64_t cols, int n, int m) {
 constexpr uint32_t kMeta12To24 = 0x88888888u;
 bool is12(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 1 && S->m == 2; }
 bool is28(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 2 && S->m == 8; }
-// 2:8 weights, and bf16 2:4 weights on the dense-MFMA engine, run the expanded-fragment products
-bool use_xp(const sra_sparse* S) {
+// bf16 N:M weights on the dense-MFMA engine, and 2:8 weights for 16 tokens or fewer, run the
+// expanded-fragment products.  Otherwise 2:8 weights run on the 2:4 kernels: every group of four
+// columns of a 2:8 row holds at most two kept entries, so the call rewrites the weight as a 2:4
+// one (the same entries plus +0.0 fillers) in its workspace first.  With few tokens a product
+// reads the weight once, and that rewrite would cost more than it saves.
+bool use_xp(const sra_sparse* S, int64_t T) {
   if (S->format != SRA_FMT_NM && S->format != SRA_FMT_NM_TILED) return false;
-  return is28(S) || (S->dtype == SRA_BF16 && sra::tuning().engine == SRA_ENGINE_DENSE_MFMA);
+  return (S->dtype == SRA_BF16 && sra::tuning().engine == SRA_ENGINE_DENSE_MFMA) || (is28(S) && T <= 16);
 }
+bool is28_on24(const sra_sparse* S, int64_t T) { return is28(S) && !use_xp(S, T); }
 size_t meta_bytes(const sra_sparse* S) {
   return (size_t)S->rows * (size_t)sra_nm_meta_words(S->cols, S->n, S->m) * 4;
 }
@@ -154,7 +159,7 @@ sra::F32Sparse f32_view(const sra_sparse* S) {
 
 // ---------------------------------------------------------------- forward plan
 struct FwdPlan {
-  size_t u_off = 0, u64_off = 0, gemm_off = 0, ffi_off = 0, meta_off = 0, total = 0;
+  size_t u_off = 0, u64_off = 0, gemm_off = 0, ffi_off = 0, meta_off = 0, v24_off = 0, total = 0;
   bool own_u = false;
 };
 
@@ -172,7 +177,7 @@ sra_status validate_fwd(const sra_sparse* Ws, int64_t T, int32_t r) {
   if (r < 0 || r > 256) return fail(SRA_ERR_UNSUPPORTED, "rank %d outside [0, 256]", r);
   if (Ws->format == SRA_FMT_NM && Ws->dtype == SRA_BF16 && Ws->cols == 0)
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 forward needs K > 0");
-  if (use_xp(Ws) && T > 0 && !sra::spmm_xp_ok(Ws->cols))
+  if (use_xp(Ws, T) && T > 0 && !sra::spmm_xp_ok(Ws->cols))
     return fail(SRA_ERR_UNSUPPORTED, "%s products need K %% 128 == 0 (K = %lld)",
                 is28(Ws) ? "2:8" : "dense-MFMA 2:4", (long long)Ws->cols);
   return SRA_OK;
@@ -186,7 +191,7 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
   if (Ws->dtype == SRA_F32 && r > 0) p.u64_off = a.take((size_t)T * r * 8);
   if (Ws->dtype == SRA_BF16) {
     size_t g = r > 0 ? sra::adapter_rows_ws(T, Ws->cols, r) : 0;
-    if (use_xp(Ws))
+    if (use_xp(Ws, T))
       g = std::max(g, sra::spmm_xp_ws(Ws->rows, Ws->cols, T));
     else if (Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED)
       g = std::max(g, sra::spmm24_ws(Ws->rows, Ws->cols, T));
@@ -195,6 +200,10 @@ size_t fwd_bytes(const sra_sparse* Ws, int64_t T, int32_t r, bool own_u, FwdPlan
       p.ffi_off = a.take(sra::spmm_ffi_ws(Ws->rows, Ws->cols, T, Ws->rows * Ws->k));
   }
   if (is12(Ws)) p.meta_off = a.take(meta_bytes(Ws));  // the 2:4 encoding of the metadata
+  if (is28_on24(Ws, T)) {  // the 2:4 form of a 2:8 weight (one metadata word per 32 columns in both)
+    p.meta_off = a.take(meta_bytes(Ws));
+    p.v24_off = a.take((size_t)Ws->rows * (size_t)(Ws->cols / 2) * 2);
+  }
 
   p.total = a.used;
   if (plan) *plan = p;
@@ -207,7 +216,8 @@ struct BwdPlan {
   size_t u_off = 0, du_off = 0, u64_off = 0, du64_off = 0, gemm_off = 0, spmm_off = 0, total = 0;
   size_t wt_off = 0, vtu_off = 0, vtdu_off = 0;  // packed B^T, split U^T (dB), split dU^T (dA)
   size_t at_off = 0;                             // packed A^T (dX epilogue)
-  size_t meta_off = 0;                           // 1:2 metadata in the 2:4 encoding
+  size_t meta_off = 0;                           // 1:2 (or 2:8) metadata in the 2:4 encoding
+  size_t v24_off = 0;                            // 2:8 values in the 2:4 layout
 };
 
 sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags) {
@@ -226,7 +236,7 @@ sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flag
   if (flags & ~15u) return fail(SRA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (P->format == SRA_FMT_NM && P->dtype == SRA_BF16 && (flags & SRA_GRAD_DX) && P->cols == 0)
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 dX needs N > 0");
-  if (use_xp(P) && (flags & SRA_GRAD_DX) && T > 0 && !sra::spmm_xp_ok(P->cols))
+  if (use_xp(P, T) && (flags & SRA_GRAD_DX) && T > 0 && !sra::spmm_xp_ok(P->cols))
     return fail(SRA_ERR_UNSUPPORTED, "%s dX needs N %% 128 == 0 (N = %lld)",
                 is28(P) ? "2:8" : "dense-MFMA 2:4", (long long)P->cols);
   return SRA_OK;
@@ -262,6 +272,10 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
   p.need_u = r > 0 && db;
   Arena a;
   if (is12(P) && dx) p.meta_off = a.take(meta_bytes(P));
+  if (is28_on24(P, T) && dx) {
+    p.meta_off = a.take(meta_bytes(P));
+    p.v24_off = a.take((size_t)P->rows * (size_t)(P->cols / 2) * 2);
+  }
   if (P->dtype == SRA_F32) {  // fp32: U and dU stay fp64; U is always recomputed
     if (p.need_u) p.u64_off = a.take((size_t)T * r * 8);
     if (p.need_du) p.du64_off = a.take((size_t)T * r * 8);
@@ -288,7 +302,7 @@ size_t bwd_bytes(const sra_sparse* P, int64_t T, int32_t r, uint32_t flags, bool
     g = std::max(g, sra::adapter_grads_ws(jobs, nj, T, r));
     p.gemm_off = a.take(g);
   }
-  if (P->dtype == SRA_BF16 && use_xp(P) && dx)
+  if (P->dtype == SRA_BF16 && use_xp(P, T) && dx)
     p.spmm_off = a.take(sra::spmm_xp_ws(K, N, T));
   else if (P->dtype == SRA_BF16 && (P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED) && dx)
     p.spmm_off = a.take(sra::spmm24_ws(K, N, T));
@@ -702,6 +716,16 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     SRA_TRY(hip_done(sra::launch_meta_or(Ws->meta, w24.meta, (int64_t)(meta_bytes(Ws) / 4), kMeta12To24, s),
                      s, "fwd 1:2 metadata"));
     Ws = &w24;
+  } else if (is28_on24(Ws, T)) {  // run on the 2:4 kernels with the weight rewritten as 2:4
+    w24 = *Ws;
+    w24.values = wsb + plan.v24_off;
+    w24.meta = (uint32_t*)(wsb + plan.meta_off);
+    w24.n = 2;
+    w24.m = 4;
+    SRA_TRY(hip_done(sra::launch_nm28_to24((const uint16_t*)Ws->values, Ws->meta, Ws->rows, Ws->cols,
+                                           (uint16_t*)w24.values, w24.meta, s),
+                     s, "fwd 2:8 as 2:4"));
+    Ws = &w24;
   }
 
   if (Ws->dtype == SRA_F32) {
@@ -715,7 +739,7 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
   }
   // U = X A^T: computed inside the SpMM when its plan allows, else by the adapter kernel first
   const bool nm24 = Ws->format == SRA_FMT_NM || Ws->format == SRA_FMT_NM_TILED;
-  const bool xp = use_xp(Ws);
+  const bool xp = use_xp(Ws, T);
   const bool fuse = r > 0 && nm24 && (xp ? sra::spmm_xp_fuses_adapter(N, K, T, r)
                                          : sra::spmm24_fuses_adapter(N, K, T, r));
   if (r > 0 && !fuse)
@@ -796,6 +820,16 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     SRA_TRY(hip_done(sra::launch_meta_or(P->meta, p24.meta, (int64_t)(meta_bytes(P) / 4), kMeta12To24, s),
                      s, "bwd 1:2 metadata"));
     P = &p24;
+  } else if (is28_on24(P, T) && fdx) {  // dX on the 2:4 kernels with P rewritten as 2:4
+    p24 = *P;
+    p24.values = wsb + plan.v24_off;
+    p24.meta = (uint32_t*)(wsb + plan.meta_off);
+    p24.n = 2;
+    p24.m = 4;
+    SRA_TRY(hip_done(sra::launch_nm28_to24((const uint16_t*)P->values, P->meta, P->rows, P->cols,
+                                           (uint16_t*)p24.values, p24.meta, s),
+                     s, "bwd 2:8 as 2:4"));
+    P = &p24;
   }
   const float* Uv = plan.need_u ? (plan.own_u ? (const float*)(wsb + plan.u_off) : U) : nullptr;
   float* dU = plan.need_du ? (plan.own_du ? (float*)(wsb + plan.du_off) : dU_out) : nullptr;
@@ -833,7 +867,7 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
   // dU = dY B: computed inside the dX SpMM (which also writes dU_out and dU^T's parts for dA)
   // when its plan allows, else by the adapter kernel first
   const bool nm24 = P->format == SRA_FMT_NM || P->format == SRA_FMT_NM_TILED;
-  const bool xp = use_xp(P);
+  const bool xp = use_xp(P, T);
   const bool fuse = dx_ad && nm24 && (xp ? sra::spmm_xp_fuses_adapter(K, N, T, r)
                                          : sra::spmm24_fuses_adapter(K, N, T, r));
   if (plan.need_du && !fuse)

@@ -125,6 +125,11 @@ hipError_t launch_double_prune12(int dtype, const void* vals, const uint32_t* me
                                  int64_t cols, void* p_vals, uint32_t* p_meta, hipStream_t s);
 hipError_t launch_meta_or(const uint32_t* in, uint32_t* out, int64_t n, uint32_t bits, hipStream_t s);
 // 2:8 (bf16): one 3-bit field per kept value, the two of a group in one byte, 4 groups per word
+// 2:8 canonical arrays (values [rows][cols/4], one byte of two 3-bit positions per 8-column
+// group) rewritten as 2:4 canonical arrays (values [rows][cols/2], 2-bit fields) holding the same
+// entries plus +0.0 fillers, for the 2:4 products (cols % 32 == 0)
+hipError_t launch_nm28_to24(const uint16_t* v8, const uint32_t* m8, int64_t rows, int64_t cols,
+                            uint16_t* v4, uint32_t* m4, hipStream_t s);
 hipError_t launch_compress28(const uint16_t* W, int64_t rows, int64_t cols, uint16_t* vals, uint32_t* meta,
                              hipStream_t s);
 hipError_t launch_double_prune28(const uint16_t* vals, const uint32_t* meta, int64_t rows, int64_t cols,

@@ -648,9 +648,70 @@ __global__ __launch_bounds__(256) void k_double_prune28(const uint16_t* __restri
   p_meta[k * (rows / 32) + g0 / 32] = word;
 }
 
+// 2:8 rows as 2:4 rows.  A 2:8 row keeps two entries of every eight columns, so each group of four
+// holds at most two of them: the row is a 2:4 row once each four-column half is filled up to two
+// stored values with +0.0 at its lowest unused positions (the zeros add nothing to any product).
+// One lane per 32-column block: 8 values and one 2:8 metadata word in, 16 values and one 2:4
+// metadata word out (both formats keep one word per 32 columns).
+// Rows are whole metadata words, so metadata word i covers 2:8 values [8i, 8i + 8) and 2:4
+// values [16i, 16i + 16) of the flat arrays: one lane per word, no row arithmetic. The 2:8 arrays
+// are read once per call and not again by the product, so their loads bypass the caches.
+__global__ __launch_bounds__(256) void k_nm28_to24(const uint16_t* __restrict__ v8,
+                                                   const uint32_t* __restrict__ m8, int64_t words,
+                                                   uint16_t* __restrict__ v4,
+                                                   uint32_t* __restrict__ m4) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= words) return;
+  union { u32x4 v; uint16_t h[8]; } in;
+  in.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v8) + id);
+  const uint32_t word8 = __builtin_nontemporal_load(m8 + id);
+  union { u32x4 v[2]; uint16_t h[16]; } out;
+  uint32_t word4 = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t byte = (word8 >> (8 * g)) & 0xFFu, p0 = byte & 7u, p1 = (byte >> 3) & 7u;
+    const uint16_t a = in.h[2 * g], b = in.h[2 * g + 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t lo = 4u * h;
+      const bool k0 = p0 >= lo && p0 < lo + 4, k1 = p1 >= lo && p1 < lo + 4;
+      uint32_t q0, q1;
+      uint16_t x0, x1;
+      if (k0 && k1) {
+        q0 = p0 - lo; q1 = p1 - lo; x0 = a; x1 = b;
+      } else if (k0 || k1) {
+        const uint32_t q = (k0 ? p0 : p1) - lo, z = q == 0 ? 1u : 0u;
+        const uint16_t v = k0 ? a : b;
+        if (z < q) { q0 = z; q1 = q; x0 = 0; x1 = v; }
+        else { q0 = q; q1 = z; x0 = v; x1 = 0; }
+      } else {
+        q0 = 0; q1 = 1; x0 = 0; x1 = 0;
+      }
+      const int grp = 2 * g + h;  // four-column group of the block
+      out.h[2 * grp] = x0;
+      out.h[2 * grp + 1] = x1;
+      word4 |= (q0 | (q1 << 2)) << (4 * grp);
+    }
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(v4) + 2 * id;
+  dst[0] = out.v[0];
+  dst[1] = out.v[1];
+  m4[id] = word4;
+}
+
 }  // namespace
 
 namespace sra {
+
+hipError_t launch_nm28_to24(const uint16_t* v8, const uint32_t* m8, int64_t rows, int64_t cols,
+                            uint16_t* v4, uint32_t* m4, hipStream_t s) {
+  const int64_t wpr = cols / 32, total = rows * wpr;
+  if (total == 0) return hipSuccess;
+  if (cols % 32) return hipErrorInvalidValue;
+  launch(SRA_KERNEL_COMPRESS, k_nm28_to24, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, v8, m8,
+         total, v4, m4);
+  return hipGetLastError();
+}
 
 hipError_t launch_compress28(const uint16_t* W, int64_t rows, int64_t cols, uint16_t* vals, uint32_t* meta,
                              hipStream_t s) {

@@ -94,9 +94,21 @@ SHAPES = [(300, 256, 384, 24), (77, 128, 640, 5), (130, 384, 256, 1), (5, 512, 2
           (1030, 2048, 1536, 128), (257, 1024, 512, 0), (700, 1152, 640, 16)]
 
 
+@pytest.mark.parametrize("engine", ["smfmac", "dense_mfma"])
 @pytest.mark.parametrize("T,K,N,r", SHAPES)
-def test_layer_2_8(gpu, T, K, N, r):
-    run_layer(Workload("nm28", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + K)
+def test_layer_2_8(gpu, T, K, N, r, engine):
+    """2:8 weights rewritten as 2:4 for the SMFMAC kernels (more than 16 tokens; the default), and
+    on the expanded-fragment dense-MFMA kernels."""
+    with sra.tuned(engine=engine):
+        run_layer(Workload("nm28", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + K)
+
+
+# shapes only the 2:4 route takes (K or N a multiple of 32, not of 128), and 16 tokens (the
+# expanded-fragment path at any engine)
+@pytest.mark.parametrize("T,K,N,r", [(100, 96, 160, 8), (257, 224, 96, 24), (40, 64, 32, 0),
+                                     (16, 256, 384, 16)])
+def test_layer_2_8_as_2_4_shapes(gpu, T, K, N, r):
+    run_layer(Workload("nm28s", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + N)
 
 
 def test_layer_2_8_opt350m_fc1(gpu):
@@ -147,10 +159,16 @@ def test_2_8_rejections(gpu):
         sra.compress(W.float(), 2, 8)
     assert e.value.status == SRA_ERR_UNSUPPORTED
     S = sra.compress(W, 2, 8)
-    X = torch.zeros(300, 64, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(SraError) as e:      # products need K % 128 == 0
+    # Up to 16 tokens the expansion product needs K % 128 == 0; above that the
+    # weight runs as 2:4, which takes this K.
+    X = torch.zeros(16, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(SraError) as e:
         sra.sparse_lora_fwd(S, X)
     assert e.value.status == SRA_ERR_UNSUPPORTED
+    X = torch.ones(300, 64, dtype=torch.bfloat16, device="cuda")
+    Y, _ = sra.sparse_lora_fwd(S, X)
+    torch.cuda.synchronize()
+    assert Y.shape == (300, 64) and not Y.float().abs().any()
     with pytest.raises(SraError):
         sra.nm_tile(S)
     with pytest.raises(SraError):
