@@ -706,11 +706,12 @@ def bench_mlp_chain(args, inputs=None, nm="2:4", engine_eval=True):
     return line, (i1, i2)
 
 
-def decode_bytes(wl, T, kernel_only=False):
+def decode_bytes(wl, T, kernel_only=False, m=4):
     """Algorithmic HBM bytes of one decode forward call (or of the decode kernel alone: the
-    down-projection U = X A^T reads A in its own launch, the kernel reads U instead)."""
+    down-projection U = X A^T reads A in its own launch, the kernel reads U instead), for a 2:4
+    (m = 4) or 2:8 (m = 8) weight."""
     K, N, r, e = wl.K, wl.N, wl.r, 2
-    w = N * K // 2 * e + N * K // 8                      # stored values + 2-bit metadata
+    w = N * K * 2 // m * e + N * K // 8                  # stored values + metadata (1 bit per entry)
     common = w + N * r * e + T * K * e + T * N * e      # + B, X, Y
     return common + (T * r * 4 if kernel_only else r * K * e)
 
@@ -732,6 +733,7 @@ def bench_decode(args, wl, Ts):
     r = wl.r
     canon = (sra.compress(W), sra.compress(W))
     streaming = tuple(sra.nm_tile(S) for S in canon)
+    nm28 = (sra.compress(W, 2, 8), sra.compress(W, 2, 8))
     main, other = (streaming, canon) if args.decode_layout == "streaming" else (canon, streaming)
     dense = (W, W.clone())
     rows = []
@@ -757,6 +759,11 @@ def bench_decode(args, wl, Ts):
         call_ms = time_graph(both, args.steps, args.warmup, not args.no_graph) / 2
         k_ms = time_kernel(SRA_KERNEL_DECODE24, alternate(main), max(20, args.steps))
         k2_ms = time_kernel(SRA_KERNEL_DECODE24, alternate(other), max(20, args.steps))
+        # the same weight at 2:8 (its own decode kernel, canonical arrays)
+        k28_ms = time_kernel(SRA_KERNEL_DECODE24, alternate(nm28), max(20, args.steps))
+        c28_ms = time_graph(lambda: [sra.sparse_lora_fwd(S, Xt, A, B, Y=Y, U=U, ws=ws) for S in nm28],
+                            args.steps, args.warmup, not args.no_graph) / 2
+        kb28 = decode_bytes(wl, T, kernel_only=True, m=8)
         d_ms = time_graph(lambda: [torch.nn.functional.linear(Xt, Wd) for Wd in dense], args.steps,
                           args.warmup, not args.no_graph) / 2
         kb = decode_bytes(wl, T, kernel_only=True)
@@ -767,7 +774,12 @@ def bench_decode(args, wl, Ts):
                      "call_GBps": round(decode_bytes(wl, T) / (call_ms * 1e-3) / 1e9, 1),
                      "dense_us": round(d_ms * 1e3, 2), "speedup_vs_dense": round(d_ms / call_ms, 3),
                      "other_layout_kernel_us": round(k2_ms * 1e3, 2),
-                     "other_layout_frac_hbm": round(kb / (k2_ms * 1e-3) / PEAK_HBM_BPS, 4)})
+                     "other_layout_frac_hbm": round(kb / (k2_ms * 1e-3) / PEAK_HBM_BPS, 4),
+                     "nm28_kernel_us": round(k28_ms * 1e3, 2),
+                     "nm28_kernel_GBps": round(kb28 / (k28_ms * 1e-3) / 1e9, 1),
+                     "nm28_kernel_frac_hbm": round(kb28 / (k28_ms * 1e-3) / PEAK_HBM_BPS, 4),
+                     "nm28_call_us": round(c28_ms * 1e3, 2),
+                     "nm28_speedup_vs_dense": round(d_ms / c28_ms, 3)})
     return rows
 
 

@@ -79,16 +79,18 @@ sra_status check_nm(int64_t rows, int64_t cols, int n, int m) {
 constexpr uint32_t kMeta12To24 = 0x88888888u;
 bool is12(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 1 && S->m == 2; }
 bool is28(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 2 && S->m == 8; }
-// bf16 N:M weights on the dense-MFMA engine, and 2:8 weights for 16 tokens or fewer, run the
-// expanded-fragment products.  Otherwise 2:8 weights run on the 2:4 kernels: every group of four
-// columns of a 2:8 row holds at most two kept entries, so the call rewrites the weight as a 2:4
-// one (the same entries plus +0.0 fillers) in its workspace first.  With few tokens a product
-// reads the weight once, and that rewrite would cost more than it saves.
+// 2:8 weights for 16 tokens or fewer run the 2:8 decode kernel (one streaming pass over the
+// weight, fragments expanded to dense in registers).  Otherwise bf16 N:M weights on the dense-MFMA
+// engine run the expanded-fragment products, and 2:8 weights run on the 2:4 kernels: every group
+// of four columns of a 2:8 row holds at most two kept entries, so the call rewrites the weight as
+// a 2:4 one (the same entries plus +0.0 fillers) in its workspace first.  With few tokens a
+// product reads the weight once, and that rewrite would cost more than it saves.
+bool use_dec28(const sra_sparse* S, int64_t T) { return is28(S) && T <= 16; }
 bool use_xp(const sra_sparse* S, int64_t T) {
   if (S->format != SRA_FMT_NM && S->format != SRA_FMT_NM_TILED) return false;
-  return (S->dtype == SRA_BF16 && sra::tuning().engine == SRA_ENGINE_DENSE_MFMA) || (is28(S) && T <= 16);
+  return S->dtype == SRA_BF16 && sra::tuning().engine == SRA_ENGINE_DENSE_MFMA && !use_dec28(S, T);
 }
-bool is28_on24(const sra_sparse* S, int64_t T) { return is28(S) && !use_xp(S, T); }
+bool is28_on24(const sra_sparse* S, int64_t T) { return is28(S) && !use_dec28(S, T) && !use_xp(S, T); }
 size_t meta_bytes(const sra_sparse* S) {
   return (size_t)S->rows * (size_t)sra_nm_meta_words(S->cols, S->n, S->m) * 4;
 }
@@ -756,6 +758,10 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     ep.g_ld = K;
     ep.u_out = U_out;
   }
+  if (use_dec28(Ws, T))
+    return hip_done(sra::launch_decode28_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
+                                              (const uint16_t*)X, T, ep, (uint16_t*)Y, s),
+                    s, "fwd spmm 2:8 (decode)");
   if (xp)
     return hip_done(sra::launch_spmm_xp_bf16(is28(Ws) ? 28 : 24, Ws->format == SRA_FMT_NM_TILED,
                                              (const uint16_t*)Ws->values, Ws->meta, N, K,
@@ -888,7 +894,11 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
       ep.vt_rp = (int)sra::vt_rows(r);
       ep.vt_tp = sra::vt_cols(T);
     }
-    if (xp)
+    if (use_dec28(P, T))
+      SRA_TRY(hip_done(sra::launch_decode28_bf16((const uint16_t*)P->values, P->meta, K, N,
+                                                 (const uint16_t*)dY, T, ep, (uint16_t*)dX, s),
+                       s, "bwd dX 2:8 (decode)"));
+    else if (xp)
       SRA_TRY(hip_done(sra::launch_spmm_xp_bf16(is28(P) ? 28 : 24, P->format == SRA_FMT_NM_TILED,
                                                 (const uint16_t*)P->values, P->meta, K, N,
                                                 (const uint16_t*)dY, T, ep, (uint16_t*)dX,

@@ -71,6 +71,110 @@ struct DecLds {
   static constexpr int BYTES = ML + XL > RED ? ML + XL : RED;
 };
 
+// Adapter epilogue of both decode kernels.  Lane (l16, q) takes E(row rt + l16, j = jb .. jb+7) and
+// U(token l16, j = jb .. jb+7) for jb = jj + 8q.  The first 64 adapter columns of the first row
+// tile a wave finishes are loaded at construction, before the weight stream, so their latency is
+// hidden behind it instead of following it (not for 64-row tiles, which have no registers to
+// spare).  finish_tile() adds U E^T to row tile i's sums on v_mfma_f32_16x16x32_bf16 (U as bf16
+// hi + lo) and stores bf16 rows 4q .. 4q+3 of token l16; finish() first sums the NW waves' partial
+// tiles through LDS in wave order (deterministic), and row tile i is finished by wave i % NW.
+template <int FR, int NW, int PF = FR == 4 ? 0 : 2>
+struct DecodeTail {
+  const sra::Epilogue& ep;
+  const int64_t R, T, row0;
+  const int w, l, l16, q;
+  const bool tok_ok, e_vec, pf;
+  u32x4 pf_e[2];
+  float pf_u[2][8];
+
+  SRA_DEV DecodeTail(const sra::Epilogue& ep_, int64_t R_, int64_t T_, int64_t row0_, int w_, int l_)
+      : ep(ep_), R(R_), T(T_), row0(row0_), w(w_), l(l_), l16(l_ & 15), q(l_ >> 4), tok_ok(l16 < T_),
+        e_vec(ep_.e_j_stride == 1 && (ep_.r & 7) == 0 && (ep_.e_row_stride & 7) == 0),
+        pf(PF > 0 && ep_.r > 0 && w_ < FR && row0_ + 16 * w_ < R_) {
+    if (pf) {
+#pragma unroll
+      for (int c = 0; c < PF; ++c) {
+        pf_e[c] = load_e(row0 + 16 * w + l16, 32 * c + 8 * q);
+        load_u(32 * c + 8 * q, pf_u[c]);
+      }
+    }
+  }
+  SRA_DEV u32x4 load_e(int64_t erow, int jb) const {
+    union { u32x4 v; uint16_t h[8]; } x;
+    x.v = u32x4{0, 0, 0, 0};
+    if (erow < R) {
+      if (e_vec && jb + 8 <= ep.r) {
+        x.v = *reinterpret_cast<const u32x4*>(ep.E + erow * ep.e_row_stride + jb);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (jb + e < ep.r) x.h[e] = ep.E[erow * ep.e_row_stride + (int64_t)(jb + e) * ep.e_j_stride];
+      }
+    }
+    return x.v;
+  }
+  SRA_DEV void load_u(int jb, float (&u)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = tok_ok && jb + e < ep.r ? ep.U[(int64_t)l16 * ep.r + jb + e] : 0.f;
+  }
+  // call after the last use of the staging LDS by any wave (a barrier)
+  SRA_DEV void finish(const f32x4 (&acc)[FR], unsigned char* lds, uint16_t* __restrict__ out) {
+    f32x4* red = reinterpret_cast<f32x4*>(lds);  // [wave][tile][lane]
+#pragma unroll
+    for (int i = 0; i < FR; ++i) red[(w * FR + i) * 64 + l] = acc[i];
+    __syncthreads();
+    for (int i = w; i < FR; i += NW) {
+      if (row0 + 16 * i >= R) break;
+      f32x4 y = red[i * 64 + l];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) y += red[(k * FR + i) * 64 + l];
+      finish_tile(y, i, out);
+    }
+  }
+  SRA_DEV void finish_tile(f32x4 y, int i, uint16_t* __restrict__ out) {
+    const int64_t rt = row0 + 16 * i;
+    if (rt >= R) return;
+    // ---- adapter epilogue: A operand = E rows (row l16, j = 8q..), B operand = U^T (token l16)
+    if (ep.r > 0) {
+      const bool first = pf && i == w;  // the prefetched tile
+      for (int jj = 0; jj < ep.r; jj += 32) {
+        const int jb = jj + 8 * q;
+        union { u32x4 v; bf16x8 b; } x;
+        float u[8];
+        if (first && jj < 32 * PF) {
+          const int c = jj / 32;
+          x.v = c == 0 ? pf_e[0] : pf_e[1];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) u[e] = c == 0 ? pf_u[0][e] : pf_u[1][e];
+        } else {
+          x.v = load_e(rt + l16, jb);
+          load_u(jb, u);
+        }
+        union UH { uint16_t h[8]; bf16x8 b; } uhi, ulo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(u[e], uhi.h[e], ulo.h[e]);
+        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, uhi.b, y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, ulo.b, y, 0, 0, 0);
+      }
+    }
+
+    // ---- store rows rt + 4q .. +3 of token l16
+    if (!tok_ok) return;
+    const int64_t n = rt + 4 * q;
+    uint16_t* o = out + (int64_t)l16 * R + n;
+    if ((R & 3) == 0 && n + 4 <= R) {
+      u32x2 v;
+      v[0] = pack_bf16x2(y[0], y[1]);
+      v[1] = pack_bf16x2(y[2], y[3]);
+      *reinterpret_cast<u32x2*>(o) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < R) o[e] = f32_to_bf16(y[e]);
+    }
+  }
+};
+
 // FR 16-row tiles per workgroup, NW waves splitting each batch's 8 steps (SPW each), OCC
 // workgroups per CU.  (3, 4): 48 rows, 3 per CU; (4, 4): 64 rows; (9, 8): 144 rows, one per CU,
 // which reads the Act block a third as often per weight byte.
@@ -178,42 +282,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode24(const uint16_t* __res
     }
   };
 
-  // Adapter operands of the epilogue: lane (l16, q) takes E(row rt + l16, j = jb .. jb+7) and
-  // U(token l16, j = jb .. jb+7) for jb = jj + 8q.  The first 64 adapter columns of the first row
-  // tile this wave finishes are loaded here, before the weight stream, so their latency is hidden
-  // behind it instead of following it.
-  const bool tok_ok = l16 < T;
-  const bool e_vec = ep.e_j_stride == 1 && (ep.r & 7) == 0 && (ep.e_row_stride & 7) == 0;
-  auto load_e = [&](int64_t erow, int jb) {
-    union { u32x4 v; uint16_t h[8]; } x;
-    x.v = u32x4{0, 0, 0, 0};
-    if (erow < R) {
-      if (e_vec && jb + 8 <= ep.r) {
-        x.v = *reinterpret_cast<const u32x4*>(ep.E + erow * ep.e_row_stride + jb);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (jb + e < ep.r) x.h[e] = ep.E[erow * ep.e_row_stride + (int64_t)(jb + e) * ep.e_j_stride];
-      }
-    }
-    return x.v;
-  };
-  auto load_u = [&](int jb, float (&u)[8]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u[e] = tok_ok && jb + e < ep.r ? ep.U[(int64_t)l16 * ep.r + jb + e] : 0.f;
-  };
-  // prefetched 32-column adapter blocks (none for 64-row tiles, which have no registers to spare)
-  constexpr int PF = FR == 4 ? 0 : 2;
-  u32x4 pf_e[2];
-  float pf_u[2][8];
-  const bool pf = PF > 0 && ep.r > 0 && w < FR && row0 + 16 * w < R;
-  if (pf) {
-#pragma unroll
-    for (int c = 0; c < PF; ++c) {
-      pf_e[c] = load_e(row0 + 16 * w + l16, 32 * c + 8 * q);
-      load_u(32 * c + 8 * q, pf_u[c]);
-    }
-  }
+  DecodeTail<FR, NW> tail(ep, R, T, row0, w, l);
 
   // Ping-pong over register batches; batches past the end are all-zero loads.  sched_barrier
   // keeps the compiler from sinking a batch's loads down to their first use.
@@ -233,60 +302,162 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode24(const uint16_t* __res
     compute(1, b1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();  // the reduction below reuses the staging LDS
+  __syncthreads();  // the reduction reuses the staging LDS
+  tail.finish(acc, lds, out);
+}
 
-  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [wave][tile][lane]
-#pragma unroll
-  for (int i = 0; i < FR; ++i) red[(w * FR + i) * 64 + l] = acc[i];
-  __syncthreads();
-  // row tile i is finished by wave i % NW: partials summed in wave order (deterministic), adapter
-  // epilogue, bf16 store
-  for (int i = w; i < FR; i += NW) {
-    const int64_t rt = row0 + 16 * i;
-    if (rt >= R) break;
-    f32x4 y = red[i * 64 + l];
-#pragma unroll
-    for (int k = 1; k < NW; ++k) y += red[(k * FR + i) * 64 + l];
+// 2:8 weights at T <= 16 (canonical arrays; SLoPe paper, section 2.1, N:M sparsity with M = 8).
+// The pass reads 5/8 of a byte per weight entry (a quarter of the values plus 3-bit positions).
+// Each 8-column group is fed to v_smfmac_f32_16x16x64_bf16 as two 2:4 groups, formed in
+// registers: the half of positions 0-3 takes the pair (first value if its position is below 4,
+// else 0; second value likewise) and the half of positions 4-7 the complementary pair, both with
+// 2-bit indices (position % 4) of the first and the second value.  A value that is zeroed in a half
+// keeps its index there (it may then name the same column as the other value, adding a zero
+// product).  That is about 9 instructions per group; expanding to dense bf16 for dense MFMA took
+// 19 and made the pass bound by them.  The layout differs from the 2:4 kernel's to keep more waves
+// in flight and fewer bytes besides the weight:
+//   - each of the NW waves owns FW whole 16-row tiles (tile w + NW f), so there is no reduction
+//     over waves, and a 256-column batch of a tile is one contiguous run per row: lane (l16, q) reads
+//     row l16's groups 8q .. 8q+7 of the batch, 32 bytes of values and its 2 metadata words (8 bytes)
+//     straight into registers (one batch ahead);
+//   - the Act batch (T x 256) is staged once per workgroup in LDS and shared by its 16 NW FW rows;
+//   - SMFMAC step j of a batch takes the lane's groups 2j and 2j + 1 (of its 8: groups 8q .. 8q+7
+//     of the batch) as its 16 logical columns 16q .. 16q+15 (the reduction order permuted the same
+//     way on both operands).  Lane (token l16, q) of the B operand holds logical rows 8q .. 8q+7,
+//     which are group 8 (q / 2) + 2j + q % 2 of the batch, and rows 32 + 8q .. +7, group
+//     8 (2 + q / 2) + 2j + q % 2.  Each 64-column block of a staged Act row is followed by 16 bytes
+//     of padding, which spreads the lanes' 16-byte reads over the banks.
+// LDS row of a staged Act batch of BW columns: each 64-column block plus 8 columns of padding, and
+// 8 more so that consecutive tokens start on different banks
+template <int BW>
+constexpr int d28_xld() { return BW + BW / 8 + 8; }
+SRA_DEV int d28_col(int c) { return c + 8 * (c >> 6); }
 
-    // ---- adapter epilogue: A operand = E rows (row l16, j = 8q..), B operand = U^T (token l16)
-    if (ep.r > 0) {
-      const bool first = pf && i == w;  // the prefetched tile
-      for (int jj = 0; jj < ep.r; jj += 32) {
-        const int jb = jj + 8 * q;
-        union { u32x4 v; bf16x8 b; } x;
-        float u[8];
-        if (first && jj < 32 * PF) {
-          const int c = jj / 32;
-          x.v = c == 0 ? pf_e[0] : pf_e[1];
+// One BW-column batch of a wave: CL = BW / 128 chunks of 16 bytes (4 groups, one 32-bit word
+// each) per row tile and lane, the lane's CL metadata words, and its share of the Act staging.
+template <int NW, int FW, int BW>
+struct Batch28 {
+  static constexpr int CL = BW / 128, XC = (2 * BW + 64 * NW - 1) / (64 * NW);
+  u32x4 v[FW][CL];
+  uint32_t m[FW][CL];
+  u32x4 x[XC];
+};
+
+template <int NW, int FW, int BW, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void k_decode28(const uint16_t* __restrict__ vals,
+                                                          const uint32_t* __restrict__ meta, int64_t R,
+                                                          int64_t C, const uint16_t* __restrict__ act,
+                                                          int64_t T, sra::Epilogue ep,
+                                                          uint16_t* __restrict__ out) {
+  using BT = Batch28<NW, FW, BW>;
+  constexpr int FR = NW * FW, RB = 16 * FR, NT = 64 * NW, CL = BT::CL, XC = BT::XC;
+  constexpr int XLD = d28_xld<BW>(), XCH = 2 * BW;  // Act chunks per batch (16 tokens x BW / 8)
+  static_assert(CL == 2 || CL == 4, "256- or 512-column batches");
+  __shared__ __attribute__((aligned(16))) uint16_t xl[2][16 * XLD];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, q = l >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * RB;
+  const int64_t vstride = C / 4, mstride = C / 32;  // stored values / metadata words per row
+  const int nb = (int)((C + BW - 1) / BW);          // batches
+  const int c32 = (int)C;
+  const int64_t nrows = min((int64_t)RB, R - row0);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vals + row0 * vstride), (short)0, (int)(nrows * vstride * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t mres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(meta + row0 * mstride), (short)0, (int)(nrows * mstride * 4), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)act, (short)0, (int)(T * C * 2), kRsrcWord3);
+
+  auto load = [&](int b, BT& B) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) u[e] = c == 0 ? pf_u[0][e] : pf_u[1][e];
-        } else {
-          x.v = load_e(rt + l16, jb);
-          load_u(jb, u);
-        }
-        union UH { uint16_t h[8]; bf16x8 b; } uhi, ulo;
+    for (int f = 0; f < FW; ++f) {
+      const int row = 16 * (w + NW * f) + l16;  // rows past nrows read zero (past the resource)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) split_bf16(u[e], uhi.h[e], ulo.h[e]);
-        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, uhi.b, y, 0, 0, 0);
-        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.b, ulo.b, y, 0, 0, 0);
+      for (int c = 0; c < CL; ++c) {  // groups 4c .. 4c+3 of the lane: columns BW b + (BW/4) q + 32 c ..
+        const bool in = BW * b + (BW / 4) * q + 32 * c < c32;
+        const uint32_t off = (uint32_t)((row * vstride + (BW / 4) * b + (BW / 16) * q + 8 * c) * 2);
+        B.v[f][c] = __builtin_amdgcn_raw_buffer_load_b128(vres, oob_unless(in, off), 0, 0);
+      }
+      // words past the row's end pair with zero values; past the resource they read zero
+      const uint32_t moff = (uint32_t)((row * mstride + (BW / 32) * b + CL * q) * 4);
+      if constexpr (CL == 2) {
+        const u32x2 m = __builtin_amdgcn_raw_buffer_load_b64(mres, moff, 0, 0);
+        B.m[f][0] = m[0];
+        B.m[f][1] = m[1];
+      } else {
+        const u32x4 m = __builtin_amdgcn_raw_buffer_load_b128(mres, moff, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) B.m[f][c] = m[c];
       }
     }
-
-    // ---- store rows rt + 4q .. +3 of token l16
-    if (!tok_ok) continue;
-    const int64_t n = rt + 4 * q;
-    uint16_t* o = out + (int64_t)l16 * R + n;
-    if ((R & 3) == 0 && n + 4 <= R) {
-      u32x2 v;
-      v[0] = pack_bf16x2(y[0], y[1]);
-      v[1] = pack_bf16x2(y[2], y[3]);
-      *reinterpret_cast<u32x2*>(o) = v;
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < R) o[e] = f32_to_bf16(y[e]);
+    for (int k = 0; k < XC; ++k) {  // chunk v: token v / (BW/8), columns 8 (v % (BW/8)) .. +7 of the batch
+      const int v = tid + NT * k, tok = v / (BW / 8), col = BW * b + 8 * (v % (BW / 8));
+      const bool in = v < XCH && tok < T && col < c32;
+      B.x[k] = __builtin_amdgcn_raw_buffer_load_b128(xres, oob_unless(in, (uint32_t)((tok * C + col) * 2)), 0, 0);
     }
+  };
+  auto stage = [&](int buf, const BT& B) {
+#pragma unroll
+    for (int k = 0; k < XC; ++k) {
+      const int v = tid + NT * k, tok = v / (BW / 8), c = 8 * (v % (BW / 8));
+      if (v < XCH) *reinterpret_cast<u32x4*>(&xl[buf][tok * XLD + d28_col(c)]) = B.x[k];
+    }
+  };
+
+  f32x4 acc[FW];
+#pragma unroll
+  for (int f = 0; f < FW; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // group g of the lane (pair s, metadata word mw, byte g % 4) as two 2:4 groups: values of the
+  // low and the high half, and the 4-bit index field both halves share
+  auto as24 = [](uint32_t s, uint32_t mw, int g, uint32_t& lo, uint32_t& hi) {
+    const int sh = 8 * (g & 3);
+    // all ones over the first / second value's 16 bits when its position is 4-7
+    const uint32_t hmask = (((uint32_t)((int32_t)(mw << (29 - sh)) >> 31)) & 0xFFFFu) |
+                           (((uint32_t)((int32_t)(mw << (26 - sh)) >> 31)) & 0xFFFF0000u);
+    lo = s & ~hmask;
+    hi = s & hmask;
+    return ((mw >> sh) & 3u) | (((mw >> (sh + 3)) & 3u) << 2);
+  };
+  auto compute = [&](int buf, const BT& B) {
+#pragma unroll
+    for (int j = 0; j < 2 * CL; ++j) {
+      union { u32x4 v[2]; bf16x16 b; } xb;
+      const int ga = 8 * (q >> 1) + 2 * j + (q & 1);
+      xb.v[0] = *reinterpret_cast<const u32x4*>(&xl[buf][l16 * XLD + d28_col(8 * ga)]);
+      xb.v[1] = *reinterpret_cast<const u32x4*>(&xl[buf][l16 * XLD + d28_col(8 * (ga + 16))]);
+#pragma unroll
+      for (int f = 0; f < FW; ++f) {
+        union { uint32_t u[4]; bf16x8 b; } af;
+        const int g0 = 2 * j, g1 = 2 * j + 1;
+        const uint32_t n0 = as24(B.v[f][g0 >> 2][g0 & 3], B.m[f][g0 >> 2], g0, af.u[0], af.u[1]);
+        const uint32_t n1 = as24(B.v[f][g1 >> 2][g1 & 3], B.m[f][g1 >> 2], g1, af.u[2], af.u[3]);
+        const uint32_t idx = (n0 | (n1 << 8)) * 0x11u;
+        acc[f] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af.b, xb.b, acc[f], (int)idx, 0, 0);
+      }
+    }
+  };
+
+  DecodeTail<FR, NW, FW == 1 ? 0 : 2> tail(ep, R, T, row0, w, l);
+
+  // ping-pong over register batches, as in the 2:4 kernel
+  BT b0, b1;
+  load(0, b0);
+  for (int b = 0; b < nb; b += 2) {
+    load(b + 1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(0, b0);
+    __syncthreads();
+    compute(0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b + 2, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(1, b1);
+    __syncthreads();
+    compute(1, b1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int f = 0; f < FW; ++f) tail.finish_tile(acc[f], w + NW * f, out);
 }
 
 // Canonical 2:4 arrays -> streaming layout (see the header comment).  One thread per 16-byte
@@ -379,6 +550,42 @@ hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, 
     else SRA_DECODE_LAUNCH(9, 8, 1, false);
   }
 #undef SRA_DECODE_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_decode28_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
+                                int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
+                                uint16_t* out, hipStream_t s) {
+  if (T <= 0 || R <= 0) return hipSuccess;
+  if (T > 16 || (C & 31) != 0) return hipErrorInvalidValue;
+  // Workgroup shapes (waves x row tiles per wave): 9 x 1 (144 rows), 4 x 2 (128), 4 x 1 (64) and
+  // 3 x 1 (48).  As in the 2:4 kernel, the shape whose busiest CU streams the fewest rows wins,
+  // ties going to the larger workgroup (fewer Act re-reads per weight byte).
+  static constexpr int kShapes[4][2] = {{9, 1}, {4, 2}, {4, 1}, {3, 1}};
+  int pick = 0;
+  int64_t best = -1;
+  for (int c = 0; c < 4; ++c) {
+    const int rows = 16 * kShapes[c][0] * kShapes[c][1];
+    const int64_t nwg = (R + rows - 1) / rows, per_cu = (nwg + 255) / 256 * rows;
+    if (best < 0 || per_cu < best) best = per_cu, pick = c;
+  }
+  if (tuning().decode_rows == 9) pick = 0;  // forced: 9 tiles (144 rows), 4, or 3
+  else if (tuning().decode_rows == 4) pick = 2;
+  else if (tuning().decode_rows == 3) pick = 3;
+  const int rows = 16 * kShapes[pick][0] * kShapes[pick][1];
+  const unsigned grid = (unsigned)((R + rows - 1) / rows);
+#define SRA_D28(NWV, FWV, BWV, OCCV)                                                                  \
+  launch(SRA_KERNEL_DECODE24, k_decode28<NWV, FWV, BWV, OCCV>, dim3(grid), dim3(64 * NWV), 0, s, s_vals, \
+         s_meta, R, C, act, T, ep, out)
+  // (512-column batches, twice the bytes in flight per wave, measured no faster at the OPT-66B
+  // FFN shape: 44.4 / 50.2 us against 44.1 / 49.6 us at T = 1 / 16)
+  switch (pick) {
+    case 0: SRA_D28(9, 1, 256, 1); break;
+    case 1: SRA_D28(4, 2, 256, 3); break;
+    case 2: SRA_D28(4, 1, 256, 3); break;
+    default: SRA_D28(3, 1, 256, 4); break;
+  }
+#undef SRA_D28
   return hipGetLastError();
 }
 

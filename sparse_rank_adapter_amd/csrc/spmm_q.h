@@ -221,50 +221,6 @@ struct AdapterRows {
 };
 
 // ---------------------------------------------------------------------------------------------
-// N:M fragments expanded to dense bf16 (zeros at the pruned positions) for dense MFMA.  A group's
-// kept values sit in one 32-bit word as (first, second) bf16, at ascending in-group positions
-// f_a < f_b.  Per group a code byte per position marks which value goes there (2: the first, 4:
-// the second, 0: none); each dense output word (positions 2k, 2k + 1) then takes three byte
-// permutes: the code bytes spread to [c, c + 1, c', c' + 1], those index a table of byte selects
-// (0x0C gives a zero byte), and the selects gather the value bytes.
-
-// one dense word from the code bytes x (spread: the permute that picks its two code bytes twice),
-// the select table {thi, tlo} and the value words {hi, lo}
-SRA_DEV uint32_t dense_word(uint32_t x, uint32_t spread, uint32_t tlo, uint32_t thi, uint32_t hi, uint32_t lo) {
-  const uint32_t idx = __builtin_amdgcn_perm(x, x, spread) | 0x01000100u;
-  return __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(thi, tlo, idx));
-}
-
-// 2:4: values (v0, v1) of group 0 in s01 and (v2, v3) of group 1 in s23, positions in m (2 bits
-// each, least significant first: v0, v1, v2, v3) -> the groups' 8 dense columns
-SRA_DEV bf16x8 expand24(uint32_t s01, uint32_t s23, uint32_t m) {
-  const uint32_t x0 = (2u << ((m & 3u) << 3)) | (4u << (((m >> 2) & 3u) << 3));
-  const uint32_t x1 = (2u << (((m >> 4) & 3u) << 3)) | (4u << (((m >> 6) & 3u) << 3));
-  union { u32x4 v; bf16x8 b; } d;
-  // group 0's values are bytes 0-3 of {s23, s01}, group 1's bytes 4-7
-  d.v[0] = dense_word(x0, 0x01010000u, 0x01000C0Cu, 0x00000302u, s23, s01);
-  d.v[1] = dense_word(x0, 0x03030202u, 0x01000C0Cu, 0x00000302u, s23, s01);
-  d.v[2] = dense_word(x1, 0x01010000u, 0x05040C0Cu, 0x00000706u, s23, s01);
-  d.v[3] = dense_word(x1, 0x03030202u, 0x05040C0Cu, 0x00000706u, s23, s01);
-  return d.b;
-}
-
-// 2:8: the group's two values in s, positions in m (3 bits each: first at bits 0-2, second at 3-5)
-// -> its 8 dense columns
-SRA_DEV bf16x8 expand28(uint32_t s, uint32_t m) {
-  const uint32_t fa = m & 7u, fb = (m >> 3) & 7u;
-  const uint32_t ca = 2u << ((fa & 3u) << 3), cb = 4u << ((fb & 3u) << 3);
-  const uint32_t xl = (fa < 4u ? ca : 0u) | (fb < 4u ? cb : 0u);    // positions 0-3
-  const uint32_t xh = (fa >= 4u ? ca : 0u) | (fb >= 4u ? cb : 0u);  // positions 4-7
-  union { u32x4 v; bf16x8 b; } d;
-  d.v[0] = dense_word(xl, 0x01010000u, 0x01000C0Cu, 0x00000302u, 0u, s);
-  d.v[1] = dense_word(xl, 0x03030202u, 0x01000C0Cu, 0x00000302u, 0u, s);
-  d.v[2] = dense_word(xh, 0x01010000u, 0x01000C0Cu, 0x00000302u, 0u, s);
-  d.v[3] = dense_word(xh, 0x03030202u, 0x01000C0Cu, 0x00000302u, 0u, s);
-  return d.b;
-}
-
-// ---------------------------------------------------------------------------------------------
 // Pipelined variant on v_smfmac_f32_16x16x64_bf16, which moves stored (non-zero) work ~20% faster
 // on gfx950 than the 32x32x32 form.  Same LDS ring, DMA transfers and swizzles as above; per
 // 64-column stage one SMFMAC per (16 weight rows, 16 tokens) pair.  Lane l of an A fragment holds

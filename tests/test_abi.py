@@ -293,8 +293,9 @@ def test_bwd_validation(lib):
 
 def test_nm28_validation(lib):
     """2:8: bf16 only, 32-column multiples, no pair or streaming forms; products above 16 tokens run
-    on the 2:4 kernels (the weight rewritten as 2:4 in the workspace, K % 32), the expanded-fragment
-    path (16 tokens or fewer, or the dense-MFMA engine) needs K % 128."""
+    on the 2:4 kernels (the weight rewritten as 2:4 in the workspace, K % 32), at 16 tokens or fewer
+    on the 2:8 decode kernel (K % 32, no workspace), and the expanded-fragment path (the dense-MFMA
+    engine above 16 tokens) needs K % 128."""
     d = SraSparse()
     d.values, d.meta = FAKE, FAKE
     assert lib.sra_compress(FAKE, SRA_F32, 64, 64, 2, 8, ctypes.byref(d), None) == SRA_ERR_UNSUPPORTED
@@ -308,11 +309,13 @@ def test_nm28_validation(lib):
     n = ctypes.c_size_t()
     assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_OK
     assert n.value >= 256 * 96 * 2 + 256 * 6 * 4  # the 2:4 values and metadata
-    assert lib.sra_fwd_workspace(ctypes.byref(W), 16, 8, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
-    assert "128" in err(lib)
+    assert lib.sra_fwd_workspace(ctypes.byref(W), 16, 0, ctypes.byref(n)) == SRA_OK
+    assert n.value == 0  # the decode kernel needs no workspace
     assert lib.sra_set_tuning(4, 1) == SRA_OK  # the dense-MFMA engine
     try:
         assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+        assert "128" in err(lib)
+        assert lib.sra_fwd_workspace(ctypes.byref(W), 16, 8, ctypes.byref(n)) == SRA_OK
     finally:
         assert lib.sra_set_tuning(0, 0) == SRA_OK
     W = nm_desc(rows=256, cols=256, n=2, m=8)

@@ -1,7 +1,9 @@
 """2:8 weights and the dense-MFMA engine for 2:4 weights, against the oracle (GPU, through the C ABI).
 
 2:8: compress and double prune must match the oracle bit for bit (values and 3-bit metadata);
-the layer's forward and double-pruned backward run on dense MFMA with expanded fragments.  2:4 on
+the layer's forward and double-pruned backward run rewritten as 2:4 on the SMFMAC kernels above 16
+tokens, on the 2:8 decode kernel (fragments expanded to dense in registers) at 16 tokens or fewer,
+and on dense MFMA with expanded fragments on the dense engine.  2:4 on
 SRA_ENGINE_DENSE_MFMA: the same products as the SMFMAC path through the same pipeline, held to the
 same tolerance.  Floats: max |gpu - oracle| / (|oracle| + 1e-3) <= 2e-2 (bf16).
 """
@@ -103,12 +105,54 @@ def test_layer_2_8(gpu, T, K, N, r, engine):
         run_layer(Workload("nm28", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + K)
 
 
-# shapes only the 2:4 route takes (K or N a multiple of 32, not of 128), and 16 tokens (the
-# expanded-fragment path at any engine)
-@pytest.mark.parametrize("T,K,N,r", [(100, 96, 160, 8), (257, 224, 96, 24), (40, 64, 32, 0),
-                                     (16, 256, 384, 16)])
+# shapes only the 2:4 route takes (K or N a multiple of 32, not of 128)
+@pytest.mark.parametrize("T,K,N,r", [(100, 96, 160, 8), (257, 224, 96, 24), (40, 64, 32, 0)])
 def test_layer_2_8_as_2_4_shapes(gpu, T, K, N, r):
     run_layer(Workload("nm28s", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + N)
+
+
+# The 2:8 decode kernel (T <= 16, forward and dX): K and N multiples of 32 but not of 128 or of
+# the 512-column batch, row counts that leave the last workgroup's row tiles partly or wholly
+# empty, one to sixteen tokens, ranks 0 to 136 (the epilogue's 32-column rounds, a partial last one)
+DECODE_SHAPES = [(1, 96, 160, 8), (3, 608, 352, 0), (16, 1056, 224, 64), (7, 224, 992, 100),
+                 (16, 5120, 2080, 16), (12, 160, 96, 136), (16, 256, 384, 16), (5, 512, 256, 8)]
+
+
+@pytest.mark.parametrize("T,K,N,r", DECODE_SHAPES)
+def test_layer_2_8_decode(gpu, T, K, N, r):
+    run_layer(Workload("nm28d", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + K + N)
+
+
+@pytest.mark.parametrize("rows", [3, 4, 9])
+def test_layer_2_8_decode_row_tiles(gpu, rows):
+    """Each workgroup shape of the 2:8 decode kernel (48, 64 or 144 weight rows), forced; the
+    planner picks 48 for small layers and 144 at the OPT-66B FFN shape."""
+    with sra.tuned(decode_rows=rows):
+        run_layer(Workload("nm28dr", T=16, K=1568, N=1184, r=40, dtype="bf16", fmt="nm"), 2, 8, seed=rows)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_opt66b_decode_2_8_sampled(gpu, T):
+    """The OPT-66B FFN weight (36864 x 9216) at 2:8, forward at decode token counts, on 514 sampled
+    output columns (2:8 selection is local to each weight row, so the oracle compresses only those
+    rows)."""
+    wl = WORKLOADS["opt66b_ffn_decode"]
+    inp = layer_inputs(wl, seed=0, T=T, with_dy=False)
+    X, A, B = (inp[k].cuda() for k in ("X", "A", "B"))
+    print(f"2:8 OPT-66B decode T={T}", flush=True)
+    S = sra.compress(inp["W"].cuda(), 2, 8)
+    Y, U = sra.sparse_lora_fwd(S, X, A, B)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(T)
+    cols_n = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 512, replace=False)]))
+    W_n = f64(inp["W"][torch.from_numpy(cols_n)])
+    _, _, mask1 = onm.compress(W_n, 2, 8)
+    X64, A64, B64 = (f64(inp[k]) for k in ("X", "A", "B"))
+    Yo, Uo = olayer.forward(X64, np.where(mask1, W_n, 0.0), A64, B64[cols_n])
+    rep = Report(torch.bfloat16)
+    rep.add("Y", f64(Y[:, torch.from_numpy(cols_n).cuda()]), Yo)
+    rep.add("U", U.cpu().numpy(), Uo)
+    rep.check()
 
 
 def test_layer_2_8_opt350m_fc1(gpu):
@@ -159,16 +203,17 @@ def test_2_8_rejections(gpu):
         sra.compress(W.float(), 2, 8)
     assert e.value.status == SRA_ERR_UNSUPPORTED
     S = sra.compress(W, 2, 8)
-    # Up to 16 tokens the expansion product needs K % 128 == 0; above that the
-    # weight runs as 2:4, which takes this K.
-    X = torch.zeros(16, 64, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(SraError) as e:
-        sra.sparse_lora_fwd(S, X)
-    assert e.value.status == SRA_ERR_UNSUPPORTED
+    # Above 16 tokens the expanded-fragment product (dense engine) needs K % 128 == 0; the
+    # default route (the weight as 2:4) and the decode kernel (16 tokens or fewer) take this K.
     X = torch.ones(300, 64, dtype=torch.bfloat16, device="cuda")
-    Y, _ = sra.sparse_lora_fwd(S, X)
-    torch.cuda.synchronize()
-    assert Y.shape == (300, 64) and not Y.float().abs().any()
+    with sra.tuned(engine="dense_mfma"):
+        with pytest.raises(SraError) as e:
+            sra.sparse_lora_fwd(S, X)
+    assert e.value.status == SRA_ERR_UNSUPPORTED
+    for T in (300, 16):
+        Y, _ = sra.sparse_lora_fwd(S, X[:T])
+        torch.cuda.synchronize()
+        assert Y.shape == (T, 64) and not Y.float().abs().any()
     with pytest.raises(SraError):
         sra.nm_tile(S)
     with pytest.raises(SraError):
