@@ -60,7 +60,7 @@ typedef enum {
   SRA_FMT_ELL = 1, /* fixed fan-in: values [rows, k], index int16 [rows, k], columns ascending */
   SRA_FMT_CSR = 2, /* transpose of an ELL matrix: row_ptr int32 [rows+1], index int16 [nnz],
                       values [nnz], column ids ascending inside each row */
-  SRA_FMT_NM_TILED = 3, /* 2:4 bf16 in the streaming layout of sra_nm_tile */
+  SRA_FMT_NM_TILED = 3, /* 2:4 or 2:8 bf16 in the streaming layout of sra_nm_tile */
   SRA_FMT_FFI_TILED = 4 /* fixed fan-in bf16 in the tiled entry lists of sra_ffi_tile */
 } sra_format;
 
@@ -112,8 +112,9 @@ int64_t sra_nm_meta_words(int64_t cols, int32_t n, int32_t m);
  * ascending column order, and per 8-column group one metadata byte holding the two in-group
  * positions (bits 0-2 and 3-5, the rest zero), four group bytes per uint32 word, so cols/32
  * words per row.  The products rewrite a 2:8 weight as a 2:4 one in their workspace above 16
- * tokens (see SRA_TUNE_ENGINE); 2:8 has no pair kernel, streaming layout or masked gradient.  The streaming layout (sra_nm_tile, sra_compress_pair_tiled) is
- * 2:4 only.  The caller sets out->values and out->meta; the call
+ * tokens (see SRA_TUNE_ENGINE) and stream it through their decode kernel at 16 tokens or fewer;
+ * 2:8 has no pair kernel or masked gradient.  sra_nm_tile takes 2:4 and 2:8 (each its own
+ * streaming layout); sra_compress_pair_tiled is 2:4 only.  The caller sets out->values and out->meta; the call
  * fills the remaining descriptor fields (format, dtype, rows, cols, n, m).
  */
 sra_status sra_compress(const void* W, int32_t dtype, int64_t rows, int64_t cols, int32_t n,
@@ -144,7 +145,7 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
                              void* stream);
 
 /*
- * nm_tile -- the same 2:4 weight in a streaming layout for memory-bound forwards of few tokens
+ * nm_tile -- the same 2:4 or 2:8 weight in a streaming layout for memory-bound forwards of few tokens
  * (SLoPe §3 inference results: with few tokens the layer is bound by reading the compressed
  * weight once; the compressed form is prepared once and reused, SLoPe §2.3).  The content is that
  * of the canonical arrays, permuted so that the decode kernel reads every block contiguously:
@@ -154,13 +155,20 @@ sra_status sra_compress_pair(const void* W, int32_t dtype, int64_t rows, int64_t
  *   meta:   for row tile t and batch b (512 columns = 16 words), a 1 KB block at byte
  *           (t * ceil(cols/512) + b) * 1024; bytes 64 i .. 64 i + 63 hold words 16 b .. 16 b + 15
  *           of row 16 t + i.
+ * 2:8 (blocks shaped for the 2:8 decode kernel, whose wave owns whole row tiles): for row tile t
+ * and batch b (256 columns = 64 stored values and 8 metadata words per row), a 2 KB value block at
+ * byte (t * ceil(cols/256) + b) * 2048 whose 16-byte chunk 64 c + l (c = 0, 1; l = 16 q + i) holds
+ * stored values 64 b + 16 q + 8 c .. +7 of row 16 t + i, and a 512-byte metadata block at byte
+ * (t * ceil(cols/256) + b) * 512 whose bytes 8 l .. 8 l + 7 hold words 8 b + 2 q and 8 b + 2 q + 1
+ * of that row.
  * Entries past the last row or column are zero.  Sizes: sra_nm_tile_bytes.
- * Ws: canonical SRA_FMT_NM, bf16, 2:4.  out: the caller sets values and meta (16-byte aligned,
+ * Ws: canonical SRA_FMT_NM, bf16, 2:4 or 2:8.  out: the caller sets values and meta (16-byte aligned,
  * value_bytes and meta_bytes long); the call fills the other fields (format SRA_FMT_NM_TILED, same
  * dtype, rows, cols, n, m).  An SRA_FMT_NM_TILED weight is accepted by sra_sparse_lora_fwd (as
  * Ws) and sra_sparse_lora_bwd (as P) for T <= 16, and for any T when cols % 128 == 0 (else
  * SRA_ERR_UNSUPPORTED); the results equal the canonical arrays' bit for bit when neither path
- * splits the reduction.
+ * splits the reduction.  A 2:8 one is accepted for any T: above 16 tokens the call rewrites it as
+ * canonical 2:4 in its workspace, as for canonical 2:8 arrays.
  */
 sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m,
                              size_t* value_bytes /* host */, size_t* meta_bytes /* host */);

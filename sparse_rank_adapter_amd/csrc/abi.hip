@@ -79,18 +79,24 @@ sra_status check_nm(int64_t rows, int64_t cols, int n, int m) {
 constexpr uint32_t kMeta12To24 = 0x88888888u;
 bool is12(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 1 && S->m == 2; }
 bool is28(const sra_sparse* S) { return S->format == SRA_FMT_NM && S->n == 2 && S->m == 8; }
+// a 2:8 weight in its streaming layout (sra_nm_tile)
+bool is28t(const sra_sparse* S) { return S->format == SRA_FMT_NM_TILED && S->n == 2 && S->m == 8; }
 // 2:8 weights for 16 tokens or fewer run the 2:8 decode kernel (one streaming pass over the
 // weight, fragments expanded to dense in registers).  Otherwise bf16 N:M weights on the dense-MFMA
 // engine run the expanded-fragment products, and 2:8 weights run on the 2:4 kernels: every group
 // of four columns of a 2:8 row holds at most two kept entries, so the call rewrites the weight as
 // a 2:4 one (the same entries plus +0.0 fillers) in its workspace first.  With few tokens a
 // product reads the weight once, and that rewrite would cost more than it saves.
-bool use_dec28(const sra_sparse* S, int64_t T) { return is28(S) && T <= 16; }
+bool use_dec28(const sra_sparse* S, int64_t T) { return (is28(S) || is28t(S)) && T <= 16; }
 bool use_xp(const sra_sparse* S, int64_t T) {
   if (S->format != SRA_FMT_NM && S->format != SRA_FMT_NM_TILED) return false;
   return S->dtype == SRA_BF16 && sra::tuning().engine == SRA_ENGINE_DENSE_MFMA && !use_dec28(S, T);
 }
-bool is28_on24(const sra_sparse* S, int64_t T) { return is28(S) && !use_dec28(S, T) && !use_xp(S, T); }
+// (a 2:8 weight in the streaming layout is rewritten as canonical 2:4 above 16 tokens on either
+// engine: the dense engine then runs the expanded-fragment product on that 2:4 form)
+bool is28_on24(const sra_sparse* S, int64_t T) {
+  return (is28(S) && !use_dec28(S, T) && !use_xp(S, T)) || (is28t(S) && T > 16);
+}
 size_t meta_bytes(const sra_sparse* S) {
   return (size_t)S->rows * (size_t)sra_nm_meta_words(S->cols, S->n, S->m) * 4;
 }
@@ -107,8 +113,9 @@ sra_status check_sparse(const sra_sparse* S, const char* name) {
     SRA_TRY(check_ptr(S->meta, any, "meta"));
   } else if (S->format == SRA_FMT_NM_TILED) {
     SRA_TRY(check_nm(S->rows, S->cols, S->n, S->m));
-    if (S->n != 2 || S->m != 4) return fail(SRA_ERR_UNSUPPORTED, "%s: the streaming layout is 2:4 only", name);
-    if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "%s: the streaming 2:4 layout is bf16 only", name);
+    if (S->n != 2 || (S->m != 4 && S->m != 8))
+      return fail(SRA_ERR_UNSUPPORTED, "%s: the streaming layout is 2:4 or 2:8 only", name);
+    if (S->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "%s: the streaming layout is bf16 only", name);
     SRA_TRY(check_ptr(S->values, any, "values"));
     SRA_TRY(check_ptr(S->meta, any, "meta"));
   } else if (S->format == SRA_FMT_ELL) {
@@ -172,7 +179,7 @@ sra_status validate_fwd(const sra_sparse* Ws, int64_t T, int32_t r) {
     return fail(SRA_ERR_UNSUPPORTED, "the tiled fixed fan-in product needs K %% 64 == 0 and K > 0 (K = %lld)",
                 (long long)Ws->cols);
   if (T < 0) return fail(SRA_ERR_INVALID_ARG, "T < 0");
-  if (Ws->format == SRA_FMT_NM_TILED && !sra::spmm24_tiled_ok(Ws->cols, T))
+  if (Ws->format == SRA_FMT_NM_TILED && !is28t(Ws) && !sra::spmm24_tiled_ok(Ws->cols, T))
     return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout needs K %% 128 == 0 above 16 tokens (T = %lld)", (long long)T);
   if (Ws->format == SRA_FMT_NM_TILED && Ws->cols == 0)
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 forward needs K > 0");
@@ -226,7 +233,7 @@ sra_status validate_bwd(const sra_sparse* P, int64_t T, int32_t r, uint32_t flag
   SRA_TRY(check_sparse(P, "P"));
   if (P->format == SRA_FMT_ELL)
     return fail(SRA_ERR_INVALID_ARG, "backward takes the double-pruned N:M weight, the CSR transpose or its tiled form");
-  if (P->format == SRA_FMT_NM_TILED && (flags & SRA_GRAD_DX) && !sra::spmm24_tiled_ok(P->cols, T))
+  if (P->format == SRA_FMT_NM_TILED && !is28t(P) && (flags & SRA_GRAD_DX) && !sra::spmm24_tiled_ok(P->cols, T))
     return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout needs N %% 128 == 0 above 16 tokens (T = %lld)", (long long)T);
   if (P->format == SRA_FMT_NM_TILED && P->cols == 0 && (flags & SRA_GRAD_DX))
     return fail(SRA_ERR_UNSUPPORTED, "bf16 2:4 backward needs N > 0");
@@ -572,17 +579,20 @@ sra_status sra_nm_axpby(const void* a_values, float beta, const void* b_values, 
 sra_status sra_nm_tile_bytes(int64_t rows, int64_t cols, int32_t n, int32_t m, size_t* value_bytes,
                              size_t* meta_bytes) {
   SRA_TRY(check_nm(rows, cols, n, m));
-  if (n != 2 || m != 4) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 only");
+  if (n != 2 || (m != 4 && m != 8)) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 or 2:8 only");
   if (!value_bytes || !meta_bytes) return fail(SRA_ERR_INVALID_ARG, "size pointers are NULL");
-  sra::nm_tile_bytes(rows, cols, value_bytes, meta_bytes);
+  if (m == 8)
+    sra::nm28_tile_bytes(rows, cols, value_bytes, meta_bytes);
+  else
+    sra::nm_tile_bytes(rows, cols, value_bytes, meta_bytes);
   return SRA_OK;
 }
 
 sra_status sra_nm_tile(const sra_sparse* Ws, sra_sparse* out, void* stream) {
   SRA_TRY(check_sparse(Ws, "Ws"));
   if (Ws->format != SRA_FMT_NM) return fail(SRA_ERR_INVALID_ARG, "nm_tile needs a canonical N:M weight");
-  if (Ws->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "the streaming 2:4 layout is bf16 only");
-  if (is12(Ws) || is28(Ws)) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 only");
+  if (Ws->dtype != SRA_BF16) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is bf16 only");
+  if (is12(Ws)) return fail(SRA_ERR_UNSUPPORTED, "the streaming layout is 2:4 or 2:8 only");
   if (!out) return fail(SRA_ERR_INVALID_ARG, "out descriptor is NULL");
   const bool any = Ws->rows > 0 && Ws->cols > 0;
   SRA_TRY(check_ptr(out->values, any, "out values"));
@@ -594,6 +604,9 @@ sra_status sra_nm_tile(const sra_sparse* Ws, sra_sparse* out, void* stream) {
   out->n = Ws->n;
   out->m = Ws->m;
   const hipStream_t s = (hipStream_t)stream;
+  if (is28(Ws))
+    return hip_done(sra::launch_nm_tile28_bf16((const uint16_t*)Ws->values, Ws->meta, Ws->rows, Ws->cols,
+                                               out->values, out->meta, s), s, "nm_tile 2:8");
   return hip_done(sra::launch_nm_tile_bf16((const uint16_t*)Ws->values, Ws->meta, Ws->rows, Ws->cols,
                                            out->values, out->meta, s), s, "nm_tile");
 }
@@ -720,12 +733,13 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
     Ws = &w24;
   } else if (is28_on24(Ws, T)) {  // run on the 2:4 kernels with the weight rewritten as 2:4
     w24 = *Ws;
+    w24.format = SRA_FMT_NM;
     w24.values = wsb + plan.v24_off;
     w24.meta = (uint32_t*)(wsb + plan.meta_off);
     w24.n = 2;
     w24.m = 4;
     SRA_TRY(hip_done(sra::launch_nm28_to24((const uint16_t*)Ws->values, Ws->meta, Ws->rows, Ws->cols,
-                                           (uint16_t*)w24.values, w24.meta, s),
+                                           (uint16_t*)w24.values, w24.meta, s, is28t(Ws)),
                      s, "fwd 2:8 as 2:4"));
     Ws = &w24;
   }
@@ -760,7 +774,7 @@ sra_status sra_sparse_lora_fwd(const sra_sparse* Ws, const void* X, int64_t T, c
   }
   if (use_dec28(Ws, T))
     return hip_done(sra::launch_decode28_bf16((const uint16_t*)Ws->values, Ws->meta, N, K,
-                                              (const uint16_t*)X, T, ep, (uint16_t*)Y, s),
+                                              (const uint16_t*)X, T, ep, (uint16_t*)Y, s, is28t(Ws)),
                     s, "fwd spmm 2:8 (decode)");
   if (xp)
     return hip_done(sra::launch_spmm_xp_bf16(is28(Ws) ? 28 : 24, Ws->format == SRA_FMT_NM_TILED,
@@ -828,12 +842,13 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     P = &p24;
   } else if (is28_on24(P, T) && fdx) {  // dX on the 2:4 kernels with P rewritten as 2:4
     p24 = *P;
+    p24.format = SRA_FMT_NM;
     p24.values = wsb + plan.v24_off;
     p24.meta = (uint32_t*)(wsb + plan.meta_off);
     p24.n = 2;
     p24.m = 4;
     SRA_TRY(hip_done(sra::launch_nm28_to24((const uint16_t*)P->values, P->meta, P->rows, P->cols,
-                                           (uint16_t*)p24.values, p24.meta, s),
+                                           (uint16_t*)p24.values, p24.meta, s, is28t(P)),
                      s, "bwd 2:8 as 2:4"));
     P = &p24;
   }
@@ -896,7 +911,7 @@ sra_status sra_sparse_lora_bwd(const sra_sparse* P, const void* dY, const void* 
     }
     if (use_dec28(P, T))
       SRA_TRY(hip_done(sra::launch_decode28_bf16((const uint16_t*)P->values, P->meta, K, N,
-                                                 (const uint16_t*)dY, T, ep, (uint16_t*)dX, s),
+                                                 (const uint16_t*)dY, T, ep, (uint16_t*)dX, s, is28t(P)),
                        s, "bwd dX 2:8 (decode)"));
     else if (xp)
       SRA_TRY(hip_done(sra::launch_spmm_xp_bf16(is28(P) ? 28 : 24, P->format == SRA_FMT_NM_TILED,

@@ -176,7 +176,7 @@ hipError_t launch_meta_or(const uint32_t* in, uint32_t* out, int64_t n, uint32_t
 // group) rewritten as 2:4 canonical arrays (values [rows][cols/2], 2-bit fields) holding the same
 // entries plus +0.0 fillers, for the 2:4 products (cols % 32 == 0)
 hipError_t launch_nm28_to24(const uint16_t* v8, const uint32_t* m8, int64_t rows, int64_t cols,
-                            uint16_t* v4, uint32_t* m4, hipStream_t s);
+                            uint16_t* v4, uint32_t* m4, hipStream_t s, bool tiled = false);
 hipError_t launch_compress28(const uint16_t* W, int64_t rows, int64_t cols, uint16_t* vals, uint32_t* meta,
                              hipStream_t s);
 hipError_t launch_double_prune28(const uint16_t* vals, const uint32_t* meta, int64_t rows, int64_t cols,
@@ -260,7 +260,11 @@ size_t spmm24_decode_ws(int64_t R, int64_t C, int64_t T);
 // 2:8 canonical arrays, T <= 16 (C % 32 == 0); no workspace
 hipError_t launch_decode28_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
                                 const uint16_t* act, int64_t T, const Epilogue& ep, uint16_t* out,
-                                hipStream_t s);
+                                hipStream_t s, bool tiled);
+// 2:8 canonical arrays -> the 2:8 streaming layout (value and metadata blocks of 16 rows x 256 columns)
+void nm28_tile_bytes(int64_t R, int64_t C, size_t* value_bytes, size_t* meta_bytes);
+hipError_t launch_nm_tile28_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+                                 void* t_vals, void* t_meta, hipStream_t s);
 hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
                                 uint16_t* out, hipStream_t s, bool tiled = false);

@@ -656,15 +656,29 @@ __global__ __launch_bounds__(256) void k_double_prune28(const uint16_t* __restri
 // Rows are whole metadata words, so metadata word i covers 2:8 values [8i, 8i + 8) and 2:4
 // values [16i, 16i + 16) of the flat arrays: one lane per word, no row arithmetic. The 2:8 arrays
 // are read once per call and not again by the product, so their loads bypass the caches.
+// TL: the 2:8 weight is in its streaming layout (16-row x 256-column blocks: 2 KB of values, lane
+// l = 16 q + i holding row i's chunk c at 1024 c + 16 l, and 512 bytes of metadata, lane l's two
+// words at 8 l), where word w of row r is chunk / word w % 2 of lane 16 ((w % 8) / 2) + r % 16 in
+// block (r / 16, w / 8); the 2:4 output is canonical either way.
+template <bool TL>
 __global__ __launch_bounds__(256) void k_nm28_to24(const uint16_t* __restrict__ v8,
                                                    const uint32_t* __restrict__ m8, int64_t words,
+                                                   int64_t words_per_row,
                                                    uint16_t* __restrict__ v4,
                                                    uint32_t* __restrict__ m4) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= words) return;
+  int64_t vi = id, mi = id;  // 16-byte value chunk and metadata word of this lane's input
+  if constexpr (TL) {
+    const int64_t row = id / words_per_row, w = id - row * words_per_row, nb = (words_per_row + 7) / 8;
+    const int64_t blk = (row / 16) * nb + w / 8;
+    const int l = (int)(16 * ((w & 7) >> 1) + (row & 15)), c = (int)(w & 1);
+    vi = blk * 128 + 64 * c + l;
+    mi = blk * 128 + 2 * l + c;
+  }
   union { u32x4 v; uint16_t h[8]; } in;
-  in.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v8) + id);
-  const uint32_t word8 = __builtin_nontemporal_load(m8 + id);
+  in.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v8) + vi);
+  const uint32_t word8 = __builtin_nontemporal_load(m8 + mi);
   union { u32x4 v[2]; uint16_t h[16]; } out;
   uint32_t word4 = 0;
 #pragma unroll
@@ -704,12 +718,16 @@ __global__ __launch_bounds__(256) void k_nm28_to24(const uint16_t* __restrict__ 
 namespace sra {
 
 hipError_t launch_nm28_to24(const uint16_t* v8, const uint32_t* m8, int64_t rows, int64_t cols,
-                            uint16_t* v4, uint32_t* m4, hipStream_t s) {
+                            uint16_t* v4, uint32_t* m4, hipStream_t s, bool tiled) {
   const int64_t wpr = cols / 32, total = rows * wpr;
   if (total == 0) return hipSuccess;
   if (cols % 32) return hipErrorInvalidValue;
-  launch(SRA_KERNEL_COMPRESS, k_nm28_to24, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, v8, m8,
-         total, v4, m4);
+  if (tiled)
+    launch(SRA_KERNEL_COMPRESS, k_nm28_to24<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+           v8, m8, total, wpr, v4, m4);
+  else
+    launch(SRA_KERNEL_COMPRESS, k_nm28_to24<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+           v8, m8, total, wpr, v4, m4);
   return hipGetLastError();
 }
 

@@ -343,7 +343,11 @@ struct Batch28 {
   u32x4 x[XC];
 };
 
-template <int NW, int FW, int BW, int OCC>
+// TL: the 2:8 streaming layout (launch_nm_tile28_bf16, 256-column batches): every (16-row tile,
+// batch) block is 2 KB of values, chunk c of lane l at 1024 c + 16 l, then 512 bytes of metadata,
+// lane l's two words at 8 l, so each wave load reads 1 KB (or 512 bytes) contiguously and
+// non-temporally, and rows past R and columns past C hold zeros.
+template <int NW, int FW, int BW, int OCC, bool TL>
 __global__ __launch_bounds__(64 * NW, OCC) void k_decode28(const uint16_t* __restrict__ vals,
                                                           const uint32_t* __restrict__ meta, int64_t R,
                                                           int64_t C, const uint16_t* __restrict__ act,
@@ -353,6 +357,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode28(const uint16_t* __res
   constexpr int FR = NW * FW, RB = 16 * FR, NT = 64 * NW, CL = BT::CL, XC = BT::XC;
   constexpr int XLD = d28_xld<BW>(), XCH = 2 * BW;  // Act chunks per batch (16 tokens x BW / 8)
   static_assert(CL == 2 || CL == 4, "256- or 512-column batches");
+  static_assert(!TL || BW == 256, "the streaming layout has 256-column batches");
   __shared__ __attribute__((aligned(16))) uint16_t xl[2][16 * XLD];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, q = l >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * RB;
@@ -360,14 +365,33 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode28(const uint16_t* __res
   const int nb = (int)((C + BW - 1) / BW);          // batches
   const int c32 = (int)C;
   const int64_t nrows = min((int64_t)RB, R - row0);
-  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vals + row0 * vstride), (short)0, (int)(nrows * vstride * 2), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t mres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(meta + row0 * mstride), (short)0, (int)(nrows * mstride * 4), kRsrcWord3);
+  const int64_t tile0 = row0 / 16, ntl = (nrows + 15) / 16;  // streaming layout: this workgroup's tiles
+  const __amdgpu_buffer_rsrc_t vres =
+      TL ? __builtin_amdgcn_make_buffer_rsrc((void*)(vals + tile0 * nb * 1024), (short)0,
+                                             (int)(ntl * nb * 2048), kRsrcWord3)
+         : __builtin_amdgcn_make_buffer_rsrc((void*)(vals + row0 * vstride), (short)0,
+                                             (int)(nrows * vstride * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t mres =
+      TL ? __builtin_amdgcn_make_buffer_rsrc((void*)(meta + tile0 * nb * 128), (short)0,
+                                             (int)(ntl * nb * 512), kRsrcWord3)
+         : __builtin_amdgcn_make_buffer_rsrc((void*)(meta + row0 * mstride), (short)0,
+                                             (int)(nrows * mstride * 4), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)act, (short)0, (int)(T * C * 2), kRsrcWord3);
 
   auto load = [&](int b, BT& B) {
+    if constexpr (TL) {
+#pragma unroll
+      for (int f = 0; f < FW; ++f) {  // tiles past the workgroup's last read zero (past the resource)
+        const uint32_t blk = (uint32_t)(((w + NW * f) * nb + b) * 2048);
+#pragma unroll
+        for (int c = 0; c < CL; ++c)
+          B.v[f][c] = __builtin_amdgcn_raw_buffer_load_b128(vres, blk + 1024 * c + 16 * l, 0, kStreamPolicy);
+        const u32x2 m = __builtin_amdgcn_raw_buffer_load_b64(mres, blk / 4 + 8 * l, 0, kStreamPolicy);
+        B.m[f][0] = m[0];
+        B.m[f][1] = m[1];
+      }
+    } else {
 #pragma unroll
     for (int f = 0; f < FW; ++f) {
       const int row = 16 * (w + NW * f) + l16;  // rows past nrows read zero (past the resource)
@@ -388,6 +412,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode28(const uint16_t* __res
 #pragma unroll
         for (int c = 0; c < 4; ++c) B.m[f][c] = m[c];
       }
+    }
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {  // chunk v: token v / (BW/8), columns 8 (v % (BW/8)) .. +7 of the batch
@@ -460,6 +485,37 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_decode28(const uint16_t* __res
   for (int f = 0; f < FW; ++f) tail.finish_tile(acc[f], w + NW * f, out);
 }
 
+// Canonical 2:8 arrays -> the 2:8 streaming layout (see k_decode28).  One thread per 16-byte chunk:
+// value chunks first (tiles x batches x 128: chunk c = g / 64 of lane g % 64), then metadata chunks
+// (tiles x batches x 32: lanes 2h and 2h + 1).  C is a multiple of 32, so a value chunk (8 stored
+// values, 4 groups) is wholly inside a row or past its end.
+__global__ void k_nm_tile28(const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta,
+                            int64_t R, int64_t C, u32x4* __restrict__ tvals, u32x4* __restrict__ tmeta) {
+  const int64_t ntiles = (R + 15) / 16, nb = (C + 255) / 256;
+  const int64_t nv = ntiles * nb * 128, nm = ntiles * nb * 32;
+  const int64_t vstride = C / 4, mstride = C / 32;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < nv + nm;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (g < nv) {
+      const int64_t blk = g >> 7, t = blk / nb, b = blk - t * nb;
+      const int c = (int)((g >> 6) & 1), l = (int)(g & 63), i = l & 15, q = l >> 4;
+      const int64_t row = 16 * t + i, col = 64 * b + 16 * q + 8 * c;  // stored-value column
+      if (row < R && col < vstride) v = *reinterpret_cast<const u32x4*>(vals + row * vstride + col);
+      tvals[g] = v;
+    } else {
+      const int64_t h = g - nv, blk = h >> 5, t = blk / nb, b = blk - t * nb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // lane 2 (h % 32) + e / 2, its word e % 2
+        const int l = (int)(2 * (h & 31) + (e >> 1)), i = l & 15, q = l >> 4;
+        const int64_t row = 16 * t + i, word = 8 * b + 2 * q + (e & 1);
+        if (row < R && word < mstride) v[e] = meta[row * mstride + word];
+      }
+      tmeta[h] = v;
+    }
+  }
+}
+
 // Canonical 2:4 arrays -> streaming layout (see the header comment).  One thread per 16-byte
 // chunk of the output: value chunks first (tiles x steps x 64), then metadata chunks
 // (tiles x batches x 64).  Values move as whole 16-byte chunks (C/2 is a multiple of 16, so a
@@ -501,6 +557,23 @@ void nm_tile_bytes(int64_t R, int64_t C, size_t* value_bytes, size_t* meta_bytes
   const int64_t ntiles = (R + 15) / 16;
   *value_bytes = (size_t)(ntiles * ((C + 63) / 64) * 1024);
   *meta_bytes = (size_t)(ntiles * ((C + 511) / 512) * 1024);
+}
+
+void nm28_tile_bytes(int64_t R, int64_t C, size_t* value_bytes, size_t* meta_bytes) {
+  const int64_t blocks = ((R + 15) / 16) * ((C + 255) / 256);
+  *value_bytes = (size_t)(blocks * 2048);
+  *meta_bytes = (size_t)(blocks * 512);
+}
+
+hipError_t launch_nm_tile28_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
+                                 void* t_vals, void* t_meta, hipStream_t s) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  if ((C & 31) != 0) return hipErrorInvalidValue;
+  const int64_t chunks = ((R + 15) / 16) * ((C + 255) / 256) * 160;
+  const unsigned grid = (unsigned)std::min<int64_t>((chunks + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_nm_tile28, dim3(grid), dim3(256), 0, s, s_vals, s_meta, R, C, (u32x4*)t_vals,
+                     (u32x4*)t_meta);
+  return hipGetLastError();
 }
 
 hipError_t launch_nm_tile_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R, int64_t C,
@@ -555,7 +628,7 @@ hipError_t launch_decode24_bf16(const uint16_t* s_vals, const uint32_t* s_meta, 
 
 hipError_t launch_decode28_bf16(const uint16_t* s_vals, const uint32_t* s_meta, int64_t R,
                                 int64_t C, const uint16_t* act, int64_t T, const Epilogue& ep,
-                                uint16_t* out, hipStream_t s) {
+                                uint16_t* out, hipStream_t s, bool tiled) {
   if (T <= 0 || R <= 0) return hipSuccess;
   if (T > 16 || (C & 31) != 0) return hipErrorInvalidValue;
   // Workgroup shapes (waves x row tiles per wave): 9 x 1 (144 rows), 4 x 2 (128), 4 x 1 (64) and
@@ -574,9 +647,15 @@ hipError_t launch_decode28_bf16(const uint16_t* s_vals, const uint32_t* s_meta, 
   else if (tuning().decode_rows == 3) pick = 3;
   const int rows = 16 * kShapes[pick][0] * kShapes[pick][1];
   const unsigned grid = (unsigned)((R + rows - 1) / rows);
-#define SRA_D28(NWV, FWV, BWV, OCCV)                                                                  \
-  launch(SRA_KERNEL_DECODE24, k_decode28<NWV, FWV, BWV, OCCV>, dim3(grid), dim3(64 * NWV), 0, s, s_vals, \
-         s_meta, R, C, act, T, ep, out)
+#define SRA_D28(NWV, FWV, BWV, OCCV)                                                             \
+  do {                                                                                             \
+    if (tiled)                                                                                     \
+      launch(SRA_KERNEL_DECODE24, k_decode28<NWV, FWV, BWV, OCCV, true>, dim3(grid), dim3(64 * NWV), \
+             0, s, s_vals, s_meta, R, C, act, T, ep, out);                                           \
+    else                                                                                           \
+      launch(SRA_KERNEL_DECODE24, k_decode28<NWV, FWV, BWV, OCCV, false>, dim3(grid), dim3(64 * NWV), \
+             0, s, s_vals, s_meta, R, C, act, T, ep, out);                                           \
+  } while (0)
   // (512-column batches, twice the bytes in flight per wave, measured no faster at the OPT-66B
   // FFN shape: 44.4 / 50.2 us against 44.1 / 49.6 us at T = 1 / 16)
   switch (pick) {

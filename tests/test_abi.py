@@ -322,10 +322,22 @@ def test_nm28_validation(lib):
     assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_OK
     W.dtype = SRA_F32
     assert lib.sra_fwd_workspace(ctypes.byref(W), 300, 8, ctypes.byref(n)) == SRA_ERR_UNSUPPORTED
+    # the 2:8 streaming layout: 16-row x 256-column blocks of 2 KB values + 512 B metadata
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sra_nm_tile_bytes(40, 288, 2, 8, ctypes.byref(vb), ctypes.byref(mb)) == SRA_OK
+    assert (vb.value, mb.value) == (3 * 2 * 2048, 3 * 2 * 512)
+    assert lib.sra_nm_tile_bytes(40, 288, 1, 2, ctypes.byref(vb), ctypes.byref(mb)) == SRA_ERR_UNSUPPORTED
     out = SraSparse()
     out.values, out.meta = FAKE, FAKE
-    assert lib.sra_nm_tile(ctypes.byref(nm_desc(rows=256, cols=256, n=2, m=8)), ctypes.byref(out),
+    assert lib.sra_nm_tile(ctypes.byref(nm_desc(rows=256, cols=256, n=1, m=2)), ctypes.byref(out),
                            None) == SRA_ERR_UNSUPPORTED
+    # a tiled 2:8 weight: any K % 32 at 16 tokens or fewer (the decode kernel) and above (the
+    # weight rewritten as 2:4), K % 128 only for the dense engine above 16 tokens
+    Wt = nm_desc(rows=256, cols=96, n=2, m=8)
+    Wt.format = SRA_FMT_NM_TILED
+    assert lib.sra_fwd_workspace(ctypes.byref(Wt), 16, 8, ctypes.byref(n)) == SRA_OK
+    assert lib.sra_fwd_workspace(ctypes.byref(Wt), 300, 8, ctypes.byref(n)) == SRA_OK
+    assert n.value >= 256 * 48 * 2 + 256 * 3 * 4
 
 
 def test_tuning_knobs(lib):

@@ -58,8 +58,9 @@ def test_lemma_2_1_on_gpu_2_8(gpu):
     assert abs(frac - 0.0339) > 0.02
 
 
-def run_layer(wl: Workload, n, m, seed=0, streaming=False, rows=None):
-    """Forward + backward of an N:M layer against the oracle (sampled token rows optional)."""
+def run_layer(wl: Workload, n, m, seed=0, streaming=False, rows=None, tile28=False):
+    """Forward + backward of an N:M layer against the oracle (sampled token rows optional).
+    tile28: both 2:8 weights in their streaming layout (sra_nm_tile)."""
     inp = layer_inputs(wl, seed=seed)
     X, W, A, B, dY = (inp[k].cuda() for k in ("X", "W", "A", "B", "dY"))
     r = wl.r
@@ -69,6 +70,8 @@ def run_layer(wl: Workload, n, m, seed=0, streaming=False, rows=None):
     else:
         S = sra.compress(W, n, m)
         P = sra.double_prune(S)
+        if tile28:
+            S, P = sra.nm_tile(S), sra.nm_tile(P)
     Y, U = sra.sparse_lora_fwd(S, X, A if r else None, B if r else None)
     g = sra.sparse_lora_bwd(P, dY, X, U, A if r else None, B if r else None, want_du=True)
     torch.cuda.synchronize()
@@ -121,6 +124,60 @@ DECODE_SHAPES = [(1, 96, 160, 8), (3, 608, 352, 0), (16, 1056, 224, 64), (7, 224
 @pytest.mark.parametrize("T,K,N,r", DECODE_SHAPES)
 def test_layer_2_8_decode(gpu, T, K, N, r):
     run_layer(Workload("nm28d", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + K + N)
+
+
+def tile28_expected(vals, meta, R, C):
+    """The 2:8 streaming layout restated from its definition: per (16-row tile t, 256-column batch b)
+    block, 2 KB of values (chunk c of lane l = 16q + i: row 16t + i's stored values 64b + 16q + 8c ..
+    +7, at element 512c + 8l) and 512 B of metadata (lane l: the row's words 8b + 2q, +1 at word
+    2l), zeros past the matrix."""
+    nt, nb = -(-R // 16), -(-C // 256)
+    tv = np.zeros((nt, nb, 2, 64, 8), np.uint16)
+    tm = np.zeros((nt, nb, 64, 2), np.uint32)
+    vs, ms = C // 4, C // 32
+    for t in range(nt):
+        for b in range(nb):
+            for l in range(64):
+                q, i = divmod(l, 16)
+                row = 16 * t + i
+                if row >= R:
+                    continue
+                for c in range(2):
+                    c0 = 64 * b + 16 * q + 8 * c
+                    if c0 < vs:
+                        tv[t, b, c, l] = vals[row, c0:c0 + 8]
+                for e in range(2):
+                    w = 8 * b + 2 * q + e
+                    if w < ms:
+                        tm[t, b, l, e] = meta[row, w]
+    return tv.ravel(), tm.ravel()
+
+
+@pytest.mark.parametrize("R,C", [(16, 32), (40, 288), (100, 608), (257, 1056)])
+def test_nm_tile_2_8_layout(gpu, R, C):
+    torch.manual_seed(R + C)
+    W = (torch.randn(R, C) * 0.02).to(torch.bfloat16).cuda()
+    S = sra.compress(W, 2, 8)
+    Tt = sra.nm_tile(S)
+    torch.cuda.synchronize()
+    ev, em = tile28_expected(bits(S.values).reshape(R, C // 4).astype(np.uint16), meta_u32(S.meta), R, C)
+    assert np.array_equal(bits(Tt.values).astype(np.uint16)[:ev.size], ev)
+    assert np.array_equal(meta_u32(Tt.meta).ravel()[:em.size], em)
+
+
+# both 2:8 weights in the streaming layout: the decode kernel reading its blocks (T <= 16, forward
+# and dX) and, above 16 tokens, the blocks rewritten as canonical 2:4 for the SMFMAC kernels (or the
+# dense engine's expanded-fragment kernels)
+@pytest.mark.parametrize("T,K,N,r", [(1, 96, 160, 8), (16, 1056, 224, 64), (7, 224, 992, 100),
+                                     (16, 5120, 2080, 16), (300, 256, 384, 24), (77, 608, 352, 5)])
+def test_layer_2_8_tiled(gpu, T, K, N, r):
+    run_layer(Workload("nm28t", T=T, K=K, N=N, r=r, dtype="bf16", fmt="nm"), 2, 8, seed=T + K, tile28=True)
+
+
+def test_layer_2_8_tiled_dense_engine(gpu):
+    with sra.tuned(engine="dense_mfma"):
+        run_layer(Workload("nm28tx", T=130, K=384, N=256, r=8, dtype="bf16", fmt="nm"), 2, 8, seed=3,
+                  tile28=True)
 
 
 @pytest.mark.parametrize("rows", [3, 4, 9])
@@ -214,7 +271,7 @@ def test_2_8_rejections(gpu):
         Y, _ = sra.sparse_lora_fwd(S, X[:T])
         torch.cuda.synchronize()
         assert Y.shape == (T, 64) and not Y.float().abs().any()
-    with pytest.raises(SraError):
-        sra.nm_tile(S)
+    with pytest.raises(SraError):  # the streaming layout is 2:4 or 2:8
+        sra.nm_tile(sra.compress(W, 1, 2))
     with pytest.raises(SraError):
         sra.compress_pair(W, 2, 8)
