@@ -199,7 +199,8 @@ static void rejections() {
   sra_sparse d8 = nm(64, 128, 2, 8, SRA_BF16);
   EXPECT(sra_masked_weight_grad(&d8, FAKE, FAKE, 16, FAKE, nullptr) == SRA_ERR_UNSUPPORTED);
   EXPECT(sra_nm_axpby(FAKE, 1.f, FAKE, 1.f, FAKE, -5, SRA_BF16, nullptr) == SRA_ERR_INVALID_ARG);
-  EXPECT(sra_nm_tile(&d8, &p, nullptr) == SRA_ERR_UNSUPPORTED);
+  sra_sparse d12 = nm(64, 128, 1, 2, SRA_BF16);
+  EXPECT(sra_nm_tile(&d12, &p, nullptr) == SRA_ERR_UNSUPPORTED);  // the streaming layout is 2:4 or 2:8
   EXPECT(sra_time_next_kernel(77, FAKE, FAKE) == SRA_ERR_INVALID_ARG);
   EXPECT(sra_time_next_kernel(3, nullptr, FAKE) == SRA_ERR_INVALID_ARG);
   EXPECT(sra_time_next_kernel(0, nullptr, nullptr) == SRA_OK);
