@@ -56,6 +56,10 @@ TRAFFIC_BYTES = {
     # (profiles/opt66b_ffn_decode_traffic.md: read requests x 128 B + 64-byte and 32-byte writes)
     "opt66b_ffn_decode/T16/streaming/k_decode24<3>": 3042927 * 128 + 12288 * 64 + 12289 * 32,
     "opt66b_ffn_decode/T1/streaming/k_decode24<3>": 3025411 * 128 + 768 * 64 + 768 * 32,
+    # the same weight at 2:8 on its streaming layout, k_decode28<9, 1, 256, 1, true>
+    # (profiles/opt66b_ffn_decode_2_8_traffic.md)
+    "opt66b_ffn_decode/T16/streaming/k_decode28<9,1>": 1725038 * 128 + 16384 * 64 + 4096 * 32,
+    "opt66b_ffn_decode/T1/streaming/k_decode28<9,1>": 1711224 * 128 + 1024 * 64 + 256 * 32,
 }
 
 
@@ -782,6 +786,7 @@ def bench_decode(args, wl, Ts):
                      "nm28_kernel_frac_hbm": round(kb28 / (k28_ms * 1e-3) / PEAK_HBM_BPS, 4),
                      "nm28_call_us": round(c28_ms * 1e3, 2),
                      "nm28_canonical_kernel_us": round(k28c_ms * 1e3, 2),
+                     "nm28_traffic": TRAFFIC_BYTES.get(f"{wl.name}/T{T}/streaming/k_decode28<9,1>"),
                      "nm28_speedup_vs_dense": round(d_ms / c28_ms, 3)})
     return rows
 
@@ -1001,7 +1006,8 @@ def loop_calls(args):
     T = args.decode_t if args.loop == "decode" else wl.T
     inp = layer_inputs(wl, seed=0, T=T, with_dy=args.loop == "spmm_bwd")
     X, W, A, B = (inp[k].to(dev) for k in ("X", "W", "A", "B"))
-    S = sra.compress(W)
+    n_, m_ = (int(x) for x in args.nm.split(":"))
+    S = sra.compress(W, n_, m_)
     if args.loop == "decode" and args.decode_layout == "streaming":
         S = sra.nm_tile(S)
     Y, U = sra.sparse_lora_fwd(S, X, A, B)
