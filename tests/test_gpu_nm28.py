@@ -180,6 +180,14 @@ def test_layer_2_8_tiled_dense_engine(gpu):
                   tile28=True)
 
 
+@pytest.mark.parametrize("tile28", [False, True])
+def test_layer_2_8_decode_128_row_workgroups(gpu, tile28):
+    """32768 output rows: the planner's pick is four waves of two row tiles (128-row workgroups, the
+    one shape with the adapter prefetch), on the canonical arrays and on the streaming layout."""
+    run_layer(Workload("nm28d128", T=4, K=256, N=32768, r=40, dtype="bf16", fmt="nm"), 2, 8, seed=11,
+              tile28=tile28)
+
+
 @pytest.mark.parametrize("rows", [3, 4, 9])
 def test_layer_2_8_decode_row_tiles(gpu, rows):
     """Each workgroup shape of the 2:8 decode kernel (48, 64 or 144 weight rows), forced; the
