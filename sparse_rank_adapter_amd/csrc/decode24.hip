@@ -2,7 +2,8 @@
 //   Out[t][row] = sum_c Act[t][c] S[row][c] + sum_j U[t][j] E(row, j)
 // (SLoPe paper, section 2.2 and its inference results: with few tokens the layer is bound by
 // reading the compressed weight, and 2:4 halves those bytes; values plus 2-bit metadata are
-// 9/16 of the dense bf16 weight.)
+// 9/16 of the dense bf16 weight.)  The 2:8 decode kernel (k_decode28, further below) computes the
+// same for 2:8 weights, 5/16 of the dense bytes, sharing the epilogue (DecodeTail).
 //
 // Design: one pass over S straight from HBM into registers, no LDS staging.  All tokens fit in
 // one v_smfmac_f32_16x16x64_bf16 column tile (tokens past T are zero), so the instruction's
