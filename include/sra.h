@@ -391,10 +391,12 @@ sra_status sra_nm_axpby(const void* a_values, float beta, const void* b_values, 
  *                          matrix instructions; SRA_ENGINE_DENSE_MFMA: the same pipeline with each
  *                          weight fragment expanded to dense bf16 (zeros at the pruned positions)
  *                          for dense MFMA (bf16, K % 128 == 0 for the forward, N % 128 == 0 for
- *                          the backward), the path 2:8 weights take for 16 tokens or fewer; above
- *                          that, on SMFMAC, a 2:8 weight is rewritten in the call's workspace as a
- *                          2:4 one (each four columns of a 2:8 row hold at most two kept entries;
- *                          +0.0 fills the rest) and runs on the 2:4 kernels
+ *                          the backward).  2:8 weights: 16 tokens or fewer always take the 2:8
+ *                          decode kernel on SMFMAC; above that, on SMFMAC, a 2:8 weight is
+ *                          rewritten in the call's workspace as a 2:4 one (each four columns of a
+ *                          2:8 row hold at most two kept entries; +0.0 fills the rest) and runs on
+ *                          the 2:4 kernels, and on the dense engine its fragments are expanded
+ *                          (the streaming layout's after the same 2:4 rewrite)
  *   SRA_TUNE_DECODE_ROWS   decode workgroup row tiles of 16 rows: 3, 4 or 9 (0 = the planner's)
  *   SRA_TUNE_ROWS_SLICES   reduction slices of the rank > 32 U / dU kernel (0 = the planner's)
  *   SRA_TUNE_GRADS_SLICES  token slices of the dA / dB kernel (0 = the planner's)
