@@ -1030,6 +1030,10 @@ def main():
         print("bench.py measures one GPU: the library runs the layer on a single MI355X and has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "opt13b_mlp" and args.nm != "2:4" and not args.loop:
+        print("--nm applies to the single-layer workloads: the opt13b_mlp line is the 2:4 step and "
+              "carries the same step on 2:8 weights as its nm28_opt13b_mlp extra", file=sys.stderr)
+        sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
